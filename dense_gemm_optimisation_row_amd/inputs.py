@@ -1,0 +1,102 @@
+"""Seeded synthetic inputs for C = A x B (shared by tests, bench and smoke).
+
+This module only draws random matrices; it holds none of the product's
+arithmetic and imports neither the GPU library nor the oracle.  Both sides
+are fed the very same arrays from here.
+
+Generator: numpy ``default_rng(seed)`` (PCG64).  A is drawn first, then B,
+from one generator per (workload, variant).  Distributions:
+
+* ``uniform``: i.i.d. uniform on [-1, 1) in binary32;
+* ``normal``: i.i.d. standard normal, rounded to binary32;
+* ``int``: i.i.d. integers in {-4, ..., 4}, so every partial sum of a product
+  with K <= 8192 is an integer of magnitude <= 16*K < 2^24, exact in binary32
+  whatever the summation order;
+* for binary16 inputs the binary32 draw is rounded once to binary16 by numpy
+  (round to nearest even) and both sides read the same bits.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    M: int
+    N: int
+    K: int
+    dtype: str          # "f32" or "f16" (input type; the output is always f32)
+    dist: str           # "uniform" or "normal"
+    seed: int           # seed of the main draw
+    int_seed: int       # seed of the small-integer variant
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.M * self.N * self.K
+
+
+# The workloads: square FP32 at 256 and 1024 (1024 is the size the pages time),
+# ragged FP32 shapes that exercise edge masking, FP32 4096 with normal inputs,
+# and FP16-input 8192.
+WORKLOADS = {
+    w.name: w for w in [
+        Workload("f32_256", 256, 256, 256, "f32", "uniform", 1001, 2001),
+        Workload("f32_1024", 1024, 1024, 1024, "f32", "uniform", 1002, 2002),
+        Workload("f32_1000", 1000, 1000, 1000, "f32", "uniform", 1003, 2003),
+        Workload("f32_4097x33x777", 4097, 33, 777, "f32", "uniform", 1004, 2004),
+        Workload("f32_4096", 4096, 4096, 4096, "f32", "normal", 1005, 2005),
+        Workload("f16_8192", 8192, 8192, 8192, "f16", "uniform", 1006, 2006),
+    ]
+}
+
+
+def _draw(rng: np.random.Generator, shape, dist: str) -> np.ndarray:
+    if dist == "uniform":
+        return rng.random(shape, dtype=np.float32) * np.float32(2.0) - np.float32(1.0)
+    if dist == "normal":
+        return rng.standard_normal(shape, dtype=np.float32)
+    if dist == "int":
+        return rng.integers(-4, 5, size=shape, dtype=np.int8).astype(np.float32)
+    raise ValueError(f"unknown distribution {dist!r}")
+
+
+def matrices(M: int, N: int, K: int, seed: int, dist: str = "uniform",
+             dtype: str = "f32"):
+    """Return (A, B): A is M x K, B is K x N, C-contiguous numpy arrays.
+
+    ``dtype`` "f32" gives float32; "f16" gives float16 (the float32 draw
+    rounded once to binary16).
+    """
+    rng = np.random.default_rng(seed)
+    A = _draw(rng, (M, K), dist)
+    B = _draw(rng, (K, N), dist)
+    if dtype == "f16":
+        A = A.astype(np.float16)
+        B = B.astype(np.float16)
+    elif dtype != "f32":
+        raise ValueError(f"unknown dtype {dtype!r}")
+    return np.ascontiguousarray(A), np.ascontiguousarray(B)
+
+
+def workload_matrices(w: Workload | str, integer: bool = False):
+    """Inputs of a named workload; ``integer`` selects its small-integer variant."""
+    if isinstance(w, str):
+        w = WORKLOADS[w]
+    if integer:
+        return matrices(w.M, w.N, w.K, w.int_seed, "int", w.dtype)
+    return matrices(w.M, w.N, w.K, w.seed, w.dist, w.dtype)
+
+
+def sample_indices(M: int, N: int, count: int, seed: int):
+    """``count`` (row, col) pairs: the four corners, the last row and column,
+    then uniform random positions.  Used to check outputs one by one."""
+    rng = np.random.default_rng(seed)
+    fixed_r = [0, 0, M - 1, M - 1, M - 1, M // 2]
+    fixed_c = [0, N - 1, 0, N - 1, N // 2, N - 1]
+    n_rand = max(0, count - len(fixed_r))
+    rows = np.concatenate([np.array(fixed_r), rng.integers(0, M, n_rand)])
+    cols = np.concatenate([np.array(fixed_c), rng.integers(0, N, n_rand)])
+    return rows.astype(np.int64), cols.astype(np.int64)

@@ -1,0 +1,159 @@
+"""CPU oracle for C = A x B (row-major, FP32 result) -- test infrastructure.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The GPU library never loads it, and it
+imports nothing from the GPU library: the two share no code.
+
+The arithmetic lives in ``oracle.c`` (plain loops, binary64 accumulation in
+ascending k, one rounding to binary32).  This module only compiles that file
+with gcc and marshals numpy arrays into it through ctypes.
+
+Sources followed: "Lesson 8: how a GPU does matrix multiply", section 1
+(C[i,j] = sum_k A[i,k] B[k,j]) and section 2 (row-major indexing); "SGEMM
+optimisation journey", Level 1; "4. GEMM optimisation", section 4.1.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+# -ffp-contract=off: no fused multiply-add may merge a product into the sum.
+# -fno-fast-math: keep IEEE semantics (no reassociation of the k-sum).
+CFLAGS = ["-O2", "-fopenmp", "-fno-fast-math", "-ffp-contract=off", "-fPIC",
+          "-shared", "-std=c11", "-Wall", "-Wextra"]
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so beside it (gcc) and return the path."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.run(["gcc", *CFLAGS, _SRC, "-o", tmp, "-lm"], check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def configure(lib):
+    """Declare the C signatures on a loaded oracle library and return it."""
+    p = ctypes.c_void_p
+    i = ctypes.c_int
+    i64 = ctypes.c_int64
+    lib.oracle_f16_to_f64.argtypes = [ctypes.c_uint16]
+    lib.oracle_f16_to_f64.restype = ctypes.c_double
+    lib.oracle_threads.argtypes = [i]
+    lib.oracle_threads.restype = i
+    for name in ("oracle_gemm_f32", "oracle_gemm_f16"):
+        f = getattr(lib, name)
+        f.argtypes = [i, i, i, p, p, p, i]
+        f.restype = i
+    for name in ("oracle_gemm_f32_at", "oracle_gemm_f16_at"):
+        f = getattr(lib, name)
+        f.argtypes = [i, i, i, p, p, i64, p, p, p, i]
+        f.restype = i
+    return lib
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        _lib = configure(ctypes.CDLL(_LIB))
+    return _lib
+
+
+def _ptr(a: np.ndarray):
+    return ctypes.c_void_p(a.ctypes.data) if a.size else None
+
+
+def _check_inputs(A, B, dtype):
+    A = np.ascontiguousarray(A)
+    B = np.ascontiguousarray(B)
+    if A.dtype != dtype or B.dtype != dtype:
+        raise TypeError(f"oracle expects {np.dtype(dtype).name} inputs")
+    if A.ndim != 2 or B.ndim != 2 or A.shape[1] != B.shape[0]:
+        raise ValueError(f"shapes {A.shape} x {B.shape} do not chain")
+    return A, B
+
+
+def threads(nthreads: int = 0) -> int:
+    """Threads the oracle uses for a request of ``nthreads`` (0 = OpenMP default)."""
+    return int(_load().oracle_threads(nthreads))
+
+
+def f16_to_f64(bits: int) -> float:
+    """Decode one IEEE binary16 bit pattern exactly."""
+    return float(_load().oracle_f16_to_f64(int(bits) & 0xFFFF))
+
+
+def gemm_f32(A: np.ndarray, B: np.ndarray, out: np.ndarray | None = None,
+             nthreads: int = 0) -> np.ndarray:
+    """C = A x B for float32 A (M x K), B (K x N); binary64 sum, binary32 result.
+
+    ``out`` (float32, M x N, contiguous) is overwritten when given; with M or N
+    zero nothing is written.
+    """
+    A, B = _check_inputs(A, B, np.float32)
+    M, K = A.shape
+    N = B.shape[1]
+    C = np.empty((M, N), np.float32) if out is None else out
+    if C.shape != (M, N) or C.dtype != np.float32 or not C.flags.c_contiguous:
+        raise ValueError("out must be a contiguous float32 M x N array")
+    rc = _load().oracle_gemm_f32(M, N, K, _ptr(A), _ptr(B), _ptr(C), nthreads)
+    if rc != 0:
+        raise RuntimeError(f"oracle_gemm_f32 failed ({rc})")
+    return C
+
+
+def gemm_f16(A: np.ndarray, B: np.ndarray, out: np.ndarray | None = None,
+             nthreads: int = 0) -> np.ndarray:
+    """C = A x B for binary16 A, B (numpy float16 or uint16 bit patterns)."""
+    A = np.ascontiguousarray(A).view(np.uint16) if np.asarray(A).dtype == np.float16 else A
+    B = np.ascontiguousarray(B).view(np.uint16) if np.asarray(B).dtype == np.float16 else B
+    A, B = _check_inputs(A, B, np.uint16)
+    M, K = A.shape
+    N = B.shape[1]
+    C = np.empty((M, N), np.float32) if out is None else out
+    if C.shape != (M, N) or C.dtype != np.float32 or not C.flags.c_contiguous:
+        raise ValueError("out must be a contiguous float32 M x N array")
+    rc = _load().oracle_gemm_f16(M, N, K, _ptr(A), _ptr(B), _ptr(C), nthreads)
+    if rc != 0:
+        raise RuntimeError(f"oracle_gemm_f16 failed ({rc})")
+    return C
+
+
+def _at(fname, A, B, rows, cols, nthreads):
+    M, K = A.shape
+    N = B.shape[1]
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    cols = np.ascontiguousarray(cols, dtype=np.int64)
+    if rows.shape != cols.shape:
+        raise ValueError("rows and cols must have the same shape")
+    out = np.empty(rows.shape, np.float32)
+    rc = getattr(_load(), fname)(M, N, K, _ptr(A), _ptr(B), rows.size,
+                                 _ptr(rows), _ptr(cols), _ptr(out), nthreads)
+    if rc != 0:
+        raise RuntimeError(f"{fname} failed ({rc})")
+    return out
+
+
+def gemm_f32_at(A, B, rows, cols, nthreads: int = 0) -> np.ndarray:
+    """C[rows[t], cols[t]] of A x B for float32 inputs, one dot product each."""
+    A, B = _check_inputs(A, B, np.float32)
+    return _at("oracle_gemm_f32_at", A, B, rows, cols, nthreads)
+
+
+def gemm_f16_at(A, B, rows, cols, nthreads: int = 0) -> np.ndarray:
+    """C[rows[t], cols[t]] of A x B for binary16 inputs, one dot product each."""
+    A = np.ascontiguousarray(A).view(np.uint16) if np.asarray(A).dtype == np.float16 else A
+    B = np.ascontiguousarray(B).view(np.uint16) if np.asarray(B).dtype == np.float16 else B
+    A, B = _check_inputs(A, B, np.uint16)
+    return _at("oracle_gemm_f16_at", A, B, rows, cols, nthreads)

@@ -1,0 +1,215 @@
+/*
+ * CPU oracle for the dense row-major matrix product C = A x B.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the slow, obviously correct
+ * definition that the HIP kernels are checked against.  Only the test suite,
+ * the smoke check and the CPU-baseline leg of the benchmark may load it; the
+ * library's own call path never does.  It shares no code, header or table
+ * with the GPU library and includes nothing from it.
+ *
+ * What it computes (the definition, nothing more):
+ *   A is M x K, B is K x N, C is M x N, all row-major with packed leading
+ *   dimensions (A[i*K+k], B[k*N+j], C[i*N+j]).
+ *   C[i][j] = sum over k = 0 .. K-1 of A[i][k] * B[k][j].
+ *   - "Lesson 8: how a GPU does matrix multiply", section 1 (the element
+ *     formula) and section 2 (the row-major index expressions);
+ *   - "SGEMM optimisation journey", Level 1 (the same sum, k from 0 to K-1);
+ *   - "4. GEMM optimisation", section 4.1 (A is MxK, B is KxN, C is MxN; the
+ *     sum starts at zero, so K = 0 yields 0, and C is overwritten).
+ *
+ * Precision: every product of two binary32 (or two binary16) values is exact
+ * in binary64, so each element is the binary64 running sum of exact products,
+ * taken in ascending k from +0.0, and rounded once to binary32 with the C
+ * cast (round to nearest, ties to even).  Build with -ffp-contract=off so no
+ * step is fused.
+ *
+ * The pages do not fix the accumulator precision (their listings accumulate
+ * in float); binary64 accumulation is the reading taken here, so a correct
+ * GPU result differs from this one by binary32 accumulation error only, and
+ * on small-integer inputs (every partial sum exact) by nothing at all.
+ *
+ * Parity pins (checked by the CPU test suite, not by re-typing this code):
+ * identity and permutation products, rank-1 closed forms, K = 1 against
+ * numpy's correctly rounded binary32 product, brute force against exact
+ * rational sums on all shapes up to 6x6x6, numpy's binary64 matmul within
+ * one binary32 ulp, exact integer products, thread-count determinism, and
+ * the binary16 decoder against numpy over all 65536 bit patterns.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_OK 0
+#define ORACLE_ERR_DIM (-1)
+#define ORACLE_ERR_ALLOC (-2)
+
+/* IEEE 754 binary16 bit pattern -> exact binary64 value.
+ * Layout: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits.
+ *   exponent 0      : subnormal, value = fraction * 2^-24
+ *   exponent 1..30  : normal,    value = (1024 + fraction) * 2^(exponent-25)
+ *   exponent 31     : infinity (fraction 0) or NaN. */
+double oracle_f16_to_f64(uint16_t h)
+{
+    const int sign = (h >> 15) & 1;
+    const int expo = (h >> 10) & 0x1f;
+    const int frac = h & 0x3ff;
+    double v;
+    if (expo == 0)
+        v = ldexp((double)frac, -24);
+    else if (expo == 31)
+        v = frac ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + frac), expo - 25);
+    return sign ? -v : v;
+}
+
+static int thread_count(int nthreads)
+{
+#ifdef _OPENMP
+    return nthreads > 0 ? nthreads : omp_get_max_threads();
+#else
+    (void)nthreads;
+    return 1;
+#endif
+}
+
+/* Number of threads the full-matrix routines use for a given request. */
+int oracle_threads(int nthreads) { return thread_count(nthreads); }
+
+/*
+ * Full product, binary32 inputs.
+ * The loop order is i, then k, then j with one binary64 accumulator per
+ * element of the current row.  For every (i, j) the operations are exactly
+ * those of the textbook i-j-k loop: start from 0.0, add A[i][k]*B[k][j] for
+ * k = 0, 1, ..., K-1, round once.  Rows are independent, so splitting rows
+ * across threads cannot change any bit.
+ * M = 0 or N = 0 writes nothing; K = 0 writes zeros.
+ */
+int oracle_gemm_f32(int M, int N, int K, const float *A, const float *B,
+                    float *C, int nthreads)
+{
+    if (M < 0 || N < 0 || K < 0)
+        return ORACLE_ERR_DIM;
+    if (M == 0 || N == 0)
+        return ORACLE_OK;
+    int failed = 0;
+#pragma omp parallel num_threads(thread_count(nthreads)) reduction(| : failed)
+    {
+        double *acc = (double *)malloc((size_t)N * sizeof(double));
+        if (!acc)
+            failed = 1;
+#pragma omp for schedule(static)
+        for (int i = 0; i < M; ++i) {
+            if (!acc)
+                continue;
+            for (int j = 0; j < N; ++j)
+                acc[j] = 0.0;
+            for (int k = 0; k < K; ++k) {
+                const double a = (double)A[(size_t)i * K + k];
+                const float *brow = B + (size_t)k * N;
+                for (int j = 0; j < N; ++j)
+                    acc[j] += a * (double)brow[j];
+            }
+            for (int j = 0; j < N; ++j)
+                C[(size_t)i * N + j] = (float)acc[j];
+        }
+        free(acc);
+    }
+    return failed ? ORACLE_ERR_ALLOC : ORACLE_OK;
+}
+
+/*
+ * Full product, binary16 inputs given as raw bit patterns, binary32 output.
+ * Each input is decoded exactly to binary64 by oracle_f16_to_f64 (through a
+ * 65536-entry table of its results), then the same sum as above is formed.
+ */
+int oracle_gemm_f16(int M, int N, int K, const uint16_t *A, const uint16_t *B,
+                    float *C, int nthreads)
+{
+    if (M < 0 || N < 0 || K < 0)
+        return ORACLE_ERR_DIM;
+    if (M == 0 || N == 0)
+        return ORACLE_OK;
+    double *dec = (double *)malloc(65536 * sizeof(double));
+    if (!dec)
+        return ORACLE_ERR_ALLOC;
+    for (int h = 0; h < 65536; ++h)
+        dec[h] = oracle_f16_to_f64((uint16_t)h);
+    int failed = 0;
+#pragma omp parallel num_threads(thread_count(nthreads)) reduction(| : failed)
+    {
+        double *acc = (double *)malloc((size_t)N * sizeof(double));
+        if (!acc)
+            failed = 1;
+#pragma omp for schedule(static)
+        for (int i = 0; i < M; ++i) {
+            if (!acc)
+                continue;
+            for (int j = 0; j < N; ++j)
+                acc[j] = 0.0;
+            for (int k = 0; k < K; ++k) {
+                const double a = dec[A[(size_t)i * K + k]];
+                const uint16_t *brow = B + (size_t)k * N;
+                for (int j = 0; j < N; ++j)
+                    acc[j] += a * dec[brow[j]];
+            }
+            for (int j = 0; j < N; ++j)
+                C[(size_t)i * N + j] = (float)acc[j];
+        }
+        free(acc);
+    }
+    free(dec);
+    return failed ? ORACLE_ERR_ALLOC : ORACLE_OK;
+}
+
+/*
+ * Selected elements only: out[t] = C[rows[t]][cols[t]], each formed as the
+ * plain dot product of row rows[t] of A with column cols[t] of B in ascending
+ * k.  Same operation sequence as the full routines, so the same bits; used
+ * where the full product would take too long on the host.
+ */
+int oracle_gemm_f32_at(int M, int N, int K, const float *A, const float *B,
+                       int64_t count, const int64_t *rows, const int64_t *cols,
+                       float *out, int nthreads)
+{
+    if (M < 0 || N < 0 || K < 0 || count < 0)
+        return ORACLE_ERR_DIM;
+    for (int64_t t = 0; t < count; ++t)
+        if (rows[t] < 0 || rows[t] >= M || cols[t] < 0 || cols[t] >= N)
+            return ORACLE_ERR_DIM;
+#pragma omp parallel for num_threads(thread_count(nthreads)) schedule(static)
+    for (int64_t t = 0; t < count; ++t) {
+        const int64_t i = rows[t], j = cols[t];
+        double acc = 0.0;
+        for (int k = 0; k < K; ++k)
+            acc += (double)A[(size_t)i * K + k] * (double)B[(size_t)k * N + j];
+        out[t] = (float)acc;
+    }
+    return ORACLE_OK;
+}
+
+int oracle_gemm_f16_at(int M, int N, int K, const uint16_t *A,
+                       const uint16_t *B, int64_t count, const int64_t *rows,
+                       const int64_t *cols, float *out, int nthreads)
+{
+    if (M < 0 || N < 0 || K < 0 || count < 0)
+        return ORACLE_ERR_DIM;
+    for (int64_t t = 0; t < count; ++t)
+        if (rows[t] < 0 || rows[t] >= M || cols[t] < 0 || cols[t] >= N)
+            return ORACLE_ERR_DIM;
+#pragma omp parallel for num_threads(thread_count(nthreads)) schedule(static)
+    for (int64_t t = 0; t < count; ++t) {
+        const int64_t i = rows[t], j = cols[t];
+        double acc = 0.0;
+        for (int k = 0; k < K; ++k)
+            acc += oracle_f16_to_f64(A[(size_t)i * K + k]) *
+                   oracle_f16_to_f64(B[(size_t)k * N + j]);
+        out[t] = (float)acc;
+    }
+    return ORACLE_OK;
+}

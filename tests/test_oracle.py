@@ -1,0 +1,264 @@
+"""Pins for the CPU oracle: each test ties it to something other than itself.
+
+The oracle computes C[i,j] = sum_k A[i,k] B[k,j] ("Lesson 8: how a GPU does
+matrix multiply", section 1; "SGEMM optimisation journey", Level 1) with
+row-major operands (Lesson 8, section 2), K = 0 giving zeros and C being
+overwritten ("4. GEMM optimisation", section 4.1).  The pages print no worked
+numeric example of C, so the pins below are closed forms, exact rational
+arithmetic, library routines in special cases and invariants.
+"""
+import ctypes
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+
+RNG = np.random.default_rng(12345)
+
+
+def _wide_f32(shape, rng, lo=-20, hi=20):
+    """Random binary32 values with exponents spread over [lo, hi)."""
+    mant = rng.uniform(1.0, 2.0, shape)
+    sign = rng.choice([-1.0, 1.0], shape)
+    expo = rng.integers(lo, hi, shape)
+    return (sign * mant * np.exp2(expo)).astype(np.float32)
+
+
+def _bits(x):
+    return np.ascontiguousarray(x, np.float32).view(np.uint32)
+
+
+# ----------------------------------------------------------------- binary16 --
+
+def test_f16_decoder_matches_numpy_on_every_bit_pattern():
+    pats = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = pats.view(np.float16).astype(np.float64)
+    got = np.array([oracle.f16_to_f64(int(h)) for h in pats])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    # sign of zero is kept
+    assert np.signbit(oracle.f16_to_f64(0x8000)) and not np.signbit(oracle.f16_to_f64(0))
+
+
+def test_f16_decoder_spot_values():
+    # 0x3C00 = 1.0, 0xC000 = -2.0, 0x0001 = 2^-24 (smallest subnormal),
+    # 0x03FF = 1023 * 2^-24 (largest subnormal), 0x0400 = 2^-14, 0x7BFF = 65504.
+    cases = {0x3C00: 1.0, 0xC000: -2.0, 0x0001: 2.0 ** -24,
+             0x03FF: 1023 * 2.0 ** -24, 0x0400: 2.0 ** -14, 0x7BFF: 65504.0,
+             0x3555: 1365 / 4096, 0x7C00: float("inf")}
+    for h, v in cases.items():
+        assert oracle.f16_to_f64(h) == v, hex(h)
+
+
+# ------------------------------------------------------- closed-form pins ---
+
+@pytest.mark.parametrize("M,K", [(1, 1), (7, 13), (64, 33), (129, 200)])
+def test_identity_right_and_left(M, K):
+    A = _wide_f32((M, K), RNG)
+    I_k = np.eye(K, dtype=np.float32)
+    I_m = np.eye(M, dtype=np.float32)
+    assert np.array_equal(oracle.gemm_f32(A, I_k), A)
+    assert np.array_equal(oracle.gemm_f32(I_m, A), A)
+
+
+@pytest.mark.parametrize("M,K,N", [(5, 9, 11), (70, 40, 90)])
+def test_permutation_products(M, K, N):
+    A = _wide_f32((M, K), RNG)
+    B = _wide_f32((K, N), RNG)
+    pr = RNG.permutation(M)
+    pc = RNG.permutation(N)
+    P_rows = np.eye(M, dtype=np.float32)[pr]          # (P A)[i] = A[pr[i]]
+    P_cols = np.eye(N, dtype=np.float32)[:, pc]       # (B Q)[:, j] = B[:, pc[j]]
+    assert np.array_equal(oracle.gemm_f32(P_rows, A), A[pr])
+    assert np.array_equal(oracle.gemm_f32(B, P_cols), B[:, pc])
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 1, 1), (6, 17, 9), (33, 300, 45)])
+def test_rank1_closed_form(M, K, N):
+    # A = u v^T, B = w z^T  =>  C = (v . w) u z^T, exact for small integers.
+    u = RNG.integers(-4, 5, M)
+    v = RNG.integers(-4, 5, K)
+    w = RNG.integers(-4, 5, K)
+    z = RNG.integers(-4, 5, N)
+    A = np.outer(u, v).astype(np.float32)
+    B = np.outer(w, z).astype(np.float32)
+    expect = (int(v @ w) * np.outer(u, z)).astype(np.float32)
+    assert np.array_equal(oracle.gemm_f32(A, B), expect)
+
+
+def test_all_ones_gives_K():
+    for K in (1, 2, 777, 4096):
+        C = oracle.gemm_f32(np.ones((3, K), np.float32), np.ones((K, 5), np.float32))
+        assert np.all(C == K)
+
+
+def test_K1_is_the_correctly_rounded_product():
+    # One term: C[i,j] = fl32(A[i,0] * B[0,j]).  numpy's binary32 multiply is
+    # IEEE correctly rounded, so the bits must agree exactly.
+    A = _wide_f32((50, 1), RNG)
+    B = _wide_f32((1, 70), RNG)
+    expect = A * B                      # float32 x float32 -> float32, RNE
+    got = oracle.gemm_f32(A, B)
+    assert np.array_equal(_bits(got), _bits(expect))
+
+
+def test_K0_writes_zeros_and_overwrites():
+    out = np.full((4, 6), np.nan, np.float32)
+    oracle.gemm_f32(np.empty((4, 0), np.float32), np.empty((0, 6), np.float32), out=out)
+    assert np.array_equal(out, np.zeros((4, 6), np.float32))
+    # C is overwritten, not accumulated into
+    A = np.ones((2, 3), np.float32)
+    out = np.full((2, 2), 100.0, np.float32)
+    oracle.gemm_f32(A, np.ones((3, 2), np.float32), out=out)
+    assert np.all(out == 3.0)
+
+
+def test_empty_M_or_N_writes_nothing_and_bad_dims_fail():
+    lib = oracle._load()
+    sentinel = np.full(8, 7.0, np.float32)
+    A = np.ones(16, np.float32)
+    p = lambda a: ctypes.c_void_p(a.ctypes.data)
+    assert lib.oracle_gemm_f32(0, 4, 3, p(A), p(A), p(sentinel), 1) == 0
+    assert lib.oracle_gemm_f32(4, 0, 3, p(A), p(A), p(sentinel), 1) == 0
+    assert np.all(sentinel == 7.0)
+    assert lib.oracle_gemm_f32(-1, 4, 3, p(A), p(A), p(sentinel), 1) == -1
+    assert lib.oracle_gemm_f32(1, 1, -3, p(A), p(A), p(sentinel), 1) == -1
+    with pytest.raises(ValueError):
+        oracle.gemm_f32(np.ones((2, 3), np.float32), np.ones((4, 2), np.float32))
+
+
+# -------------------------------------------------- exact rational brute force
+
+def _exact_product(A, B):
+    M, K = A.shape
+    N = B.shape[1]
+    Af = [[Fraction(float(x)) for x in row] for row in A]
+    Bf = [[Fraction(float(x)) for x in row] for row in B]
+    return [[sum((Af[i][k] * Bf[k][j] for k in range(K)), Fraction(0))
+             for j in range(N)] for i in range(M)]
+
+
+def _round_exact_to_f32(q: Fraction) -> np.float32:
+    d = float(q)
+    # the exact sum must be a binary64 number, so this is a single rounding
+    assert Fraction(d) == q
+    return np.float32(d)
+
+
+def test_bruteforce_dyadic_all_shapes_up_to_6():
+    # Inputs j/16, j in [-16, 16]: every sum is exact in binary32 and binary64.
+    rng = np.random.default_rng(7)
+    for M in range(1, 7):
+        for N in range(1, 7):
+            for K in range(1, 7):
+                A = (rng.integers(-16, 17, (M, K)) / 16).astype(np.float32)
+                B = (rng.integers(-16, 17, (K, N)) / 16).astype(np.float32)
+                ex = _exact_product(A, B)
+                expect = np.array([[_round_exact_to_f32(q) for q in r] for r in ex],
+                                  np.float32)
+                assert np.array_equal(oracle.gemm_f32(A, B), expect), (M, N, K)
+
+
+def test_bruteforce_final_rounding_is_round_to_nearest_even():
+    # 12-bit mantissas with exponents in [-6, 6]: products have 24-bit
+    # mantissas, sums of up to 6 of them fit binary64 exactly but need up to
+    # ~50 bits, so the result must be the exact sum rounded once (RNE).
+    rng = np.random.default_rng(8)
+    rounded = 0
+    for M in range(1, 7):
+        for N in range(1, 7):
+            for K in range(1, 7):
+                def draw(shape):
+                    m = rng.integers(2048, 4096, shape)
+                    e = rng.integers(-6, 7, shape)
+                    s = rng.choice([-1, 1], shape)
+                    return (s * m * np.exp2(e - 11)).astype(np.float32)
+                A, B = draw((M, K)), draw((K, N))
+                ex = _exact_product(A, B)
+                expect = np.array([[_round_exact_to_f32(q) for q in r] for r in ex],
+                                  np.float32)
+                got = oracle.gemm_f32(A, B)
+                assert np.array_equal(_bits(got), _bits(expect)), (M, N, K)
+                rounded += sum(Fraction(float(g)) != q
+                               for g, q in zip(got.ravel(), sum(ex, [])))
+    assert rounded > 100   # the rounding step was really exercised
+
+
+def test_numpy_float64_matmul_within_one_ulp():
+    A = RNG.uniform(-1, 1, (67, 129)).astype(np.float32)
+    B = RNG.uniform(-1, 1, (129, 93)).astype(np.float32)
+    ref = (A.astype(np.float64) @ B.astype(np.float64)).astype(np.float32)
+    got = oracle.gemm_f32(A, B)
+    ulp = np.abs(_bits(got).astype(np.int64) - _bits(ref).astype(np.int64))
+    same_sign = np.signbit(got) == np.signbit(ref)
+    assert np.all(ulp[same_sign] <= 1)
+    assert np.all(np.abs(got[~same_sign]) < 1e-30)
+    # and against the (much looser) binary32 product numpy computes itself
+    assert np.max(np.abs(got - A @ B)) < 1e-4
+
+
+def test_small_integer_products_are_exact():
+    A = RNG.integers(-4, 5, (37, 300))
+    B = RNG.integers(-4, 5, (300, 53))
+    got = oracle.gemm_f32(A.astype(np.float32), B.astype(np.float32))
+    assert np.array_equal(got, (A @ B).astype(np.float32))
+
+
+def test_result_does_not_depend_on_thread_count():
+    A = RNG.standard_normal((203, 301)).astype(np.float32)
+    B = RNG.standard_normal((301, 157)).astype(np.float32)
+    one = oracle.gemm_f32(A, B, nthreads=1)
+    many = oracle.gemm_f32(A, B, nthreads=8)
+    assert np.array_equal(_bits(one), _bits(many))
+    assert oracle.threads(3) == 3
+
+
+def test_selected_elements_match_full_product_bit_for_bit():
+    A = RNG.standard_normal((97, 211)).astype(np.float32)
+    B = RNG.standard_normal((211, 83)).astype(np.float32)
+    full = oracle.gemm_f32(A, B)
+    r = RNG.integers(0, 97, 500)
+    c = RNG.integers(0, 83, 500)
+    assert np.array_equal(_bits(oracle.gemm_f32_at(A, B, r, c)), _bits(full[r, c]))
+    A16 = A.astype(np.float16)
+    B16 = B.astype(np.float16)
+    full16 = oracle.gemm_f16(A16, B16)
+    assert np.array_equal(_bits(oracle.gemm_f16_at(A16, B16, r, c)), _bits(full16[r, c]))
+    with pytest.raises(RuntimeError):
+        oracle.gemm_f32_at(A, B, [97], [0])
+
+
+# ------------------------------------------------------------ binary16 path --
+
+def test_f16_product_equals_f32_product_of_the_decoded_values():
+    # binary16 values are exactly binary32 values, so the binary16 routine
+    # must give the same bits as the (pinned) binary32 routine on them.
+    A = RNG.uniform(-1, 1, (61, 250)).astype(np.float16)
+    B = RNG.uniform(-1, 1, (250, 77)).astype(np.float16)
+    a32 = A.astype(np.float32)
+    b32 = B.astype(np.float32)
+    assert np.array_equal(_bits(oracle.gemm_f16(A, B)), _bits(oracle.gemm_f32(a32, b32)))
+
+
+def test_f16_bruteforce_exact():
+    rng = np.random.default_rng(9)
+    for M in range(1, 7):
+        for N in range(1, 7):
+            for K in range(1, 7):
+                A = rng.uniform(-1, 1, (M, K)).astype(np.float16)
+                B = rng.uniform(-1, 1, (K, N)).astype(np.float16)
+                ex = _exact_product(A.astype(np.float64), B.astype(np.float64))
+                expect = np.array([[_round_exact_to_f32(q) for q in r] for r in ex],
+                                  np.float32)
+                assert np.array_equal(_bits(oracle.gemm_f16(A, B)), _bits(expect)), (M, N, K)
+
+
+def test_f16_accepts_raw_bit_patterns_and_small_integers_are_exact():
+    A = RNG.integers(-4, 5, (20, 500))
+    B = RNG.integers(-4, 5, (500, 30))
+    A16 = A.astype(np.float16).view(np.uint16)
+    B16 = B.astype(np.float16).view(np.uint16)
+    assert np.array_equal(oracle.gemm_f16(A16, B16), (A @ B).astype(np.float32))

@@ -1,0 +1,96 @@
+"""The oracle's pins are discriminating: plant a plausible mistake in a copy of
+oracle.c (on the CPU, in a temporary directory), load that copy in place of
+the oracle, and check that at least one pin of ``test_oracle.py`` fails.
+
+Each mutant is a one-token slip of the kind a hand-written loop nest invites:
+a dropped term, a wrong sign, a transposed operand, a wrong index, a start
+value other than zero, binary32 accumulation, or a misdecoded binary16 field.
+"""
+import ctypes
+import shutil
+import subprocess
+
+import pytest
+
+import oracle
+import test_oracle as pins
+
+MUTANTS = {
+    # f32 routine
+    "f32_drops_last_term": ("for (int k = 0; k < K; ++k) {\n                const double a = (double)A",
+                            "for (int k = 0; k < K - 1; ++k) {\n                const double a = (double)A"),
+    "f32_subtracts": ("acc[j] += a * (double)brow[j];", "acc[j] -= a * (double)brow[j];"),
+    "f32_B_transposed": ("acc[j] += a * (double)brow[j];",
+                         "acc[j] += a * (double)B[((size_t)j * K + k) % ((size_t)K * N)];"),
+    "f32_A_transposed": ("const double a = (double)A[(size_t)i * K + k];",
+                         "const double a = (double)A[((size_t)k * M + i) % ((size_t)M * K)];"),
+    "f32_accumulates_into_C": ("for (int j = 0; j < N; ++j)\n                acc[j] = 0.0;\n            for (int k = 0; k < K; ++k) {\n                const double a = (double)A",
+                               "for (int j = 0; j < N; ++j)\n                acc[j] = C[(size_t)i * N + j];\n            for (int k = 0; k < K; ++k) {\n                const double a = (double)A"),
+    "f32_float_accumulator": ("double *acc = (double *)malloc((size_t)N * sizeof(double));\n        if (!acc)\n            failed = 1;\n#pragma omp for schedule(static)\n        for (int i = 0; i < M; ++i) {\n            if (!acc)\n                continue;\n            for (int j = 0; j < N; ++j)\n                acc[j] = 0.0;\n            for (int k = 0; k < K; ++k) {\n                const double a = (double)A",
+                              "float *acc = (float *)malloc((size_t)N * sizeof(float));\n        if (!acc)\n            failed = 1;\n#pragma omp for schedule(static)\n        for (int i = 0; i < M; ++i) {\n            if (!acc)\n                continue;\n            for (int j = 0; j < N; ++j)\n                acc[j] = 0.0;\n            for (int k = 0; k < K; ++k) {\n                const double a = (double)A"),
+    "f32_row_offset_slip": ("C[(size_t)i * N + j] = (float)acc[j];\n        }\n        free(acc);\n    }\n    return failed ? ORACLE_ERR_ALLOC : ORACLE_OK;\n}\n\n/*\n * Full product, binary16",
+                            "C[(size_t)i * N + (j + 1) % N] = (float)acc[j];\n        }\n        free(acc);\n    }\n    return failed ? ORACLE_ERR_ALLOC : ORACLE_OK;\n}\n\n/*\n * Full product, binary16"),
+    # f16 routine and decoder
+    "f16_drops_first_term": ("for (int k = 0; k < K; ++k) {\n                const double a = dec",
+                             "for (int k = 1; k < K; ++k) {\n                const double a = dec"),
+    "f16_B_transposed": ("acc[j] += a * dec[brow[j]];",
+                         "acc[j] += a * dec[B[((size_t)j * K + k) % ((size_t)K * N)]];"),
+    "f16_subnormal_scale": ("v = ldexp((double)frac, -24);", "v = ldexp((double)frac, -25);"),
+    "f16_exponent_bias": ("v = ldexp((double)(1024 + frac), expo - 25);",
+                          "v = ldexp((double)(1024 + frac), expo - 24);"),
+    "f16_hidden_bit": ("v = ldexp((double)(1024 + frac), expo - 25);",
+                       "v = ldexp((double)(frac), expo - 15);"),
+    # selected-element routine
+    "at_wrong_column": ("* (double)B[(size_t)k * N + j];", "* (double)B[(size_t)k * N + i % N];"),
+}
+
+PINS = [
+    lambda: pins.test_f16_decoder_matches_numpy_on_every_bit_pattern(),
+    lambda: pins.test_f16_decoder_spot_values(),
+    lambda: pins.test_identity_right_and_left(7, 13),
+    lambda: pins.test_identity_right_and_left(64, 33),
+    lambda: pins.test_permutation_products(5, 9, 11),
+    lambda: pins.test_rank1_closed_form(6, 17, 9),
+    lambda: pins.test_all_ones_gives_K(),
+    lambda: pins.test_K1_is_the_correctly_rounded_product(),
+    lambda: pins.test_K0_writes_zeros_and_overwrites(),
+    lambda: pins.test_bruteforce_dyadic_all_shapes_up_to_6(),
+    lambda: pins.test_bruteforce_final_rounding_is_round_to_nearest_even(),
+    lambda: pins.test_numpy_float64_matmul_within_one_ulp(),
+    lambda: pins.test_small_integer_products_are_exact(),
+    lambda: pins.test_selected_elements_match_full_product_bit_for_bit(),
+    lambda: pins.test_f16_product_equals_f32_product_of_the_decoded_values(),
+    lambda: pins.test_f16_bruteforce_exact(),
+    lambda: pins.test_f16_accepts_raw_bit_patterns_and_small_integers_are_exact(),
+]
+
+
+def _build_mutant(tmp_path, old, new):
+    src = open(oracle._SRC).read()
+    assert old in src, "mutation anchor not found in oracle.c"
+    mutated = src.replace(old, new, 1)
+    assert mutated != src
+    c = tmp_path / "mutant.c"
+    c.write_text(mutated)
+    so = tmp_path / "libmutant.so"
+    subprocess.run(["gcc", *oracle.CFLAGS, "-w", str(c), "-o", str(so), "-lm"], check=True)
+    return oracle.configure(ctypes.CDLL(str(so)))
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="needs gcc")
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name, tmp_path, monkeypatch):
+    lib = _build_mutant(tmp_path, *MUTANTS[name])
+    monkeypatch.setattr(oracle, "_lib", lib)
+    caught = 0
+    for pin in PINS:
+        try:
+            pin()
+        except (AssertionError, RuntimeError, ValueError):
+            caught += 1
+    assert caught > 0, f"no pin notices mutant {name}"
+
+
+def test_unmutated_oracle_passes_every_pin():
+    for pin in PINS:
+        pin()
