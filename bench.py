@@ -1,0 +1,290 @@
+#!/usr/bin/env python3
+"""Benchmark of the GEMM hot path on one MI355X.
+
+A step is one pass of the hot path over the two headline workloads, with all
+inputs resident in HBM before timing starts:
+  * gemm_f32          M = N = K = 4096, A, B ~ normal(0, 1)      (seed 1005)
+  * gemm_f16_f32acc   M = N = K = 8192, A, B ~ uniform[-1, 1) -> binary16 (seed 1006)
+Throughput is 2MNK per step over the step time, in TFLOP/s.  Each kernel is
+also timed on its own, with HIP events recorded on the stream it runs on,
+and compared with the matrix peak of its input type.
+
+Prints ONE JSON line (rank 0; this benchmark runs on one GPU only).
+
+  python bench.py [--steps K] [--warmup W] [--only f32|f16] [--ladder]
+                  [--no-cpu-baseline] [--copy-calibration]
+
+--ladder additionally times every kernel variant (rung) at 1024^3 and
+4096^3 FP32 and 8192^3 FP16 and adds a "ladder" object to the line.
+--copy-calibration runs a plain device-to-device copy of known size first;
+used only by the hardware-counter runs that calibrate HBM byte counts.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "GEMM TFLOP/s (2MNK/t) at FP32 4096³ and FP16-in 8192³; % of matrix peak"
+PEAK_TFLOPS = {"f32": 157.3, "f16": 2516.6}   # MI355X dense matrix peaks
+HBM_PEAK_GBS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = {
+    "f32": ["dense_gemm_optimisation_row_amd/csrc/mfma_f32.hip",
+            "dense_gemm_optimisation_row_amd/csrc/common.h"],
+    "f16": ["dense_gemm_optimisation_row_amd/csrc/mfma_f16.hip",
+            "dense_gemm_optimisation_row_amd/csrc/common.h"],
+}
+
+
+def kernel_source_hash(kind: str) -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kind: str, launches_per_kernel: int = 1):
+    """HBM bytes per launch from the committed counter summary, or None when
+    it is missing or was taken on a different kernel source."""
+    path = os.path.join(PROFILES, f"traffic_{kind}.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        m = re.match(r"\s*([a-z_0-9]+)\s*[:=]\s*(\S+)", line)
+        if m:
+            vals[m.group(1)] = m.group(2)
+    if vals.get("kernel_source_sha256_16") != kernel_source_hash(kind):
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"]) * launches_per_kernel
+    except (KeyError, ValueError):
+        return None
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--only", choices=["all", "f32", "f16"], default="all")
+    ap.add_argument("--ladder", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target host time of the CPU-baseline sample")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the GEMM path here is single-GPU "
+              "(no collectives); run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import dense_gemm_optimisation_row_amd as dg
+    from dense_gemm_optimisation_row_amd import inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    dg.binding.load()   # fail loudly if the HIP library is missing
+    stream = torch.cuda.current_stream(dev)
+
+    if args.copy_calibration:
+        # plain copy of known size, for scaling HBM byte counters
+        src = torch.empty(256 * 2 ** 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    kinds = ["f32", "f16"] if args.only == "all" else [args.only]
+    wl = {"f32": inputs.WORKLOADS["f32_4096"], "f16": inputs.WORKLOADS["f16_8192"]}
+    dev_in = {}
+    for k in kinds:
+        A, B = inputs.workload_matrices(wl[k])
+        a = torch.from_numpy(A).to(dev)
+        b = torch.from_numpy(B).to(dev)
+        c = torch.empty((wl[k].M, wl[k].N), dtype=torch.float32, device=dev)
+        dev_in[k] = (a, b, c)
+        del A, B
+    torch.cuda.synchronize()
+
+    def call(k):
+        a, b, c = dev_in[k]
+        if k == "f32":
+            dg.gemm_f32(a, b, c, stream=stream)
+        else:
+            dg.gemm_f16_f32acc(a, b, c, stream=stream)
+
+    for _ in range(args.warmup):
+        for k in kinds:
+            call(k)
+    torch.cuda.synchronize()
+
+    # timed region: K whole steps, each kernel bracketed by events on its stream
+    ev = {k: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)] for k in kinds}
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for s in range(args.steps):
+        for k in kinds:
+            ev[k][s][0].record(stream)
+            call(k)
+            ev[k][s][1].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / args.steps
+    flops_step = sum(wl[k].flops for k in kinds)
+    value = flops_step / (ms_per_step * 1e-3) / 1e12
+
+    per = {}
+    for k in kinds:
+        ms = [a.elapsed_time(b) for a, b in ev[k]]
+        avg = float(np.mean(ms))
+        tf = wl[k].flops / (avg * 1e-3) / 1e12
+        a, b, c = dev_in[k]
+        in_bytes = (a.numel() + b.numel()) * a.element_size()
+        per[k] = {
+            "workload": wl[k].name, "M": wl[k].M, "N": wl[k].N, "K": wl[k].K,
+            "kernel": dg.variant_name(dg.plan(k == "f16", wl[k].M, wl[k].N, wl[k].K)["variant"]),
+            "avg_ms": round(avg, 5), "min_ms": round(float(np.min(ms)), 5),
+            "tflops": round(tf, 2), "peak_tflops": PEAK_TFLOPS[k],
+            "frac_of_peak": round(tf / PEAK_TFLOPS[k], 4),
+            "algorithmic_bytes": in_bytes + c.numel() * 4,
+        }
+
+    dom = max(kinds, key=lambda k: per[k]["avg_ms"])
+    roofline = {
+        "kernel": per[dom]["kernel"], "workload": per[dom]["workload"],
+        "bound": "mfma", "achieved": per[dom]["tflops"], "peak": PEAK_TFLOPS[dom],
+        "unit": "TFLOP/s", "frac": per[dom]["frac_of_peak"],
+        "traffic": read_traffic(dom),
+        "algorithmic_flops": wl[dom].flops, "algorithmic_bytes": per[dom]["algorithmic_bytes"],
+    }
+    others = [
+        {"kernel": per[k]["kernel"], "workload": per[k]["workload"], "bound": "mfma",
+         "achieved": per[k]["tflops"], "peak": PEAK_TFLOPS[k], "unit": "TFLOP/s",
+         "frac": per[k]["frac_of_peak"], "traffic": read_traffic(k)}
+        for k in kinds if k != dom]
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "+".join({"f32": "f32", "f16": "f16-in/f32-acc"}[k] for k in kinds),
+        "data": "synthetic (seeded numpy PCG64: normal(0,1) f32 4096^3; uniform[-1,1) "
+                "rounded to f16, 8192^3)",
+        "config": {"workload": " + ".join(
+            {"f32": "FP32 GEMM 4096x4096x4096 row-major",
+             "f16": "FP16-in/FP32-acc GEMM 8192x8192x8192 row-major"}[k] for k in kinds),
+            "per_step": [wl[k].name for k in kinds]},
+        "per_workload": per,
+        "roofline": roofline,
+        "roofline_other": others,
+        "device": torch.cuda.get_device_name(dev),
+    }
+
+    if args.ladder:
+        out["ladder"] = ladder(dg, inputs, torch, dev, stream)
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(kinds, wl, args.cpu_seconds)
+
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def _time_calls(fn, torch, stream, reps):
+    fn()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def ladder(dg, inputs, torch, dev, stream):
+    """Time every rung on the workloads (same inputs as the step)."""
+    res = []
+    for name, variants in (("f32_1024", dg.F32_VARIANTS), ("f32_4096", dg.F32_VARIANTS),
+                           ("f16_8192", dg.F16_VARIANTS)):
+        w = inputs.WORKLOADS[name]
+        A, B = inputs.workload_matrices(w)
+        a, b = torch.from_numpy(A).to(dev), torch.from_numpy(B).to(dev)
+        c = torch.empty((w.M, w.N), dtype=torch.float32, device=dev)
+        half = w.dtype == "f16"
+        for v in variants:
+            f = dg.gemm_f16_f32acc_variant if half else dg.gemm_f32_variant
+            est = _time_calls(lambda: f(v, a, b, c, stream), torch, stream, 1)
+            reps = max(1, min(50, int(200.0 / max(est, 1e-3))))
+            ms = _time_calls(lambda: f(v, a, b, c, stream), torch, stream, reps)
+            tf = w.flops / (ms * 1e-3) / 1e12
+            res.append({"workload": name, "variant": dg.variant_name(v), "ms": round(ms, 4),
+                        "tflops": round(tf, 3),
+                        "frac_of_peak": round(tf / PEAK_TFLOPS["f16" if half else "f32"], 4)})
+            print(f"# ladder {name} {dg.variant_name(v)}: {ms:.3f} ms {tf:.2f} TFLOP/s",
+                  file=sys.stderr, flush=True)
+        del a, b, c
+    return res
+
+
+def cpu_baseline(kinds, wl, seconds):
+    """The oracle as it stands, on a bounded row sample of the same inputs."""
+    import numpy as np
+
+    import oracle
+    from dense_gemm_optimisation_row_amd import inputs
+
+    threads = oracle.threads(0)
+    rates = {}
+    samples = []
+    budget = seconds / len(kinds)
+    for k in kinds:
+        w = wl[k]
+        A, B = inputs.workload_matrices(w)
+        fn = oracle.gemm_f16 if k == "f16" else oracle.gemm_f32
+        rows = max(threads, 8)
+        t0 = time.perf_counter()
+        fn(A[:rows], B)
+        dt = time.perf_counter() - t0
+        rows2 = int(min(w.M, max(rows, rows * budget / max(dt, 1e-3))))
+        t0 = time.perf_counter()
+        fn(A[:rows2], B)
+        dt = time.perf_counter() - t0
+        rates[k] = 2.0 * rows2 * w.N * w.K / dt        # flop/s
+        samples.append(f"{rows2} of {w.M} rows of {w.name} ({dt:.1f} s)")
+        del A, B
+    step_flops = sum(wl[k].flops for k in kinds)
+    step_seconds = sum(wl[k].flops / rates[k] for k in kinds)
+    return {"value": round(step_flops / step_seconds / 1e12, 6), "unit": "TFLOP/s",
+            "cores": threads, "kind": "oracle",
+            "sample": "; ".join(samples) + " (FP64-accumulating C loop nest, OpenMP over rows)",
+            "per_workload_gflops": {wl[k].name: round(rates[k] / 1e9, 3) for k in kinds}}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

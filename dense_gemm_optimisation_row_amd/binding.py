@@ -1,0 +1,190 @@
+"""ctypes binding of the C ABI in ``include/gemm.h`` (argument marshalling only).
+
+Two layers:
+
+* ``raw_*`` functions pass integers (device addresses, sizes, a stream
+  handle) straight to the library and return its status code;
+* ``gemm_f32`` / ``gemm_f16_f32acc`` (and ``*_variant``) take torch tensors
+  that already live on the GPU, check shape / dtype / contiguity, call the
+  library on the tensors' current stream and raise ``GemmError`` on a
+  non-zero status.
+
+All arithmetic happens in the HIP kernels.  There is no fallback: if the
+library is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libdgor_gemm.so")
+
+# Mirrors gemm_status / gemm_variant of include/gemm.h.
+GEMM_OK = 0
+GEMM_ERR_INVALID_DIM = -1
+GEMM_ERR_NULL_PTR = -2
+GEMM_ERR_LAUNCH = -3
+GEMM_ERR_UNSUPPORTED_DEVICE = -4
+GEMM_ERR_INVALID_VARIANT = -5
+GEMM_ERR_RUNTIME = -6
+
+AUTO = -1
+R0_NAIVE, R1_LDS_TILED, R2_VECTOR_LOADS, R3_LDS_PADDED = 0, 1, 2, 3
+R4_DOUBLE_BUFFER, R5_REGISTER_BLOCKED, R6_MFMA_F32, R7_MFMA_F16 = 4, 5, 6, 7
+F32_VARIANTS = (0, 1, 2, 3, 4, 5, 6)
+F16_VARIANTS = (0, 7)
+
+EXPORTS = ("gemm_f32", "gemm_f16_f32acc", "gemm_f32_variant", "gemm_f16_f32acc_variant",
+           "gemm_f32_plan", "gemm_f16_f32acc_plan", "gemm_status_string", "gemm_variant_name")
+
+
+class GemmError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int) for n in (
+        "variant", "launches", "tile_m", "tile_n", "tile_k", "threads", "grid_x", "grid_y",
+        "k_stages", "lds_stages", "lds_bytes", "tile_bytes", "outputs_per_thread",
+        "vector_a", "vector_b", "vector_c")]
+
+    def as_dict(self) -> dict:
+        return {n: getattr(self, n) for n, _ in self._fields_}
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load the library once (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(path):
+            raise RuntimeError(
+                f"HIP library {path} is missing: build it with "
+                "`python -m dense_gemm_optimisation_row_amd.build`")
+        lib = ctypes.CDLL(path)
+        i, p = ctypes.c_int, ctypes.c_void_p
+        for name in ("gemm_f32", "gemm_f16_f32acc"):
+            f = getattr(lib, name)
+            f.argtypes = [i, i, i, p, p, p, p]
+            f.restype = i
+        for name in ("gemm_f32_variant", "gemm_f16_f32acc_variant"):
+            f = getattr(lib, name)
+            f.argtypes = [i, i, i, i, p, p, p, p]
+            f.restype = i
+        for name in ("gemm_f32_plan", "gemm_f16_f32acc_plan"):
+            f = getattr(lib, name)
+            f.argtypes = [i, i, i, i, p, p, p, ctypes.POINTER(Plan)]
+            f.restype = i
+        lib.gemm_status_string.argtypes = [i]
+        lib.gemm_status_string.restype = ctypes.c_char_p
+        lib.gemm_variant_name.argtypes = [i]
+        lib.gemm_variant_name.restype = ctypes.c_char_p
+        _lib = lib
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return load().gemm_status_string(int(status)).decode()
+
+
+def variant_name(variant: int) -> str:
+    return load().gemm_variant_name(int(variant)).decode()
+
+
+# ------------------------------------------------------------- raw layer --
+
+def raw_gemm(half: bool, variant: int | None, M: int, N: int, K: int,
+             A: int | None, B: int | None, C: int | None, stream: int | None) -> int:
+    """Call the library with plain integers; returns the status code."""
+    lib = load()
+    if variant is None:
+        f = lib.gemm_f16_f32acc if half else lib.gemm_f32
+        return int(f(M, N, K, A, B, C, stream))
+    f = lib.gemm_f16_f32acc_variant if half else lib.gemm_f32_variant
+    return int(f(variant, M, N, K, A, B, C, stream))
+
+
+def plan(half: bool, M: int, N: int, K: int, variant: int = AUTO,
+         A: int = 0, B: int = 0, C: int = 0) -> dict:
+    """Launch plan for these arguments (host arithmetic only; no GPU needed).
+
+    Addresses matter only through their 16-byte alignment; 0 counts as aligned.
+    """
+    lib = load()
+    out = Plan()
+    f = lib.gemm_f16_f32acc_plan if half else lib.gemm_f32_plan
+    rc = f(variant, M, N, K, A or None, B or None, C or None, ctypes.byref(out))
+    if rc != GEMM_OK:
+        raise GemmError(rc, "plan")
+    return out.as_dict()
+
+
+# ----------------------------------------------------------- torch layer --
+
+def _check(A, B, C, in_dtype):
+    import torch
+    if A.dim() != 2 or B.dim() != 2 or A.shape[1] != B.shape[0]:
+        raise ValueError(f"shapes {tuple(A.shape)} x {tuple(B.shape)} do not chain")
+    if A.dtype != in_dtype or B.dtype != in_dtype:
+        raise TypeError(f"A and B must be {in_dtype}")
+    if not (A.is_cuda and B.is_cuda):
+        raise ValueError("A and B must be GPU tensors")
+    if not (A.is_contiguous() and B.is_contiguous()):
+        raise ValueError("A and B must be contiguous (row-major)")
+    M, K = A.shape
+    N = B.shape[1]
+    if C is None:
+        C = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    elif (tuple(C.shape) != (M, N) or C.dtype != torch.float32 or not C.is_contiguous()
+          or C.device != A.device):
+        raise ValueError("C must be a contiguous float32 M x N tensor on A's device")
+    if B.device != A.device:
+        raise ValueError("A and B must be on the same device")
+    return M, N, K, C
+
+
+def _stream_handle(device, stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ptr(t):
+    return t.data_ptr() if t.numel() else None
+
+
+def _call(half, variant, A, B, C, stream):
+    import torch
+    M, N, K, C = _check(A, B, C, torch.float16 if half else torch.float32)
+    with torch.cuda.device(A.device):
+        rc = raw_gemm(half, variant, M, N, K, _ptr(A), _ptr(B), _ptr(C),
+                      _stream_handle(A.device, stream))
+    if rc != GEMM_OK:
+        raise GemmError(rc, "gemm_f16_f32acc" if half else "gemm_f32")
+    return C
+
+
+def gemm_f32(A, B, C=None, stream=None):
+    """C = A x B for float32 GPU tensors; returns C (allocated if not given)."""
+    return _call(False, None, A, B, C, stream)
+
+
+def gemm_f16_f32acc(A, B, C=None, stream=None):
+    """C = A x B for float16 GPU tensors with FP32 accumulation and output."""
+    return _call(True, None, A, B, C, stream)
+
+
+def gemm_f32_variant(variant, A, B, C=None, stream=None):
+    """``gemm_f32`` with the kernel variant (rung) forced."""
+    return _call(False, int(variant), A, B, C, stream)
+
+
+def gemm_f16_f32acc_variant(variant, A, B, C=None, stream=None):
+    """``gemm_f16_f32acc`` with the kernel variant (rung) forced."""
+    return _call(True, int(variant), A, B, C, stream)

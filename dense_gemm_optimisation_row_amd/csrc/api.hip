@@ -1,0 +1,310 @@
+// C ABI of the library (declared in include/gemm.h): argument validation,
+// launch planning and dispatch.  Host code only; the kernels live in
+// ladder.hip, mfma_f32.hip and mfma_f16.hip.
+//
+// Planning is pure arithmetic on the arguments (no HIP call), so the plan
+// entry points work on a machine without a GPU.  The grid follows the
+// pages' ceil-div rule ("Lesson 8: how a GPU does matrix multiply", section 3):
+// ceil(N / tile_n) workgroups along N and ceil(M / tile_m) along M.
+#include <atomic>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace {
+
+using dgor::MfmaConfig;
+
+constexpr int kDevCache = 64;
+std::atomic<int> g_dev_state[kDevCache];  // 0 unknown, 1 gfx950, 2 other
+
+int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_device()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return GEMM_ERR_RUNTIME;
+    if (dev >= 0 && dev < kDevCache) {
+        const int st = g_dev_state[dev].load(std::memory_order_relaxed);
+        if (st == 1)
+            return GEMM_OK;
+        if (st == 2)
+            return GEMM_ERR_UNSUPPORTED_DEVICE;
+    }
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+        return GEMM_ERR_RUNTIME;
+    const char *arch = prop.gcnArchName;
+    const bool ok = arch[0] == 'g' && arch[1] == 'f' && arch[2] == 'x' && arch[3] == '9' &&
+                    arch[4] == '5' && arch[5] == '0' && (arch[6] == 0 || arch[6] == ':');
+    if (dev >= 0 && dev < kDevCache)
+        g_dev_state[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+    return ok ? GEMM_OK : GEMM_ERR_UNSUPPORTED_DEVICE;
+}
+
+void clear(gemm_plan *p)
+{
+    *p = gemm_plan{};
+}
+
+// Fill the tile-independent fields of a plan.
+void finish(gemm_plan *p, int M, int N, int K)
+{
+    p->launches = 1;
+    p->grid_x = ceil_div(N, p->tile_n);
+    p->grid_y = ceil_div(M, p->tile_m);
+    p->k_stages = p->tile_k ? ceil_div(K, p->tile_k) : 0;
+}
+
+// Which matrix-core configuration a shape gets: the largest tile that still
+// yields at least two workgroups per compute unit (256 CUs), else the tile
+// that yields the most workgroups; N <= 64 takes the narrow FP32 tile.
+template <size_t NC>
+int pick_config(const MfmaConfig (&cfg)[NC], int M, int N, bool narrow_ok)
+{
+    if (narrow_ok && N <= 64)
+        return (int)NC - 1;
+    const int full = narrow_ok ? (int)NC - 1 : (int)NC;
+    for (int i = 0; i < full; ++i) {
+        const long tiles = (long)ceil_div(M, cfg[i].bm) * ceil_div(N, cfg[i].bn);
+        if (tiles >= 512)
+            return i;
+    }
+    return full - 1;
+}
+
+int plan_f32(int variant, int M, int N, int K, const void *A, const void *B, const void *C,
+             gemm_plan *p)
+{
+    if (!p)
+        return GEMM_ERR_NULL_PTR;
+    if (M < 0 || N < 0 || K < 0)
+        return GEMM_ERR_INVALID_DIM;
+    if (variant == GEMM_VARIANT_AUTO)
+        variant = GEMM_R6_MFMA_F32;
+    if (variant < GEMM_R0_NAIVE || variant > GEMM_R6_MFMA_F32)
+        return GEMM_ERR_INVALID_VARIANT;
+    clear(p);
+    p->variant = variant;
+    p->vector_a = (K % 4 == 0) && aligned16(A);
+    p->vector_b = (N % 4 == 0) && aligned16(B);
+    p->vector_c = (N % 4 == 0) && aligned16(C);
+    if (M == 0 || N == 0)
+        return GEMM_OK;
+    if (K == 0) {  // empty sum: one zero-fill launch
+        p->launches = 1;
+        p->threads = 256;
+        p->vector_a = p->vector_b = p->vector_c = 0;
+        return GEMM_OK;
+    }
+    switch (variant) {
+    case GEMM_R0_NAIVE:
+        p->tile_m = p->tile_n = 16;
+        p->tile_k = 0;
+        p->threads = 256;
+        p->outputs_per_thread = 1;
+        p->vector_a = p->vector_b = p->vector_c = 0;
+        break;
+    case GEMM_R1_LDS_TILED:
+        p->tile_m = p->tile_n = p->tile_k = 16;
+        p->threads = 256;
+        p->lds_stages = 1;
+        p->lds_bytes = 2 * 16 * 16 * 4;
+        p->tile_bytes = 2 * 16 * 16 * 4;
+        p->outputs_per_thread = 1;
+        p->vector_a = p->vector_b = p->vector_c = 0;
+        break;
+    case GEMM_R2_VECTOR_LOADS:
+    case GEMM_R3_LDS_PADDED:
+    case GEMM_R4_DOUBLE_BUFFER: {
+        const bool pad = variant != GEMM_R2_VECTOR_LOADS;
+        p->tile_m = p->tile_n = 16;
+        p->tile_k = 64;
+        p->threads = 256;
+        p->lds_stages = variant == GEMM_R4_DOUBLE_BUFFER ? 2 : 1;
+        const int pa = pad ? dgor::kLadderPadA : 0, pb = pad ? dgor::kLadderPadB : 0;
+        p->lds_bytes = p->lds_stages * (16 * (64 + pa) + 64 * (16 + pb)) * 4;
+        p->tile_bytes = (16 * 64 + 64 * 16) * 4;
+        p->outputs_per_thread = 1;
+        p->vector_c = 0;
+        break;
+    }
+    case GEMM_R5_REGISTER_BLOCKED:
+        p->tile_m = p->tile_n = 128;
+        p->tile_k = 8;
+        p->threads = 256;
+        p->lds_stages = 2;
+        p->lds_bytes = 2 * (8 * (128 + dgor::kRegblockPad) + 8 * 128) * 4;
+        p->tile_bytes = (128 * 8 + 8 * 128) * 4;
+        p->outputs_per_thread = 64;
+        break;
+    case GEMM_R6_MFMA_F32: {
+        const MfmaConfig &c = dgor::kF32Configs[pick_config(dgor::kF32Configs, M, N, true)];
+        p->tile_m = c.bm;
+        p->tile_n = c.bn;
+        p->tile_k = c.bk;
+        p->threads = 64 * c.waves_m * c.waves_n;
+        p->lds_stages = 2;
+        p->lds_bytes = dgor::mfma_f32_lds_bytes(c);
+        p->tile_bytes = (c.bm * c.bk + c.bk * c.bn) * 4;
+        p->outputs_per_thread = c.bm * c.bn / p->threads;
+        p->vector_c = 0;
+        break;
+    }
+    }
+    finish(p, M, N, K);
+    return GEMM_OK;
+}
+
+int plan_f16(int variant, int M, int N, int K, const void *A, const void *B, const void *C,
+             gemm_plan *p)
+{
+    if (!p)
+        return GEMM_ERR_NULL_PTR;
+    if (M < 0 || N < 0 || K < 0)
+        return GEMM_ERR_INVALID_DIM;
+    if (variant == GEMM_VARIANT_AUTO)
+        variant = GEMM_R7_MFMA_F16;
+    if (variant != GEMM_R0_NAIVE && variant != GEMM_R7_MFMA_F16)
+        return GEMM_ERR_INVALID_VARIANT;
+    clear(p);
+    p->variant = variant;
+    p->vector_a = (K % 8 == 0) && aligned16(A);
+    p->vector_b = (N % 8 == 0) && aligned16(B);
+    p->vector_c = 0;
+    if (M == 0 || N == 0)
+        return GEMM_OK;
+    if (K == 0) {
+        p->launches = 1;
+        p->threads = 256;
+        p->vector_a = p->vector_b = 0;
+        return GEMM_OK;
+    }
+    if (variant == GEMM_R0_NAIVE) {
+        p->tile_m = p->tile_n = 16;
+        p->threads = 256;
+        p->outputs_per_thread = 1;
+        p->vector_a = p->vector_b = 0;
+    } else {
+        const MfmaConfig &c = dgor::kF16Configs[pick_config(dgor::kF16Configs, M, N, false)];
+        p->tile_m = c.bm;
+        p->tile_n = c.bn;
+        p->tile_k = c.bk;
+        p->threads = 64 * c.waves_m * c.waves_n;
+        p->lds_stages = 2;
+        p->lds_bytes = dgor::mfma_f16_lds_bytes(c);
+        p->tile_bytes = (c.bm * c.bk + c.bk * c.bn) * 2;
+        p->outputs_per_thread = c.bm * c.bn / p->threads;
+    }
+    finish(p, M, N, K);
+    return GEMM_OK;
+}
+
+bool null_with_extent(const void *A, const void *B, const void *C, int M, int N, int K)
+{
+    const bool a_needed = (long)M * K > 0, b_needed = (long)K * N > 0, c_needed = (long)M * N > 0;
+    return (a_needed && !A) || (b_needed && !B) || (c_needed && !C);
+}
+
+int run(bool half, int variant, int M, int N, int K, const void *A, const void *B, float *C,
+        void *stream)
+{
+    gemm_plan plan;
+    const int rc = half ? plan_f16(variant, M, N, K, A, B, C, &plan)
+                        : plan_f32(variant, M, N, K, A, B, C, &plan);
+    if (rc != GEMM_OK)
+        return rc;
+    if (null_with_extent(A, B, C, M, N, K))
+        return GEMM_ERR_NULL_PTR;
+    if (plan.launches == 0)
+        return GEMM_OK;
+    const int dev = check_device();
+    if (dev != GEMM_OK)
+        return dev;
+    dgor::Problem p{M, N, K, A, B, C, plan.vector_a != 0, plan.vector_b != 0, plan.vector_c != 0};
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t err;
+    if (K == 0)
+        err = dgor::launch_zero_fill(p, s);
+    else if (half)
+        err = plan.variant == GEMM_R7_MFMA_F16 ? dgor::launch_mfma_f16(p, plan, s)
+                                               : dgor::launch_naive_f16(p, plan, s);
+    else
+        err = plan.variant == GEMM_R6_MFMA_F32 ? dgor::launch_mfma_f32(p, plan, s)
+                                               : dgor::launch_ladder_f32(p, plan, s);
+    return err == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gemm_f32(int M, int N, int K, const float *A, const float *B, float *C, void *stream)
+{
+    return run(false, GEMM_VARIANT_AUTO, M, N, K, A, B, C, stream);
+}
+
+int gemm_f16_f32acc(int M, int N, int K, const uint16_t *A, const uint16_t *B, float *C,
+                    void *stream)
+{
+    return run(true, GEMM_VARIANT_AUTO, M, N, K, A, B, C, stream);
+}
+
+int gemm_f32_variant(int variant, int M, int N, int K, const float *A, const float *B,
+                     float *C, void *stream)
+{
+    return run(false, variant, M, N, K, A, B, C, stream);
+}
+
+int gemm_f16_f32acc_variant(int variant, int M, int N, int K, const uint16_t *A,
+                            const uint16_t *B, float *C, void *stream)
+{
+    return run(true, variant, M, N, K, A, B, C, stream);
+}
+
+int gemm_f32_plan(int variant, int M, int N, int K, const float *A, const float *B,
+                  const float *C, gemm_plan *plan)
+{
+    return plan_f32(variant, M, N, K, A, B, C, plan);
+}
+
+int gemm_f16_f32acc_plan(int variant, int M, int N, int K, const uint16_t *A,
+                         const uint16_t *B, const float *C, gemm_plan *plan)
+{
+    return plan_f16(variant, M, N, K, A, B, C, plan);
+}
+
+const char *gemm_status_string(int status)
+{
+    switch (status) {
+    case GEMM_OK: return "ok";
+    case GEMM_ERR_INVALID_DIM: return "invalid dimension (M, N or K negative)";
+    case GEMM_ERR_NULL_PTR: return "null pointer for an operand with nonzero extent";
+    case GEMM_ERR_LAUNCH: return "kernel launch failed";
+    case GEMM_ERR_UNSUPPORTED_DEVICE: return "current device is not gfx950";
+    case GEMM_ERR_INVALID_VARIANT: return "variant not available for this entry point";
+    case GEMM_ERR_RUNTIME: return "HIP runtime query failed";
+    default: return "unknown status";
+    }
+}
+
+const char *gemm_variant_name(int variant)
+{
+    switch (variant) {
+    case GEMM_VARIANT_AUTO: return "auto";
+    case GEMM_R0_NAIVE: return "R0 naive";
+    case GEMM_R1_LDS_TILED: return "R1 LDS 16x16 tiles";
+    case GEMM_R2_VECTOR_LOADS: return "R2 128-bit loads";
+    case GEMM_R3_LDS_PADDED: return "R3 padded LDS";
+    case GEMM_R4_DOUBLE_BUFFER: return "R4 double-buffered LDS";
+    case GEMM_R5_REGISTER_BLOCKED: return "R5 register-blocked 8x8";
+    case GEMM_R6_MFMA_F32: return "R6 FP32 MFMA";
+    case GEMM_R7_MFMA_F16: return "R7 FP16 MFMA, FP32 accumulate";
+    default: return "unknown variant";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,95 @@
+// Internal declarations shared by the host dispatcher and the kernel files.
+// Not part of the public ABI (include/gemm.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gemm.h"
+
+namespace dgor {
+
+// One GEMM call after validation: row-major A (M x K), B (K x N), C (M x N).
+struct Problem {
+    int M, N, K;
+    const void *A;  // float or binary16 bits
+    const void *B;
+    float *C;
+    bool vec_a;     // A rows start 16-byte aligned and hold whole 128-bit vectors
+    bool vec_b;     // same for B
+    bool vec_c;     // same for C (FP32, 4 per vector)
+};
+
+// Launchers.  Each enqueues exactly the kernel `plan` describes on `stream`
+// and returns the launch status.  Shapes were validated by the caller.
+hipError_t launch_zero_fill(const Problem &p, hipStream_t stream);
+hipError_t launch_ladder_f32(const Problem &p, const gemm_plan &plan, hipStream_t stream);
+hipError_t launch_naive_f16(const Problem &p, const gemm_plan &plan, hipStream_t stream);
+hipError_t launch_mfma_f32(const Problem &p, const gemm_plan &plan, hipStream_t stream);
+hipError_t launch_mfma_f16(const Problem &p, const gemm_plan &plan, hipStream_t stream);
+
+// LDS padding of the ladder rungs, in floats per row.  R3 and R4 pad each
+// A row of their 16 x 64 tile by one float, moving consecutive rows to
+// consecutive banks (the pages' one extra column); R5 pads each k row of its
+// transposed 8 x 128 A tile by 8 floats.
+constexpr int kLadderPadA = 1;
+constexpr int kLadderPadB = 0;
+constexpr int kRegblockPad = 8;
+
+// Tile shapes of the matrix-core rungs.  The dispatcher picks one per call
+// and the launcher recognises it by (plan.tile_m, plan.tile_n).
+struct MfmaConfig { int bm, bn, bk, waves_m, waves_n; };
+
+// FP32 (R6): LDS rows of A padded by 4 floats, rows of B by 8 floats.
+constexpr int kF32PadA = 4;
+constexpr int kF32PadB = 8;
+constexpr MfmaConfig kF32Configs[] = {
+    {128, 128, 16, 2, 2},   // large problems
+    {64, 64, 16, 2, 2},     // problems too small to fill the chip with 128^2 tiles
+    {32, 64, 16, 1, 2},     // N <= 64
+};
+constexpr int mfma_f32_lds_bytes(const MfmaConfig &c)
+{
+    return 2 * (c.bm * (c.bk + kF32PadA) + c.bk * (c.bn + kF32PadB)) * 4;
+}
+
+// FP16 (R7): LDS rows of A padded by 8 halves; k-pair rows of B by 8 words.
+constexpr int kF16PadA = 8;
+constexpr int kF16PadB = 8;
+constexpr MfmaConfig kF16Configs[] = {
+    {256, 256, 32, 2, 2},   // large problems: 128 x 128 per wavefront
+    {128, 128, 32, 2, 2},
+    {64, 64, 32, 1, 2},
+};
+constexpr int mfma_f16_lds_bytes(const MfmaConfig &c)
+{
+    return 2 * (c.bm * (c.bk + kF16PadA) * 2 + (c.bk / 2) * (c.bn + kF16PadB) * 4);
+}
+
+}  // namespace dgor
+
+// ---------------------------------------------------------------------------
+// Device helpers
+// ---------------------------------------------------------------------------
+
+// Workgroup -> output tile, aware of the chip's 8 XCDs.  Consecutive
+// workgroup ids are dealt round-robin to the XCDs, each with its own L2, so
+// id b runs on XCD b % 8.  The ids of one XCD are first renumbered into one
+// contiguous range of logical tiles; logical tiles are then walked in groups
+// of `group_m` tile rows, column by column inside a group, so the tiles that
+// one XCD runs at the same time share a few A row-panels and B column-panels.
+__host__ __device__ __forceinline__ void dgor_tile_of_block(int bid, int tiles_m, int tiles_n,
+                                                   int group_m, int &tm, int &tn)
+{
+    const int nb = tiles_m * tiles_n;
+    const int per = nb >> 3, rem = nb & 7;
+    const int xcd = bid & 7, local = bid >> 3;
+    const int logical = xcd * per + (xcd < rem ? xcd : rem) + local;
+    const int span = group_m * tiles_n;
+    const int group = logical / span;
+    const int first_m = group * group_m;
+    const int gm = min(tiles_m - first_m, group_m);
+    const int in_group = logical - group * span;
+    tm = first_m + in_group % gm;
+    tn = in_group / gm;
+}

@@ -1,0 +1,146 @@
+/*
+ * gemm.h -- C ABI of the MI355X (gfx950) dense row-major GEMM library.
+ *
+ * Operation (all entry points): C = A x B, where
+ *   A is M x K, B is K x N, C is M x N, each row-major with packed leading
+ *   dimensions:  A[i*K + k],  B[k*N + j],  C[i*N + j];
+ *   C[i][j] = sum over k in [0, K) of A[i][k] * B[k][j], accumulated in FP32.
+ * Definition: "Lesson 8: how a GPU does matrix multiply", section 1 (element
+ * formula) and section 2 (row-major index expressions); "SGEMM optimisation
+ * journey", Level 1 (argument order M, N, K, A, B, C); "4. GEMM optimisation",
+ * section 4.1 (shapes; C written once, not accumulated into).
+ *
+ * Conventions shared by every call:
+ *   - A, B, C are DEVICE pointers owned by the caller.  The library allocates
+ *     and frees nothing, keeps no per-call state, and never copies to the host.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
+ *     and the call returns without waiting: the caller synchronises.
+ *   - C is overwritten.  C must not overlap A or B.  Inputs must be finite.
+ *   - Pointers need only natural element alignment.  16-byte alignment of a
+ *     base pointer, with K (for A) or N (for B, C) a multiple of the vector
+ *     width, is detected and used for 128-bit accesses; it is never required.
+ *   - Dimensions are `int`; every offset is computed in 64 bits.
+ *   - Edge cases: M, N or K negative -> GEMM_ERR_INVALID_DIM.  M == 0 or
+ *     N == 0 -> GEMM_OK with nothing launched or written.  K == 0 -> C is set
+ *     to 0.0f (an empty sum).  A NULL pointer whose extent is nonzero ->
+ *     GEMM_ERR_NULL_PTR (extents: A M*K, B K*N, C M*N; checked before
+ *     the M == 0 / N == 0 early return).  Nothing is launched when a status
+ *     other than GEMM_OK is returned, except GEMM_ERR_LAUNCH.
+ *   - Errors are returned, never printed or thrown.  A current device that is
+ *     not gfx950 -> GEMM_ERR_UNSUPPORTED_DEVICE.  A failed launch ->
+ *     GEMM_ERR_LAUNCH.  A failed HIP runtime query -> GEMM_ERR_RUNTIME.
+ *   - Calls are thread-safe; concurrent calls on different streams are fine.
+ */
+#ifndef DGOR_GEMM_H
+#define DGOR_GEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GEMM_OK = 0,
+    GEMM_ERR_INVALID_DIM = -1,
+    GEMM_ERR_NULL_PTR = -2,
+    GEMM_ERR_LAUNCH = -3,
+    GEMM_ERR_UNSUPPORTED_DEVICE = -4,
+    GEMM_ERR_INVALID_VARIANT = -5,
+    GEMM_ERR_RUNTIME = -6
+} gemm_status;
+
+/*
+ * Kernel variants ("rungs"), in the order the pages build them up:
+ *   R0 one thread per output element            ("4. GEMM optimisation" 4.1;
+ *                                                 Lesson 8 section 4)
+ *   R1 16x16 LDS tiles, masked loads, two barriers (Lesson 8 section 10,
+ *                                                 section 26 for the masking)
+ *   R2 R1 with 128-bit global loads             ("4. GEMM optimisation" 4.3)
+ *   R3 R2 with padded LDS rows                  (Lesson 8 section 27;
+ *                                                 SGEMM journey Level 3)
+ *   R4 R3 with two LDS stages, one barrier/step (Lesson 8 section 24;
+ *                                                 SGEMM journey Level 4)
+ *   R5 register-blocked 8x8 outputs per thread  (Lesson 8 section 18;
+ *                                                 SGEMM journey Level 5)
+ *   R6 FP32 matrix-core (MFMA) tiles             (Lesson 8 section 21)
+ *   R7 FP16 matrix-core (MFMA) tiles, FP32 acc.  (SGEMM journey Level 6)
+ * GEMM_VARIANT_AUTO lets the library choose from the shape and alignment.
+ */
+typedef enum {
+    GEMM_VARIANT_AUTO = -1,
+    GEMM_R0_NAIVE = 0,
+    GEMM_R1_LDS_TILED = 1,
+    GEMM_R2_VECTOR_LOADS = 2,
+    GEMM_R3_LDS_PADDED = 3,
+    GEMM_R4_DOUBLE_BUFFER = 4,
+    GEMM_R5_REGISTER_BLOCKED = 5,
+    GEMM_R6_MFMA_F32 = 6,
+    GEMM_R7_MFMA_F16 = 7,
+    GEMM_VARIANT_COUNT = 8
+} gemm_variant;
+
+/* FP32 inputs, FP32 accumulation and output.  Chooses the fastest variant
+ * for the shape (R6 in practice).  See the conventions above. */
+int gemm_f32(int M, int N, int K, const float *A, const float *B, float *C,
+             void *stream);
+
+/* IEEE binary16 inputs (raw 16-bit patterns), exact products, FP32
+ * accumulation and FP32 output ("SGEMM optimisation journey", Level 6: half
+ * operands with a float accumulator).  Chooses R7 in practice. */
+int gemm_f16_f32acc(int M, int N, int K, const uint16_t *A, const uint16_t *B,
+                    float *C, void *stream);
+
+/* Same operations with the variant forced (GEMM_VARIANT_AUTO allowed), for
+ * benchmarking and testing every rung.  gemm_f32_variant accepts R0..R6;
+ * gemm_f16_f32acc_variant accepts R0 and R7.  Any other value ->
+ * GEMM_ERR_INVALID_VARIANT.  Same semantics and errors otherwise. */
+int gemm_f32_variant(int variant, int M, int N, int K, const float *A,
+                     const float *B, float *C, void *stream);
+int gemm_f16_f32acc_variant(int variant, int M, int N, int K,
+                            const uint16_t *A, const uint16_t *B, float *C,
+                            void *stream);
+
+/*
+ * Launch plan: what a call with these arguments would launch.  Pure host
+ * arithmetic (no device is touched), so it can be queried without a GPU.
+ * Pointers are used only for their alignment; they are never dereferenced.
+ * `variant` may be GEMM_VARIANT_AUTO.  Fills *plan and returns GEMM_OK, or
+ * returns GEMM_ERR_INVALID_DIM / GEMM_ERR_INVALID_VARIANT /
+ * GEMM_ERR_NULL_PTR (plan == NULL).  For M == 0 or N == 0 the plan has
+ * launches == 0; for K == 0 it describes the zero-fill launch.
+ */
+typedef struct {
+    int variant;        /* rung that runs (a gemm_variant value) */
+    int launches;       /* kernels enqueued: 0 or 1 */
+    int tile_m;         /* output rows per workgroup */
+    int tile_n;         /* output columns per workgroup */
+    int tile_k;         /* k extent of one LDS stage (0 for R0 / zero-fill) */
+    int threads;        /* threads per workgroup */
+    int grid_x;         /* workgroups along N */
+    int grid_y;         /* workgroups along M */
+    int k_stages;       /* ceil(K / tile_k): k-loop trips of one workgroup */
+    int lds_stages;     /* LDS buffers per operand (1, or 2 if double-buffered) */
+    int lds_bytes;      /* LDS per workgroup, padding included */
+    int tile_bytes;     /* bytes of one unpadded A tile plus one B tile */
+    int outputs_per_thread; /* C elements each thread accumulates */
+    int vector_a;       /* 1 if A is read with 128-bit loads */
+    int vector_b;       /* 1 if B is read with 128-bit loads */
+    int vector_c;       /* 1 if C is written with 128-bit stores */
+} gemm_plan;
+
+int gemm_f32_plan(int variant, int M, int N, int K, const float *A,
+                  const float *B, const float *C, gemm_plan *plan);
+int gemm_f16_f32acc_plan(int variant, int M, int N, int K, const uint16_t *A,
+                         const uint16_t *B, const float *C, gemm_plan *plan);
+
+/* Static, NUL-terminated descriptions; never NULL ("unknown ..." for values
+ * outside the enums). */
+const char *gemm_status_string(int status);
+const char *gemm_variant_name(int variant);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DGOR_GEMM_H */

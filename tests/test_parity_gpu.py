@@ -1,0 +1,267 @@
+"""GPU parity: every kernel, called through the C ABI, against the CPU oracle.
+
+Bars (elementwise, FP32 output):
+  * small-integer inputs (values in {-4..4}): bit-exact, every shape;
+  * FP32 inputs: |C - C_ref| <= 2e-6 K;
+  * binary16 inputs: |C - C_ref| <= 2e-3 sqrt(K) max|C_ref|.
+Shapes span several tiles of each kernel configuration and end in ragged
+tails in M, N and K.  The full-size workloads are checked in the launch
+configuration the benchmark times: in full where the oracle is quick, else on
+sampled elements plus an invariant over every output (C v = A (B v) for a
+random +-1 vector v, exact on integer inputs).
+"""
+import numpy as np
+import pytest
+
+import dense_gemm_optimisation_row_amd as dg
+from dense_gemm_optimisation_row_amd import binding, inputs
+
+import oracle
+from helpers import (assert_bits_equal, assert_within, oracle_at, oracle_full, say, to_dev,
+                     tol_f16, tol_f32, workload)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU (run the CPU suite with -m 'not gpu')")
+    binding.load()  # raises if the HIP library was not built
+    return torch.device("cuda")
+
+
+def run(half, variant, A, B, C=None):
+    import torch
+    a, b = to_dev(A), to_dev(B)
+    if half:
+        c = dg.gemm_f16_f32acc_variant(variant, a, b, C)
+    else:
+        c = dg.gemm_f32_variant(variant, a, b, C)
+    torch.cuda.synchronize()
+    return c.cpu().numpy()
+
+
+def ints(M, N, K, seed, half=False):
+    return inputs.matrices(M, N, K, seed, "int", "f16" if half else "f32")
+
+
+def floats(M, N, K, seed, half=False):
+    return inputs.matrices(M, N, K, seed, "uniform", "f16" if half else "f32")
+
+
+SMALL_SHAPES = [
+    (1, 1, 1), (1, 1, 37), (5, 3, 2), (16, 16, 16), (17, 33, 65), (64, 64, 64),
+    (100, 70, 9), (127, 129, 131), (256, 256, 256), (300, 200, 100), (129, 257, 513),
+    (33, 1000, 48), (1000, 33, 777),
+]
+
+
+@pytest.mark.parametrize("variant", dg.F32_VARIANTS)
+@pytest.mark.parametrize("shape", SMALL_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_f32_variants_small_shapes(variant, shape):
+    M, N, K = shape
+    say("f32", dg.variant_name(variant), shape)
+    A, B = ints(M, N, K, 11)
+    assert_bits_equal(run(False, variant, A, B), oracle.gemm_f32(A, B), f"ints {shape}")
+    A, B = floats(M, N, K, 12)
+    assert_within(run(False, variant, A, B), oracle.gemm_f32(A, B), tol_f32(K), f"floats {shape}")
+
+
+@pytest.mark.parametrize("variant", dg.F16_VARIANTS)
+@pytest.mark.parametrize("shape", SMALL_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_f16_variants_small_shapes(variant, shape):
+    M, N, K = shape
+    say("f16", dg.variant_name(variant), shape)
+    A, B = ints(M, N, K, 13, half=True)
+    assert_bits_equal(run(True, variant, A, B), oracle.gemm_f16(A, B), f"ints {shape}")
+    A, B = floats(M, N, K, 14, half=True)
+    ref = oracle.gemm_f16(A, B)
+    assert_within(run(True, variant, A, B), ref, tol_f16(K, ref), f"floats {shape}")
+
+
+# Shapes large enough that the automatic choice takes each matrix-core tile
+# configuration, with ragged edges in all three dimensions.
+CONFIG_SHAPES = [
+    (False, (2049, 4100, 100), (128, 128)),   # FP32 128 x 128 tiles
+    (False, (1000, 1000, 1000), (64, 64)),    # FP32 64 x 64 tiles
+    (False, (4097, 33, 777), (32, 64)),       # FP32 narrow tiles
+    (True, (8191, 4097, 72), (256, 256)),     # FP16 256 x 256 tiles
+    (True, (2047, 4095, 200), (128, 128)),    # FP16 128 x 128 tiles
+    (True, (1000, 1000, 1000), (64, 64)),     # FP16 64 x 64 tiles
+]
+
+
+@pytest.mark.parametrize("half,shape,tile", CONFIG_SHAPES,
+                         ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else str(v))
+def test_every_matrix_core_configuration(half, shape, tile):
+    M, N, K = shape
+    p = dg.plan(half, M, N, K)
+    assert (p["tile_m"], p["tile_n"]) == tile
+    say("auto", "f16" if half else "f32", shape, "tile", tile)
+    A, B = ints(M, N, K, 21, half)
+    ref = oracle.gemm_f16(A, B) if half else oracle.gemm_f32(A, B)
+    assert_bits_equal(run(half, dg.AUTO, A, B), ref, f"ints {shape}")
+    A, B = floats(M, N, K, 22, half)
+    ref = oracle.gemm_f16(A, B) if half else oracle.gemm_f32(A, B)
+    tol = tol_f16(K, ref) if half else tol_f32(K)
+    assert_within(run(half, dg.AUTO, A, B), ref, tol, f"floats {shape}")
+
+
+# ------------------------------------------------------ full-size workloads --
+
+FULL = ["f32_256", "f32_1024", "f32_1000", "f32_4097x33x777"]
+SAMPLED = ["f32_4096", "f16_8192"]
+
+
+def _gpu_full(name, integer):
+    w = inputs.WORKLOADS[name]
+    A, B = workload(name, integer)
+    return run(w.dtype == "f16", dg.AUTO, A, B)
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_workload_full_compare(name):
+    w = inputs.WORKLOADS[name]
+    say("workload", name, "integer")
+    assert_bits_equal(_gpu_full(name, True), oracle_full(name, True), f"{name} ints")
+    say("workload", name, w.dist)
+    assert_within(_gpu_full(name, False), oracle_full(name, False), tol_f32(w.K), name)
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_ladder_rungs_on_workloads(name):
+    w = inputs.WORKLOADS[name]
+    A, B = workload(name, False)
+    ref = oracle_full(name, False)
+    for v in dg.F32_VARIANTS:
+        say("workload", name, dg.variant_name(v))
+        assert_within(run(False, v, A, B), ref, tol_f32(w.K), f"{name} {dg.variant_name(v)}")
+
+
+def _invariant_vector(N, seed):
+    rng = np.random.default_rng(seed)
+    return rng.choice(np.array([-1.0, 1.0], np.float32), N).astype(np.float32)
+
+
+@pytest.mark.parametrize("name", SAMPLED)
+def test_workload_sampled_and_invariant(name):
+    w = inputs.WORKLOADS[name]
+    half = w.dtype == "f16"
+    rows, cols = inputs.sample_indices(w.M, w.N, 4096, seed=w.seed + 7)
+
+    # integer variant: every output is an exact integer
+    say("workload", name, "integer")
+    A, B = workload(name, True)
+    C = _gpu_full(name, True)
+    assert_bits_equal(C[rows, cols], oracle_at(A, B, rows, cols), f"{name} ints sampled")
+    v = _invariant_vector(w.N, w.seed)
+    v_in = v.astype(np.float16) if half else v
+    Bv = (oracle.gemm_f16 if half else oracle.gemm_f32)(B, v_in.reshape(-1, 1))
+    ABv = oracle.gemm_f32(A.astype(np.float32), Bv)          # exact: |A B v| < 2^24 below
+    assert np.max(np.abs(ABv)) < 2 ** 24
+    Cv = C.astype(np.float64) @ v.astype(np.float64)
+    assert_bits_equal(Cv.reshape(-1, 1), ABv.astype(np.float64), f"{name} C v = A (B v)")
+    del C
+
+    say("workload", name, w.dist)
+    A, B = workload(name, False)
+    C = _gpu_full(name, False)
+    ref = oracle_at(A, B, rows, cols)
+    tol = tol_f16(w.K, ref) if half else tol_f32(w.K)
+    assert_within(C[rows, cols], ref, tol, f"{name} sampled")
+    if half:  # report whether the much tighter FP32-path bound also holds
+        err = float(np.max(np.abs(C[rows, cols] - ref)))
+        print(f"{name}: sampled max |dC| = {err:.3e} (FP32-path bound 2e-6 K = {tol_f32(w.K):.3e})")
+
+
+# -------------------------------------------------------------- edge cases --
+
+@pytest.mark.parametrize("half", [False, True])
+def test_k0_writes_zeros_and_empty_m_n_write_nothing(half):
+    import torch
+    say("edge K=0 / M=0 / N=0", "f16" if half else "f32")
+    dt = torch.float16 if half else torch.float32
+    a = torch.empty((5, 0), dtype=dt, device="cuda")
+    b = torch.empty((0, 7), dtype=dt, device="cuda")
+    c = torch.full((5, 7), float("nan"), device="cuda")
+    (dg.gemm_f16_f32acc if half else dg.gemm_f32)(a, b, c)
+    torch.cuda.synchronize()
+    assert torch.equal(c.cpu(), torch.zeros(5, 7))
+    sentinel = torch.full((4,), 3.0, device="cuda")
+    fn = binding.raw_gemm
+    A = torch.ones(16, dtype=dt, device="cuda")
+    assert fn(half, None, 0, 4, 4, A.data_ptr(), A.data_ptr(), sentinel.data_ptr(), None) == 0
+    assert fn(half, None, 4, 0, 4, A.data_ptr(), A.data_ptr(), sentinel.data_ptr(), None) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(sentinel.cpu(), torch.full((4,), 3.0))
+
+
+@pytest.mark.parametrize("half", [False, True])
+def test_misaligned_base_pointers_take_the_narrow_path(half):
+    import torch
+    M, N, K = 130, 136, 264
+    say("edge misaligned", "f16" if half else "f32", (M, N, K))
+    A, B = ints(M, N, K, 31, half)
+    ref = oracle.gemm_f16(A, B) if half else oracle.gemm_f32(A, B)
+    a_big = to_dev(np.concatenate([np.zeros(1, A.dtype), A.ravel()]))
+    b_big = to_dev(np.concatenate([np.zeros(1, B.dtype), B.ravel()]))
+    c_big = torch.zeros(M * N + 1, device="cuda")
+    a, b, c = a_big[1:].view(M, K), b_big[1:].view(K, N), c_big[1:].view(M, N)
+    assert a.data_ptr() % 16 and b.data_ptr() % 16 and c.data_ptr() % 16
+    p = dg.plan(half, M, N, K, A=a.data_ptr(), B=b.data_ptr(), C=c.data_ptr())
+    assert p["vector_a"] == 0 and p["vector_b"] == 0
+    variants = dg.F16_VARIANTS if half else dg.F32_VARIANTS
+    for v in variants:
+        c.zero_()
+        (dg.gemm_f16_f32acc_variant if half else dg.gemm_f32_variant)(v, a, b, c)
+        torch.cuda.synchronize()
+        assert_bits_equal(c.cpu().numpy(), ref, f"misaligned {dg.variant_name(v)}")
+    assert c_big[0].item() == 0.0   # nothing written before C
+
+
+def test_non_default_stream_and_determinism():
+    import torch
+    M, N, K = 1000, 1000, 1000
+    say("edge stream", (M, N, K))
+    A, B = floats(M, N, K, 41)
+    a, b = to_dev(A), to_dev(B)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        c1 = dg.gemm_f32(a, b)
+        c2 = dg.gemm_f32(a, b)
+    s.synchronize()
+    assert torch.equal(c1, c2)                  # same bits run to run
+    assert_within(c1.cpu().numpy(), oracle.gemm_f32(A, B), tol_f32(K), "stream")
+    A16, B16 = floats(M, N, K, 42, half=True)
+    h1 = dg.gemm_f16_f32acc(to_dev(A16), to_dev(B16), stream=s)
+    h2 = dg.gemm_f16_f32acc(to_dev(A16), to_dev(B16), stream=s)
+    s.synchronize()
+    assert torch.equal(h1, h2)
+
+
+def test_k1_is_a_single_rounded_product():
+    M, N = 70, 90
+    say("edge K=1")
+    A, B = floats(M, N, 1, 51)
+    expect = A * B            # one correctly rounded binary32 product
+    for v in dg.F32_VARIANTS:
+        assert_bits_equal(run(False, v, A, B), expect, f"K=1 {dg.variant_name(v)}")
+
+
+def test_error_paths_on_the_gpu():
+    import torch
+    say("edge error paths")
+    x = torch.ones(64, device="cuda")
+    p = x.data_ptr()
+    raw = binding.raw_gemm
+    assert raw(False, None, -1, 2, 2, p, p, p, None) == binding.GEMM_ERR_INVALID_DIM
+    assert raw(False, None, 2, 2, 2, None, p, p, None) == binding.GEMM_ERR_NULL_PTR
+    assert raw(True, 3, 2, 2, 2, p, p, p, None) == binding.GEMM_ERR_INVALID_VARIANT
+    with pytest.raises(dg.GemmError):
+        dg.gemm_f32_variant(7, x.view(8, 8), x.view(8, 8))
+    with pytest.raises(TypeError):
+        dg.gemm_f32(x.view(8, 8).half(), x.view(8, 8).half())
+    with pytest.raises(ValueError):
+        dg.gemm_f32(x.view(8, 8), x[:56].view(7, 8))
