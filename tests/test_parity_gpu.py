@@ -87,7 +87,8 @@ CONFIG_SHAPES = [
     (False, (2049, 4100, 100), (128, 128)),   # FP32 128 x 128 tiles
     (False, (1000, 1000, 1000), (64, 64)),    # FP32 64 x 64 tiles
     (False, (4097, 33, 777), (32, 64)),       # FP32 narrow tiles
-    (True, (8191, 4097, 72), (256, 256)),     # FP16 256 x 256 tiles
+    (True, (8191, 4097, 72), (256, 256)),     # FP16 256 x 256 tiles, unaligned rows
+    (True, (8000, 4104, 200), (256, 256)),    # FP16 256 x 256 tiles, 128-bit rows, ragged M/N/K
     (True, (2047, 4095, 200), (128, 128)),    # FP16 128 x 128 tiles
     (True, (1000, 1000, 1000), (64, 64)),     # FP16 64 x 64 tiles
 ]
