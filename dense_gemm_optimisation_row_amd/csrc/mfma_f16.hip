@@ -430,6 +430,186 @@ __global__ __launch_bounds__(256) void mfma_f16_big_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// Large-tile kernel with direct global->LDS loads (the gfx950 path).
+// 256 x 256 workgroup tile, 64-deep k-stages, two LDS buffers, four
+// wavefronts of 128 x 128 (16 MFMA 32x32x16 blocks, 256 accumulators).
+//
+// * Loads: buffer_load_dwordx4 ... lds.  One instruction moves 64 lanes x 16
+//   bytes into 1 KB of LDS, lane p landing at byte 16 p of the block; which
+//   16-byte chunk of the matrix lane p fetches is free, so the LDS layout is
+//   chosen by permuting the lanes' sources.  A lane whose offset is out of
+//   range writes zeros, which zero-fills every edge without a branch.
+// * LDS layout, in 16-byte units (8 halves):
+//     A tile (256 m x 64 k, 8 units per row):   unit c of row r sits at
+//       8 r + (c ^ ((r >> 1) & 7));
+//     B tile (64 k x 256 n, 32 units per row, row-major as in memory): unit u
+//       of row k sits at 32 k + (u ^ (4 (k & 3))).
+//   A fragments are 128-bit reads of 16 consecutive rows at one unit; B
+//   fragments are transposing reads (ds_read_b64_tr_b16): in each group of 16
+//   lanes, source lane s points at 4 halves of row kb + s/4, columns
+//   nb + 4 (s % 4), and output lane i receives rows kb..kb+3 of column nb + i,
+//   so two reads give a lane eight consecutive k of its column.  With these
+//   swizzles every 256-byte LDS cycle of either read touches each bank once.
+// * Ordering: on this chip a wavefront's LDS reads wait for its own earlier
+//   global->LDS loads to land.  So each stage starts (after the barrier that
+//   publishes it) by issuing all 32 fragment reads of the stage, then the
+//   loads of the next stage into the other buffer, then the 64 MFMAs; the
+//   next LDS read comes a full stage of MFMAs later, by when the loads have
+//   landed.
+namespace dma {
+constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int A_BYTES = BM * BK * 2;                 // 32 KB
+constexpr int B_BYTES = BK * BN * 2;                 // 32 KB
+constexpr int STAGE_BYTES = A_BYTES + B_BYTES;       // 64 KB
+constexpr int LDS_BYTES = 2 * STAGE_BYTES;
+}  // namespace dma
+
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
+
+__device__ __forceinline__ void load_to_lds(__amdgpu_buffer_rsrc_t r, uint8_t *lds_block,
+                                            uint32_t voff)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds_block, 16, voff, 0, 0, 0);
+}
+
+__global__ __launch_bounds__(256) void mfma_f16_dma_kernel(
+    int M, int N, int K, const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
+    float *__restrict__ C, int tiles_m, int tiles_n, int group_m)
+{
+    using namespace dma;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
+
+    int tm, tn;
+    dgor_tile_of_block(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wr = (wave >> 1) * 128, wc = (wave & 1) * 128;
+    const int l32 = lane & 31, g = lane >> 5;
+    constexpr uint32_t OOB = 0x80000000u;
+
+    // ---- loader: wave w fills A blocks 8w..8w+7 (8 rows each) and B blocks
+    // 8w..8w+7 (2 rows each); per lane, offsets relative to the stage base.
+    uint32_t a_off[8], b_off[8];
+    int a_c[8], b_k[8];
+    bool a_row_ok[8], b_col_ok[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const int blk = 8 * wave + q;
+        const int r = 8 * blk + (lane >> 3);                     // A row in the tile
+        const int c = (lane & 7) ^ ((r >> 1) & 7);               // its logical unit
+        a_c[q] = c;
+        a_row_ok[q] = m0 + r < M;
+        a_off[q] = (uint32_t)(r * K + 8 * c) * 2u;
+        const int k = 2 * blk + (lane >> 5);                     // B row in the tile
+        const int u = (lane & 31) ^ (4 * (k & 3));               // its logical unit
+        b_k[q] = k;
+        b_col_ok[q] = n0 + 8 * u < N;
+        b_off[q] = (uint32_t)(k * N + 8 * u) * 2u;
+    }
+    auto issue = [&](int stage) {
+        const int k0 = stage * BK;
+        uint8_t *base = lds + (stage & 1) * STAGE_BYTES;
+        const __amdgpu_buffer_rsrc_t ra =
+            make_rsrc(A + (size_t)m0 * K + k0, ((long long)(M - m0) * K - k0) * 2);
+        const __amdgpu_buffer_rsrc_t rb =
+            make_rsrc(B + (size_t)k0 * N + n0, ((long long)(K - k0) * N - n0) * 2);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const bool ok = a_row_ok[q] && k0 + 8 * a_c[q] < K;
+            load_to_lds(ra, base + (8 * wave + q) * 1024, ok ? a_off[q] : OOB);
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const bool ok = b_col_ok[q] && k0 + b_k[q] < K;
+            load_to_lds(rb, base + A_BYTES + (8 * wave + q) * 1024, ok ? b_off[q] : OOB);
+        }
+    };
+
+    // ---- fragment readers (per k-step s = 0..3 of a stage)
+    const int a_swz = (l32 >> 1) & 7;
+    const uint32_t a_lane = (uint32_t)(8 * (wr + l32)) * 16u;
+    uint32_t a_unit[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+        a_unit[s] = (uint32_t)((2 * s + g) ^ a_swz) * 16u;
+    const int sl = lane & 15, grp = lane >> 4;
+    const uint32_t b_lane = (uint32_t)(512 * (8 * (grp >> 1) + (sl >> 2)) + 8 * (sl & 1));
+    uint32_t b_unit[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int u = (wc >> 3) + 4 * j + 2 * (grp & 1) + ((sl & 3) >> 1);
+        b_unit[j] = (uint32_t)(u ^ (4 * (sl >> 2))) * 16u;
+    }
+
+    halfx8 fa[4][4], fb[4][4];   // [k-step][block]
+    auto fread = [&](int stage) {
+        const uint8_t *base = lds + (stage & 1) * STAGE_BYTES;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                fa[s][i] = *reinterpret_cast<const halfx8 *>(base + a_lane + a_unit[s] + i * 32 * 128);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint8_t *bp = base + A_BYTES + b_lane + b_unit[j] + 512 * 16 * s;
+                const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4 *)(bp));
+                const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4 *)(bp + 512 * 4));
+                fb[s][j] = __builtin_bit_cast(halfx8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            }
+        }
+    };
+
+    floatx16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                acc[i][j][r] = 0.f;
+
+    const int steps = (K + BK - 1) / BK;
+    issue(0);
+    for (int t = 0; t < steps; ++t) {
+        // this wave's loads of stage t are the only ones outstanding
+        __builtin_amdgcn_s_waitcnt((0) | (7 << 4) | (15 << 8));   // vmcnt(0)
+        __syncthreads();   // everyone's loads of stage t landed; stage t-1 fully read
+        fread(t);
+        if (t + 1 < steps)
+            issue(t + 1);  // into the buffer of stage t-1, read by no one any more
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[s][i], fb[s][j], acc[i][j], 0, 0, 0);
+    }
+
+    // Epilogue: buffer stores; an element outside C gets an out-of-range lane
+    // offset, so it is dropped.
+    const int col = n0 + wc + l32;
+    const int rows_left = M - m0 - wr - 4 * g;
+    const __amdgpu_buffer_rsrc_t rc =
+        make_rsrc(C + (size_t)(m0 + wr) * N + n0 + wc, ((long long)(M - m0 - wr) * N - n0 - wc) * 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t cv = (col + 32 * j < N) ? (uint32_t)((4 * g) * N + l32 + 32 * j) * 4u : OOB;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int ro = 32 * i + 8 * (r >> 2) + (r & 3);
+                const float v = acc[i][j][r];
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rc, ro < rows_left ? cv : OOB,
+                                                      (uint32_t)(ro * N) * 4u, 0);
+            }
+    }
+}
+
 template <int BM, int BN, int BK, int WM, int WN>
 hipError_t launch_cfg(const Problem &p, const gemm_plan &plan, hipStream_t s)
 {
@@ -457,7 +637,7 @@ hipError_t launch_mfma_f16(const Problem &p, const gemm_plan &plan, hipStream_t 
 {
     if (plan.tile_m == 256 && plan.tile_n == 256) {
         if (p.vec_a && p.vec_b && p.K <= (1 << 22) && p.N <= (1 << 22)) {
-            hipLaunchKernelGGL(mfma_f16_big_kernel, dim3(plan.grid_x * plan.grid_y), dim3(256), 0, s,
+            hipLaunchKernelGGL(mfma_f16_dma_kernel, dim3(plan.grid_x * plan.grid_y), dim3(256), 0, s,
                                p.M, p.N, p.K, (const uint16_t *)p.A, (const uint16_t *)p.B, p.C,
                                plan.grid_y, plan.grid_x, 4);
             return hipGetLastError();
