@@ -193,241 +193,12 @@ __global__ __launch_bounds__(64 * WM * WN) void mfma_f16_kernel(
         }
 }
 
-// ---------------------------------------------------------------------------
-// Large-tile kernel: 256 x 256 workgroup tile, 64-deep k-stages, four
-// wavefronts of 128 x 128 (16 MFMA blocks of 32 x 32, 256 FP32 accumulators
-// per lane).  Used when A and B rows are 16-byte aligned (K % 8 == 0,
-// N % 8 == 0, aligned bases).
-//
-// * Loads: buffer loads.  One per-lane byte offset serves all eight loads of
-//   an operand (the eight loads differ by a uniform scalar offset) and the
-//   descriptor is re-based per k-stage.  A load whose lane offset lies past
-//   the descriptor's end reads as zero; the scalar offset may not take part
-//   in that range check, so every load that would touch a row or chunk
-//   outside the matrix gets an out-of-range lane offset (0x80000000) by a
-//   select.  All offsets fit 32 bits for K, N <= 2^22 (checked on launch).
-// * LDS: A as [m][k] rows and B transposed to [n][k] rows, both 64 halves +
-//   8 padding halves (144 bytes) per row, so the 16 or 32 rows that one
-//   128-bit fragment read touches start on distinct bank groups.  B is
-//   transposed in registers while staging (8 x 8 blocks of halves, one per
-//   thread and stage), so both fragments are single 128-bit LDS reads.
-// * Pipelining: global loads for stage t+1 are issued at the start of stage
-//   t and written to the other LDS buffer at its end; the fragments of
-//   k-step s+1 are read while the 16 MFMAs of step s run; one barrier per
-//   stage.
-namespace big {
-constexpr int BM = 256, BN = 256, BK = 64, NT = 256;
-constexpr int ROW = BK + 8;               // halves per LDS row
-constexpr int TILE = 256 * ROW;           // halves per operand per stage
-constexpr int LDS_BYTES = 2 * 2 * TILE * 2;
-}  // namespace big
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
+// Buffer descriptor over [base, base + bytes): loads past the end read as
+// zero, stores past it are dropped (bytes <= 0 gives an empty range).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, long long bytes)
 {
     const int n = bytes <= 0 ? 0 : (bytes > 0x7fffffffLL ? 0x7fffffff : (int)bytes);
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, n, 0x00020000);
-}
-
-__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
-{
-    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
-}
-
-// 8 x 8 block of halves: in[k] holds (k, n0..n7); out[n] holds (k0..k7, n).
-__device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[8])
-{
-#pragma unroll
-    for (int n = 0; n < 8; ++n)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            out[n][j] = __builtin_amdgcn_perm(in[2 * j + 1][n >> 1], in[2 * j][n >> 1],
-                                              (n & 1) ? 0x07060302u : 0x05040100u);
-}
-
-__global__ __launch_bounds__(256) void mfma_f16_big_kernel(
-    int M, int N, int K, const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
-    float *__restrict__ C, int tiles_m, int tiles_n, int group_m)
-{
-    using namespace big;
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][TILE];  // [buf][A/B]
-
-    int tm, tn;
-    dgor_tile_of_block(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
-    const int m0 = tm * BM, n0 = tn * BN;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wr = (wave >> 1) * 128, wc = (wave & 1) * 128;
-    const int l32 = lane & 31, g = lane >> 5;
-
-    // loader coordinates
-    const int a_row = tid >> 3, a_chunk = tid & 7;      // + 32 j rows, j = 0..7
-    const int b_kb = tid & 7, b_nb = tid >> 3;          // 8 x 8 block (k, n)
-    constexpr uint32_t OOB = 0x80000000u;
-    const uint32_t a_voff = (uint32_t)(a_row * K + a_chunk * 8) * 2u;
-    const uint32_t a_step = (uint32_t)(32 * K) * 2u;
-    const int a_rows_left = M - m0 - a_row;             // rows a_row + 32 j valid while < this
-    const uint32_t b_voff = (n0 + b_nb * 8 < N) ? (uint32_t)(b_kb * 8 * N + b_nb * 8) * 2u : OOB;
-    const uint32_t b_step = (uint32_t)N * 2u;
-
-    u32x4 ast[8], bst[8];
-    auto gload = [&](int k0) {
-        const __amdgpu_buffer_rsrc_t ra =
-            make_rsrc(A + (size_t)m0 * K + k0, ((long long)(M - m0) * K - k0) * 2);
-        const uint32_t av = (k0 + a_chunk * 8 < K) ? a_voff : OOB;
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            ast[j] = bload16(ra, (32 * j < a_rows_left) ? av : OOB, j * a_step);
-        const __amdgpu_buffer_rsrc_t rb =
-            make_rsrc(B + (size_t)k0 * N + n0, ((long long)(K - k0) * N - n0) * 2);
-        const int b_rows_left = K - k0 - b_kb * 8;
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            bst[i] = bload16(rb, (i < b_rows_left) ? b_voff : OOB, i * b_step);
-    };
-    auto sstore = [&](int buf) {
-        uint16_t *as = lds[buf][0];
-        uint16_t *bs = lds[buf][1];
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            *reinterpret_cast<u32x4 *>(&as[(a_row + 32 * j) * ROW + a_chunk * 8]) = ast[j];
-        u32x4 bt[8];
-        transpose8x8(bst, bt);
-#pragma unroll
-        for (int n = 0; n < 8; ++n)
-            *reinterpret_cast<u32x4 *>(&bs[(b_nb * 8 + n) * ROW + b_kb * 8]) = bt[n];
-    };
-
-    halfx8 fa[2][4], fb[2][4];
-    auto fread = [&](int buf, int s, int slot) {
-        const uint16_t *as = lds[buf][0];
-        const uint16_t *bs = lds[buf][1];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            fa[slot][i] = *reinterpret_cast<const halfx8 *>(&as[(wr + 32 * i + l32) * ROW + 16 * s + 8 * g]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            fb[slot][j] = *reinterpret_cast<const halfx8 *>(&bs[(wc + 32 * j + l32) * ROW + 16 * s + 8 * g]);
-    };
-
-    floatx16 acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                acc[i][j][r] = 0.f;
-
-    // MFMAs of one k-step: the 16 blocks, or half of them (8 per half).
-    auto mfmas = [&](int slot, int first, int count) {
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-            if (q < first || q >= first + count)
-                continue;
-            const int i = q >> 2, j = q & 3;
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[slot][i], fb[slot][j], acc[i][j], 0, 0, 0);
-        }
-    };
-    // Issue order hints (masks: 0x008 MFMA, 0x100 LDS read, 0x200 LDS write,
-    // 0x002 VALU, 0x020 global read).  Each k-step interleaves its 16 MFMAs
-    // with the 8 fragment reads of the next step.
-    auto order_step = [&]() {
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-    };
-    // First half of the last k-step: 8 MFMAs with the 16 LDS writes and the
-    // 32 register permutes of the next stage's tiles.
-    auto order_stage_end = [&]() {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);
-        }
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
-            __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);
-        }
-    };
-    // Second half, after the barrier: 8 MFMAs with the 16 global loads of the
-    // stage after next and the 8 fragment reads of the next stage's step 0.
-    auto order_stage_start = [&]() {
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-    };
-
-    const int steps = (K + BK - 1) / BK;
-    gload(0);
-    sstore(0);
-    __syncthreads();
-    if (steps > 1)
-        gload(BK);
-    fread(0, 0, 0);
-    // One stage: k-steps 0..3 of LDS buffer `buf`; with a next stage, its
-    // staged tiles go to the other buffer around the barrier.
-    auto stage = [&](int t, auto has_next) {
-        const int buf = t & 1;
-        fread(buf, 1, 1);
-        mfmas(0, 0, 16);
-        order_step();
-        fread(buf, 2, 0);
-        mfmas(1, 0, 16);
-        order_step();
-        fread(buf, 3, 1);
-        mfmas(0, 0, 16);
-        order_step();
-        if constexpr (decltype(has_next)::value) {
-            sstore(buf ^ 1);  // buffer buf^1 was last read before the previous barrier
-            mfmas(1, 0, 8);
-            order_stage_end();
-            __syncthreads();
-            // past the last stage every lane offset is out of range: the
-            // loads return zeros without touching memory, and the block
-            // stays free of branches for the scheduler
-            gload((t + 2) * BK);
-            fread(buf ^ 1, 0, 0);
-            mfmas(1, 8, 8);
-            order_stage_start();
-        } else {
-            mfmas(1, 0, 16);
-        }
-    };
-    for (int t = 0; t + 1 < steps; ++t)
-        stage(t, std::integral_constant<bool, true>{});
-    stage(steps - 1, std::integral_constant<bool, false>{});
-
-    // Epilogue: buffer stores; an element outside C gets an out-of-range lane
-    // offset, so it is dropped.
-    const int col = n0 + wc + l32;
-    const int rows_left = M - m0 - wr - 4 * g;          // row offsets below this are valid
-    const __amdgpu_buffer_rsrc_t rc =
-        make_rsrc(C + (size_t)(m0 + wr) * N + n0 + wc, ((long long)(M - m0 - wr) * N - n0 - wc) * 4);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const uint32_t cv = (col + 32 * j < N) ? (uint32_t)((4 * g) * N + l32 + 32 * j) * 4u : OOB;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int ro = 32 * i + 8 * (r >> 2) + (r & 3);
-                const uint32_t so = (uint32_t)(ro * N) * 4u;
-                // copy the element out first: bit-casting the vector element
-                // in place read element 0 with this compiler
-                const float v = acc[i][j][r];
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rc, ro < rows_left ? cv : OOB,
-                                                      so, 0);
-            }
-    }
 }
 
 // ---------------------------------------------------------------------------
