@@ -169,6 +169,165 @@ __global__ __launch_bounds__(64 * WM * WN) void mfma_f32_kernel(
         }
 }
 
+// ---------------------------------------------------------------------------
+// 128 x 128 x 16 tile with direct global->LDS loads, for 16-byte aligned rows.
+// Same wavefront tiling and k-mapping as above; what changes is the supply:
+// * Loads: buffer_load_dwordx4 ... lds, 1 KB of LDS per instruction (lane p
+//   -> byte 16 p); the matrix chunk each lane fetches is permuted so the LDS
+//   layout comes out swizzled, and a lane with an out-of-range offset writes
+//   zeros, which masks every edge.  Units are 16 bytes (4 floats):
+//     A tile (128 m x 16 k, 4 units per row):  unit c of row r at
+//       4 r + (c ^ ((r >> 2) & 3));
+//     B tile (16 k x 128 n, 32 units per row): unit u of row k at
+//       32 k + (u ^ (8 ((k >> 2) & 1))).
+//   A reads (128-bit, 16 consecutive rows at one unit) and B reads (32-bit,
+//   32 consecutive columns of rows k and k + 4) then touch each bank once per
+//   256-byte LDS cycle.
+// * Order: a wavefront's LDS reads wait for its own earlier global->LDS loads,
+//   so each stage issues all of its fragment reads first, then the next
+//   stage's loads, then its 32 MFMAs.  Several workgroups share a compute
+//   unit, so their MFMAs cover one another's waits.
+namespace f32dma {
+constexpr int BM = 128, BN = 128, BK = 16;
+constexpr int A_BYTES = BM * BK * 4;            // 8 KB
+constexpr int B_BYTES = BK * BN * 4;            // 8 KB
+constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+constexpr int LDS_BYTES = 2 * STAGE_BYTES;      // 32 KB
+}  // namespace f32dma
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, long long bytes)
+{
+    const int n = bytes <= 0 ? 0 : (bytes > 0x7fffffffLL ? 0x7fffffff : (int)bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, n, 0x00020000);
+}
+
+__global__ __launch_bounds__(256) void mfma_f32_dma_kernel(
+    int M, int N, int K, const float *__restrict__ A, const float *__restrict__ B,
+    float *__restrict__ C, int tiles_m, int tiles_n, int group_m)
+{
+    using namespace f32dma;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
+
+    int tm, tn;
+    dgor_tile_of_block(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wr = (wave >> 1) * 64, wc = (wave & 1) * 64;
+    const int l32 = lane & 31, g = lane >> 5;
+    constexpr uint32_t OOB = 0x80000000u;
+
+    // loader: wave w fills A blocks 2w, 2w+1 (16 rows each) and B blocks
+    // 2w, 2w+1 (2 rows each)
+    uint32_t a_off[2], b_off[2];
+    int a_c[2], b_k[2];
+    bool a_row_ok[2], b_col_ok[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int blk = 2 * wave + q;
+        const int r = 16 * blk + (lane >> 2);
+        const int c = (lane & 3) ^ ((r >> 2) & 3);
+        a_c[q] = c;
+        a_row_ok[q] = m0 + r < M;
+        a_off[q] = (uint32_t)(r * K + 4 * c) * 4u;
+        const int k = 2 * blk + (lane >> 5);
+        const int u = (lane & 31) ^ (8 * ((k >> 2) & 1));
+        b_k[q] = k;
+        b_col_ok[q] = n0 + 4 * u < N;
+        b_off[q] = (uint32_t)(k * N + 4 * u) * 4u;
+    }
+    auto issue = [&](int stage) {
+        const int k0 = stage * BK;
+        uint8_t *base = lds + (stage & 1) * STAGE_BYTES;
+        const __amdgpu_buffer_rsrc_t ra =
+            make_rsrc(A + (size_t)m0 * K + k0, ((long long)(M - m0) * K - k0) * 4);
+        const __amdgpu_buffer_rsrc_t rb =
+            make_rsrc(B + (size_t)k0 * N + n0, ((long long)(K - k0) * N - n0) * 4);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const bool ok = a_row_ok[q] && k0 + 4 * a_c[q] < K;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(base + (2 * wave + q) * 1024), 16,
+                                                     ok ? a_off[q] : OOB, 0, 0, 0);
+        }
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const bool ok = b_col_ok[q] && k0 + b_k[q] < K;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(base + A_BYTES + (2 * wave + q) * 1024),
+                                                     16, ok ? b_off[q] : OOB, 0, 0, 0);
+        }
+    };
+
+    // fragment addresses (bytes within a stage)
+    const int a_swz = (l32 >> 2) & 3;
+    const uint32_t a_lane = (uint32_t)(4 * (wr + l32)) * 16u;
+    const uint32_t a_unit0 = (uint32_t)((0 + g) ^ a_swz) * 16u;   // k 0..7 of the stage
+    const uint32_t a_unit1 = (uint32_t)((2 + g) ^ a_swz) * 16u;   // k 8..15
+    // B value of block fn, k = 8 s + 4 g + q: row k, unit 16 (wc/64) + 8 (fn ^ g) + l32/4
+    const uint32_t b_lane = (uint32_t)(512 * (4 * g) + 16 * (16 * (wc >> 6) + (l32 >> 2)) + 4 * (l32 & 3));
+
+    float4 fa[2][2];     // [k-slice s][block fm]
+    float fb[2][2][4];   // [s][fn][q]
+    auto fread = [&](int stage) {
+        const uint8_t *base = lds + (stage & 1) * STAGE_BYTES;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                fa[s][i] = *reinterpret_cast<const float4 *>(base + a_lane + (s ? a_unit1 : a_unit0) + i * 32 * 64);
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    fb[s][j][q] = *reinterpret_cast<const float *>(
+                        base + A_BYTES + b_lane + 512 * (8 * s + q) + 16 * 8 * (j ^ g));
+        }
+    };
+
+    floatx16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                acc[i][j][r] = 0.f;
+
+    const int steps = (K + BK - 1) / BK;
+    issue(0);
+    for (int t = 0; t < steps; ++t) {
+        __builtin_amdgcn_s_waitcnt((0) | (7 << 4) | (15 << 8));   // vmcnt(0): own loads of stage t
+        __syncthreads();   // everyone's loads of stage t landed; stage t-1 fully read
+        fread(t);
+        if (t + 1 < steps)
+            issue(t + 1);  // into the other buffer, read by no one any more
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        const float av = q == 0 ? fa[s][i].x : q == 1 ? fa[s][i].y : q == 2 ? fa[s][i].z : fa[s][i].w;
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, fb[s][j][q], acc[i][j], 0, 0, 0);
+                    }
+    }
+
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int col = n0 + wc + j * 32 + l32;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = m0 + wr + i * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+                if (row < M && col < N)
+                    C[(size_t)row * N + col] = acc[i][j][r];
+            }
+        }
+}
+
 template <int BM, int BN, int BK, int WM, int WN>
 hipError_t launch_cfg(const Problem &p, const gemm_plan &plan, hipStream_t s)
 {
@@ -194,8 +353,15 @@ hipError_t launch_cfg(const Problem &p, const gemm_plan &plan, hipStream_t s)
 
 hipError_t launch_mfma_f32(const Problem &p, const gemm_plan &plan, hipStream_t s)
 {
-    if (plan.tile_m == 128 && plan.tile_n == 128)
+    if (plan.tile_m == 128 && plan.tile_n == 128) {
+        if (p.vec_a && p.vec_b && p.K <= (1 << 22) && p.N <= (1 << 22)) {
+            hipLaunchKernelGGL(mfma_f32_dma_kernel, dim3(plan.grid_x * plan.grid_y), dim3(256), 0, s,
+                               p.M, p.N, p.K, (const float *)p.A, (const float *)p.B, p.C,
+                               plan.grid_y, plan.grid_x, 8);
+            return hipGetLastError();
+        }
         return launch_cfg<128, 128, 16, 2, 2>(p, plan, s);
+    }
     if (plan.tile_m == 64 && plan.tile_n == 64)
         return launch_cfg<64, 64, 16, 2, 2>(p, plan, s);
     if (plan.tile_m == 32 && plan.tile_n == 64)
