@@ -147,8 +147,13 @@ int plan_f32(int variant, int M, int N, int K, const void *A, const void *B, con
         p->tile_n = c.bn;
         p->tile_k = c.bk;
         p->threads = 64 * c.waves_m * c.waves_n;
-        p->lds_stages = 2;
-        p->lds_bytes = dgor::mfma_f32_lds_bytes(c);
+        if (dgor::direct_lds_applies(c.bm, dgor::kF32Configs[0].bm, p->vector_a, p->vector_b, N, K)) {
+            p->lds_stages = dgor::kF32DirectStages;
+            p->lds_bytes = dgor::kF32DirectLdsBytes;
+        } else {
+            p->lds_stages = 2;
+            p->lds_bytes = dgor::mfma_f32_lds_bytes(c);
+        }
         p->tile_bytes = (c.bm * c.bk + c.bk * c.bn) * 4;
         p->outputs_per_thread = c.bm * c.bn / p->threads;
         p->vector_c = 0;
@@ -194,8 +199,13 @@ int plan_f16(int variant, int M, int N, int K, const void *A, const void *B, con
         p->tile_n = c.bn;
         p->tile_k = c.bk;
         p->threads = 64 * c.waves_m * c.waves_n;
-        p->lds_stages = 2;
-        p->lds_bytes = dgor::mfma_f16_lds_bytes(c);
+        if (dgor::direct_lds_applies(c.bm, dgor::kF16Configs[0].bm, p->vector_a, p->vector_b, N, K)) {
+            p->lds_stages = dgor::kF16RingStages;
+            p->lds_bytes = dgor::kF16RingLdsBytes;
+        } else {
+            p->lds_stages = 2;
+            p->lds_bytes = dgor::mfma_f16_lds_bytes(c);
+        }
         p->tile_bytes = (c.bm * c.bk + c.bk * c.bn) * 2;
         p->outputs_per_thread = c.bm * c.bn / p->threads;
     }

@@ -26,6 +26,7 @@ namespace {
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 // Eight halves of row r from column c of a rows x cols row-major binary16
 // matrix, zero outside it.  VEC: rows start 16-byte aligned and cols % 8 == 0.
@@ -93,7 +94,9 @@ __global__ __launch_bounds__(64 * WM * WN) void mfma_f16_kernel(
     int tm, tn;
     dgor_tile_of_block(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    // wave-uniform, so per-wave offsets and buffer descriptors stay scalar
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wr = (wave / WN) * WTM, wc = (wave % WN) * WTN;
     const int l32 = lane & 31, g = lane >> 5;
 
@@ -202,178 +205,268 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, lo
 }
 
 // ---------------------------------------------------------------------------
-// Large-tile kernel with direct global->LDS loads (the gfx950 path).
-// 256 x 256 workgroup tile, 64-deep k-stages, two LDS buffers, four
-// wavefronts of 128 x 128 (16 MFMA 32x32x16 blocks, 256 accumulators).
+// Large-tile kernel (the gfx950 path for 16-byte aligned operands):
+// 256 x 256 workgroup tile, 32-deep k-stages in a ring of four LDS buffers,
+// four wavefronts of 128 x 128, each an 8 x 8 grid of
+// v_mfma_f32_16x16x32_f16 blocks (256 accumulators per lane).
 //
-// * Loads: buffer_load_dwordx4 ... lds.  One instruction moves 64 lanes x 16
-//   bytes into 1 KB of LDS, lane p landing at byte 16 p of the block; which
-//   16-byte chunk of the matrix lane p fetches is free, so the LDS layout is
-//   chosen by permuting the lanes' sources.  A lane whose offset is out of
-//   range writes zeros, which zero-fills every edge without a branch.
-// * LDS layout, in 16-byte units (8 halves):
-//     A tile (256 m x 64 k, 8 units per row):   unit c of row r sits at
-//       8 r + (c ^ ((r >> 1) & 7));
-//     B tile (64 k x 256 n, 32 units per row, row-major as in memory): unit u
-//       of row k sits at 32 k + (u ^ (4 (k & 3))).
-//   A fragments are 128-bit reads of 16 consecutive rows at one unit; B
-//   fragments are transposing reads (ds_read_b64_tr_b16): in each group of 16
+// v_mfma_f32_16x16x32_f16 (wave64): lane l = 16 g + s supplies eight halves
+// A[s][8 g + 0..7] and B[8 g + 0..7][s] and holds C[4 g + r][s], r = 0..3.
+//
+// * Loads go straight from global memory into LDS (buffer_load_dwordx4 ...
+//   lds): one instruction moves 64 lanes x 16 bytes into 1 KB of LDS, lane p
+//   landing at byte 16 p; which 16-byte chunk of the matrix lane p fetches is
+//   free, so the LDS layout is chosen by permuting the sources.  A lane whose
+//   offset is out of range writes zeros, which zero-fills every edge.
+// * LDS layout of one stage, in 16-byte units (8 halves):
+//     A (256 m x 32 k, 4 units per row): unit c of row r at
+//       4 r + (c ^ (2 ((r >> 2) & 1)));
+//     B (32 k x 256 n, 32 units per row): unit u of row k at
+//       32 k + (u ^ (4 (k & 3) + 2 ((k >> 3) & 1))).
+//   A fragments are 128-bit reads of 16 consecutive rows at one unit.  B
+//   fragments are transposing reads (ds_read_b64_tr_b16): in a group of 16
 //   lanes, source lane s points at 4 halves of row kb + s/4, columns
-//   nb + 4 (s % 4), and output lane i receives rows kb..kb+3 of column nb + i,
-//   so two reads give a lane eight consecutive k of its column.  With these
-//   swizzles every 256-byte LDS cycle of either read touches each bank once.
-// * Ordering: on this chip a wavefront's LDS reads wait for its own earlier
-//   global->LDS loads to land.  So each stage starts (after the barrier that
-//   publishes it) by issuing all 32 fragment reads of the stage, then the
-//   loads of the next stage into the other buffer, then the 64 MFMAs; the
-//   next LDS read comes a full stage of MFMAs later, by when the loads have
-//   landed.
-namespace dma {
-constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int A_BYTES = BM * BK * 2;                 // 32 KB
-constexpr int B_BYTES = BK * BN * 2;                 // 32 KB
-constexpr int STAGE_BYTES = A_BYTES + B_BYTES;       // 64 KB
-constexpr int LDS_BYTES = 2 * STAGE_BYTES;
-}  // namespace dma
+//   nb + 4 (s % 4), and output lane i receives rows kb..kb+3 of column nb + i;
+//   two such reads give a lane its eight k.  The LDS serves 256 bytes (16
+//   units) a cycle.  A 128-bit read is served in four cycles, each taking
+//   the 16 lanes that agree in lane bit 5 and in the parity of lane bits
+//   2..4; a cycle is free of bank conflicts when its 16 units differ modulo
+//   16.  (This rule reproduces the bank-conflict counter for thirteen
+//   probed patterns.)  The A swizzle keeps every such group apart, and a
+//   64-bit transposing read, served 32 lanes a cycle, measures free of
+//   conflicts with the B swizzle.
+// * Pipeline.  The loads of stage t + 3 and the fragment reads of stage t + 1
+//   are spread between the 64 MFMAs of stage t.  Before stage t each
+//   wavefront waits for its own loads of stage t + 1 (the loads of t + 2 stay
+//   in flight) and the workgroup meets at one barrier: after it every load of
+//   stage t + 1 has landed, and every wavefront has consumed stage t - 1, whose
+//   buffer stage t + 3 then refills.
+// * The hardware lets a wavefront's LDS reads run ahead of its own
+//   outstanding global->LDS loads, but the compiler, when it sees such a load
+//   in flight, waits for it before every transposing LDS read.  The loads are
+//   therefore issued from inline assembly that the compiler does not track,
+//   and the kernel orders them itself with the waits and barriers above.
+namespace pipe {
+constexpr int BM = 256, BN = 256, BK = 32, NBUF = 4;
+constexpr int A_BYTES = BM * BK * 2;                 // 16 KB
+constexpr int B_BYTES = BK * BN * 2;                 // 16 KB
+constexpr int STAGE_BYTES = A_BYTES + B_BYTES;       // 32 KB
+constexpr int LDS_BYTES = NBUF * STAGE_BYTES;        // 128 KB
+constexpr int LOADS_PER_STAGE = 8;                   // per wavefront: 4 of A, 4 of B
+}  // namespace pipe
 
 typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef int intx4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
 
-__device__ __forceinline__ void load_to_lds(__amdgpu_buffer_rsrc_t r, uint8_t *lds_block,
-                                            uint32_t voff)
+// The four words of a raw buffer descriptor over [base, base + bytes), as
+// make_rsrc builds it, for use as an inline-assembly operand.
+__device__ __forceinline__ intx4 rsrc_words(const void *base, long long bytes)
 {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds_block, 16, voff, 0, 0, 0);
+    const uint64_t p = (uint64_t)(uintptr_t)base;
+    const int n = bytes <= 0 ? 0 : (bytes > 0x7fffffffLL ? 0x7fffffff : (int)bytes);
+    intx4 d;
+    d.x = (int)(uint32_t)p;
+    d.y = (int)((uint32_t)(p >> 32) & 0xffffu);
+    d.z = n;
+    d.w = 0x00020000;
+    return d;
 }
 
-__global__ __launch_bounds__(256) void mfma_f16_dma_kernel(
+// One global->LDS load of 64 x 16 bytes: lane p reads 16 bytes at byte offset
+// voff of the descriptor's range (zeros when out of range) and writes them to
+// LDS address lds + 16 p.  M0 carries the LDS address; one wait state
+// separates its write from the load that reads it.  The kernel that uses
+// this keeps nothing of its own in M0 (the compiler emits no M0 access in
+// it, which a test checks on the generated code), so M0 is not restored.
+// Not tracked by the compiler's wait counters: the caller waits with vmcnt.
+__device__ __forceinline__ void load_to_lds(intx4 rsrc, uint32_t lds, uint32_t voff)
+{
+    asm volatile("s_mov_b32 m0, %0\n\t"
+                 "s_nop 0\n\t"
+                 "buffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(lds), "v"(voff), "s"(rsrc)
+                 : "memory");
+}
+
+// s_waitcnt immediate (gfx9 encoding) for vmcnt(n) alone: vmcnt bits 3:0 and
+// 15:14, expcnt (6:4) and lgkmcnt (11:8) left at their maximum.
+constexpr int wait_vmcnt(int n)
+{
+    return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);
+}
+static_assert(wait_vmcnt(0) == 0x0f70 && wait_vmcnt(8) == 0x0f78 && wait_vmcnt(24) == 0x4f78,
+              "vmcnt encoding");
+
+__global__ __launch_bounds__(256) void mfma_f16_pipe_kernel(
     int M, int N, int K, const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     float *__restrict__ C, int tiles_m, int tiles_n, int group_m)
 {
-    using namespace dma;
+    using namespace pipe;
     __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
+    const uint32_t ring = (uint32_t)(uintptr_t)(lds_void *)lds;   // LDS byte address
 
     int tm, tn;
     dgor_tile_of_block(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lane = threadIdx.x & 63;
+    // wave-uniform, so per-wave offsets and descriptors stay scalar
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int wr = (wave >> 1) * 128, wc = (wave & 1) * 128;
-    const int l32 = lane & 31, g = lane >> 5;
     constexpr uint32_t OOB = 0x80000000u;
 
-    // ---- loader: wave w fills A blocks 8w..8w+7 (8 rows each) and B blocks
-    // 8w..8w+7 (2 rows each); per lane, offsets relative to the stage base.
-    uint32_t a_off[8], b_off[8];
-    int a_c[8], b_k[8];
-    bool a_row_ok[8], b_col_ok[8];
+    // ---- loader.  Per stage, wavefront w fills A blocks 4w..4w+3 (16 rows
+    // each) and B blocks 4w..4w+3 (2 rows each).  Lane offsets are relative
+    // to the stage's first element and do not change from stage to stage;
+    // columns past N get OOB.  The descriptors' ranges end at the last row
+    // of A and at row K of B, which zero-fills rows past M and B rows past K;
+    // A columns past K are masked per lane in the last stage.  A stage past
+    // the last one gets empty ranges: its loads write zeros and keep the
+    // wait counts of every stage alike.
+    // logical unit; the same in every block (row r of a block is lane / 4)
+    const int a_c = (lane & 3) ^ (2 * ((lane >> 4) & 1));
+    uint32_t a_off[4], b_off[4];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-        const int blk = 8 * wave + q;
-        const int r = 8 * blk + (lane >> 3);                     // A row in the tile
-        const int c = (lane & 7) ^ ((r >> 1) & 7);               // its logical unit
-        a_c[q] = c;
-        a_row_ok[q] = m0 + r < M;
-        a_off[q] = (uint32_t)(r * K + 8 * c) * 2u;
-        const int k = 2 * blk + (lane >> 5);                     // B row in the tile
-        const int u = (lane & 31) ^ (4 * (k & 3));               // its logical unit
-        b_k[q] = k;
-        b_col_ok[q] = n0 + 8 * u < N;
-        b_off[q] = (uint32_t)(k * N + 8 * u) * 2u;
+    for (int q = 0; q < 4; ++q) {
+        const int r = 16 * (4 * wave + q) + (lane >> 2);
+        a_off[q] = (uint32_t)(r * K + 8 * a_c) * 2u;
+        const int k = 2 * (4 * wave + q) + (lane >> 5);
+        const int u = (lane & 31) ^ (4 * (k & 3) + 2 * ((k >> 3) & 1));
+        b_off[q] = n0 + 8 * u < N ? (uint32_t)(k * N + 8 * u) * 2u : OOB;
     }
-    auto issue = [&](int stage) {
-        const int k0 = stage * BK;
-        uint8_t *base = lds + (stage & 1) * STAGE_BYTES;
-        const __amdgpu_buffer_rsrc_t ra =
-            make_rsrc(A + (size_t)m0 * K + k0, ((long long)(M - m0) * K - k0) * 2);
-        const __amdgpu_buffer_rsrc_t rb =
-            make_rsrc(B + (size_t)k0 * N + n0, ((long long)(K - k0) * N - n0) * 2);
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const bool ok = a_row_ok[q] && k0 + 8 * a_c[q] < K;
-            load_to_lds(ra, base + (8 * wave + q) * 1024, ok ? a_off[q] : OOB);
-        }
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const bool ok = b_col_ok[q] && k0 + b_k[q] < K;
-            load_to_lds(rb, base + A_BYTES + (8 * wave + q) * 1024, ok ? b_off[q] : OOB);
+    const bool a_full = m0 + BM <= M;                     // every row of the tile exists
+    const uint32_t a_rows_bytes = (uint32_t)(M - m0) * (uint32_t)K * 2u;   // < 2^31 when !a_full
+    const uint32_t lds_a = ring + (uint32_t)(4 * wave * 1024);
+    const uint32_t lds_b = ring + (uint32_t)(A_BYTES + 4 * wave * 1024);
+    // all eight loads of stage `st`, the i-th after MFMA slot slot_of(i)
+    struct StageLoads { intx4 ra, rb; uint32_t lds; bool a_tail; int k_left; };
+    auto prep = [&](int st) {
+        StageLoads L;
+        const int k0 = st * BK;
+        const int k_left = K - k0;                         // <= 0 past the last stage
+        const uint32_t ka = (uint32_t)k0 * 2u;
+        L.ra = rsrc_words(A + (size_t)m0 * K + k0, 0);
+        L.ra.z = k_left <= 0 ? 0 : (a_full ? 0x7fffffff : (int)(a_rows_bytes - ka));
+        L.rb = rsrc_words(B + (size_t)k0 * N + n0, 0);
+        L.rb.z = k_left >= BK ? 0x7fffffff
+                              : (k_left <= 0 ? 0 : (int)(((uint32_t)k_left * (uint32_t)N - (uint32_t)n0) * 2u));
+        L.lds = (uint32_t)((st % NBUF) * STAGE_BYTES);
+        L.a_tail = k_left < BK;
+        L.k_left = k_left;
+        return L;
+    };
+    auto load = [&](const StageLoads &L, int q) {
+        if (q < 4) {
+            const uint32_t off = (L.a_tail && 8 * a_c >= L.k_left) ? OOB : a_off[q];
+            load_to_lds(L.ra, lds_a + L.lds + (uint32_t)(q * 1024), off);
+        } else {
+            load_to_lds(L.rb, lds_b + L.lds + (uint32_t)((q - 4) * 1024), b_off[q - 4]);
         }
     };
 
-    // ---- fragment readers (per k-step s = 0..3 of a stage)
-    const int a_swz = (l32 >> 1) & 7;
-    const uint32_t a_lane = (uint32_t)(8 * (wr + l32)) * 16u;
-    uint32_t a_unit[4];
+    // ---- fragment reads.  Lane (g, s) = (lane / 16, lane % 16).
+    const int s16 = lane & 15, g = lane >> 4;
+    const int a_sw = 2 * ((s16 >> 2) & 1);
+    const uint32_t a_lane = (uint32_t)((wr + s16) * 64 + ((g ^ a_sw) * 16));
+    const uint32_t b_lane = (uint32_t)(A_BYTES + (8 * g + (s16 >> 2)) * 512 + 8 * (s16 & 1) + 2 * wc);
+    const int b_x = 4 * (s16 >> 2) + 2 * (g & 1);
+    uint32_t b_unit[8];
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
-        a_unit[s] = (uint32_t)((2 * s + g) ^ a_swz) * 16u;
-    const int sl = lane & 15, grp = lane >> 4;
-    const uint32_t b_lane = (uint32_t)(512 * (8 * (grp >> 1) + (sl >> 2)) + 8 * (sl & 1));
-    uint32_t b_unit[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int u = (wc >> 3) + 4 * j + 2 * (grp & 1) + ((sl & 3) >> 1);
-        b_unit[j] = (uint32_t)(u ^ (4 * (sl >> 2))) * 16u;
-    }
+    for (int j = 0; j < 8; ++j)
+        b_unit[j] = (uint32_t)(((2 * j + ((s16 & 3) >> 1)) ^ b_x) * 16);
 
-    halfx8 fa[4][4], fb[4][4];   // [k-step][block]
-    auto fread = [&](int stage) {
-        const uint8_t *base = lds + (stage & 1) * STAGE_BYTES;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                fa[s][i] = *reinterpret_cast<const halfx8 *>(base + a_lane + a_unit[s] + i * 32 * 128);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint8_t *bp = base + A_BYTES + b_lane + b_unit[j] + 512 * 16 * s;
-                const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4 *)(bp));
-                const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4 *)(bp + 512 * 4));
-                fb[s][j] = __builtin_bit_cast(halfx8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-            }
+    // read r (0..15) of stage `stage`: A block 0, the eight B blocks, then A
+    // blocks 1..7 (the order the next stage's first MFMAs want them).  A B
+    // block is two transposing reads, rows kb..kb+3 and kb+4..kb+7.
+    auto fread = [&](int stage, int r, halfx8 *fa, halfx8 *fb) {
+        const uint8_t *buf = lds + (stage % NBUF) * STAGE_BYTES;
+        if (r == 0 || r >= 9) {
+            const int i = r == 0 ? 0 : r - 8;
+            fa[i] = *reinterpret_cast<const halfx8 *>(buf + a_lane + i * 1024);
+        } else {
+            const int j = r - 1;
+            const uint8_t *bp = buf + b_lane + b_unit[j];
+            const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4 *)bp);
+            const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4 *)(bp + 2048));
+            fb[j] = __builtin_bit_cast(halfx8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         }
     };
 
-    floatx16 acc[4][4];
+    floatx4 acc[8][8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 8; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
+            for (int r = 0; r < 4; ++r)
                 acc[i][j][r] = 0.f;
 
+    // One stage: the 64 MFMAs of stage t from (ca, cb); the 16 fragment
+    // reads of stage t + 1 into (na, nb), one after each of the first 16
+    // MFMAs, so they complete long before the next stage needs them; the 8
+    // loads of stage t + 3, one after every sixth of the remaining MFMAs.
+    // Before it: this wavefront's loads of stage t + 1 have landed (those of
+    // t + 2 may stay in flight), and the workgroup meets at the barrier.
+    // Reads and loads past the last stage touch unused data, harmlessly.
     const int steps = (K + BK - 1) / BK;
-    issue(0);
-    for (int t = 0; t < steps; ++t) {
-        // this wave's loads of stage t are the only ones outstanding
-        __builtin_amdgcn_s_waitcnt((0) | (7 << 4) | (15 << 8));   // vmcnt(0)
-        __syncthreads();   // everyone's loads of stage t landed; stage t-1 fully read
-        fread(t);
-        if (t + 1 < steps)
-            issue(t + 1);  // into the buffer of stage t-1, read by no one any more
+    auto stage = [&](int t, halfx8 *ca, halfx8 *cb, halfx8 *na, halfx8 *nb) {
+        __builtin_amdgcn_s_waitcnt(wait_vmcnt(LOADS_PER_STAGE));
+        __builtin_amdgcn_s_barrier();
+        const StageLoads L = prep(t + 3);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
+        for (int m = 0; m < 64; ++m) {
+            const int i = m >> 3, j = m & 7;
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ca[i], cb[j], acc[i][j], 0, 0, 0);
+            if (m < 16)
+                fread(t + 1, m, na, nb);
+            if (m >= 16 && (m - 16) % 6 == 5)
+                load(L, (m - 16) / 6);
+            // keep this order: the compiler would otherwise cluster the reads
+            // and loads, and move MFMAs across the barrier
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // prologue: loads of stages 0, 1, 2, then the reads of stage 0
+    halfx8 fa0[8], fa1[8], fb0[8], fb1[8];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+    for (int st = 0; st < 3; ++st) {
+        const StageLoads L = prep(st);
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[s][i], fb[s][j], acc[i][j], 0, 0, 0);
+        for (int q = 0; q < 8; ++q)
+            load(L, q);
     }
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(2 * LOADS_PER_STAGE));
+    __builtin_amdgcn_s_barrier();
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+        fread(0, r, fa0, fb0);
+
+    for (int t = 0; t < steps; t += 2) {
+        stage(t, fa0, fb0, fa1, fb1);
+        if (t + 1 < steps)
+            stage(t + 1, fa1, fb1, fa0, fb0);
+    }
+    // no load may still be writing this workgroup's LDS when it ends
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
 
     // Epilogue: buffer stores; an element outside C gets an out-of-range lane
-    // offset, so it is dropped.
-    const int col = n0 + wc + l32;
+    // offset and is dropped.
+    const int col = n0 + wc + s16;
     const int rows_left = M - m0 - wr - 4 * g;
     const __amdgpu_buffer_rsrc_t rc =
         make_rsrc(C + (size_t)(m0 + wr) * N + n0 + wc, ((long long)(M - m0 - wr) * N - n0 - wc) * 4);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const uint32_t cv = (col + 32 * j < N) ? (uint32_t)((4 * g) * N + l32 + 32 * j) * 4u : OOB;
+    for (int j = 0; j < 8; ++j) {
+        const uint32_t cv = (col + 16 * j < N) ? (uint32_t)((4 * g) * N + s16 + 16 * j) * 4u : OOB;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 8; ++i)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int ro = 32 * i + 8 * (r >> 2) + (r & 3);
+            for (int r = 0; r < 4; ++r) {
+                const int ro = 16 * i + r;
                 const float v = acc[i][j][r];
                 __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rc, ro < rows_left ? cv : OOB,
                                                       (uint32_t)(ro * N) * 4u, 0);
@@ -407,8 +500,8 @@ hipError_t launch_cfg(const Problem &p, const gemm_plan &plan, hipStream_t s)
 hipError_t launch_mfma_f16(const Problem &p, const gemm_plan &plan, hipStream_t s)
 {
     if (plan.tile_m == 256 && plan.tile_n == 256) {
-        if (p.vec_a && p.vec_b && p.K <= (1 << 22) && p.N <= (1 << 22)) {
-            hipLaunchKernelGGL(mfma_f16_dma_kernel, dim3(plan.grid_x * plan.grid_y), dim3(256), 0, s,
+        if (direct_lds_applies(plan.tile_m, 256, p.vec_a, p.vec_b, p.N, p.K)) {
+            hipLaunchKernelGGL(mfma_f16_pipe_kernel, dim3(plan.grid_x * plan.grid_y), dim3(256), 0, s,
                                p.M, p.N, p.K, (const uint16_t *)p.A, (const uint16_t *)p.B, p.C,
                                plan.grid_y, plan.grid_x, 4);
             return hipGetLastError();

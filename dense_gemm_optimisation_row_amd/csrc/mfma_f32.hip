@@ -71,7 +71,9 @@ __global__ __launch_bounds__(64 * WM * WN) void mfma_f32_kernel(
     int tm, tn;
     dgor_tile_of_block(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    // wave-uniform, so per-wave offsets and buffer descriptors stay scalar
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wr = (wave / WN) * WTM, wc = (wave % WN) * WTN;
     const int l32 = lane & 31, g = lane >> 5;
 
@@ -213,7 +215,9 @@ __global__ __launch_bounds__(256) void mfma_f32_dma_kernel(
     int tm, tn;
     dgor_tile_of_block(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    // wave-uniform, so per-wave offsets and buffer descriptors stay scalar
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wr = (wave >> 1) * 64, wc = (wave & 1) * 64;
     const int l32 = lane & 31, g = lane >> 5;
     constexpr uint32_t OOB = 0x80000000u;
@@ -354,7 +358,7 @@ hipError_t launch_cfg(const Problem &p, const gemm_plan &plan, hipStream_t s)
 hipError_t launch_mfma_f32(const Problem &p, const gemm_plan &plan, hipStream_t s)
 {
     if (plan.tile_m == 128 && plan.tile_n == 128) {
-        if (p.vec_a && p.vec_b && p.K <= (1 << 22) && p.N <= (1 << 22)) {
+        if (direct_lds_applies(plan.tile_m, 128, p.vec_a, p.vec_b, p.N, p.K)) {
             hipLaunchKernelGGL(mfma_f32_dma_kernel, dim3(plan.grid_x * plan.grid_y), dim3(256), 0, s,
                                p.M, p.N, p.K, (const float *)p.A, (const float *)p.B, p.C,
                                plan.grid_y, plan.grid_x, 8);

@@ -120,7 +120,7 @@ typedef struct {
     int grid_x;         /* workgroups along N */
     int grid_y;         /* workgroups along M */
     int k_stages;       /* ceil(K / tile_k): k-loop trips of one workgroup */
-    int lds_stages;     /* LDS buffers per operand (1, or 2 if double-buffered) */
+    int lds_stages;     /* LDS k-stages in flight (1, 2, or a ring of 4) */
     int lds_bytes;      /* LDS per workgroup, padding included */
     int tile_bytes;     /* bytes of one unpadded A tile plus one B tile */
     int outputs_per_thread; /* C elements each thread accumulates */

@@ -1,0 +1,67 @@
+"""Checks on the generated gfx950 code of the FP16 ring kernel (CPU only:
+the kernel source is compiled to assembly with the library's own flags).
+
+The kernel issues its global->LDS loads from inline assembly that sets M0
+and is invisible to the compiler's wait counters.  That is sound only if the
+compiler keeps nothing of its own in M0 in that kernel and spills nothing
+(a spill reload is a vector-memory load whose wait would also wait on the
+in-flight tile loads), so both are checked here on the real output."""
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+from dense_gemm_optimisation_row_amd import build as hipbuild
+
+KERNEL = "mfma_f16_pipe_kernel"
+
+
+@pytest.fixture(scope="module")
+def asm(tmp_path_factory):
+    if shutil.which("hipcc") is None and not os.path.exists("/opt/rocm/bin/hipcc"):
+        pytest.skip("hipcc not available")
+    out = tmp_path_factory.mktemp("isa") / "mfma_f16.s"
+    cmd = [hipbuild.hipcc(), *hipbuild.FLAGS, "-S", "--cuda-device-only",
+           os.path.join(hipbuild.CSRC, "mfma_f16.hip"), "-o", str(out)]
+    subprocess.run(cmd, check=True, capture_output=True, text=True)
+    return out.read_text()
+
+
+def _function_body(text, name):
+    m = re.search(rf"^(_Z\S*{name}\S*):.*$", text, flags=re.M)
+    assert m, f"{name} not found in the generated code"
+    start = m.end()
+    end = text.index("s_endpgm", start)
+    return m.group(1), text[start:end]
+
+
+def test_m0_is_touched_only_by_the_load_helper(asm):
+    _, body = _function_body(asm, KERNEL)
+    inside = False
+    outside_uses = []
+    loads = 0
+    for line in body.splitlines():
+        if "ASMSTART" in line:
+            inside = True
+            continue
+        if "ASMEND" in line:
+            inside = False
+            continue
+        code = line.split(";")[0]
+        if re.search(r"\bm0\b", code) and not inside:
+            outside_uses.append(code.strip())
+        if inside and "buffer_load_dwordx4" in code and " lds" in code:
+            loads += 1
+    assert loads > 0, "no global->LDS load found inside inline assembly"
+    assert outside_uses == [], f"compiler-generated M0 accesses: {outside_uses[:5]}"
+
+
+def test_ring_kernel_spills_nothing(asm):
+    sym, _ = _function_body(asm, KERNEL)
+    priv = re.search(rf"^\s*\.set\s+{re.escape(sym)}\.private_seg_size,\s*(\d+)", asm, flags=re.M)
+    agpr = re.search(rf"^\s*\.set\s+{re.escape(sym)}\.num_agpr,\s*(\d+)", asm, flags=re.M)
+    assert priv and int(priv.group(1)) == 0, "scratch (spill) memory in use"
+    assert agpr and int(agpr.group(1)) == 256, "accumulators not held in the 256 AGPRs"
+    assert "scratch_" not in _function_body(asm, KERNEL)[1]

@@ -110,6 +110,22 @@ def test_every_matrix_core_configuration(half, shape, tile):
     assert_within(run(half, dg.AUTO, A, B), ref, tol, f"floats {shape}")
 
 
+# The large FP16 tile runs a ring of k-stages (32 deep) whose prologue and
+# drain differ with the stage count: these K give 1, 1, 2, 2, 3, 3, 4 and 5
+# stages, full and ragged, on a shape with ragged M and N that takes the tile.
+@pytest.mark.parametrize("K", [8, 32, 40, 64, 72, 96, 104, 136])
+def test_f16_large_tile_stage_counts(K):
+    M, N = 8000, 4104
+    p = dg.plan(True, M, N, K)
+    assert (p["tile_m"], p["tile_n"]) == (256, 256)
+    say("f16 large tile stages", (M, N, K))
+    A, B = ints(M, N, K, 61 + K, half=True)
+    assert_bits_equal(run(True, dg.AUTO, A, B), oracle.gemm_f16(A, B), f"ints K={K}")
+    A, B = floats(M, N, K, 62 + K, half=True)
+    ref = oracle.gemm_f16(A, B)
+    assert_within(run(True, dg.AUTO, A, B), ref, tol_f16(K, ref), f"floats K={K}")
+
+
 # ------------------------------------------------------ full-size workloads --
 
 FULL = ["f32_256", "f32_1024", "f32_1000", "f32_4097x33x777"]
