@@ -39,9 +39,11 @@ HBM_PEAK_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {
     "f32": ["dense_gemm_optimisation_row_amd/csrc/mfma_f32.hip",
-            "dense_gemm_optimisation_row_amd/csrc/common.h"],
+            "dense_gemm_optimisation_row_amd/csrc/common.h",
+            "dense_gemm_optimisation_row_amd/csrc/lds_dma.h"],
     "f16": ["dense_gemm_optimisation_row_amd/csrc/mfma_f16.hip",
-            "dense_gemm_optimisation_row_amd/csrc/common.h"],
+            "dense_gemm_optimisation_row_amd/csrc/common.h",
+            "dense_gemm_optimisation_row_amd/csrc/lds_dma.h"],
 }
 
 

@@ -142,6 +142,17 @@ int plan_f32(int variant, int M, int N, int K, const void *A, const void *B, con
         p->outputs_per_thread = 64;
         break;
     case GEMM_R6_MFMA_F32: {
+        if (dgor::f32_ring_applies(M, N, K, p->vector_a, p->vector_b)) {
+            p->tile_m = p->tile_n = dgor::kF32RingTile;
+            p->tile_k = dgor::kF32RingDepth;
+            p->threads = 256;
+            p->lds_stages = dgor::kF32RingStages;
+            p->lds_bytes = dgor::kF32RingLdsBytes;
+            p->tile_bytes = 2 * dgor::kF32RingTile * dgor::kF32RingDepth * 4;
+            p->outputs_per_thread = dgor::kF32RingTile * dgor::kF32RingTile / 256;
+            p->vector_c = 0;
+            break;
+        }
         const MfmaConfig &c = dgor::kF32Configs[pick_config(dgor::kF32Configs, M, N, true)];
         p->tile_m = c.bm;
         p->tile_n = c.bn;

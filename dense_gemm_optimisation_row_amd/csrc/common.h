@@ -79,6 +79,19 @@ inline bool direct_lds_applies(int tile_m, int top_tile, bool vec_a, bool vec_b,
     return tile_m == top_tile && vec_a && vec_b && K < (1 << 22) && N < (1 << 22);
 }
 
+// FP32 problems with both operands in 128-bit loads and at least one
+// 256 x 256 tile per compute unit take a 256 x 256 x 16 tile fed through a
+// ring of four LDS stages (lane byte offsets inside a tile stay below 2^31).
+constexpr int kF32RingTile = 256;
+constexpr int kF32RingDepth = 16;
+constexpr int kF32RingStages = 4;
+constexpr int kF32RingLdsBytes = kF32RingStages * (256 * 16 + 16 * 256) * 4;
+inline bool f32_ring_applies(int M, int N, int K, bool vec_a, bool vec_b)
+{
+    const long tiles = (long)((M + kF32RingTile - 1) / kF32RingTile) * ((N + kF32RingTile - 1) / kF32RingTile);
+    return vec_a && vec_b && K < (1 << 21) && N < (1 << 22) && tiles >= 256;
+}
+
 }  // namespace dgor
 
 // ---------------------------------------------------------------------------

@@ -20,6 +20,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "lds_dma.h"
 
 namespace dgor {
 namespace {
@@ -196,13 +197,6 @@ __global__ __launch_bounds__(64 * WM * WN) void mfma_f16_kernel(
         }
 }
 
-// Buffer descriptor over [base, base + bytes): loads past the end read as
-// zero, stores past it are dropped (bytes <= 0 gives an empty range).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, long long bytes)
-{
-    const int n = bytes <= 0 ? 0 : (bytes > 0x7fffffffLL ? 0x7fffffff : (int)bytes);
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, n, 0x00020000);
-}
 
 // ---------------------------------------------------------------------------
 // Large-tile kernel (the gfx950 path for 16-byte aligned operands):
@@ -256,49 +250,7 @@ constexpr int LOADS_PER_STAGE = 8;                   // per wavefront: 4 of A, 4
 }  // namespace pipe
 
 typedef short shortx4 __attribute__((ext_vector_type(4)));
-typedef int intx4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
-
-// The four words of a raw buffer descriptor over [base, base + bytes), as
-// make_rsrc builds it, for use as an inline-assembly operand.
-__device__ __forceinline__ intx4 rsrc_words(const void *base, long long bytes)
-{
-    const uint64_t p = (uint64_t)(uintptr_t)base;
-    const int n = bytes <= 0 ? 0 : (bytes > 0x7fffffffLL ? 0x7fffffff : (int)bytes);
-    intx4 d;
-    d.x = (int)(uint32_t)p;
-    d.y = (int)((uint32_t)(p >> 32) & 0xffffu);
-    d.z = n;
-    d.w = 0x00020000;
-    return d;
-}
-
-// One global->LDS load of 64 x 16 bytes: lane p reads 16 bytes at byte offset
-// voff of the descriptor's range (zeros when out of range) and writes them to
-// LDS address lds + 16 p.  M0 carries the LDS address; one wait state
-// separates its write from the load that reads it.  The kernel that uses
-// this keeps nothing of its own in M0 (the compiler emits no M0 access in
-// it, which a test checks on the generated code), so M0 is not restored.
-// Not tracked by the compiler's wait counters: the caller waits with vmcnt.
-__device__ __forceinline__ void load_to_lds(intx4 rsrc, uint32_t lds, uint32_t voff)
-{
-    asm volatile("s_mov_b32 m0, %0\n\t"
-                 "s_nop 0\n\t"
-                 "buffer_load_dwordx4 %1, %2, 0 offen lds"
-                 :
-                 : "s"(lds), "v"(voff), "s"(rsrc)
-                 : "memory");
-}
-
-// s_waitcnt immediate (gfx9 encoding) for vmcnt(n) alone: vmcnt bits 3:0 and
-// 15:14, expcnt (6:4) and lgkmcnt (11:8) left at their maximum.
-constexpr int wait_vmcnt(int n)
-{
-    return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);
-}
-static_assert(wait_vmcnt(0) == 0x0f70 && wait_vmcnt(8) == 0x0f78 && wait_vmcnt(24) == 0x4f78,
-              "vmcnt encoding");
 
 __global__ __launch_bounds__(256) void mfma_f16_pipe_kernel(
     int M, int N, int K, const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
@@ -306,7 +258,7 @@ __global__ __launch_bounds__(256) void mfma_f16_pipe_kernel(
 {
     using namespace pipe;
     __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
-    const uint32_t ring = (uint32_t)(uintptr_t)(lds_void *)lds;   // LDS byte address
+    const uint32_t ring = lds_address(lds);
 
     int tm, tn;
     dgor_tile_of_block(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);

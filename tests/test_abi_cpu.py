@@ -118,8 +118,13 @@ def test_grid_is_ceil_div_for_every_variant():
 
 def test_auto_picks_matrix_cores_and_tile_by_size():
     big = dg.plan(False, 4096, 4096, 4096)
-    assert big["variant"] == dg.R6_MFMA_F32 and (big["tile_m"], big["tile_n"]) == (128, 128)
-    assert big["grid_x"] * big["grid_y"] >= 512
+    # aligned operands with a tile per compute unit: the 256 x 256 ring
+    assert big["variant"] == dg.R6_MFMA_F32 and (big["tile_m"], big["tile_n"]) == (256, 256)
+    assert big["grid_x"] * big["grid_y"] == 256 and big["lds_stages"] == 4
+    # the same shape with A off 16-byte alignment: 128 x 128, two per compute unit
+    odd = dg.plan(False, 4096, 4096, 4096, A=4)
+    assert (odd["tile_m"], odd["tile_n"]) == (128, 128) and odd["vector_a"] == 0
+    assert odd["grid_x"] * odd["grid_y"] >= 512
     small = dg.plan(False, 1024, 1024, 1024)
     assert small["variant"] == dg.R6_MFMA_F32 and small["grid_x"] * small["grid_y"] >= 256
     skinny = dg.plan(False, 4097, 33, 777)

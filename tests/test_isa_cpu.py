@@ -1,11 +1,11 @@
-"""Checks on the generated gfx950 code of the FP16 ring kernel (CPU only:
-the kernel source is compiled to assembly with the library's own flags).
+"""Checks on the generated gfx950 code of the ring kernels (CPU only: the
+kernel sources are compiled to assembly with the library's own flags).
 
-The kernel issues its global->LDS loads from inline assembly that sets M0
-and is invisible to the compiler's wait counters.  That is sound only if the
-compiler keeps nothing of its own in M0 in that kernel and spills nothing
-(a spill reload is a vector-memory load whose wait would also wait on the
-in-flight tile loads), so both are checked here on the real output."""
+These kernels issue their global->LDS loads from inline assembly that sets
+M0 and is invisible to the compiler's wait counters.  That is sound only if
+the compiler keeps nothing of its own in M0 in such a kernel and spills
+nothing (a spill reload is a vector-memory load whose wait would also wait on
+the in-flight tile loads), so both are checked here on the real output."""
 import os
 import re
 import shutil
@@ -15,18 +15,19 @@ import pytest
 
 from dense_gemm_optimisation_row_amd import build as hipbuild
 
-KERNEL = "mfma_f16_pipe_kernel"
+RING_KERNELS = [("mfma_f16.hip", "mfma_f16_pipe_kernel"), ("mfma_f32.hip", "mfma_f32_ring_kernel")]
 
 
-@pytest.fixture(scope="module")
-def asm(tmp_path_factory):
+@pytest.fixture(scope="module", params=RING_KERNELS, ids=lambda v: v[1])
+def ring(request, tmp_path_factory):
     if shutil.which("hipcc") is None and not os.path.exists("/opt/rocm/bin/hipcc"):
         pytest.skip("hipcc not available")
-    out = tmp_path_factory.mktemp("isa") / "mfma_f16.s"
+    src, kernel = request.param
+    out = tmp_path_factory.mktemp("isa") / (src + ".s")
     cmd = [hipbuild.hipcc(), *hipbuild.FLAGS, "-S", "--cuda-device-only",
-           os.path.join(hipbuild.CSRC, "mfma_f16.hip"), "-o", str(out)]
+           os.path.join(hipbuild.CSRC, src), "-o", str(out)]
     subprocess.run(cmd, check=True, capture_output=True, text=True)
-    return out.read_text()
+    return out.read_text(), kernel
 
 
 def _function_body(text, name):
@@ -37,8 +38,9 @@ def _function_body(text, name):
     return m.group(1), text[start:end]
 
 
-def test_m0_is_touched_only_by_the_load_helper(asm):
-    _, body = _function_body(asm, KERNEL)
+def test_m0_is_touched_only_by_the_load_helper(ring):
+    asm, kernel = ring
+    _, body = _function_body(asm, kernel)
     inside = False
     outside_uses = []
     loads = 0
@@ -58,10 +60,11 @@ def test_m0_is_touched_only_by_the_load_helper(asm):
     assert outside_uses == [], f"compiler-generated M0 accesses: {outside_uses[:5]}"
 
 
-def test_ring_kernel_spills_nothing(asm):
-    sym, _ = _function_body(asm, KERNEL)
+def test_ring_kernel_spills_nothing(ring):
+    asm, kernel = ring
+    sym, body = _function_body(asm, kernel)
     priv = re.search(rf"^\s*\.set\s+{re.escape(sym)}\.private_seg_size,\s*(\d+)", asm, flags=re.M)
     agpr = re.search(rf"^\s*\.set\s+{re.escape(sym)}\.num_agpr,\s*(\d+)", asm, flags=re.M)
     assert priv and int(priv.group(1)) == 0, "scratch (spill) memory in use"
     assert agpr and int(agpr.group(1)) == 256, "accumulators not held in the 256 AGPRs"
-    assert "scratch_" not in _function_body(asm, KERNEL)[1]
+    assert "scratch_" not in body

@@ -84,6 +84,7 @@ def test_f16_variants_small_shapes(variant, shape):
 # Shapes large enough that the automatic choice takes each matrix-core tile
 # configuration, with ragged edges in all three dimensions.
 CONFIG_SHAPES = [
+    (False, (4000, 4100, 200), (256, 256)),   # FP32 256 x 256 ring, ragged M/N/K
     (False, (2049, 4100, 100), (128, 128)),   # FP32 128 x 128 tiles
     (False, (1000, 1000, 1000), (64, 64)),    # FP32 64 x 64 tiles
     (False, (4097, 33, 777), (32, 64)),       # FP32 narrow tiles
@@ -124,6 +125,20 @@ def test_f16_large_tile_stage_counts(K):
     A, B = floats(M, N, K, 62 + K, half=True)
     ref = oracle.gemm_f16(A, B)
     assert_within(run(True, dg.AUTO, A, B), ref, tol_f16(K, ref), f"floats K={K}")
+
+
+# The large FP32 tile runs the same kind of ring with 16-deep stages: these K
+# give 1, 1, 2, 2, 3, 3, 4 and 5 stages, full and ragged.
+@pytest.mark.parametrize("K", [4, 16, 20, 32, 36, 48, 52, 68])
+def test_f32_large_tile_stage_counts(K):
+    M, N = 4000, 4100
+    p = dg.plan(False, M, N, K)
+    assert (p["tile_m"], p["tile_n"]) == (256, 256)
+    say("f32 large tile stages", (M, N, K))
+    A, B = ints(M, N, K, 71 + K)
+    assert_bits_equal(run(False, dg.AUTO, A, B), oracle.gemm_f32(A, B), f"ints K={K}")
+    A, B = floats(M, N, K, 72 + K)
+    assert_within(run(False, dg.AUTO, A, B), oracle.gemm_f32(A, B), tol_f32(K), f"floats K={K}")
 
 
 # ------------------------------------------------------ full-size workloads --
