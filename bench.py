@@ -34,7 +34,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "GEMM TFLOP/s (2MNK/t) at FP32 4096³ and FP16-in 8192³; % of matrix peak"
-PEAK_TFLOPS = {"f32": 157.3, "f16": 2516.6}   # MI355X dense matrix peaks
+PEAK_TFLOPS = {"f32": 157.3, "f16": 2516.6, "bf16": 2516.6}   # MI355X dense matrix peaks
 HBM_PEAK_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {
@@ -238,22 +238,29 @@ def all_workloads(dg, inputs, torch, dev, stream, dev_in, wl):
     """2MNK/t and fraction of the matrix peak for every workload, each timed
     on its own after the main timed region (the headline ones reuse their
     resident inputs)."""
+    import numpy as np
+
     res = {}
+    entry = {"f32": dg.gemm_f32, "f16": dg.gemm_f16_f32acc, "bf16": dg.gemm_bf16_f32acc}
     for name, w in inputs.WORKLOADS.items():
-        half = w.dtype == "f16"
-        kind = "f16" if half else "f32"
+        kind = w.dtype
         if wl.get(kind) is not None and wl[kind].name == name and kind in dev_in:
             a, b, c = dev_in[kind]
         else:
             A, B = inputs.workload_matrices(w)
-            a, b = torch.from_numpy(A).to(dev), torch.from_numpy(B).to(dev)
+            if kind == "bf16":   # uint16 bit patterns -> bfloat16 tensors
+                a = torch.from_numpy(A.view(np.int16)).view(torch.bfloat16).to(dev)
+                b = torch.from_numpy(B.view(np.int16)).view(torch.bfloat16).to(dev)
+            else:
+                a, b = torch.from_numpy(A).to(dev), torch.from_numpy(B).to(dev)
             c = torch.empty((w.M, w.N), dtype=torch.float32, device=dev)
-        f = dg.gemm_f16_f32acc if half else dg.gemm_f32
+            del A, B
+        f = entry[kind]
         est = _time_calls(lambda: f(a, b, c, stream), torch, stream, 3)
         reps = max(3, min(200, int(100.0 / max(est, 1e-3))))
         ms = _time_calls(lambda: f(a, b, c, stream), torch, stream, reps)
         tf = w.flops / (ms * 1e-3) / 1e12
-        p = dg.plan(half, w.M, w.N, w.K)
+        p = dg.plan(kind, w.M, w.N, w.K)
         res[name] = {"M": w.M, "N": w.N, "K": w.K, "dtype": w.dtype, "ms": round(ms, 5),
                      "tflops": round(tf, 3), "frac_of_peak": round(tf / PEAK_TFLOPS[kind], 4),
                      "kernel": dg.variant_name(p["variant"]), "tile": [p["tile_m"], p["tile_n"]]}

@@ -4,7 +4,8 @@ Two layers:
 
 * ``raw_*`` functions pass integers (device addresses, sizes, a stream
   handle) straight to the library and return its status code;
-* ``gemm_f32`` / ``gemm_f16_f32acc`` (and ``*_variant``) take torch tensors
+* ``gemm_f32`` / ``gemm_f16_f32acc`` / ``gemm_bf16_f32acc`` (and
+  ``*_variant``) take torch tensors
   that already live on the GPU, check shape / dtype / contiguity, call the
   library on the tensors' current stream and raise ``GemmError`` on a
   non-zero status.
@@ -34,9 +35,25 @@ R0_NAIVE, R1_LDS_TILED, R2_VECTOR_LOADS, R3_LDS_PADDED = 0, 1, 2, 3
 R4_DOUBLE_BUFFER, R5_REGISTER_BLOCKED, R6_MFMA_F32, R7_MFMA_F16 = 4, 5, 6, 7
 F32_VARIANTS = (0, 1, 2, 3, 4, 5, 6)
 F16_VARIANTS = (0, 7)
+BF16_VARIANTS = (0, 7)
 
-EXPORTS = ("gemm_f32", "gemm_f16_f32acc", "gemm_f32_variant", "gemm_f16_f32acc_variant",
-           "gemm_f32_plan", "gemm_f16_f32acc_plan", "gemm_status_string", "gemm_variant_name")
+EXPORTS = ("gemm_f32", "gemm_f16_f32acc", "gemm_bf16_f32acc",
+           "gemm_f32_variant", "gemm_f16_f32acc_variant", "gemm_bf16_f32acc_variant",
+           "gemm_f32_plan", "gemm_f16_f32acc_plan", "gemm_bf16_f32acc_plan",
+           "gemm_status_string", "gemm_variant_name")
+
+# Entry-point name stem per input format.
+_STEM = {"f32": "gemm_f32", "f16": "gemm_f16_f32acc", "bf16": "gemm_bf16_f32acc"}
+
+
+def kind_of(kind) -> str:
+    """Input format of a call: "f32", "f16" or "bf16"; a bool means f16 (True)
+    or f32 (False)."""
+    if isinstance(kind, bool):
+        return "f16" if kind else "f32"
+    if kind in _STEM:
+        return kind
+    raise ValueError(f"unknown input format {kind!r}")
 
 
 class GemmError(RuntimeError):
@@ -68,16 +85,14 @@ def load(path: str = LIB_PATH):
                 "`python -m dense_gemm_optimisation_row_amd.build`")
         lib = ctypes.CDLL(path)
         i, p = ctypes.c_int, ctypes.c_void_p
-        for name in ("gemm_f32", "gemm_f16_f32acc"):
-            f = getattr(lib, name)
+        for stem in _STEM.values():
+            f = getattr(lib, stem)
             f.argtypes = [i, i, i, p, p, p, p]
             f.restype = i
-        for name in ("gemm_f32_variant", "gemm_f16_f32acc_variant"):
-            f = getattr(lib, name)
+            f = getattr(lib, stem + "_variant")
             f.argtypes = [i, i, i, i, p, p, p, p]
             f.restype = i
-        for name in ("gemm_f32_plan", "gemm_f16_f32acc_plan"):
-            f = getattr(lib, name)
+            f = getattr(lib, stem + "_plan")
             f.argtypes = [i, i, i, i, p, p, p, ctypes.POINTER(Plan)]
             f.restype = i
         lib.gemm_status_string.argtypes = [i]
@@ -98,18 +113,18 @@ def variant_name(variant: int) -> str:
 
 # ------------------------------------------------------------- raw layer --
 
-def raw_gemm(half: bool, variant: int | None, M: int, N: int, K: int,
+def raw_gemm(kind, variant: int | None, M: int, N: int, K: int,
              A: int | None, B: int | None, C: int | None, stream: int | None) -> int:
-    """Call the library with plain integers; returns the status code."""
+    """Call the library with plain integers; returns the status code.
+    ``kind`` is the input format ("f32", "f16", "bf16", or a bool for f16)."""
     lib = load()
+    stem = _STEM[kind_of(kind)]
     if variant is None:
-        f = lib.gemm_f16_f32acc if half else lib.gemm_f32
-        return int(f(M, N, K, A, B, C, stream))
-    f = lib.gemm_f16_f32acc_variant if half else lib.gemm_f32_variant
-    return int(f(variant, M, N, K, A, B, C, stream))
+        return int(getattr(lib, stem)(M, N, K, A, B, C, stream))
+    return int(getattr(lib, stem + "_variant")(variant, M, N, K, A, B, C, stream))
 
 
-def plan(half: bool, M: int, N: int, K: int, variant: int = AUTO,
+def plan(kind, M: int, N: int, K: int, variant: int = AUTO,
          A: int = 0, B: int = 0, C: int = 0) -> dict:
     """Launch plan for these arguments (host arithmetic only; no GPU needed).
 
@@ -117,7 +132,7 @@ def plan(half: bool, M: int, N: int, K: int, variant: int = AUTO,
     """
     lib = load()
     out = Plan()
-    f = lib.gemm_f16_f32acc_plan if half else lib.gemm_f32_plan
+    f = getattr(lib, _STEM[kind_of(kind)] + "_plan")
     rc = f(variant, M, N, K, A or None, B or None, C or None, ctypes.byref(out))
     if rc != GEMM_OK:
         raise GemmError(rc, "plan")
@@ -159,14 +174,16 @@ def _ptr(t):
     return t.data_ptr() if t.numel() else None
 
 
-def _call(half, variant, A, B, C, stream):
+def _call(kind, variant, A, B, C, stream):
     import torch
-    M, N, K, C = _check(A, B, C, torch.float16 if half else torch.float32)
+    kind = kind_of(kind)
+    dtype = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[kind]
+    M, N, K, C = _check(A, B, C, dtype)
     with torch.cuda.device(A.device):
-        rc = raw_gemm(half, variant, M, N, K, _ptr(A), _ptr(B), _ptr(C),
+        rc = raw_gemm(kind, variant, M, N, K, _ptr(A), _ptr(B), _ptr(C),
                       _stream_handle(A.device, stream))
     if rc != GEMM_OK:
-        raise GemmError(rc, "gemm_f16_f32acc" if half else "gemm_f32")
+        raise GemmError(rc, _STEM[kind])
     return C
 
 
@@ -188,3 +205,13 @@ def gemm_f32_variant(variant, A, B, C=None, stream=None):
 def gemm_f16_f32acc_variant(variant, A, B, C=None, stream=None):
     """``gemm_f16_f32acc`` with the kernel variant (rung) forced."""
     return _call(True, int(variant), A, B, C, stream)
+
+
+def gemm_bf16_f32acc(A, B, C=None, stream=None):
+    """C = A x B for bfloat16 GPU tensors with FP32 accumulation and output."""
+    return _call("bf16", None, A, B, C, stream)
+
+
+def gemm_bf16_f32acc_variant(variant, A, B, C=None, stream=None):
+    """``gemm_bf16_f32acc`` with the kernel variant (rung) forced."""
+    return _call("bf16", int(variant), A, B, C, stream)

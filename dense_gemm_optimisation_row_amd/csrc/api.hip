@@ -230,10 +230,14 @@ bool null_with_extent(const void *A, const void *B, const void *C, int M, int N,
     return (a_needed && !A) || (b_needed && !B) || (c_needed && !C);
 }
 
-int run(bool half, int variant, int M, int N, int K, const void *A, const void *B, float *C,
+// Input format of a call: binary32, binary16 or bfloat16.
+enum class In { F32, F16, BF16 };
+
+int run(In in, int variant, int M, int N, int K, const void *A, const void *B, float *C,
         void *stream)
 {
     gemm_plan plan;
+    const bool half = in != In::F32;
     const int rc = half ? plan_f16(variant, M, N, K, A, B, C, &plan)
                         : plan_f32(variant, M, N, K, A, B, C, &plan);
     if (rc != GEMM_OK)
@@ -251,8 +255,8 @@ int run(bool half, int variant, int M, int N, int K, const void *A, const void *
     if (K == 0)
         err = dgor::launch_zero_fill(p, s);
     else if (half)
-        err = plan.variant == GEMM_R7_MFMA_F16 ? dgor::launch_mfma_f16(p, plan, s)
-                                               : dgor::launch_naive_f16(p, plan, s);
+        err = plan.variant == GEMM_R7_MFMA_F16 ? dgor::launch_mfma_f16(p, plan, s, in == In::BF16)
+                                               : dgor::launch_naive_f16(p, plan, s, in == In::BF16);
     else
         err = plan.variant == GEMM_R6_MFMA_F32 ? dgor::launch_mfma_f32(p, plan, s)
                                                : dgor::launch_ladder_f32(p, plan, s);
@@ -265,25 +269,37 @@ extern "C" {
 
 int gemm_f32(int M, int N, int K, const float *A, const float *B, float *C, void *stream)
 {
-    return run(false, GEMM_VARIANT_AUTO, M, N, K, A, B, C, stream);
+    return run(In::F32, GEMM_VARIANT_AUTO, M, N, K, A, B, C, stream);
 }
 
 int gemm_f16_f32acc(int M, int N, int K, const uint16_t *A, const uint16_t *B, float *C,
                     void *stream)
 {
-    return run(true, GEMM_VARIANT_AUTO, M, N, K, A, B, C, stream);
+    return run(In::F16, GEMM_VARIANT_AUTO, M, N, K, A, B, C, stream);
+}
+
+int gemm_bf16_f32acc(int M, int N, int K, const uint16_t *A, const uint16_t *B, float *C,
+                     void *stream)
+{
+    return run(In::BF16, GEMM_VARIANT_AUTO, M, N, K, A, B, C, stream);
 }
 
 int gemm_f32_variant(int variant, int M, int N, int K, const float *A, const float *B,
                      float *C, void *stream)
 {
-    return run(false, variant, M, N, K, A, B, C, stream);
+    return run(In::F32, variant, M, N, K, A, B, C, stream);
 }
 
 int gemm_f16_f32acc_variant(int variant, int M, int N, int K, const uint16_t *A,
                             const uint16_t *B, float *C, void *stream)
 {
-    return run(true, variant, M, N, K, A, B, C, stream);
+    return run(In::F16, variant, M, N, K, A, B, C, stream);
+}
+
+int gemm_bf16_f32acc_variant(int variant, int M, int N, int K, const uint16_t *A,
+                             const uint16_t *B, float *C, void *stream)
+{
+    return run(In::BF16, variant, M, N, K, A, B, C, stream);
 }
 
 int gemm_f32_plan(int variant, int M, int N, int K, const float *A, const float *B,
@@ -294,6 +310,12 @@ int gemm_f32_plan(int variant, int M, int N, int K, const float *A, const float 
 
 int gemm_f16_f32acc_plan(int variant, int M, int N, int K, const uint16_t *A,
                          const uint16_t *B, const float *C, gemm_plan *plan)
+{
+    return plan_f16(variant, M, N, K, A, B, C, plan);
+}
+
+int gemm_bf16_f32acc_plan(int variant, int M, int N, int K, const uint16_t *A,
+                          const uint16_t *B, const float *C, gemm_plan *plan)
 {
     return plan_f16(variant, M, N, K, A, B, C, plan);
 }
@@ -323,7 +345,7 @@ const char *gemm_variant_name(int variant)
     case GEMM_R4_DOUBLE_BUFFER: return "R4 double-buffered LDS";
     case GEMM_R5_REGISTER_BLOCKED: return "R5 register-blocked 8x8";
     case GEMM_R6_MFMA_F32: return "R6 FP32 MFMA";
-    case GEMM_R7_MFMA_F16: return "R7 FP16 MFMA, FP32 accumulate";
+    case GEMM_R7_MFMA_F16: return "R7 16-bit MFMA, FP32 accumulate";
     default: return "unknown variant";
     }
 }

@@ -24,9 +24,11 @@ struct Problem {
 // and returns the launch status.  Shapes were validated by the caller.
 hipError_t launch_zero_fill(const Problem &p, hipStream_t stream);
 hipError_t launch_ladder_f32(const Problem &p, const gemm_plan &plan, hipStream_t stream);
-hipError_t launch_naive_f16(const Problem &p, const gemm_plan &plan, hipStream_t stream);
+// The 16-bit-input launchers take the input format: binary16 (bf16 false) or
+// bfloat16 (bf16 true); tiles and data movement are the same for both.
+hipError_t launch_naive_f16(const Problem &p, const gemm_plan &plan, hipStream_t stream, bool bf16);
 hipError_t launch_mfma_f32(const Problem &p, const gemm_plan &plan, hipStream_t stream);
-hipError_t launch_mfma_f16(const Problem &p, const gemm_plan &plan, hipStream_t stream);
+hipError_t launch_mfma_f16(const Problem &p, const gemm_plan &plan, hipStream_t stream, bool bf16);
 
 // LDS padding of the ladder rungs, in floats per row.  R3 and R4 pad each
 // A row of their 16 x 64 tile by one float, moving consecutive rows to

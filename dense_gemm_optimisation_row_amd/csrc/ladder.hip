@@ -74,21 +74,29 @@ __global__ __launch_bounds__(256) void naive_f32(int M, int N, int K,
     }
 }
 
-// Binary16 operands, FP32 accumulation: each product of two halves is exact
-// in FP32, so this computes the same sum as the FP16 matrix-core kernel.
-__global__ __launch_bounds__(256) void naive_f16(int M, int N, int K,
-                                                 const _Float16 *__restrict__ A,
-                                                 const _Float16 *__restrict__ B,
-                                                 float *__restrict__ C)
+// 16-bit operands (binary16 or bfloat16 bit patterns), FP32 accumulation:
+// each product of two 16-bit values is exact in FP32, so this computes the
+// same sum as the 16-bit matrix-core kernels.  A bfloat16 pattern is the high
+// half of the binary32 with the same value.
+__device__ __forceinline__ float widen16(uint16_t h, bool bf16)
+{
+    return bf16 ? __uint_as_float((uint32_t)h << 16) : (float)__builtin_bit_cast(_Float16, h);
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void naive_16(int M, int N, int K,
+                                                const uint16_t *__restrict__ A,
+                                                const uint16_t *__restrict__ B,
+                                                float *__restrict__ C)
 {
     const int row = blockIdx.y * 16 + threadIdx.y;
     const int col = blockIdx.x * 16 + threadIdx.x;
     if (row < M && col < N) {
-        const _Float16 *a = A + (size_t)row * K;
-        const _Float16 *b = B + col;
+        const uint16_t *a = A + (size_t)row * K;
+        const uint16_t *b = B + col;
         float sum = 0.f;
         for (int k = 0; k < K; ++k)
-            sum = fmaf((float)a[k], (float)b[(size_t)k * N], sum);
+            sum = fmaf(widen16(a[k], BF16), widen16(b[(size_t)k * N], BF16), sum);
         C[(size_t)row * N + col] = sum;
     }
 }
@@ -302,10 +310,15 @@ hipError_t launch_zero_fill(const Problem &p, hipStream_t stream)
     return hipGetLastError();
 }
 
-hipError_t launch_naive_f16(const Problem &p, const gemm_plan &plan, hipStream_t stream)
+hipError_t launch_naive_f16(const Problem &p, const gemm_plan &plan, hipStream_t stream, bool bf16)
 {
-    hipLaunchKernelGGL(naive_f16, dim3(plan.grid_x, plan.grid_y), dim3(16, 16), 0, stream,
-                       p.M, p.N, p.K, (const _Float16 *)p.A, (const _Float16 *)p.B, p.C);
+    const uint16_t *A = (const uint16_t *)p.A, *B = (const uint16_t *)p.B;
+    if (bf16)
+        hipLaunchKernelGGL(naive_16<true>, dim3(plan.grid_x, plan.grid_y), dim3(16, 16), 0, stream,
+                           p.M, p.N, p.K, A, B, p.C);
+    else
+        hipLaunchKernelGGL(naive_16<false>, dim3(plan.grid_x, plan.grid_y), dim3(16, 16), 0, stream,
+                           p.M, p.N, p.K, A, B, p.C);
     return hipGetLastError();
 }
 

@@ -28,6 +28,33 @@ namespace {
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// The matrix-core operation of each 16-bit input format.  Fragments travel
+// as eight 16-bit patterns (halfx8) whatever the format; only the MFMA
+// differs (binary16: v_mfma_f32_*_f16, bfloat16: v_mfma_f32_*_bf16).
+struct OpF16 {
+    static __device__ __forceinline__ floatx4 mfma16(halfx8 a, halfx8 b, floatx4 c)
+    {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ floatx16 mfma32(halfx8 a, halfx8 b, floatx16 c)
+    {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
+};
+struct OpBF16 {
+    static __device__ __forceinline__ floatx4 mfma16(halfx8 a, halfx8 b, floatx4 c)
+    {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ floatx16 mfma32(halfx8 a, halfx8 b, floatx16 c)
+    {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    }
+};
 
 // Eight halves of row r from column c of a rows x cols row-major binary16
 // matrix, zero outside it.  VEC: rows start 16-byte aligned and cols % 8 == 0.
@@ -72,7 +99,7 @@ __device__ __forceinline__ void pair_words(const uint4 &x, const uint4 &y, uint4
 // BM x BN workgroup tile, BK-deep k-stages, WM x WN wavefronts each owning a
 // (BM/WM) x (BN/WN) tile of 32 x 32 MFMA blocks.  A rows in LDS hold BK
 // halves plus kF16PadA; pair rows of B hold BN words plus kF16PadB.
-template <int BM, int BN, int BK, int WM, int WN, bool VEC_A, bool VEC_B>
+template <class Op, int BM, int BN, int BK, int WM, int WN, bool VEC_A, bool VEC_B>
 __global__ __launch_bounds__(64 * WM * WN) void mfma_f16_kernel(
     int M, int N, int K, const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     float *__restrict__ C, int tiles_m, int tiles_n, int group_m)
@@ -164,7 +191,7 @@ __global__ __launch_bounds__(64 * WM * WN) void mfma_f16_kernel(
             for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+                    acc[i][j] = Op::mfma32(a[i], b[j], acc[i][j]);
         }
     };
 
@@ -252,6 +279,7 @@ constexpr int LOADS_PER_STAGE = 8;                   // per wavefront: 4 of A, 4
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
 
+template <class Op>
 __global__ __launch_bounds__(256) void mfma_f16_pipe_kernel(
     int M, int N, int K, const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     float *__restrict__ C, int tiles_m, int tiles_n, int group_m)
@@ -371,7 +399,7 @@ __global__ __launch_bounds__(256) void mfma_f16_pipe_kernel(
 #pragma unroll
         for (int m = 0; m < 64; ++m) {
             const int i = m >> 3, j = m & 7;
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ca[i], cb[j], acc[i][j], 0, 0, 0);
+            acc[i][j] = Op::mfma16(ca[i], cb[j], acc[i][j]);
             if (m < 16)
                 fread(t + 1, m, na, nb);
             if (m >= 16 && (m - 16) % 6 == 5)
@@ -426,45 +454,51 @@ __global__ __launch_bounds__(256) void mfma_f16_pipe_kernel(
     }
 }
 
-template <int BM, int BN, int BK, int WM, int WN>
+template <class Op, int BM, int BN, int BK, int WM, int WN>
 hipError_t launch_cfg(const Problem &p, const gemm_plan &plan, hipStream_t s)
 {
     const uint16_t *A = (const uint16_t *)p.A, *B = (const uint16_t *)p.B;
     const dim3 grid(plan.grid_x * plan.grid_y), blk(64 * WM * WN);
     const int gm = 4;
     if (p.vec_a && p.vec_b)
-        hipLaunchKernelGGL((mfma_f16_kernel<BM, BN, BK, WM, WN, true, true>), grid, blk, 0, s,
+        hipLaunchKernelGGL((mfma_f16_kernel<Op, BM, BN, BK, WM, WN, true, true>), grid, blk, 0, s,
                            p.M, p.N, p.K, A, B, p.C, plan.grid_y, plan.grid_x, gm);
     else if (p.vec_a)
-        hipLaunchKernelGGL((mfma_f16_kernel<BM, BN, BK, WM, WN, true, false>), grid, blk, 0, s,
+        hipLaunchKernelGGL((mfma_f16_kernel<Op, BM, BN, BK, WM, WN, true, false>), grid, blk, 0, s,
                            p.M, p.N, p.K, A, B, p.C, plan.grid_y, plan.grid_x, gm);
     else if (p.vec_b)
-        hipLaunchKernelGGL((mfma_f16_kernel<BM, BN, BK, WM, WN, false, true>), grid, blk, 0, s,
+        hipLaunchKernelGGL((mfma_f16_kernel<Op, BM, BN, BK, WM, WN, false, true>), grid, blk, 0, s,
                            p.M, p.N, p.K, A, B, p.C, plan.grid_y, plan.grid_x, gm);
     else
-        hipLaunchKernelGGL((mfma_f16_kernel<BM, BN, BK, WM, WN, false, false>), grid, blk, 0, s,
+        hipLaunchKernelGGL((mfma_f16_kernel<Op, BM, BN, BK, WM, WN, false, false>), grid, blk, 0, s,
                            p.M, p.N, p.K, A, B, p.C, plan.grid_y, plan.grid_x, gm);
     return hipGetLastError();
 }
 
-}  // namespace
-
-hipError_t launch_mfma_f16(const Problem &p, const gemm_plan &plan, hipStream_t s)
+template <class Op>
+hipError_t launch_op(const Problem &p, const gemm_plan &plan, hipStream_t s)
 {
     if (plan.tile_m == 256 && plan.tile_n == 256) {
         if (direct_lds_applies(plan.tile_m, 256, p.vec_a, p.vec_b, p.N, p.K)) {
-            hipLaunchKernelGGL(mfma_f16_pipe_kernel, dim3(plan.grid_x * plan.grid_y), dim3(256), 0, s,
+            hipLaunchKernelGGL(mfma_f16_pipe_kernel<Op>, dim3(plan.grid_x * plan.grid_y), dim3(256), 0, s,
                                p.M, p.N, p.K, (const uint16_t *)p.A, (const uint16_t *)p.B, p.C,
                                plan.grid_y, plan.grid_x, 4);
             return hipGetLastError();
         }
-        return launch_cfg<256, 256, 32, 2, 2>(p, plan, s);
+        return launch_cfg<Op, 256, 256, 32, 2, 2>(p, plan, s);
     }
     if (plan.tile_m == 128 && plan.tile_n == 128)
-        return launch_cfg<128, 128, 32, 2, 2>(p, plan, s);
+        return launch_cfg<Op, 128, 128, 32, 2, 2>(p, plan, s);
     if (plan.tile_m == 64 && plan.tile_n == 64)
-        return launch_cfg<64, 64, 32, 1, 2>(p, plan, s);
+        return launch_cfg<Op, 64, 64, 32, 1, 2>(p, plan, s);
     return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_mfma_f16(const Problem &p, const gemm_plan &plan, hipStream_t s, bool bf16)
+{
+    return bf16 ? launch_op<OpBF16>(p, plan, s) : launch_op<OpF16>(p, plan, s);
 }
 
 }  // namespace dgor

@@ -13,7 +13,9 @@ from one generator per (workload, variant).  Distributions:
   with K <= 8192 is an integer of magnitude <= 16*K < 2^24, exact in binary32
   whatever the summation order;
 * for binary16 inputs the binary32 draw is rounded once to binary16 by numpy
-  (round to nearest even) and both sides read the same bits.
+  (round to nearest even) and both sides read the same bits;
+* for bfloat16 inputs the binary32 draw is rounded once to its upper 16 bits
+  (round to nearest, ties to even), given as uint16 bit patterns.
 """
 from __future__ import annotations
 
@@ -28,7 +30,7 @@ class Workload:
     M: int
     N: int
     K: int
-    dtype: str          # "f32" or "f16" (input type; the output is always f32)
+    dtype: str          # "f32", "f16" or "bf16" (input type; the output is always f32)
     dist: str           # "uniform" or "normal"
     seed: int           # seed of the main draw
     int_seed: int       # seed of the small-integer variant
@@ -40,7 +42,7 @@ class Workload:
 
 # The workloads: square FP32 at 256 and 1024 (1024 is the size the pages time),
 # ragged FP32 shapes that exercise edge masking, FP32 4096 with normal inputs,
-# and FP16-input 8192.
+# FP16-input 8192, and BF16-input 8192 (the bfloat16 entry point).
 WORKLOADS = {
     w.name: w for w in [
         Workload("f32_256", 256, 256, 256, "f32", "uniform", 1001, 2001),
@@ -49,6 +51,7 @@ WORKLOADS = {
         Workload("f32_4097x33x777", 4097, 33, 777, "f32", "uniform", 1004, 2004),
         Workload("f32_4096", 4096, 4096, 4096, "f32", "normal", 1005, 2005),
         Workload("f16_8192", 8192, 8192, 8192, "f16", "uniform", 1006, 2006),
+        Workload("bf16_8192", 8192, 8192, 8192, "bf16", "uniform", 1007, 2007),
     ]
 }
 
@@ -63,12 +66,22 @@ def _draw(rng: np.random.Generator, shape, dist: str) -> np.ndarray:
     raise ValueError(f"unknown distribution {dist!r}")
 
 
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round finite float32 values to bfloat16 (nearest, ties to even); return
+    the 16-bit patterns as uint16.  Adding 0x7FFF plus the lowest kept bit and
+    truncating rounds the discarded 16 bits to nearest with ties to even."""
+    bits = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    keep_lsb = (bits >> np.uint64(16)) & np.uint64(1)
+    return ((bits + np.uint64(0x7FFF) + keep_lsb) >> np.uint64(16)).astype(np.uint16)
+
+
 def matrices(M: int, N: int, K: int, seed: int, dist: str = "uniform",
              dtype: str = "f32"):
     """Return (A, B): A is M x K, B is K x N, C-contiguous numpy arrays.
 
     ``dtype`` "f32" gives float32; "f16" gives float16 (the float32 draw
-    rounded once to binary16).
+    rounded once to binary16); "bf16" gives uint16 bfloat16 bit patterns (the
+    float32 draw rounded once to bfloat16).
     """
     rng = np.random.default_rng(seed)
     A = _draw(rng, (M, K), dist)
@@ -76,6 +89,9 @@ def matrices(M: int, N: int, K: int, seed: int, dist: str = "uniform",
     if dtype == "f16":
         A = A.astype(np.float16)
         B = B.astype(np.float16)
+    elif dtype == "bf16":
+        A = to_bf16_bits(A)
+        B = to_bf16_bits(B)
     elif dtype != "f32":
         raise ValueError(f"unknown dtype {dtype!r}")
     return np.ascontiguousarray(A), np.ascontiguousarray(B)

@@ -64,7 +64,8 @@ typedef enum {
  *   R5 register-blocked 8x8 outputs per thread  (Lesson 8 section 18;
  *                                                 SGEMM journey Level 5)
  *   R6 FP32 matrix-core (MFMA) tiles             (Lesson 8 section 21)
- *   R7 FP16 matrix-core (MFMA) tiles, FP32 acc.  (SGEMM journey Level 6)
+ *   R7 16-bit-input matrix-core (MFMA) tiles,     (SGEMM journey Level 6;
+ *      FP32 accumulation (binary16 or bfloat16)   Lesson 8 section 22)
  * GEMM_VARIANT_AUTO lets the library choose from the shape and alignment.
  */
 typedef enum {
@@ -91,15 +92,27 @@ int gemm_f32(int M, int N, int K, const float *A, const float *B, float *C,
 int gemm_f16_f32acc(int M, int N, int K, const uint16_t *A, const uint16_t *B,
                     float *C, void *stream);
 
+/* bfloat16 inputs (raw 16-bit patterns: the high half of a binary32, 8
+ * exponent and 7 fraction bits), exact products, FP32 accumulation and FP32
+ * output -- one of the input formats "Lesson 8: how a GPU does matrix
+ * multiply", section 22, lists for matrix units.  Same tiles as the binary16
+ * path with the bfloat16 matrix-core instructions.  Chooses R7 in practice. */
+int gemm_bf16_f32acc(int M, int N, int K, const uint16_t *A, const uint16_t *B,
+                     float *C, void *stream);
+
 /* Same operations with the variant forced (GEMM_VARIANT_AUTO allowed), for
  * benchmarking and testing every rung.  gemm_f32_variant accepts R0..R6;
- * gemm_f16_f32acc_variant accepts R0 and R7.  Any other value ->
- * GEMM_ERR_INVALID_VARIANT.  Same semantics and errors otherwise. */
+ * gemm_f16_f32acc_variant and gemm_bf16_f32acc_variant accept R0 and R7.
+ * Any other value -> GEMM_ERR_INVALID_VARIANT.  Same semantics and errors
+ * otherwise. */
 int gemm_f32_variant(int variant, int M, int N, int K, const float *A,
                      const float *B, float *C, void *stream);
 int gemm_f16_f32acc_variant(int variant, int M, int N, int K,
                             const uint16_t *A, const uint16_t *B, float *C,
                             void *stream);
+int gemm_bf16_f32acc_variant(int variant, int M, int N, int K,
+                             const uint16_t *A, const uint16_t *B, float *C,
+                             void *stream);
 
 /*
  * Launch plan: what a call with these arguments would launch.  Pure host
@@ -133,6 +146,8 @@ int gemm_f32_plan(int variant, int M, int N, int K, const float *A,
                   const float *B, const float *C, gemm_plan *plan);
 int gemm_f16_f32acc_plan(int variant, int M, int N, int K, const uint16_t *A,
                          const uint16_t *B, const float *C, gemm_plan *plan);
+int gemm_bf16_f32acc_plan(int variant, int M, int N, int K, const uint16_t *A,
+                          const uint16_t *B, const float *C, gemm_plan *plan);
 
 /* Static, NUL-terminated descriptions; never NULL ("unknown ..." for values
  * outside the enums). */

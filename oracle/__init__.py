@@ -46,15 +46,17 @@ def configure(lib):
     p = ctypes.c_void_p
     i = ctypes.c_int
     i64 = ctypes.c_int64
-    lib.oracle_f16_to_f64.argtypes = [ctypes.c_uint16]
-    lib.oracle_f16_to_f64.restype = ctypes.c_double
+    for name in ("oracle_f16_to_f64", "oracle_bf16_to_f64"):
+        f = getattr(lib, name)
+        f.argtypes = [ctypes.c_uint16]
+        f.restype = ctypes.c_double
     lib.oracle_threads.argtypes = [i]
     lib.oracle_threads.restype = i
-    for name in ("oracle_gemm_f32", "oracle_gemm_f16"):
+    for name in ("oracle_gemm_f32", "oracle_gemm_f16", "oracle_gemm_bf16"):
         f = getattr(lib, name)
         f.argtypes = [i, i, i, p, p, p, i]
         f.restype = i
-    for name in ("oracle_gemm_f32_at", "oracle_gemm_f16_at"):
+    for name in ("oracle_gemm_f32_at", "oracle_gemm_f16_at", "oracle_gemm_bf16_at"):
         f = getattr(lib, name)
         f.argtypes = [i, i, i, p, p, i64, p, p, p, i]
         f.restype = i
@@ -94,6 +96,11 @@ def f16_to_f64(bits: int) -> float:
     return float(_load().oracle_f16_to_f64(int(bits) & 0xFFFF))
 
 
+def bf16_to_f64(bits: int) -> float:
+    """Decode one bfloat16 bit pattern exactly."""
+    return float(_load().oracle_bf16_to_f64(int(bits) & 0xFFFF))
+
+
 def gemm_f32(A: np.ndarray, B: np.ndarray, out: np.ndarray | None = None,
              nthreads: int = 0) -> np.ndarray:
     """C = A x B for float32 A (M x K), B (K x N); binary64 sum, binary32 result.
@@ -130,6 +137,21 @@ def gemm_f16(A: np.ndarray, B: np.ndarray, out: np.ndarray | None = None,
     return C
 
 
+def gemm_bf16(A: np.ndarray, B: np.ndarray, out: np.ndarray | None = None,
+              nthreads: int = 0) -> np.ndarray:
+    """C = A x B for bfloat16 A, B given as uint16 bit patterns."""
+    A, B = _check_inputs(A, B, np.uint16)
+    M, K = A.shape
+    N = B.shape[1]
+    C = np.empty((M, N), np.float32) if out is None else out
+    if C.shape != (M, N) or C.dtype != np.float32 or not C.flags.c_contiguous:
+        raise ValueError("out must be a contiguous float32 M x N array")
+    rc = _load().oracle_gemm_bf16(M, N, K, _ptr(A), _ptr(B), _ptr(C), nthreads)
+    if rc != 0:
+        raise RuntimeError(f"oracle_gemm_bf16 failed ({rc})")
+    return C
+
+
 def _at(fname, A, B, rows, cols, nthreads):
     M, K = A.shape
     N = B.shape[1]
@@ -157,3 +179,9 @@ def gemm_f16_at(A, B, rows, cols, nthreads: int = 0) -> np.ndarray:
     B = np.ascontiguousarray(B).view(np.uint16) if np.asarray(B).dtype == np.float16 else B
     A, B = _check_inputs(A, B, np.uint16)
     return _at("oracle_gemm_f16_at", A, B, rows, cols, nthreads)
+
+
+def gemm_bf16_at(A, B, rows, cols, nthreads: int = 0) -> np.ndarray:
+    """C[rows[t], cols[t]] of A x B for bfloat16 bit-pattern inputs, one dot product each."""
+    A, B = _check_inputs(A, B, np.uint16)
+    return _at("oracle_gemm_bf16_at", A, B, rows, cols, nthreads)

@@ -32,8 +32,14 @@
  * identity and permutation products, rank-1 closed forms, K = 1 against
  * numpy's correctly rounded binary32 product, brute force against exact
  * rational sums on all shapes up to 6x6x6, numpy's binary64 matmul within
- * one binary32 ulp, exact integer products, thread-count determinism, and
- * the binary16 decoder against numpy over all 65536 bit patterns.
+ * one binary32 ulp, exact integer products, thread-count determinism, the
+ * binary16 decoder against numpy and the bfloat16 decoder against torch over
+ * all 65536 bit patterns each.
+ *
+ * bfloat16 inputs ("Lesson 8: how a GPU does matrix multiply", section 22,
+ * lists it among the matrix-unit input formats) are handled exactly like
+ * binary16 ones: each value is decoded exactly, every product of two of them
+ * is exact in binary64, and the same sum is formed.
  */
 #include <math.h>
 #include <stddef.h>
@@ -65,6 +71,26 @@ double oracle_f16_to_f64(uint16_t h)
         v = frac ? NAN : INFINITY;
     else
         v = ldexp((double)(1024 + frac), expo - 25);
+    return sign ? -v : v;
+}
+
+/* bfloat16 bit pattern -> exact binary64 value.
+ * Layout: 1 sign bit, 8 exponent bits (bias 127), 7 fraction bits.
+ *   exponent 0      : subnormal, value = fraction * 2^-133
+ *   exponent 1..254 : normal,    value = (128 + fraction) * 2^(exponent-134)
+ *   exponent 255    : infinity (fraction 0) or NaN. */
+double oracle_bf16_to_f64(uint16_t h)
+{
+    const int sign = (h >> 15) & 1;
+    const int expo = (h >> 7) & 0xff;
+    const int frac = h & 0x7f;
+    double v;
+    if (expo == 0)
+        v = ldexp((double)frac, -133);
+    else if (expo == 255)
+        v = frac ? NAN : INFINITY;
+    else
+        v = ldexp((double)(128 + frac), expo - 134);
     return sign ? -v : v;
 }
 
@@ -168,6 +194,49 @@ int oracle_gemm_f16(int M, int N, int K, const uint16_t *A, const uint16_t *B,
 }
 
 /*
+ * Full product, bfloat16 inputs given as raw bit patterns, binary32 output:
+ * the binary16 routine with oracle_bf16_to_f64 as the decoder.
+ */
+int oracle_gemm_bf16(int M, int N, int K, const uint16_t *A, const uint16_t *B,
+                     float *C, int nthreads)
+{
+    if (M < 0 || N < 0 || K < 0)
+        return ORACLE_ERR_DIM;
+    if (M == 0 || N == 0)
+        return ORACLE_OK;
+    double *bdec = (double *)malloc(65536 * sizeof(double));
+    if (!bdec)
+        return ORACLE_ERR_ALLOC;
+    for (int h = 0; h < 65536; ++h)
+        bdec[h] = oracle_bf16_to_f64((uint16_t)h);
+    int failed = 0;
+#pragma omp parallel num_threads(thread_count(nthreads)) reduction(| : failed)
+    {
+        double *acc = (double *)malloc((size_t)N * sizeof(double));
+        if (!acc)
+            failed = 1;
+#pragma omp for schedule(static)
+        for (int i = 0; i < M; ++i) {
+            if (!acc)
+                continue;
+            for (int j = 0; j < N; ++j)
+                acc[j] = 0.0;
+            for (int k = 0; k < K; ++k) {
+                const double a = bdec[A[(size_t)i * K + k]];
+                const uint16_t *brow = B + (size_t)k * N;
+                for (int j = 0; j < N; ++j)
+                    acc[j] += a * bdec[brow[j]];
+            }
+            for (int j = 0; j < N; ++j)
+                C[(size_t)i * N + j] = (float)acc[j];
+        }
+        free(acc);
+    }
+    free(bdec);
+    return failed ? ORACLE_ERR_ALLOC : ORACLE_OK;
+}
+
+/*
  * Selected elements only: out[t] = C[rows[t]][cols[t]], each formed as the
  * plain dot product of row rows[t] of A with column cols[t] of B in ascending
  * k.  Same operation sequence as the full routines, so the same bits; used
@@ -209,6 +278,27 @@ int oracle_gemm_f16_at(int M, int N, int K, const uint16_t *A,
         for (int k = 0; k < K; ++k)
             acc += oracle_f16_to_f64(A[(size_t)i * K + k]) *
                    oracle_f16_to_f64(B[(size_t)k * N + j]);
+        out[t] = (float)acc;
+    }
+    return ORACLE_OK;
+}
+
+int oracle_gemm_bf16_at(int M, int N, int K, const uint16_t *A,
+                        const uint16_t *B, int64_t count, const int64_t *rows,
+                        const int64_t *cols, float *out, int nthreads)
+{
+    if (M < 0 || N < 0 || K < 0 || count < 0)
+        return ORACLE_ERR_DIM;
+    for (int64_t t = 0; t < count; ++t)
+        if (rows[t] < 0 || rows[t] >= M || cols[t] < 0 || cols[t] >= N)
+            return ORACLE_ERR_DIM;
+#pragma omp parallel for num_threads(thread_count(nthreads)) schedule(static)
+    for (int64_t t = 0; t < count; ++t) {
+        const int64_t i = rows[t], j = cols[t];
+        double acc = 0.0;
+        for (int k = 0; k < K; ++k)
+            acc += oracle_bf16_to_f64(A[(size_t)i * K + k]) *
+                   oracle_bf16_to_f64(B[(size_t)k * N + j]);
         out[t] = (float)acc;
     }
     return ORACLE_OK;

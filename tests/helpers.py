@@ -16,8 +16,18 @@ def say(*args):
 
 
 def to_dev(a: np.ndarray):
+    """numpy -> GPU tensor; uint16 arrays hold bfloat16 bit patterns."""
     import torch
-    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to("cuda")
+    return torch.from_numpy(a).to("cuda")
+
+
+def kind(a: np.ndarray) -> str:
+    """Input format of a numpy operand: float32, float16 or bfloat16 bits."""
+    return {np.dtype(np.float32): "f32", np.dtype(np.float16): "f16",
+            np.dtype(np.uint16): "bf16"}[a.dtype]
 
 
 def tol_f32(K: int) -> float:
@@ -28,7 +38,9 @@ def tol_f32(K: int) -> float:
 
 
 def tol_f16(K: int, cref: np.ndarray) -> float:
-    """Elementwise bound for binary16 inputs: 2e-3 sqrt(K) max|C_ref|."""
+    """Elementwise bound for 16-bit inputs (binary16, and bfloat16 under the
+    same reading: products of two 16-bit values are exact in binary32 either
+    way, so only the binary32 accumulation errs): 2e-3 sqrt(K) max|C_ref|."""
     m = float(np.max(np.abs(cref))) if cref.size else 0.0
     return 2e-3 * np.sqrt(max(K, 1)) * m
 
@@ -39,18 +51,28 @@ def workload(name: str, integer: bool = False):
     return inputs.workload_matrices(name, integer)
 
 
+def as_f32(a: np.ndarray) -> np.ndarray:
+    """The binary32 values of a numpy operand of any input format (a
+    bfloat16 pattern is the upper half of the binary32 with its value)."""
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << np.uint32(16)).view(np.float32)
+    return a.astype(np.float32)
+
+
+def oracle_gemm(A, B):
+    """Full oracle product for any input format."""
+    return {"f32": oracle.gemm_f32, "f16": oracle.gemm_f16, "bf16": oracle.gemm_bf16}[kind(A)](A, B)
+
+
 @functools.lru_cache(maxsize=None)
 def oracle_full(name: str, integer: bool = False):
     A, B = workload(name, integer)
-    if A.dtype == np.float16:
-        return oracle.gemm_f16(A, B)
-    return oracle.gemm_f32(A, B)
+    return oracle_gemm(A, B)
 
 
 def oracle_at(A, B, rows, cols):
-    if A.dtype == np.float16:
-        return oracle.gemm_f16_at(A, B, rows, cols)
-    return oracle.gemm_f32_at(A, B, rows, cols)
+    f = {"f32": oracle.gemm_f32_at, "f16": oracle.gemm_f16_at, "bf16": oracle.gemm_bf16_at}[kind(A)]
+    return f(A, B, rows, cols)
 
 
 def assert_bits_equal(got: np.ndarray, ref: np.ndarray, what: str):

@@ -262,3 +262,90 @@ def test_f16_accepts_raw_bit_patterns_and_small_integers_are_exact():
     A16 = A.astype(np.float16).view(np.uint16)
     B16 = B.astype(np.float16).view(np.uint16)
     assert np.array_equal(oracle.gemm_f16(A16, B16), (A @ B).astype(np.float32))
+
+
+# ------------------------------------------------------------ bfloat16 path --
+# bfloat16 keeps the sign, the 8 exponent bits and the top 7 fraction bits of
+# a binary32 ("Lesson 8: how a GPU does matrix multiply", section 22, names
+# the format).  torch's CPU conversion of bfloat16 to float32 is an
+# independent implementation of the decode.
+
+def _bf16_to_f32_via_torch(bits):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(bits, np.uint16).view(np.int16)).view(torch.bfloat16)
+    with np.errstate(invalid="ignore"):   # NaN patterns widen quietly
+        return t.float().numpy().astype(np.float64)
+
+
+def test_bf16_decoder_matches_torch_on_every_bit_pattern():
+    pats = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = _bf16_to_f32_via_torch(pats)
+    got = np.array([oracle.bf16_to_f64(int(h)) for h in pats])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.signbit(oracle.bf16_to_f64(0x8000)) and not np.signbit(oracle.bf16_to_f64(0))
+
+
+def test_bf16_decoder_spot_values():
+    # 0x3F80 = 1.0, 0xC000 = -2.0, 0x0001 = 2^-133 (smallest subnormal),
+    # 0x007F = 127 * 2^-133 (largest subnormal), 0x0080 = 2^-126,
+    # 0x7F7F = 255 * 2^120 (largest finite), 0x3EAB = 171 * 2^-9.
+    cases = {0x3F80: 1.0, 0xC000: -2.0, 0x0001: 2.0 ** -133, 0x007F: 127 * 2.0 ** -133,
+             0x0080: 2.0 ** -126, 0x7F7F: 255 * 2.0 ** 120, 0x3EAB: 171 * 2.0 ** -9,
+             0x7F80: float("inf")}
+    for h, v in cases.items():
+        assert oracle.bf16_to_f64(h) == v, hex(h)
+
+
+def _bf16_bits(x):
+    from dense_gemm_optimisation_row_amd import inputs
+    return inputs.to_bf16_bits(np.asarray(x, np.float32))
+
+
+def test_bf16_input_rounding_matches_torch():
+    # the shared input generator's float32 -> bfloat16 rounding (nearest,
+    # ties to even) against torch's conversion, including exact ties
+    import torch
+    rng = np.random.default_rng(21)
+    x = (rng.standard_normal(200000) * np.exp2(rng.integers(-60, 60, 200000))).astype(np.float32)
+    ties = np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, -(1 + 2.0 ** -8), 2.0 ** -130], np.float32)
+    x = np.concatenate([x, ties])
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(_bf16_bits(x), ref)
+
+
+def test_bf16_product_equals_f32_product_of_the_decoded_values():
+    # bfloat16 values are exactly binary32 values: the bfloat16 routine must
+    # give the bits of the (pinned) binary32 routine on the decoded inputs.
+    A = _bf16_bits(RNG.uniform(-1, 1, (61, 250)))
+    B = _bf16_bits(RNG.uniform(-1, 1, (250, 77)))
+    a32 = _bf16_to_f32_via_torch(A).astype(np.float32)
+    b32 = _bf16_to_f32_via_torch(B).astype(np.float32)
+    assert np.array_equal(_bits(oracle.gemm_bf16(A, B)), _bits(oracle.gemm_f32(a32, b32)))
+    r = RNG.integers(0, 61, 300)
+    c = RNG.integers(0, 77, 300)
+    full = oracle.gemm_bf16(A, B)
+    assert np.array_equal(_bits(oracle.gemm_bf16_at(A, B, r, c)), _bits(full[r, c]))
+
+
+def test_bf16_bruteforce_exact():
+    rng = np.random.default_rng(10)
+    for M in range(1, 7):
+        for N in range(1, 7):
+            for K in range(1, 7):
+                A = _bf16_bits(rng.uniform(-1, 1, (M, K)))
+                B = _bf16_bits(rng.uniform(-1, 1, (K, N)))
+                a = _bf16_to_f32_via_torch(A).reshape(M, K)
+                b = _bf16_to_f32_via_torch(B).reshape(K, N)
+                ex = _exact_product(a, b)
+                expect = np.array([[_round_exact_to_f32(q) for q in r] for r in ex],
+                                  np.float32)
+                assert np.array_equal(_bits(oracle.gemm_bf16(A, B)), _bits(expect)), (M, N, K)
+
+
+def test_bf16_small_integers_are_exact():
+    A = RNG.integers(-4, 5, (20, 500))
+    B = RNG.integers(-4, 5, (500, 30))
+    assert np.array_equal(oracle.gemm_bf16(_bf16_bits(A), _bf16_bits(B)),
+                          (A @ B).astype(np.float32))

@@ -4,7 +4,8 @@ the oracle, and check that at least one pin of ``test_oracle.py`` fails.
 
 Each mutant is a one-token slip of the kind a hand-written loop nest invites:
 a dropped term, a wrong sign, a transposed operand, a wrong index, a start
-value other than zero, binary32 accumulation, or a misdecoded binary16 field.
+value other than zero, binary32 accumulation, or a misdecoded binary16 or
+bfloat16 field.
 """
 import ctypes
 import shutil
@@ -40,6 +41,15 @@ MUTANTS = {
                           "v = ldexp((double)(1024 + frac), expo - 24);"),
     "f16_hidden_bit": ("v = ldexp((double)(1024 + frac), expo - 25);",
                        "v = ldexp((double)(frac), expo - 15);"),
+    # bfloat16 routine and decoder
+    "bf16_subnormal_scale": ("v = ldexp((double)frac, -133);", "v = ldexp((double)frac, -134);"),
+    "bf16_exponent_bias": ("v = ldexp((double)(128 + frac), expo - 134);",
+                           "v = ldexp((double)(128 + frac), expo - 133);"),
+    "bf16_hidden_bit": ("v = ldexp((double)(128 + frac), expo - 134);",
+                        "v = ldexp((double)(frac), expo - 127);"),
+    "bf16_B_transposed": ("acc[j] += a * bdec[brow[j]];",
+                          "acc[j] += a * bdec[B[((size_t)j * K + k) % ((size_t)K * N)]];"),
+    "bf16_fraction_field": ("const int frac = h & 0x7f;", "const int frac = h & 0x3f;"),
     # selected-element routine
     "at_wrong_column": ("* (double)B[(size_t)k * N + j];", "* (double)B[(size_t)k * N + i % N];"),
 }
@@ -62,6 +72,11 @@ PINS = [
     lambda: pins.test_f16_product_equals_f32_product_of_the_decoded_values(),
     lambda: pins.test_f16_bruteforce_exact(),
     lambda: pins.test_f16_accepts_raw_bit_patterns_and_small_integers_are_exact(),
+    lambda: pins.test_bf16_decoder_matches_torch_on_every_bit_pattern(),
+    lambda: pins.test_bf16_decoder_spot_values(),
+    lambda: pins.test_bf16_product_equals_f32_product_of_the_decoded_values(),
+    lambda: pins.test_bf16_bruteforce_exact(),
+    lambda: pins.test_bf16_small_integers_are_exact(),
 ]
 
 

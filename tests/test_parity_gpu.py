@@ -17,8 +17,8 @@ import dense_gemm_optimisation_row_amd as dg
 from dense_gemm_optimisation_row_amd import binding, inputs
 
 import oracle
-from helpers import (assert_bits_equal, assert_within, oracle_at, oracle_full, say, to_dev,
-                     tol_f16, tol_f32, workload)
+from helpers import (as_f32, assert_bits_equal, assert_within, kind, oracle_at, oracle_full,
+                     oracle_gemm, say, to_dev, tol_f16, tol_f32, workload)
 
 pytestmark = pytest.mark.gpu
 
@@ -33,22 +33,27 @@ def gpu():
 
 
 def run(half, variant, A, B, C=None):
+    """Run the entry point for A's input format (``half`` is kept for the
+    callers' readability; the format comes from the arrays)."""
     import torch
     a, b = to_dev(A), to_dev(B)
-    if half:
-        c = dg.gemm_f16_f32acc_variant(variant, a, b, C)
-    else:
-        c = dg.gemm_f32_variant(variant, a, b, C)
+    fn = {"f32": dg.gemm_f32_variant, "f16": dg.gemm_f16_f32acc_variant,
+          "bf16": dg.gemm_bf16_f32acc_variant}[kind(A)]
+    c = fn(variant, a, b, C)
     torch.cuda.synchronize()
     return c.cpu().numpy()
 
 
+def _fmt(half):
+    return half if isinstance(half, str) else ("f16" if half else "f32")
+
+
 def ints(M, N, K, seed, half=False):
-    return inputs.matrices(M, N, K, seed, "int", "f16" if half else "f32")
+    return inputs.matrices(M, N, K, seed, "int", _fmt(half))
 
 
 def floats(M, N, K, seed, half=False):
-    return inputs.matrices(M, N, K, seed, "uniform", "f16" if half else "f32")
+    return inputs.matrices(M, N, K, seed, "uniform", _fmt(half))
 
 
 SMALL_SHAPES = [
@@ -81,6 +86,18 @@ def test_f16_variants_small_shapes(variant, shape):
     assert_within(run(True, variant, A, B), ref, tol_f16(K, ref), f"floats {shape}")
 
 
+@pytest.mark.parametrize("variant", dg.BF16_VARIANTS)
+@pytest.mark.parametrize("shape", SMALL_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_bf16_variants_small_shapes(variant, shape):
+    M, N, K = shape
+    say("bf16", dg.variant_name(variant), shape)
+    A, B = ints(M, N, K, 15, "bf16")
+    assert_bits_equal(run("bf16", variant, A, B), oracle.gemm_bf16(A, B), f"ints {shape}")
+    A, B = floats(M, N, K, 16, "bf16")
+    ref = oracle.gemm_bf16(A, B)
+    assert_within(run("bf16", variant, A, B), ref, tol_f16(K, ref), f"floats {shape}")
+
+
 # Shapes large enough that the automatic choice takes each matrix-core tile
 # configuration, with ragged edges in all three dimensions.
 CONFIG_SHAPES = [
@@ -92,6 +109,10 @@ CONFIG_SHAPES = [
     (True, (8000, 4104, 200), (256, 256)),    # FP16 256 x 256 tiles, 128-bit rows, ragged M/N/K
     (True, (2047, 4095, 200), (128, 128)),    # FP16 128 x 128 tiles
     (True, (1000, 1000, 1000), (64, 64)),     # FP16 64 x 64 tiles
+    ("bf16", (8000, 4104, 200), (256, 256)),  # BF16 ring, ragged M/N/K
+    ("bf16", (8191, 4097, 72), (256, 256)),   # BF16 256 x 256, unaligned rows
+    ("bf16", (2047, 4095, 200), (128, 128)),  # BF16 128 x 128 tiles
+    ("bf16", (1000, 1000, 1000), (64, 64)),   # BF16 64 x 64 tiles
 ]
 
 
@@ -101,12 +122,12 @@ def test_every_matrix_core_configuration(half, shape, tile):
     M, N, K = shape
     p = dg.plan(half, M, N, K)
     assert (p["tile_m"], p["tile_n"]) == tile
-    say("auto", "f16" if half else "f32", shape, "tile", tile)
+    say("auto", _fmt(half), shape, "tile", tile)
     A, B = ints(M, N, K, 21, half)
-    ref = oracle.gemm_f16(A, B) if half else oracle.gemm_f32(A, B)
+    ref = oracle_gemm(A, B)
     assert_bits_equal(run(half, dg.AUTO, A, B), ref, f"ints {shape}")
     A, B = floats(M, N, K, 22, half)
-    ref = oracle.gemm_f16(A, B) if half else oracle.gemm_f32(A, B)
+    ref = oracle_gemm(A, B)
     tol = tol_f16(K, ref) if half else tol_f32(K)
     assert_within(run(half, dg.AUTO, A, B), ref, tol, f"floats {shape}")
 
@@ -114,17 +135,18 @@ def test_every_matrix_core_configuration(half, shape, tile):
 # The large FP16 tile runs a ring of k-stages (32 deep) whose prologue and
 # drain differ with the stage count: these K give 1, 1, 2, 2, 3, 3, 4 and 5
 # stages, full and ragged, on a shape with ragged M and N that takes the tile.
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
 @pytest.mark.parametrize("K", [8, 32, 40, 64, 72, 96, 104, 136])
-def test_f16_large_tile_stage_counts(K):
+def test_f16_large_tile_stage_counts(K, fmt):
     M, N = 8000, 4104
     p = dg.plan(True, M, N, K)
     assert (p["tile_m"], p["tile_n"]) == (256, 256)
-    say("f16 large tile stages", (M, N, K))
-    A, B = ints(M, N, K, 61 + K, half=True)
-    assert_bits_equal(run(True, dg.AUTO, A, B), oracle.gemm_f16(A, B), f"ints K={K}")
-    A, B = floats(M, N, K, 62 + K, half=True)
-    ref = oracle.gemm_f16(A, B)
-    assert_within(run(True, dg.AUTO, A, B), ref, tol_f16(K, ref), f"floats K={K}")
+    say(fmt, "large tile stages", (M, N, K))
+    A, B = ints(M, N, K, 61 + K, fmt)
+    assert_bits_equal(run(fmt, dg.AUTO, A, B), oracle_gemm(A, B), f"ints K={K}")
+    A, B = floats(M, N, K, 62 + K, fmt)
+    ref = oracle_gemm(A, B)
+    assert_within(run(fmt, dg.AUTO, A, B), ref, tol_f16(K, ref), f"floats K={K}")
 
 
 # The large FP32 tile runs the same kind of ring with 16-deep stages: these K
@@ -144,7 +166,7 @@ def test_f32_large_tile_stage_counts(K):
 # ------------------------------------------------------ full-size workloads --
 
 FULL = ["f32_256", "f32_1024", "f32_1000", "f32_4097x33x777"]
-SAMPLED = ["f32_4096", "f16_8192"]
+SAMPLED = ["f32_4096", "f16_8192", "bf16_8192"]
 
 
 def _gpu_full(name, integer):
@@ -180,7 +202,7 @@ def _invariant_vector(N, seed):
 @pytest.mark.parametrize("name", SAMPLED)
 def test_workload_sampled_and_invariant(name):
     w = inputs.WORKLOADS[name]
-    half = w.dtype == "f16"
+    half = w.dtype != "f32"
     rows, cols = inputs.sample_indices(w.M, w.N, 4096, seed=w.seed + 7)
 
     # integer variant: every output is an exact integer
@@ -189,9 +211,9 @@ def test_workload_sampled_and_invariant(name):
     C = _gpu_full(name, True)
     assert_bits_equal(C[rows, cols], oracle_at(A, B, rows, cols), f"{name} ints sampled")
     v = _invariant_vector(w.N, w.seed)
-    v_in = v.astype(np.float16) if half else v
-    Bv = (oracle.gemm_f16 if half else oracle.gemm_f32)(B, v_in.reshape(-1, 1))
-    ABv = oracle.gemm_f32(A.astype(np.float32), Bv)          # exact: |A B v| < 2^24 below
+    v_in = {"f32": v, "f16": v.astype(np.float16), "bf16": inputs.to_bf16_bits(v)}[w.dtype]
+    Bv = oracle_gemm(B, v_in.reshape(-1, 1))
+    ABv = oracle.gemm_f32(as_f32(A), Bv)                     # exact: |A B v| < 2^24 below
     assert np.max(np.abs(ABv)) < 2 ** 24
     Cv = C.astype(np.float64) @ v.astype(np.float64)
     assert_bits_equal(Cv.reshape(-1, 1), ABv.astype(np.float64), f"{name} C v = A (B v)")
@@ -210,33 +232,40 @@ def test_workload_sampled_and_invariant(name):
 
 # -------------------------------------------------------------- edge cases --
 
-@pytest.mark.parametrize("half", [False, True])
+_ENTRY = {"f32": dg.gemm_f32, "f16": dg.gemm_f16_f32acc, "bf16": dg.gemm_bf16_f32acc}
+_ENTRY_VARIANT = {"f32": dg.gemm_f32_variant, "f16": dg.gemm_f16_f32acc_variant,
+                  "bf16": dg.gemm_bf16_f32acc_variant}
+
+
+@pytest.mark.parametrize("half", [False, True, "bf16"])
 def test_k0_writes_zeros_and_empty_m_n_write_nothing(half):
     import torch
-    say("edge K=0 / M=0 / N=0", "f16" if half else "f32")
-    dt = torch.float16 if half else torch.float32
+    fmt = _fmt(half)
+    say("edge K=0 / M=0 / N=0", fmt)
+    dt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[fmt]
     a = torch.empty((5, 0), dtype=dt, device="cuda")
     b = torch.empty((0, 7), dtype=dt, device="cuda")
     c = torch.full((5, 7), float("nan"), device="cuda")
-    (dg.gemm_f16_f32acc if half else dg.gemm_f32)(a, b, c)
+    _ENTRY[fmt](a, b, c)
     torch.cuda.synchronize()
     assert torch.equal(c.cpu(), torch.zeros(5, 7))
     sentinel = torch.full((4,), 3.0, device="cuda")
     fn = binding.raw_gemm
     A = torch.ones(16, dtype=dt, device="cuda")
-    assert fn(half, None, 0, 4, 4, A.data_ptr(), A.data_ptr(), sentinel.data_ptr(), None) == 0
-    assert fn(half, None, 4, 0, 4, A.data_ptr(), A.data_ptr(), sentinel.data_ptr(), None) == 0
+    assert fn(fmt, None, 0, 4, 4, A.data_ptr(), A.data_ptr(), sentinel.data_ptr(), None) == 0
+    assert fn(fmt, None, 4, 0, 4, A.data_ptr(), A.data_ptr(), sentinel.data_ptr(), None) == 0
     torch.cuda.synchronize()
     assert torch.equal(sentinel.cpu(), torch.full((4,), 3.0))
 
 
-@pytest.mark.parametrize("half", [False, True])
+@pytest.mark.parametrize("half", [False, True, "bf16"])
 def test_misaligned_base_pointers_take_the_narrow_path(half):
     import torch
     M, N, K = 130, 136, 264
-    say("edge misaligned", "f16" if half else "f32", (M, N, K))
+    fmt = _fmt(half)
+    say("edge misaligned", fmt, (M, N, K))
     A, B = ints(M, N, K, 31, half)
-    ref = oracle.gemm_f16(A, B) if half else oracle.gemm_f32(A, B)
+    ref = oracle_gemm(A, B)
     a_big = to_dev(np.concatenate([np.zeros(1, A.dtype), A.ravel()]))
     b_big = to_dev(np.concatenate([np.zeros(1, B.dtype), B.ravel()]))
     c_big = torch.zeros(M * N + 1, device="cuda")
@@ -247,7 +276,7 @@ def test_misaligned_base_pointers_take_the_narrow_path(half):
     variants = dg.F16_VARIANTS if half else dg.F32_VARIANTS
     for v in variants:
         c.zero_()
-        (dg.gemm_f16_f32acc_variant if half else dg.gemm_f32_variant)(v, a, b, c)
+        _ENTRY_VARIANT[fmt](v, a, b, c)
         torch.cuda.synchronize()
         assert_bits_equal(c.cpu().numpy(), ref, f"misaligned {dg.variant_name(v)}")
     assert c_big[0].item() == 0.0   # nothing written before C
