@@ -8,7 +8,9 @@ Two layers:
   ``*_variant``) take torch tensors
   that already live on the GPU, check shape / dtype / contiguity, call the
   library on the tensors' current stream and raise ``GemmError`` on a
-  non-zero status.
+  non-zero status;
+* ``gemm_*_ex`` take strided 2-D views (one unit stride each) and read the
+  operand layout (transposed or not, leading dimension) off the strides.
 
 All arithmetic happens in the HIP kernels.  There is no fallback: if the
 library is missing, every call raises.
@@ -29,6 +31,8 @@ GEMM_ERR_LAUNCH = -3
 GEMM_ERR_UNSUPPORTED_DEVICE = -4
 GEMM_ERR_INVALID_VARIANT = -5
 GEMM_ERR_RUNTIME = -6
+GEMM_ERR_INVALID_LAYOUT = -7
+GEMM_OP_N, GEMM_OP_T = 0, 1
 
 AUTO = -1
 R0_NAIVE, R1_LDS_TILED, R2_VECTOR_LOADS, R3_LDS_PADDED = 0, 1, 2, 3
@@ -40,6 +44,7 @@ BF16_VARIANTS = (0, 7)
 EXPORTS = ("gemm_f32", "gemm_f16_f32acc", "gemm_bf16_f32acc",
            "gemm_f32_variant", "gemm_f16_f32acc_variant", "gemm_bf16_f32acc_variant",
            "gemm_f32_plan", "gemm_f16_f32acc_plan", "gemm_bf16_f32acc_plan",
+           "gemm_f32_ex", "gemm_f16_f32acc_ex", "gemm_bf16_f32acc_ex",
            "gemm_status_string", "gemm_variant_name")
 
 # Entry-point name stem per input format.
@@ -95,6 +100,9 @@ def load(path: str = LIB_PATH):
             f = getattr(lib, stem + "_plan")
             f.argtypes = [i, i, i, i, p, p, p, ctypes.POINTER(Plan)]
             f.restype = i
+            f = getattr(lib, stem + "_ex")
+            f.argtypes = [i, i, i, i, i, ctypes.c_float, p, i, p, i, ctypes.c_float, p, i, p]
+            f.restype = i
         lib.gemm_status_string.argtypes = [i]
         lib.gemm_status_string.restype = ctypes.c_char_p
         lib.gemm_variant_name.argtypes = [i]
@@ -122,6 +130,14 @@ def raw_gemm(kind, variant: int | None, M: int, N: int, K: int,
     if variant is None:
         return int(getattr(lib, stem)(M, N, K, A, B, C, stream))
     return int(getattr(lib, stem + "_variant")(variant, M, N, K, A, B, C, stream))
+
+
+def raw_gemm_ex(kind, op_a: int, op_b: int, M: int, N: int, K: int, alpha: float,
+                A: int | None, lda: int, B: int | None, ldb: int, beta: float,
+                C: int | None, ldc: int, stream: int | None) -> int:
+    """``gemm_*_ex`` with plain integers; returns the status code."""
+    f = getattr(load(), _STEM[kind_of(kind)] + "_ex")
+    return int(f(op_a, op_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream))
 
 
 def plan(kind, M: int, N: int, K: int, variant: int = AUTO,
@@ -215,3 +231,65 @@ def gemm_bf16_f32acc(A, B, C=None, stream=None):
 def gemm_bf16_f32acc_variant(variant, A, B, C=None, stream=None):
     """``gemm_bf16_f32acc`` with the kernel variant (rung) forced."""
     return _call("bf16", int(variant), A, B, C, stream)
+
+
+def _layout(t, name):
+    """(op, leading dimension) of a 2-D view with one unit stride: op N when
+    rows are contiguous (X[r][c] at r*ld + c), op T when columns are (the view
+    is the transpose of a row-major matrix with row stride ld)."""
+    rows, cols = t.shape
+    s0, s1 = t.stride()
+    if s1 == 1 or cols <= 1:
+        return GEMM_OP_N, (s0 if rows > 1 else max(cols, 1))
+    if s0 == 1 or rows <= 1:
+        return GEMM_OP_T, (s1 if cols > 1 else max(rows, 1))
+    raise ValueError(f"{name} needs a unit stride in one dimension (strides {t.stride()})")
+
+
+def _call_ex(kind, A, B, C, alpha, beta, stream):
+    import torch
+    kind = kind_of(kind)
+    dtype = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[kind]
+    if A.dim() != 2 or B.dim() != 2 or A.shape[1] != B.shape[0]:
+        raise ValueError(f"shapes {tuple(A.shape)} x {tuple(B.shape)} do not chain")
+    if A.dtype != dtype or B.dtype != dtype:
+        raise TypeError(f"A and B must be {dtype}")
+    if not (A.is_cuda and B.is_cuda) or B.device != A.device:
+        raise ValueError("A and B must be GPU tensors on one device")
+    M, K = A.shape
+    N = B.shape[1]
+    if C is None:
+        if beta != 0:
+            raise ValueError("beta != 0 needs an input C")
+        C = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    elif tuple(C.shape) != (M, N) or C.dtype != torch.float32 or C.device != A.device:
+        raise ValueError("C must be a float32 M x N tensor on A's device")
+    op_a, lda = _layout(A, "A")
+    op_b, ldb = _layout(B, "B")
+    op_c, ldc = _layout(C, "C")
+    if op_c != GEMM_OP_N:
+        raise ValueError("C must have contiguous rows")
+    with torch.cuda.device(A.device):
+        rc = raw_gemm_ex(kind, op_a, op_b, M, N, K, float(alpha), _ptr(A), lda, _ptr(B), ldb,
+                         float(beta), _ptr(C), ldc, _stream_handle(A.device, stream))
+    if rc != GEMM_OK:
+        raise GemmError(rc, _STEM[kind] + "_ex")
+    return C
+
+
+def gemm_f32_ex(A, B, C=None, alpha=1.0, beta=0.0, stream=None):
+    """C = alpha A B + beta C for float32 GPU views A (M x K) and B (K x N),
+    each row- or column-contiguous with any leading dimension (a transposed
+    view is passed as op T); C is an M x N float32 view with contiguous rows.
+    Returns C (allocated when not given, which needs beta == 0)."""
+    return _call_ex("f32", A, B, C, alpha, beta, stream)
+
+
+def gemm_f16_f32acc_ex(A, B, C=None, alpha=1.0, beta=0.0, stream=None):
+    """``gemm_f32_ex`` for float16 A and B (FP32 accumulation and output)."""
+    return _call_ex("f16", A, B, C, alpha, beta, stream)
+
+
+def gemm_bf16_f32acc_ex(A, B, C=None, alpha=1.0, beta=0.0, stream=None):
+    """``gemm_f32_ex`` for bfloat16 A and B (FP32 accumulation and output)."""
+    return _call_ex("bf16", A, B, C, alpha, beta, stream)

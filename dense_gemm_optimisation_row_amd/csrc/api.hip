@@ -7,6 +7,7 @@
 // pages' ceil-div rule ("Lesson 8: how a GPU does matrix multiply", section 3):
 // ceil(N / tile_n) workgroups along N and ceil(M / tile_m) along M.
 #include <atomic>
+#include <math.h>
 #include <stdint.h>
 
 #include "common.h"
@@ -263,6 +264,83 @@ int run(In in, int variant, int M, int N, int K, const void *A, const void *B, f
     return err == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
 }
 
+// ------------------------------------------------------- general layouts --
+
+bool is_finite(float x) { return x - x == 0.f; }
+
+// Whether the ring kernels take this call: 16-byte aligned operands, leading
+// dimensions and the vector-read dimensions whole 128-bit vectors, and byte
+// offsets inside a tile below 2^31.
+bool ring_ok(In in, int opA, int opB, int M, int N, int K, const void *A, int lda, const void *B, int ldb,
+             int ldc)
+{
+    const int v = in == In::F32 ? 4 : 8;               // elements per 16 bytes
+    const int ld_max = in == In::F32 ? (1 << 21) : (1 << 22);
+    if (!aligned16(A) || !aligned16(B) || lda % v || ldb % v || lda >= ld_max || ldb >= ld_max ||
+        ldc >= (1 << 22))
+        return false;
+    const bool a_ok = opA ? M % v == 0 : K % v == 0;
+    const bool b_ok = opB ? K % v == 0 : N % v == 0;
+    return a_ok && b_ok;
+}
+
+int run_ex(In in, int opA, int opB, int M, int N, int K, float alpha, const void *A, int lda,
+           const void *B, int ldb, float beta, float *C, int ldc, void *stream)
+{
+    if (M < 0 || N < 0 || K < 0)
+        return GEMM_ERR_INVALID_DIM;
+    if ((opA != GEMM_OP_N && opA != GEMM_OP_T) || (opB != GEMM_OP_N && opB != GEMM_OP_T))
+        return GEMM_ERR_INVALID_LAYOUT;
+    const int a_cols = opA ? M : K, b_cols = opB ? K : N;
+    if (lda < (a_cols > 1 ? a_cols : 1) || ldb < (b_cols > 1 ? b_cols : 1) || ldc < (N > 1 ? N : 1))
+        return GEMM_ERR_INVALID_LAYOUT;
+    if (null_with_extent(A, B, C, M, N, K))
+        return GEMM_ERR_NULL_PTR;
+    if (M == 0 || N == 0)
+        return GEMM_OK;
+    // the plain row-major product takes the tuned path of gemm_* itself
+    if (opA == GEMM_OP_N && opB == GEMM_OP_N && lda == K && ldb == N && ldc == N && alpha == 1.f && beta == 0.f)
+        return run(in, GEMM_VARIANT_AUTO, M, N, K, A, B, C, stream);
+    const int dev = check_device();
+    if (dev != GEMM_OK)
+        return dev;
+    hipStream_t s = (hipStream_t)stream;
+    auto ok = [](hipError_t e) { return e == hipSuccess; };
+    if (K == 0 || alpha == 0.f)   // C = beta C (zeros when beta == 0, C not read)
+        return ok(dgor::launch_scale_c(C, M, N, ldc, beta, s)) ? GEMM_OK : GEMM_ERR_LAUNCH;
+
+    dgor::RingArgs a{M, N, K, A, lda, B, ldb, C, ldc, (M + 255) / 256, (N + 255) / 256, 4,
+                     opA == GEMM_OP_T, opB == GEMM_OP_T, false};
+    const int in16 = in == In::F32 ? 0 : (in == In::F16 ? 1 : 2);
+    // C = alpha A B + beta C from the ring kernels' two forms (C = A B and
+    // C += A B) and scaling passes over C:
+    //   beta == 0:  C = A B, then C *= alpha;
+    //   alpha == 1: C *= beta, then C += A B;
+    //   otherwise:  C *= beta / alpha, C += A B, C *= alpha.
+    const float ratio = beta / alpha;
+    const bool ratio_ok = beta == 0.f || alpha == 1.f ||
+                          (is_finite(ratio) && fabsf(ratio) >= 0x1p-60f && fabsf(ratio) <= 0x1p60f);
+    if (!ring_ok(in, opA, opB, M, N, K, A, lda, B, ldb, ldc) || !ratio_ok)
+        return ok(dgor::launch_naive_ex(a, alpha, beta, in16, s)) ? GEMM_OK : GEMM_ERR_LAUNCH;
+    auto ring = [&]() { return in == In::F32 ? dgor::launch_ring32(a, s) : dgor::launch_ring16(a, s, in == In::BF16); };
+    if (beta == 0.f) {
+        if (!ok(ring()))
+            return GEMM_ERR_LAUNCH;
+        if (alpha != 1.f && !ok(dgor::launch_scale_c(C, M, N, ldc, alpha, s)))
+            return GEMM_ERR_LAUNCH;
+        return GEMM_OK;
+    }
+    const float pre = alpha == 1.f ? beta : ratio;
+    if (pre != 1.f && !ok(dgor::launch_scale_c(C, M, N, ldc, pre, s)))
+        return GEMM_ERR_LAUNCH;
+    a.accumulate = true;
+    if (!ok(ring()))
+        return GEMM_ERR_LAUNCH;
+    if (alpha != 1.f && !ok(dgor::launch_scale_c(C, M, N, ldc, alpha, s)))
+        return GEMM_ERR_LAUNCH;
+    return GEMM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -320,6 +398,24 @@ int gemm_bf16_f32acc_plan(int variant, int M, int N, int K, const uint16_t *A,
     return plan_f16(variant, M, N, K, A, B, C, plan);
 }
 
+int gemm_f32_ex(int opA, int opB, int M, int N, int K, float alpha, const float *A, int lda, const float *B,
+                int ldb, float beta, float *C, int ldc, void *stream)
+{
+    return run_ex(In::F32, opA, opB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+}
+
+int gemm_f16_f32acc_ex(int opA, int opB, int M, int N, int K, float alpha, const uint16_t *A, int lda,
+                       const uint16_t *B, int ldb, float beta, float *C, int ldc, void *stream)
+{
+    return run_ex(In::F16, opA, opB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+}
+
+int gemm_bf16_f32acc_ex(int opA, int opB, int M, int N, int K, float alpha, const uint16_t *A, int lda,
+                        const uint16_t *B, int ldb, float beta, float *C, int ldc, void *stream)
+{
+    return run_ex(In::BF16, opA, opB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+}
+
 const char *gemm_status_string(int status)
 {
     switch (status) {
@@ -330,6 +426,7 @@ const char *gemm_status_string(int status)
     case GEMM_ERR_UNSUPPORTED_DEVICE: return "current device is not gfx950";
     case GEMM_ERR_INVALID_VARIANT: return "variant not available for this entry point";
     case GEMM_ERR_RUNTIME: return "HIP runtime query failed";
+    case GEMM_ERR_INVALID_LAYOUT: return "invalid operand layout (op flag or leading dimension)";
     default: return "unknown status";
     }
 }

@@ -20,6 +20,24 @@ struct Problem {
     bool vec_c;     // same for C (FP32, 4 per vector)
 };
 
+// One launch of a ring kernel with general operand layouts: op(A) is M x K
+// and op(B) is K x N.  A is M x K row-major (lda >= K) or, with trans_a,
+// K x M row-major (lda >= M); B is K x N (ldb >= N) or, with trans_b, N x K
+// (ldb >= K); C is M x N (ldc >= N).  The kernel writes C = op(A) op(B), or
+// with `accumulate` C = C + op(A) op(B) (C read first).  Operands must be
+// 16-byte aligned with every leading dimension a multiple of 16 bytes.
+struct RingArgs {
+    int M, N, K;
+    const void *A;
+    int lda;
+    const void *B;
+    int ldb;
+    float *C;
+    int ldc;
+    int tiles_m, tiles_n, group_m;
+    bool trans_a, trans_b, accumulate;
+};
+
 // Launchers.  Each enqueues exactly the kernel `plan` describes on `stream`
 // and returns the launch status.  Shapes were validated by the caller.
 hipError_t launch_zero_fill(const Problem &p, hipStream_t stream);
@@ -29,6 +47,22 @@ hipError_t launch_ladder_f32(const Problem &p, const gemm_plan &plan, hipStream_
 hipError_t launch_naive_f16(const Problem &p, const gemm_plan &plan, hipStream_t stream, bool bf16);
 hipError_t launch_mfma_f32(const Problem &p, const gemm_plan &plan, hipStream_t stream);
 hipError_t launch_mfma_f16(const Problem &p, const gemm_plan &plan, hipStream_t stream, bool bf16);
+// Ring kernels with general layouts (256 x 256 tiles; args.tiles_* set).
+hipError_t launch_ring16(const RingArgs &args, hipStream_t stream, bool bf16);
+hipError_t launch_ring32(const RingArgs &args, hipStream_t stream);
+// C = s C over an M x N block with row stride ldc; s == 0 writes zeros
+// without reading C.
+hipError_t launch_scale_c(float *C, int M, int N, int ldc, float s, hipStream_t stream);
+// The plain strided kernel for any layout: C = alpha op(A) op(B) + beta C
+// (C not read when beta == 0).  in16: 0 binary32 inputs, 1 binary16, 2 bfloat16.
+hipError_t launch_naive_ex(const RingArgs &args, float alpha, float beta, int in16, hipStream_t stream);
+
+// The arguments of the ring kernels for a plain row-major product.
+inline RingArgs ring_args_nn(const Problem &p, const gemm_plan &plan)
+{
+    return RingArgs{p.M, p.N, p.K, p.A, p.K, p.B, p.N, p.C, p.N,
+                    plan.grid_y, plan.grid_x, 4, false, false, false};
+}
 
 // LDS padding of the ladder rungs, in floats per row.  R3 and R4 pad each
 // A row of their 16 x 64 tile by one float, moving consecutive rows to

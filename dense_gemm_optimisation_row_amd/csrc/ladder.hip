@@ -52,6 +52,57 @@ __global__ __launch_bounds__(256) void zero_fill(float *__restrict__ C, size_t n
         C[i] = 0.f;
 }
 
+// C = s C on an M x N block with row stride ldc (s == 0: zeros, C unread).
+__global__ __launch_bounds__(256) void scale_c(float *__restrict__ C, int M, int N, int ldc, float s)
+{
+    // rows blockIdx.y, blockIdx.y + gridDim.y, ...; 1024 columns per block
+    for (int row = blockIdx.y; row < M; row += gridDim.y) {
+        float *c = C + (size_t)row * ldc;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int col = blockIdx.x * 1024 + u * 256 + threadIdx.x;
+            if (col < N)
+                c[col] = s == 0.f ? 0.f : s * c[col];
+        }
+    }
+}
+
+// The strided plain kernel for any operand layout and input format: one
+// thread per element, the k-sum in FP32 in ascending k, then
+// C = alpha sum + beta C (C read only when beta != 0).  A is M x K (lda) or,
+// with TA, K x M; B is K x N (ldb) or, with TB, N x K.
+__device__ __forceinline__ float widen16(uint16_t h, bool bf16)
+{
+    return bf16 ? __uint_as_float((uint32_t)h << 16) : (float)__builtin_bit_cast(_Float16, h);
+}
+
+__device__ __forceinline__ float widen_in(const void *p, size_t idx, int in16)
+{
+    if (in16 == 0)
+        return ((const float *)p)[idx];
+    const uint16_t h = ((const uint16_t *)p)[idx];
+    return widen16(h, in16 == 2);
+}
+
+template <bool TA, bool TB>
+__global__ __launch_bounds__(256) void naive_ex(int M, int N, int K, const void *A, int lda, const void *B,
+                                                int ldb, float *C, int ldc, float alpha, float beta, int in16)
+{
+    const int row = blockIdx.y * 16 + threadIdx.y;
+    const int col = blockIdx.x * 16 + threadIdx.x;
+    if (row < M && col < N) {
+        float sum = 0.f;
+        for (int k = 0; k < K; ++k) {
+            const float a = widen_in(A, TA ? (size_t)k * lda + row : (size_t)row * lda + k, in16);
+            const float b = widen_in(B, TB ? (size_t)col * ldb + k : (size_t)k * ldb + col, in16);
+            sum = fmaf(a, b, sum);
+        }
+        float *c = C + (size_t)row * ldc + col;
+        const float v = alpha * sum;
+        *c = beta == 0.f ? v : fmaf(beta, *c, v);
+    }
+}
+
 // ------------------------------------------------------------- R0 naive ---
 // One thread per element of C, 16 x 16 threads per workgroup, the k-sum held
 // in a register and C written once ("4. GEMM optimisation", 4.1; Lesson 8
@@ -78,10 +129,6 @@ __global__ __launch_bounds__(256) void naive_f32(int M, int N, int K,
 // each product of two 16-bit values is exact in FP32, so this computes the
 // same sum as the 16-bit matrix-core kernels.  A bfloat16 pattern is the high
 // half of the binary32 with the same value.
-__device__ __forceinline__ float widen16(uint16_t h, bool bf16)
-{
-    return bf16 ? __uint_as_float((uint32_t)h << 16) : (float)__builtin_bit_cast(_Float16, h);
-}
 
 template <bool BF16>
 __global__ __launch_bounds__(256) void naive_16(int M, int N, int K,
@@ -300,6 +347,32 @@ __global__ __launch_bounds__(256) void regblock_f32(int M, int N, int K,
 }  // namespace
 
 // ------------------------------------------------------------- launchers --
+
+hipError_t launch_scale_c(float *C, int M, int N, int ldc, float s, hipStream_t stream)
+{
+    const unsigned gx = (unsigned)((N + 1023) / 1024);
+    const unsigned gy = (unsigned)(M < 8192 ? M : 8192);
+    hipLaunchKernelGGL(scale_c, dim3(gx, gy), dim3(256), 0, stream, C, M, N, ldc, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_naive_ex(const RingArgs &a, float alpha, float beta, int in16, hipStream_t stream)
+{
+    const dim3 grid((a.N + 15) / 16, (a.M + 15) / 16), blk(16, 16);
+    if (a.trans_a && a.trans_b)
+        hipLaunchKernelGGL((naive_ex<true, true>), grid, blk, 0, stream, a.M, a.N, a.K, a.A, a.lda, a.B, a.ldb,
+                           a.C, a.ldc, alpha, beta, in16);
+    else if (a.trans_a)
+        hipLaunchKernelGGL((naive_ex<true, false>), grid, blk, 0, stream, a.M, a.N, a.K, a.A, a.lda, a.B, a.ldb,
+                           a.C, a.ldc, alpha, beta, in16);
+    else if (a.trans_b)
+        hipLaunchKernelGGL((naive_ex<false, true>), grid, blk, 0, stream, a.M, a.N, a.K, a.A, a.lda, a.B, a.ldb,
+                           a.C, a.ldc, alpha, beta, in16);
+    else
+        hipLaunchKernelGGL((naive_ex<false, false>), grid, blk, 0, stream, a.M, a.N, a.K, a.A, a.lda, a.B, a.ldb,
+                           a.C, a.ldc, alpha, beta, in16);
+    return hipGetLastError();
+}
 
 hipError_t launch_zero_fill(const Problem &p, hipStream_t stream)
 {

@@ -279,17 +279,73 @@ constexpr int LOADS_PER_STAGE = 8;                   // per wavefront: 4 of A, 4
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
 
-template <class Op>
-__global__ __launch_bounds__(256) void mfma_f16_pipe_kernel(
-    int M, int N, int K, const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
-    float *__restrict__ C, int tiles_m, int tiles_n, int group_m)
+// Ring-kernel support for one operand tile (256 m or n x 32 k per stage).
+// A k-contiguous operand (A, or B given as N x K) is stored in LDS as 256
+// rows of 32 k (four 16-byte units, unit c of row r at 4 r + (c ^ 2((r>>2)&1)))
+// and read with 128-bit reads; a k-strided operand (B, or A given as K x M)
+// as 32 k rows of 256 (unit u of row k at 32 k + (u ^ (4 (k&3) + 2 ((k>>3)&1))))
+// and read with transposing reads.  Either way the fragment a lane gets holds
+// the eight k of its row of op(A) or column of op(B) that the 16x16x32 MFMA
+// wants from it.
+namespace ring16 {
+
+// Lane offsets of wave w's four 1 KB loads of one stage, relative to the
+// stage's first element (k0 for the k-contiguous layout, row k0 for the
+// k-strided one).  ext is the extent of the operand's non-k dimension (M or
+// N), t0 the tile's first index in it, ld the row stride.
+template <bool KSTRIDED>
+__device__ __forceinline__ void load_offsets(int wave, int lane, int t0, int ext, int ld,
+                                             uint32_t off[4], int &kc)
+{
+    constexpr uint32_t OOB = 0x80000000u;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        if (!KSTRIDED) {
+            const int r = 16 * (4 * wave + q) + (lane >> 2);
+            kc = 8 * ((lane & 3) ^ (2 * ((lane >> 4) & 1)));   // same in every block
+            off[q] = (uint32_t)(r * ld + kc) * 2u;
+        } else {
+            const int k = 2 * (4 * wave + q) + (lane >> 5);
+            const int u = (lane & 31) ^ (4 * (k & 3) + 2 * ((k >> 3) & 1));
+            off[q] = t0 + 8 * u < ext ? (uint32_t)(k * ld + 8 * u) * 2u : OOB;
+            kc = 0;
+        }
+    }
+}
+
+// Range in bytes of one stage's descriptor (the first element is row t0, k0
+// for the k-contiguous layout, row k0, column t0 for the k-strided one):
+// everything past it is a row past the operand, or a k row past K.
+template <bool KSTRIDED>
+__device__ __forceinline__ int stage_range(int k0, int K, int t0, int ext, int ld)
+{
+    const int k_left = K - k0;
+    if (k_left <= 0)
+        return 0;   // a stage past the last: every load writes zeros
+    if (!KSTRIDED) {
+        if (t0 + 256 <= ext)
+            return 0x7fffffff;
+        return (int)(((uint32_t)(ext - t0 - 1) * (uint32_t)ld + (uint32_t)k_left) * 2u);
+    }
+    if (k_left >= 32)
+        return 0x7fffffff;
+    return (int)(((uint32_t)(k_left - 1) * (uint32_t)ld + (uint32_t)(ext - t0)) * 2u);
+}
+
+}  // namespace ring16
+
+template <class Op, bool TA, bool TB, bool ACC>
+__global__ __launch_bounds__(256) void mfma_f16_pipe_kernel(RingArgs args)
 {
     using namespace pipe;
     __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
     const uint32_t ring = lds_address(lds);
+    const int M = args.M, N = args.N, K = args.K, lda = args.lda, ldb = args.ldb;
+    const uint16_t *__restrict__ A = (const uint16_t *)args.A;
+    const uint16_t *__restrict__ B = (const uint16_t *)args.B;
 
     int tm, tn;
-    dgor_tile_of_block(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
+    dgor_tile_of_block(blockIdx.x, args.tiles_m, args.tiles_n, args.group_m, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const int lane = threadIdx.x & 63;
     // wave-uniform, so per-wave offsets and descriptors stay scalar
@@ -297,91 +353,111 @@ __global__ __launch_bounds__(256) void mfma_f16_pipe_kernel(
     const int wr = (wave >> 1) * 128, wc = (wave & 1) * 128;
     constexpr uint32_t OOB = 0x80000000u;
 
-    // ---- loader.  Per stage, wavefront w fills A blocks 4w..4w+3 (16 rows
-    // each) and B blocks 4w..4w+3 (2 rows each).  Lane offsets are relative
-    // to the stage's first element and do not change from stage to stage;
-    // columns past N get OOB.  The descriptors' ranges end at the last row
-    // of A and at row K of B, which zero-fills rows past M and B rows past K;
-    // A columns past K are masked per lane in the last stage.  A stage past
-    // the last one gets empty ranges: its loads write zeros and keep the
-    // wait counts of every stage alike.
-    // logical unit; the same in every block (row r of a block is lane / 4)
-    const int a_c = (lane & 3) ^ (2 * ((lane >> 4) & 1));
+    // ---- loader.  Per stage, wavefront w fills blocks 4w..4w+3 of each
+    // operand tile.  A is k-strided when given as K x M (TA), B unless given
+    // as N x K (TB).  Lane offsets do not change from stage to stage; the
+    // descriptors' ranges zero-fill rows past the operand and k rows past K;
+    // k-contiguous columns past K are masked per lane in the last stage.  A
+    // stage past the last one gets empty ranges: its loads write zeros and
+    // keep the wait counts of every stage alike.
     uint32_t a_off[4], b_off[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int r = 16 * (4 * wave + q) + (lane >> 2);
-        a_off[q] = (uint32_t)(r * K + 8 * a_c) * 2u;
-        const int k = 2 * (4 * wave + q) + (lane >> 5);
-        const int u = (lane & 31) ^ (4 * (k & 3) + 2 * ((k >> 3) & 1));
-        b_off[q] = n0 + 8 * u < N ? (uint32_t)(k * N + 8 * u) * 2u : OOB;
-    }
-    const bool a_full = m0 + BM <= M;                     // every row of the tile exists
-    const uint32_t a_rows_bytes = (uint32_t)(M - m0) * (uint32_t)K * 2u;   // < 2^31 when !a_full
+    int a_kc, b_kc;
+    ring16::load_offsets<TA>(wave, lane, m0, M, lda, a_off, a_kc);
+    ring16::load_offsets<!TB>(wave, lane, n0, N, ldb, b_off, b_kc);
     const uint32_t lds_a = ring + (uint32_t)(4 * wave * 1024);
     const uint32_t lds_b = ring + (uint32_t)(A_BYTES + 4 * wave * 1024);
-    // all eight loads of stage `st`, the i-th after MFMA slot slot_of(i)
-    struct StageLoads { intx4 ra, rb; uint32_t lds; bool a_tail; int k_left; };
+    struct StageLoads { intx4 ra, rb; uint32_t lds; bool tail; int k_left; };
     auto prep = [&](int st) {
         StageLoads L;
         const int k0 = st * BK;
-        const int k_left = K - k0;                         // <= 0 past the last stage
-        const uint32_t ka = (uint32_t)k0 * 2u;
-        L.ra = rsrc_words(A + (size_t)m0 * K + k0, 0);
-        L.ra.z = k_left <= 0 ? 0 : (a_full ? 0x7fffffff : (int)(a_rows_bytes - ka));
-        L.rb = rsrc_words(B + (size_t)k0 * N + n0, 0);
-        L.rb.z = k_left >= BK ? 0x7fffffff
-                              : (k_left <= 0 ? 0 : (int)(((uint32_t)k_left * (uint32_t)N - (uint32_t)n0) * 2u));
+        L.ra = rsrc_words(TA ? A + (size_t)k0 * lda + m0 : A + (size_t)m0 * lda + k0, 0);
+        L.ra.z = ring16::stage_range<TA>(k0, K, m0, M, lda);
+        L.rb = rsrc_words(TB ? B + (size_t)n0 * ldb + k0 : B + (size_t)k0 * ldb + n0, 0);
+        L.rb.z = ring16::stage_range<!TB>(k0, K, n0, N, ldb);
         L.lds = (uint32_t)((st % NBUF) * STAGE_BYTES);
-        L.a_tail = k_left < BK;
-        L.k_left = k_left;
+        L.k_left = K - k0;
+        L.tail = L.k_left < BK;
         return L;
     };
     auto load = [&](const StageLoads &L, int q) {
         if (q < 4) {
-            const uint32_t off = (L.a_tail && 8 * a_c >= L.k_left) ? OOB : a_off[q];
+            const uint32_t off = (!TA && L.tail && a_kc >= L.k_left) ? OOB : a_off[q];
             load_to_lds(L.ra, lds_a + L.lds + (uint32_t)(q * 1024), off);
         } else {
-            load_to_lds(L.rb, lds_b + L.lds + (uint32_t)((q - 4) * 1024), b_off[q - 4]);
+            const uint32_t off = (TB && L.tail && b_kc >= L.k_left) ? OOB : b_off[q - 4];
+            load_to_lds(L.rb, lds_b + L.lds + (uint32_t)((q - 4) * 1024), off);
         }
     };
 
-    // ---- fragment reads.  Lane (g, s) = (lane / 16, lane % 16).
+    // ---- fragment reads.  Lane (g, s) = (lane / 16, lane % 16).  A
+    // k-contiguous operand block is one 128-bit read of row base + s at unit
+    // g; a k-strided one is two transposing reads (k rows 8g..8g+3 and
+    // 8g+4..8g+7 of column base + s).
     const int s16 = lane & 15, g = lane >> 4;
-    const int a_sw = 2 * ((s16 >> 2) & 1);
-    const uint32_t a_lane = (uint32_t)((wr + s16) * 64 + ((g ^ a_sw) * 16));
-    const uint32_t b_lane = (uint32_t)(A_BYTES + (8 * g + (s16 >> 2)) * 512 + 8 * (s16 & 1) + 2 * wc);
-    const int b_x = 4 * (s16 >> 2) + 2 * (g & 1);
-    uint32_t b_unit[8];
+    const int kc_sw = 2 * ((s16 >> 2) & 1);
+    const int ks_x = 4 * (s16 >> 2) + 2 * (g & 1);
+    uint32_t ks_unit[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-        b_unit[j] = (uint32_t)(((2 * j + ((s16 & 3) >> 1)) ^ b_x) * 16);
-
+        ks_unit[j] = (uint32_t)(((2 * j + ((s16 & 3) >> 1)) ^ ks_x) * 16);
+    auto kc_lane = [&](uint32_t region, int base) {
+        return region + (uint32_t)((base + s16) * 64 + ((g ^ kc_sw) * 16));
+    };
+    auto ks_lane = [&](uint32_t region, int base) {
+        return region + (uint32_t)((8 * g + (s16 >> 2)) * 512 + 8 * (s16 & 1) + 2 * base);
+    };
+    const uint32_t a_lane = TA ? ks_lane(0, wr) : kc_lane(0, wr);
+    const uint32_t b_lane = TB ? kc_lane(A_BYTES, wc) : ks_lane(A_BYTES, wc);
+    auto read_block = [&](const uint8_t *buf, uint32_t lane_off, bool kstrided, int blk) -> halfx8 {
+        if (!kstrided)
+            return *reinterpret_cast<const halfx8 *>(buf + lane_off + blk * 1024);
+        const uint8_t *p = buf + lane_off + ks_unit[blk];
+        const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4 *)p);
+        const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4 *)(p + 2048));
+        return __builtin_bit_cast(halfx8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
     // read r (0..15) of stage `stage`: A block 0, the eight B blocks, then A
-    // blocks 1..7 (the order the next stage's first MFMAs want them).  A B
-    // block is two transposing reads, rows kb..kb+3 and kb+4..kb+7.
+    // blocks 1..7 (the order the next stage's first MFMAs want them)
     auto fread = [&](int stage, int r, halfx8 *fa, halfx8 *fb) {
         const uint8_t *buf = lds + (stage % NBUF) * STAGE_BYTES;
         if (r == 0 || r >= 9) {
             const int i = r == 0 ? 0 : r - 8;
-            fa[i] = *reinterpret_cast<const halfx8 *>(buf + a_lane + i * 1024);
+            fa[i] = read_block(buf, a_lane, TA, i);
         } else {
-            const int j = r - 1;
-            const uint8_t *bp = buf + b_lane + b_unit[j];
-            const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4 *)bp);
-            const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4 *)(bp + 2048));
-            fb[j] = __builtin_bit_cast(halfx8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            fb[r - 1] = read_block(buf, b_lane, !TB, r - 1);
         }
     };
 
+    // ---- C tile: lane (g, s) of the wave owns rows 16 i + 4 g + r and
+    // columns 16 j + s of the wave's 128 x 128 block.  An element outside C
+    // gets an out-of-range lane offset, so it reads zero and is not written.
+    const int ldc = args.ldc;
+    const int c_col = n0 + wc + s16;
+    const int c_rows_left = M - m0 - wr - 4 * g;
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(
+        args.C + (size_t)(m0 + wr) * ldc + n0 + wc, ((long long)(M - m0 - wr - 1) * ldc + N - n0 - wc) * 4);
+    auto c_offset = [&](int col, int rows_left, int i, int j, int r, uint32_t &vo, uint32_t &so) {
+        const int ro = 16 * i + r;
+        vo = (ro < rows_left && col + 16 * j < N) ? (uint32_t)((4 * g) * ldc + s16 + 16 * j) * 4u : OOB;
+        so = (uint32_t)(ro * ldc) * 4u;
+    };
+
+    // Accumulators start at zero, or at C itself (ACC: C += op(A) op(B)).
     floatx4 acc[8][8];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
         for (int j = 0; j < 8; ++j)
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                acc[i][j][r] = 0.f;
+            for (int r = 0; r < 4; ++r) {
+                if (ACC) {
+                    uint32_t vo, so;
+                    c_offset(c_col, c_rows_left, i, j, r, vo, so);
+                    acc[i][j][r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rc, vo, so, 0));
+                } else {
+                    acc[i][j][r] = 0.f;
+                }
+            }
 
     // One stage: the 64 MFMAs of stage t from (ca, cb); the 16 fragment
     // reads of stage t + 1 into (na, nb), one after each of the first 16
@@ -433,25 +509,24 @@ __global__ __launch_bounds__(256) void mfma_f16_pipe_kernel(
     // no load may still be writing this workgroup's LDS when it ends
     __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
 
-    // Epilogue: buffer stores; an element outside C gets an out-of-range lane
-    // offset and is dropped.
-    const int col = n0 + wc + s16;
-    const int rows_left = M - m0 - wr - 4 * g;
-    const __amdgpu_buffer_rsrc_t rc =
-        make_rsrc(C + (size_t)(m0 + wr) * N + n0 + wc, ((long long)(M - m0 - wr) * N - n0 - wc) * 4);
+    // Epilogue: write the accumulators (ACC: they started from C).  No
+    // vector instruction touches them on the way: arithmetic here makes the
+    // compiler hold them in ordinary registers, which do not fit beside the
+    // fragments, so scaling by alpha and beta is left to separate passes.
+    // The offsets are recomputed from opaque copies: shared with the loads
+    // above, they would stay live across the loop and crowd it out.
+    int col_e = c_col, rows_e = c_rows_left;
+    asm volatile("" : "+v"(col_e), "+v"(rows_e));
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const uint32_t cv = (col + 16 * j < N) ? (uint32_t)((4 * g) * N + s16 + 16 * j) * 4u : OOB;
+    for (int j = 0; j < 8; ++j)
 #pragma unroll
         for (int i = 0; i < 8; ++i)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int ro = 16 * i + r;
-                const float v = acc[i][j][r];
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rc, ro < rows_left ? cv : OOB,
-                                                      (uint32_t)(ro * N) * 4u, 0);
+                uint32_t vo, so;
+                c_offset(col_e, rows_e, i, j, r, vo, so);
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][r]), rc, vo, so, 0);
             }
-    }
 }
 
 template <class Op, int BM, int BN, int BK, int WM, int WN>
@@ -475,15 +550,31 @@ hipError_t launch_cfg(const Problem &p, const gemm_plan &plan, hipStream_t s)
     return hipGetLastError();
 }
 
+template <class Op, bool TA, bool TB>
+hipError_t launch_ring(const RingArgs &a, hipStream_t s)
+{
+    const dim3 grid(a.tiles_m * a.tiles_n);
+    if (a.accumulate)
+        hipLaunchKernelGGL((mfma_f16_pipe_kernel<Op, TA, TB, true>), grid, dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL((mfma_f16_pipe_kernel<Op, TA, TB, false>), grid, dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+template <class Op>
+hipError_t launch_ring_any(const RingArgs &a, hipStream_t s)
+{
+    if (a.trans_a)
+        return a.trans_b ? launch_ring<Op, true, true>(a, s) : launch_ring<Op, true, false>(a, s);
+    return a.trans_b ? launch_ring<Op, false, true>(a, s) : launch_ring<Op, false, false>(a, s);
+}
+
 template <class Op>
 hipError_t launch_op(const Problem &p, const gemm_plan &plan, hipStream_t s)
 {
     if (plan.tile_m == 256 && plan.tile_n == 256) {
         if (direct_lds_applies(plan.tile_m, 256, p.vec_a, p.vec_b, p.N, p.K)) {
-            hipLaunchKernelGGL(mfma_f16_pipe_kernel<Op>, dim3(plan.grid_x * plan.grid_y), dim3(256), 0, s,
-                               p.M, p.N, p.K, (const uint16_t *)p.A, (const uint16_t *)p.B, p.C,
-                               plan.grid_y, plan.grid_x, 4);
-            return hipGetLastError();
+            return launch_ring<Op, false, false>(ring_args_nn(p, plan), s);
         }
         return launch_cfg<Op, 256, 256, 32, 2, 2>(p, plan, s);
     }
@@ -499,6 +590,11 @@ hipError_t launch_op(const Problem &p, const gemm_plan &plan, hipStream_t s)
 hipError_t launch_mfma_f16(const Problem &p, const gemm_plan &plan, hipStream_t s, bool bf16)
 {
     return bf16 ? launch_op<OpBF16>(p, plan, s) : launch_op<OpF16>(p, plan, s);
+}
+
+hipError_t launch_ring16(const RingArgs &a, hipStream_t s, bool bf16)
+{
+    return bf16 ? launch_ring_any<OpBF16>(a, s) : launch_ring_any<OpF16>(a, s);
 }
 
 }  // namespace dgor

@@ -328,40 +328,85 @@ __global__ __launch_bounds__(256) void mfma_f32_dma_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Large FP32 tile (16-byte aligned operands, at least one 256 x 256 tile per
-// compute unit): 256 x 256 workgroup tile, 16-deep k-stages in a ring of four
-// LDS buffers, four wavefronts of 128 x 128 (4 x 4 blocks of 32 x 32, 256
-// accumulators per lane).  The structure is that of the FP16 ring kernel:
-// direct global->LDS loads issued from assembly, one vmcnt wait and one
-// barrier per stage, the reads of stage t + 1 and the loads of stage t + 3
-// spread between the 128 MFMAs of stage t.
-// * LDS layout of one stage, in 16-byte units (4 floats):
-//     A (256 m x 16 k, 4 units per row): unit c of row r at 4 r + (c ^ ((r >> 2) & 3));
-//     B (16 k x 256 n, 64 units per row): unit u of row k at 64 k + (u ^ (8 ((k >> 2) & 1))).
-//   For k-slice q (8 deep) of a stage, lane l reads with one 128-bit read the
-//   four A values k = 8q + 4 (l / 32) + 0..3 of its row, and with four 32-bit
-//   reads the B values of the same four k in its column; 32 lanes read 32
-//   rows at one unit (A) or 32 columns of one row (B), and the swizzles keep
-//   both on distinct banks.
+// Large FP32 tile (16-byte aligned operands): 256 x 256 workgroup tile,
+// 16-deep k-stages in a ring of four LDS buffers, four wavefronts of
+// 128 x 128 (4 x 4 blocks of 32 x 32, 256 accumulators per lane).  The
+// structure is that of the 16-bit ring kernel: direct global->LDS loads
+// issued from assembly, one vmcnt wait and one barrier per stage, the reads
+// of stage t + 1 and the loads of stage t + 3 spread between the 128 MFMAs
+// of stage t.
+// * Each operand tile is stored in one of two ways (16-byte units of 4
+//   floats):
+//     k-contiguous (A, or B given as N x K): 256 rows of 16 k, unit c of
+//       row r at 4 r + (c ^ ((r >> 2) & 3));
+//     k-strided (B, or A given as K x M): 16 k rows of 256, unit u of row k
+//       at 64 k + (u ^ (8 ((k >> 2) & 1))).
+//   For k-slice q (8 deep) of a stage, lane l wants, of its row of op(A) or
+//   column of op(B), the four values k = 8q + 4 (l / 32) + 0..3, one per
+//   MFMA of a group of four: from the k-contiguous layout that is one
+//   128-bit read, from the k-strided one four 32-bit reads (32 lanes read 32
+//   consecutive values of one row).  The swizzles keep both on distinct banks.
 namespace f32ring {
 constexpr int BM = 256, BN = 256, BK = 16, NBUF = 4;
 constexpr int A_BYTES = BM * BK * 4;                 // 16 KB
 constexpr int B_BYTES = BK * BN * 4;                 // 16 KB
 constexpr int STAGE_BYTES = A_BYTES + B_BYTES;       // 32 KB
 constexpr int LDS_BYTES = NBUF * STAGE_BYTES;        // 128 KB
-constexpr int LOADS_PER_STAGE = 8;                   // per wavefront: 4 of A, 4 of B
+constexpr int LOADS_PER_STAGE = 8;                   // per wavefront: 4 per operand
+
+// Lane offsets of wave w's four 1 KB loads of one operand tile per stage,
+// relative to the stage's first element (as for the 16-bit ring).
+template <bool KSTRIDED>
+__device__ __forceinline__ void load_offsets(int wave, int lane, int t0, int ext, int ld,
+                                             uint32_t off[4], int &kc)
+{
+    constexpr uint32_t OOB = 0x80000000u;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        if (!KSTRIDED) {
+            const int r = 16 * (4 * wave + q) + (lane >> 2);
+            kc = 4 * ((lane & 3) ^ ((lane >> 4) & 3));   // same in every block
+            off[q] = (uint32_t)(r * ld + kc) * 4u;
+        } else {
+            const int k = 4 * wave + q;
+            const int u = lane ^ (8 * ((k >> 2) & 1));
+            off[q] = t0 + 4 * u < ext ? (uint32_t)(k * ld + 4 * u) * 4u : OOB;
+            kc = 0;
+        }
+    }
+}
+
+// Range in bytes of one stage's descriptor (first element: row t0, k0 for
+// the k-contiguous layout; row k0, column t0 for the k-strided one).
+template <bool KSTRIDED>
+__device__ __forceinline__ int stage_range(int k0, int K, int t0, int ext, int ld)
+{
+    const int k_left = K - k0;
+    if (k_left <= 0)
+        return 0;
+    if (!KSTRIDED) {
+        if (t0 + 256 <= ext)
+            return 0x7fffffff;
+        return (int)(((uint32_t)(ext - t0 - 1) * (uint32_t)ld + (uint32_t)k_left) * 4u);
+    }
+    if (k_left >= 16)
+        return 0x7fffffff;
+    return (int)(((uint32_t)(k_left - 1) * (uint32_t)ld + (uint32_t)(ext - t0)) * 4u);
+}
 }  // namespace f32ring
 
-__global__ __launch_bounds__(256) void mfma_f32_ring_kernel(
-    int M, int N, int K, const float *__restrict__ A, const float *__restrict__ B,
-    float *__restrict__ C, int tiles_m, int tiles_n, int group_m)
+template <bool TA, bool TB, bool ACC>
+__global__ __launch_bounds__(256) void mfma_f32_ring_kernel(RingArgs args)
 {
     using namespace f32ring;
     __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
     const uint32_t ring = lds_address(lds);
+    const int M = args.M, N = args.N, K = args.K, lda = args.lda, ldb = args.ldb;
+    const float *__restrict__ A = (const float *)args.A;
+    const float *__restrict__ B = (const float *)args.B;
 
     int tm, tn;
-    dgor_tile_of_block(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
+    dgor_tile_of_block(blockIdx.x, args.tiles_m, args.tiles_n, args.group_m, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const int lane = threadIdx.x & 63;
     // wave-uniform, so per-wave offsets and descriptors stay scalar
@@ -369,92 +414,108 @@ __global__ __launch_bounds__(256) void mfma_f32_ring_kernel(
     const int wr = (wave >> 1) * 128, wc = (wave & 1) * 128;
     constexpr uint32_t OOB = 0x80000000u;
 
-    // ---- loader.  Per stage, wavefront w fills A blocks 4w..4w+3 (16 rows
-    // each) and B blocks 4w..4w+3 (one k row of 256 floats each).  Lane
-    // offsets are relative to the stage's first element; columns past N get
-    // OOB.  The descriptor ranges end at the last row of A and at row K of B;
-    // A columns past K are masked per lane in the last stage; a stage past
-    // the last one gets empty ranges, so its loads write zeros.
-    const int a_c = (lane & 3) ^ ((lane >> 4) & 3);   // logical unit; same in every block
+    // ---- loader (see the 16-bit ring kernel for the range rules)
     uint32_t a_off[4], b_off[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int r = 16 * (4 * wave + q) + (lane >> 2);
-        a_off[q] = (uint32_t)(r * K + 4 * a_c) * 4u;
-        const int k = 4 * wave + q;
-        const int u = lane ^ (8 * ((k >> 2) & 1));
-        b_off[q] = n0 + 4 * u < N ? (uint32_t)(k * N + 4 * u) * 4u : OOB;
-    }
-    const bool a_full = m0 + BM <= M;
-    const uint32_t a_rows_bytes = (uint32_t)(M - m0) * (uint32_t)K * 4u;   // < 2^31 when !a_full
+    int a_kc, b_kc;
+    load_offsets<TA>(wave, lane, m0, M, lda, a_off, a_kc);
+    load_offsets<!TB>(wave, lane, n0, N, ldb, b_off, b_kc);
     const uint32_t lds_a = ring + (uint32_t)(4 * wave * 1024);
     const uint32_t lds_b = ring + (uint32_t)(A_BYTES + 4 * wave * 1024);
-    struct StageLoads { intx4 ra, rb; uint32_t lds; bool a_tail; int k_left; };
+    struct StageLoads { intx4 ra, rb; uint32_t lds; bool tail; int k_left; };
     auto prep = [&](int st) {
         StageLoads L;
         const int k0 = st * BK;
-        const int k_left = K - k0;
-        L.ra = rsrc_words(A + (size_t)m0 * K + k0, 0);
-        L.ra.z = k_left <= 0 ? 0 : (a_full ? 0x7fffffff : (int)(a_rows_bytes - (uint32_t)k0 * 4u));
-        L.rb = rsrc_words(B + (size_t)k0 * N + n0, 0);
-        L.rb.z = k_left >= BK ? 0x7fffffff
-                              : (k_left <= 0 ? 0 : (int)(((uint32_t)k_left * (uint32_t)N - (uint32_t)n0) * 4u));
+        L.ra = rsrc_words(TA ? A + (size_t)k0 * lda + m0 : A + (size_t)m0 * lda + k0, 0);
+        L.ra.z = stage_range<TA>(k0, K, m0, M, lda);
+        L.rb = rsrc_words(TB ? B + (size_t)n0 * ldb + k0 : B + (size_t)k0 * ldb + n0, 0);
+        L.rb.z = stage_range<!TB>(k0, K, n0, N, ldb);
         L.lds = (uint32_t)((st % NBUF) * STAGE_BYTES);
-        L.a_tail = k_left < BK;
-        L.k_left = k_left;
+        L.k_left = K - k0;
+        L.tail = L.k_left < BK;
         return L;
     };
     auto load = [&](const StageLoads &L, int q) {
         if (q < 4) {
-            const uint32_t off = (L.a_tail && 4 * a_c >= L.k_left) ? OOB : a_off[q];
+            const uint32_t off = (!TA && L.tail && a_kc >= L.k_left) ? OOB : a_off[q];
             load_to_lds(L.ra, lds_a + L.lds + (uint32_t)(q * 1024), off);
         } else {
-            load_to_lds(L.rb, lds_b + L.lds + (uint32_t)((q - 4) * 1024), b_off[q - 4]);
+            const uint32_t off = (TB && L.tail && b_kc >= L.k_left) ? OOB : b_off[q - 4];
+            load_to_lds(L.rb, lds_b + L.lds + (uint32_t)((q - 4) * 1024), off);
         }
     };
 
     // ---- fragment reads.  Lane (g, l32) = (lane / 32, lane % 32).
     const int l32 = lane & 31, g = lane >> 5;
-    const uint32_t a_lane = (uint32_t)((wr + l32) * 64);
-    const int a_sw = (l32 >> 2) & 3;
-    // B value (k-slice q, sub-step j', block j): row 8q + 4g + j', unit
-    // (wc + 32 j + l32) / 4 ^ 8g, float l32 % 4 of the unit
-    const uint32_t b_lane = (uint32_t)(A_BYTES + (4 * g) * 1024 + 4 * (l32 & 3));
-    uint32_t b_unit[4];
+    const int kc_sw = (l32 >> 2) & 3;
+    auto kc_lane = [&](uint32_t region, int base) { return region + (uint32_t)((base + l32) * 64); };
+    auto ks_lane = [&](uint32_t region) { return region + (uint32_t)((4 * g) * 1024 + 4 * (l32 & 3)); };
+    uint32_t a_unit[4], b_unit[4];   // k-strided column units of each block
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 4; ++j) {
+        a_unit[j] = (uint32_t)((((wr + 32 * j + l32) >> 2) ^ (8 * g)) * 16);
         b_unit[j] = (uint32_t)((((wc + 32 * j + l32) >> 2) ^ (8 * g)) * 16);
-
-    // read r (0..39) of stage `stage`: k-slice r / 20; within it the four A
-    // blocks, then the B values in the order the MFMAs use them (sub-step
-    // j' outer, block j inner)
-    auto fread = [&](int stage, int r, floatx4 *fa, float *fb) {
+    }
+    const uint32_t a_lane = TA ? ks_lane(0) : kc_lane(0, wr);
+    const uint32_t b_lane = TB ? kc_lane(A_BYTES, wc) : ks_lane(A_BYTES);
+    // One read instruction of operand X (k-slice q, block blk, sub-step e of
+    // a k-strided block) into x[4 q + blk].
+    auto read_one = [&](const uint8_t *buf, uint32_t lane_off, const uint32_t *unit, bool kstrided, int q,
+                        int blk, int e, floatx4 *x) {
+        if (!kstrided)
+            x[4 * q + blk] = *reinterpret_cast<const floatx4 *>(
+                buf + lane_off + blk * 32 * 64 + (((2 * q + g) ^ kc_sw) * 16));
+        else
+            x[4 * q + blk][e] = *reinterpret_cast<const float *>(buf + lane_off + (8 * q + e) * 1024 + unit[blk]);
+    };
+    // Read r of stage `stage`, in k-slice order; within a slice, for each
+    // block, A's read(s) then B's.
+    constexpr int NA = TA ? 4 : 1, NB = TB ? 1 : 4, PER = NA + NB;
+    constexpr int READS = 8 * PER;
+    auto fread = [&](int stage, int r, floatx4 *fa, floatx4 *fb) {
         const uint8_t *buf = lds + (stage % NBUF) * STAGE_BYTES;
-        const int q = r / 20, x = r % 20;
-        if (x < 4) {
-            fa[4 * q + x] = *reinterpret_cast<const floatx4 *>(
-                buf + a_lane + x * 32 * 64 + (((2 * q + g) ^ a_sw) * 16));
-        } else {
-            const int jp = (x - 4) >> 2, j = (x - 4) & 3;
-            fb[16 * q + 4 * jp + j] =
-                *reinterpret_cast<const float *>(buf + b_lane + (8 * q + jp) * 1024 + b_unit[j]);
-        }
+        const int item = r / PER, x = r % PER, q = item >> 2, blk = item & 3;
+        if (x < NA)
+            read_one(buf, a_lane, a_unit, TA, q, blk, x, fa);
+        else
+            read_one(buf, b_lane, b_unit, !TB, q, blk, x - NA, fb);
     };
 
+    // ---- C tile: lane (g, l32) owns rows 32 i + 8 (r / 4) + 4 g + r % 4 and
+    // columns 32 j + l32 of the wave's block.
+    const int ldc = args.ldc;
+    const int c_col = n0 + wc + l32;
+    const int c_rows_left = M - m0 - wr - 4 * g;
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(
+        args.C + (size_t)(m0 + wr) * ldc + n0 + wc, ((long long)(M - m0 - wr - 1) * ldc + N - n0 - wc) * 4);
+    auto c_offset = [&](int col, int rows_left, int i, int j, int r, uint32_t &vo, uint32_t &so) {
+        const int ro = 32 * i + 8 * (r >> 2) + (r & 3);
+        vo = (ro < rows_left && col + 32 * j < N) ? (uint32_t)((4 * g) * ldc + l32 + 32 * j) * 4u : OOB;
+        so = (uint32_t)(ro * ldc) * 4u;
+    };
+
+    // Accumulators start at zero, or at C itself (ACC: C += op(A) op(B)).
     floatx16 acc[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                acc[i][j][r] = 0.f;
+            for (int r = 0; r < 16; ++r) {
+                if (ACC) {
+                    uint32_t vo, so;
+                    c_offset(c_col, c_rows_left, i, j, r, vo, so);
+                    acc[i][j][r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rc, vo, so, 0));
+                } else {
+                    acc[i][j][r] = 0.f;
+                }
+            }
 
-    // One stage: the 128 MFMAs of stage t from (ca, cb); the 40 reads of
-    // stage t + 1 into (na, nb), one after each of the first 40 MFMAs; the 8
-    // loads of stage t + 3, one after every eleventh MFMA from the 44th.
+    // One stage: the 128 MFMAs of stage t from (ca, cb); the reads of stage
+    // t + 1 into (na, nb), one after each of the first READS MFMAs (at most
+    // 64); the 8 loads of stage t + 3, one after every eighth MFMA from the
+    // 64th.
     const int steps = (K + BK - 1) / BK;
-    auto stage = [&](int t, floatx4 *ca, float *cb, floatx4 *na, float *nb) {
+    auto stage = [&](int t, floatx4 *ca, floatx4 *cb, floatx4 *na, floatx4 *nb) {
         __builtin_amdgcn_s_waitcnt(wait_vmcnt(LOADS_PER_STAGE));
         __builtin_amdgcn_s_barrier();
         const StageLoads L = prep(t + 3);
@@ -462,12 +523,12 @@ __global__ __launch_bounds__(256) void mfma_f32_ring_kernel(
 #pragma unroll
         for (int m = 0; m < 128; ++m) {
             const int q = m >> 6, jp = (m >> 4) & 3, i = (m >> 2) & 3, j = m & 3;
-            const floatx4 av = ca[4 * q + i];
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[jp], cb[16 * q + 4 * jp + j], acc[i][j], 0, 0, 0);
-            if (m < 40)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(ca[4 * q + i][jp], cb[4 * q + j][jp], acc[i][j], 0,
+                                                              0, 0);
+            if (m < READS)
                 fread(t + 1, m, na, nb);
-            if (m >= 44 && (m - 44) % 11 == 0 && (m - 44) / 11 < 8)
-                load(L, (m - 44) / 11);
+            if (m >= 64 && (m - 64) % 8 == 0)
+                load(L, (m - 64) / 8);
             // keep this order: the compiler would otherwise cluster the reads
             // and loads, and move MFMAs across the barrier
             __builtin_amdgcn_sched_barrier(0);
@@ -475,8 +536,7 @@ __global__ __launch_bounds__(256) void mfma_f32_ring_kernel(
     };
 
     // prologue: loads of stages 0, 1, 2, then the reads of stage 0
-    floatx4 fa0[8], fa1[8];
-    float fb0[32], fb1[32];
+    floatx4 fa0[8], fa1[8], fb0[8], fb1[8];
 #pragma unroll
     for (int st = 0; st < 3; ++st) {
         const StageLoads L = prep(st);
@@ -487,7 +547,7 @@ __global__ __launch_bounds__(256) void mfma_f32_ring_kernel(
     __builtin_amdgcn_s_waitcnt(wait_vmcnt(2 * LOADS_PER_STAGE));
     __builtin_amdgcn_s_barrier();
 #pragma unroll
-    for (int r = 0; r < 40; ++r)
+    for (int r = 0; r < READS; ++r)
         fread(0, r, fa0, fb0);
 
     for (int t = 0; t < steps; t += 2) {
@@ -498,25 +558,31 @@ __global__ __launch_bounds__(256) void mfma_f32_ring_kernel(
     // no load may still be writing this workgroup's LDS when it ends
     __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
 
-    // Epilogue: buffer stores; an element outside C gets an out-of-range lane
-    // offset and is dropped.  Lane (g, l32) holds rows 8 (r / 4) + 4 g + r % 4.
-    const int col = n0 + wc + l32;
-    const int rows_left = M - m0 - wr - 4 * g;
-    const __amdgpu_buffer_rsrc_t rc =
-        make_rsrc(C + (size_t)(m0 + wr) * N + n0 + wc, ((long long)(M - m0 - wr) * N - n0 - wc) * 4);
+    // Epilogue: write the accumulators, unchanged (see the 16-bit ring
+    // kernel); offsets are recomputed from opaque copies.
+    int col_e = c_col, rows_e = c_rows_left;
+    asm volatile("" : "+v"(col_e), "+v"(rows_e));
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const uint32_t cv = (col + 32 * j < N) ? (uint32_t)((4 * g) * N + l32 + 32 * j) * 4u : OOB;
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int ro = 32 * i + 8 * (r >> 2) + (r & 3);
-                const float v = acc[i][j][r];
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rc, ro < rows_left ? cv : OOB,
-                                                      (uint32_t)(ro * N) * 4u, 0);
+                uint32_t vo, so;
+                c_offset(col_e, rows_e, i, j, r, vo, so);
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][r]), rc, vo, so, 0);
             }
-    }
+}
+
+template <bool TA, bool TB>
+hipError_t launch_ring32_t(const RingArgs &a, hipStream_t s)
+{
+    const dim3 grid(a.tiles_m * a.tiles_n);
+    if (a.accumulate)
+        hipLaunchKernelGGL((mfma_f32_ring_kernel<TA, TB, true>), grid, dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL((mfma_f32_ring_kernel<TA, TB, false>), grid, dim3(256), 0, s, a);
+    return hipGetLastError();
 }
 
 template <int BM, int BN, int BK, int WM, int WN>
@@ -547,10 +613,7 @@ hipError_t launch_mfma_f32(const Problem &p, const gemm_plan &plan, hipStream_t 
     if (plan.tile_m == kF32RingTile) {   // the planner chose it only where f32_ring_applies
         if (!f32_ring_applies(p.M, p.N, p.K, p.vec_a, p.vec_b))
             return hipErrorInvalidValue;
-        hipLaunchKernelGGL(mfma_f32_ring_kernel, dim3(plan.grid_x * plan.grid_y), dim3(256), 0, s,
-                           p.M, p.N, p.K, (const float *)p.A, (const float *)p.B, p.C,
-                           plan.grid_y, plan.grid_x, 4);
-        return hipGetLastError();
+        return launch_ring32_t<false, false>(ring_args_nn(p, plan), s);
     }
     if (plan.tile_m == 128 && plan.tile_n == 128) {
         if (direct_lds_applies(plan.tile_m, 128, p.vec_a, p.vec_b, p.N, p.K)) {
@@ -566,6 +629,13 @@ hipError_t launch_mfma_f32(const Problem &p, const gemm_plan &plan, hipStream_t 
     if (plan.tile_m == 32 && plan.tile_n == 64)
         return launch_cfg<32, 64, 16, 1, 2>(p, plan, s);
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_ring32(const RingArgs &a, hipStream_t s)
+{
+    if (a.trans_a)
+        return a.trans_b ? launch_ring32_t<true, true>(a, s) : launch_ring32_t<true, false>(a, s);
+    return a.trans_b ? launch_ring32_t<false, true>(a, s) : launch_ring32_t<false, false>(a, s);
 }
 
 }  // namespace dgor

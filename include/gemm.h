@@ -47,7 +47,8 @@ typedef enum {
     GEMM_ERR_LAUNCH = -3,
     GEMM_ERR_UNSUPPORTED_DEVICE = -4,
     GEMM_ERR_INVALID_VARIANT = -5,
-    GEMM_ERR_RUNTIME = -6
+    GEMM_ERR_RUNTIME = -6,
+    GEMM_ERR_INVALID_LAYOUT = -7
 } gemm_status;
 
 /*
@@ -148,6 +149,45 @@ int gemm_f16_f32acc_plan(int variant, int M, int N, int K, const uint16_t *A,
                          const uint16_t *B, const float *C, gemm_plan *plan);
 int gemm_bf16_f32acc_plan(int variant, int M, int N, int K, const uint16_t *A,
                           const uint16_t *B, const float *C, gemm_plan *plan);
+
+/*
+ * General operand layouts and scaling, the interface "Lesson 8: how a GPU
+ * does matrix multiply", section 28, describes libraries exposing (with the
+ * D = A x B + C of its section 21):
+ *     C = alpha * op(A) * op(B) + beta * C,   op(A) M x K, op(B) K x N,
+ * where op(X) is X (GEMM_OP_N) or its transpose (GEMM_OP_T), all matrices
+ * row-major with the given leading dimensions (row strides, in elements):
+ *     opA N: A is M x K, A[i*lda + k], lda >= K;  opA T: A is K x M, lda >= M;
+ *     opB N: B is K x N, B[k*ldb + j], ldb >= N;  opB T: B is N x K, ldb >= K;
+ *     C is M x N, C[i*ldc + j], ldc >= N.
+ * Products are exact and summed in FP32 as in the plain entry points.  When
+ * beta == 0, C is not read (it may hold anything); when K == 0 or alpha == 0,
+ * A and B are not used and C = beta * C.
+ * Calls with 16-byte aligned A and B, leading dimensions (and the
+ * dimension read along rows of a transposed operand) in whole 16-byte
+ * vectors take the 256 x 256 ring kernels; C = alpha A B + beta C is then
+ * formed from C = A B or C += A B and separate scaling passes over C
+ * (alpha != 1 and beta != 0 together: C *= beta / alpha first, C *= alpha
+ * last, so the beta C term may differ from the one-step value by a few
+ * units in its last place).  Other calls take a plain kernel that forms
+ * alpha * sum + beta * C directly.  The plain row-major case (N, N,
+ * lda = K, ldb = ldc = N, alpha 1, beta 0) is exactly gemm_f32 /
+ * gemm_f16_f32acc / gemm_bf16_f32acc.
+ * Errors as for those, plus GEMM_ERR_INVALID_LAYOUT for an op flag other
+ * than GEMM_OP_N / GEMM_OP_T or a leading dimension below its minimum
+ * (checked before anything else but negative dimensions).
+ */
+typedef enum { GEMM_OP_N = 0, GEMM_OP_T = 1 } gemm_op;
+
+int gemm_f32_ex(int opA, int opB, int M, int N, int K, float alpha,
+                const float *A, int lda, const float *B, int ldb, float beta,
+                float *C, int ldc, void *stream);
+int gemm_f16_f32acc_ex(int opA, int opB, int M, int N, int K, float alpha,
+                       const uint16_t *A, int lda, const uint16_t *B, int ldb,
+                       float beta, float *C, int ldc, void *stream);
+int gemm_bf16_f32acc_ex(int opA, int opB, int M, int N, int K, float alpha,
+                        const uint16_t *A, int lda, const uint16_t *B, int ldb,
+                        float beta, float *C, int ldc, void *stream);
 
 /* Static, NUL-terminated descriptions; never NULL ("unknown ..." for values
  * outside the enums). */

@@ -60,6 +60,9 @@ def configure(lib):
         f = getattr(lib, name)
         f.argtypes = [i, i, i, p, p, i64, p, p, p, i]
         f.restype = i
+    d = ctypes.c_double
+    lib.oracle_gemm_ex.argtypes = [i, i, i, i, i, i, d, p, i, p, i, d, p, i, i]
+    lib.oracle_gemm_ex.restype = i
     return lib
 
 
@@ -185,3 +188,36 @@ def gemm_bf16_at(A, B, rows, cols, nthreads: int = 0) -> np.ndarray:
     """C[rows[t], cols[t]] of A x B for bfloat16 bit-pattern inputs, one dot product each."""
     A, B = _check_inputs(A, B, np.uint16)
     return _at("oracle_gemm_bf16_at", A, B, rows, cols, nthreads)
+
+
+_IN_CODE = {"f32": 0, "f16": 1, "bf16": 2}
+
+
+def gemm_ex(fmt: str, op_a: int, op_b: int, M: int, N: int, K: int, alpha: float,
+            A: np.ndarray, lda: int, B: np.ndarray, ldb: int, beta: float,
+            C: np.ndarray, ldc: int, nthreads: int = 0) -> np.ndarray:
+    """C = alpha op(A) op(B) + beta C in place on the flat float32 array C
+    (row stride ldc); A and B are flat arrays holding the operands with the
+    given row strides (binary16 as float16 or uint16 bits, bfloat16 as uint16
+    bits).  Returns C."""
+    code = _IN_CODE[fmt]
+    A = np.ascontiguousarray(A)
+    B = np.ascontiguousarray(B)
+    if fmt == "f16":
+        A = A.view(np.uint16) if A.dtype == np.float16 else A
+        B = B.view(np.uint16) if B.dtype == np.float16 else B
+    want = np.float32 if fmt == "f32" else np.uint16
+    if A.dtype != want or B.dtype != want:
+        raise TypeError(f"{fmt} oracle expects {np.dtype(want).name} operands")
+    if C.dtype != np.float32 or not C.flags.c_contiguous:
+        raise ValueError("C must be a contiguous float32 array")
+    need_a = ((K - 1) * lda + M if op_a else (M - 1) * lda + K) if M and K else 0
+    need_b = ((N - 1) * ldb + K if op_b else (K - 1) * ldb + N) if N and K else 0
+    need_c = (M - 1) * ldc + N if M and N else 0
+    if A.size < need_a or B.size < need_b or C.size < need_c:
+        raise ValueError("operand arrays too small for the given shape and strides")
+    rc = _load().oracle_gemm_ex(code, op_a, op_b, M, N, K, float(alpha), _ptr(A), lda, _ptr(B), ldb,
+                                float(beta), _ptr(C), ldc, nthreads)
+    if rc != 0:
+        raise RuntimeError(f"oracle_gemm_ex failed ({rc})")
+    return C

@@ -303,3 +303,49 @@ int oracle_gemm_bf16_at(int M, int N, int K, const uint16_t *A,
     }
     return ORACLE_OK;
 }
+
+/*
+ * General layouts and scaling: C = alpha * op(A) * op(B) + beta * C, the form
+ * "Lesson 8: how a GPU does matrix multiply", section 28, says libraries
+ * expose (its section 21 writes the matrix unit's D = A x B + C).
+ *   op(A)[i][k] = A[i*lda + k]      (opA == 0)  or  A[k*lda + i]  (opA == 1)
+ *   op(B)[k][j] = B[k*ldb + j]      (opB == 0)  or  B[j*ldb + k]  (opB == 1)
+ *   C[i][j]     = C[i*ldc + j]
+ * Each element: the binary64 sum of the exact products in ascending k from
+ * +0.0, then alpha * sum + beta * C_in in binary64 (C_in is not read when
+ * beta == 0), rounded once to binary32.  `in` selects the input format:
+ * 0 binary32, 1 binary16 bits, 2 bfloat16 bits.
+ */
+static double oracle_in_value(int in, const void *p, size_t idx)
+{
+    if (in == 0)
+        return (double)((const float *)p)[idx];
+    const uint16_t h = ((const uint16_t *)p)[idx];
+    return in == 1 ? oracle_f16_to_f64(h) : oracle_bf16_to_f64(h);
+}
+
+int oracle_gemm_ex(int in, int opA, int opB, int M, int N, int K, double alpha,
+                   const void *A, int lda, const void *B, int ldb, double beta,
+                   float *C, int ldc, int nthreads)
+{
+    if (M < 0 || N < 0 || K < 0 || in < 0 || in > 2 || opA < 0 || opA > 1 || opB < 0 || opB > 1)
+        return ORACLE_ERR_DIM;
+    if (lda < (opA ? M : K) || ldb < (opB ? K : N) || ldc < N)
+        return ORACLE_ERR_DIM;
+#pragma omp parallel for num_threads(thread_count(nthreads)) schedule(static)
+    for (int i = 0; i < M; ++i) {
+        for (int j = 0; j < N; ++j) {
+            double acc = 0.0;
+            for (int k = 0; k < K; ++k) {
+                const size_t ia = opA ? (size_t)k * lda + i : (size_t)i * lda + k;
+                const size_t ib = opB ? (size_t)j * ldb + k : (size_t)k * ldb + j;
+                acc += oracle_in_value(in, A, ia) * oracle_in_value(in, B, ib);
+            }
+            double v = alpha * acc;
+            if (beta != 0.0)
+                v += beta * (double)C[(size_t)i * ldc + j];
+            C[(size_t)i * ldc + j] = (float)v;
+        }
+    }
+    return ORACLE_OK;
+}

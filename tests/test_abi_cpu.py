@@ -63,7 +63,7 @@ def test_header_is_plain_c(tmp_path):
 
 def test_status_and_variant_names():
     assert dg.status_string(0) == "ok"
-    for s in range(-6, 0):
+    for s in range(-7, 0):
         assert dg.status_string(s) and dg.status_string(s) != "unknown status"
     assert dg.status_string(-99) == "unknown status"
     for v in range(8):
@@ -189,9 +189,39 @@ def test_entry_points_validate_before_touching_a_device():
         assert raw(half, 99, 4, 4, 4, 16, 16, 16, None) == binding.GEMM_ERR_INVALID_VARIANT
 
 
+def test_ex_entry_points_validate_layout_before_touching_a_device():
+    ex = binding.raw_gemm_ex
+    OK, DIM, NUL, LAY = (binding.GEMM_OK, binding.GEMM_ERR_INVALID_DIM, binding.GEMM_ERR_NULL_PTR,
+                         binding.GEMM_ERR_INVALID_LAYOUT)
+    for kind in ("f32", "f16", "bf16"):
+        def call(op_a=0, op_b=0, M=4, N=5, K=6, A=16, lda=None, B=16, ldb=None, C=16, ldc=None,
+                 alpha=1.0, beta=0.0):
+            lda = max(M if op_a else K, 1) if lda is None else lda
+            ldb = max(K if op_b else N, 1) if ldb is None else ldb
+            ldc = max(N, 1) if ldc is None else ldc
+            return ex(kind, op_a, op_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, None)
+        assert call(M=-1) == DIM and call(K=-1) == DIM and call(N=-1, op_a=5) == DIM
+        for bad in (2, -1, 7):
+            assert call(op_a=bad) == LAY and call(op_b=bad) == LAY
+        # leading dimensions below the row length of the stored matrix
+        assert call(lda=5) == LAY and call(op_a=1, lda=3) == LAY
+        assert call(ldb=4) == LAY and call(op_b=1, ldb=5) == LAY
+        assert call(ldc=4) == LAY and call(ldc=0, N=0) == LAY
+        assert call(op_a=1, lda=4) != LAY and call(op_b=1, ldb=6) != LAY
+        assert call(lda=64, ldb=64, ldc=64) != LAY
+        # layout is checked before pointers, pointers before the device
+        assert call(lda=1, A=None) == LAY
+        assert call(A=None) == NUL and call(B=None) == NUL and call(C=None) == NUL
+        assert call(M=0, A=None, C=None) == OK and call(N=0, B=None, C=None) == OK
+        assert call(M=0, N=0, K=0, A=None, B=None, C=None) == OK
+
+
 def test_no_device_is_reported_not_crashed():
     import torch
     if torch.cuda.is_available():
         pytest.skip("a GPU is present; covered by the GPU tests")
     rc = binding.raw_gemm(False, None, 4, 4, 4, 16, 16, 16, None)
     assert rc in (binding.GEMM_ERR_RUNTIME, binding.GEMM_ERR_UNSUPPORTED_DEVICE)
+    for kind in ("f32", "f16", "bf16"):
+        rc = binding.raw_gemm_ex(kind, 1, 0, 4, 4, 4, 2.0, 16, 4, 16, 4, 0.5, 16, 4, None)
+        assert rc in (binding.GEMM_ERR_RUNTIME, binding.GEMM_ERR_UNSUPPORTED_DEVICE)

@@ -30,41 +30,51 @@ def ring(request, tmp_path_factory):
     return out.read_text(), kernel
 
 
-def _function_body(text, name):
-    m = re.search(rf"^(_Z\S*{name}\S*):.*$", text, flags=re.M)
-    assert m, f"{name} not found in the generated code"
-    start = m.end()
-    end = text.index("s_endpgm", start)
-    return m.group(1), text[start:end]
+def _instances(text, name):
+    """(symbol, body) of every instantiation of the kernel template ``name``
+    (operand layouts, accumulate-into-C, input formats)."""
+    found = []
+    for m in re.finditer(rf"^(_Z\S*{name}\S*):.*$", text, flags=re.M):
+        end = text.index("s_endpgm", m.end())
+        found.append((m.group(1), text[m.end():end]))
+    assert found, f"{name} not found in the generated code"
+    return found
+
+
+def test_every_layout_variant_is_generated(ring):
+    asm, kernel = ring
+    # op(A) x op(B) x (overwrite, accumulate), times two input formats for 16-bit
+    want = 16 if kernel == "mfma_f16_pipe_kernel" else 8
+    assert len(_instances(asm, kernel)) == want
 
 
 def test_m0_is_touched_only_by_the_load_helper(ring):
     asm, kernel = ring
-    _, body = _function_body(asm, kernel)
-    inside = False
-    outside_uses = []
-    loads = 0
-    for line in body.splitlines():
-        if "ASMSTART" in line:
-            inside = True
-            continue
-        if "ASMEND" in line:
-            inside = False
-            continue
-        code = line.split(";")[0]
-        if re.search(r"\bm0\b", code) and not inside:
-            outside_uses.append(code.strip())
-        if inside and "buffer_load_dwordx4" in code and " lds" in code:
-            loads += 1
-    assert loads > 0, "no global->LDS load found inside inline assembly"
-    assert outside_uses == [], f"compiler-generated M0 accesses: {outside_uses[:5]}"
+    for sym, body in _instances(asm, kernel):
+        inside = False
+        outside_uses = []
+        loads = 0
+        for line in body.splitlines():
+            if "ASMSTART" in line:
+                inside = True
+                continue
+            if "ASMEND" in line:
+                inside = False
+                continue
+            code = line.split(";")[0]
+            if re.search(r"\bm0\b", code) and not inside:
+                outside_uses.append(code.strip())
+            if inside and "buffer_load_dwordx4" in code and " lds" in code:
+                loads += 1
+        assert loads > 0, f"{sym}: no global->LDS load found inside inline assembly"
+        assert outside_uses == [], f"{sym}: compiler-generated M0 accesses: {outside_uses[:5]}"
 
 
 def test_ring_kernel_spills_nothing(ring):
     asm, kernel = ring
-    sym, body = _function_body(asm, kernel)
-    priv = re.search(rf"^\s*\.set\s+{re.escape(sym)}\.private_seg_size,\s*(\d+)", asm, flags=re.M)
-    agpr = re.search(rf"^\s*\.set\s+{re.escape(sym)}\.num_agpr,\s*(\d+)", asm, flags=re.M)
-    assert priv and int(priv.group(1)) == 0, "scratch (spill) memory in use"
-    assert agpr and int(agpr.group(1)) == 256, "accumulators not held in the 256 AGPRs"
-    assert "scratch_" not in body
+    for sym, body in _instances(asm, kernel):
+        priv = re.search(rf"^\s*\.set\s+{re.escape(sym)}\.private_seg_size,\s*(\d+)", asm, flags=re.M)
+        agpr = re.search(rf"^\s*\.set\s+{re.escape(sym)}\.num_agpr,\s*(\d+)", asm, flags=re.M)
+        assert priv and int(priv.group(1)) == 0, f"{sym}: scratch (spill) memory in use"
+        assert agpr and int(agpr.group(1)) == 256, f"{sym}: accumulators not held in the 256 AGPRs"
+        assert "scratch_" not in body, sym

@@ -349,3 +349,156 @@ def test_bf16_small_integers_are_exact():
     B = RNG.integers(-4, 5, (500, 30))
     assert np.array_equal(oracle.gemm_bf16(_bf16_bits(A), _bf16_bits(B)),
                           (A @ B).astype(np.float32))
+
+
+# ------------------------------------------ general layouts, alpha and beta --
+# C = alpha op(A) op(B) + beta C with row strides lda / ldb / ldc ("Lesson 8:
+# how a GPU does matrix multiply", section 28 on the library interface; its
+# section 21 writes the matrix unit's D = A x B + C).
+
+def _store(X, op, ld, fill, rng=None):
+    """Flat storage of the logical matrix X (rows x cols) as op N (X itself,
+    row stride ld) or op T (X's transpose stored row-major, row stride ld),
+    with every padding element set to ``fill``."""
+    S = X.T if op else X
+    r, c = S.shape
+    buf = np.full(max((r - 1) * ld + c, 0) if r and c else 0, fill, dtype=X.dtype)
+    for i in range(r):
+        buf[i * ld:i * ld + c] = S[i]
+    return buf
+
+
+def _ex_layouts():
+    for op_a in (0, 1):
+        for op_b in (0, 1):
+            for pad in (0, 3):
+                yield op_a, op_b, pad
+
+
+@pytest.mark.parametrize("fmt", ["f32", "f16", "bf16"])
+def test_ex_transposed_and_padded_operands_match_the_plain_product(fmt):
+    # alpha 1, beta 0: the same products summed in the same order as the
+    # row-major routine, whatever the storage; padding holds NaN (never read)
+    # and C's padding columns keep their sentinel.
+    rng = np.random.default_rng(31)
+    M, N, K = 9, 7, 11
+    A32 = rng.standard_normal((M, K)).astype(np.float32)
+    B32 = rng.standard_normal((K, N)).astype(np.float32)
+    if fmt == "f32":
+        A, B, nan = A32, B32, np.float32(np.nan)
+        plain = oracle.gemm_f32(A, B)
+    elif fmt == "f16":
+        A, B, nan = A32.astype(np.float16).view(np.uint16), B32.astype(np.float16).view(np.uint16), 0x7E00
+        plain = oracle.gemm_f16(A, B)
+    else:
+        A, B, nan = _bf16_bits(A32), _bf16_bits(B32), 0x7FC0
+        plain = oracle.gemm_bf16(A, B)
+    for op_a, op_b, pad in _ex_layouts():
+        lda = (M if op_a else K) + pad
+        ldb = (K if op_b else N) + pad
+        ldc = N + pad
+        Cs = np.full(M * ldc, -7.25, np.float32)
+        oracle.gemm_ex(fmt, op_a, op_b, M, N, K, 1.0, _store(A, op_a, lda, nan), lda,
+                       _store(B, op_b, ldb, nan), ldb, 0.0, Cs, ldc)
+        C = Cs.reshape(M, ldc)
+        assert np.array_equal(_bits(C[:, :N]), _bits(plain)), (op_a, op_b, pad)
+        assert np.all(C[:, N:] == np.float32(-7.25))
+
+
+def _few_bit(rng, shape, mant_bits, e_lo, e_hi):
+    m = rng.integers(1 << (mant_bits - 1), 1 << mant_bits, shape)
+    e = rng.integers(e_lo, e_hi + 1, shape)
+    s = rng.choice([-1, 1], shape)
+    return (s * m * np.exp2(e - (mant_bits - 1))).astype(np.float32)
+
+
+def test_ex_bruteforce_alpha_beta_single_rounding():
+    # Inputs with 8-bit mantissas, alpha and beta with 5, C with 12: every
+    # intermediate of alpha * sum + beta * c spans under 46 bits, so binary64
+    # holds it exactly and the result must be the exact value rounded once to
+    # binary32 (nearest, ties to even).
+    rng = np.random.default_rng(41)
+    rounded = 0
+    for M in range(1, 5):
+        for N in range(1, 5):
+            for K in range(1, 7):
+                A = _few_bit(rng, (M, K), 8, -4, 4)
+                B = _few_bit(rng, (K, N), 8, -4, 4)
+                C0 = _few_bit(rng, (M, N), 12, -4, 4)
+                alpha = float(_few_bit(rng, (), 5, -2, 2))
+                beta = float(_few_bit(rng, (), 5, -2, 2))
+                op_a, op_b = int(rng.integers(0, 2)), int(rng.integers(0, 2))
+                lda, ldb = (M if op_a else K) + 1, (K if op_b else N) + 2
+                Cs = C0.ravel().copy()
+                oracle.gemm_ex("f32", op_a, op_b, M, N, K, alpha, _store(A, op_a, lda, np.nan), lda,
+                               _store(B, op_b, ldb, np.nan), ldb, beta, Cs, N)
+                ex = _exact_product(A, B)
+                for i in range(M):
+                    for j in range(N):
+                        q = Fraction(alpha) * ex[i][j] + Fraction(beta) * Fraction(float(C0[i, j]))
+                        want = _round_exact_to_f32(q)
+                        assert _bits(Cs[i * N + j]) == _bits(want), (M, N, K, i, j)
+                        rounded += Fraction(float(want)) != q
+    assert rounded > 100
+
+
+def test_ex_small_integers_alpha_beta_closed_form():
+    rng = np.random.default_rng(43)
+    M, N, K = 23, 19, 300
+    A = rng.integers(-4, 5, (M, K))
+    B = rng.integers(-4, 5, (K, N))
+    C0 = rng.integers(-1000, 1001, (M, N))
+    for alpha, beta in ((1, 0), (3, -2), (-1, 1), (0.5, 0.25), (2, 1)):
+        want = alpha * (A @ B).astype(np.float64) + beta * C0
+        for op_a, op_b, pad in _ex_layouts():
+            lda, ldb = (M if op_a else K) + pad, (K if op_b else N) + pad
+            Cs = C0.astype(np.float32).ravel().copy()
+            oracle.gemm_ex("f32", op_a, op_b, M, N, K, alpha, _store(A.astype(np.float32), op_a, lda, np.nan),
+                           lda, _store(B.astype(np.float32), op_b, ldb, np.nan), ldb, beta, Cs, N)
+            assert np.array_equal(Cs.reshape(M, N), want.astype(np.float32)), (alpha, beta, op_a, op_b)
+
+
+def test_ex_beta_zero_never_reads_C_and_K0_scales_C():
+    rng = np.random.default_rng(47)
+    M, N, K = 5, 6, 4
+    A = rng.standard_normal((M, K)).astype(np.float32)
+    B = rng.standard_normal((K, N)).astype(np.float32)
+    Cs = np.full(M * N, np.nan, np.float32)
+    oracle.gemm_ex("f32", 0, 0, M, N, K, 2.0, A.ravel(), K, B.ravel(), N, 0.0, Cs, N)
+    assert np.array_equal(Cs.reshape(M, N), np.float32(2.0) * oracle.gemm_f32(A, B))
+    # K = 0: C = beta C (zeros when beta == 0, even over NaN)
+    C0 = rng.standard_normal(M * N).astype(np.float32)
+    Cs = C0.copy()
+    oracle.gemm_ex("f32", 1, 1, M, N, 0, 3.0, np.zeros(1, np.float32), M, np.zeros(1, np.float32), 1, -0.5, Cs, N)
+    assert np.array_equal(Cs, (np.float64(-0.5) * C0).astype(np.float32))
+    Cs = np.full(M * N, np.nan, np.float32)
+    oracle.gemm_ex("f32", 0, 0, M, N, 0, 3.0, np.zeros(1, np.float32), 1, np.zeros(1, np.float32), N, 0.0, Cs, N)
+    assert np.all(Cs == 0)
+    # operand arrays shorter than the shape and strides need are refused
+    with pytest.raises(ValueError):
+        oracle.gemm_ex("f32", 0, 0, M, N, K, 1.0, A.ravel()[:3], K, B.ravel(), N, 0.0, Cs, N)
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+def test_ex_16bit_equals_f32_on_the_decoded_values(fmt):
+    rng = np.random.default_rng(53)
+    M, N, K = 6, 10, 13
+    A32 = rng.standard_normal((M, K)).astype(np.float32)
+    B32 = rng.standard_normal((K, N)).astype(np.float32)
+    if fmt == "f16":
+        A, B = A32.astype(np.float16), B32.astype(np.float16)
+        Ad, Bd = A.astype(np.float32), B.astype(np.float32)
+        A, B = A.view(np.uint16), B.view(np.uint16)
+    else:
+        A, B = _bf16_bits(A32), _bf16_bits(B32)
+        Ad = (A.astype(np.uint32) << 16).view(np.float32)
+        Bd = (B.astype(np.uint32) << 16).view(np.float32)
+    C0 = rng.standard_normal(M * N).astype(np.float32)
+    for op_a, op_b, pad in _ex_layouts():
+        lda, ldb = (M if op_a else K) + pad, (K if op_b else N) + pad
+        got, want = C0.copy(), C0.copy()
+        oracle.gemm_ex(fmt, op_a, op_b, M, N, K, -1.5, _store(A, op_a, lda, 0), lda,
+                       _store(B, op_b, ldb, 0), ldb, 0.75, got, N)
+        oracle.gemm_ex("f32", op_a, op_b, M, N, K, -1.5, _store(Ad, op_a, lda, 0), lda,
+                       _store(Bd, op_b, ldb, 0), ldb, 0.75, want, N)
+        assert np.array_equal(_bits(got), _bits(want)), (op_a, op_b, pad)

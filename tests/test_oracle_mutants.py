@@ -4,8 +4,9 @@ the oracle, and check that at least one pin of ``test_oracle.py`` fails.
 
 Each mutant is a one-token slip of the kind a hand-written loop nest invites:
 a dropped term, a wrong sign, a transposed operand, a wrong index, a start
-value other than zero, binary32 accumulation, or a misdecoded binary16 or
-bfloat16 field.
+value other than zero, binary32 accumulation, a misdecoded binary16 or
+bfloat16 field, an ignored leading dimension or scale factor, or a second
+rounding.
 """
 import ctypes
 import shutil
@@ -50,6 +51,18 @@ MUTANTS = {
     "bf16_B_transposed": ("acc[j] += a * bdec[brow[j]];",
                           "acc[j] += a * bdec[B[((size_t)j * K + k) % ((size_t)K * N)]];"),
     "bf16_fraction_field": ("const int frac = h & 0x7f;", "const int frac = h & 0x3f;"),
+    # general-layout routine
+    "ex_lda_ignored": ("const size_t ia = opA ? (size_t)k * lda + i : (size_t)i * lda + k;",
+                       "const size_t ia = opA ? (size_t)k * M + i : (size_t)i * lda + k;"),
+    "ex_ldb_ignored": ("const size_t ib = opB ? (size_t)j * ldb + k : (size_t)k * ldb + j;",
+                       "const size_t ib = opB ? (size_t)j * ldb + k : (size_t)k * N + j;"),
+    "ex_ldc_ignored": ("C[(size_t)i * ldc + j] = (float)v;", "C[(size_t)i * N + j] = (float)v;"),
+    "ex_alpha_dropped": ("double v = alpha * acc;", "double v = acc;"),
+    "ex_beta_as_one": ("v += beta * (double)C[(size_t)i * ldc + j];", "v += (double)C[(size_t)i * ldc + j];"),
+    "ex_reads_C_when_beta_zero": ("if (beta != 0.0)\n                v += beta", "if (1)\n                v += beta"),
+    "ex_rounds_sum_before_alpha": ("double v = alpha * acc;", "double v = alpha * (double)(float)acc;"),
+    "ex_decoders_swapped": ("return in == 1 ? oracle_f16_to_f64(h) : oracle_bf16_to_f64(h);",
+                            "return in == 2 ? oracle_f16_to_f64(h) : oracle_bf16_to_f64(h);"),
     # selected-element routine
     "at_wrong_column": ("* (double)B[(size_t)k * N + j];", "* (double)B[(size_t)k * N + i % N];"),
 }
@@ -77,6 +90,14 @@ PINS = [
     lambda: pins.test_bf16_product_equals_f32_product_of_the_decoded_values(),
     lambda: pins.test_bf16_bruteforce_exact(),
     lambda: pins.test_bf16_small_integers_are_exact(),
+    lambda: pins.test_ex_transposed_and_padded_operands_match_the_plain_product("f32"),
+    lambda: pins.test_ex_transposed_and_padded_operands_match_the_plain_product("f16"),
+    lambda: pins.test_ex_transposed_and_padded_operands_match_the_plain_product("bf16"),
+    lambda: pins.test_ex_bruteforce_alpha_beta_single_rounding(),
+    lambda: pins.test_ex_small_integers_alpha_beta_closed_form(),
+    lambda: pins.test_ex_beta_zero_never_reads_C_and_K0_scales_C(),
+    lambda: pins.test_ex_16bit_equals_f32_on_the_decoded_values("f16"),
+    lambda: pins.test_ex_16bit_equals_f32_on_the_decoded_values("bf16"),
 ]
 
 
