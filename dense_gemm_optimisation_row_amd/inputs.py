@@ -15,7 +15,12 @@ from one generator per (workload, variant).  Distributions:
 * for binary16 inputs the binary32 draw is rounded once to binary16 by numpy
   (round to nearest even) and both sides read the same bits;
 * for bfloat16 inputs the binary32 draw is rounded once to its upper 16 bits
-  (round to nearest, ties to even), given as uint16 bit patterns.
+  (round to nearest, ties to even), given as uint16 bit patterns;
+* for the OCP FP8 formats (E4M3, E5M2) the binary32 draw is rounded once to
+  the nearest code (ties to the even code), given as uint8 codes;
+* for INT8 inputs the uniform draw on [-1, 1) is scaled by 128 and rounded
+  down, giving integers uniform on [-128, 127]; the small-integer variant is
+  the {-4..4} draw itself.
 """
 from __future__ import annotations
 
@@ -30,7 +35,8 @@ class Workload:
     M: int
     N: int
     K: int
-    dtype: str          # "f32", "f16" or "bf16" (input type; the output is always f32)
+    dtype: str          # "f32", "f16", "bf16", "e4m3", "e5m2" or "i8" (input type;
+                        # the output is f32, or int32 for i8)
     dist: str           # "uniform" or "normal"
     seed: int           # seed of the main draw
     int_seed: int       # seed of the small-integer variant
@@ -42,7 +48,8 @@ class Workload:
 
 # The workloads: square FP32 at 256 and 1024 (1024 is the size the pages time),
 # ragged FP32 shapes that exercise edge masking, FP32 4096 with normal inputs,
-# FP16-input 8192, and BF16-input 8192 (the bfloat16 entry point).
+# FP16-input 8192, BF16-input 8192 (the bfloat16 entry point), and the
+# 8-bit inputs (FP8 E4M3, FP8 E5M2, INT8) at 8192.
 WORKLOADS = {
     w.name: w for w in [
         Workload("f32_256", 256, 256, 256, "f32", "uniform", 1001, 2001),
@@ -52,6 +59,9 @@ WORKLOADS = {
         Workload("f32_4096", 4096, 4096, 4096, "f32", "normal", 1005, 2005),
         Workload("f16_8192", 8192, 8192, 8192, "f16", "uniform", 1006, 2006),
         Workload("bf16_8192", 8192, 8192, 8192, "bf16", "uniform", 1007, 2007),
+        Workload("e4m3_8192", 8192, 8192, 8192, "e4m3", "uniform", 1008, 2008),
+        Workload("e5m2_8192", 8192, 8192, 8192, "e5m2", "uniform", 1009, 2009),
+        Workload("i8_8192", 8192, 8192, 8192, "i8", "uniform", 1010, 2010),
     ]
 }
 
@@ -75,13 +85,46 @@ def to_bf16_bits(x: np.ndarray) -> np.ndarray:
     return ((bits + np.uint64(0x7FFF) + keep_lsb) >> np.uint64(16)).astype(np.uint16)
 
 
+def _fp8_grid(exp_bits: int, man_bits: int, finite_codes: int) -> np.ndarray:
+    """Values of the non-negative FP8 codes 0 .. finite_codes-1, in code order
+    (which is value order): subnormals fraction * 2^(1-bias-man_bits), then
+    (2^man_bits + fraction) * 2^(exponent-bias-man_bits)."""
+    bias = (1 << (exp_bits - 1)) - 1
+    codes = np.arange(finite_codes)
+    e = codes >> man_bits
+    f = codes & ((1 << man_bits) - 1)
+    sub = f * 2.0 ** (1 - bias - man_bits)
+    nor = (f + (1 << man_bits)) * np.exp2(e - bias - man_bits)
+    return np.where(e == 0, sub, nor)
+
+
+# E4M3: codes 0..126 finite (127 is NaN); E5M2: codes 0..123 finite.
+_E4M3 = _fp8_grid(4, 3, 127)
+_E5M2 = _fp8_grid(5, 2, 124)
+
+
+def to_fp8_codes(x: np.ndarray, fmt: str) -> np.ndarray:
+    """Round finite float32 values to the nearest OCP FP8 code of ``fmt``
+    ("e4m3" or "e5m2"), ties to the even code; magnitudes beyond the largest
+    finite value saturate to it.  Returns uint8 codes."""
+    grid = _E4M3 if fmt == "e4m3" else _E5M2
+    x = np.asarray(x, dtype=np.float32).astype(np.float64)
+    ax = np.abs(x)
+    mid = (grid[:-1] + grid[1:]) / 2
+    code = np.searchsorted(mid, ax, side="left")          # first midpoint >= |x|
+    tie = (code < mid.size) & (ax == mid[np.minimum(code, mid.size - 1)])
+    code = np.where(tie & (code % 2 == 1), code + 1, code)
+    return (code | np.where(np.signbit(x), 0x80, 0)).astype(np.uint8)
+
+
 def matrices(M: int, N: int, K: int, seed: int, dist: str = "uniform",
              dtype: str = "f32"):
     """Return (A, B): A is M x K, B is K x N, C-contiguous numpy arrays.
 
     ``dtype`` "f32" gives float32; "f16" gives float16 (the float32 draw
     rounded once to binary16); "bf16" gives uint16 bfloat16 bit patterns (the
-    float32 draw rounded once to bfloat16).
+    float32 draw rounded once to bfloat16); "e4m3" / "e5m2" give uint8 FP8
+    codes (the draw rounded once); "i8" gives int8.
     """
     rng = np.random.default_rng(seed)
     A = _draw(rng, (M, K), dist)
@@ -92,6 +135,15 @@ def matrices(M: int, N: int, K: int, seed: int, dist: str = "uniform",
     elif dtype == "bf16":
         A = to_bf16_bits(A)
         B = to_bf16_bits(B)
+    elif dtype in ("e4m3", "e5m2"):
+        A = to_fp8_codes(A, dtype)
+        B = to_fp8_codes(B, dtype)
+    elif dtype == "i8":
+        if dist != "int":
+            A = np.floor(A.astype(np.float64) * 128)
+            B = np.floor(B.astype(np.float64) * 128)
+        A = np.clip(A, -128, 127).astype(np.int8)
+        B = np.clip(B, -128, 127).astype(np.int8)
     elif dtype != "f32":
         raise ValueError(f"unknown dtype {dtype!r}")
     return np.ascontiguousarray(A), np.ascontiguousarray(B)

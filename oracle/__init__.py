@@ -60,6 +60,18 @@ def configure(lib):
         f = getattr(lib, name)
         f.argtypes = [i, i, i, p, p, i64, p, p, p, i]
         f.restype = i
+    for name in ("oracle_e4m3_to_f64", "oracle_e5m2_to_f64"):
+        f = getattr(lib, name)
+        f.argtypes = [ctypes.c_uint8]
+        f.restype = ctypes.c_double
+    for name in ("oracle_gemm_e4m3", "oracle_gemm_e5m2", "oracle_gemm_i8"):
+        f = getattr(lib, name)
+        f.argtypes = [i, i, i, p, p, p, i]
+        f.restype = i
+    lib.oracle_gemm_fp8_at.argtypes = [i, i, i, i, p, p, i64, p, p, p, i]
+    lib.oracle_gemm_fp8_at.restype = i
+    lib.oracle_gemm_i8_at.argtypes = [i, i, i, p, p, i64, p, p, p, i]
+    lib.oracle_gemm_i8_at.restype = i
     d = ctypes.c_double
     lib.oracle_gemm_ex.argtypes = [i, i, i, i, i, i, d, p, i, p, i, d, p, i, i]
     lib.oracle_gemm_ex.restype = i
@@ -221,3 +233,79 @@ def gemm_ex(fmt: str, op_a: int, op_b: int, M: int, N: int, K: int, alpha: float
     if rc != 0:
         raise RuntimeError(f"oracle_gemm_ex failed ({rc})")
     return C
+
+
+# ------------------------------------------------------------ 8-bit inputs --
+
+def e4m3_to_f64(code: int) -> float:
+    """Decode one OCP FP8 E4M3 code exactly."""
+    return float(_load().oracle_e4m3_to_f64(int(code) & 0xFF))
+
+
+def e5m2_to_f64(code: int) -> float:
+    """Decode one OCP FP8 E5M2 code exactly."""
+    return float(_load().oracle_e5m2_to_f64(int(code) & 0xFF))
+
+
+def _gemm8(fname, A, B, dtype, out_dtype, out, nthreads):
+    A, B = _check_inputs(A, B, dtype)
+    M, K = A.shape
+    N = B.shape[1]
+    C = np.empty((M, N), out_dtype) if out is None else out
+    if C.shape != (M, N) or C.dtype != out_dtype or not C.flags.c_contiguous:
+        raise ValueError(f"out must be a contiguous {np.dtype(out_dtype).name} M x N array")
+    rc = getattr(_load(), fname)(M, N, K, _ptr(A), _ptr(B), _ptr(C), nthreads)
+    if rc != 0:
+        raise RuntimeError(f"{fname} failed ({rc})")
+    return C
+
+
+def gemm_e4m3(A, B, out=None, nthreads: int = 0) -> np.ndarray:
+    """C = A x B for FP8 E4M3 codes (uint8) A, B; binary64 sum, binary32 result."""
+    return _gemm8("oracle_gemm_e4m3", A, B, np.uint8, np.float32, out, nthreads)
+
+
+def gemm_e5m2(A, B, out=None, nthreads: int = 0) -> np.ndarray:
+    """C = A x B for FP8 E5M2 codes (uint8) A, B; binary64 sum, binary32 result."""
+    return _gemm8("oracle_gemm_e5m2", A, B, np.uint8, np.float32, out, nthreads)
+
+
+def gemm_i8(A, B, out=None, nthreads: int = 0) -> np.ndarray:
+    """C = A x B for int8 A, B; exact, int32 result (error if it overflows)."""
+    return _gemm8("oracle_gemm_i8", A, B, np.int8, np.int32, out, nthreads)
+
+
+def _at8(A, B, rows, cols, nthreads, fmt=None):
+    M, K = A.shape
+    N = B.shape[1]
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    cols = np.ascontiguousarray(cols, dtype=np.int64)
+    if rows.shape != cols.shape:
+        raise ValueError("rows and cols must have the same shape")
+    lib = _load()
+    if fmt is None:
+        out = np.empty(rows.shape, np.int32)
+        rc = lib.oracle_gemm_i8_at(M, N, K, _ptr(A), _ptr(B), rows.size, _ptr(rows), _ptr(cols),
+                                   _ptr(out), nthreads)
+    else:
+        out = np.empty(rows.shape, np.float32)
+        rc = lib.oracle_gemm_fp8_at(fmt, M, N, K, _ptr(A), _ptr(B), rows.size, _ptr(rows), _ptr(cols),
+                                    _ptr(out), nthreads)
+    if rc != 0:
+        raise RuntimeError(f"8-bit sampled oracle failed ({rc})")
+    return out
+
+
+def gemm_e4m3_at(A, B, rows, cols, nthreads: int = 0) -> np.ndarray:
+    A, B = _check_inputs(A, B, np.uint8)
+    return _at8(A, B, rows, cols, nthreads, 0)
+
+
+def gemm_e5m2_at(A, B, rows, cols, nthreads: int = 0) -> np.ndarray:
+    A, B = _check_inputs(A, B, np.uint8)
+    return _at8(A, B, rows, cols, nthreads, 1)
+
+
+def gemm_i8_at(A, B, rows, cols, nthreads: int = 0) -> np.ndarray:
+    A, B = _check_inputs(A, B, np.int8)
+    return _at8(A, B, rows, cols, nthreads)

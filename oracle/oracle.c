@@ -53,6 +53,7 @@
 #define ORACLE_OK 0
 #define ORACLE_ERR_DIM (-1)
 #define ORACLE_ERR_ALLOC (-2)
+#define ORACLE_ERR_RANGE (-3)
 
 /* IEEE 754 binary16 bit pattern -> exact binary64 value.
  * Layout: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits.
@@ -348,4 +349,188 @@ int oracle_gemm_ex(int in, int opA, int opB, int M, int N, int K, double alpha,
         }
     }
     return ORACLE_OK;
+}
+
+/*
+ * 8-bit inputs ("Lesson 8: how a GPU does matrix multiply", section 22 lists
+ * FP8 and INT8 among the matrix units' input formats).
+ *
+ * OCP FP8 E4M3 (the "FN" variant, no infinities): 1 sign bit, 4 exponent
+ * bits (bias 7), 3 fraction bits.
+ *   exponent 0             : subnormal, value = fraction * 2^-9
+ *   exponent 1..15         : normal,    value = (8 + fraction) * 2^(exponent-10)
+ *   exponent 15, fraction 7: NaN (the format's only non-finite code).
+ */
+double oracle_e4m3_to_f64(uint8_t b)
+{
+    const int sign = (b >> 7) & 1;
+    const int expo = (b >> 3) & 0xf;
+    const int frac = b & 0x7;
+    double v;
+    if (expo == 0)
+        v = ldexp((double)frac, -9);
+    else if (expo == 15 && frac == 7)
+        v = NAN;
+    else
+        v = ldexp((double)(8 + frac), expo - 10);
+    return sign ? -v : v;
+}
+
+/*
+ * OCP FP8 E5M2: 1 sign bit, 5 exponent bits (bias 15), 2 fraction bits.
+ *   exponent 0     : subnormal, value = fraction * 2^-16
+ *   exponent 1..30 : normal,    value = (4 + fraction) * 2^(exponent-17)
+ *   exponent 31    : infinity (fraction 0) or NaN.
+ */
+double oracle_e5m2_to_f64(uint8_t b)
+{
+    const int sign = (b >> 7) & 1;
+    const int expo = (b >> 2) & 0x1f;
+    const int frac = b & 0x3;
+    double v;
+    if (expo == 0)
+        v = ldexp((double)frac, -16);
+    else if (expo == 31)
+        v = frac ? NAN : INFINITY;
+    else
+        v = ldexp((double)(4 + frac), expo - 17);
+    return sign ? -v : v;
+}
+
+/*
+ * Full product of two 8-bit floating-point matrices given as codes, binary32
+ * output: the binary64 sum in ascending k of the exact products of the
+ * decoded values, rounded once.  `fmt` 0 is E4M3, 1 is E5M2.
+ */
+static int gemm_fp8(int fmt, int M, int N, int K, const uint8_t *A, const uint8_t *B, float *C,
+                    int nthreads)
+{
+    if (M < 0 || N < 0 || K < 0)
+        return ORACLE_ERR_DIM;
+    if (M == 0 || N == 0)
+        return ORACLE_OK;
+    double dec[256];
+    for (int b = 0; b < 256; ++b)
+        dec[b] = fmt == 0 ? oracle_e4m3_to_f64((uint8_t)b) : oracle_e5m2_to_f64((uint8_t)b);
+    int failed = 0;
+#pragma omp parallel num_threads(thread_count(nthreads)) reduction(| : failed)
+    {
+        double *acc = (double *)malloc((size_t)N * sizeof(double));
+        if (!acc)
+            failed = 1;
+#pragma omp for schedule(static)
+        for (int i = 0; i < M; ++i) {
+            if (!acc)
+                continue;
+            for (int j = 0; j < N; ++j)
+                acc[j] = 0.0;
+            for (int k = 0; k < K; ++k) {
+                const double a = dec[A[(size_t)i * K + k]];
+                const uint8_t *brow = B + (size_t)k * N;
+                for (int j = 0; j < N; ++j)
+                    acc[j] += a * dec[brow[j]];
+            }
+            for (int j = 0; j < N; ++j)
+                C[(size_t)i * N + j] = (float)acc[j];
+        }
+        free(acc);
+    }
+    return failed ? ORACLE_ERR_ALLOC : ORACLE_OK;
+}
+
+int oracle_gemm_e4m3(int M, int N, int K, const uint8_t *A, const uint8_t *B, float *C, int nthreads)
+{
+    return gemm_fp8(0, M, N, K, A, B, C, nthreads);
+}
+
+int oracle_gemm_e5m2(int M, int N, int K, const uint8_t *A, const uint8_t *B, float *C, int nthreads)
+{
+    return gemm_fp8(1, M, N, K, A, B, C, nthreads);
+}
+
+/*
+ * INT8 inputs, exact integer result: C[i][j] = sum_k A[i][k] B[k][j] as a
+ * 64-bit integer, stored as int32.  A result outside the int32 range is an
+ * error (ORACLE_ERR_RANGE): it cannot occur for K <= 131072.
+ */
+int oracle_gemm_i8(int M, int N, int K, const int8_t *A, const int8_t *B, int32_t *C, int nthreads)
+{
+    if (M < 0 || N < 0 || K < 0)
+        return ORACLE_ERR_DIM;
+    if (M == 0 || N == 0)
+        return ORACLE_OK;
+    int failed = 0;
+#pragma omp parallel num_threads(thread_count(nthreads)) reduction(| : failed)
+    {
+        int64_t *acc = (int64_t *)malloc((size_t)N * sizeof(int64_t));
+        if (!acc)
+            failed |= 1;
+#pragma omp for schedule(static)
+        for (int i = 0; i < M; ++i) {
+            if (!acc)
+                continue;
+            for (int j = 0; j < N; ++j)
+                acc[j] = 0;
+            for (int k = 0; k < K; ++k) {
+                const int64_t a = A[(size_t)i * K + k];
+                const int8_t *brow = B + (size_t)k * N;
+                for (int j = 0; j < N; ++j)
+                    acc[j] += a * brow[j];
+            }
+            for (int j = 0; j < N; ++j) {
+                if (acc[j] > INT32_MAX || acc[j] < INT32_MIN)
+                    failed |= 2;
+                C[(size_t)i * N + j] = (int32_t)acc[j];
+            }
+        }
+        free(acc);
+    }
+    return (failed & 1) ? ORACLE_ERR_ALLOC : (failed & 2) ? ORACLE_ERR_RANGE : ORACLE_OK;
+}
+
+/* Selected elements of the 8-bit products, one dot product each (same
+ * operation sequence as the full routines, so the same bits). */
+int oracle_gemm_fp8_at(int fmt, int M, int N, int K, const uint8_t *A, const uint8_t *B,
+                       int64_t count, const int64_t *rows, const int64_t *cols, float *out,
+                       int nthreads)
+{
+    if (M < 0 || N < 0 || K < 0 || count < 0 || fmt < 0 || fmt > 1)
+        return ORACLE_ERR_DIM;
+    for (int64_t t = 0; t < count; ++t)
+        if (rows[t] < 0 || rows[t] >= M || cols[t] < 0 || cols[t] >= N)
+            return ORACLE_ERR_DIM;
+#pragma omp parallel for num_threads(thread_count(nthreads)) schedule(static)
+    for (int64_t t = 0; t < count; ++t) {
+        const int64_t i = rows[t], j = cols[t];
+        double acc = 0.0;
+        for (int k = 0; k < K; ++k) {
+            const uint8_t a = A[(size_t)i * K + k], b = B[(size_t)k * N + j];
+            acc += fmt == 0 ? oracle_e4m3_to_f64(a) * oracle_e4m3_to_f64(b)
+                            : oracle_e5m2_to_f64(a) * oracle_e5m2_to_f64(b);
+        }
+        out[t] = (float)acc;
+    }
+    return ORACLE_OK;
+}
+
+int oracle_gemm_i8_at(int M, int N, int K, const int8_t *A, const int8_t *B, int64_t count,
+                      const int64_t *rows, const int64_t *cols, int32_t *out, int nthreads)
+{
+    if (M < 0 || N < 0 || K < 0 || count < 0)
+        return ORACLE_ERR_DIM;
+    for (int64_t t = 0; t < count; ++t)
+        if (rows[t] < 0 || rows[t] >= M || cols[t] < 0 || cols[t] >= N)
+            return ORACLE_ERR_DIM;
+    int failed = 0;
+#pragma omp parallel for num_threads(thread_count(nthreads)) schedule(static) reduction(| : failed)
+    for (int64_t t = 0; t < count; ++t) {
+        const int64_t i = rows[t], j = cols[t];
+        int64_t acc = 0;
+        for (int k = 0; k < K; ++k)
+            acc += (int64_t)A[(size_t)i * K + k] * B[(size_t)k * N + j];
+        if (acc > INT32_MAX || acc < INT32_MIN)
+            failed = 1;
+        out[t] = (int32_t)acc;
+    }
+    return failed ? ORACLE_ERR_RANGE : ORACLE_OK;
 }

@@ -5,8 +5,8 @@ the oracle, and check that at least one pin of ``test_oracle.py`` fails.
 Each mutant is a one-token slip of the kind a hand-written loop nest invites:
 a dropped term, a wrong sign, a transposed operand, a wrong index, a start
 value other than zero, binary32 accumulation, a misdecoded binary16 or
-bfloat16 field, an ignored leading dimension or scale factor, or a second
-rounding.
+bfloat16 field, an ignored leading dimension or scale factor, a second
+rounding, a misdecoded FP8 field, or a sign or width slip in the INT8 sum.
 """
 import ctypes
 import shutil
@@ -63,6 +63,17 @@ MUTANTS = {
     "ex_rounds_sum_before_alpha": ("double v = alpha * acc;", "double v = alpha * (double)(float)acc;"),
     "ex_decoders_swapped": ("return in == 1 ? oracle_f16_to_f64(h) : oracle_bf16_to_f64(h);",
                             "return in == 2 ? oracle_f16_to_f64(h) : oracle_bf16_to_f64(h);"),
+    # 8-bit routines and decoders
+    "e4m3_exponent_bias": ("v = ldexp((double)(8 + frac), expo - 10);", "v = ldexp((double)(8 + frac), expo - 11);"),
+    "e4m3_nan_as_number": ("else if (expo == 15 && frac == 7)\n        v = NAN;", "else if (expo == 16)\n        v = NAN;"),
+    "e4m3_subnormal_scale": ("v = ldexp((double)frac, -9);", "v = ldexp((double)frac, -10);"),
+    "e5m2_hidden_bit": ("v = ldexp((double)(4 + frac), expo - 17);", "v = ldexp((double)(frac), expo - 15);"),
+    "e5m2_fraction_field": ("const int frac = b & 0x3;", "const int frac = b & 0x1;"),
+    "fp8_B_transposed": ("acc[j] += a * dec[brow[j]];",
+                         "acc[j] += a * dec[B[((size_t)j * K + k) % ((size_t)K * N)]];"),
+    "i8_unsigned_A": ("const int64_t a = A[(size_t)i * K + k];", "const int64_t a = (uint8_t)A[(size_t)i * K + k];"),
+    "i8_narrow_accumulator": ("int64_t *acc = (int64_t *)malloc((size_t)N * sizeof(int64_t));",
+                              "int32_t *acc = (int32_t *)malloc((size_t)N * sizeof(int32_t));"),
     # selected-element routine
     "at_wrong_column": ("* (double)B[(size_t)k * N + j];", "* (double)B[(size_t)k * N + i % N];"),
 }
@@ -98,6 +109,15 @@ PINS = [
     lambda: pins.test_ex_beta_zero_never_reads_C_and_K0_scales_C(),
     lambda: pins.test_ex_16bit_equals_f32_on_the_decoded_values("f16"),
     lambda: pins.test_ex_16bit_equals_f32_on_the_decoded_values("bf16"),
+    lambda: pins.test_fp8_decoder_matches_torch_on_every_code("e4m3"),
+    lambda: pins.test_fp8_decoder_matches_torch_on_every_code("e5m2"),
+    lambda: pins.test_fp8_decoder_spot_values(),
+    lambda: pins.test_fp8_product_equals_f32_product_of_the_decoded_values("e4m3"),
+    lambda: pins.test_fp8_product_equals_f32_product_of_the_decoded_values("e5m2"),
+    lambda: pins.test_fp8_bruteforce_exact("e4m3"),
+    lambda: pins.test_fp8_bruteforce_exact("e5m2"),
+    lambda: pins.test_i8_product_is_numpy_int64_product(),
+    lambda: pins.test_i8_extremes_and_overflow(),
 ]
 
 
@@ -122,7 +142,7 @@ def test_pins_catch_mutant(name, tmp_path, monkeypatch):
     for pin in PINS:
         try:
             pin()
-        except (AssertionError, RuntimeError, ValueError):
+        except (AssertionError, RuntimeError, ValueError, pytest.fail.Exception):
             caught += 1
     assert caught > 0, f"no pin notices mutant {name}"
 
