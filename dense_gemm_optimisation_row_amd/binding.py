@@ -4,7 +4,8 @@ Two layers:
 
 * ``raw_*`` functions pass integers (device addresses, sizes, a stream
   handle) straight to the library and return its status code;
-* ``gemm_f32`` / ``gemm_f16_f32acc`` / ``gemm_bf16_f32acc`` (and
+* ``gemm_f32`` / ``gemm_f16_f32acc`` / ``gemm_bf16_f32acc`` and the 8-bit
+  ``gemm_e4m3_f32acc`` / ``gemm_e5m2_f32acc`` / ``gemm_i8_i32acc`` (and
   ``*_variant``) take torch tensors
   that already live on the GPU, check shape / dtype / contiguity, call the
   library on the tensors' current stream and raise ``GemmError`` on a
@@ -37,23 +38,31 @@ GEMM_OP_N, GEMM_OP_T = 0, 1
 AUTO = -1
 R0_NAIVE, R1_LDS_TILED, R2_VECTOR_LOADS, R3_LDS_PADDED = 0, 1, 2, 3
 R4_DOUBLE_BUFFER, R5_REGISTER_BLOCKED, R6_MFMA_F32, R7_MFMA_F16 = 4, 5, 6, 7
+R8_MFMA_8BIT = 8
 F32_VARIANTS = (0, 1, 2, 3, 4, 5, 6)
 F16_VARIANTS = (0, 7)
 BF16_VARIANTS = (0, 7)
+EIGHT_BIT_VARIANTS = (0, 8)
 
 EXPORTS = ("gemm_f32", "gemm_f16_f32acc", "gemm_bf16_f32acc",
            "gemm_f32_variant", "gemm_f16_f32acc_variant", "gemm_bf16_f32acc_variant",
            "gemm_f32_plan", "gemm_f16_f32acc_plan", "gemm_bf16_f32acc_plan",
+           "gemm_e4m3_f32acc", "gemm_e5m2_f32acc", "gemm_i8_i32acc",
+           "gemm_e4m3_f32acc_variant", "gemm_e5m2_f32acc_variant", "gemm_i8_i32acc_variant",
+           "gemm_e4m3_f32acc_plan", "gemm_e5m2_f32acc_plan", "gemm_i8_i32acc_plan",
            "gemm_f32_ex", "gemm_f16_f32acc_ex", "gemm_bf16_f32acc_ex",
            "gemm_status_string", "gemm_variant_name")
 
 # Entry-point name stem per input format.
-_STEM = {"f32": "gemm_f32", "f16": "gemm_f16_f32acc", "bf16": "gemm_bf16_f32acc"}
+_STEM = {"f32": "gemm_f32", "f16": "gemm_f16_f32acc", "bf16": "gemm_bf16_f32acc",
+         "e4m3": "gemm_e4m3_f32acc", "e5m2": "gemm_e5m2_f32acc", "i8": "gemm_i8_i32acc"}
+# Formats with a general-layout (``_ex``) entry point.
+_EX_KINDS = ("f32", "f16", "bf16")
 
 
 def kind_of(kind) -> str:
-    """Input format of a call: "f32", "f16" or "bf16"; a bool means f16 (True)
-    or f32 (False)."""
+    """Input format of a call: "f32", "f16", "bf16", "e4m3", "e5m2" or "i8"; a
+    bool means f16 (True) or f32 (False)."""
     if isinstance(kind, bool):
         return "f16" if kind else "f32"
     if kind in _STEM:
@@ -90,7 +99,7 @@ def load(path: str = LIB_PATH):
                 "`python -m dense_gemm_optimisation_row_amd.build`")
         lib = ctypes.CDLL(path)
         i, p = ctypes.c_int, ctypes.c_void_p
-        for stem in _STEM.values():
+        for kind, stem in _STEM.items():
             f = getattr(lib, stem)
             f.argtypes = [i, i, i, p, p, p, p]
             f.restype = i
@@ -100,9 +109,10 @@ def load(path: str = LIB_PATH):
             f = getattr(lib, stem + "_plan")
             f.argtypes = [i, i, i, i, p, p, p, ctypes.POINTER(Plan)]
             f.restype = i
-            f = getattr(lib, stem + "_ex")
-            f.argtypes = [i, i, i, i, i, ctypes.c_float, p, i, p, i, ctypes.c_float, p, i, p]
-            f.restype = i
+            if kind in _EX_KINDS:
+                f = getattr(lib, stem + "_ex")
+                f.argtypes = [i, i, i, i, i, ctypes.c_float, p, i, p, i, ctypes.c_float, p, i, p]
+                f.restype = i
         lib.gemm_status_string.argtypes = [i]
         lib.gemm_status_string.restype = ctypes.c_char_p
         lib.gemm_variant_name.argtypes = [i]
@@ -157,8 +167,9 @@ def plan(kind, M: int, N: int, K: int, variant: int = AUTO,
 
 # ----------------------------------------------------------- torch layer --
 
-def _check(A, B, C, in_dtype):
+def _check(A, B, C, in_dtype, out_dtype=None):
     import torch
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
     if A.dim() != 2 or B.dim() != 2 or A.shape[1] != B.shape[0]:
         raise ValueError(f"shapes {tuple(A.shape)} x {tuple(B.shape)} do not chain")
     if A.dtype != in_dtype or B.dtype != in_dtype:
@@ -170,10 +181,10 @@ def _check(A, B, C, in_dtype):
     M, K = A.shape
     N = B.shape[1]
     if C is None:
-        C = torch.empty((M, N), dtype=torch.float32, device=A.device)
-    elif (tuple(C.shape) != (M, N) or C.dtype != torch.float32 or not C.is_contiguous()
+        C = torch.empty((M, N), dtype=out_dtype, device=A.device)
+    elif (tuple(C.shape) != (M, N) or C.dtype != out_dtype or not C.is_contiguous()
           or C.device != A.device):
-        raise ValueError("C must be a contiguous float32 M x N tensor on A's device")
+        raise ValueError(f"C must be a contiguous {out_dtype} M x N tensor on A's device")
     if B.device != A.device:
         raise ValueError("A and B must be on the same device")
     return M, N, K, C
@@ -190,11 +201,18 @@ def _ptr(t):
     return t.data_ptr() if t.numel() else None
 
 
+def _dtypes(kind):
+    """(input dtype, output dtype) of a format."""
+    import torch
+    return {"f32": (torch.float32, torch.float32), "f16": (torch.float16, torch.float32),
+            "bf16": (torch.bfloat16, torch.float32), "e4m3": (torch.float8_e4m3fn, torch.float32),
+            "e5m2": (torch.float8_e5m2, torch.float32), "i8": (torch.int8, torch.int32)}[kind]
+
+
 def _call(kind, variant, A, B, C, stream):
     import torch
     kind = kind_of(kind)
-    dtype = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[kind]
-    M, N, K, C = _check(A, B, C, dtype)
+    M, N, K, C = _check(A, B, C, *_dtypes(kind))
     with torch.cuda.device(A.device):
         rc = raw_gemm(kind, variant, M, N, K, _ptr(A), _ptr(B), _ptr(C),
                       _stream_handle(A.device, stream))
@@ -249,7 +267,9 @@ def _layout(t, name):
 def _call_ex(kind, A, B, C, alpha, beta, stream):
     import torch
     kind = kind_of(kind)
-    dtype = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[kind]
+    if kind not in _EX_KINDS:
+        raise ValueError(f"no general-layout entry point for {kind}")
+    dtype = _dtypes(kind)[0]
     if A.dim() != 2 or B.dim() != 2 or A.shape[1] != B.shape[0]:
         raise ValueError(f"shapes {tuple(A.shape)} x {tuple(B.shape)} do not chain")
     if A.dtype != dtype or B.dtype != dtype:
@@ -293,3 +313,30 @@ def gemm_f16_f32acc_ex(A, B, C=None, alpha=1.0, beta=0.0, stream=None):
 def gemm_bf16_f32acc_ex(A, B, C=None, alpha=1.0, beta=0.0, stream=None):
     """``gemm_f32_ex`` for bfloat16 A and B (FP32 accumulation and output)."""
     return _call_ex("bf16", A, B, C, alpha, beta, stream)
+
+
+def gemm_e4m3_f32acc(A, B, C=None, stream=None):
+    """C = A x B for FP8 E4M3 GPU tensors (torch.float8_e4m3fn), FP32 accumulation and output."""
+    return _call("e4m3", None, A, B, C, stream)
+
+
+def gemm_e5m2_f32acc(A, B, C=None, stream=None):
+    """C = A x B for FP8 E5M2 GPU tensors (torch.float8_e5m2), FP32 accumulation and output."""
+    return _call("e5m2", None, A, B, C, stream)
+
+
+def gemm_i8_i32acc(A, B, C=None, stream=None):
+    """C = A x B for int8 GPU tensors, exact INT32 accumulation and int32 output."""
+    return _call("i8", None, A, B, C, stream)
+
+
+def gemm_e4m3_f32acc_variant(variant, A, B, C=None, stream=None):
+    return _call("e4m3", int(variant), A, B, C, stream)
+
+
+def gemm_e5m2_f32acc_variant(variant, A, B, C=None, stream=None):
+    return _call("e5m2", int(variant), A, B, C, stream)
+
+
+def gemm_i8_i32acc_variant(variant, A, B, C=None, stream=None):
+    return _call("i8", int(variant), A, B, C, stream)

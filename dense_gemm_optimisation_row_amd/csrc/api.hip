@@ -1,6 +1,6 @@
 // C ABI of the library (declared in include/gemm.h): argument validation,
 // launch planning and dispatch.  Host code only; the kernels live in
-// ladder.hip, mfma_f32.hip and mfma_f16.hip.
+// ladder.hip, mfma_f32.hip, mfma_f16.hip and mfma_8bit.hip.
 //
 // Planning is pure arithmetic on the arguments (no HIP call), so the plan
 // entry points work on a machine without a GPU.  The grid follows the
@@ -264,6 +264,76 @@ int run(In in, int variant, int M, int N, int K, const void *A, const void *B, f
     return err == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
 }
 
+// ----------------------------------------------------------- 8-bit inputs --
+
+// Plan for the 8-bit entry points: R8 (the 256 x 256 x 64 ring) when both
+// operands can be read with 16-byte loads, else R0.  INT8 caps K so that the
+// INT32 sum cannot overflow.
+int plan_8(int fmt, int variant, int M, int N, int K, const void *A, const void *B, gemm_plan *p)
+{
+    if (!p)
+        return GEMM_ERR_NULL_PTR;
+    if (M < 0 || N < 0 || K < 0 || (fmt == dgor::kFmtI8 && K > dgor::kI8MaxK))
+        return GEMM_ERR_INVALID_DIM;
+    if (variant != GEMM_VARIANT_AUTO && variant != GEMM_R0_NAIVE && variant != GEMM_R8_MFMA_8BIT)
+        return GEMM_ERR_INVALID_VARIANT;
+    clear(p);
+    p->vector_a = (K % 16 == 0) && aligned16(A);
+    p->vector_b = (N % 16 == 0) && aligned16(B);
+    p->vector_c = 0;
+    const bool ring = p->vector_a && p->vector_b && K < (1 << 22) && N < (1 << 22);
+    p->variant = (variant != GEMM_R0_NAIVE && ring) ? GEMM_R8_MFMA_8BIT : GEMM_R0_NAIVE;
+    if (M == 0 || N == 0)
+        return GEMM_OK;
+    if (K == 0) {
+        p->launches = 1;
+        p->threads = 256;
+        p->vector_a = p->vector_b = 0;
+        return GEMM_OK;
+    }
+    if (p->variant == GEMM_R0_NAIVE) {
+        p->tile_m = p->tile_n = 16;
+        p->threads = 256;
+        p->outputs_per_thread = 1;
+        p->vector_a = p->vector_b = 0;
+    } else {
+        p->tile_m = p->tile_n = dgor::kRing8Tile;
+        p->tile_k = dgor::kRing8Depth;
+        p->threads = 256;
+        p->lds_stages = dgor::kRing8Stages;
+        p->lds_bytes = dgor::kRing8LdsBytes;
+        p->tile_bytes = 2 * dgor::kRing8Tile * dgor::kRing8Depth;
+        p->outputs_per_thread = dgor::kRing8Tile * dgor::kRing8Tile / 256;
+    }
+    finish(p, M, N, K);
+    return GEMM_OK;
+}
+
+int run8(int fmt, int variant, int M, int N, int K, const void *A, const void *B, void *C, void *stream)
+{
+    gemm_plan plan;
+    const int rc = plan_8(fmt, variant, M, N, K, A, B, &plan);
+    if (rc != GEMM_OK)
+        return rc;
+    if (null_with_extent(A, B, C, M, N, K))
+        return GEMM_ERR_NULL_PTR;
+    if (plan.launches == 0)
+        return GEMM_OK;
+    const int dev = check_device();
+    if (dev != GEMM_OK)
+        return dev;
+    dgor::Problem p{M, N, K, A, B, (float *)C, false, false, false};
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t err;
+    if (K == 0)
+        err = dgor::launch_zero_fill(p, s);   // +0.0f and integer 0 share their bits
+    else if (plan.variant == GEMM_R0_NAIVE)
+        err = dgor::launch_naive_8bit(p, fmt, s);
+    else
+        err = dgor::launch_ring8(dgor::ring_args_nn(p, plan), fmt, s);
+    return err == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
+}
+
 // ------------------------------------------------------- general layouts --
 
 bool is_finite(float x) { return x - x == 0.f; }
@@ -398,6 +468,60 @@ int gemm_bf16_f32acc_plan(int variant, int M, int N, int K, const uint16_t *A,
     return plan_f16(variant, M, N, K, A, B, C, plan);
 }
 
+int gemm_e4m3_f32acc(int M, int N, int K, const uint8_t *A, const uint8_t *B, float *C, void *stream)
+{
+    return run8(dgor::kFmtE4M3, GEMM_VARIANT_AUTO, M, N, K, A, B, C, stream);
+}
+
+int gemm_e5m2_f32acc(int M, int N, int K, const uint8_t *A, const uint8_t *B, float *C, void *stream)
+{
+    return run8(dgor::kFmtE5M2, GEMM_VARIANT_AUTO, M, N, K, A, B, C, stream);
+}
+
+int gemm_i8_i32acc(int M, int N, int K, const int8_t *A, const int8_t *B, int32_t *C, void *stream)
+{
+    return run8(dgor::kFmtI8, GEMM_VARIANT_AUTO, M, N, K, A, B, C, stream);
+}
+
+int gemm_e4m3_f32acc_variant(int variant, int M, int N, int K, const uint8_t *A, const uint8_t *B, float *C,
+                             void *stream)
+{
+    return run8(dgor::kFmtE4M3, variant, M, N, K, A, B, C, stream);
+}
+
+int gemm_e5m2_f32acc_variant(int variant, int M, int N, int K, const uint8_t *A, const uint8_t *B, float *C,
+                             void *stream)
+{
+    return run8(dgor::kFmtE5M2, variant, M, N, K, A, B, C, stream);
+}
+
+int gemm_i8_i32acc_variant(int variant, int M, int N, int K, const int8_t *A, const int8_t *B, int32_t *C,
+                           void *stream)
+{
+    return run8(dgor::kFmtI8, variant, M, N, K, A, B, C, stream);
+}
+
+int gemm_e4m3_f32acc_plan(int variant, int M, int N, int K, const uint8_t *A, const uint8_t *B, const float *C,
+                          gemm_plan *plan)
+{
+    (void)C;
+    return plan_8(dgor::kFmtE4M3, variant, M, N, K, A, B, plan);
+}
+
+int gemm_e5m2_f32acc_plan(int variant, int M, int N, int K, const uint8_t *A, const uint8_t *B, const float *C,
+                          gemm_plan *plan)
+{
+    (void)C;
+    return plan_8(dgor::kFmtE5M2, variant, M, N, K, A, B, plan);
+}
+
+int gemm_i8_i32acc_plan(int variant, int M, int N, int K, const int8_t *A, const int8_t *B, const int32_t *C,
+                        gemm_plan *plan)
+{
+    (void)C;
+    return plan_8(dgor::kFmtI8, variant, M, N, K, A, B, plan);
+}
+
 int gemm_f32_ex(int opA, int opB, int M, int N, int K, float alpha, const float *A, int lda, const float *B,
                 int ldb, float beta, float *C, int ldc, void *stream)
 {
@@ -443,6 +567,7 @@ const char *gemm_variant_name(int variant)
     case GEMM_R5_REGISTER_BLOCKED: return "R5 register-blocked 8x8";
     case GEMM_R6_MFMA_F32: return "R6 FP32 MFMA";
     case GEMM_R7_MFMA_F16: return "R7 16-bit MFMA, FP32 accumulate";
+    case GEMM_R8_MFMA_8BIT: return "R8 8-bit MFMA (FP8: FP32, INT8: INT32 accumulate)";
     default: return "unknown variant";
     }
 }

@@ -103,6 +103,45 @@ __global__ __launch_bounds__(256) void naive_ex(int M, int N, int K, const void 
     }
 }
 
+// The plain kernel for 8-bit inputs: one thread per element, the k-sum in
+// ascending k, FP32 for the FP8 formats (the products of two FP8 values are
+// exact in FP32) and INT32 for INT8 (exact).  The FP8 codes are decoded here
+// from the OCP definitions: E4M3 has 4 exponent bits (bias 7) and 3 fraction
+// bits, E5M2 5 exponent bits (bias 15) and 2 fraction bits; exponent 0 is
+// subnormal.  Inputs are finite by contract.
+__device__ __forceinline__ float fp8_value(uint32_t b, int fmt)
+{
+    const bool e4 = fmt == kFmtE4M3;
+    const uint32_t man_bits = e4 ? 3u : 2u;
+    const int bias = e4 ? 7 : 15;
+    const uint32_t expo = (b & 0x7fu) >> man_bits;
+    const uint32_t frac = b & ((1u << man_bits) - 1u);
+    const float mag = expo ? ldexpf((float)(frac + (1u << man_bits)), (int)expo - bias - (int)man_bits)
+                           : ldexpf((float)frac, 1 - bias - (int)man_bits);
+    return (b & 0x80u) ? -mag : mag;
+}
+
+template <int FMT>
+__global__ __launch_bounds__(256) void naive_8bit(int M, int N, int K, const uint8_t *__restrict__ A,
+                                                  const uint8_t *__restrict__ B, float *__restrict__ C)
+{
+    const int row = blockIdx.y * 16 + threadIdx.y;
+    const int col = blockIdx.x * 16 + threadIdx.x;
+    if (row < M && col < N) {
+        if (FMT == kFmtI8) {
+            int sum = 0;
+            for (int k = 0; k < K; ++k)
+                sum += (int)(int8_t)A[(size_t)row * K + k] * (int)(int8_t)B[(size_t)k * N + col];
+            reinterpret_cast<int *>(C)[(size_t)row * N + col] = sum;
+        } else {
+            float sum = 0.f;
+            for (int k = 0; k < K; ++k)
+                sum = fmaf(fp8_value(A[(size_t)row * K + k], FMT), fp8_value(B[(size_t)k * N + col], FMT), sum);
+            C[(size_t)row * N + col] = sum;
+        }
+    }
+}
+
 // ------------------------------------------------------------- R0 naive ---
 // One thread per element of C, 16 x 16 threads per workgroup, the k-sum held
 // in a register and C written once ("4. GEMM optimisation", 4.1; Lesson 8
@@ -371,6 +410,19 @@ hipError_t launch_naive_ex(const RingArgs &a, float alpha, float beta, int in16,
     else
         hipLaunchKernelGGL((naive_ex<false, false>), grid, blk, 0, stream, a.M, a.N, a.K, a.A, a.lda, a.B, a.ldb,
                            a.C, a.ldc, alpha, beta, in16);
+    return hipGetLastError();
+}
+
+hipError_t launch_naive_8bit(const Problem &p, int fmt, hipStream_t stream)
+{
+    const dim3 grid((p.N + 15) / 16, (p.M + 15) / 16), blk(16, 16);
+    const uint8_t *A = (const uint8_t *)p.A, *B = (const uint8_t *)p.B;
+    if (fmt == kFmtE4M3)
+        hipLaunchKernelGGL(naive_8bit<kFmtE4M3>, grid, blk, 0, stream, p.M, p.N, p.K, A, B, p.C);
+    else if (fmt == kFmtE5M2)
+        hipLaunchKernelGGL(naive_8bit<kFmtE5M2>, grid, blk, 0, stream, p.M, p.N, p.K, A, B, p.C);
+    else
+        hipLaunchKernelGGL(naive_8bit<kFmtI8>, grid, blk, 0, stream, p.M, p.N, p.K, A, B, p.C);
     return hipGetLastError();
 }
 

@@ -67,6 +67,8 @@ typedef enum {
  *   R6 FP32 matrix-core (MFMA) tiles             (Lesson 8 section 21)
  *   R7 16-bit-input matrix-core (MFMA) tiles,     (SGEMM journey Level 6;
  *      FP32 accumulation (binary16 or bfloat16)   Lesson 8 section 22)
+ *   R8 8-bit-input matrix-core (MFMA) tiles:      (Lesson 8 section 22)
+ *      FP8 with FP32, INT8 with INT32 accumulation
  * GEMM_VARIANT_AUTO lets the library choose from the shape and alignment.
  */
 typedef enum {
@@ -79,7 +81,8 @@ typedef enum {
     GEMM_R5_REGISTER_BLOCKED = 5,
     GEMM_R6_MFMA_F32 = 6,
     GEMM_R7_MFMA_F16 = 7,
-    GEMM_VARIANT_COUNT = 8
+    GEMM_R8_MFMA_8BIT = 8,
+    GEMM_VARIANT_COUNT = 9
 } gemm_variant;
 
 /* FP32 inputs, FP32 accumulation and output.  Chooses the fastest variant
@@ -101,11 +104,39 @@ int gemm_f16_f32acc(int M, int N, int K, const uint16_t *A, const uint16_t *B,
 int gemm_bf16_f32acc(int M, int N, int K, const uint16_t *A, const uint16_t *B,
                      float *C, void *stream);
 
+/*
+ * 8-bit inputs, the FP8 and INT8 formats "Lesson 8: how a GPU does matrix
+ * multiply", section 22, lists for matrix units.  One byte per element,
+ * row-major with packed leading dimensions as above.
+ *   gemm_e4m3_f32acc: OCP FP8 E4M3 codes (4 exponent bits, bias 7, 3
+ *     fraction bits, no infinities; 0x7F / 0xFF are NaN);
+ *   gemm_e5m2_f32acc: OCP FP8 E5M2 codes (5 exponent bits, bias 15, 2
+ *     fraction bits);
+ *   both with unscaled values, exact products and FP32 accumulation and
+ *   output.  The matrix cores add each group of eight products of a k-step
+ *   at a fixed point aligned to the group's largest product, keeping about
+ *   13 bits below it, before the FP32 accumulation: a product more than
+ *   2^13 times smaller than the largest of its group is lost.
+ *   gemm_i8_i32acc: signed INT8 inputs, exact INT32 accumulation and output
+ *     (C is int32_t).  K above 131072 -> GEMM_ERR_INVALID_DIM, since
+ *     128 * 128 * K must fit int32.
+ * Calls with 16-byte aligned A and B, K and N multiples of 16, K and N
+ * below 2^22 take R8 (256 x 256 x 64 tiles through a four-stage LDS ring);
+ * others take R0.  Same conventions and errors as gemm_f32 otherwise.
+ */
+int gemm_e4m3_f32acc(int M, int N, int K, const uint8_t *A, const uint8_t *B,
+                     float *C, void *stream);
+int gemm_e5m2_f32acc(int M, int N, int K, const uint8_t *A, const uint8_t *B,
+                     float *C, void *stream);
+int gemm_i8_i32acc(int M, int N, int K, const int8_t *A, const int8_t *B,
+                   int32_t *C, void *stream);
+
 /* Same operations with the variant forced (GEMM_VARIANT_AUTO allowed), for
  * benchmarking and testing every rung.  gemm_f32_variant accepts R0..R6;
- * gemm_f16_f32acc_variant and gemm_bf16_f32acc_variant accept R0 and R7.
- * Any other value -> GEMM_ERR_INVALID_VARIANT.  Same semantics and errors
- * otherwise. */
+ * gemm_f16_f32acc_variant and gemm_bf16_f32acc_variant accept R0 and R7;
+ * the 8-bit ones accept R0 and R8 (R8 on a call its tiles cannot take runs
+ * R0, which the plan reports).  Any other value -> GEMM_ERR_INVALID_VARIANT.
+ * Same semantics and errors otherwise. */
 int gemm_f32_variant(int variant, int M, int N, int K, const float *A,
                      const float *B, float *C, void *stream);
 int gemm_f16_f32acc_variant(int variant, int M, int N, int K,
@@ -114,6 +145,14 @@ int gemm_f16_f32acc_variant(int variant, int M, int N, int K,
 int gemm_bf16_f32acc_variant(int variant, int M, int N, int K,
                              const uint16_t *A, const uint16_t *B, float *C,
                              void *stream);
+int gemm_e4m3_f32acc_variant(int variant, int M, int N, int K,
+                             const uint8_t *A, const uint8_t *B, float *C,
+                             void *stream);
+int gemm_e5m2_f32acc_variant(int variant, int M, int N, int K,
+                             const uint8_t *A, const uint8_t *B, float *C,
+                             void *stream);
+int gemm_i8_i32acc_variant(int variant, int M, int N, int K, const int8_t *A,
+                           const int8_t *B, int32_t *C, void *stream);
 
 /*
  * Launch plan: what a call with these arguments would launch.  Pure host
@@ -149,6 +188,12 @@ int gemm_f16_f32acc_plan(int variant, int M, int N, int K, const uint16_t *A,
                          const uint16_t *B, const float *C, gemm_plan *plan);
 int gemm_bf16_f32acc_plan(int variant, int M, int N, int K, const uint16_t *A,
                           const uint16_t *B, const float *C, gemm_plan *plan);
+int gemm_e4m3_f32acc_plan(int variant, int M, int N, int K, const uint8_t *A,
+                          const uint8_t *B, const float *C, gemm_plan *plan);
+int gemm_e5m2_f32acc_plan(int variant, int M, int N, int K, const uint8_t *A,
+                          const uint8_t *B, const float *C, gemm_plan *plan);
+int gemm_i8_i32acc_plan(int variant, int M, int N, int K, const int8_t *A,
+                        const int8_t *B, const int32_t *C, gemm_plan *plan);
 
 /*
  * General operand layouts and scaling, the interface "Lesson 8: how a GPU

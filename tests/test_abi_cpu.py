@@ -66,7 +66,7 @@ def test_status_and_variant_names():
     for s in range(-7, 0):
         assert dg.status_string(s) and dg.status_string(s) != "unknown status"
     assert dg.status_string(-99) == "unknown status"
-    for v in range(8):
+    for v in range(9):
         assert dg.variant_name(v).startswith(f"R{v} ")
     assert dg.variant_name(42) == "unknown variant"
 
@@ -144,6 +144,44 @@ def test_vector_path_needs_divisible_rows_and_16_byte_alignment():
     assert p["vector_a"] == p["vector_b"] == 1
     p = dg.plan(True, 64, 60, 68)            # f16 needs multiples of 8 halves
     assert p["vector_a"] == 0 and p["vector_b"] == 0
+
+
+def test_8bit_plans_take_the_ring_when_operands_are_aligned():
+    for kind in ("e4m3", "e5m2", "i8"):
+        p = dg.plan(kind, 8192, 8192, 8192)
+        assert p["variant"] == dg.R8_MFMA_8BIT and (p["tile_m"], p["tile_n"], p["tile_k"]) == (256, 256, 64)
+        assert p["lds_stages"] == 4 and p["lds_bytes"] == 4 * 2 * 256 * 64 and p["k_stages"] == 128
+        assert p["grid_x"] * p["grid_y"] == 1024 and p["outputs_per_thread"] == 256
+        # rows read along k must be whole 16-byte vectors, and both operands 16-byte aligned
+        assert dg.plan(kind, 300, 272, 80)["variant"] == dg.R8_MFMA_8BIT
+        assert dg.plan(kind, 300, 272, 88)["variant"] == dg.R0_NAIVE
+        assert dg.plan(kind, 300, 264, 80)["variant"] == dg.R0_NAIVE
+        assert dg.plan(kind, 256, 256, 256, A=8)["variant"] == dg.R0_NAIVE
+        # forcing R8 on a call the ring cannot take runs R0; forcing R0 runs R0
+        assert dg.plan(kind, 300, 264, 80, variant=dg.R8_MFMA_8BIT)["variant"] == dg.R0_NAIVE
+        assert dg.plan(kind, 256, 256, 256, variant=dg.R0_NAIVE)["variant"] == dg.R0_NAIVE
+        for bad in (1, 6, 7, 9):
+            with pytest.raises(dg.GemmError) as e:
+                dg.plan(kind, 4, 4, 4, variant=bad)
+            assert e.value.status == binding.GEMM_ERR_INVALID_VARIANT
+        z = dg.plan(kind, 5, 6, 0)
+        assert z["launches"] == 1 and z["tile_k"] == 0
+    # INT8: 128 * 128 * K must fit int32
+    assert dg.plan("i8", 4, 4, 131072)["launches"] == 1
+    with pytest.raises(dg.GemmError) as e:
+        dg.plan("i8", 4, 4, 131073)
+    assert e.value.status == binding.GEMM_ERR_INVALID_DIM
+    assert dg.plan("e4m3", 4, 4, 131088)["launches"] == 1
+
+
+def test_8bit_entry_points_validate_before_touching_a_device():
+    raw = binding.raw_gemm
+    for kind in ("e4m3", "e5m2", "i8"):
+        assert raw(kind, None, -1, 4, 4, 16, 16, 16, None) == binding.GEMM_ERR_INVALID_DIM
+        assert raw(kind, None, 4, 4, 4, None, 16, 16, None) == binding.GEMM_ERR_NULL_PTR
+        assert raw(kind, None, 0, 4, 4, None, 16, None, None) == binding.GEMM_OK
+        assert raw(kind, 7, 4, 4, 4, 16, 16, 16, None) == binding.GEMM_ERR_INVALID_VARIANT
+    assert raw("i8", None, 4, 4, 200000, 16, 16, 16, None) == binding.GEMM_ERR_INVALID_DIM
 
 
 def test_empty_and_k0_plans():

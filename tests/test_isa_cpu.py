@@ -15,7 +15,8 @@ import pytest
 
 from dense_gemm_optimisation_row_amd import build as hipbuild
 
-RING_KERNELS = [("mfma_f16.hip", "mfma_f16_pipe_kernel"), ("mfma_f32.hip", "mfma_f32_ring_kernel")]
+RING_KERNELS = [("mfma_f16.hip", "mfma_f16_pipe_kernel"), ("mfma_f32.hip", "mfma_f32_ring_kernel"),
+                ("mfma_8bit.hip", "mfma_8bit_ring_kernel")]
 
 
 @pytest.fixture(scope="module", params=RING_KERNELS, ids=lambda v: v[1])
@@ -43,8 +44,9 @@ def _instances(text, name):
 
 def test_every_layout_variant_is_generated(ring):
     asm, kernel = ring
-    # op(A) x op(B) x (overwrite, accumulate), times two input formats for 16-bit
-    want = 16 if kernel == "mfma_f16_pipe_kernel" else 8
+    # 16-bit: op(A) x op(B) x (overwrite, accumulate) x two formats; FP32:
+    # op(A) x op(B) x (overwrite, accumulate); 8-bit: op(A) x op(B) x three formats
+    want = {"mfma_f16_pipe_kernel": 16, "mfma_f32_ring_kernel": 8, "mfma_8bit_ring_kernel": 12}[kernel]
     assert len(_instances(asm, kernel)) == want
 
 
