@@ -16,6 +16,8 @@ Prints ONE JSON line (rank 0; this benchmark runs on one GPU only).
 
 --ladder additionally times every kernel variant (rung) at 1024^3 and
 4096^3 FP32 and 8192^3 FP16 and adds a "ladder" object to the line.
+Unless --no-all-workloads is given, every named workload (the BF16, FP8 and
+INT8 entry points included) is then timed on its own under "all_workloads".
 --copy-calibration runs a plain device-to-device copy of known size first;
 used only by the hardware-counter runs that calibrate HBM byte counts.
 """
@@ -34,7 +36,9 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "GEMM TFLOP/s (2MNK/t) at FP32 4096³ and FP16-in 8192³; % of matrix peak"
-PEAK_TFLOPS = {"f32": 157.3, "f16": 2516.6, "bf16": 2516.6}   # MI355X dense matrix peaks
+# MI355X dense matrix peaks (TFLOP/s, TOP/s for INT8): 1024 SIMDs at 2.4 GHz
+# doing 64 FP32, 1024 16-bit or 2048 8-bit multiply-adds' worth of flops a clock
+PEAK_TFLOPS = {"f32": 157.3, "f16": 2516.6, "bf16": 2516.6, "e4m3": 5033.2, "e5m2": 5033.2, "i8": 5033.2}
 HBM_PEAK_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {
@@ -241,7 +245,9 @@ def all_workloads(dg, inputs, torch, dev, stream, dev_in, wl):
     import numpy as np
 
     res = {}
-    entry = {"f32": dg.gemm_f32, "f16": dg.gemm_f16_f32acc, "bf16": dg.gemm_bf16_f32acc}
+    entry = {"f32": dg.gemm_f32, "f16": dg.gemm_f16_f32acc, "bf16": dg.gemm_bf16_f32acc,
+             "e4m3": dg.gemm_e4m3_f32acc, "e5m2": dg.gemm_e5m2_f32acc, "i8": dg.gemm_i8_i32acc}
+    fp8 = {"e4m3": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2}
     for name, w in inputs.WORKLOADS.items():
         kind = w.dtype
         if wl.get(kind) is not None and wl[kind].name == name and kind in dev_in:
@@ -251,9 +257,12 @@ def all_workloads(dg, inputs, torch, dev, stream, dev_in, wl):
             if kind == "bf16":   # uint16 bit patterns -> bfloat16 tensors
                 a = torch.from_numpy(A.view(np.int16)).view(torch.bfloat16).to(dev)
                 b = torch.from_numpy(B.view(np.int16)).view(torch.bfloat16).to(dev)
+            elif kind in fp8:    # uint8 codes -> float8 tensors
+                a = torch.from_numpy(A).to(dev).view(fp8[kind])
+                b = torch.from_numpy(B).to(dev).view(fp8[kind])
             else:
                 a, b = torch.from_numpy(A).to(dev), torch.from_numpy(B).to(dev)
-            c = torch.empty((w.M, w.N), dtype=torch.float32, device=dev)
+            c = torch.empty((w.M, w.N), dtype=torch.int32 if kind == "i8" else torch.float32, device=dev)
             del A, B
         f = entry[kind]
         est = _time_calls(lambda: f(a, b, c, stream), torch, stream, 3)

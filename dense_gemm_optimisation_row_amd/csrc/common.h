@@ -58,13 +58,14 @@ hipError_t launch_scale_c(float *C, int M, int N, int ldc, float s, hipStream_t 
 hipError_t launch_naive_ex(const RingArgs &args, float alpha, float beta, int in16, hipStream_t stream);
 
 // 8-bit inputs: OCP FP8 E4M3 and E5M2 (FP32 accumulation and output), INT8
-// (INT32 accumulation and output).  The ring kernel takes 256 x 256 tiles of
-// 64 k (one byte per element) and needs 16-byte aligned operands with the
-// row length read along k (and the non-k row length of a k-strided operand)
-// a multiple of 16; the plain kernel takes anything.
+// (INT32 accumulation and output).  The ring kernel takes 256 x 256 tiles in
+// k-steps of 64 (one byte per element), with A staged two steps at a time in
+// three buffers and B one step at a time in four (160 KB of LDS); it needs
+// 16-byte aligned operands with K and N multiples of 16.  The plain kernel
+// takes anything.
 constexpr int kFmtE4M3 = 0, kFmtE5M2 = 1, kFmtI8 = 2;
 constexpr int kRing8Tile = 256, kRing8Depth = 64, kRing8Stages = 4;
-constexpr int kRing8LdsBytes = kRing8Stages * 2 * kRing8Tile * kRing8Depth;
+constexpr int kRing8LdsBytes = 3 * kRing8Tile * 2 * kRing8Depth + kRing8Stages * kRing8Depth * kRing8Tile;
 constexpr int kI8MaxK = 131072;   // |sum| <= 128 * 128 * K must fit int32
 hipError_t launch_ring8(const RingArgs &args, int fmt, hipStream_t stream);
 hipError_t launch_naive_8bit(const Problem &p, int fmt, hipStream_t stream);

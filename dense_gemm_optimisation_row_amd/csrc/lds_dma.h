@@ -62,6 +62,13 @@ constexpr int wait_vmcnt(int n)
 {
     return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);
 }
+// The same with lgkmcnt(0): this wavefront's LDS reads have also returned.
+constexpr int wait_vmcnt_lgkm0(int n)
+{
+    return (n & 15) | ((n >> 4) << 14) | (7 << 4);
+}
+
+static_assert(wait_vmcnt_lgkm0(16) == 0x4070, "vmcnt/lgkmcnt encoding");
 static_assert(wait_vmcnt(0) == 0x0f70 && wait_vmcnt(8) == 0x0f78 && wait_vmcnt(24) == 0x4f78,
               "vmcnt encoding");
 

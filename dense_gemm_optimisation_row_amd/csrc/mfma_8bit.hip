@@ -37,11 +37,17 @@
 //   bit 5 and the parity of lane bits 2..4; a 64-bit read 32 lanes a cycle;
 //   a cycle is conflict-free when its 16-byte units, or 8-byte halves,
 //   differ modulo the 256-byte row of banks).
-// * Pipeline: as the 16-bit ring.  Four stages of 32 KB; each wavefront
-//   issues the fragment reads of the next (sub-)step over the first three
-//   quarters of the current one's MFMAs, and the 8 loads of stage t + 3
-//   spread over all of stage t's MFMAs; one vmcnt(8) wait and one barrier
-//   precede each stage.
+// * Pipeline.  Four LDS buffers of 32 KB.  FP8 reads all fragments of
+//   stage t during stage t - 1, so stage t's buffer is free once stage t
+//   begins: during stage t each wavefront refills it with the 8 loads of
+//   stage t + 4.  INT8 still reads stage t's second sub-step during stage t,
+//   so it refills the buffer of stage t - 1 with stage t + 3.  The loads are
+//   spread over the stage's MFMAs, and the fragment reads of the next
+//   (sub-)step over the first three quarters of those of the current one.
+//   Before stage t: one wait for the loads of stage t + 1 (the later ones
+//   stay in flight) and for this wavefront's own LDS reads, then one
+//   barrier, after which no wavefront still reads the buffer the stage's
+//   loads overwrite.
 #include "common.h"
 #include "lds_dma.h"
 
@@ -105,57 +111,20 @@ struct OpI8 {
 };
 
 namespace ring8 {
-constexpr int BM = 256, BN = 256, BK = 64, NBUF = 4;
-constexpr int A_BYTES = BM * BK;                     // 16 KB
-constexpr int B_BYTES = BK * BN;                     // 16 KB
-constexpr int STAGE_BYTES = A_BYTES + B_BYTES;       // 32 KB
-constexpr int LDS_BYTES = NBUF * STAGE_BYTES;        // 128 KB
-constexpr int LOADS_PER_STAGE = 8;                   // per wavefront: 4 of A, 4 of B
-
-// Lane offsets (bytes) of wave w's four 1 KB loads of one operand tile per
-// stage, relative to the stage's first element (k0 of row t0 for the
-// k-contiguous layout, column t0 of row k0 for the k-strided one).  ext is
-// the extent of the operand's non-k dimension, ld its row stride.
-template <bool KSTRIDED>
-__device__ __forceinline__ void load_offsets(int wave, int lane, int t0, int ext, int ld, uint32_t off[4],
-                                             int &kc)
-{
-    constexpr uint32_t OOB = 0x80000000u;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        if (!KSTRIDED) {
-            const int r = 16 * (4 * wave + q) + (lane >> 2);
-            kc = 16 * ((lane & 3) ^ ((lane >> 4) & 3));   // same in every block
-            off[q] = (uint32_t)(r * ld + kc);
-        } else {
-            const int k = 4 * (4 * wave + q) + (lane >> 4);
-            const int u = (lane & 15) ^ (2 * (k & 7));
-            off[q] = t0 + 16 * u < ext ? (uint32_t)(k * ld + 16 * u) : OOB;
-            kc = 0;
-        }
-    }
-}
-
-// Range in bytes of one stage's descriptor: everything past it is a row
-// past the operand, or a k row past K.
-template <bool KSTRIDED>
-__device__ __forceinline__ int stage_range(int k0, int K, int t0, int ext, int ld)
-{
-    const int k_left = K - k0;
-    if (k_left <= 0)
-        return 0;   // a stage past the last: every load writes zeros
-    if (!KSTRIDED) {
-        if (t0 + 256 <= ext)
-            return 0x7fffffff;
-        return (int)((uint32_t)(ext - t0 - 1) * (uint32_t)ld + (uint32_t)k_left);
-    }
-    if (k_left >= BK)
-        return 0x7fffffff;
-    return (int)((uint32_t)(k_left - 1) * (uint32_t)ld + (uint32_t)(ext - t0));
-}
+constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int A_PAIR_BYTES = BM * 2 * BK;            // 32 KB: A for two k-steps
+constexpr int A_PAIRS = 3;
+constexpr int B_BYTES = BK * BN;                     // 16 KB: B for one k-step
+constexpr int B_BUFS = 4;
+constexpr int B_REGION = A_PAIRS * A_PAIR_BYTES;     // 96 KB
+constexpr int LDS_BYTES = B_REGION + B_BUFS * B_BYTES;   // 160 KB
+constexpr int LOADS_PER_STEP = 8;                    // per wavefront: 4 of A, 4 of B
 }  // namespace ring8
 
-template <class Op, bool TA, bool TB>
+// The plain row-major product (A M x K, B K x N).  A is staged two k-steps
+// at a time so that every A row a load touches is one whole 128-byte line;
+// B rows (256 bytes of a tile) are whole lines already.
+template <class Op>
 __global__ __launch_bounds__(256) void mfma_8bit_ring_kernel(RingArgs args)
 {
     using namespace ring8;
@@ -173,95 +142,108 @@ __global__ __launch_bounds__(256) void mfma_8bit_ring_kernel(RingArgs args)
     const int wr = (wave >> 1) * 128, wc = (wave & 1) * 128;
     constexpr uint32_t OOB = 0x80000000u;
 
-    // ---- loader (the range rules of the 16-bit ring, in bytes)
-    uint32_t a_off[4], b_off[4];
-    int a_kc, b_kc;
-    ring8::load_offsets<TA>(wave, lane, m0, M, lda, a_off, a_kc);
-    ring8::load_offsets<!TB>(wave, lane, n0, N, ldb, b_off, b_kc);
-    const uint32_t lds_a = ring + (uint32_t)(4 * wave * 1024);
-    const uint32_t lds_b = ring + (uint32_t)(A_BYTES + 4 * wave * 1024);
-    struct StageLoads { intx4 ra, rb; uint32_t lds; bool tail; int k_left; };
-    auto prep = [&](int st) {
-        StageLoads L;
-        const int k0 = st * BK;
-        L.ra = rsrc_words(TA ? A + (size_t)k0 * lda + m0 : A + (size_t)m0 * lda + k0, 0);
-        L.ra.z = ring8::stage_range<TA>(k0, K, m0, M, lda);
-        L.rb = rsrc_words(TB ? B + (size_t)n0 * ldb + k0 : B + (size_t)k0 * ldb + n0, 0);
-        L.rb.z = ring8::stage_range<!TB>(k0, K, n0, N, ldb);
-        L.lds = (uint32_t)((st % NBUF) * STAGE_BYTES);
+    // ---- loader.  Step s (k = 64 s .. 64 s + 63) of B lives in B buffer
+    // s % 4; steps 2P and 2P + 1 of A (pair P) in A buffer P % 3.
+    //   A pair buffer: 256 rows of 128 bytes, 16-byte unit c of row r at
+    //     8 r + (c ^ ((r >> 1) & 7)); wave w's load j (0..7) fills rows
+    //     8 n .. 8 n + 7, n = 8 w + j, lane p taking physical unit p % 8 of
+    //     row 8 n + p / 8.
+    //   B buffer: 64 k rows of 256 bytes, unit u of row k at
+    //     16 k + (u ^ (2 (k & 7))); wave w's load q fills rows 4 n .. 4 n + 3,
+    //     n = 4 w + q, lane p taking physical unit p % 16 of row 4 n + p / 16.
+    // Descriptor ranges end at the last row of the operand and at K, so
+    // everything past them loads as zero; A lanes past K in the last pair are
+    // masked (K is a multiple of 16).
+    uint32_t a_off[8], b_off[4];
+    int a_kc[2];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int r = 8 * (8 * wave + j) + (lane >> 3);
+        const int c = (lane & 7) ^ ((4 * (j & 1) + (lane >> 4)) & 7);
+        a_off[j] = (uint32_t)(r * lda + 16 * c);
+        a_kc[j & 1] = 16 * c;
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int k = 4 * (4 * wave + q) + (lane >> 4);
+        const int u = (lane & 15) ^ (2 * (k & 7));
+        b_off[q] = n0 + 16 * u < N ? (uint32_t)(k * ldb + 16 * u) : OOB;
+    }
+    const uint32_t lds_a = ring + (uint32_t)(8 * wave * 1024);
+    const uint32_t lds_b = ring + (uint32_t)(B_REGION + 4 * wave * 1024);
+    // A pair P (into the pair buffer at byte offset buf): its descriptor,
+    // and this wave's load j (0..7) of it
+    struct PairLoads { intx4 r; int k_left; uint32_t dst; };
+    auto a_rsrc = [&](int P, uint32_t buf) {
+        PairLoads L;
+        const int k0 = 2 * BK * P;
         L.k_left = K - k0;
-        L.tail = L.k_left < BK;
+        L.r = rsrc_words(A + (size_t)m0 * lda + k0, 0);
+        L.r.z = L.k_left <= 0 ? 0
+              : (m0 + BM <= M ? 0x7fffffff
+                              : (int)((uint32_t)(M - m0 - 1) * (uint32_t)lda + (uint32_t)L.k_left));
+        L.dst = lds_a + buf;
         return L;
     };
-    auto load = [&](const StageLoads &L, int q) {
-        if (q < 4) {
-            const uint32_t off = (!TA && L.tail && a_kc >= L.k_left) ? OOB : a_off[q];
-            load_to_lds(L.ra, lds_a + L.lds + (uint32_t)(q * 1024), off);
-        } else {
-            const uint32_t off = (TB && L.tail && b_kc >= L.k_left) ? OOB : b_off[q - 4];
-            load_to_lds(L.rb, lds_b + L.lds + (uint32_t)((q - 4) * 1024), off);
-        }
+    auto load_a = [&](const PairLoads &L, int j) {
+        const uint32_t off = a_kc[j & 1] >= L.k_left ? OOB : a_off[j];
+        load_to_lds(L.r, L.dst + (uint32_t)(j * 1024), off);
+    };
+    // B step st: its descriptor
+    auto b_rsrc = [&](int st) {
+        const int k0 = BK * st, k_left = K - k0;
+        intx4 r = rsrc_words(B + (size_t)k0 * ldb + n0, 0);
+        r.z = k_left <= 0 ? 0
+            : (k_left >= BK ? 0x7fffffff : (int)((uint32_t)(k_left - 1) * (uint32_t)ldb + (uint32_t)(N - n0)));
+        return r;
     };
 
     // ---- fragment reads
     const int r32 = lane & 31, g = lane >> 5;
     const int s16 = lane & 15, hg = (lane >> 4) & 1;
-    // k-contiguous block blk: row base + 32 blk + r32, logical units 2 g, 2 g + 1
-    auto kc_addr = [&](uint32_t region, int base, int h) {
-        return region + (uint32_t)((base + r32) * 64 + (((2 * g + h) ^ ((r32 >> 2) & 3)) * 16));
-    };
-    // k-strided block blk, read q: row 32 g + 8 q + s16 / 2, byte 8 (s16 % 2)
-    // of logical unit base / 16 + 2 blk + hg, at physical unit
-    // unit ^ (2 (row & 7)) = unit ^ (s16 & 14); base is 0 or 128, so its unit
-    // bit (8) is applied by XOR on the byte offset.
-    auto ks_units = [&](int base, uint32_t unit[4]) {
+    // A block blk of a step: row wr + 32 blk + r32 of its pair buffer, logical
+    // unit c = 4 half + 2 g + u (u = 0, 1: the lane's two units), physical
+    // unit c ^ ((row >> 1) & 7).  The bits of c do not overlap, so the lane
+    // part (2 g ^ ((r32 >> 1) & 7)) is folded in once and (half, u) applied by
+    // XOR on bits 4..6 of the byte offset, which the row part leaves clear.
+    const uint32_t a_lane = (uint32_t)((wr + r32) * 128) | (uint32_t)(((2 * g) ^ ((r32 >> 1) & 7)) * 16);
+    auto a_lane_at = [&](int half, int u) { return a_lane ^ (uint32_t)((4 * half + u) * 16); };
+    // B block blk, read q (8 k rows): row 32 g + 8 q + s16 / 2, byte
+    // 8 (s16 % 2) of logical unit wc / 16 + 2 blk + hg, at physical unit
+    // unit ^ (s16 & 14); wc (0 or 128) sets unit bit 8, applied by XOR.
+    uint32_t b_lane[4];
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
-            unit[b] = ((uint32_t)(((2 * b) ^ (s16 & 14)) | hg) * 16u) ^ (uint32_t)base;
-    };
-    auto ks_row = [&](uint32_t region) {
-        return region + (uint32_t)((32 * g + (s16 >> 1)) * 256 + 8 * (s16 & 1));
-    };
-    uint32_t a_unit[4], b_unit[4];
-    if (TA)
-        ks_units(wr, a_unit);
-    if (!TB)
-        ks_units(wc, b_unit);
-    const uint32_t a_lane0 = TA ? ks_row(0) : kc_addr(0, wr, 0);
-    const uint32_t a_lane1 = kc_addr(0, wr, 1);
-    const uint32_t b_lane0 = TB ? kc_addr(A_BYTES, wc, 0) : ks_row(A_BYTES);
-    const uint32_t b_lane1 = kc_addr(A_BYTES, wc, 1);
+    for (int b = 0; b < 4; ++b)
+        b_lane[b] = (uint32_t)(B_REGION + (32 * g + (s16 >> 1)) * 256 + 8 * (s16 & 1)) +
+                    (((uint32_t)(((2 * b) ^ (s16 & 14)) | hg) * 16u) ^ (uint32_t)wc);
 
-    // Read `part` (0 .. reads per fragment - 1) of sub-step h's fragment of
-    // block blk: k-contiguous unit 2 g + h kReadsKC + part, or k-strided rows
-    // 32 g + 8 (h kReadsKS + part) + s16 / 2.
     typedef typename Op::Frag Frag;
-    auto read_part = [&](uint32_t stage_off, bool kstrided, uint32_t lane0, uint32_t lane1,
-                         const uint32_t *unit, int blk, int h, int part, Frag &f) {
-        if (!kstrided) {
-            const int u = h * Op::kReadsKC + part;   // 0 or 1: which of the lane's two units
-            const uint32_t addr = (u ? lane1 : lane0) + stage_off + (uint32_t)(blk * 2048);
-            Op::put16(f, part, *reinterpret_cast<const intx4 *>(lds + addr));
-        } else {
-            const int q = h * Op::kReadsKS + part;
-            const uint32_t addr = lane0 + stage_off + (uint32_t)(q * 2048) + unit[blk];
-            Op::put8(f, part, __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_intx2 *)(lds + addr)));
-        }
+    // Where the reads of one sub-step come from: A pair buffer (byte offset)
+    // and half (which step of the pair), B buffer (byte offset), sub-step h.
+    struct ReadSrc { uint32_t a_buf; int a_half; uint32_t b_buf; int h; };
+    auto read_a = [&](const ReadSrc &R, int blk, int part, Frag &f) {
+        const int u = R.h * Op::kReadsKC + part;
+        const uint32_t addr = a_lane_at(R.a_half, u) + R.a_buf + (uint32_t)(blk * 32 * 128);
+        Op::put16(f, part, *reinterpret_cast<const intx4 *>(lds + addr));
+    };
+    auto read_b = [&](const ReadSrc &R, int blk, int part, Frag &f) {
+        const int q = R.h * Op::kReadsKS + part;
+        const uint32_t addr = b_lane[blk] + R.b_buf + (uint32_t)(q * 2048);
+        Op::put8(f, part, __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_intx2 *)(lds + addr)));
     };
     // The reads of one sub-step in the order its MFMAs want them: A block 0,
     // B blocks 0..3, A blocks 1..3; r runs over 0 .. R_SUB - 1.
-    constexpr int PA = TA ? Op::kReadsKS : Op::kReadsKC, PB = TB ? Op::kReadsKC : Op::kReadsKS;
+    constexpr int PA = Op::kReadsKC, PB = Op::kReadsKS;
     constexpr int R_SUB = 4 * PA + 4 * PB;
-    auto fread = [&](int stage, int h, int r, Frag *fa, Frag *fb) {
-        const uint32_t so = (uint32_t)((stage % NBUF) * STAGE_BYTES);
+    auto fread = [&](const ReadSrc &R, int r, Frag *fa, Frag *fb) {
         if (r < PA) {
-            read_part(so, TA, a_lane0, a_lane1, a_unit, 0, h, r, fa[0]);
+            read_a(R, 0, r, fa[0]);
         } else if (r < PA + 4 * PB) {
             const int q = r - PA;
-            read_part(so, !TB, b_lane0, b_lane1, b_unit, q / PB, h, q % PB, fb[q / PB]);
+            read_b(R, q / PB, q % PB, fb[q / PB]);
         } else {
             const int q = r - PA - 4 * PB;
-            read_part(so, TA, a_lane0, a_lane1, a_unit, 1 + q / PA, h, q % PA, fa[1 + q / PA]);
+            read_a(R, 1 + q / PA, q % PA, fa[1 + q / PA]);
         }
     };
 
@@ -288,73 +270,123 @@ __global__ __launch_bounds__(256) void mfma_8bit_ring_kernel(RingArgs args)
             for (int e = 0; e < 16; ++e)
                 acc[i][j][e] = 0;
 
-    // One sub-step h of stage t: its 16 MFMAs (row-major over the blocks)
-    // from (ca, cb); the reads of the next sub-step (h + 1 of stage t, or 0
-    // of stage t + 1) into (na, nb) over the first 12 of them; this
-    // sub-step's share of the 8 loads of stage t + 3, spread evenly over the
-    // stage's MFMAs.
+    // One sub-step h of step s: its 16 MFMAs (row-major over the blocks) from
+    // (ca, cb); the reads of the next sub-step (h + 1 of step s, or 0 of step
+    // s + 1), described by R, into (na, nb) over the first 12 of them; this
+    // sub-step's share of step s's 8 loads (B step s + 3, then half `par` of
+    // A pair s / 2 + 2), spread over the step's MFMAs.
+    //
+    // Buffers: A pair P is read during steps 2P - 1 .. 2P + 1 and refilled
+    // with pair P + 3 during steps 2P + 2, 2P + 3; B step s is read during
+    // steps s - 1 and s and its buffer refilled with step s + 4 during step
+    // s + 1.  Both refills start after the barrier that ends the last reads.
     constexpr int READ_SLOTS = 12;
-    constexpr int LOAD_EVERY = 16 * Op::kSub / LOADS_PER_STAGE;
-    auto substep = [&](int t, int h, const StageLoads &L, Frag *ca, Frag *cb, Frag *na, Frag *nb) {
-        const int nt = h + 1 < Op::kSub ? t : t + 1, nh = h + 1 < Op::kSub ? h + 1 : 0;
+    constexpr int LOAD_EVERY = 16 * Op::kSub / LOADS_PER_STEP;
+    struct StepLoads { intx4 rb; uint32_t b_dst; PairLoads a; };
+    auto substep = [&](int h, int par, const StepLoads &L, const ReadSrc &R, Frag *ca, Frag *cb, Frag *na,
+                       Frag *nb) {
 #pragma unroll
         for (int m = 0; m < 16; ++m) {
             acc[m >> 2][m & 3] = Op::mma(ca[m >> 2], cb[m & 3], acc[m >> 2][m & 3]);
             if (m < READ_SLOTS) {
 #pragma unroll
                 for (int r = m * R_SUB / READ_SLOTS; r < (m + 1) * R_SUB / READ_SLOTS; ++r)
-                    fread(nt, nh, r, na, nb);
+                    fread(R, r, na, nb);
             }
             const int mg = 16 * h + m;
-            if (mg % LOAD_EVERY == LOAD_EVERY - 1)
-                load(L, mg / LOAD_EVERY);
+            if (mg % LOAD_EVERY == LOAD_EVERY - 1) {
+                const int ld = mg / LOAD_EVERY;   // 0..7: B loads 0..3, then the A half
+                if (ld < 4)
+                    load_to_lds(L.rb, L.b_dst + (uint32_t)(ld * 1024), b_off[ld]);
+                else
+                    load_a(L.a, 4 * par + ld - 4);
+            }
             // keep this order: the compiler would otherwise cluster the reads
             // and loads, and move MFMAs across the barrier
             __builtin_amdgcn_sched_barrier(0);
         }
     };
-    // Before stage t: this wavefront's loads of stage t + 1 have landed
-    // (those of t + 2 may stay in flight), and the workgroup meets at the
-    // barrier.  Reads and loads past the last stage touch unused data.
-    auto stage_begin = [&](int t) {
-        __builtin_amdgcn_s_waitcnt(wait_vmcnt(LOADS_PER_STAGE));
+    // Before step s: this wavefront's loads issued before step s - 1 have
+    // landed (B step s + 1, A pair (s + 1) / 2), its LDS reads have returned,
+    // and the workgroup meets at the barrier.  Step 0 needs B step 1 with 12
+    // younger prologue loads in flight; later steps let the previous step's 8
+    // loads fly.
+    auto step_begin = [&](int s, uint32_t a_load_buf) {
+        if (s == 0)
+            __builtin_amdgcn_s_waitcnt(wait_vmcnt_lgkm0(12));
+        else
+            __builtin_amdgcn_s_waitcnt(wait_vmcnt_lgkm0(LOADS_PER_STEP));
         __builtin_amdgcn_s_barrier();
-        const StageLoads L = prep(t + 3);
+        StepLoads L;
+        L.rb = b_rsrc(s + 3);
+        L.b_dst = lds_b + (uint32_t)(((s + 3) & 3) * B_BYTES);
+        L.a = a_rsrc((s >> 1) + 2, a_load_buf);
         __builtin_amdgcn_sched_barrier(0);
         return L;
     };
+    auto b_buf = [](int st) { return (uint32_t)((st & 3) * B_BYTES); };
+    auto next_pair = [](uint32_t pb) { return pb == (uint32_t)((A_PAIRS - 1) * A_PAIR_BYTES) ? 0u : pb + A_PAIR_BYTES; };
 
-    // prologue: loads of stages 0, 1, 2, then the reads of stage 0
+    // prologue: A pair 0, B steps 0 and 1, A pair 1, B step 2; then the reads
+    // of step 0 (A pair 0 and B step 0 landed: 16 younger loads may fly)
     Frag fa0[4], fa1[4], fb0[4], fb1[4];
+    {
+        const PairLoads L = a_rsrc(0, 0);
 #pragma unroll
-    for (int st = 0; st < 3; ++st) {
-        const StageLoads L = prep(st);
-#pragma unroll
-        for (int q = 0; q < 8; ++q)
-            load(L, q);
+        for (int j = 0; j < 8; ++j)
+            load_a(L, j);
     }
-    __builtin_amdgcn_s_waitcnt(wait_vmcnt(2 * LOADS_PER_STAGE));
-    __builtin_amdgcn_s_barrier();
 #pragma unroll
-    for (int r = 0; r < R_SUB; ++r)
-        fread(0, 0, r, fa0, fb0);
+    for (int st = 0; st < 2; ++st) {
+        const intx4 rb = b_rsrc(st);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            load_to_lds(rb, lds_b + b_buf(st) + (uint32_t)(q * 1024), b_off[q]);
+    }
+    {
+        const PairLoads L = a_rsrc(1, A_PAIR_BYTES);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            load_a(L, j);
+    }
+    {
+        const intx4 rb = b_rsrc(2);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            load_to_lds(rb, lds_b + b_buf(2) + (uint32_t)(q * 1024), b_off[q]);
+    }
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(16));
+    __builtin_amdgcn_s_barrier();
+    {
+        const ReadSrc R0{0u, 0, b_buf(0), 0};
+#pragma unroll
+        for (int r = 0; r < R_SUB; ++r)
+            fread(R0, r, fa0, fb0);
+    }
 
+    // Two steps (one A pair, P = s / 2) per trip, so each step's parity is
+    // known here; pa, pa1, pa2 are the buffers of pairs P, P + 1, P + 2.
     const int steps = (K + BK - 1) / BK;
-    if constexpr (Op::kSub == 1) {
-        for (int t = 0; t < steps; t += 2) {
-            StageLoads L = stage_begin(t);
-            substep(t, 0, L, fa0, fb0, fa1, fb1);
-            if (t + 1 < steps) {
-                L = stage_begin(t + 1);
-                substep(t + 1, 0, L, fa1, fb1, fa0, fb0);
+    uint32_t pa = 0;
+    for (int s = 0; s < steps; s += 2) {
+        const uint32_t pa1 = next_pair(pa), pa2 = next_pair(pa1);
+        StepLoads L = step_begin(s, pa2);
+        if constexpr (Op::kSub == 1) {
+            substep(0, 0, L, ReadSrc{pa, 1, b_buf(s + 1), 0}, fa0, fb0, fa1, fb1);
+        } else {
+            substep(0, 0, L, ReadSrc{pa, 0, b_buf(s), 1}, fa0, fb0, fa1, fb1);
+            substep(1, 0, L, ReadSrc{pa, 1, b_buf(s + 1), 0}, fa1, fb1, fa0, fb0);
+        }
+        if (s + 1 < steps) {
+            L = step_begin(s + 1, pa2);
+            if constexpr (Op::kSub == 1) {
+                substep(0, 1, L, ReadSrc{pa1, 0, b_buf(s + 2), 0}, fa1, fb1, fa0, fb0);
+            } else {
+                substep(0, 1, L, ReadSrc{pa, 1, b_buf(s + 1), 1}, fa0, fb0, fa1, fb1);
+                substep(1, 1, L, ReadSrc{pa1, 0, b_buf(s + 2), 0}, fa1, fb1, fa0, fb0);
             }
         }
-    } else {
-        for (int t = 0; t < steps; ++t) {
-            const StageLoads L = stage_begin(t);
-            substep(t, 0, L, fa0, fb0, fa1, fb1);
-            substep(t, 1, L, fa1, fb1, fa0, fb0);
-        }
+        pa = pa1;
     }
     // no load may still be writing this workgroup's LDS when it ends
     __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
@@ -373,39 +405,27 @@ __global__ __launch_bounds__(256) void mfma_8bit_ring_kernel(RingArgs args)
             }
 }
 
-template <class Op, bool TA, bool TB>
+template <class Op>
 hipError_t launch_ring(const RingArgs &a, hipStream_t s)
 {
     const dim3 grid(a.tiles_m * a.tiles_n);
-    hipLaunchKernelGGL((mfma_8bit_ring_kernel<Op, TA, TB>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL(mfma_8bit_ring_kernel<Op>, grid, dim3(256), 0, s, a);
     return hipGetLastError();
-}
-
-template <class Op>
-hipError_t launch_any(const RingArgs &a, hipStream_t s)
-{
-    if (a.trans_a && a.trans_b)
-        return launch_ring<Op, true, true>(a, s);
-    if (a.trans_a)
-        return launch_ring<Op, true, false>(a, s);
-    if (a.trans_b)
-        return launch_ring<Op, false, true>(a, s);
-    return launch_ring<Op, false, false>(a, s);
 }
 
 }  // namespace
 
 hipError_t launch_ring8(const RingArgs &a, int fmt, hipStream_t s)
 {
-    if (a.accumulate)
+    if (a.accumulate || a.trans_a || a.trans_b)
         return hipErrorInvalidValue;
     switch (fmt) {
     case kFmtE4M3:
-        return launch_any<OpFp8<0>>(a, s);
+        return launch_ring<OpFp8<0>>(a, s);
     case kFmtE5M2:
-        return launch_any<OpFp8<1>>(a, s);
+        return launch_ring<OpFp8<1>>(a, s);
     case kFmtI8:
-        return launch_any<OpI8>(a, s);
+        return launch_ring<OpI8>(a, s);
     default:
         return hipErrorInvalidValue;
     }

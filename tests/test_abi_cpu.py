@@ -150,7 +150,8 @@ def test_8bit_plans_take_the_ring_when_operands_are_aligned():
     for kind in ("e4m3", "e5m2", "i8"):
         p = dg.plan(kind, 8192, 8192, 8192)
         assert p["variant"] == dg.R8_MFMA_8BIT and (p["tile_m"], p["tile_n"], p["tile_k"]) == (256, 256, 64)
-        assert p["lds_stages"] == 4 and p["lds_bytes"] == 4 * 2 * 256 * 64 and p["k_stages"] == 128
+        # A in three two-step buffers, B in four one-step buffers: all 160 KB of LDS
+        assert p["lds_stages"] == 4 and p["lds_bytes"] == 163840 and p["k_stages"] == 128
         assert p["grid_x"] * p["grid_y"] == 1024 and p["outputs_per_thread"] == 256
         # rows read along k must be whole 16-byte vectors, and both operands 16-byte aligned
         assert dg.plan(kind, 300, 272, 80)["variant"] == dg.R8_MFMA_8BIT
