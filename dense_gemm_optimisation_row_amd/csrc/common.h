@@ -118,11 +118,14 @@ constexpr int mfma_f16_lds_bytes(const MfmaConfig &c)
 // The largest tile of each type runs a kernel that loads tiles straight from
 // global memory into LDS (unpadded, swizzled stages) when both operands take
 // 128-bit loads; lane byte offsets inside one tile then stay below 2^31.
-// FP32: 128 x 128 x 16, two stages.  FP16: 256 x 256 x 32, a ring of four.
+// FP32: 128 x 128 x 16, two stages.  FP16: 256 x 256 x 32, B in a ring of
+// four stages and (for an A given as M x K) A in three buffers of two stages.
 constexpr int kF32DirectStages = 2;
 constexpr int kF32DirectLdsBytes = kF32DirectStages * (128 * 16 + 16 * 128) * 4;
 constexpr int kF16RingStages = 4;
-constexpr int kF16RingLdsBytes = kF16RingStages * (256 * 32 + 32 * 256) * 2;
+// A staged two stages at a time (three 32 KB buffers), B one stage at a time
+// (four 16 KB buffers): all 160 KB of LDS.
+constexpr int kF16RingLdsBytes = 3 * 256 * 64 * 2 + kF16RingStages * 32 * 256 * 2;
 inline bool direct_lds_applies(int tile_m, int top_tile, bool vec_a, bool vec_b, int N, int K)
 {
     return tile_m == top_tile && vec_a && vec_b && K < (1 << 22) && N < (1 << 22);

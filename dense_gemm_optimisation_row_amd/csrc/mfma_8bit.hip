@@ -154,15 +154,17 @@ __global__ __launch_bounds__(256) void mfma_8bit_ring_kernel(RingArgs args)
     // Descriptor ranges end at the last row of the operand and at K, so
     // everything past them loads as zero; A lanes past K in the last pair are
     // masked (K is a multiple of 16).
-    uint32_t a_off[8], b_off[4];
+    // A load j's lane offset: a_off[j & 1] plus (j / 2) * 16 rows (wave-uniform)
+    uint32_t a_off[2], b_off[4];
     int a_kc[2];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int r = 8 * (8 * wave + j) + (lane >> 3);
-        const int c = (lane & 7) ^ ((4 * (j & 1) + (lane >> 4)) & 7);
+    for (int j = 0; j < 2; ++j) {
+        const int r = 64 * wave + 8 * j + (lane >> 3);
+        const int c = (lane & 7) ^ ((4 * j + (lane >> 4)) & 7);
         a_off[j] = (uint32_t)(r * lda + 16 * c);
-        a_kc[j & 1] = 16 * c;
+        a_kc[j] = 16 * c;
     }
+    const uint32_t a_row16 = (uint32_t)(16 * lda);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int k = 4 * (4 * wave + q) + (lane >> 4);
@@ -186,7 +188,7 @@ __global__ __launch_bounds__(256) void mfma_8bit_ring_kernel(RingArgs args)
         return L;
     };
     auto load_a = [&](const PairLoads &L, int j) {
-        const uint32_t off = a_kc[j & 1] >= L.k_left ? OOB : a_off[j];
+        const uint32_t off = a_kc[j & 1] >= L.k_left ? OOB : a_off[j & 1] + (uint32_t)(j >> 1) * a_row16;
         load_to_lds(L.r, L.dst + (uint32_t)(j * 1024), off);
     };
     // B step st: its descriptor

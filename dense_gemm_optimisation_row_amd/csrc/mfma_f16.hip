@@ -529,6 +529,273 @@ __global__ __launch_bounds__(256) void mfma_f16_pipe_kernel(RingArgs args)
             }
 }
 
+// The ring kernel for a k-contiguous A (A given as M x K), with A staged two
+// k-stages (64 k, 128 bytes of each row) at a time, so that every A row a
+// load touches is one whole 128-byte line rather than half of one; B keeps
+// one stage per buffer (a k-strided B row of a tile is 512 bytes, whole
+// lines already).  Three A pair buffers of 32 KB and four B buffers of
+// 16 KB fill the 160 KB of LDS.
+//   A pair buffer: 256 rows of 128 bytes (eight 16-byte units), unit c of
+//     row r at 8 r + (c ^ ((r >> 1) & 7)); wave w's load j (0..7) fills rows
+//     8 n .. 8 n + 7, n = 8 w + j, lane p taking physical unit p % 8 of row
+//     8 n + p / 8.  A fragment of stage half h (0: first stage of the pair)
+//     is the 128-bit read of unit 4 h + g of row base + s; the swizzle keeps
+//     each 16-lane read cycle on distinct banks.
+//   B buffers: the layouts, loads and reads of the four-stage ring above.
+// Buffers: A pair P is read during stages 2P - 1 and 2P and refilled with
+// pair P + 3 during stages 2P + 2 and 2P + 3; B stage t is read during stage
+// t - 1 and its buffer refilled with stage t + 4 during stage t + 1.  Each
+// stage begins with a wait for the loads issued two stages before (B stage
+// t + 1, A pair (t + 1) / 2) and this wavefront's LDS reads, then a barrier.
+namespace pair16 {
+constexpr int A_PAIR_BYTES = 256 * 64 * 2;           // 32 KB
+constexpr int A_PAIRS = 3;
+constexpr int B_BYTES = 32 * 256 * 2;                // 16 KB
+constexpr int B_REGION = A_PAIRS * A_PAIR_BYTES;     // 96 KB
+constexpr int LDS_BYTES = B_REGION + 4 * B_BYTES;    // 160 KB
+}  // namespace pair16
+
+template <class Op, bool TB, bool ACC>
+__global__ __launch_bounds__(256) void mfma_f16_pair_kernel(RingArgs args)
+{
+    using namespace pair16;
+    constexpr int BK = pipe::BK;                        // 32 k per stage
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
+    const uint32_t ring = lds_address(lds);
+    const int M = args.M, N = args.N, K = args.K, lda = args.lda, ldb = args.ldb;
+    const uint16_t *__restrict__ A = (const uint16_t *)args.A;
+    const uint16_t *__restrict__ B = (const uint16_t *)args.B;
+
+    int tm, tn;
+    dgor_tile_of_block(blockIdx.x, args.tiles_m, args.tiles_n, args.group_m, tm, tn);
+    const int m0 = tm * 256, n0 = tn * 256;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int wr = (wave >> 1) * 128, wc = (wave & 1) * 128;
+    constexpr uint32_t OOB = 0x80000000u;
+
+    // ---- loaders
+    // load j's lane offset: a_off[j & 1] plus (j / 2) * 16 rows (wave-uniform)
+    uint32_t a_off[2];
+    int a_kc[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int r = 64 * wave + 8 * j + (lane >> 3);
+        const int c = (lane & 7) ^ ((4 * j + (lane >> 4)) & 7);
+        a_off[j] = (uint32_t)(r * lda + 8 * c) * 2u;
+        a_kc[j] = 8 * c;
+    }
+    const uint32_t a_row16 = (uint32_t)(16 * lda) * 2u;
+    uint32_t b_off[4];
+    int b_kc;
+    ring16::load_offsets<!TB>(wave, lane, n0, N, ldb, b_off, b_kc);
+    const uint32_t lds_a = ring + (uint32_t)(8 * wave * 1024);
+    const uint32_t lds_b = ring + (uint32_t)(B_REGION + 4 * wave * 1024);
+    struct PairLoads { intx4 r; int k_left; uint32_t dst; };
+    auto a_rsrc = [&](int P, uint32_t buf) {
+        PairLoads L;
+        const int k0 = 2 * BK * P;
+        L.k_left = K - k0;
+        L.r = rsrc_words(A + (size_t)m0 * lda + k0, 0);
+        L.r.z = L.k_left <= 0 ? 0
+              : (m0 + 256 <= M ? 0x7fffffff
+                               : (int)(((uint32_t)(M - m0 - 1) * (uint32_t)lda + (uint32_t)L.k_left) * 2u));
+        L.dst = lds_a + buf;
+        return L;
+    };
+    auto load_a = [&](const PairLoads &L, int j) {
+        const uint32_t off = a_kc[j & 1] >= L.k_left ? OOB : a_off[j & 1] + (uint32_t)(j >> 1) * a_row16;
+        load_to_lds(L.r, L.dst + (uint32_t)(j * 1024), off);
+    };
+    struct BLoads { intx4 r; int k_left; uint32_t dst; };
+    auto b_rsrc = [&](int st) {
+        BLoads L;
+        const int k0 = st * BK;
+        L.k_left = K - k0;
+        L.r = rsrc_words(TB ? B + (size_t)n0 * ldb + k0 : B + (size_t)k0 * ldb + n0, 0);
+        L.r.z = ring16::stage_range<!TB>(k0, K, n0, N, ldb);
+        L.dst = lds_b + (uint32_t)((st & 3) * B_BYTES);
+        return L;
+    };
+    auto load_b = [&](const BLoads &L, int q) {
+        const uint32_t off = (TB && L.k_left < BK && b_kc >= L.k_left) ? OOB : b_off[q];
+        load_to_lds(L.r, L.dst + (uint32_t)(q * 1024), off);
+    };
+
+    // ---- fragment reads.  Lane (g, s) = (lane / 16, lane % 16).
+    const int s16 = lane & 15, g = lane >> 4;
+    // A block i of half h: row wr + 16 i + s16, unit 4 h + g, physical unit
+    // (4 h + g) ^ ((s16 >> 1) & 7); the bits of 4 h and g do not overlap, so
+    // h is applied by XOR on bit 6 of the byte offset.
+    const uint32_t a_lane = (uint32_t)((wr + s16) * 128) | (uint32_t)((g ^ ((s16 >> 1) & 7)) * 16);
+    // B blocks: as in the four-stage ring
+    const int kc_sw = 2 * ((s16 >> 2) & 1);
+    const int ks_x = 4 * (s16 >> 2) + 2 * (g & 1);
+    uint32_t ks_unit[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        ks_unit[j] = (uint32_t)(((2 * j + ((s16 & 3) >> 1)) ^ ks_x) * 16);
+    const uint32_t b_lane = TB ? (uint32_t)(B_REGION + (wc + s16) * 64 + ((g ^ kc_sw) * 16))
+                               : (uint32_t)(B_REGION + (8 * g + (s16 >> 2)) * 512 + 8 * (s16 & 1) + 2 * wc);
+    struct ReadSrc { uint32_t a_buf; int a_half; uint32_t b_buf; };
+    auto read_a = [&](const ReadSrc &R, int i) -> halfx8 {
+        const uint32_t addr = (a_lane ^ (uint32_t)(64 * R.a_half)) + R.a_buf + (uint32_t)(i * 2048);
+        return *reinterpret_cast<const halfx8 *>(lds + addr);
+    };
+    auto read_b = [&](const ReadSrc &R, int j) -> halfx8 {
+        if (TB)
+            return *reinterpret_cast<const halfx8 *>(lds + b_lane + R.b_buf + j * 1024);
+        const uint8_t *p = lds + b_lane + R.b_buf + ks_unit[j];
+        const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4 *)p);
+        const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4 *)(p + 2048));
+        return __builtin_bit_cast(halfx8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    // read r (0..15): A block 0, the eight B blocks, then A blocks 1..7
+    auto fread = [&](const ReadSrc &R, int r, halfx8 *fa, halfx8 *fb) {
+        if (r == 0 || r >= 9)
+            fa[r == 0 ? 0 : r - 8] = read_a(R, r == 0 ? 0 : r - 8);
+        else
+            fb[r - 1] = read_b(R, r - 1);
+    };
+
+    // ---- C tile: lane (g, s) of the wave owns rows 16 i + 4 g + r and
+    // columns 16 j + s of the wave's 128 x 128 block.  An element outside C
+    // gets an out-of-range lane offset, so it reads zero and is not written.
+    const int ldc = args.ldc;
+    const int c_col = n0 + wc + s16;
+    const int c_rows_left = M - m0 - wr - 4 * g;
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(
+        args.C + (size_t)(m0 + wr) * ldc + n0 + wc, ((long long)(M - m0 - wr - 1) * ldc + N - n0 - wc) * 4);
+    auto c_offset = [&](int col, int rows_left, int i, int j, int r, uint32_t &vo, uint32_t &so) {
+        const int ro = 16 * i + r;
+        vo = (ro < rows_left && col + 16 * j < N) ? (uint32_t)((4 * g) * ldc + s16 + 16 * j) * 4u : OOB;
+        so = (uint32_t)(ro * ldc) * 4u;
+    };
+
+    // Accumulators start at zero, or at C itself (ACC: C += A op(B)).
+    floatx4 acc[8][8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                if (ACC) {
+                    uint32_t vo, so;
+                    c_offset(c_col, c_rows_left, i, j, r, vo, so);
+                    acc[i][j][r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rc, vo, so, 0));
+                } else {
+                    acc[i][j][r] = 0.f;
+                }
+            }
+
+    // One stage t (parity `par` within its pair): the 64 MFMAs from (ca, cb);
+    // the 16 fragment reads of stage t + 1 (source R) into (na, nb), one after
+    // each of the first 16 MFMAs; the stage's 8 loads (B stage t + 3, then
+    // half `par` of A pair t / 2 + 2), one after every sixth of the rest.
+    struct StageLoads { BLoads b; PairLoads a; };
+    auto stage = [&](int par, const StageLoads &L, const ReadSrc &R, halfx8 *ca, halfx8 *cb, halfx8 *na,
+                     halfx8 *nb) {
+#pragma unroll
+        for (int m = 0; m < 64; ++m) {
+            const int i = m >> 3, j = m & 7;
+            acc[i][j] = Op::mfma16(ca[i], cb[j], acc[i][j]);
+            if (m < 16)
+                fread(R, m, na, nb);
+            if (m >= 16 && (m - 16) % 6 == 5) {
+                const int ld = (m - 16) / 6;   // 0..7
+                if (ld < 4)
+                    load_b(L.b, ld);
+                else
+                    load_a(L.a, 4 * par + ld - 4);
+            }
+            // keep this order: the compiler would otherwise cluster the reads
+            // and loads, and move MFMAs across the barrier
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    auto stage_begin = [&](int t, uint32_t a_load_buf) {
+        if (t == 0)
+            __builtin_amdgcn_s_waitcnt(wait_vmcnt_lgkm0(12));
+        else
+            __builtin_amdgcn_s_waitcnt(wait_vmcnt_lgkm0(8));
+        __builtin_amdgcn_s_barrier();
+        const StageLoads L{b_rsrc(t + 3), a_rsrc((t >> 1) + 2, a_load_buf)};
+        __builtin_amdgcn_sched_barrier(0);
+        return L;
+    };
+    auto b_buf = [](int st) { return (uint32_t)((st & 3) * B_BYTES); };
+    auto next_pair = [](uint32_t pb) { return pb == (uint32_t)((A_PAIRS - 1) * A_PAIR_BYTES) ? 0u : pb + A_PAIR_BYTES; };
+
+    // prologue: A pair 0, B stages 0 and 1, A pair 1, B stage 2; then the
+    // reads of stage 0 (A pair 0 and B stage 0 landed: 16 younger loads fly)
+    halfx8 fa0[8], fa1[8], fb0[8], fb1[8];
+    {
+        const PairLoads L = a_rsrc(0, 0);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            load_a(L, j);
+    }
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+        const BLoads L = b_rsrc(st);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            load_b(L, q);
+    }
+    {
+        const PairLoads L = a_rsrc(1, A_PAIR_BYTES);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            load_a(L, j);
+    }
+    {
+        const BLoads L = b_rsrc(2);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            load_b(L, q);
+    }
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(16));
+    __builtin_amdgcn_s_barrier();
+    {
+        const ReadSrc R0{0u, 0, b_buf(0)};
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            fread(R0, r, fa0, fb0);
+    }
+
+    // two stages (one A pair) per trip; pa, pa1, pa2: buffers of pairs P, P+1, P+2
+    const int steps = (K + BK - 1) / BK;
+    uint32_t pa = 0;
+    for (int t = 0; t < steps; t += 2) {
+        const uint32_t pa1 = next_pair(pa), pa2 = next_pair(pa1);
+        StageLoads L = stage_begin(t, pa2);
+        stage(0, L, ReadSrc{pa, 1, b_buf(t + 1)}, fa0, fb0, fa1, fb1);
+        if (t + 1 < steps) {
+            L = stage_begin(t + 1, pa2);
+            stage(1, L, ReadSrc{pa1, 0, b_buf(t + 2)}, fa1, fb1, fa0, fb0);
+        }
+        pa = pa1;
+    }
+    // no load may still be writing this workgroup's LDS when it ends
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+
+    // Epilogue: as in the four-stage ring (offsets recomputed from opaque
+    // copies; the accumulators stored as they are).
+    int col_e = c_col, rows_e = c_rows_left;
+    asm volatile("" : "+v"(col_e), "+v"(rows_e));
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                uint32_t vo, so;
+                c_offset(col_e, rows_e, i, j, r, vo, so);
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][r]), rc, vo, so, 0);
+            }
+}
+
 template <class Op, int BM, int BN, int BK, int WM, int WN>
 hipError_t launch_cfg(const Problem &p, const gemm_plan &plan, hipStream_t s)
 {
@@ -554,10 +821,17 @@ template <class Op, bool TA, bool TB>
 hipError_t launch_ring(const RingArgs &a, hipStream_t s)
 {
     const dim3 grid(a.tiles_m * a.tiles_n);
-    if (a.accumulate)
-        hipLaunchKernelGGL((mfma_f16_pipe_kernel<Op, TA, TB, true>), grid, dim3(256), 0, s, a);
-    else
-        hipLaunchKernelGGL((mfma_f16_pipe_kernel<Op, TA, TB, false>), grid, dim3(256), 0, s, a);
+    if constexpr (!TA) {   // k-contiguous A: whole-line A loads
+        if (a.accumulate)
+            hipLaunchKernelGGL((mfma_f16_pair_kernel<Op, TB, true>), grid, dim3(256), 0, s, a);
+        else
+            hipLaunchKernelGGL((mfma_f16_pair_kernel<Op, TB, false>), grid, dim3(256), 0, s, a);
+    } else {
+        if (a.accumulate)
+            hipLaunchKernelGGL((mfma_f16_pipe_kernel<Op, TA, TB, true>), grid, dim3(256), 0, s, a);
+        else
+            hipLaunchKernelGGL((mfma_f16_pipe_kernel<Op, TA, TB, false>), grid, dim3(256), 0, s, a);
+    }
     return hipGetLastError();
 }
 

@@ -15,8 +15,8 @@ import pytest
 
 from dense_gemm_optimisation_row_amd import build as hipbuild
 
-RING_KERNELS = [("mfma_f16.hip", "mfma_f16_pipe_kernel"), ("mfma_f32.hip", "mfma_f32_ring_kernel"),
-                ("mfma_8bit.hip", "mfma_8bit_ring_kernel")]
+RING_KERNELS = [("mfma_f16.hip", "mfma_f16_pipe_kernel"), ("mfma_f16.hip", "mfma_f16_pair_kernel"),
+                ("mfma_f32.hip", "mfma_f32_ring_kernel"), ("mfma_8bit.hip", "mfma_8bit_ring_kernel")]
 
 
 @pytest.fixture(scope="module", params=RING_KERNELS, ids=lambda v: v[1])
@@ -24,7 +24,7 @@ def ring(request, tmp_path_factory):
     if shutil.which("hipcc") is None and not os.path.exists("/opt/rocm/bin/hipcc"):
         pytest.skip("hipcc not available")
     src, kernel = request.param
-    out = tmp_path_factory.mktemp("isa") / (src + ".s")
+    out = tmp_path_factory.mktemp("isa") / (src + "." + kernel + ".s")
     cmd = [hipbuild.hipcc(), *hipbuild.FLAGS, "-S", "--cuda-device-only",
            os.path.join(hipbuild.CSRC, src), "-o", str(out)]
     subprocess.run(cmd, check=True, capture_output=True, text=True)
@@ -44,10 +44,12 @@ def _instances(text, name):
 
 def test_every_layout_variant_is_generated(ring):
     asm, kernel = ring
-    # 16-bit: op(A) x op(B) x (overwrite, accumulate) x two formats; FP32:
+    # 16-bit: op(B) x (overwrite, accumulate) x two formats for each of a
+    # k-contiguous A (pair kernel) and a k-strided A (pipe kernel); FP32:
     # op(A) x op(B) x (overwrite, accumulate); 8-bit: the row-major product in
     # three formats
-    want = {"mfma_f16_pipe_kernel": 16, "mfma_f32_ring_kernel": 8, "mfma_8bit_ring_kernel": 3}[kernel]
+    want = {"mfma_f16_pipe_kernel": 8, "mfma_f16_pair_kernel": 8, "mfma_f32_ring_kernel": 8,
+            "mfma_8bit_ring_kernel": 3}[kernel]
     assert len(_instances(asm, kernel)) == want
 
 
