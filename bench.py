@@ -11,8 +11,12 @@ and compared with the matrix peak of its input type.
 
 Prints ONE JSON line (rank 0; this benchmark runs on one GPU only).
 
-  python bench.py [--steps K] [--warmup W] [--only f32|f16] [--ladder]
-                  [--no-cpu-baseline] [--copy-calibration]
+  python bench.py [--steps K] [--warmup W] [--only f32|f16|bf16|e4m3|e5m2|i8]
+                  [--ladder] [--no-cpu-baseline] [--copy-calibration]
+
+--only times one workload instead of the two-kernel step: the two headline
+ones, or the 8192^3 workloads of the BF16, FP8 (E4M3, E5M2) and INT8 entry
+points (2MNK integer operations per second for INT8).
 
 --ladder additionally times every kernel variant (rung) at 1024^3 and
 4096^3 FP32 and 8192^3 FP16 and adds a "ladder" object to the line.
@@ -41,14 +45,40 @@ METRIC = "GEMM TFLOP/s (2MNK/t) at FP32 4096³ and FP16-in 8192³; % of matrix p
 PEAK_TFLOPS = {"f32": 157.3, "f16": 2516.6, "bf16": 2516.6, "e4m3": 5033.2, "e5m2": 5033.2, "i8": 5033.2}
 HBM_PEAK_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
+_COMMON = ["dense_gemm_optimisation_row_amd/csrc/common.h", "dense_gemm_optimisation_row_amd/csrc/lds_dma.h"]
 KERNEL_SOURCES = {
-    "f32": ["dense_gemm_optimisation_row_amd/csrc/mfma_f32.hip",
-            "dense_gemm_optimisation_row_amd/csrc/common.h",
-            "dense_gemm_optimisation_row_amd/csrc/lds_dma.h"],
-    "f16": ["dense_gemm_optimisation_row_amd/csrc/mfma_f16.hip",
-            "dense_gemm_optimisation_row_amd/csrc/common.h",
-            "dense_gemm_optimisation_row_amd/csrc/lds_dma.h"],
+    "f32": ["dense_gemm_optimisation_row_amd/csrc/mfma_f32.hip"] + _COMMON,
+    "f16": ["dense_gemm_optimisation_row_amd/csrc/mfma_f16.hip"] + _COMMON,
+    "bf16": ["dense_gemm_optimisation_row_amd/csrc/mfma_f16.hip"] + _COMMON,
+    "e4m3": ["dense_gemm_optimisation_row_amd/csrc/mfma_8bit.hip"] + _COMMON,
+    "e5m2": ["dense_gemm_optimisation_row_amd/csrc/mfma_8bit.hip"] + _COMMON,
+    "i8": ["dense_gemm_optimisation_row_amd/csrc/mfma_8bit.hip"] + _COMMON,
 }
+# the workload each format is timed on
+KIND_WORKLOAD = {"f32": "f32_4096", "f16": "f16_8192", "bf16": "bf16_8192", "e4m3": "e4m3_8192",
+                 "e5m2": "e5m2_8192", "i8": "i8_8192"}
+KIND_DTYPE = {"f32": "f32", "f16": "f16-in/f32-acc", "bf16": "bf16-in/f32-acc", "e4m3": "fp8e4m3-in/f32-acc",
+              "e5m2": "fp8e5m2-in/f32-acc", "i8": "i8-in/i32-acc"}
+KIND_LABEL = {"f32": "FP32 GEMM 4096x4096x4096 row-major",
+              "f16": "FP16-in/FP32-acc GEMM 8192x8192x8192 row-major",
+              "bf16": "BF16-in/FP32-acc GEMM 8192x8192x8192 row-major",
+              "e4m3": "FP8 E4M3-in/FP32-acc GEMM 8192x8192x8192 row-major",
+              "e5m2": "FP8 E5M2-in/FP32-acc GEMM 8192x8192x8192 row-major",
+              "i8": "INT8-in/INT32-acc GEMM 8192x8192x8192 row-major"}
+
+
+def entry_point(dg, kind):
+    return {"f32": dg.gemm_f32, "f16": dg.gemm_f16_f32acc, "bf16": dg.gemm_bf16_f32acc,
+            "e4m3": dg.gemm_e4m3_f32acc, "e5m2": dg.gemm_e5m2_f32acc, "i8": dg.gemm_i8_i32acc}[kind]
+
+
+def to_device(torch, np, A, kind, dev):
+    """numpy operand of a format -> device tensor of the entry point's dtype."""
+    if kind == "bf16":      # uint16 bit patterns
+        return torch.from_numpy(A.view(np.int16)).view(torch.bfloat16).to(dev)
+    if kind in ("e4m3", "e5m2"):   # uint8 codes
+        return torch.from_numpy(A).to(dev).view(torch.float8_e4m3fn if kind == "e4m3" else torch.float8_e5m2)
+    return torch.from_numpy(A).to(dev)
 
 
 def kernel_source_hash(kind: str) -> str:
@@ -83,7 +113,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", choices=["all", "f32", "f16"], default="all")
+    ap.add_argument("--only", choices=["all", "f32", "f16", "bf16", "e4m3", "e5m2", "i8"], default="all")
     ap.add_argument("--ladder", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -123,23 +153,20 @@ def main() -> int:
         del src, dst
 
     kinds = ["f32", "f16"] if args.only == "all" else [args.only]
-    wl = {"f32": inputs.WORKLOADS["f32_4096"], "f16": inputs.WORKLOADS["f16_8192"]}
+    wl = {k: inputs.WORKLOADS[KIND_WORKLOAD[k]] for k in kinds}
     dev_in = {}
     for k in kinds:
         A, B = inputs.workload_matrices(wl[k])
-        a = torch.from_numpy(A).to(dev)
-        b = torch.from_numpy(B).to(dev)
-        c = torch.empty((wl[k].M, wl[k].N), dtype=torch.float32, device=dev)
+        a = to_device(torch, np, A, k, dev)
+        b = to_device(torch, np, B, k, dev)
+        c = torch.empty((wl[k].M, wl[k].N), dtype=torch.int32 if k == "i8" else torch.float32, device=dev)
         dev_in[k] = (a, b, c)
         del A, B
     torch.cuda.synchronize()
 
     def call(k):
         a, b, c = dev_in[k]
-        if k == "f32":
-            dg.gemm_f32(a, b, c, stream=stream)
-        else:
-            dg.gemm_f16_f32acc(a, b, c, stream=stream)
+        entry_point(dg, k)(a, b, c, stream=stream)
 
     for _ in range(args.warmup):
         for k in kinds:
@@ -174,7 +201,7 @@ def main() -> int:
         in_bytes = (a.numel() + b.numel()) * a.element_size()
         per[k] = {
             "workload": wl[k].name, "M": wl[k].M, "N": wl[k].N, "K": wl[k].K,
-            "kernel": dg.variant_name(dg.plan(k == "f16", wl[k].M, wl[k].N, wl[k].K)["variant"]),
+            "kernel": dg.variant_name(dg.plan(k, wl[k].M, wl[k].N, wl[k].K)["variant"]),
             "avg_ms": round(avg, 5), "min_ms": round(float(np.min(ms)), 5),
             "tflops": round(tf, 2), "peak_tflops": PEAK_TFLOPS[k],
             "frac_of_peak": round(tf / PEAK_TFLOPS[k], 4),
@@ -185,7 +212,7 @@ def main() -> int:
     roofline = {
         "kernel": per[dom]["kernel"], "workload": per[dom]["workload"],
         "bound": "mfma", "achieved": per[dom]["tflops"], "peak": PEAK_TFLOPS[dom],
-        "unit": "TFLOP/s", "frac": per[dom]["frac_of_peak"],
+        "unit": "TOP/s" if dom == "i8" else "TFLOP/s", "frac": per[dom]["frac_of_peak"],
         "traffic": read_traffic(dom),
         "algorithmic_flops": wl[dom].flops, "algorithmic_bytes": per[dom]["algorithmic_bytes"],
     }
@@ -195,16 +222,15 @@ def main() -> int:
          "frac": per[k]["frac_of_peak"], "traffic": read_traffic(k)}
         for k in kinds if k != dom]
 
+    unit = "TOP/s" if kinds == ["i8"] else "TFLOP/s"
     out = {
-        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "metric": METRIC, "value": round(value, 2), "unit": unit, "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "+".join({"f32": "f32", "f16": "f16-in/f32-acc"}[k] for k in kinds),
+        "dtype": "+".join(KIND_DTYPE[k] for k in kinds),
         "data": "synthetic (seeded numpy PCG64: normal(0,1) f32 4096^3; uniform[-1,1) "
-                "rounded to f16, 8192^3)",
-        "config": {"workload": " + ".join(
-            {"f32": "FP32 GEMM 4096x4096x4096 row-major",
-             "f16": "FP16-in/FP32-acc GEMM 8192x8192x8192 row-major"}[k] for k in kinds),
+                "rounded to the input format, 8192^3)",
+        "config": {"workload": " + ".join(KIND_LABEL[k] for k in kinds),
             "per_step": [wl[k].name for k in kinds]},
         "per_workload": per,
         "roofline": roofline,
@@ -245,26 +271,16 @@ def all_workloads(dg, inputs, torch, dev, stream, dev_in, wl):
     import numpy as np
 
     res = {}
-    entry = {"f32": dg.gemm_f32, "f16": dg.gemm_f16_f32acc, "bf16": dg.gemm_bf16_f32acc,
-             "e4m3": dg.gemm_e4m3_f32acc, "e5m2": dg.gemm_e5m2_f32acc, "i8": dg.gemm_i8_i32acc}
-    fp8 = {"e4m3": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2}
     for name, w in inputs.WORKLOADS.items():
         kind = w.dtype
         if wl.get(kind) is not None and wl[kind].name == name and kind in dev_in:
             a, b, c = dev_in[kind]
         else:
             A, B = inputs.workload_matrices(w)
-            if kind == "bf16":   # uint16 bit patterns -> bfloat16 tensors
-                a = torch.from_numpy(A.view(np.int16)).view(torch.bfloat16).to(dev)
-                b = torch.from_numpy(B.view(np.int16)).view(torch.bfloat16).to(dev)
-            elif kind in fp8:    # uint8 codes -> float8 tensors
-                a = torch.from_numpy(A).to(dev).view(fp8[kind])
-                b = torch.from_numpy(B).to(dev).view(fp8[kind])
-            else:
-                a, b = torch.from_numpy(A).to(dev), torch.from_numpy(B).to(dev)
+            a, b = to_device(torch, np, A, kind, dev), to_device(torch, np, B, kind, dev)
             c = torch.empty((w.M, w.N), dtype=torch.int32 if kind == "i8" else torch.float32, device=dev)
             del A, B
-        f = entry[kind]
+        f = entry_point(dg, kind)
         est = _time_calls(lambda: f(a, b, c, stream), torch, stream, 3)
         reps = max(3, min(200, int(100.0 / max(est, 1e-3))))
         ms = _time_calls(lambda: f(a, b, c, stream), torch, stream, reps)
@@ -315,7 +331,8 @@ def cpu_baseline(kinds, wl, seconds):
     for k in kinds:
         w = wl[k]
         A, B = inputs.workload_matrices(w)
-        fn = oracle.gemm_f16 if k == "f16" else oracle.gemm_f32
+        fn = {"f32": oracle.gemm_f32, "f16": oracle.gemm_f16, "bf16": oracle.gemm_bf16,
+              "e4m3": oracle.gemm_e4m3, "e5m2": oracle.gemm_e5m2, "i8": oracle.gemm_i8}[k]
         rows = max(threads, 8)
         t0 = time.perf_counter()
         fn(A[:rows], B)
