@@ -72,6 +72,8 @@ def configure(lib):
     lib.oracle_gemm_fp8_at.restype = i
     lib.oracle_gemm_i8_at.argtypes = [i, i, i, p, p, i64, p, p, p, i]
     lib.oracle_gemm_i8_at.restype = i
+    lib.oracle_conv2d.argtypes = [i] * 14 + [p, p, p, i]
+    lib.oracle_conv2d.restype = i
     d = ctypes.c_double
     lib.oracle_gemm_ex.argtypes = [i, i, i, i, i, i, d, p, i, p, i, d, p, i, i]
     lib.oracle_gemm_ex.restype = i
@@ -309,3 +311,39 @@ def gemm_e5m2_at(A, B, rows, cols, nthreads: int = 0) -> np.ndarray:
 def gemm_i8_at(A, B, rows, cols, nthreads: int = 0) -> np.ndarray:
     A, B = _check_inputs(A, B, np.int8)
     return _at8(A, B, rows, cols, nthreads)
+
+
+# -------------------------------------------------------------- convolution --
+
+def conv2d_out_size(H: int, W: int, R: int, S: int, stride=(1, 1), pad=(0, 0), dil=(1, 1)):
+    """(P, Q) of a convolution of an H x W image with an R x S filter."""
+    P = (H + 2 * pad[0] - dil[0] * (R - 1) - 1) // stride[0] + 1
+    Q = (W + 2 * pad[1] - dil[1] * (S - 1) - 1) // stride[1] + 1
+    return P, Q
+
+
+def conv2d(fmt: str, x: np.ndarray, w: np.ndarray, stride=(1, 1), pad=(0, 0), dil=(1, 1),
+           nthreads: int = 0) -> np.ndarray:
+    """Direct 2-D convolution (cross-correlation), x N x C x H x W, w K x C x R x S
+    (binary32, binary16 as float16 or uint16 bits, bfloat16 as uint16 bits);
+    returns y N x K x P x Q in binary32."""
+    code = _IN_CODE[fmt]
+    x = np.ascontiguousarray(x)
+    w = np.ascontiguousarray(w)
+    if fmt == "f16":
+        x = x.view(np.uint16) if x.dtype == np.float16 else x
+        w = w.view(np.uint16) if w.dtype == np.float16 else w
+    want = np.float32 if fmt == "f32" else np.uint16
+    if x.dtype != want or w.dtype != want or x.ndim != 4 or w.ndim != 4 or x.shape[1] != w.shape[1]:
+        raise ValueError("x must be N x C x H x W and w K x C x R x S of the input format")
+    N, C, H, W = x.shape
+    K, _, R, S = w.shape
+    P, Q = conv2d_out_size(H, W, R, S, stride, pad, dil)
+    if P <= 0 or Q <= 0:
+        raise ValueError("empty output")
+    y = np.empty((N, K, P, Q), np.float32)
+    rc = _load().oracle_conv2d(code, N, C, H, W, K, R, S, stride[0], stride[1], pad[0], pad[1], dil[0], dil[1],
+                               _ptr(x), _ptr(w), _ptr(y), nthreads)
+    if rc != 0:
+        raise RuntimeError(f"oracle_conv2d failed ({rc})")
+    return y

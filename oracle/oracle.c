@@ -534,3 +534,49 @@ int oracle_gemm_i8_at(int M, int N, int K, const int8_t *A, const int8_t *B, int
     }
     return failed ? ORACLE_ERR_RANGE : ORACLE_OK;
 }
+
+/*
+ * Two-dimensional convolution as deep-learning frameworks define it (a
+ * cross-correlation), the operator "Lesson 8: how a GPU does matrix
+ * multiply" names as the next lesson (convolution as matrix multiplication;
+ * input and output feature maps and weights; channel, height, width; direct
+ * convolution against im2col).  Written out directly, with no im2col:
+ *   x: N x C x H x W, w: K x C x R x S, y: N x K x P x Q (row-major, NCHW),
+ *   P = (H + 2 ph - dh (R - 1) - 1) / sh + 1, Q likewise with W, S, pw, sw, dw,
+ *   y[n][k][p][q] = sum over c, r, s (in that order, ascending) of
+ *       x[n][c][p sh - ph + r dh][q sw - pw + s dw] * w[k][c][r][s],
+ *   terms whose input row or column falls outside the image being zero.
+ * Each element is the binary64 sum of the exact products, rounded once to
+ * binary32.  `in` selects the input format: 0 binary32, 1 binary16 bits,
+ * 2 bfloat16 bits.
+ */
+int oracle_conv2d(int in, int N, int C, int H, int W, int K, int R, int S, int sh, int sw, int ph, int pw,
+                  int dh, int dw, const void *x, const void *w, float *y, int nthreads)
+{
+    if (N < 0 || C < 0 || H < 0 || W < 0 || K < 0 || R < 1 || S < 1 || sh < 1 || sw < 1 || ph < 0 ||
+        pw < 0 || dh < 1 || dw < 1 || in < 0 || in > 2)
+        return ORACLE_ERR_DIM;
+    const int P = (H + 2 * ph - dh * (R - 1) - 1) / sh + 1;
+    const int Q = (W + 2 * pw - dw * (S - 1) - 1) / sw + 1;
+    if (H + 2 * ph - dh * (R - 1) - 1 < 0 || W + 2 * pw - dw * (S - 1) - 1 < 0)
+        return ORACLE_ERR_DIM;
+#pragma omp parallel for collapse(2) num_threads(thread_count(nthreads)) schedule(static)
+    for (int n = 0; n < N; ++n)
+        for (int k = 0; k < K; ++k)
+            for (int p = 0; p < P; ++p)
+                for (int q = 0; q < Q; ++q) {
+                    double acc = 0.0;
+                    for (int c = 0; c < C; ++c)
+                        for (int r = 0; r < R; ++r)
+                            for (int s = 0; s < S; ++s) {
+                                const int h = p * sh - ph + r * dh, v = q * sw - pw + s * dw;
+                                if (h < 0 || h >= H || v < 0 || v >= W)
+                                    continue;
+                                const size_t ix = (((size_t)n * C + c) * H + h) * W + v;
+                                const size_t iw = (((size_t)k * C + c) * R + r) * S + s;
+                                acc += oracle_in_value(in, x, ix) * oracle_in_value(in, w, iw);
+                            }
+                    y[(((size_t)n * K + k) * P + p) * Q + q] = (float)acc;
+                }
+    return ORACLE_OK;
+}

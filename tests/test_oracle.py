@@ -614,3 +614,103 @@ def test_i8_extremes_and_overflow():
         oracle.gemm_i8(A, B)
     with pytest.raises(RuntimeError):
         oracle.gemm_i8_at(A, B, [0], [0])
+
+
+# --------------------------------------------------------------- convolution --
+# 2-D convolution as deep-learning frameworks define it (cross-correlation,
+# NCHW input, KCRS weights, NKPQ output), the operator "Lesson 8: how a GPU
+# does matrix multiply" lists next (convolution as matrix multiplication;
+# direct convolution and im2col).
+
+CONV_CASES = [
+    # (N, C, H, W, K, R, S, stride, pad, dil)
+    (1, 1, 5, 5, 1, 3, 3, (1, 1), (0, 0), (1, 1)),
+    (2, 3, 7, 6, 4, 3, 2, (2, 1), (1, 0), (1, 2)),
+    (1, 4, 9, 9, 5, 3, 3, (1, 1), (1, 1), (1, 1)),
+    (3, 2, 8, 11, 3, 5, 3, (2, 3), (2, 1), (1, 1)),
+    (2, 5, 10, 7, 2, 2, 4, (1, 2), (0, 2), (2, 1)),
+    (1, 3, 6, 6, 6, 1, 1, (2, 2), (0, 0), (1, 1)),
+]
+
+
+def _torch_conv64(x, w, stride, pad, dil):
+    import torch
+    return torch.nn.functional.conv2d(torch.from_numpy(np.asarray(x, np.float64)),
+                                      torch.from_numpy(np.asarray(w, np.float64)),
+                                      stride=stride, padding=pad, dilation=dil).numpy()
+
+
+@pytest.mark.parametrize("case", CONV_CASES, ids=lambda c: "x".join(map(str, c[:7])))
+def test_conv2d_matches_torch_float64_within_one_ulp(case):
+    N, C, H, W, K, R, S, st, pd, dl = case
+    rng = np.random.default_rng(71)
+    x = rng.standard_normal((N, C, H, W)).astype(np.float32)
+    w = rng.standard_normal((K, C, R, S)).astype(np.float32)
+    got = oracle.conv2d("f32", x, w, st, pd, dl)
+    ref = _torch_conv64(x, w, st, pd, dl).astype(np.float32)
+    assert got.shape == ref.shape
+    ulp = np.abs(_bits(got).astype(np.int64) - _bits(ref).astype(np.int64))
+    same_sign = np.signbit(got) == np.signbit(ref)
+    assert np.all(ulp[same_sign] <= 1)
+    assert np.all(np.abs(got[~same_sign]) < 1e-30)
+
+
+def test_conv2d_one_by_one_is_the_gemm_per_image():
+    rng = np.random.default_rng(72)
+    N, C, H, W, K = 3, 19, 5, 7, 11
+    x = rng.standard_normal((N, C, H, W)).astype(np.float32)
+    w = rng.standard_normal((K, C, 1, 1)).astype(np.float32)
+    y = oracle.conv2d("f32", x, w)
+    for n in range(N):
+        want = oracle.gemm_f32(np.ascontiguousarray(w[:, :, 0, 0]), np.ascontiguousarray(x[n].reshape(C, H * W)))
+        assert np.array_equal(_bits(y[n].reshape(K, H * W)), _bits(want))
+
+
+@pytest.mark.parametrize("case", CONV_CASES, ids=lambda c: "x".join(map(str, c[:7])))
+def test_conv2d_all_ones_counts_the_taps_inside_the_image(case):
+    N, C, H, W, K, R, S, st, pd, dl = case
+    y = oracle.conv2d("f32", np.ones((N, C, H, W), np.float32), np.ones((K, C, R, S), np.float32), st, pd, dl)
+    P, Q = y.shape[2:]
+    for p in range(P):
+        rows = sum(0 <= p * st[0] - pd[0] + r * dl[0] < H for r in range(R))
+        for q in range(Q):
+            cols = sum(0 <= q * st[1] - pd[1] + s * dl[1] < W for s in range(S))
+            assert np.all(y[:, :, p, q] == C * rows * cols), (p, q)
+
+
+@pytest.mark.parametrize("case", CONV_CASES, ids=lambda c: "x".join(map(str, c[:7])))
+def test_conv2d_single_input_pixel_picks_out_the_weights(case):
+    # x = one 1 at (n0, c0, h0, v0): y[n0][k][p][q] = w[k][c0][r][s] exactly where
+    # h0 = p sh - ph + r dh and v0 = q sw - pw + s dw, and 0 everywhere else
+    N, C, H, W, K, R, S, st, pd, dl = case
+    rng = np.random.default_rng(73)
+    w = rng.standard_normal((K, C, R, S)).astype(np.float32)
+    for (n0, c0, h0, v0) in [(0, 0, 0, 0), (N - 1, C - 1, H - 1, W - 1), (N // 2, C // 2, H // 2, W // 3)]:
+        x = np.zeros((N, C, H, W), np.float32)
+        x[n0, c0, h0, v0] = 1.0
+        y = oracle.conv2d("f32", x, w, st, pd, dl)
+        want = np.zeros_like(y)
+        for p in range(y.shape[2]):
+            for q in range(y.shape[3]):
+                for r in range(R):
+                    for s in range(S):
+                        if p * st[0] - pd[0] + r * dl[0] == h0 and q * st[1] - pd[1] + s * dl[1] == v0:
+                            want[n0, :, p, q] += w[:, c0, r, s]
+        assert np.array_equal(y, want), (n0, c0, h0, v0)
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+def test_conv2d_16bit_equals_f32_on_the_decoded_values(fmt):
+    rng = np.random.default_rng(74)
+    N, C, H, W, K, R, S, st, pd, dl = CONV_CASES[1]
+    x32 = rng.standard_normal((N, C, H, W)).astype(np.float32)
+    w32 = rng.standard_normal((K, C, R, S)).astype(np.float32)
+    if fmt == "f16":
+        x, w = x32.astype(np.float16), w32.astype(np.float16)
+        xd, wd = x.astype(np.float32), w.astype(np.float32)
+    else:
+        x, w = _bf16_bits(x32), _bf16_bits(w32)
+        xd = (x.astype(np.uint32) << 16).view(np.float32)
+        wd = (w.astype(np.uint32) << 16).view(np.float32)
+    got = oracle.conv2d(fmt, x, w, st, pd, dl)
+    assert np.array_equal(_bits(got), _bits(oracle.conv2d("f32", xd, wd, st, pd, dl)))

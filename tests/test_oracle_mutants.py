@@ -6,7 +6,8 @@ Each mutant is a one-token slip of the kind a hand-written loop nest invites:
 a dropped term, a wrong sign, a transposed operand, a wrong index, a start
 value other than zero, binary32 accumulation, a misdecoded binary16 or
 bfloat16 field, an ignored leading dimension or scale factor, a second
-rounding, a misdecoded FP8 field, or a sign or width slip in the INT8 sum.
+rounding, a misdecoded FP8 field, a sign or width slip in the INT8 sum, or
+a convolution index slip (filter axes, dilation, padding, stride, channel).
 """
 import ctypes
 import shutil
@@ -74,6 +75,17 @@ MUTANTS = {
     "i8_unsigned_A": ("const int64_t a = A[(size_t)i * K + k];", "const int64_t a = (uint8_t)A[(size_t)i * K + k];"),
     "i8_narrow_accumulator": ("int64_t *acc = (int64_t *)malloc((size_t)N * sizeof(int64_t));",
                               "int32_t *acc = (int32_t *)malloc((size_t)N * sizeof(int32_t));"),
+    # convolution
+    "conv_r_s_swapped": ("const size_t iw = (((size_t)k * C + c) * R + r) * S + s;",
+                         "const size_t iw = (((size_t)k * C + c) * R + s % R) * S + r % S;"),
+    "conv_no_row_dilation": ("const int h = p * sh - ph + r * dh, v = q * sw - pw + s * dw;",
+                             "const int h = p * sh - ph + r, v = q * sw - pw + s * dw;"),
+    "conv_padding_sign": ("const int h = p * sh - ph + r * dh, v = q * sw - pw + s * dw;",
+                          "const int h = p * sh + ph + r * dh, v = q * sw - pw + s * dw;"),
+    "conv_column_stride_ignored": ("const int h = p * sh - ph + r * dh, v = q * sw - pw + s * dw;",
+                                   "const int h = p * sh - ph + r * dh, v = q - pw + s * dw;"),
+    "conv_wrong_channel": ("const size_t ix = (((size_t)n * C + c) * H + h) * W + v;",
+                           "const size_t ix = (((size_t)n * C + (c + 1) % C) * H + h) * W + v;"),
     # selected-element routine
     "at_wrong_column": ("* (double)B[(size_t)k * N + j];", "* (double)B[(size_t)k * N + i % N];"),
 }
@@ -118,6 +130,12 @@ PINS = [
     lambda: pins.test_fp8_bruteforce_exact("e5m2"),
     lambda: pins.test_i8_product_is_numpy_int64_product(),
     lambda: pins.test_i8_extremes_and_overflow(),
+    *[(lambda c=c: pins.test_conv2d_matches_torch_float64_within_one_ulp(c)) for c in pins.CONV_CASES],
+    lambda: pins.test_conv2d_one_by_one_is_the_gemm_per_image(),
+    *[(lambda c=c: pins.test_conv2d_all_ones_counts_the_taps_inside_the_image(c)) for c in pins.CONV_CASES],
+    *[(lambda c=c: pins.test_conv2d_single_input_pixel_picks_out_the_weights(c)) for c in pins.CONV_CASES],
+    lambda: pins.test_conv2d_16bit_equals_f32_on_the_decoded_values("f16"),
+    lambda: pins.test_conv2d_16bit_equals_f32_on_the_decoded_values("bf16"),
 ]
 
 
