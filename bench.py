@@ -21,7 +21,9 @@ points (2MNK integer operations per second for INT8).
 --ladder additionally times every kernel variant (rung) at 1024^3 and
 4096^3 FP32 and 8192^3 FP16 and adds a "ladder" object to the line.
 Unless --no-all-workloads is given, every named workload (the BF16, FP8 and
-INT8 entry points included) is then timed on its own under "all_workloads".
+INT8 entry points included) is then timed on its own under "all_workloads",
+and the convolution workloads (im2col + GEMM) under "conv_workloads";
+--conv-only times just the latter.
 --copy-calibration runs a plain device-to-device copy of known size first;
 used only by the hardware-counter runs that calibrate HBM byte counts.
 """
@@ -121,6 +123,8 @@ def main() -> int:
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--no-all-workloads", action="store_true",
                     help="skip timing the smaller parity workloads after the main run")
+    ap.add_argument("--conv-only", action="store_true",
+                    help="time only the convolution workloads (for kernel traces of the im2col path)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -142,6 +146,10 @@ def main() -> int:
     torch.cuda.set_device(dev)
     dg.binding.load()   # fail loudly if the HIP library is missing
     stream = torch.cuda.current_stream(dev)
+
+    if args.conv_only:
+        print(json.dumps({"conv_workloads": conv_workloads(dg, inputs, torch, dev, stream)}), flush=True)
+        return 0
 
     if args.copy_calibration:
         # plain copy of known size, for scaling HBM byte counters
@@ -240,6 +248,7 @@ def main() -> int:
 
     if not args.no_all_workloads:
         out["all_workloads"] = all_workloads(dg, inputs, torch, dev, stream, dev_in, wl)
+        out["conv_workloads"] = conv_workloads(dg, inputs, torch, dev, stream)
 
     if args.ladder:
         out["ladder"] = ladder(dg, inputs, torch, dev, stream)
@@ -289,6 +298,36 @@ def all_workloads(dg, inputs, torch, dev, stream, dev_in, wl):
         res[name] = {"M": w.M, "N": w.N, "K": w.K, "dtype": w.dtype, "ms": round(ms, 5),
                      "tflops": round(tf, 3), "frac_of_peak": round(tf / PEAK_TFLOPS[kind], 4),
                      "kernel": dg.variant_name(p["variant"]), "tile": [p["tile_m"], p["tile_n"]]}
+    return res
+
+
+def conv_workloads(dg, inputs, torch, dev, stream):
+    """Convolutions through im2col + GEMM: 2 N K P Q C R S per call over the
+    whole call (im2col, GEMM and output layout), workspace allocated once."""
+    import numpy as np
+
+    res = {}
+    for name, w in inputs.CONV_WORKLOADS.items():
+        x, wt = inputs.conv_tensors(w)
+        xd, wd = to_device(torch, np, x, w.dtype, dev), to_device(torch, np, wt, w.dtype, dev)
+        P, Q = w.out_hw
+        y = torch.empty((w.N, w.K, P, Q), dtype=torch.float32, device=dev)
+        prm = dg.conv_params(w.N, w.C, w.H, w.W, w.K, w.R, w.S, (w.stride, w.stride), (w.pad, w.pad))
+        ws = torch.empty(dg.conv2d_workspace(prm, xd.element_size()), dtype=torch.uint8, device=dev)
+        f = lambda: dg.conv2d(w.dtype, xd, wd, (w.stride, w.stride), (w.pad, w.pad), y=y, workspace=ws,
+                              stream=stream)
+        est = _time_calls(f, torch, stream, 3)
+        reps = max(3, min(200, int(100.0 / max(est, 1e-3))))
+        ms = _time_calls(f, torch, stream, reps)
+        tf = w.flops / (ms * 1e-3) / 1e12
+        gemm_plan = dg.plan(w.dtype, w.K, -(-w.N * P * Q // 8) * 8, -(-w.C * w.R * w.S // 8) * 8)
+        res[name] = {"N": w.N, "C": w.C, "H": w.H, "W": w.W, "K": w.K, "R": w.R, "S": w.S,
+                     "stride": w.stride, "pad": w.pad, "dtype": w.dtype, "ms": round(ms, 5),
+                     "tflops": round(tf, 3), "frac_of_peak": round(tf / PEAK_TFLOPS[w.dtype], 4),
+                     "gemm": [w.K, w.N * P * Q, w.C * w.R * w.S],
+                     "gemm_tile": [gemm_plan["tile_m"], gemm_plan["tile_n"]],
+                     "workspace_bytes": int(ws.numel())}
+        del xd, wd, y, ws
     return res
 
 

@@ -33,6 +33,7 @@ GEMM_ERR_UNSUPPORTED_DEVICE = -4
 GEMM_ERR_INVALID_VARIANT = -5
 GEMM_ERR_RUNTIME = -6
 GEMM_ERR_INVALID_LAYOUT = -7
+GEMM_ERR_WORKSPACE = -8
 GEMM_OP_N, GEMM_OP_T = 0, 1
 
 AUTO = -1
@@ -51,6 +52,7 @@ EXPORTS = ("gemm_f32", "gemm_f16_f32acc", "gemm_bf16_f32acc",
            "gemm_e4m3_f32acc_variant", "gemm_e5m2_f32acc_variant", "gemm_i8_i32acc_variant",
            "gemm_e4m3_f32acc_plan", "gemm_e5m2_f32acc_plan", "gemm_i8_i32acc_plan",
            "gemm_f32_ex", "gemm_f16_f32acc_ex", "gemm_bf16_f32acc_ex",
+           "gemm_conv2d_workspace", "gemm_conv2d_f32", "gemm_conv2d_f16_f32acc", "gemm_conv2d_bf16_f32acc",
            "gemm_status_string", "gemm_variant_name")
 
 # Entry-point name stem per input format.
@@ -74,6 +76,16 @@ class GemmError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
         super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+class ConvParams(ctypes.Structure):
+    """gemm_conv2d_params of include/gemm.h."""
+    _fields_ = [(n, ctypes.c_int) for n in (
+        "N", "C", "H", "W", "K", "R", "S", "stride_h", "stride_w", "pad_h", "pad_w",
+        "dilation_h", "dilation_w")]
+
+
+_CONV_STEM = {"f32": "gemm_conv2d_f32", "f16": "gemm_conv2d_f16_f32acc", "bf16": "gemm_conv2d_bf16_f32acc"}
 
 
 class Plan(ctypes.Structure):
@@ -113,6 +125,12 @@ def load(path: str = LIB_PATH):
                 f = getattr(lib, stem + "_ex")
                 f.argtypes = [i, i, i, i, i, ctypes.c_float, p, i, p, i, ctypes.c_float, p, i, p]
                 f.restype = i
+        lib.gemm_conv2d_workspace.argtypes = [ctypes.POINTER(ConvParams), i, ctypes.POINTER(ctypes.c_size_t)]
+        lib.gemm_conv2d_workspace.restype = i
+        for stem in _CONV_STEM.values():
+            f = getattr(lib, stem)
+            f.argtypes = [ctypes.POINTER(ConvParams), p, p, p, p, ctypes.c_size_t, p]
+            f.restype = i
         lib.gemm_status_string.argtypes = [i]
         lib.gemm_status_string.restype = ctypes.c_char_p
         lib.gemm_variant_name.argtypes = [i]
@@ -340,3 +358,62 @@ def gemm_e5m2_f32acc_variant(variant, A, B, C=None, stream=None):
 
 def gemm_i8_i32acc_variant(variant, A, B, C=None, stream=None):
     return _call("i8", int(variant), A, B, C, stream)
+
+
+# ------------------------------------------------------------- convolution --
+
+def conv_params(N, C, H, W, K, R, S, stride=(1, 1), pad=(0, 0), dil=(1, 1)) -> ConvParams:
+    return ConvParams(N, C, H, W, K, R, S, stride[0], stride[1], pad[0], pad[1], dil[0], dil[1])
+
+
+def conv2d_workspace(params: ConvParams, input_bytes: int) -> int:
+    """Workspace bytes gemm_conv2d_* needs (host arithmetic; raises on bad params)."""
+    out = ctypes.c_size_t()
+    rc = load().gemm_conv2d_workspace(ctypes.byref(params), int(input_bytes), ctypes.byref(out))
+    if rc != GEMM_OK:
+        raise GemmError(rc, "gemm_conv2d_workspace")
+    return int(out.value)
+
+
+def raw_conv2d(kind, params: ConvParams, x: int | None, w: int | None, y: int | None,
+               workspace: int | None, workspace_bytes: int, stream: int | None) -> int:
+    """gemm_conv2d_* with plain integers; returns the status code."""
+    f = getattr(load(), _CONV_STEM[kind_of(kind)])
+    return int(f(ctypes.byref(params), x, w, y, workspace, workspace_bytes, stream))
+
+
+def conv2d(kind, x, w, stride=(1, 1), padding=(0, 0), dilation=(1, 1), y=None, workspace=None, stream=None):
+    """2-D convolution (NCHW x KCRS -> NKPQ, cross-correlation) of contiguous
+    GPU tensors through im2col and one GEMM.  ``kind`` is "f32", "f16" or
+    "bf16" (FP32 output).  The workspace (a uint8 GPU tensor) is allocated
+    here when not given; the library itself allocates nothing."""
+    import torch
+    kind = kind_of(kind)
+    if kind not in _CONV_STEM:
+        raise ValueError(f"no convolution entry point for {kind}")
+    dtype = _dtypes(kind)[0]
+    if x.dim() != 4 or w.dim() != 4 or x.shape[1] != w.shape[1]:
+        raise ValueError(f"x {tuple(x.shape)} and w {tuple(w.shape)} must be N x C x H x W and K x C x R x S")
+    if x.dtype != dtype or w.dtype != dtype or not (x.is_cuda and w.is_cuda):
+        raise TypeError(f"x and w must be {dtype} GPU tensors")
+    if not (x.is_contiguous() and w.is_contiguous()):
+        raise ValueError("x and w must be contiguous")
+    N, C, H, W = x.shape
+    K, _, R, S = w.shape
+    prm = conv_params(N, C, H, W, K, R, S, stride, padding, dilation)
+    P = (H + 2 * padding[0] - dilation[0] * (R - 1) - 1) // stride[0] + 1
+    Q = (W + 2 * padding[1] - dilation[1] * (S - 1) - 1) // stride[1] + 1
+    if y is None:
+        y = torch.empty((N, K, max(P, 0), max(Q, 0)), dtype=torch.float32, device=x.device)
+    elif (tuple(y.shape) != (N, K, P, Q) or y.dtype != torch.float32 or not y.is_contiguous()
+          or y.device != x.device):
+        raise ValueError("y must be a contiguous float32 N x K x P x Q tensor on x's device")
+    need = conv2d_workspace(prm, x.element_size())
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    with torch.cuda.device(x.device):
+        rc = raw_conv2d(kind, prm, _ptr(x), _ptr(w), _ptr(y), workspace.data_ptr(), workspace.numel(),
+                        _stream_handle(x.device, stream))
+    if rc != GEMM_OK:
+        raise GemmError(rc, _CONV_STEM[kind])
+    return y

@@ -22,7 +22,7 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(ROOT, "_build", "obj")
 LIB = os.path.join(PKG, "libdgor_gemm.so")
 
-SOURCES = ["api.hip", "ladder.hip", "mfma_f32.hip", "mfma_f16.hip", "mfma_8bit.hip"]
+SOURCES = ["api.hip", "ladder.hip", "mfma_f32.hip", "mfma_f16.hip", "mfma_8bit.hip", "conv.hip"]
 ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

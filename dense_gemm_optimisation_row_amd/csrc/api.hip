@@ -411,6 +411,82 @@ int run_ex(In in, int opA, int opB, int M, int N, int K, float alpha, const void
     return GEMM_OK;
 }
 
+// ------------------------------------------------------------ convolution --
+
+constexpr size_t kWsAlign = 256;
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Shape checks and the workspace layout of a convolution: padded weights,
+// im2col matrix, FP32 GEMM result, each starting on a 256-byte boundary.
+struct ConvPlan {
+    dgor::Conv2d cv;
+    int crsp, npqp;
+    size_t off_col, off_y, bytes;
+};
+
+int conv_plan(const gemm_conv2d_params *pr, int elem_bytes, ConvPlan &cp)
+{
+    if (!pr)
+        return GEMM_ERR_NULL_PTR;
+    const gemm_conv2d_params &q = *pr;
+    if (q.N < 0 || q.C < 0 || q.H < 0 || q.W < 0 || q.K < 0 || q.R < 1 || q.S < 1 || q.stride_h < 1 ||
+        q.stride_w < 1 || q.pad_h < 0 || q.pad_w < 0 || q.dilation_h < 1 || q.dilation_w < 1 ||
+        (elem_bytes != 4 && elem_bytes != 2))
+        return GEMM_ERR_INVALID_DIM;
+    const long long span_h = (long long)q.H + 2LL * q.pad_h - (long long)q.dilation_h * (q.R - 1) - 1;
+    const long long span_w = (long long)q.W + 2LL * q.pad_w - (long long)q.dilation_w * (q.S - 1) - 1;
+    if (span_h < 0 || span_w < 0 || span_h > INT32_MAX || span_w > INT32_MAX)
+        return GEMM_ERR_INVALID_DIM;
+    const long long P = span_h / q.stride_h + 1, Q = span_w / q.stride_w + 1;
+    const long long crs = (long long)q.C * q.R * q.S, npq = (long long)q.N * P * Q;
+    const long long crsp = (crs + 7) / 8 * 8, npqp = (npq + 7) / 8 * 8;
+    if (crsp > INT32_MAX || npqp > INT32_MAX || (long long)q.K * npqp > (1LL << 40) ||
+        crsp * npqp > (1LL << 40) || (long long)q.N * q.C * q.H * q.W > (1LL << 40))
+        return GEMM_ERR_INVALID_DIM;
+    cp.cv = dgor::Conv2d{q.N, q.C, q.H, q.W, q.K, q.R, q.S, q.stride_h, q.stride_w, q.pad_h, q.pad_w,
+                         q.dilation_h, q.dilation_w, (int)P, (int)Q};
+    cp.crsp = (int)crsp;
+    cp.npqp = (int)npqp;
+    cp.off_col = round_up((size_t)q.K * (size_t)crsp * elem_bytes, kWsAlign);
+    cp.off_y = cp.off_col + round_up((size_t)crsp * (size_t)npqp * elem_bytes, kWsAlign);
+    cp.bytes = cp.off_y + round_up((size_t)q.K * (size_t)npqp * 4, kWsAlign);
+    return GEMM_OK;
+}
+
+int run_conv(In in, const gemm_conv2d_params *pr, const void *x, const void *w, float *y, void *ws,
+             size_t ws_bytes, void *stream)
+{
+    ConvPlan cp;
+    const int eb = in == In::F32 ? 4 : 2;
+    const int rc = conv_plan(pr, eb, cp);
+    if (rc != GEMM_OK)
+        return rc;
+    const dgor::Conv2d &cv = cp.cv;
+    const long long xs = (long long)cv.N * cv.C * cv.H * cv.W, wsz = (long long)cv.K * cv.C * cv.R * cv.S;
+    const long long ys = (long long)cv.N * cv.K * cv.P * cv.Q;
+    if ((xs > 0 && !x) || (wsz > 0 && !w) || (ys > 0 && !y))
+        return GEMM_ERR_NULL_PTR;
+    if (ys == 0)
+        return GEMM_OK;
+    if (!ws || ws_bytes < cp.bytes || ((uintptr_t)ws & (kWsAlign - 1)))
+        return GEMM_ERR_WORKSPACE;
+    const int dev = check_device();
+    if (dev != GEMM_OK)
+        return dev;
+    hipStream_t s = (hipStream_t)stream;
+    uint8_t *base = (uint8_t *)ws;
+    void *wp = base, *col = base + cp.off_col;
+    float *yp = (float *)(base + cp.off_y);
+    if (dgor::launch_conv_prepare(cv, eb, x, w, wp, col, cp.crsp, cp.npqp, s) != hipSuccess)
+        return GEMM_ERR_LAUNCH;
+    // the GEMM: K x CRSp by CRSp x NPQp, packed, so the planner picks the tile
+    const int g = run(in, GEMM_VARIANT_AUTO, cv.K, cp.npqp, cp.crsp, wp, col, yp, stream);
+    if (g != GEMM_OK)
+        return g;
+    return dgor::launch_conv_output(cv, yp, y, cp.npqp, s) == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
+}
+
 }  // namespace
 
 extern "C" {
@@ -522,6 +598,35 @@ int gemm_i8_i32acc_plan(int variant, int M, int N, int K, const int8_t *A, const
     return plan_8(dgor::kFmtI8, variant, M, N, K, A, B, plan);
 }
 
+int gemm_conv2d_workspace(const gemm_conv2d_params *params, int input_bytes, size_t *bytes)
+{
+    if (!bytes)
+        return GEMM_ERR_NULL_PTR;
+    ConvPlan cp;
+    const int rc = conv_plan(params, input_bytes, cp);
+    if (rc == GEMM_OK)
+        *bytes = cp.bytes;
+    return rc;
+}
+
+int gemm_conv2d_f32(const gemm_conv2d_params *params, const float *x, const float *w, float *y, void *workspace,
+                    size_t workspace_bytes, void *stream)
+{
+    return run_conv(In::F32, params, x, w, y, workspace, workspace_bytes, stream);
+}
+
+int gemm_conv2d_f16_f32acc(const gemm_conv2d_params *params, const uint16_t *x, const uint16_t *w, float *y,
+                           void *workspace, size_t workspace_bytes, void *stream)
+{
+    return run_conv(In::F16, params, x, w, y, workspace, workspace_bytes, stream);
+}
+
+int gemm_conv2d_bf16_f32acc(const gemm_conv2d_params *params, const uint16_t *x, const uint16_t *w, float *y,
+                            void *workspace, size_t workspace_bytes, void *stream)
+{
+    return run_conv(In::BF16, params, x, w, y, workspace, workspace_bytes, stream);
+}
+
 int gemm_f32_ex(int opA, int opB, int M, int N, int K, float alpha, const float *A, int lda, const float *B,
                 int ldb, float beta, float *C, int ldc, void *stream)
 {
@@ -551,6 +656,7 @@ const char *gemm_status_string(int status)
     case GEMM_ERR_INVALID_VARIANT: return "variant not available for this entry point";
     case GEMM_ERR_RUNTIME: return "HIP runtime query failed";
     case GEMM_ERR_INVALID_LAYOUT: return "invalid operand layout (op flag or leading dimension)";
+    case GEMM_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     default: return "unknown status";
     }
 }

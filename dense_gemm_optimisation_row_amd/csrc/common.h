@@ -68,6 +68,15 @@ constexpr int kRing8Tile = 256, kRing8Depth = 64, kRing8Stages = 4;
 constexpr int kRing8LdsBytes = 3 * kRing8Tile * 2 * kRing8Depth + kRing8Stages * kRing8Depth * kRing8Tile;
 constexpr int kI8MaxK = 131072;   // |sum| <= 128 * 128 * K must fit int32
 hipError_t launch_ring8(const RingArgs &args, int fmt, hipStream_t stream);
+
+// Convolution through im2col: shape (P, Q derived), and the passes around the
+// GEMM (conv.hip).  elem_bytes is 4 (binary32) or 2 (16-bit inputs).
+struct Conv2d {
+    int N, C, H, W, K, R, S, sh, sw, ph, pw, dh, dw, P, Q;
+};
+hipError_t launch_conv_prepare(const Conv2d &cv, int elem_bytes, const void *x, const void *w, void *wp, void *col,
+                               int crsp, int npqp, hipStream_t stream);
+hipError_t launch_conv_output(const Conv2d &cv, const float *yp, float *y, int npqp, hipStream_t stream);
 hipError_t launch_naive_8bit(const Problem &p, int fmt, hipStream_t stream);
 
 // The arguments of the ring kernels for a plain row-major product.

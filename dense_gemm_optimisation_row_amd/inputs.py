@@ -66,6 +66,50 @@ WORKLOADS = {
 }
 
 
+@dataclass(frozen=True)
+class ConvWorkload:
+    name: str
+    N: int
+    C: int
+    H: int
+    W: int
+    K: int
+    R: int
+    S: int
+    stride: int
+    pad: int
+    dtype: str
+    seed: int
+
+    @property
+    def out_hw(self):
+        P = (self.H + 2 * self.pad - (self.R - 1) - 1) // self.stride + 1
+        Q = (self.W + 2 * self.pad - (self.S - 1) - 1) // self.stride + 1
+        return P, Q
+
+    @property
+    def flops(self) -> int:
+        P, Q = self.out_hw
+        return 2 * self.N * self.K * P * Q * self.C * self.R * self.S
+
+
+# Convolution workloads (im2col + GEMM): 3 x 3 layers at a 56 x 56 and a
+# 14 x 14 feature map, batch 32, as in image networks; uniform[-1, 1) inputs.
+CONV_WORKLOADS = {
+    w.name: w for w in [
+        ConvWorkload("conv_f16_n32_c64_56x56_k64_3x3", 32, 64, 56, 56, 64, 3, 3, 1, 1, "f16", 1101),
+        ConvWorkload("conv_f16_n32_c256_14x14_k256_3x3", 32, 256, 14, 14, 256, 3, 3, 1, 1, "f16", 1102),
+        ConvWorkload("conv_f32_n32_c256_14x14_k256_3x3", 32, 256, 14, 14, 256, 3, 3, 1, 1, "f32", 1103),
+    ]
+}
+
+
+def conv_tensors(w: ConvWorkload):
+    """(x, w) of a convolution workload: N x C x H x W and K x C x R x S."""
+    return (tensor((w.N, w.C, w.H, w.W), w.seed, "uniform", w.dtype),
+            tensor((w.K, w.C, w.R, w.S), w.seed + 1, "uniform", w.dtype))
+
+
 def _draw(rng: np.random.Generator, shape, dist: str) -> np.ndarray:
     if dist == "uniform":
         return rng.random(shape, dtype=np.float32) * np.float32(2.0) - np.float32(1.0)
@@ -129,24 +173,29 @@ def matrices(M: int, N: int, K: int, seed: int, dist: str = "uniform",
     rng = np.random.default_rng(seed)
     A = _draw(rng, (M, K), dist)
     B = _draw(rng, (K, N), dist)
+    return _convert(A, dtype, dist), _convert(B, dtype, dist)
+
+
+def _convert(X: np.ndarray, dtype: str, dist: str) -> np.ndarray:
+    """A binary32 draw in the input format ``dtype`` (see the module notes)."""
     if dtype == "f16":
-        A = A.astype(np.float16)
-        B = B.astype(np.float16)
+        X = X.astype(np.float16)
     elif dtype == "bf16":
-        A = to_bf16_bits(A)
-        B = to_bf16_bits(B)
+        X = to_bf16_bits(X)
     elif dtype in ("e4m3", "e5m2"):
-        A = to_fp8_codes(A, dtype)
-        B = to_fp8_codes(B, dtype)
+        X = to_fp8_codes(X, dtype)
     elif dtype == "i8":
         if dist != "int":
-            A = np.floor(A.astype(np.float64) * 128)
-            B = np.floor(B.astype(np.float64) * 128)
-        A = np.clip(A, -128, 127).astype(np.int8)
-        B = np.clip(B, -128, 127).astype(np.int8)
+            X = np.floor(X.astype(np.float64) * 128)
+        X = np.clip(X, -128, 127).astype(np.int8)
     elif dtype != "f32":
         raise ValueError(f"unknown dtype {dtype!r}")
-    return np.ascontiguousarray(A), np.ascontiguousarray(B)
+    return np.ascontiguousarray(X)
+
+
+def tensor(shape, seed: int, dist: str = "uniform", dtype: str = "f32") -> np.ndarray:
+    """One seeded array of any shape in the input format ``dtype``."""
+    return _convert(_draw(np.random.default_rng(seed), tuple(shape), dist), dtype, dist)
 
 
 def workload_matrices(w: Workload | str, integer: bool = False):

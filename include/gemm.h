@@ -34,6 +34,7 @@
 #ifndef DGOR_GEMM_H
 #define DGOR_GEMM_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -48,7 +49,8 @@ typedef enum {
     GEMM_ERR_UNSUPPORTED_DEVICE = -4,
     GEMM_ERR_INVALID_VARIANT = -5,
     GEMM_ERR_RUNTIME = -6,
-    GEMM_ERR_INVALID_LAYOUT = -7
+    GEMM_ERR_INVALID_LAYOUT = -7,
+    GEMM_ERR_WORKSPACE = -8
 } gemm_status;
 
 /*
@@ -233,6 +235,52 @@ int gemm_f16_f32acc_ex(int opA, int opB, int M, int N, int K, float alpha,
 int gemm_bf16_f32acc_ex(int opA, int opB, int M, int N, int K, float alpha,
                         const uint16_t *A, int lda, const uint16_t *B, int ldb,
                         float beta, float *C, int ldc, void *stream);
+
+/*
+ * Two-dimensional convolution through im2col and one GEMM -- the operator
+ * "Lesson 8: how a GPU does matrix multiply" names as the next lesson
+ * (convolution as matrix multiplication; input feature maps, weights and
+ * output feature maps; direct convolution against im2col).  As deep-learning
+ * frameworks define it (a cross-correlation), all tensors row-major:
+ *   x: N x C x H x W (NCHW), w: K x C x R x S, y: N x K x P x Q,
+ *   P = (H + 2 pad_h - dilation_h (R - 1) - 1) / stride_h + 1, Q likewise,
+ *   y[n][k][p][q] = sum over c, r, s of
+ *       x[n][c][p stride_h - pad_h + r dilation_h][q stride_w - pad_w + s dilation_w]
+ *       * w[k][c][r][s],  input positions outside the image contributing 0.
+ * Products are exact and summed in FP32 by the GEMM kernels (16-bit inputs:
+ * FP32 accumulation and output, as gemm_f16_f32acc / gemm_bf16_f32acc).
+ * The library allocates nothing: the caller passes a device workspace of at
+ * least the size gemm_conv2d_workspace reports.  It holds the padded weights
+ * (K x CRSp), the im2col matrix (CRSp x NPQp) and the GEMM result
+ * (K x NPQp, FP32), where CRS = C R S and NPQ = N P Q are rounded up to
+ * multiples of 8.  Errors: negative sizes, R, S, strides or dilations below
+ * 1, negative padding, an empty output (P or Q below 1), or sizes whose
+ * products overflow int -> GEMM_ERR_INVALID_DIM; NULL params or a NULL
+ * tensor with nonzero extent -> GEMM_ERR_NULL_PTR; a workspace that is NULL,
+ * not 256-byte aligned, or too small -> GEMM_ERR_WORKSPACE; otherwise as
+ * gemm_f32.  N == 0 or
+ * K == 0 writes nothing; C == 0 writes zeros.  Work is enqueued on `stream`;
+ * the workspace must not be reused until it completes.
+ */
+typedef struct {
+    int N, C, H, W;            /* input: N images, C channels, H x W pixels */
+    int K, R, S;               /* K filters of C x R x S */
+    int stride_h, stride_w;    /* >= 1 */
+    int pad_h, pad_w;          /* >= 0, zero padding on each side */
+    int dilation_h, dilation_w;/* >= 1 */
+} gemm_conv2d_params;
+
+/* Workspace bytes for a convolution with these parameters and input element
+ * size (4 for gemm_conv2d_f32, 2 for the 16-bit forms), in *bytes.  Host
+ * arithmetic only.  Errors as the convolution entry points. */
+int gemm_conv2d_workspace(const gemm_conv2d_params *params, int input_bytes, size_t *bytes);
+
+int gemm_conv2d_f32(const gemm_conv2d_params *params, const float *x, const float *w, float *y,
+                    void *workspace, size_t workspace_bytes, void *stream);
+int gemm_conv2d_f16_f32acc(const gemm_conv2d_params *params, const uint16_t *x, const uint16_t *w,
+                           float *y, void *workspace, size_t workspace_bytes, void *stream);
+int gemm_conv2d_bf16_f32acc(const gemm_conv2d_params *params, const uint16_t *x, const uint16_t *w,
+                            float *y, void *workspace, size_t workspace_bytes, void *stream);
 
 /* Static, NUL-terminated descriptions; never NULL ("unknown ..." for values
  * outside the enums). */

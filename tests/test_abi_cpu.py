@@ -63,7 +63,7 @@ def test_header_is_plain_c(tmp_path):
 
 def test_status_and_variant_names():
     assert dg.status_string(0) == "ok"
-    for s in range(-7, 0):
+    for s in range(-8, 0):
         assert dg.status_string(s) and dg.status_string(s) != "unknown status"
     assert dg.status_string(-99) == "unknown status"
     for v in range(9):
@@ -253,6 +253,50 @@ def test_ex_entry_points_validate_layout_before_touching_a_device():
         assert call(A=None) == NUL and call(B=None) == NUL and call(C=None) == NUL
         assert call(M=0, A=None, C=None) == OK and call(N=0, B=None, C=None) == OK
         assert call(M=0, N=0, K=0, A=None, B=None, C=None) == OK
+
+
+def test_conv2d_workspace_layout_and_validation():
+    cp = binding.conv_params
+    # 32 x 256 x 14 x 14, 256 filters 3 x 3, padding 1: CRS 2304, NPQ 6272 (multiples of 8)
+    p = cp(32, 256, 14, 14, 256, 3, 3, (1, 1), (1, 1))
+    r = lambda v: -(-v // 256) * 256
+    assert dg.conv2d_workspace(p, 2) == r(256 * 2304 * 2) + r(2304 * 6272 * 2) + r(256 * 6272 * 4)
+    assert dg.conv2d_workspace(p, 4) == r(256 * 2304 * 4) + r(2304 * 6272 * 4) + r(256 * 6272 * 4)
+    # CRS 27 and NPQ 2 * 112 * 112 round up to multiples of 8
+    p = cp(2, 3, 224, 224, 64, 3, 3, (2, 2), (1, 1))
+    assert dg.conv2d_workspace(p, 2) == r(64 * 32 * 2) + r(32 * 25088 * 2) + r(64 * 25088 * 4)
+    bad = [cp(-1, 1, 4, 4, 1, 1, 1), cp(1, 1, 4, 4, 1, 0, 1), cp(1, 1, 4, 4, 1, 1, 1, (0, 1)),
+           cp(1, 1, 4, 4, 1, 1, 1, (1, 1), (-1, 0)), cp(1, 1, 4, 4, 1, 1, 1, dil=(1, 0)),
+           cp(1, 1, 2, 2, 1, 5, 1), cp(1, 1, 4, 4, 1, 3, 3, dil=(2, 2))]
+    for b in bad:
+        with pytest.raises(dg.GemmError) as e:
+            dg.conv2d_workspace(b, 4)
+        assert e.value.status == binding.GEMM_ERR_INVALID_DIM
+    with pytest.raises(dg.GemmError):
+        dg.conv2d_workspace(cp(1, 1, 4, 4, 1, 1, 1), 3)
+    lib = binding.load()
+    assert lib.gemm_conv2d_workspace(None, 4, None) == binding.GEMM_ERR_NULL_PTR
+
+
+def test_conv2d_entry_points_validate_before_touching_a_device():
+    cp = binding.conv_params
+    p = cp(2, 3, 8, 8, 4, 3, 3, (1, 1), (1, 1))
+    need = dg.conv2d_workspace(p, 4)
+    for kind in ("f32", "f16", "bf16"):
+        raw = lambda *a: binding.raw_conv2d(kind, *a)
+        assert raw(cp(1, 1, 2, 2, 1, 5, 1), 256, 256, 256, 256, 1 << 20, None) == binding.GEMM_ERR_INVALID_DIM
+        assert raw(p, None, 256, 256, 256, need, None) == binding.GEMM_ERR_NULL_PTR
+        assert raw(p, 256, None, 256, 256, need, None) == binding.GEMM_ERR_NULL_PTR
+        assert raw(p, 256, 256, None, 256, need, None) == binding.GEMM_ERR_NULL_PTR
+        nb = dg.conv2d_workspace(p, 4 if kind == "f32" else 2)
+        assert raw(p, 256, 256, 256, None, nb, None) == binding.GEMM_ERR_WORKSPACE
+        assert raw(p, 256, 256, 256, 256, nb - 1, None) == binding.GEMM_ERR_WORKSPACE
+        assert raw(p, 256, 256, 256, 256 + 16, nb, None) == binding.GEMM_ERR_WORKSPACE
+        # nothing to compute: OK without touching anything
+        assert raw(cp(0, 3, 8, 8, 4, 3, 3), None, 256, None, None, 0, None) == binding.GEMM_OK
+        assert raw(cp(2, 3, 8, 8, 0, 3, 3), 256, None, None, None, 0, None) == binding.GEMM_OK
+    lib = binding.load()
+    assert lib.gemm_conv2d_f32(None, None, None, None, None, 0, None) == binding.GEMM_ERR_NULL_PTR
 
 
 def test_no_device_is_reported_not_crashed():

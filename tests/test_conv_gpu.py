@@ -1,0 +1,143 @@
+"""GPU parity of the convolution entry points (im2col + GEMM) against the
+oracle's direct convolution ("Lesson 8: how a GPU does matrix multiply",
+next lesson: convolution as matrix multiplication, direct against im2col).
+
+Bars: small-integer inputs (values in {-4..4}) bit-exact for every format
+(every partial sum is an integer below 2^24); otherwise the GEMM bars with
+the reduction length CRS = C R S in place of K: FP32 |dy| <= 2e-6 CRS for
+inputs in [-1, 1), 16-bit |dy| <= 2e-3 sqrt(CRS) max|y_ref|.  Shapes cover
+stride, padding, dilation, rectangular filters and images, a reduction
+length that is not a multiple of 8 (padded inside the workspace), and
+layer-sized cases that take the matrix-core tiles.
+"""
+import numpy as np
+import pytest
+
+import dense_gemm_optimisation_row_amd as dg
+from dense_gemm_optimisation_row_amd import binding, inputs
+
+import oracle
+from helpers import say, tol_f16, tol_f32
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU (run the CPU suite with -m 'not gpu')")
+    binding.load()
+    return torch.device("cuda")
+
+
+def draw(fmt, shape, seed, dist):
+    """Seeded tensor in the input format (drawn as an M x K matrix and reshaped)."""
+    n = int(np.prod(shape))
+    A, _ = inputs.matrices(1, 1, n, seed, dist, fmt)
+    return A.reshape(shape)
+
+
+def to_dev(a):
+    import torch
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to("cuda")
+    return torch.from_numpy(a).to("cuda")
+
+
+def run(fmt, x, w, st, pd, dl):
+    import torch
+    y = dg.conv2d(fmt, to_dev(x), to_dev(w), st, pd, dl)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+def check(fmt, got, ref, crs, integer, what):
+    assert got.shape == ref.shape, what
+    if integer:
+        bad = got != ref
+        assert not bad.any(), f"{what}: {int(bad.sum())} elements differ, first {np.argwhere(bad)[0]}"
+        return
+    assert np.all(np.isfinite(got)), what
+    tol = tol_f32(crs) if fmt == "f32" else tol_f16(crs, ref)
+    err = float(np.max(np.abs(got.astype(np.float64) - ref))) if got.size else 0.0
+    assert err <= tol, f"{what}: max |dy| {err:.3e} > {tol:.3e}"
+
+
+SMALL = [
+    # (N, C, H, W, K, R, S, stride, pad, dil)
+    (1, 1, 5, 5, 1, 3, 3, (1, 1), (0, 0), (1, 1)),
+    (2, 3, 7, 6, 4, 3, 2, (2, 1), (1, 0), (1, 2)),
+    (1, 4, 9, 9, 5, 3, 3, (1, 1), (1, 1), (1, 1)),
+    (3, 2, 8, 11, 3, 5, 3, (2, 3), (2, 1), (1, 1)),
+    (2, 5, 10, 7, 2, 2, 4, (1, 2), (0, 2), (2, 1)),
+    (1, 3, 6, 6, 6, 1, 1, (2, 2), (0, 0), (1, 1)),
+    (2, 3, 32, 32, 16, 3, 3, (1, 1), (1, 1), (1, 1)),     # CRS 27: padded to 32
+    (4, 16, 17, 13, 24, 3, 3, (2, 2), (1, 1), (1, 1)),
+]
+LAYERS = [
+    (8, 64, 56, 56, 64, 3, 3, (1, 1), (1, 1), (1, 1)),    # a 56 x 56 stage
+    (4, 128, 28, 28, 256, 3, 3, (2, 2), (1, 1), (1, 1)),  # a strided transition
+    (16, 256, 14, 14, 256, 1, 1, (1, 1), (0, 0), (1, 1)), # a 1 x 1 projection
+    (2, 3, 224, 224, 64, 7, 7, (2, 2), (3, 3), (1, 1)),   # a 7 x 7 stem (CRS 147)
+]
+
+
+def _case(fmt, case, seed, integer):
+    N, C, H, W, K, R, S, st, pd, dl = case
+    dist = "int" if integer else "uniform"
+    x = draw(fmt, (N, C, H, W), seed, dist)
+    w = draw(fmt, (K, C, R, S), seed + 1, dist)
+    what = f"{fmt} {case[:7]} st{st} pd{pd} dl{dl} int={integer}"
+    say("conv", what)
+    ref = oracle.conv2d(fmt, x, w, st, pd, dl).astype(np.float64)
+    check(fmt, run(fmt, x, w, st, pd, dl), ref, C * R * S, integer, what)
+
+
+@pytest.mark.parametrize("fmt", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: "x".join(map(str, c[:7])))
+def test_conv2d_small(fmt, case):
+    _case(fmt, case, 5100, True)
+    _case(fmt, case, 5200, False)
+
+
+@pytest.mark.parametrize("fmt", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("case", LAYERS, ids=lambda c: "x".join(map(str, c[:7])))
+def test_conv2d_layers(fmt, case):
+    _case(fmt, case, 5300, True)
+    _case(fmt, case, 5400, False)
+
+
+@pytest.mark.parametrize("fmt", ["f32", "f16"])
+def test_conv2d_zero_channels_and_empty_batch(fmt):
+    import torch
+    say("conv edges", fmt)
+    dt = torch.float32 if fmt == "f32" else torch.float16
+    x = torch.empty((2, 0, 6, 6), dtype=dt, device="cuda")
+    w = torch.empty((3, 0, 3, 3), dtype=dt, device="cuda")
+    y = torch.full((2, 3, 4, 4), 7.0, device="cuda")
+    dg.conv2d(fmt, x, w, y=y)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(y).item() == 0          # an empty sum
+    x = torch.empty((0, 2, 6, 6), dtype=dt, device="cuda")
+    w = torch.ones((3, 2, 3, 3), dtype=dt, device="cuda")
+    assert dg.conv2d(fmt, x, w).numel() == 0
+
+
+def test_conv2d_workspace_errors_on_the_gpu():
+    import torch
+    say("conv workspace errors")
+    x = torch.ones((1, 2, 6, 6), device="cuda")
+    w = torch.ones((3, 2, 3, 3), device="cuda")
+    y = torch.empty((1, 3, 4, 4), device="cuda")
+    p = binding.conv_params(1, 2, 6, 6, 3, 3, 3)
+    need = dg.conv2d_workspace(p, 4)
+    ws = torch.empty(need + 512, dtype=torch.uint8, device="cuda")
+    rc = binding.raw_conv2d("f32", p, x.data_ptr(), w.data_ptr(), y.data_ptr(), ws.data_ptr(), need - 1, None)
+    assert rc == binding.GEMM_ERR_WORKSPACE
+    rc = binding.raw_conv2d("f32", p, x.data_ptr(), w.data_ptr(), y.data_ptr(), ws.data_ptr() + 8, need, None)
+    assert rc == binding.GEMM_ERR_WORKSPACE
+    rc = binding.raw_conv2d("f32", p, x.data_ptr(), w.data_ptr(), y.data_ptr(), ws.data_ptr(), need, None)
+    torch.cuda.synchronize()
+    assert rc == binding.GEMM_OK and torch.all(y == 18.0).item()
