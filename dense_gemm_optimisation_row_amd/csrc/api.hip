@@ -422,7 +422,9 @@ size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 struct ConvPlan {
     dgor::Conv2d cv;
     int crsp, npqp;
-    size_t off_col, off_y, bytes;
+    bool ring;        // the GEMM runs on the 256 x 256 ring kernels, split over k
+    int splits, k_chunk;
+    size_t off_col, off_y, split_stride, bytes;
 };
 
 int conv_plan(const gemm_conv2d_params *pr, int elem_bytes, ConvPlan &cp)
@@ -448,9 +450,28 @@ int conv_plan(const gemm_conv2d_params *pr, int elem_bytes, ConvPlan &cp)
                          q.dilation_h, q.dilation_w, (int)P, (int)Q};
     cp.crsp = (int)crsp;
     cp.npqp = (int)npqp;
+    // The GEMM (K x CRSp by CRSp x NPQp) runs on the 256 x 256 ring kernels
+    // when at least 192 filters fill most of a tile's 256 rows and the
+    // reduction is at least one 64-deep chunk, split over k until tiles x
+    // splits covers the 256 CUs (chunks of at least 64, multiples of 64); the
+    // partial results are summed by the output pass.  Otherwise the planner's
+    // tiles take it whole.
+    cp.ring = q.K >= 192 && crsp >= 64 && npqp < (1 << 21) && crsp < (1 << 21);
+    cp.splits = 1;
+    cp.k_chunk = (int)crsp;
+    if (cp.ring) {
+        const long long tiles = ((q.K + 255) / 256) * ((npqp + 255) / 256);
+        long long want = (256 + tiles - 1) / tiles;
+        want = want < crsp / 64 ? want : crsp / 64;
+        want = want > 1 ? want : 1;
+        const long long chunk = ((crsp + want - 1) / want + 63) / 64 * 64;
+        cp.k_chunk = (int)chunk;
+        cp.splits = (int)((crsp + chunk - 1) / chunk);
+    }
     cp.off_col = round_up((size_t)q.K * (size_t)crsp * elem_bytes, kWsAlign);
     cp.off_y = cp.off_col + round_up((size_t)crsp * (size_t)npqp * elem_bytes, kWsAlign);
-    cp.bytes = cp.off_y + round_up((size_t)q.K * (size_t)npqp * 4, kWsAlign);
+    cp.split_stride = round_up((size_t)q.K * (size_t)npqp * 4, kWsAlign) / 4;
+    cp.bytes = cp.off_y + (size_t)cp.splits * cp.split_stride * 4;
     return GEMM_OK;
 }
 
@@ -480,11 +501,23 @@ int run_conv(In in, const gemm_conv2d_params *pr, const void *x, const void *w, 
     float *yp = (float *)(base + cp.off_y);
     if (dgor::launch_conv_prepare(cv, eb, x, w, wp, col, cp.crsp, cp.npqp, s) != hipSuccess)
         return GEMM_ERR_LAUNCH;
-    // the GEMM: K x CRSp by CRSp x NPQp, packed, so the planner picks the tile
-    const int g = run(in, GEMM_VARIANT_AUTO, cv.K, cp.npqp, cp.crsp, wp, col, yp, stream);
-    if (g != GEMM_OK)
-        return g;
-    return dgor::launch_conv_output(cv, yp, y, cp.npqp, s) == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
+    // the GEMM: K x CRSp by CRSp x NPQp
+    if (cp.ring) {
+        dgor::RingArgs a{cv.K, cp.npqp, cp.crsp, wp, cp.crsp, col, cp.npqp, yp, cp.npqp,
+                         (cv.K + 255) / 256, (cp.npqp + 255) / 256, 4, false, false, false};
+        a.splits = cp.splits;
+        a.k_chunk = cp.k_chunk;
+        a.c_split_stride = cp.split_stride;
+        const hipError_t e = in == In::F32 ? dgor::launch_ring32(a, s) : dgor::launch_ring16(a, s, in == In::BF16);
+        if (e != hipSuccess)
+            return GEMM_ERR_LAUNCH;
+    } else {
+        const int g = run(in, GEMM_VARIANT_AUTO, cv.K, cp.npqp, cp.crsp, wp, col, yp, stream);
+        if (g != GEMM_OK)
+            return g;
+    }
+    return dgor::launch_conv_output(cv, yp, y, cp.npqp, cp.splits, cp.split_stride, s) == hipSuccess
+               ? GEMM_OK : GEMM_ERR_LAUNCH;
 }
 
 }  // namespace

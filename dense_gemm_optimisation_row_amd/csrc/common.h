@@ -26,6 +26,11 @@ struct Problem {
 // (ldb >= K); C is M x N (ldc >= N).  The kernel writes C = op(A) op(B), or
 // with `accumulate` C = C + op(A) op(B) (C read first).  Operands must be
 // 16-byte aligned with every leading dimension a multiple of 16 bytes.
+// Split-K (splits > 1, not with accumulate): the launch has tiles_m *
+// tiles_n * splits workgroups; workgroup b computes tile b % (tiles_m
+// tiles_n) over k-range [s k_chunk, min(K, (s + 1) k_chunk)) with
+// s = b / (tiles_m tiles_n), and writes it to C + s c_split_stride.  k_chunk
+// is a multiple of 64.
 struct RingArgs {
     int M, N, K;
     const void *A;
@@ -36,6 +41,8 @@ struct RingArgs {
     int ldc;
     int tiles_m, tiles_n, group_m;
     bool trans_a, trans_b, accumulate;
+    int splits = 1, k_chunk = 0;
+    size_t c_split_stride = 0;
 };
 
 // Launchers.  Each enqueues exactly the kernel `plan` describes on `stream`
@@ -76,7 +83,8 @@ struct Conv2d {
 };
 hipError_t launch_conv_prepare(const Conv2d &cv, int elem_bytes, const void *x, const void *w, void *wp, void *col,
                                int crsp, int npqp, hipStream_t stream);
-hipError_t launch_conv_output(const Conv2d &cv, const float *yp, float *y, int npqp, hipStream_t stream);
+hipError_t launch_conv_output(const Conv2d &cv, const float *yp, float *y, int npqp, int splits,
+                              size_t split_stride, hipStream_t stream);
 hipError_t launch_naive_8bit(const Problem &p, int fmt, hipStream_t stream);
 
 // The arguments of the ring kernels for a plain row-major product.
@@ -158,6 +166,25 @@ inline bool f32_ring_applies(int M, int N, int K, bool vec_a, bool vec_b)
 // ---------------------------------------------------------------------------
 // Device helpers
 // ---------------------------------------------------------------------------
+
+// The part of a split-K launch this workgroup computes: narrows a's k-range
+// and moves its A, B and C to that split (elem_bytes: input element size),
+// and returns the workgroup's tile index.  Wave-uniform.
+__device__ __forceinline__ int dgor_ring_split(dgor::RingArgs &a, int elem_bytes)
+{
+    int bid = blockIdx.x;
+    if (a.splits > 1) {
+        const int tiles = a.tiles_m * a.tiles_n;
+        const int sp = bid / tiles;
+        bid -= sp * tiles;
+        const int k0 = sp * a.k_chunk;
+        a.K = min(a.k_chunk, a.K - k0);
+        a.A = (const char *)a.A + (a.trans_a ? (size_t)k0 * a.lda : (size_t)k0) * elem_bytes;
+        a.B = (const char *)a.B + (a.trans_b ? (size_t)k0 : (size_t)k0 * a.ldb) * elem_bytes;
+        a.C += (size_t)sp * a.c_split_stride;
+    }
+    return bid;
+}
 
 // Workgroup -> output tile, aware of the chip's 8 XCDs.  Consecutive
 // workgroup ids are dealt round-robin to the XCDs, each with its own L2, so

@@ -10,7 +10,7 @@
 // bound passes here prepare its operands and lay its result out as NKPQ:
 //   pad_weights: W (K x CRS) into K x CRSp, zero columns past CRS;
 //   im2col:      col into CRSp x NPQp, zero rows past CRS and columns past NPQ;
-//   to_nkpq:     Y' (K x NPQp) into y.
+//   to_nkpq:     Y' (K x NPQp) into y, summing the split-K partials in order.
 // CRSp and NPQp round CRS and NPQ up to multiples of 8, so both GEMM operands
 // take 16-byte loads; the padding adds exact zeros only.
 #include "common.h"
@@ -71,15 +71,21 @@ __global__ __launch_bounds__(256) void im2col(const T *__restrict__ x, T *__rest
     }
 }
 
+// y[n][k][p Q + q] = sum over s < splits, ascending, of the split-K partials
+// Y'_s[k][n PQ + p Q + q] (one partial without split-K).
 __global__ __launch_bounds__(256) void to_nkpq(const float *__restrict__ yp, float *__restrict__ y, int N, int K,
-                                               int PQ, int npqp)
+                                               int PQ, int npqp, int splits, size_t split_stride)
 {
     const size_t total = (size_t)N * K * PQ;
     for (size_t e = (size_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (size_t)gridDim.x * 256) {
         const int pq = (int)(e % PQ);
         const size_t nk = e / PQ;
         const int k = (int)(nk % K), n = (int)(nk / K);
-        y[e] = yp[(size_t)k * npqp + (size_t)n * PQ + pq];
+        const float *src = yp + (size_t)k * npqp + (size_t)n * PQ + pq;
+        float v = src[0];
+        for (int sp = 1; sp < splits; ++sp)
+            v += src[(size_t)sp * split_stride];
+        y[e] = v;
     }
 }
 
@@ -112,10 +118,12 @@ hipError_t launch_conv_prepare(const Conv2d &cv, int elem_bytes, const void *x, 
     return hipGetLastError();
 }
 
-hipError_t launch_conv_output(const Conv2d &cv, const float *yp, float *y, int npqp, hipStream_t s)
+hipError_t launch_conv_output(const Conv2d &cv, const float *yp, float *y, int npqp, int splits,
+                              size_t split_stride, hipStream_t s)
 {
     const size_t total = (size_t)cv.N * cv.K * cv.P * cv.Q;
-    hipLaunchKernelGGL(to_nkpq, dim3(blocks_for(total)), dim3(256), 0, s, yp, y, cv.N, cv.K, cv.P * cv.Q, npqp);
+    hipLaunchKernelGGL(to_nkpq, dim3(blocks_for(total)), dim3(256), 0, s, yp, y, cv.N, cv.K, cv.P * cv.Q, npqp,
+                       splits, split_stride);
     return hipGetLastError();
 }
 

@@ -337,6 +337,7 @@ __device__ __forceinline__ int stage_range(int k0, int K, int t0, int ext, int l
 template <class Op, bool TA, bool TB, bool ACC>
 __global__ __launch_bounds__(256) void mfma_f16_pipe_kernel(RingArgs args)
 {
+    const int bid = dgor_ring_split(args, 2);   // split-K: this workgroup's k-range and tile
     using namespace pipe;
     __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
     const uint32_t ring = lds_address(lds);
@@ -345,7 +346,7 @@ __global__ __launch_bounds__(256) void mfma_f16_pipe_kernel(RingArgs args)
     const uint16_t *__restrict__ B = (const uint16_t *)args.B;
 
     int tm, tn;
-    dgor_tile_of_block(blockIdx.x, args.tiles_m, args.tiles_n, args.group_m, tm, tn);
+    dgor_tile_of_block(bid, args.tiles_m, args.tiles_n, args.group_m, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const int lane = threadIdx.x & 63;
     // wave-uniform, so per-wave offsets and descriptors stay scalar
@@ -558,6 +559,7 @@ constexpr int LDS_BYTES = B_REGION + 4 * B_BYTES;    // 160 KB
 template <class Op, bool TB, bool ACC>
 __global__ __launch_bounds__(256) void mfma_f16_pair_kernel(RingArgs args)
 {
+    const int bid = dgor_ring_split(args, 2);   // split-K: this workgroup's k-range and tile
     using namespace pair16;
     constexpr int BK = pipe::BK;                        // 32 k per stage
     __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
@@ -567,7 +569,7 @@ __global__ __launch_bounds__(256) void mfma_f16_pair_kernel(RingArgs args)
     const uint16_t *__restrict__ B = (const uint16_t *)args.B;
 
     int tm, tn;
-    dgor_tile_of_block(blockIdx.x, args.tiles_m, args.tiles_n, args.group_m, tm, tn);
+    dgor_tile_of_block(bid, args.tiles_m, args.tiles_n, args.group_m, tm, tn);
     const int m0 = tm * 256, n0 = tn * 256;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -820,7 +822,7 @@ hipError_t launch_cfg(const Problem &p, const gemm_plan &plan, hipStream_t s)
 template <class Op, bool TA, bool TB>
 hipError_t launch_ring(const RingArgs &a, hipStream_t s)
 {
-    const dim3 grid(a.tiles_m * a.tiles_n);
+    const dim3 grid(a.tiles_m * a.tiles_n * (a.splits > 1 ? a.splits : 1));
     if constexpr (!TA) {   // k-contiguous A: whole-line A loads
         if (a.accumulate)
             hipLaunchKernelGGL((mfma_f16_pair_kernel<Op, TB, true>), grid, dim3(256), 0, s, a);

@@ -398,6 +398,7 @@ __device__ __forceinline__ int stage_range(int k0, int K, int t0, int ext, int l
 template <bool TA, bool TB, bool ACC>
 __global__ __launch_bounds__(256) void mfma_f32_ring_kernel(RingArgs args)
 {
+    const int bid = dgor_ring_split(args, 4);   // split-K: this workgroup's k-range and tile
     using namespace f32ring;
     __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
     const uint32_t ring = lds_address(lds);
@@ -406,7 +407,7 @@ __global__ __launch_bounds__(256) void mfma_f32_ring_kernel(RingArgs args)
     const float *__restrict__ B = (const float *)args.B;
 
     int tm, tn;
-    dgor_tile_of_block(blockIdx.x, args.tiles_m, args.tiles_n, args.group_m, tm, tn);
+    dgor_tile_of_block(bid, args.tiles_m, args.tiles_n, args.group_m, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const int lane = threadIdx.x & 63;
     // wave-uniform, so per-wave offsets and descriptors stay scalar
@@ -577,7 +578,7 @@ __global__ __launch_bounds__(256) void mfma_f32_ring_kernel(RingArgs args)
 template <bool TA, bool TB>
 hipError_t launch_ring32_t(const RingArgs &a, hipStream_t s)
 {
-    const dim3 grid(a.tiles_m * a.tiles_n);
+    const dim3 grid(a.tiles_m * a.tiles_n * (a.splits > 1 ? a.splits : 1));
     if (a.accumulate)
         hipLaunchKernelGGL((mfma_f32_ring_kernel<TA, TB, true>), grid, dim3(256), 0, s, a);
     else

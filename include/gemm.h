@@ -253,7 +253,10 @@ int gemm_bf16_f32acc_ex(int opA, int opB, int M, int N, int K, float alpha,
  * least the size gemm_conv2d_workspace reports.  It holds the padded weights
  * (K x CRSp), the im2col matrix (CRSp x NPQp) and the GEMM result
  * (K x NPQp, FP32), where CRS = C R S and NPQ = N P Q are rounded up to
- * multiples of 8.  Errors: negative sizes, R, S, strides or dilations below
+ * multiples of 8.  When K >= 192 and CRSp >= 64 the GEMM is split over k into chunks of
+ * a multiple of 64 (at least 64) until its 256 x 256 tiles times the splits
+ * reach 256, and the workspace holds one FP32 result per split; the output
+ * pass adds them in split order.  Errors: negative sizes, R, S, strides or dilations below
  * 1, negative padding, an empty output (P or Q below 1), or sizes whose
  * products overflow int -> GEMM_ERR_INVALID_DIM; NULL params or a NULL
  * tensor with nonzero extent -> GEMM_ERR_NULL_PTR; a workspace that is NULL,

@@ -255,16 +255,37 @@ def test_ex_entry_points_validate_layout_before_touching_a_device():
         assert call(M=0, N=0, K=0, A=None, B=None, C=None) == OK
 
 
+def _conv_splits(K, crsp, npqp):
+    """Split-K count of the convolution GEMM: k-chunks of at least 64 (multiples
+    of 64) until tiles x splits reaches 256, when K >= 192 and CRSp >= 64."""
+    if crsp < 64 or K < 192:
+        return 1
+    tiles = -(-K // 256) * -(-npqp // 256)
+    want = max(1, min(-(-256 // tiles), crsp // 64))
+    chunk = -(-(-(-crsp // want)) // 64) * 64
+    return -(-crsp // chunk)
+
+
 def test_conv2d_workspace_layout_and_validation():
     cp = binding.conv_params
-    # 32 x 256 x 14 x 14, 256 filters 3 x 3, padding 1: CRS 2304, NPQ 6272 (multiples of 8)
-    p = cp(32, 256, 14, 14, 256, 3, 3, (1, 1), (1, 1))
     r = lambda v: -(-v // 256) * 256
-    assert dg.conv2d_workspace(p, 2) == r(256 * 2304 * 2) + r(2304 * 6272 * 2) + r(256 * 6272 * 4)
-    assert dg.conv2d_workspace(p, 4) == r(256 * 2304 * 4) + r(2304 * 6272 * 4) + r(256 * 6272 * 4)
-    # CRS 27 and NPQ 2 * 112 * 112 round up to multiples of 8
+    # 32 x 256 x 14 x 14, 256 filters 3 x 3, padding 1: CRS 2304, NPQ 6272 (multiples
+    # of 8); 25 tiles, so the GEMM is split over k into chunks of 256 (9 partials)
+    p = cp(32, 256, 14, 14, 256, 3, 3, (1, 1), (1, 1))
+    assert _conv_splits(256, 2304, 6272) == 9
+    for eb in (2, 4):
+        assert dg.conv2d_workspace(p, eb) == r(256 * 2304 * eb) + r(2304 * 6272 * eb) + 9 * r(256 * 6272 * 4)
+    # 392 tiles: no split
+    p = cp(32, 64, 56, 56, 64, 3, 3, (1, 1), (1, 1))
+    assert _conv_splits(64, 576, 100352) == 1
+    assert dg.conv2d_workspace(p, 2) == r(64 * 576 * 2) + r(576 * 100352 * 2) + r(64 * 100352 * 4)
+    # CRS 27 rounds up to 32 (below one chunk: the planner's tiles, no split)
     p = cp(2, 3, 224, 224, 64, 3, 3, (2, 2), (1, 1))
     assert dg.conv2d_workspace(p, 2) == r(64 * 32 * 2) + r(32 * 25088 * 2) + r(64 * 25088 * 4)
+    # a 7 x 7 stem with 256 filters: CRS 147 -> 152, 98 tiles -> 2 chunks of 128 and 24
+    p = cp(2, 3, 224, 224, 256, 7, 7, (2, 2), (3, 3))
+    assert _conv_splits(256, 152, 25088) == 2
+    assert dg.conv2d_workspace(p, 2) == r(256 * 152 * 2) + r(152 * 25088 * 2) + 2 * r(256 * 25088 * 4)
     bad = [cp(-1, 1, 4, 4, 1, 1, 1), cp(1, 1, 4, 4, 1, 0, 1), cp(1, 1, 4, 4, 1, 1, 1, (0, 1)),
            cp(1, 1, 4, 4, 1, 1, 1, (1, 1), (-1, 0)), cp(1, 1, 4, 4, 1, 1, 1, dil=(1, 0)),
            cp(1, 1, 2, 2, 1, 5, 1), cp(1, 1, 4, 4, 1, 3, 3, dil=(2, 2))]

@@ -81,6 +81,7 @@ LAYERS = [
     (4, 128, 28, 28, 256, 3, 3, (2, 2), (1, 1), (1, 1)),  # a strided transition
     (16, 256, 14, 14, 256, 1, 1, (1, 1), (0, 0), (1, 1)), # a 1 x 1 projection
     (2, 3, 224, 224, 64, 7, 7, (2, 2), (3, 3), (1, 1)),   # a 7 x 7 stem (CRS 147)
+    (2, 3, 96, 96, 256, 7, 7, (2, 2), (3, 3), (1, 1)),    # split-K with a ragged last chunk (CRSp 152)
 ]
 
 
