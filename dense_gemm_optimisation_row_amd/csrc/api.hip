@@ -382,33 +382,23 @@ int run_ex(In in, int opA, int opB, int M, int N, int K, float alpha, const void
     dgor::RingArgs a{M, N, K, A, lda, B, ldb, C, ldc, (M + 255) / 256, (N + 255) / 256, 4,
                      opA == GEMM_OP_T, opB == GEMM_OP_T, false};
     const int in16 = in == In::F32 ? 0 : (in == In::F16 ? 1 : 2);
-    // C = alpha A B + beta C from the ring kernels' two forms (C = A B and
-    // C += A B) and scaling passes over C:
-    //   beta == 0:  C = A B, then C *= alpha;
-    //   alpha == 1: C *= beta, then C += A B;
-    //   otherwise:  C *= beta / alpha, C += A B, C *= alpha.
-    const float ratio = beta / alpha;
+    // C = alpha A B + beta C from the ring kernels' two forms, C = alpha A B
+    // and C = alpha (C + A B), the second after a pass C *= beta / alpha
+    // when beta != alpha (beta itself when alpha == 1, so the common cases
+    // alpha == 1 with beta in {0, 1} take one kernel and no pass).
+    const float ratio = beta == 0.f ? 0.f : (alpha == 1.f ? beta : beta / alpha);
     const bool ratio_ok = beta == 0.f || alpha == 1.f ||
                           (is_finite(ratio) && fabsf(ratio) >= 0x1p-60f && fabsf(ratio) <= 0x1p60f);
     if (!ring_ok(in, opA, opB, M, N, K, A, lda, B, ldb, ldc) || !ratio_ok)
         return ok(dgor::launch_naive_ex(a, alpha, beta, in16, s)) ? GEMM_OK : GEMM_ERR_LAUNCH;
     auto ring = [&]() { return in == In::F32 ? dgor::launch_ring32(a, s) : dgor::launch_ring16(a, s, in == In::BF16); };
-    if (beta == 0.f) {
-        if (!ok(ring()))
+    a.alpha = alpha;   // applied by the ring kernel as it stores C
+    if (beta != 0.f) {
+        if (ratio != 1.f && !ok(dgor::launch_scale_c(C, M, N, ldc, ratio, s)))
             return GEMM_ERR_LAUNCH;
-        if (alpha != 1.f && !ok(dgor::launch_scale_c(C, M, N, ldc, alpha, s)))
-            return GEMM_ERR_LAUNCH;
-        return GEMM_OK;
+        a.accumulate = true;
     }
-    const float pre = alpha == 1.f ? beta : ratio;
-    if (pre != 1.f && !ok(dgor::launch_scale_c(C, M, N, ldc, pre, s)))
-        return GEMM_ERR_LAUNCH;
-    a.accumulate = true;
-    if (!ok(ring()))
-        return GEMM_ERR_LAUNCH;
-    if (alpha != 1.f && !ok(dgor::launch_scale_c(C, M, N, ldc, alpha, s)))
-        return GEMM_ERR_LAUNCH;
-    return GEMM_OK;
+    return ok(ring()) ? GEMM_OK : GEMM_ERR_LAUNCH;
 }
 
 // ------------------------------------------------------------ convolution --

@@ -26,6 +26,8 @@ struct Problem {
 // (ldb >= K); C is M x N (ldc >= N).  The kernel writes C = op(A) op(B), or
 // with `accumulate` C = C + op(A) op(B) (C read first).  Operands must be
 // 16-byte aligned with every leading dimension a multiple of 16 bytes.
+// The kernel stores alpha times its accumulators, which start at zero or,
+// with accumulate, at C: C = alpha op(A) op(B) or C = alpha (C + op(A) op(B)).
 // Split-K (splits > 1, not with accumulate): the launch has tiles_m *
 // tiles_n * splits workgroups; workgroup b computes tile b % (tiles_m
 // tiles_n) over k-range [s k_chunk, min(K, (s + 1) k_chunk)) with
@@ -43,6 +45,7 @@ struct RingArgs {
     bool trans_a, trans_b, accumulate;
     int splits = 1, k_chunk = 0;
     size_t c_split_stride = 0;
+    float alpha = 1.f;
 };
 
 // Launchers.  Each enqueues exactly the kernel `plan` describes on `stream`
@@ -186,6 +189,26 @@ __device__ __forceinline__ int dgor_ring_split(dgor::RingArgs &a, int elem_bytes
     return bid;
 }
 
+// The ring kernels keep their 256 accumulators per lane in the AGPRs; VALU
+// arithmetic on them written in C++ makes the compiler move the whole array
+// into ordinary registers, which do not fit beside the fragments.  The
+// epilogue reads one accumulator at a time through an explicit AGPR move
+// (and the accumulators are zeroed by AGPR writes, for the same reason).
+// dgor_acc_hazard_wait() goes between the last MFMA and the first read: a
+// 16-pass MFMA's result may be read by v_accvgpr_read only 19 wait states
+// after it issues (CDNA3/CDNA4 instruction set, MFMA dependency rules).
+__device__ __forceinline__ void dgor_acc_hazard_wait()
+{
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
+    __builtin_amdgcn_sched_barrier(0);
+}
+__device__ __forceinline__ float dgor_acc_read(float acc)
+{
+    float v;
+    asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(acc));
+    return v;
+}
 // Workgroup -> output tile, aware of the chip's 8 XCDs.  Consecutive
 // workgroup ids are dealt round-robin to the XCDs, each with its own L2, so
 // id b runs on XCD b % 8.  The ids of one XCD are first renumbered into one

@@ -419,7 +419,7 @@ hipError_t launch_ring(const RingArgs &a, hipStream_t s)
 
 hipError_t launch_ring8(const RingArgs &a, int fmt, hipStream_t s)
 {
-    if (a.accumulate || a.trans_a || a.trans_b || a.splits > 1)
+    if (a.accumulate || a.trans_a || a.trans_b || a.splits > 1 || a.alpha != 1.f)
         return hipErrorInvalidValue;
     switch (fmt) {
     case kFmtE4M3:

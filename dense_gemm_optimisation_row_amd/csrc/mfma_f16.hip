@@ -443,7 +443,7 @@ __global__ __launch_bounds__(256) void mfma_f16_pipe_kernel(RingArgs args)
         so = (uint32_t)(ro * ldc) * 4u;
     };
 
-    // Accumulators start at zero, or at C itself (ACC: C += op(A) op(B)).
+    // Accumulators start at zero, or at C itself (ACC: C = alpha (C + op(A) op(B))).
     floatx4 acc[8][8];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
@@ -456,7 +456,8 @@ __global__ __launch_bounds__(256) void mfma_f16_pipe_kernel(RingArgs args)
                     c_offset(c_col, c_rows_left, i, j, r, vo, so);
                     acc[i][j][r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rc, vo, so, 0));
                 } else {
-                    acc[i][j][r] = 0.f;
+                    // an AGPR write, so the compiler keeps the array in AGPRs
+                    asm("v_accvgpr_write_b32 %0, 0" : "=a"(acc[i][j][r]));
                 }
             }
 
@@ -510,14 +511,16 @@ __global__ __launch_bounds__(256) void mfma_f16_pipe_kernel(RingArgs args)
     // no load may still be writing this workgroup's LDS when it ends
     __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
 
-    // Epilogue: write the accumulators (ACC: they started from C).  No
-    // vector instruction touches them on the way: arithmetic here makes the
-    // compiler hold them in ordinary registers, which do not fit beside the
-    // fragments, so scaling by alpha and beta is left to separate passes.
-    // The offsets are recomputed from opaque copies: shared with the loads
-    // above, they would stay live across the loop and crowd it out.
+    // Epilogue: write alpha times the accumulators (ACC: they started from
+    // C), each moved out of its AGPR, scaled and stored on its own
+    // (arithmetic on the array as a whole would pull it into ordinary
+    // registers, which do not fit beside the fragments; a runtime branch on
+    // alpha == 1 here makes the compiler restructure the whole kernel).  The
+    // offsets are recomputed from opaque copies: shared with the loads above,
+    // they would stay live across the loop and crowd it out.
     int col_e = c_col, rows_e = c_rows_left;
     asm volatile("" : "+v"(col_e), "+v"(rows_e));
+    dgor_acc_hazard_wait();
 #pragma unroll
     for (int j = 0; j < 8; ++j)
 #pragma unroll
@@ -526,7 +529,8 @@ __global__ __launch_bounds__(256) void mfma_f16_pipe_kernel(RingArgs args)
             for (int r = 0; r < 4; ++r) {
                 uint32_t vo, so;
                 c_offset(col_e, rows_e, i, j, r, vo, so);
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][r]), rc, vo, so, 0);
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dgor_acc_read(acc[i][j][r]) * args.alpha), rc,
+                                                      vo, so, 0);
             }
 }
 
@@ -674,7 +678,7 @@ __global__ __launch_bounds__(256) void mfma_f16_pair_kernel(RingArgs args)
         so = (uint32_t)(ro * ldc) * 4u;
     };
 
-    // Accumulators start at zero, or at C itself (ACC: C += A op(B)).
+    // Accumulators start at zero, or at C itself (ACC: C = alpha (C + A op(B))).
     floatx4 acc[8][8];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
@@ -687,7 +691,8 @@ __global__ __launch_bounds__(256) void mfma_f16_pair_kernel(RingArgs args)
                     c_offset(c_col, c_rows_left, i, j, r, vo, so);
                     acc[i][j][r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rc, vo, so, 0));
                 } else {
-                    acc[i][j][r] = 0.f;
+                    // an AGPR write, so the compiler keeps the array in AGPRs
+                    asm("v_accvgpr_write_b32 %0, 0" : "=a"(acc[i][j][r]));
                 }
             }
 
@@ -783,9 +788,10 @@ __global__ __launch_bounds__(256) void mfma_f16_pair_kernel(RingArgs args)
     __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
 
     // Epilogue: as in the four-stage ring (offsets recomputed from opaque
-    // copies; the accumulators stored as they are).
+    // copies; alpha applied one accumulator at a time).
     int col_e = c_col, rows_e = c_rows_left;
     asm volatile("" : "+v"(col_e), "+v"(rows_e));
+    dgor_acc_hazard_wait();
 #pragma unroll
     for (int j = 0; j < 8; ++j)
 #pragma unroll
@@ -794,7 +800,8 @@ __global__ __launch_bounds__(256) void mfma_f16_pair_kernel(RingArgs args)
             for (int r = 0; r < 4; ++r) {
                 uint32_t vo, so;
                 c_offset(col_e, rows_e, i, j, r, vo, so);
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][r]), rc, vo, so, 0);
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dgor_acc_read(acc[i][j][r]) * args.alpha), rc,
+                                                      vo, so, 0);
             }
 }
 

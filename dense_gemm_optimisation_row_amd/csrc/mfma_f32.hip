@@ -494,7 +494,7 @@ __global__ __launch_bounds__(256) void mfma_f32_ring_kernel(RingArgs args)
         so = (uint32_t)(ro * ldc) * 4u;
     };
 
-    // Accumulators start at zero, or at C itself (ACC: C += op(A) op(B)).
+    // Accumulators start at zero, or at C itself (ACC: C = alpha (C + op(A) op(B))).
     floatx16 acc[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -507,7 +507,8 @@ __global__ __launch_bounds__(256) void mfma_f32_ring_kernel(RingArgs args)
                     c_offset(c_col, c_rows_left, i, j, r, vo, so);
                     acc[i][j][r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rc, vo, so, 0));
                 } else {
-                    acc[i][j][r] = 0.f;
+                    // an AGPR write, so the compiler keeps the array in AGPRs
+                    asm("v_accvgpr_write_b32 %0, 0" : "=a"(acc[i][j][r]));
                 }
             }
 
@@ -559,10 +560,11 @@ __global__ __launch_bounds__(256) void mfma_f32_ring_kernel(RingArgs args)
     // no load may still be writing this workgroup's LDS when it ends
     __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
 
-    // Epilogue: write the accumulators, unchanged (see the 16-bit ring
-    // kernel); offsets are recomputed from opaque copies.
+    // Epilogue: write alpha times the accumulators, one at a time (see the
+    // 16-bit ring kernel); offsets are recomputed from opaque copies.
     int col_e = c_col, rows_e = c_rows_left;
     asm volatile("" : "+v"(col_e), "+v"(rows_e));
+    dgor_acc_hazard_wait();
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -571,7 +573,8 @@ __global__ __launch_bounds__(256) void mfma_f32_ring_kernel(RingArgs args)
             for (int r = 0; r < 16; ++r) {
                 uint32_t vo, so;
                 c_offset(col_e, rows_e, i, j, r, vo, so);
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][r]), rc, vo, so, 0);
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dgor_acc_read(acc[i][j][r]) * args.alpha), rc,
+                                                      vo, so, 0);
             }
 }
 
