@@ -154,6 +154,19 @@ int plan_f32(int variant, int M, int N, int K, const void *A, const void *B, con
             p->vector_c = 0;
             break;
         }
+        dgor::F32NarrowPlan nw;
+        if (dgor::f32_narrow_plan(M, N, K, nw)) {
+            p->tile_m = 16 * nw.rb;
+            p->tile_n = 16 * nw.nb;
+            p->tile_k = 4 * nw.kq_len;
+            p->threads = 256 * nw.rb;
+            p->lds_stages = 1;
+            p->lds_bytes = nw.b_floats * 4;
+            p->tile_bytes = (p->tile_m * p->tile_k + p->tile_k * p->tile_n) * 4;
+            p->outputs_per_thread = p->tile_m * p->tile_n / p->threads;
+            p->vector_c = 0;
+            break;
+        }
         const MfmaConfig &c = dgor::kF32Configs[pick_config(dgor::kF32Configs, M, N, true)];
         p->tile_m = c.bm;
         p->tile_n = c.bn;
@@ -162,11 +175,15 @@ int plan_f32(int variant, int M, int N, int K, const void *A, const void *B, con
         if (dgor::direct_lds_applies(c.bm, dgor::kF32Configs[0].bm, p->vector_a, p->vector_b, N, K)) {
             p->lds_stages = dgor::kF32DirectStages;
             p->lds_bytes = dgor::kF32DirectLdsBytes;
+        } else if (dgor::f32_small_ring_applies(c.bm, c.bn, N, K, p->vector_a, p->vector_b)) {
+            p->tile_k = dgor::kF32SmallDepth;
+            p->lds_stages = dgor::kF32SmallStages;
+            p->lds_bytes = dgor::kF32SmallLdsBytes;
         } else {
             p->lds_stages = 2;
             p->lds_bytes = dgor::mfma_f32_lds_bytes(c);
         }
-        p->tile_bytes = (c.bm * c.bk + c.bk * c.bn) * 4;
+        p->tile_bytes = (c.bm * p->tile_k + p->tile_k * c.bn) * 4;
         p->outputs_per_thread = c.bm * c.bn / p->threads;
         p->vector_c = 0;
         break;

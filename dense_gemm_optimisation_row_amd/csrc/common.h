@@ -151,6 +151,39 @@ inline bool direct_lds_applies(int tile_m, int top_tile, bool vec_a, bool vec_b,
     return tile_m == top_tile && vec_a && vec_b && K < (1 << 22) && N < (1 << 22);
 }
 
+// FP32 problems that take the 64 x 64 tile with both operands in 128-bit
+// loads run a ring of kF32SmallStages LDS stages kF32SmallDepth deep, loaded
+// straight from global memory; lane byte offsets (k + depth) N 4 of B must
+// stay below 2^31.
+constexpr int kF32SmallDepth = 64;
+constexpr int kF32SmallStages = 4;
+constexpr int kF32SmallLdsBytes = kF32SmallStages * (64 * kF32SmallDepth + kF32SmallDepth * 64) * 4;
+inline bool f32_small_ring_applies(int tile_m, int tile_n, int N, int K, bool vec_a, bool vec_b)
+{
+    return tile_m == 64 && tile_n == 64 && vec_a && vec_b && K < (1 << 22) &&
+           (long long)(K + kF32SmallDepth) * N < (1LL << 29);
+}
+
+// Tall, narrow FP32 problems (1 <= N <= 64, K <= kF32NarrowMaxK, any
+// alignment): workgroups of 16 rb rows (4 rb wavefronts), nb = ceil(N / 16)
+// column blocks of 16, four wavefronts per row block each taking kq_len of K
+// (a multiple of 16), and B's first b_floats floats (4 kq_len rows plus a
+// 64-float guard, rounded to whole 1 KB loads) in LDS.  Two row blocks per
+// workgroup when one would need more than 256 workgroups.
+constexpr int kF32NarrowMaxK = 1024;
+constexpr int kF32NarrowLdsFloats = 40960;   // 160 KB
+struct F32NarrowPlan { int nb, rb, kq_len, b_floats; };
+inline bool f32_narrow_plan(int M, int N, int K, F32NarrowPlan &n)
+{
+    if (N < 1 || N > 64 || K < 1 || K > kF32NarrowMaxK || (long long)M * K * 4 >= (1LL << 31))
+        return false;
+    n.nb = (N + 15) / 16;
+    n.rb = (M + 15) / 16 > 256 ? 2 : 1;
+    n.kq_len = ((K + 3) / 4 + 15) / 16 * 16;
+    n.b_floats = (4 * n.kq_len * N + 64 + 255) / 256 * 256;
+    return n.b_floats <= kF32NarrowLdsFloats;
+}
+
 // FP32 problems with both operands in 128-bit loads and at least one
 // 256 x 256 tile per compute unit take a 256 x 256 x 16 tile fed through a
 // ring of four LDS stages (lane byte offsets inside a tile stay below 2^31).

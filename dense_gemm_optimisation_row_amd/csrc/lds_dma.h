@@ -56,6 +56,18 @@ __device__ __forceinline__ void load_to_lds(intx4 rsrc, uint32_t lds, uint32_t v
                  : "memory");
 }
 
+// The same with 4 bytes per lane: lane p reads the dword at byte offset voff
+// and writes it to LDS address lds + 4 p (a 256-byte run per load).
+__device__ __forceinline__ void load_dword_to_lds(intx4 rsrc, uint32_t lds, uint32_t voff)
+{
+    asm volatile("s_mov_b32 m0, %0\n\t"
+                 "s_nop 0\n\t"
+                 "buffer_load_dword %1, %2, 0 offen lds"
+                 :
+                 : "s"(lds), "v"(voff), "s"(rsrc)
+                 : "memory");
+}
+
 // s_waitcnt immediate (gfx9 encoding) for vmcnt(n) alone: vmcnt bits 3:0 and
 // 15:14, expcnt (6:4) and lgkmcnt (11:8) left at their maximum.
 constexpr int wait_vmcnt(int n)

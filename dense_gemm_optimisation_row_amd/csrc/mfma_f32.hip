@@ -515,18 +515,22 @@ __global__ __launch_bounds__(256) void mfma_f32_ring_kernel(RingArgs args)
     // One stage: the 128 MFMAs of stage t from (ca, cb); the reads of stage
     // t + 1 into (na, nb), one after each of the first READS MFMAs (at most
     // 64); the 8 loads of stage t + 3, one after every eighth MFMA from the
-    // 64th.
+    // 64th.  The loads' descriptors are set up behind the first MFMA: with
+    // one wavefront per SIMD, scalar work between the barrier and the first
+    // MFMA leaves the matrix core idle.
     const int steps = (K + BK - 1) / BK;
     auto stage = [&](int t, floatx4 *ca, floatx4 *cb, floatx4 *na, floatx4 *nb) {
         __builtin_amdgcn_s_waitcnt(wait_vmcnt(LOADS_PER_STAGE));
         __builtin_amdgcn_s_barrier();
-        const StageLoads L = prep(t + 3);
         __builtin_amdgcn_sched_barrier(0);
+        StageLoads L;
 #pragma unroll
         for (int m = 0; m < 128; ++m) {
             const int q = m >> 6, jp = (m >> 4) & 3, i = (m >> 2) & 3, j = m & 3;
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(ca[4 * q + i][jp], cb[4 * q + j][jp], acc[i][j], 0,
                                                               0, 0);
+            if (m == 1)
+                L = prep(t + 3);
             if (m < READS)
                 fread(t + 1, m, na, nb);
             if (m >= 64 && (m - 64) % 8 == 0)
@@ -589,6 +593,328 @@ hipError_t launch_ring32_t(const RingArgs &a, hipStream_t s)
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Mid-size FP32 problems (16-byte aligned operands, too few 256 x 256 tiles
+// to fill the chip, so 64 x 64 tiles): one workgroup per tile computes only
+// about 260 K flops per 16-deep k-step, far less than one memory latency
+// takes, so k-stages come through a deep ring of LDS buffers, NBUF of BK k,
+// loaded straight from global memory NBUF - 1 stages ahead ("Lesson 8: how a
+// GPU does matrix multiply", sections 24 and 25 on overlapping loads with
+// compute, taken several stages deep).  Four wavefronts of 32 x 32, each 2 x 2
+// blocks of v_mfma_f32_16x16x4_f32 (lane l supplies A[l % 16][l / 16] and
+// B[l / 16][l % 16] and holds C[4 (l / 16) + r][l % 16], r = 0..3); for the
+// four instructions e = 0..3 of a 16-deep k-slice q, lane l takes
+// k = 16 q + 4 (l / 16) + e, so its A values are one 128-bit read and its B
+// values four 32-bit reads of one column.
+//   A stage: 64 rows of BK floats (U = BK / 4 units of 16 bytes), unit u of
+//     row r at U r + (u ^ fa(r)), fa(r) = (r U / 16) mod U: the 16 rows one
+//     128-bit read cycle touches land on 16 distinct groups of 4 banks.
+//   B stage: BK rows of 64 floats, unit u of row k at 16 k + (u ^ fb(k)),
+//     fb(k) = 4 ((k / 4) mod 4): the four rows k, k + 4, k + 8, k + 12 that
+//     one 32-bit read touches fall on four distinct quarters of the banks.
+// Edges and the k tail are zero-filled through out-of-range lane offsets
+// (K and N are multiples of 4, so a 16-byte unit is wholly in or out).
+namespace f32small {
+__host__ __device__ constexpr int fa(int r, int U) { return (r * U / 16) & (U - 1); }
+__host__ __device__ constexpr int fb(int k) { return 4 * ((k >> 2) & 3); }
+}  // namespace f32small
+
+template <int BK, int NBUF>
+__global__ __launch_bounds__(256) void mfma_f32_small_ring_kernel(int M, int N, int K,
+                                                                  const float *__restrict__ A,
+                                                                  const float *__restrict__ B,
+                                                                  float *__restrict__ C, int tiles_m,
+                                                                  int tiles_n, int group_m)
+{
+    using namespace f32small;
+    constexpr int BM = 64, BN = 64, U = BK / 4;
+    constexpr int A_BYTES = BM * BK * 4, STAGE = A_BYTES + BK * BN * 4;
+    constexpr int LA = BK / 16, LB = BK / 16, LPS = LA + LB;   // loads per wavefront and stage
+    constexpr int SLICES = BK / 16, READS = 10 * SLICES, MFMAS = 16 * SLICES;
+    static_assert(U == 8 || U == 16, "A rows of 8 or 16 units");
+    static_assert((NBUF & (NBUF - 1)) == 0 && NBUF >= 4, "ring of a power of two, at least 4");
+    static_assert(READS <= MFMAS, "one read after each of the first MFMAs");
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[NBUF * STAGE];
+    const uint32_t lds0 = lds_address(lds);
+
+    int tm, tn;
+    dgor_tile_of_block(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int wr = (wave >> 1) * 32, wc = (wave & 1) * 32;
+    constexpr uint32_t OOB = 0x80000000u;
+
+    // ---- loader: wave w issues A loads w LA .. w LA + LA - 1 and B loads
+    // w LB .. w LB + LB - 1 of each stage (1 KB each).  A load j covers rows
+    // j 64 / U ..; lane p takes physical unit p % U of row j 64 / U + p / U.
+    // B load j covers k-rows 4 j .. 4 j + 3; lane p takes physical unit p % 16
+    // of k-row 4 j + p / 16.
+    const intx4 ra = rsrc_words(A + (size_t)m0 * K, 0x7fffffff);
+    const intx4 rb = rsrc_words(B + n0, 0x7fffffff);
+    uint32_t a_row[LA], b_row[LB];   // byte offsets of the lane's row start
+    int a_k[LA], b_k[LB];            // the lane's k within a stage (A: of its unit)
+    bool a_ok[LA], b_ok[LB];         // row inside A, column inside B
+#pragma unroll
+    for (int i = 0; i < LA; ++i) {
+        const int j = wave * LA + i, r = j * (64 / U) + lane / U;
+        const int u = (lane % U) ^ fa(r, U);
+        a_row[i] = (uint32_t)(r * K + 4 * u) * 4u;
+        a_k[i] = 4 * u;
+        a_ok[i] = m0 + r < M;
+    }
+#pragma unroll
+    for (int i = 0; i < LB; ++i) {
+        const int j = wave * LB + i, k = 4 * j + lane / 16;
+        const int u = (lane % 16) ^ fb(k);
+        b_row[i] = (uint32_t)(k * N + 4 * u) * 4u;
+        b_k[i] = k;
+        b_ok[i] = n0 + 4 * u < N;
+    }
+    auto load = [&](int st, int x) {   // load x (0 .. LPS - 1) of stage st
+        const int k0 = st * BK;
+        const uint32_t buf = lds0 + (uint32_t)((st & (NBUF - 1)) * STAGE);
+        if (x < LA) {
+            const bool ok = a_ok[x] && k0 + a_k[x] < K;
+            load_to_lds(ra, buf + (uint32_t)((wave * LA + x) * 1024), ok ? a_row[x] + (uint32_t)k0 * 4u : OOB);
+        } else {
+            const int i = x - LA;
+            const bool ok = b_ok[i] && k0 + b_k[i] < K;
+            load_to_lds(rb, buf + (uint32_t)(A_BYTES + (wave * LB + i) * 1024),
+                        ok ? b_row[i] + (uint32_t)k0 * (uint32_t)N * 4u : OOB);
+        }
+    };
+
+    // ---- fragment reads (read rd of a stage: slice q = rd / 10, then A
+    // block 0, A block 1, B block 0 rows e = 0..3, B block 1 rows e = 0..3).
+    // A block x, slice q: logical unit 4 q + h of row wr + 16 x + l16.  B block
+    // b, slice q, row e: k-row 16 q + 4 h + e (so fb = 4 h), column
+    // wc + 16 b + l16.
+    const int l16 = lane & 15, h = lane >> 4;
+    uint32_t a_off[2 * SLICES], b_lane[2];
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+        const int r = wr + 16 * x + l16;
+#pragma unroll
+        for (int q = 0; q < SLICES; ++q)
+            a_off[2 * q + x] = (uint32_t)(r * U * 16 + (((4 * q + h) ^ fa(r, U)) * 16));
+        const int col = wc + 16 * x + l16;
+        b_lane[x] = (uint32_t)(A_BYTES + (4 * h) * 256 + (((col >> 2) ^ (4 * h)) * 16) + (col & 3) * 4);
+    }
+    auto fread = [&](int st, int rd, floatx4 *fa_, floatx4 *fb_) {
+        const uint8_t *buf = lds + (st & (NBUF - 1)) * STAGE;
+        const int q = rd / 10, x = rd % 10;
+        if (x < 2) {
+            fa_[2 * q + x] = *reinterpret_cast<const floatx4 *>(buf + a_off[2 * q + x]);
+        } else {
+            const int b = (x - 2) >> 2, e = (x - 2) & 3;
+            fb_[2 * q + b][e] = *reinterpret_cast<const float *>(buf + b_lane[b] + (16 * q + e) * 256);
+        }
+    };
+
+    floatx4 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    // One stage t: its MFMAS matrix instructions from (ca, cb); the READS
+    // reads of stage t + 1 into (na, nb), one after each of the first ones;
+    // the LPS loads of stage t + NBUF - 1 spread over the stage.  Before it,
+    // this wavefront's loads of stage t + 1 have landed (those of the NBUF - 3
+    // later stages may fly) and the workgroup meets at the barrier, so every
+    // wavefront's part of stage t + 1 is in LDS and nobody still reads the
+    // buffer the new loads refill (stage t - 1's, read during stage t - 2).
+    const int steps = (K + BK - 1) / BK;
+    auto stage = [&](int t, floatx4 *ca, floatx4 *cb, floatx4 *na, floatx4 *nb) {
+        __builtin_amdgcn_s_waitcnt(wait_vmcnt((NBUF - 3) * LPS));
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int m = 0; m < MFMAS; ++m) {
+            const int q = m >> 4, e = (m >> 2) & 3, i = (m >> 1) & 1, j = m & 1;
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(ca[2 * q + i][e], cb[2 * q + j][e], acc[i][j], 0, 0,
+                                                             0);
+            if (m < READS)
+                fread(t + 1, m, na, nb);
+            if (m % (MFMAS / LPS) == MFMAS / LPS / 2)
+                load(t + NBUF - 1, m / (MFMAS / LPS));
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // prologue: stages 0 .. NBUF - 2 in flight; once stage 0 has landed, its reads
+    floatx4 fa0[2 * SLICES], fb0[2 * SLICES], fa1[2 * SLICES], fb1[2 * SLICES];
+    for (int st = 0; st < NBUF - 1; ++st)
+#pragma unroll
+        for (int x = 0; x < LPS; ++x)
+            load(st, x);
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt((NBUF - 2) * LPS));
+    __builtin_amdgcn_s_barrier();
+#pragma unroll
+    for (int r = 0; r < READS; ++r)
+        fread(0, r, fa0, fb0);
+
+    for (int t = 0; t < steps; t += 2) {
+        stage(t, fa0, fb0, fa1, fb1);
+        if (t + 1 < steps)
+            stage(t + 1, fa1, fb1, fa0, fb0);
+    }
+    // no load may still be writing this workgroup's LDS when it ends
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+
+    const __amdgpu_buffer_rsrc_t rc =
+        make_rsrc(C + (size_t)m0 * N + n0, ((long long)(M - m0 - 1) * N + N - n0) * 4);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = wr + 16 * i + 4 * h + r, col = wc + 16 * j + l16;
+                const uint32_t vo = (m0 + row < M && n0 + col < N) ? (uint32_t)(row * N + col) * 4u : OOB;
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][r]), rc, vo, 0, 0);
+            }
+}
+
+// ---------------------------------------------------------------------------
+// Tall, narrow FP32 problems (N <= 64, K <= 1024, any alignment).  Reading A
+// once is most of their time (B and C are small), so every wavefront issues
+// all of its A loads at once instead of meeting memory latency stage by
+// stage.  A workgroup takes 16 RB rows with 4 RB wavefronts: wavefront w
+// takes row block w / 4 and k in [q kq_len, (q + 1) kq_len), q = w % 4
+// (kq_len a multiple of 16), with the first 4 kq_len rows of B (zeros past K,
+// then a 64-float guard) copied whole into LDS.  The four partial sums of a
+// row block are added in LDS in order of q.  The matrix instruction is
+// v_mfma_f32_16x16x4_f32 with the k assignment of the 64 x 64 ring kernel
+// (lane l: A[l % 16][k], B[k][l % 16], k = 16 s + 4 (l / 16) + e for the
+// instructions e = 0..3 of slice s), so a lane's A values of a slice are four
+// consecutive floats of its row: one 16-byte load (rows need only 4-byte
+// alignment), or four 4-byte loads for the one unit that runs past K.
+// Column blocks past N read whatever follows in LDS and are not stored.
+template <int NB, int RB>
+__global__ __launch_bounds__(256 * RB) void mfma_f32_narrow_kernel(int M, int N, int K, int kq_len, int b_floats,
+                                                                   int b_vec, const float *__restrict__ A,
+                                                                   const float *__restrict__ B,
+                                                                   float *__restrict__ C)
+{
+    constexpr int QMAX = kF32NarrowMaxK / 64;   // 16-deep slices per wavefront
+    __shared__ __attribute__((aligned(1024))) float lds[kF32NarrowLdsFloats];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int rb = wave >> 2, q = wave & 3;
+    const int r16 = lane & 15, h = lane >> 4;
+    const int m0 = blockIdx.x * 16 * RB;
+    constexpr uint32_t OOB = 0x80000000u;
+
+    // B's first b_floats floats (zeros past K N) into LDS: 1 KB a load when B
+    // is 16-byte aligned and K N a multiple of 4, else 256 bytes
+    {
+        const intx4 rsb = rsrc_words(B, (long long)K * N * 4);
+        const uint32_t base = lds_address(lds);
+        if (b_vec) {
+            for (int i = wave; i < b_floats / 256; i += 4 * RB)
+                load_to_lds(rsb, base + (uint32_t)(i * 1024), (uint32_t)(i * 1024 + lane * 16));
+        } else {
+            for (int i = wave; i < b_floats / 64; i += 4 * RB)
+                load_dword_to_lds(rsb, base + (uint32_t)(i * 256), (uint32_t)(i * 256 + lane * 4));
+        }
+    }
+    // A[m0 + 16 rb + r16][k0 + 16 s + 4 h + e], zero outside A or past this
+    // wavefront's slices
+    const int k0 = q * kq_len, slices = kq_len / 16;
+    const int row = m0 + 16 * rb + r16;
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, (long long)M * K * 4);
+    floatx4 a[QMAX];
+#pragma unroll
+    for (int s = 0; s < QMAX; ++s) {
+        const int k = k0 + 16 * s + 4 * h;
+        const bool live = s < slices && row < M;
+        const uint32_t off = (uint32_t)(row * K + k) * 4u;
+        a[s] = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(ra, live && k + 4 <= K ? off : OOB,
+                                                                                 0, 0));
+        if (live && k < K && k + 4 > K) {   // the unit that runs past K
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                a[s][e] = __uint_as_float(
+                    __builtin_amdgcn_raw_buffer_load_b32(ra, k + e < K ? off + 4u * e : OOB, 0, 0));
+        }
+    }
+    // all of them issued here, not moved next to their uses
+#pragma unroll
+    for (int s = 0; s < QMAX; ++s)
+        asm volatile("" : "+v"(a[s]));
+    // B's copy is not tracked by the compiler's counters
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+    __builtin_amdgcn_s_barrier();
+
+    floatx4 acc[NB];
+#pragma unroll
+    for (int c = 0; c < NB; ++c)
+        acc[c] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < QMAX; ++s) {
+        if (s < slices) {   // wave-uniform; rows past 4 kq_len are not in LDS
+            float bv[4][NB];   // the slice's B values, read before its MFMAs
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int c = 0; c < NB; ++c)
+                    bv[e][c] = lds[(k0 + 16 * s + 4 * h + e) * N + 16 * c + r16];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int c = 0; c < NB; ++c)
+                    acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s][e], bv[e][c], acc[c], 0, 0, 0);
+        }
+    }
+
+    // partial sums: wavefront w's block c at floats (w NB + c) 256; the four
+    // of an output block are added in order of q and stored (lane l holds
+    // rows 4 (l / 16) + r, column l % 16 of a 16 x 16 block)
+    __syncthreads();   // B is no longer read
+#pragma unroll
+    for (int c = 0; c < NB; ++c)
+        *reinterpret_cast<floatx4 *>(lds + (wave * NB + c) * 256 + lane * 4) = acc[c];
+    __syncthreads();
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(C, (long long)M * N * 4);
+    // output block p = (row block p / NB, column block p % NB); wavefront w
+    // takes p = w, w + 4 RB, ...
+#pragma unroll
+    for (int i = 0; i < (RB * NB + 4 * RB - 1) / (4 * RB); ++i) {
+        const int p = wave + 4 * RB * i;
+        if (p >= RB * NB)
+            break;
+        const int b = p / NB, c = p % NB, col = 16 * c + r16;
+        floatx4 v = *reinterpret_cast<const floatx4 *>(lds + ((4 * b) * NB + c) * 256 + lane * 4);
+#pragma unroll
+        for (int w = 1; w < 4; ++w)
+            v += *reinterpret_cast<const floatx4 *>(lds + ((4 * b + w) * NB + c) * 256 + lane * 4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int orow = m0 + 16 * b + 4 * h + r;
+            const uint32_t vo = (orow < M && col < N) ? (uint32_t)(orow * N + col) * 4u : OOB;
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[r]), rc, vo, 0, 0);
+        }
+    }
+}
+
+template <int NB>
+void launch_narrow_nb(const Problem &p, const F32NarrowPlan &n, hipStream_t s)
+{
+    const dim3 grid((unsigned)((p.M + 16 * n.rb - 1) / (16 * n.rb)));
+    // 16-byte copies of B only when its extent is whole 16-byte units: a
+    // copy that ran past the end would be partly out of range
+    const int b_vec = n.b_floats % 256 == 0 && ((uintptr_t)p.B & 15) == 0 && (long long)p.K * p.N % 4 == 0;
+    if (n.rb == 2)
+        hipLaunchKernelGGL((mfma_f32_narrow_kernel<NB, 2>), grid, dim3(512), 0, s, p.M, p.N, p.K, n.kq_len,
+                           n.b_floats, b_vec, (const float *)p.A, (const float *)p.B, p.C);
+    else
+        hipLaunchKernelGGL((mfma_f32_narrow_kernel<NB, 1>), grid, dim3(256), 0, s, p.M, p.N, p.K, n.kq_len,
+                           n.b_floats, b_vec, (const float *)p.A, (const float *)p.B, p.C);
+}
+
 template <int BM, int BN, int BK, int WM, int WN>
 hipError_t launch_cfg(const Problem &p, const gemm_plan &plan, hipStream_t s)
 {
@@ -628,8 +954,25 @@ hipError_t launch_mfma_f32(const Problem &p, const gemm_plan &plan, hipStream_t 
         }
         return launch_cfg<128, 128, 16, 2, 2>(p, plan, s);
     }
-    if (plan.tile_m == 64 && plan.tile_n == 64)
+    if (plan.tile_m == 64 && plan.tile_n == 64) {
+        if (f32_small_ring_applies(64, 64, p.N, p.K, p.vec_a, p.vec_b)) {
+            hipLaunchKernelGGL((mfma_f32_small_ring_kernel<kF32SmallDepth, kF32SmallStages>),
+                               dim3(plan.grid_x * plan.grid_y), dim3(256), 0, s, p.M, p.N, p.K,
+                               (const float *)p.A, (const float *)p.B, p.C, plan.grid_y, plan.grid_x, 8);
+            return hipGetLastError();
+        }
         return launch_cfg<64, 64, 16, 2, 2>(p, plan, s);
+    }
+    F32NarrowPlan n;
+    if (f32_narrow_plan(p.M, p.N, p.K, n) && plan.tile_m == 16 * n.rb && plan.tile_n == 16 * n.nb) {
+        switch (n.nb) {
+        case 1: launch_narrow_nb<1>(p, n, s); break;
+        case 2: launch_narrow_nb<2>(p, n, s); break;
+        case 3: launch_narrow_nb<3>(p, n, s); break;
+        default: launch_narrow_nb<4>(p, n, s); break;
+        }
+        return hipGetLastError();
+    }
     if (plan.tile_m == 32 && plan.tile_n == 64)
         return launch_cfg<32, 64, 16, 1, 2>(p, plan, s);
     return hipErrorInvalidValue;

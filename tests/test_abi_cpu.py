@@ -127,8 +127,16 @@ def test_auto_picks_matrix_cores_and_tile_by_size():
     assert odd["grid_x"] * odd["grid_y"] >= 512
     small = dg.plan(False, 1024, 1024, 1024)
     assert small["variant"] == dg.R6_MFMA_F32 and small["grid_x"] * small["grid_y"] >= 256
+    # tall and narrow (N <= 64, K <= 1024): 16-row blocks, 16-column blocks
+    # up to N, two row blocks per workgroup past 256 blocks; B in LDS
     skinny = dg.plan(False, 4097, 33, 777)
-    assert skinny["tile_n"] == 64 and skinny["grid_x"] == 1
+    assert (skinny["tile_m"], skinny["tile_n"], skinny["grid_x"], skinny["grid_y"]) == (32, 48, 1, 129)
+    assert skinny["tile_k"] == 4 * 208 and skinny["lds_bytes"] == 4 * ((4 * 208 * 33 + 64 + 255) // 256 * 256)
+    assert skinny["threads"] == 512
+    assert (dg.plan(False, 4000, 64, 512)["tile_m"], dg.plan(False, 4000, 64, 512)["tile_n"]) == (16, 64)
+    # B too large for LDS, or K past 1024: the 32 x 64 tile
+    assert (dg.plan(False, 4097, 64, 1024)["tile_m"], dg.plan(False, 4097, 64, 1024)["tile_n"]) == (32, 64)
+    assert (dg.plan(False, 4097, 16, 2048)["tile_m"], dg.plan(False, 4097, 16, 2048)["tile_n"]) == (32, 64)
     h = dg.plan(True, 8192, 8192, 8192)
     assert h["variant"] == dg.R7_MFMA_F16 and (h["tile_m"], h["tile_n"]) == (256, 256)
 

@@ -104,7 +104,8 @@ CONFIG_SHAPES = [
     (False, (4000, 4100, 200), (256, 256)),   # FP32 256 x 256 ring, ragged M/N/K
     (False, (2049, 4100, 100), (128, 128)),   # FP32 128 x 128 tiles
     (False, (1000, 1000, 1000), (64, 64)),    # FP32 64 x 64 tiles
-    (False, (4097, 33, 777), (32, 64)),       # FP32 narrow tiles
+    (False, (4097, 33, 777), (32, 48)),       # FP32 tall, narrow: B in LDS, 2 row blocks
+    (False, (4097, 64, 1024), (32, 64)),      # FP32 narrow tiles (B too large for LDS)
     (True, (8191, 4097, 72), (256, 256)),     # FP16 256 x 256 tiles, unaligned rows
     (True, (8000, 4104, 200), (256, 256)),    # FP16 256 x 256 tiles, 128-bit rows, ragged M/N/K
     (True, (2047, 4095, 200), (128, 128)),    # FP16 128 x 128 tiles
@@ -161,6 +162,57 @@ def test_f32_large_tile_stage_counts(K):
     assert_bits_equal(run(False, dg.AUTO, A, B), oracle.gemm_f32(A, B), f"ints K={K}")
     A, B = floats(M, N, K, 72 + K)
     assert_within(run(False, dg.AUTO, A, B), oracle.gemm_f32(A, B), tol_f32(K), f"floats K={K}")
+
+
+# The 64 x 64 FP32 tile with 128-bit operands runs a ring of four 64-deep
+# stages, three loaded ahead: these K give 1, 1, 2, 2, 3, 4, 4, 5 and 6
+# stages, full and ragged; the shapes have ragged M and N (1000 = 15 x 64 +
+# 40), fewer rows than one tile, and a single row.
+@pytest.mark.parametrize("shape", [(1000, 1000, K) for K in (4, 64, 68, 128, 192, 196, 256, 260, 324)]
+                         + [(40, 1000, 200), (1, 1024, 128), (1000, 8, 64)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_f32_mid_tile_stage_counts(shape):
+    M, N, K = shape
+    p = dg.plan(False, M, N, K)
+    if N > 64:
+        assert (p["tile_m"], p["tile_n"], p["tile_k"], p["lds_stages"]) == (64, 64, 64, 4)
+    say("f32 mid tile stages", shape)
+    A, B = ints(M, N, K, 81 + K)
+    assert_bits_equal(run(False, dg.AUTO, A, B), oracle.gemm_f32(A, B), f"ints {shape}")
+    A, B = floats(M, N, K, 82 + K)
+    assert_within(run(False, dg.AUTO, A, B), oracle.gemm_f32(A, B), tol_f32(K), f"floats {shape}")
+
+
+# Tall, narrow FP32 problems (N <= 64, K <= 1024) take a kernel that holds B
+# in LDS and splits K four ways: N across 1..4 column blocks (ragged), K
+# from 1 to 1024 (the split lands mid-slice, or leaves wavefronts empty),
+# one and two row blocks per workgroup, fewer rows than a block, and base
+# pointers one float off 16-byte alignment (the kernel reads 4 bytes a lane).
+NARROW_SHAPES = [(4100, 33, 777), (4097, 1, 1), (300, 16, 17), (257, 17, 3), (5000, 48, 64),
+                 (1000, 63, 600), (4097, 64, 576), (9, 40, 900), (16, 15, 5), (4096, 2, 1024)]
+
+
+@pytest.mark.parametrize("shape", NARROW_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_f32_tall_narrow(shape):
+    M, N, K = shape
+    p = dg.plan(False, M, N, K)
+    assert p["tile_n"] == 16 * -(-N // 16) and p["tile_m"] in (16, 32) and p["grid_x"] == 1
+    assert p["lds_stages"] == 1 and p["tile_k"] % 64 == 0 and p["tile_k"] >= K
+    say("f32 tall narrow", shape)
+    A, B = ints(M, N, K, 91)
+    assert_bits_equal(run(False, dg.AUTO, A, B), oracle.gemm_f32(A, B), f"ints {shape}")
+    A, B = floats(M, N, K, 92)
+    ref = oracle.gemm_f32(A, B)
+    assert_within(run(False, dg.AUTO, A, B), ref, tol_f32(K), f"floats {shape}")
+    # the same through base pointers 4 bytes past 16-byte alignment
+    import torch
+    a = torch.from_numpy(np.concatenate([np.zeros(1, np.float32), A.ravel()])).to("cuda")
+    b = torch.from_numpy(np.concatenate([np.zeros(1, np.float32), B.ravel()])).to("cuda")
+    c = torch.empty(M * N + 1, dtype=torch.float32, device="cuda")
+    assert binding.raw_gemm("f32", None, M, N, K, a.data_ptr() + 4, b.data_ptr() + 4, c.data_ptr() + 4,
+                            None) == binding.GEMM_OK
+    torch.cuda.synchronize()
+    assert_within(c.cpu().numpy()[1:].reshape(M, N), ref, tol_f32(K), f"misaligned {shape}")
 
 
 # ------------------------------------------------------ full-size workloads --
