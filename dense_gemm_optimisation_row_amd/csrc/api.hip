@@ -176,6 +176,7 @@ int plan_f32(int variant, int M, int N, int K, const void *A, const void *B, con
             p->lds_stages = dgor::kF32DirectStages;
             p->lds_bytes = dgor::kF32DirectLdsBytes;
         } else if (dgor::f32_small_ring_applies(c.bm, c.bn, N, K, p->vector_a, p->vector_b)) {
+            p->threads = 128 * dgor::kF32SmallWavesN;
             p->tile_k = dgor::kF32SmallDepth;
             p->lds_stages = dgor::kF32SmallStages;
             p->lds_bytes = dgor::kF32SmallLdsBytes;

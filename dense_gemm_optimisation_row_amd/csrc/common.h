@@ -157,6 +157,7 @@ inline bool direct_lds_applies(int tile_m, int top_tile, bool vec_a, bool vec_b,
 // stay below 2^31.
 constexpr int kF32SmallDepth = 64;
 constexpr int kF32SmallStages = 4;
+constexpr int kF32SmallWavesN = 4;   // wavefronts along N (2 along M): 32 x 64 / kF32SmallWavesN each
 constexpr int kF32SmallLdsBytes = kF32SmallStages * (64 * kF32SmallDepth + kF32SmallDepth * 64) * 4;
 inline bool f32_small_ring_applies(int tile_m, int tile_n, int N, int K, bool vec_a, bool vec_b)
 {

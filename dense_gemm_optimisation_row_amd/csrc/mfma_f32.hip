@@ -600,8 +600,8 @@ hipError_t launch_ring32_t(const RingArgs &a, hipStream_t s)
 // takes, so k-stages come through a deep ring of LDS buffers, NBUF of BK k,
 // loaded straight from global memory NBUF - 1 stages ahead ("Lesson 8: how a
 // GPU does matrix multiply", sections 24 and 25 on overlapping loads with
-// compute, taken several stages deep).  Four wavefronts of 32 x 32, each 2 x 2
-// blocks of v_mfma_f32_16x16x4_f32 (lane l supplies A[l % 16][l / 16] and
+// compute, taken several stages deep).  2 WN wavefronts of 32 x 64 / WN, each
+// 2 x (4 / WN) blocks of v_mfma_f32_16x16x4_f32 (lane l supplies A[l % 16][l / 16] and
 // B[l / 16][l % 16] and holds C[4 (l / 16) + r][l % 16], r = 0..3); for the
 // four instructions e = 0..3 of a 16-deep k-slice q, lane l takes
 // k = 16 q + 4 (l / 16) + e, so its A values are one 128-bit read and its B
@@ -614,13 +614,16 @@ hipError_t launch_ring32_t(const RingArgs &a, hipStream_t s)
 //     one 32-bit read touches fall on four distinct quarters of the banks.
 // Edges and the k tail are zero-filled through out-of-range lane offsets
 // (K and N are multiples of 4, so a 16-byte unit is wholly in or out).
+// Each direct load costs its wavefront some issue time in which the matrix
+// core has nothing else to run; with eight wavefronts (two per SIMD, WN = 4)
+// the other wavefront's MFMAs fill it, 9% faster than four at 1024^3.
 namespace f32small {
 __host__ __device__ constexpr int fa(int r, int U) { return (r * U / 16) & (U - 1); }
 __host__ __device__ constexpr int fb(int k) { return 4 * ((k >> 2) & 3); }
 }  // namespace f32small
 
-template <int BK, int NBUF>
-__global__ __launch_bounds__(256) void mfma_f32_small_ring_kernel(int M, int N, int K,
+template <int BK, int NBUF, int WN>
+__global__ __launch_bounds__(128 * WN) void mfma_f32_small_ring_kernel(int M, int N, int K,
                                                                   const float *__restrict__ A,
                                                                   const float *__restrict__ B,
                                                                   float *__restrict__ C, int tiles_m,
@@ -628,9 +631,12 @@ __global__ __launch_bounds__(256) void mfma_f32_small_ring_kernel(int M, int N, 
 {
     using namespace f32small;
     constexpr int BM = 64, BN = 64, U = BK / 4;
+    constexpr int W = 2 * WN, BJ = 4 / WN;   // wavefronts; 16-column blocks per wavefront
     constexpr int A_BYTES = BM * BK * 4, STAGE = A_BYTES + BK * BN * 4;
-    constexpr int LA = BK / 16, LB = BK / 16, LPS = LA + LB;   // loads per wavefront and stage
-    constexpr int SLICES = BK / 16, READS = 10 * SLICES, MFMAS = 16 * SLICES;
+    constexpr int LA = BK / 4 / W, LB = BK / 4 / W, LPS = LA + LB;   // loads per wavefront and stage
+    constexpr int RPS = 2 + 4 * BJ;                                   // reads per slice
+    constexpr int SLICES = BK / 16, READS = RPS * SLICES, MFMAS = 8 * BJ * SLICES;
+    static_assert(LA >= 1 && LA * W * 4 == BK, "whole loads per wavefront");
     static_assert(U == 8 || U == 16, "A rows of 8 or 16 units");
     static_assert((NBUF & (NBUF - 1)) == 0 && NBUF >= 4, "ring of a power of two, at least 4");
     static_assert(READS <= MFMAS, "one read after each of the first MFMAs");
@@ -642,7 +648,7 @@ __global__ __launch_bounds__(256) void mfma_f32_small_ring_kernel(int M, int N, 
     const int m0 = tm * BM, n0 = tn * BN;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-    const int wr = (wave >> 1) * 32, wc = (wave & 1) * 32;
+    const int wr = (wave / WN) * 32, wc = (wave % WN) * 16 * BJ;
     constexpr uint32_t OOB = 0x80000000u;
 
     // ---- loader: wave w issues A loads w LA .. w LA + LA - 1 and B loads
@@ -685,38 +691,40 @@ __global__ __launch_bounds__(256) void mfma_f32_small_ring_kernel(int M, int N, 
         }
     };
 
-    // ---- fragment reads (read rd of a stage: slice q = rd / 10, then A
-    // block 0, A block 1, B block 0 rows e = 0..3, B block 1 rows e = 0..3).
-    // A block x, slice q: logical unit 4 q + h of row wr + 16 x + l16.  B block
-    // b, slice q, row e: k-row 16 q + 4 h + e (so fb = 4 h), column
-    // wc + 16 b + l16.
+    // ---- fragment reads (read rd of a stage: slice q = rd / RPS, then A
+    // block 0, A block 1, and rows e = 0..3 of each B block).  A block x,
+    // slice q: logical unit 4 q + h of row wr + 16 x + l16.  B block b, slice
+    // q, row e: k-row 16 q + 4 h + e (so fb = 4 h), column wc + 16 b + l16.
     const int l16 = lane & 15, h = lane >> 4;
-    uint32_t a_off[2 * SLICES], b_lane[2];
+    uint32_t a_off[2 * SLICES], b_lane[BJ];
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
         const int r = wr + 16 * x + l16;
 #pragma unroll
         for (int q = 0; q < SLICES; ++q)
             a_off[2 * q + x] = (uint32_t)(r * U * 16 + (((4 * q + h) ^ fa(r, U)) * 16));
-        const int col = wc + 16 * x + l16;
-        b_lane[x] = (uint32_t)(A_BYTES + (4 * h) * 256 + (((col >> 2) ^ (4 * h)) * 16) + (col & 3) * 4);
+    }
+#pragma unroll
+    for (int b = 0; b < BJ; ++b) {
+        const int col = wc + 16 * b + l16;
+        b_lane[b] = (uint32_t)(A_BYTES + (4 * h) * 256 + (((col >> 2) ^ (4 * h)) * 16) + (col & 3) * 4);
     }
     auto fread = [&](int st, int rd, floatx4 *fa_, floatx4 *fb_) {
         const uint8_t *buf = lds + (st & (NBUF - 1)) * STAGE;
-        const int q = rd / 10, x = rd % 10;
+        const int q = rd / RPS, x = rd % RPS;
         if (x < 2) {
             fa_[2 * q + x] = *reinterpret_cast<const floatx4 *>(buf + a_off[2 * q + x]);
         } else {
             const int b = (x - 2) >> 2, e = (x - 2) & 3;
-            fb_[2 * q + b][e] = *reinterpret_cast<const float *>(buf + b_lane[b] + (16 * q + e) * 256);
+            fb_[BJ * q + b][e] = *reinterpret_cast<const float *>(buf + b_lane[b] + (16 * q + e) * 256);
         }
     };
 
-    floatx4 acc[2][2];
+    floatx4 acc[2][BJ];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < BJ; ++j)
             acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
     // One stage t: its MFMAS matrix instructions from (ca, cb); the READS
@@ -733,9 +741,9 @@ __global__ __launch_bounds__(256) void mfma_f32_small_ring_kernel(int M, int N, 
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int m = 0; m < MFMAS; ++m) {
-            const int q = m >> 4, e = (m >> 2) & 3, i = (m >> 1) & 1, j = m & 1;
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(ca[2 * q + i][e], cb[2 * q + j][e], acc[i][j], 0, 0,
-                                                             0);
+            const int q = m / (8 * BJ), e = (m / (2 * BJ)) & 3, i = (m / BJ) & 1, j = m % BJ;
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(ca[2 * q + i][e], cb[BJ * q + j][e], acc[i][j], 0,
+                                                             0, 0);
             if (m < READS)
                 fread(t + 1, m, na, nb);
             if (m % (MFMAS / LPS) == MFMAS / LPS / 2)
@@ -745,7 +753,7 @@ __global__ __launch_bounds__(256) void mfma_f32_small_ring_kernel(int M, int N, 
     };
 
     // prologue: stages 0 .. NBUF - 2 in flight; once stage 0 has landed, its reads
-    floatx4 fa0[2 * SLICES], fb0[2 * SLICES], fa1[2 * SLICES], fb1[2 * SLICES];
+    floatx4 fa0[2 * SLICES], fb0[BJ * SLICES], fa1[2 * SLICES], fb1[BJ * SLICES];
     for (int st = 0; st < NBUF - 1; ++st)
 #pragma unroll
         for (int x = 0; x < LPS; ++x)
@@ -769,7 +777,7 @@ __global__ __launch_bounds__(256) void mfma_f32_small_ring_kernel(int M, int N, 
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < BJ; ++j)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int row = wr + 16 * i + 4 * h + r, col = wc + 16 * j + l16;
@@ -956,8 +964,8 @@ hipError_t launch_mfma_f32(const Problem &p, const gemm_plan &plan, hipStream_t 
     }
     if (plan.tile_m == 64 && plan.tile_n == 64) {
         if (f32_small_ring_applies(64, 64, p.N, p.K, p.vec_a, p.vec_b)) {
-            hipLaunchKernelGGL((mfma_f32_small_ring_kernel<kF32SmallDepth, kF32SmallStages>),
-                               dim3(plan.grid_x * plan.grid_y), dim3(256), 0, s, p.M, p.N, p.K,
+            hipLaunchKernelGGL((mfma_f32_small_ring_kernel<kF32SmallDepth, kF32SmallStages, kF32SmallWavesN>),
+                               dim3(plan.grid_x * plan.grid_y), dim3(128 * kF32SmallWavesN), 0, s, p.M, p.N, p.K,
                                (const float *)p.A, (const float *)p.B, p.C, plan.grid_y, plan.grid_x, 8);
             return hipGetLastError();
         }
