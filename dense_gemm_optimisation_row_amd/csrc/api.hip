@@ -146,11 +146,11 @@ int plan_f32(int variant, int M, int N, int K, const void *A, const void *B, con
         if (dgor::f32_ring_applies(M, N, K, p->vector_a, p->vector_b)) {
             p->tile_m = p->tile_n = dgor::kF32RingTile;
             p->tile_k = dgor::kF32RingDepth;
-            p->threads = 256;
+            p->threads = 64 * dgor::kF32RingWaves;
             p->lds_stages = dgor::kF32RingStages;
             p->lds_bytes = dgor::kF32RingLdsBytes;
             p->tile_bytes = 2 * dgor::kF32RingTile * dgor::kF32RingDepth * 4;
-            p->outputs_per_thread = dgor::kF32RingTile * dgor::kF32RingTile / 256;
+            p->outputs_per_thread = dgor::kF32RingTile * dgor::kF32RingTile / p->threads;
             p->vector_c = 0;
             break;
         }

@@ -192,6 +192,7 @@ constexpr int kF32RingTile = 256;
 constexpr int kF32RingDepth = 16;
 constexpr int kF32RingStages = 4;
 constexpr int kF32RingLdsBytes = kF32RingStages * (256 * 16 + 16 * 256) * 4;
+constexpr int kF32RingWaves = 8;   // wavefronts per workgroup: 4 (128 x 128 each) or 8 (128 x 64)
 inline bool f32_ring_applies(int M, int N, int K, bool vec_a, bool vec_b)
 {
     const long tiles = (long)((M + kF32RingTile - 1) / kF32RingTile) * ((N + kF32RingTile - 1) / kF32RingTile);

@@ -352,23 +352,23 @@ constexpr int A_BYTES = BM * BK * 4;                 // 16 KB
 constexpr int B_BYTES = BK * BN * 4;                 // 16 KB
 constexpr int STAGE_BYTES = A_BYTES + B_BYTES;       // 32 KB
 constexpr int LDS_BYTES = NBUF * STAGE_BYTES;        // 128 KB
-constexpr int LOADS_PER_STAGE = 8;                   // per wavefront: 4 per operand
 
-// Lane offsets of wave w's four 1 KB loads of one operand tile per stage,
-// relative to the stage's first element (as for the 16-bit ring).
-template <bool KSTRIDED>
+// Lane offsets of wave w's LPO 1 KB loads of one operand tile per stage
+// (loads LPO w .. LPO w + LPO - 1 of the stage's 16), relative to the stage's
+// first element (as for the 16-bit ring).
+template <bool KSTRIDED, int LPO>
 __device__ __forceinline__ void load_offsets(int wave, int lane, int t0, int ext, int ld,
-                                             uint32_t off[4], int &kc)
+                                             uint32_t off[LPO], int &kc)
 {
     constexpr uint32_t OOB = 0x80000000u;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < LPO; ++q) {
         if (!KSTRIDED) {
-            const int r = 16 * (4 * wave + q) + (lane >> 2);
+            const int r = 16 * (LPO * wave + q) + (lane >> 2);
             kc = 4 * ((lane & 3) ^ ((lane >> 4) & 3));   // same in every block
             off[q] = (uint32_t)(r * ld + kc) * 4u;
         } else {
-            const int k = 4 * wave + q;
+            const int k = LPO * wave + q;
             const int u = lane ^ (8 * ((k >> 2) & 1));
             off[q] = t0 + 4 * u < ext ? (uint32_t)(k * ld + 4 * u) * 4u : OOB;
             kc = 0;
@@ -395,11 +395,16 @@ __device__ __forceinline__ int stage_range(int k0, int K, int t0, int ext, int l
 }
 }  // namespace f32ring
 
-template <bool TA, bool TB, bool ACC>
-__global__ __launch_bounds__(256) void mfma_f32_ring_kernel(RingArgs args)
+template <bool TA, bool TB, bool ACC, int W>
+__global__ __launch_bounds__(64 * W) void mfma_f32_ring_kernel(RingArgs args)
 {
     const int bid = dgor_ring_split(args, 4);   // split-K: this workgroup's k-range and tile
     using namespace f32ring;
+    // W wavefronts of 128 x 256 / (W / 2): BI x BJ blocks of 32 x 32 each;
+    // LPO loads per operand and wavefront per stage
+    constexpr int WN = W / 2, BI = 4, BJ = 8 / WN, LPO = 16 / W, LOADS_PER_STAGE = 2 * LPO;
+    constexpr int MFMAS = 8 * BI * BJ;   // per stage: 2 k-slices x 4 k-steps x the blocks
+    static_assert(W == 4 || W == 8, "four or eight wavefronts");
     __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
     const uint32_t ring = lds_address(lds);
     const int M = args.M, N = args.N, K = args.K, lda = args.lda, ldb = args.ldb;
@@ -412,16 +417,16 @@ __global__ __launch_bounds__(256) void mfma_f32_ring_kernel(RingArgs args)
     const int lane = threadIdx.x & 63;
     // wave-uniform, so per-wave offsets and descriptors stay scalar
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-    const int wr = (wave >> 1) * 128, wc = (wave & 1) * 128;
+    const int wr = (wave / WN) * 128, wc = (wave % WN) * (256 / WN);
     constexpr uint32_t OOB = 0x80000000u;
 
     // ---- loader (see the 16-bit ring kernel for the range rules)
-    uint32_t a_off[4], b_off[4];
+    uint32_t a_off[LPO], b_off[LPO];
     int a_kc, b_kc;
-    load_offsets<TA>(wave, lane, m0, M, lda, a_off, a_kc);
-    load_offsets<!TB>(wave, lane, n0, N, ldb, b_off, b_kc);
-    const uint32_t lds_a = ring + (uint32_t)(4 * wave * 1024);
-    const uint32_t lds_b = ring + (uint32_t)(A_BYTES + 4 * wave * 1024);
+    load_offsets<TA, LPO>(wave, lane, m0, M, lda, a_off, a_kc);
+    load_offsets<!TB, LPO>(wave, lane, n0, N, ldb, b_off, b_kc);
+    const uint32_t lds_a = ring + (uint32_t)(LPO * wave * 1024);
+    const uint32_t lds_b = ring + (uint32_t)(A_BYTES + LPO * wave * 1024);
     struct StageLoads { intx4 ra, rb; uint32_t lds; bool tail; int k_left; };
     auto prep = [&](int st) {
         StageLoads L;
@@ -436,12 +441,12 @@ __global__ __launch_bounds__(256) void mfma_f32_ring_kernel(RingArgs args)
         return L;
     };
     auto load = [&](const StageLoads &L, int q) {
-        if (q < 4) {
+        if (q < LPO) {
             const uint32_t off = (!TA && L.tail && a_kc >= L.k_left) ? OOB : a_off[q];
             load_to_lds(L.ra, lds_a + L.lds + (uint32_t)(q * 1024), off);
         } else {
-            const uint32_t off = (TB && L.tail && b_kc >= L.k_left) ? OOB : b_off[q - 4];
-            load_to_lds(L.rb, lds_b + L.lds + (uint32_t)((q - 4) * 1024), off);
+            const uint32_t off = (TB && L.tail && b_kc >= L.k_left) ? OOB : b_off[q - LPO];
+            load_to_lds(L.rb, lds_b + L.lds + (uint32_t)((q - LPO) * 1024), off);
         }
     };
 
@@ -450,35 +455,38 @@ __global__ __launch_bounds__(256) void mfma_f32_ring_kernel(RingArgs args)
     const int kc_sw = (l32 >> 2) & 3;
     auto kc_lane = [&](uint32_t region, int base) { return region + (uint32_t)((base + l32) * 64); };
     auto ks_lane = [&](uint32_t region) { return region + (uint32_t)((4 * g) * 1024 + 4 * (l32 & 3)); };
-    uint32_t a_unit[4], b_unit[4];   // k-strided column units of each block
+    uint32_t a_unit[BI], b_unit[BJ];   // k-strided column units of each block
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < BI; ++j)
         a_unit[j] = (uint32_t)((((wr + 32 * j + l32) >> 2) ^ (8 * g)) * 16);
+#pragma unroll
+    for (int j = 0; j < BJ; ++j)
         b_unit[j] = (uint32_t)((((wc + 32 * j + l32) >> 2) ^ (8 * g)) * 16);
-    }
     const uint32_t a_lane = TA ? ks_lane(0) : kc_lane(0, wr);
     const uint32_t b_lane = TB ? kc_lane(A_BYTES, wc) : ks_lane(A_BYTES);
-    // One read instruction of operand X (k-slice q, block blk, sub-step e of
-    // a k-strided block) into x[4 q + blk].
-    auto read_one = [&](const uint8_t *buf, uint32_t lane_off, const uint32_t *unit, bool kstrided, int q,
-                        int blk, int e, floatx4 *x) {
+    // One read instruction of operand X (k-slice q, block blk of nblk,
+    // sub-step e of a k-strided block) into x[nblk q + blk].
+    auto read_one = [&](const uint8_t *buf, uint32_t lane_off, const uint32_t *unit, bool kstrided, int nblk,
+                        int q, int blk, int e, floatx4 *x) {
         if (!kstrided)
-            x[4 * q + blk] = *reinterpret_cast<const floatx4 *>(
+            x[nblk * q + blk] = *reinterpret_cast<const floatx4 *>(
                 buf + lane_off + blk * 32 * 64 + (((2 * q + g) ^ kc_sw) * 16));
         else
-            x[4 * q + blk][e] = *reinterpret_cast<const float *>(buf + lane_off + (8 * q + e) * 1024 + unit[blk]);
+            x[nblk * q + blk][e] =
+                *reinterpret_cast<const float *>(buf + lane_off + (8 * q + e) * 1024 + unit[blk]);
     };
-    // Read r of stage `stage`, in k-slice order; within a slice, for each
-    // block, A's read(s) then B's.
-    constexpr int NA = TA ? 4 : 1, NB = TB ? 1 : 4, PER = NA + NB;
-    constexpr int READS = 8 * PER;
+    // Read r of stage `stage`, in k-slice order; within a slice, A's reads
+    // (NA per block) then B's (NB per block).
+    constexpr int NA = TA ? 4 : 1, NB = TB ? 1 : 4, RPS = BI * NA + BJ * NB;
+    constexpr int READS = 2 * RPS;
+    static_assert(READS <= MFMAS, "one read after each of the first MFMAs");
     auto fread = [&](int stage, int r, floatx4 *fa, floatx4 *fb) {
         const uint8_t *buf = lds + (stage % NBUF) * STAGE_BYTES;
-        const int item = r / PER, x = r % PER, q = item >> 2, blk = item & 3;
-        if (x < NA)
-            read_one(buf, a_lane, a_unit, TA, q, blk, x, fa);
+        const int q = r / RPS, x = r % RPS;
+        if (x < BI * NA)
+            read_one(buf, a_lane, a_unit, TA, BI, q, x / NA, x % NA, fa);
         else
-            read_one(buf, b_lane, b_unit, !TB, q, blk, x - NA, fb);
+            read_one(buf, b_lane, b_unit, !TB, BJ, q, (x - BI * NA) / NB, (x - BI * NA) % NB, fb);
     };
 
     // ---- C tile: lane (g, l32) owns rows 32 i + 8 (r / 4) + 4 g + r % 4 and
@@ -495,11 +503,11 @@ __global__ __launch_bounds__(256) void mfma_f32_ring_kernel(RingArgs args)
     };
 
     // Accumulators start at zero, or at C itself (ACC: C = alpha (C + op(A) op(B))).
-    floatx16 acc[4][4];
+    floatx16 acc[BI][BJ];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < BI; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < BJ; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 if (ACC) {
@@ -512,12 +520,11 @@ __global__ __launch_bounds__(256) void mfma_f32_ring_kernel(RingArgs args)
                 }
             }
 
-    // One stage: the 128 MFMAs of stage t from (ca, cb); the reads of stage
-    // t + 1 into (na, nb), one after each of the first READS MFMAs (at most
-    // 64); the 8 loads of stage t + 3, one after every eighth MFMA from the
-    // 64th.  The loads' descriptors are set up behind the first MFMA: with
-    // one wavefront per SIMD, scalar work between the barrier and the first
-    // MFMA leaves the matrix core idle.
+    // One stage: the MFMAS matrix instructions of stage t from (ca, cb); the
+    // reads of stage t + 1 into (na, nb), one after each of the first READS
+    // MFMAs; the loads of stage t + 3 spread over the second half.  The loads'
+    // descriptors are set up behind the first MFMA: scalar work between the
+    // barrier and the first MFMA leaves the matrix core idle.
     const int steps = (K + BK - 1) / BK;
     auto stage = [&](int t, floatx4 *ca, floatx4 *cb, floatx4 *na, floatx4 *nb) {
         __builtin_amdgcn_s_waitcnt(wait_vmcnt(LOADS_PER_STAGE));
@@ -525,16 +532,17 @@ __global__ __launch_bounds__(256) void mfma_f32_ring_kernel(RingArgs args)
         __builtin_amdgcn_sched_barrier(0);
         StageLoads L;
 #pragma unroll
-        for (int m = 0; m < 128; ++m) {
-            const int q = m >> 6, jp = (m >> 4) & 3, i = (m >> 2) & 3, j = m & 3;
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(ca[4 * q + i][jp], cb[4 * q + j][jp], acc[i][j], 0,
-                                                              0, 0);
+        for (int m = 0; m < MFMAS; ++m) {
+            const int q = m / (4 * BI * BJ), jp = (m / (BI * BJ)) & 3, i = (m / BJ) % BI, j = m % BJ;
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(ca[BI * q + i][jp], cb[BJ * q + j][jp], acc[i][j],
+                                                              0, 0, 0);
             if (m == 1)
                 L = prep(t + 3);
             if (m < READS)
                 fread(t + 1, m, na, nb);
-            if (m >= 64 && (m - 64) % 8 == 0)
-                load(L, (m - 64) / 8);
+            constexpr int HALF = MFMAS / 2, EVERY = HALF / LOADS_PER_STAGE;
+            if (m >= HALF && (m - HALF) % EVERY == 0)
+                load(L, (m - HALF) / EVERY);
             // keep this order: the compiler would otherwise cluster the reads
             // and loads, and move MFMAs across the barrier
             __builtin_amdgcn_sched_barrier(0);
@@ -542,12 +550,12 @@ __global__ __launch_bounds__(256) void mfma_f32_ring_kernel(RingArgs args)
     };
 
     // prologue: loads of stages 0, 1, 2, then the reads of stage 0
-    floatx4 fa0[8], fa1[8], fb0[8], fb1[8];
+    floatx4 fa0[2 * BI], fa1[2 * BI], fb0[2 * BJ], fb1[2 * BJ];
 #pragma unroll
     for (int st = 0; st < 3; ++st) {
         const StageLoads L = prep(st);
 #pragma unroll
-        for (int q = 0; q < 8; ++q)
+        for (int q = 0; q < LOADS_PER_STAGE; ++q)
             load(L, q);
     }
     __builtin_amdgcn_s_waitcnt(wait_vmcnt(2 * LOADS_PER_STAGE));
@@ -570,9 +578,9 @@ __global__ __launch_bounds__(256) void mfma_f32_ring_kernel(RingArgs args)
     asm volatile("" : "+v"(col_e), "+v"(rows_e));
     dgor_acc_hazard_wait();
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < BJ; ++j)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < BI; ++i)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 uint32_t vo, so;
@@ -586,10 +594,11 @@ template <bool TA, bool TB>
 hipError_t launch_ring32_t(const RingArgs &a, hipStream_t s)
 {
     const dim3 grid(a.tiles_m * a.tiles_n * (a.splits > 1 ? a.splits : 1));
+    constexpr int W = kF32RingWaves;
     if (a.accumulate)
-        hipLaunchKernelGGL((mfma_f32_ring_kernel<TA, TB, true>), grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((mfma_f32_ring_kernel<TA, TB, true, W>), grid, dim3(64 * W), 0, s, a);
     else
-        hipLaunchKernelGGL((mfma_f32_ring_kernel<TA, TB, false>), grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((mfma_f32_ring_kernel<TA, TB, false, W>), grid, dim3(64 * W), 0, s, a);
     return hipGetLastError();
 }
 
