@@ -505,9 +505,14 @@ int run_conv(In in, const gemm_conv2d_params *pr, const void *x, const void *w, 
         return dev;
     hipStream_t s = (hipStream_t)stream;
     uint8_t *base = (uint8_t *)ws;
-    void *wp = base, *col = base + cp.off_col;
+    void *col = base + cp.off_col;
     float *yp = (float *)(base + cp.off_y);
-    if (dgor::launch_conv_prepare(cv, eb, x, w, wp, col, cp.crsp, cp.npqp, s) != hipSuccess)
+    // W (K x CRS) is already the GEMM's K x CRSp operand when CRS is a
+    // multiple of 8 and W is 16-byte aligned: no padded copy then
+    const bool w_direct = cp.crsp == cv.C * cv.R * cv.S && aligned16(w);
+    const void *wp = w_direct ? w : base;
+    if (dgor::launch_conv_prepare(cv, eb, x, w, w_direct ? nullptr : base, col, cp.crsp, cp.npqp, s) !=
+        hipSuccess)
         return GEMM_ERR_LAUNCH;
     // the GEMM: K x CRSp by CRSp x NPQp
     if (cp.ring) {

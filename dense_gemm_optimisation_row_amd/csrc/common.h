@@ -84,6 +84,7 @@ hipError_t launch_ring8(const RingArgs &args, int fmt, hipStream_t stream);
 struct Conv2d {
     int N, C, H, W, K, R, S, sh, sw, ph, pw, dh, dw, P, Q;
 };
+// wp null: W is used as it is (no padded copy)
 hipError_t launch_conv_prepare(const Conv2d &cv, int elem_bytes, const void *x, const void *w, void *wp, void *col,
                                int crsp, int npqp, hipStream_t stream);
 hipError_t launch_conv_output(const Conv2d &cv, const float *yp, float *y, int npqp, int splits,

@@ -8,9 +8,11 @@
 //     col[c R S + r S + s][n PQ + p Q + q] = x[n][c][p sh - ph + r dh][q sw - pw + s dw]
 // (zero outside the image), a K x CRS by CRS x NPQ GEMM.  The three memory-
 // bound passes here prepare its operands and lay its result out as NKPQ:
-//   pad_weights: W (K x CRS) into K x CRSp, zero columns past CRS;
+//   pad_weights: W (K x CRS) into K x CRSp, zero columns past CRS (skipped
+//                when CRS is a multiple of 8: W is then used as it is);
 //   im2col:      col into CRSp x NPQp, zero rows past CRS and columns past NPQ;
-//   to_nkpq:     Y' (K x NPQp) into y, summing the split-K partials in order.
+//   to_nkpq:     Y' (K x NPQp) into y, summing the split-K partials in order
+//                (four outputs a thread when PQ is a multiple of 4).
 // CRSp and NPQp round CRS and NPQ up to multiples of 8, so both GEMM operands
 // take 16-byte loads; the padding adds exact zeros only.
 #include "common.h"
@@ -89,6 +91,30 @@ __global__ __launch_bounds__(256) void to_nkpq(const float *__restrict__ yp, flo
     }
 }
 
+// The same with four consecutive outputs per thread (PQ a multiple of 4, so
+// they share n and k; y and the partials 16-byte aligned).
+__global__ __launch_bounds__(256) void to_nkpq4(const float *__restrict__ yp, float *__restrict__ y, int N, int K,
+                                                int PQ, int npqp, int splits, size_t split_stride)
+{
+    const size_t total4 = (size_t)N * K * PQ / 4;
+    for (size_t e = (size_t)blockIdx.x * 256 + threadIdx.x; e < total4; e += (size_t)gridDim.x * 256) {
+        const size_t e0 = 4 * e;
+        const int pq = (int)(e0 % PQ);
+        const size_t nk = e0 / PQ;
+        const int k = (int)(nk % K), n = (int)(nk / K);
+        const float *src = yp + (size_t)k * npqp + (size_t)n * PQ + pq;
+        float4 v = *reinterpret_cast<const float4 *>(src);
+        for (int sp = 1; sp < splits; ++sp) {
+            const float4 w = *reinterpret_cast<const float4 *>(src + (size_t)sp * split_stride);
+            v.x += w.x;
+            v.y += w.y;
+            v.z += w.z;
+            v.w += w.w;
+        }
+        *reinterpret_cast<float4 *>(y + e0) = v;
+    }
+}
+
 unsigned blocks_for(size_t n)
 {
     const size_t b = (n + 255) / 256;
@@ -106,12 +132,14 @@ hipError_t launch_conv_prepare(const Conv2d &cv, int elem_bytes, const void *x, 
     const int chunks = (crsp + kRowChunk - 1) / kRowChunk;
     const dim3 g_im((unsigned)((npqp + 255) / 256), (unsigned)(chunks < 65535 ? chunks : 65535));
     if (elem_bytes == 4) {
-        hipLaunchKernelGGL(pad_weights<float>, dim3(blocks_for((size_t)cv.K * crsp)), dim3(256), 0, s,
-                           (const float *)w, (float *)wp, cv.K, crs, crsp);
+        if (wp)
+            hipLaunchKernelGGL(pad_weights<float>, dim3(blocks_for((size_t)cv.K * crsp)), dim3(256), 0, s,
+                               (const float *)w, (float *)wp, cv.K, crs, crsp);
         hipLaunchKernelGGL(im2col<float>, g_im, dim3(256), 0, s, (const float *)x, (float *)col, cv, crsp, npqp);
     } else {
-        hipLaunchKernelGGL(pad_weights<uint16_t>, dim3(blocks_for((size_t)cv.K * crsp)), dim3(256), 0, s,
-                           (const uint16_t *)w, (uint16_t *)wp, cv.K, crs, crsp);
+        if (wp)
+            hipLaunchKernelGGL(pad_weights<uint16_t>, dim3(blocks_for((size_t)cv.K * crsp)), dim3(256), 0, s,
+                               (const uint16_t *)w, (uint16_t *)wp, cv.K, crs, crsp);
         hipLaunchKernelGGL(im2col<uint16_t>, g_im, dim3(256), 0, s, (const uint16_t *)x, (uint16_t *)col, cv, crsp,
                            npqp);
     }
@@ -122,8 +150,15 @@ hipError_t launch_conv_output(const Conv2d &cv, const float *yp, float *y, int n
                               size_t split_stride, hipStream_t s)
 {
     const size_t total = (size_t)cv.N * cv.K * cv.P * cv.Q;
-    hipLaunchKernelGGL(to_nkpq, dim3(blocks_for(total)), dim3(256), 0, s, yp, y, cv.N, cv.K, cv.P * cv.Q, npqp,
-                       splits, split_stride);
+    const int PQ = cv.P * cv.Q;
+    // partials: yp 16-byte aligned, rows of npqp (a multiple of 8) floats,
+    // split_stride a multiple of 64 floats
+    if (PQ % 4 == 0 && ((uintptr_t)y & 15) == 0 && ((uintptr_t)yp & 15) == 0 && split_stride % 4 == 0)
+        hipLaunchKernelGGL(to_nkpq4, dim3(blocks_for(total / 4)), dim3(256), 0, s, yp, y, cv.N, cv.K, PQ, npqp,
+                           splits, split_stride);
+    else
+        hipLaunchKernelGGL(to_nkpq, dim3(blocks_for(total)), dim3(256), 0, s, yp, y, cv.N, cv.K, PQ, npqp, splits,
+                           split_stride);
     return hipGetLastError();
 }
 
