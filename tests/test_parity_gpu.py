@@ -354,6 +354,49 @@ def test_non_default_stream_and_determinism():
     assert torch.equal(h1, h2)
 
 
+def test_concurrent_calls_from_threads_on_their_own_streams():
+    """The ABI's calls are thread-safe and may overlap on different streams:
+    eight host threads, each with its own stream and its own shape (every
+    FP32 and 16-bit path the planner has), call the library 20 times each at
+    once (ctypes drops the GIL around the call); every result must equal the
+    oracle's bit for bit (integer inputs)."""
+    import threading
+    import torch
+    shapes = [(4096, 4096, 16, "f32"), (1024, 1024, 256, "f32"), (4097, 33, 777, "f32"), (2049, 1000, 100, "f32"),
+              (300, 200, 100, "f32"), (8192, 4096, 32, "f16"), (1000, 1000, 200, "bf16"), (513, 257, 129, "f16")]
+    cases = []
+    for i, (M, N, K, fmt) in enumerate(shapes):
+        A, B = inputs.matrices(M, N, K, 8100 + i, "int", fmt)
+        cases.append((fmt, M, N, K, to_dev(A), to_dev(B), oracle_gemm(A, B)))
+    torch.cuda.synchronize()
+    fns = {"f32": dg.gemm_f32, "f16": dg.gemm_f16_f32acc, "bf16": dg.gemm_bf16_f32acc}
+    results, errors = [None] * len(cases), []
+
+    def worker(i):
+        try:
+            fmt, M, N, K, a, b, _ = cases[i]
+            s = torch.cuda.Stream()
+            outs = [torch.empty((M, N), device="cuda") for _ in range(2)]
+            for r in range(20):
+                fns[fmt](a, b, outs[r % 2], stream=s)
+            s.synchronize()
+            results[i] = [o.cpu().numpy() for o in outs]
+        except Exception as e:   # reported in the main thread
+            errors.append((i, repr(e)))
+
+    say("concurrent threads", len(cases))
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(len(cases))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=100)
+    assert not any(t.is_alive() for t in threads), "a worker did not finish"
+    assert not errors, errors
+    for (fmt, M, N, K, _, _, ref), outs in zip(cases, results):
+        for o in outs:
+            assert_bits_equal(o, ref, f"concurrent {fmt} {(M, N, K)}")
+
+
 def test_k1_is_a_single_rounded_product():
     M, N = 70, 90
     say("edge K=1")
