@@ -511,6 +511,13 @@ int run_conv(In in, const gemm_conv2d_params *pr, const void *x, const void *w, 
     // multiple of 8 and W is 16-byte aligned: no padded copy then
     const bool w_direct = cp.crsp == cv.C * cv.R * cv.S && aligned16(w);
     const void *wp = w_direct ? w : base;
+    if (dgor::conv_igemm_applies(cv, eb)) {   // 16-bit, enough tiles: no im2col matrix
+        if (!w_direct &&
+            dgor::launch_conv_prepare(cv, eb, x, w, base, nullptr, cp.crsp, cp.npqp, s) != hipSuccess)
+            return GEMM_ERR_LAUNCH;
+        return dgor::launch_conv_igemm(cv, in == In::BF16, x, wp, y, cp.crsp, s) == hipSuccess ? GEMM_OK
+                                                                                               : GEMM_ERR_LAUNCH;
+    }
     if (dgor::launch_conv_prepare(cv, eb, x, w, w_direct ? nullptr : base, col, cp.crsp, cp.npqp, s) !=
         hipSuccess)
         return GEMM_ERR_LAUNCH;

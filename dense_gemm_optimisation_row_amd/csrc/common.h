@@ -84,11 +84,17 @@ hipError_t launch_ring8(const RingArgs &args, int fmt, hipStream_t stream);
 struct Conv2d {
     int N, C, H, W, K, R, S, sh, sw, ph, pw, dh, dw, P, Q;
 };
-// wp null: W is used as it is (no padded copy)
+// wp null: W is used as it is (no padded copy); col null: no im2col matrix
 hipError_t launch_conv_prepare(const Conv2d &cv, int elem_bytes, const void *x, const void *w, void *wp, void *col,
                                int crsp, int npqp, hipStream_t stream);
 hipError_t launch_conv_output(const Conv2d &cv, const float *yp, float *y, int npqp, int splits,
                               size_t split_stride, hipStream_t stream);
+// The implicit-GEMM convolution for 16-bit inputs (no im2col matrix): taken
+// when its 128-filter x 256-pixel tiles number at least 256.  wa is K x CRSp
+// with 16-byte aligned rows; y is written directly.
+bool conv_igemm_applies(const Conv2d &cv, int elem_bytes);
+hipError_t launch_conv_igemm(const Conv2d &cv, bool bf16, const void *x, const void *wa, float *y, int crsp,
+                             hipStream_t stream);
 hipError_t launch_naive_8bit(const Problem &p, int fmt, hipStream_t stream);
 
 // The arguments of the ring kernels for a plain row-major product.

@@ -16,6 +16,9 @@
 // CRSp and NPQp round CRS and NPQ up to multiples of 8, so both GEMM operands
 // take 16-byte loads; the padding adds exact zeros only.
 #include "common.h"
+#include "lds_dma.h"
+
+#include <type_traits>
 
 namespace dgor {
 namespace {
@@ -115,6 +118,186 @@ __global__ __launch_bounds__(256) void to_nkpq4(const float *__restrict__ yp, fl
     }
 }
 
+// ---------------------------------------------------------------------------
+// Implicit GEMM for 16-bit inputs: the same K x CRS by CRS x NPQ product
+// with the im2col matrix never written.  Each workgroup computes BM filters x
+// 256 output pixels; its 256 threads each own one pixel (decoded once) and
+// gather that pixel's 32 values of every 32-deep k-stage straight from x
+// (stepping c, r, s; a tap outside the image reads a valid element of x and
+// is replaced by zero, so the loads carry no branch and all 32 are in flight
+// together), two stages ahead of the MFMAs, in registers.  LDS holds two
+// stages, both operands stored with k contiguous (80-byte rows: 32 halves and
+// 16 bytes of padding, so the 16 rows one 128-bit read cycle touches fall on
+// distinct banks), and each v_mfma_f32_16x16x32 operand is one 128-bit read
+// (lane (g, s) takes k = 8 g .. 8 g + 7 of row or pixel s).  Results go
+// straight to y (NKPQ).  Wavefront w takes pixels 64 w .. 64 w + 63 and all
+// BM filters.
+typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+template <bool BF16>
+__device__ __forceinline__ floatx4 igemm_mma(uint4 a, uint4 b, floatx4 c)
+{
+    if constexpr (BF16)
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                       c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(halfx8, a), __builtin_bit_cast(halfx8, b),
+                                                      c, 0, 0, 0);
+}
+
+template <bool BF16, int BM>
+__global__ __launch_bounds__(256) void conv_igemm(const uint16_t *__restrict__ x, const uint16_t *__restrict__ wa,
+                                                  float *__restrict__ y, Conv2d cv, int crsp, int tiles_m)
+{
+    constexpr int BN = 256, BK = 32, ROWB = 80, FM = BM / 16, AV = BM / 64;
+    constexpr int A_BYTES = BM * ROWB, STAGE = A_BYTES + BN * ROWB;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * STAGE];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int tm = blockIdx.x % tiles_m, tn = blockIdx.x / tiles_m;   // a pixel block's filter tiles adjacent
+    const int m0 = tm * BM, j0 = tn * BN;
+    const int RS = cv.R * cv.S, crs_n = cv.C * RS, PQ = cv.P * cv.Q, npq = cv.N * PQ;
+
+    // this thread's pixel: its offset into x at tap (c, r, s) = (0, 0, 0),
+    // and the top-left input position; the tap offset c H W + r dh W + s dw
+    // and the gather state (c, r, s, k) are the same in every lane
+    constexpr uint32_t OOB = 0x80000000u;
+    const int jp = j0 + tid;
+    const bool jv = jp < npq;
+    const int n = jv ? jp / PQ : 0, pq = jv ? jp - n * PQ : 0, p = pq / cv.Q, q = pq - p * cv.Q;
+    const int h0 = p * cv.sh - cv.ph, w0 = q * cv.sw - cv.pw;
+    const int lane_base = (n * cv.C * cv.H + h0) * cv.W + w0;   // x < 2^30 elements
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, (long long)cv.N * cv.C * cv.H * cv.W * 2);
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(wa, (long long)cv.K * crsp * 2);
+    int gc = 0, gr = 0, gs = 0, gk = 0;
+    // the next BK values of this pixel; a tap outside the image (or past CRS,
+    // or of a pixel past NPQ) has an out-of-range offset and reads zero
+    auto gather = [&](uint32_t (&dst)[BK]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int e = 0; e < BK; ++e) {
+            const int rh = gr * cv.dh, sw = gs * cv.dw;
+            const bool ok = jv & (gk + e < crs_n) & ((unsigned)(h0 + rh) < (unsigned)cv.H) &
+                            ((unsigned)(w0 + sw) < (unsigned)cv.W);
+            const uint32_t off = ok ? (uint32_t)(lane_base + (gc * cv.H + rh) * cv.W + sw) * 2u : OOB;
+            dst[e] = __builtin_amdgcn_raw_buffer_load_b16(rx, off, 0, 0);
+            if (++gs == cv.S) {
+                gs = 0;
+                if (++gr == cv.R) {
+                    gr = 0;
+                    ++gc;
+                }
+            }
+        }
+        gk += BK;
+    };
+    // W (K x CRSp, rows 16-byte aligned): thread t loads 16-byte units
+    // t + 256 i of the stage's BM x 32 block (zero past K or CRSp)
+    auto load_a = [&](int st, uint4 (&dst)[AV]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < AV; ++i) {
+            const int u = tid + 256 * i, row = u >> 2, kq = (u & 3) * 8, kk = st * BK + kq;
+            const bool ok = (m0 + row < cv.K) & (kk < crsp);
+            const uint32_t off = ok ? (uint32_t)((m0 + row) * crsp + kk) * 2u : OOB;
+            dst[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, 0));
+        }
+    };
+    auto store = [&](int buf, const uint32_t (&rb)[BK], const uint4 (&ra)[AV]) __attribute__((always_inline)) {
+        uint8_t *st = lds + buf * STAGE;
+#pragma unroll
+        for (int i = 0; i < AV; ++i) {
+            const int u = tid + 256 * i;
+            *reinterpret_cast<uint4 *>(st + (u >> 2) * ROWB + (u & 3) * 16) = ra[i];
+        }
+        uint32_t pk[BK / 2];
+#pragma unroll
+        for (int e = 0; e < BK / 2; ++e)
+            pk[e] = (rb[2 * e] & 0xffffu) | (rb[2 * e + 1] << 16);
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            *reinterpret_cast<uint4 *>(st + A_BYTES + tid * ROWB + 16 * v) =
+                make_uint4(pk[4 * v], pk[4 * v + 1], pk[4 * v + 2], pk[4 * v + 3]);
+    };
+
+    const int g = lane >> 4, s16 = lane & 15;
+    floatx4 acc[FM][4];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)   // AGPR writes, so the accumulators stay in AGPRs
+                asm("v_accvgpr_write_b32 %0, 0" : "=a"(acc[i][jb][r]));
+    auto compute = [&](int buf) __attribute__((always_inline)) {
+        const uint8_t *st = lds + buf * STAGE;
+        uint4 a[FM], b[4];
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+            a[i] = *reinterpret_cast<const uint4 *>(st + (16 * i + s16) * ROWB + 16 * g);
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb)
+            b[jb] = *reinterpret_cast<const uint4 *>(st + A_BYTES + (64 * wave + 16 * jb + s16) * ROWB + 16 * g);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int jb = 0; jb < 4; ++jb)
+                acc[i][jb] = igemm_mma<BF16>(a[i], b[jb], acc[i][jb]);
+    };
+
+    // stages t and t + 1 gathered before the loop; during stage t the gather
+    // of stage t + 2 flies while stage t computes, then stage t + 1 (gathered
+    // during t - 1) is stored for the next trip.  A register set is reused
+    // once its stage is in LDS; an LDS buffer once the barrier after its
+    // stage's MFMAs has passed.
+    const int steps = (crsp + BK - 1) / BK;
+    uint32_t rb[2][BK];
+    uint4 ra[2][AV];
+    gather(rb[0]);
+    load_a(0, ra[0]);
+    gather(rb[1]);   // past the last stage every tap is out of range
+    load_a(1, ra[1]);
+    store(0, rb[0], ra[0]);
+    __syncthreads();
+    auto stage = [&](int t, auto cur_c) __attribute__((always_inline)) {
+        constexpr int cur = decltype(cur_c)::value;
+        gather(rb[cur]);   // stage t + 2 (no condition: a load under one is waited for)
+        load_a(t + 2, ra[cur]);
+        // keep the order: the store waits for the loads of stage t + 1 only
+        // if it stays behind this stage's MFMAs and the new gathers
+        __builtin_amdgcn_sched_barrier(0);
+        compute(cur);
+        __builtin_amdgcn_sched_barrier(0);
+        if (t + 1 < steps)
+            store(cur ^ 1, rb[cur ^ 1], ra[cur ^ 1]);
+        __syncthreads();
+    };
+    for (int t = 0; t < steps; t += 2) {
+        stage(t, std::integral_constant<int, 0>{});
+        if (t + 1 < steps)
+            stage(t + 1, std::integral_constant<int, 1>{});
+    }
+
+    // lane (g, s16) of wavefront w holds filters m0 + 16 i + 4 g + r of pixel
+    // j0 + 64 w + 16 jb + s16
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb) {
+        const int jo = j0 + 64 * wave + 16 * jb + s16;
+        if (jo >= npq)
+            continue;
+        const int no = jo / PQ, pqo = jo - no * PQ;
+        float *yo = y + (size_t)no * cv.K * PQ + pqo;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int k = m0 + 16 * i + 4 * g + r;
+                if (k < cv.K)
+                    yo[(size_t)k * PQ] = acc[i][jb][r];
+            }
+    }
+}
+
 unsigned blocks_for(size_t n)
 {
     const size_t b = (n + 255) / 256;
@@ -135,13 +318,51 @@ hipError_t launch_conv_prepare(const Conv2d &cv, int elem_bytes, const void *x, 
         if (wp)
             hipLaunchKernelGGL(pad_weights<float>, dim3(blocks_for((size_t)cv.K * crsp)), dim3(256), 0, s,
                                (const float *)w, (float *)wp, cv.K, crs, crsp);
-        hipLaunchKernelGGL(im2col<float>, g_im, dim3(256), 0, s, (const float *)x, (float *)col, cv, crsp, npqp);
+        if (col)
+            hipLaunchKernelGGL(im2col<float>, g_im, dim3(256), 0, s, (const float *)x, (float *)col, cv, crsp, npqp);
     } else {
         if (wp)
             hipLaunchKernelGGL(pad_weights<uint16_t>, dim3(blocks_for((size_t)cv.K * crsp)), dim3(256), 0, s,
                                (const uint16_t *)w, (uint16_t *)wp, cv.K, crs, crsp);
-        hipLaunchKernelGGL(im2col<uint16_t>, g_im, dim3(256), 0, s, (const uint16_t *)x, (uint16_t *)col, cv, crsp,
-                           npqp);
+        if (col)
+            hipLaunchKernelGGL(im2col<uint16_t>, g_im, dim3(256), 0, s, (const uint16_t *)x, (uint16_t *)col, cv,
+                               crsp, npqp);
+    }
+    return hipGetLastError();
+}
+
+bool conv_igemm_applies(const Conv2d &cv, int elem_bytes)
+{
+    if (elem_bytes != 2 || cv.C == 0)
+        return false;
+    const long long npq = (long long)cv.N * cv.P * cv.Q;
+    const long long tiles = (long long)((cv.K + 127) / 128) * ((npq + 255) / 256);
+    // byte offsets into x and W stay below 2^31
+    return tiles >= 256 && npq < (1LL << 30) && (long long)cv.N * cv.C * cv.H * cv.W < (1LL << 30) &&
+           (long long)cv.K * cv.C * cv.R * cv.S < (1LL << 29);
+}
+
+hipError_t launch_conv_igemm(const Conv2d &cv, bool bf16, const void *x, const void *wa, float *y, int crsp,
+                             hipStream_t s)
+{
+    const long long npq = (long long)cv.N * cv.P * cv.Q;
+    const int tn = (int)((npq + 255) / 256);
+    if (cv.K <= 64) {
+        const dim3 grid((unsigned)(((cv.K + 63) / 64) * tn));
+        if (bf16)
+            hipLaunchKernelGGL((conv_igemm<true, 64>), grid, dim3(256), 0, s, (const uint16_t *)x,
+                               (const uint16_t *)wa, y, cv, crsp, (cv.K + 63) / 64);
+        else
+            hipLaunchKernelGGL((conv_igemm<false, 64>), grid, dim3(256), 0, s, (const uint16_t *)x,
+                               (const uint16_t *)wa, y, cv, crsp, (cv.K + 63) / 64);
+    } else {
+        const dim3 grid((unsigned)(((cv.K + 127) / 128) * tn));
+        if (bf16)
+            hipLaunchKernelGGL((conv_igemm<true, 128>), grid, dim3(256), 0, s, (const uint16_t *)x,
+                               (const uint16_t *)wa, y, cv, crsp, (cv.K + 127) / 128);
+        else
+            hipLaunchKernelGGL((conv_igemm<false, 128>), grid, dim3(256), 0, s, (const uint16_t *)x,
+                               (const uint16_t *)wa, y, cv, crsp, (cv.K + 127) / 128);
     }
     return hipGetLastError();
 }

@@ -110,6 +110,32 @@ def test_conv2d_layers(fmt, case):
     _case(fmt, case, 5400, False)
 
 
+# 16-bit layers whose implicit-GEMM tiles (128 filters x 256 pixels) number
+# at least 256, so they take the implicit-GEMM kernel (no im2col matrix):
+# BM = 64 and 128 (K <= 64 and K > 64, ragged), C R S a multiple of 8 (W used
+# as it is) and not (padded copy), stride, dilation and a 1 x 1 filter, and
+# NPQ not a multiple of 256.  Few channels keep the oracle quick.
+IGEMM = [
+    (32, 8, 56, 56, 16, 3, 3, (1, 1), (1, 1), (1, 1)),      # CRS 72, K 16
+    (30, 3, 58, 57, 40, 3, 3, (1, 1), (1, 1), (1, 1)),      # CRS 27 (padded), NPQ 99180
+    (16, 16, 66, 66, 200, 3, 3, (1, 1), (1, 1), (1, 1)),    # K 200: two 128-filter tiles
+    (16, 8, 130, 130, 24, 5, 5, (2, 2), (2, 2), (1, 1)),    # stride 2, 5 x 5
+    (8, 4, 128, 128, 33, 3, 3, (1, 1), (2, 2), (2, 2)),     # dilation 2
+    (64, 32, 32, 32, 64, 1, 1, (1, 1), (0, 0), (1, 1)),     # 1 x 1, CRS 32
+]
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+@pytest.mark.parametrize("case", IGEMM, ids=lambda c: "x".join(map(str, c[:7])))
+def test_conv2d_implicit_gemm_layers(fmt, case):
+    N, C, H, W, K, R, S, st, pd, dl = case
+    P = (H + 2 * pd[0] - dl[0] * (R - 1) - 1) // st[0] + 1
+    Q = (W + 2 * pd[1] - dl[1] * (S - 1) - 1) // st[1] + 1
+    assert -(-K // 128) * -(-(N * P * Q) // 256) >= 256   # the implicit-GEMM rule
+    _case(fmt, case, 5500, True)
+    _case(fmt, case, 5600, False)
+
+
 @pytest.mark.parametrize("fmt", ["f32", "f16"])
 def test_conv2d_zero_channels_and_empty_batch(fmt):
     import torch
