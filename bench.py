@@ -302,8 +302,9 @@ def all_workloads(dg, inputs, torch, dev, stream, dev_in, wl):
 
 
 def conv_workloads(dg, inputs, torch, dev, stream):
-    """Convolutions through im2col + GEMM: 2 N K P Q C R S per call over the
-    whole call (im2col, GEMM and output layout), workspace allocated once."""
+    """Convolutions (im2col + GEMM, or the implicit GEMM for 16-bit layers
+    with enough tiles): 2 N K P Q C R S per call over the whole call,
+    workspace allocated once."""
     import numpy as np
 
     res = {}
@@ -320,12 +321,15 @@ def conv_workloads(dg, inputs, torch, dev, stream):
         reps = max(3, min(200, int(100.0 / max(est, 1e-3))))
         ms = _time_calls(f, torch, stream, reps)
         tf = w.flops / (ms * 1e-3) / 1e12
+        implicit = dg.conv2d_algorithm(prm, xd.element_size()) == dg.CONV_IMPLICIT
         gemm_plan = dg.plan(w.dtype, w.K, -(-w.N * P * Q // 8) * 8, -(-w.C * w.R * w.S // 8) * 8)
         res[name] = {"N": w.N, "C": w.C, "H": w.H, "W": w.W, "K": w.K, "R": w.R, "S": w.S,
                      "stride": w.stride, "pad": w.pad, "dtype": w.dtype, "ms": round(ms, 5),
                      "tflops": round(tf, 3), "frac_of_peak": round(tf / PEAK_TFLOPS[w.dtype], 4),
                      "gemm": [w.K, w.N * P * Q, w.C * w.R * w.S],
-                     "gemm_tile": [gemm_plan["tile_m"], gemm_plan["tile_n"]],
+                     "algorithm": "implicit_gemm" if implicit else "im2col_gemm",
+                     "gemm_tile": [128 if w.K > 64 else 64, 256] if implicit else
+                     [gemm_plan["tile_m"], gemm_plan["tile_n"]],
                      "workspace_bytes": int(ws.numel())}
         del xd, wd, y, ws
     return res

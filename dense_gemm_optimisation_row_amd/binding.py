@@ -52,7 +52,7 @@ EXPORTS = ("gemm_f32", "gemm_f16_f32acc", "gemm_bf16_f32acc",
            "gemm_e4m3_f32acc_variant", "gemm_e5m2_f32acc_variant", "gemm_i8_i32acc_variant",
            "gemm_e4m3_f32acc_plan", "gemm_e5m2_f32acc_plan", "gemm_i8_i32acc_plan",
            "gemm_f32_ex", "gemm_f16_f32acc_ex", "gemm_bf16_f32acc_ex",
-           "gemm_conv2d_workspace", "gemm_conv2d_f32", "gemm_conv2d_f16_f32acc", "gemm_conv2d_bf16_f32acc",
+           "gemm_conv2d_workspace", "gemm_conv2d_algorithm", "gemm_conv2d_f32", "gemm_conv2d_f16_f32acc", "gemm_conv2d_bf16_f32acc",
            "gemm_status_string", "gemm_variant_name")
 
 # Entry-point name stem per input format.
@@ -127,6 +127,8 @@ def load(path: str = LIB_PATH):
                 f.restype = i
         lib.gemm_conv2d_workspace.argtypes = [ctypes.POINTER(ConvParams), i, ctypes.POINTER(ctypes.c_size_t)]
         lib.gemm_conv2d_workspace.restype = i
+        lib.gemm_conv2d_algorithm.argtypes = [ctypes.POINTER(ConvParams), i, ctypes.POINTER(i)]
+        lib.gemm_conv2d_algorithm.restype = i
         for stem in _CONV_STEM.values():
             f = getattr(lib, stem)
             f.argtypes = [ctypes.POINTER(ConvParams), p, p, p, p, ctypes.c_size_t, p]
@@ -372,6 +374,19 @@ def conv2d_workspace(params: ConvParams, input_bytes: int) -> int:
     rc = load().gemm_conv2d_workspace(ctypes.byref(params), int(input_bytes), ctypes.byref(out))
     if rc != GEMM_OK:
         raise GemmError(rc, "gemm_conv2d_workspace")
+    return int(out.value)
+
+
+CONV_IM2COL, CONV_IMPLICIT = 0, 1   # gemm_conv_algorithm
+
+
+def conv2d_algorithm(params: ConvParams, input_bytes: int) -> int:
+    """The path gemm_conv2d_* takes: CONV_IM2COL or CONV_IMPLICIT (host
+    arithmetic; raises on bad params)."""
+    out = ctypes.c_int()
+    rc = load().gemm_conv2d_algorithm(ctypes.byref(params), int(input_bytes), ctypes.byref(out))
+    if rc != GEMM_OK:
+        raise GemmError(rc, "gemm_conv2d_algorithm")
     return int(out.value)
 
 

@@ -477,7 +477,13 @@ int conv_plan(const gemm_conv2d_params *pr, int elem_bytes, ConvPlan &cp)
         cp.splits = (int)((crsp + chunk - 1) / chunk);
     }
     cp.off_col = round_up((size_t)q.K * (size_t)crsp * elem_bytes, kWsAlign);
-    cp.off_y = cp.off_col + round_up((size_t)crsp * (size_t)npqp * elem_bytes, kWsAlign);
+    // the im2col matrix, or the implicit GEMM's padded copy of x
+    size_t col_bytes = (size_t)crsp * (size_t)npqp * elem_bytes;
+    if (dgor::conv_igemm_vec_applies(cp.cv, elem_bytes)) {
+        const size_t xp_bytes = ((size_t)dgor::conv_padded_input_elems(cp.cv) + 8) * 2;
+        col_bytes = col_bytes > xp_bytes ? col_bytes : xp_bytes;
+    }
+    cp.off_y = cp.off_col + round_up(col_bytes, kWsAlign);
     cp.split_stride = round_up((size_t)q.K * (size_t)npqp * 4, kWsAlign) / 4;
     cp.bytes = cp.off_y + (size_t)cp.splits * cp.split_stride * 4;
     return GEMM_OK;
@@ -515,8 +521,8 @@ int run_conv(In in, const gemm_conv2d_params *pr, const void *x, const void *w, 
         if (!w_direct &&
             dgor::launch_conv_prepare(cv, eb, x, w, base, nullptr, cp.crsp, cp.npqp, s) != hipSuccess)
             return GEMM_ERR_LAUNCH;
-        return dgor::launch_conv_igemm(cv, in == In::BF16, x, wp, y, cp.crsp, s) == hipSuccess ? GEMM_OK
-                                                                                               : GEMM_ERR_LAUNCH;
+        return dgor::launch_conv_igemm(cv, in == In::BF16, x, wp, y, cp.crsp, col, s) == hipSuccess
+                   ? GEMM_OK : GEMM_ERR_LAUNCH;
     }
     if (dgor::launch_conv_prepare(cv, eb, x, w, w_direct ? nullptr : base, col, cp.crsp, cp.npqp, s) !=
         hipSuccess)
@@ -659,6 +665,17 @@ int gemm_conv2d_workspace(const gemm_conv2d_params *params, int input_bytes, siz
     const int rc = conv_plan(params, input_bytes, cp);
     if (rc == GEMM_OK)
         *bytes = cp.bytes;
+    return rc;
+}
+
+int gemm_conv2d_algorithm(const gemm_conv2d_params *params, int input_bytes, int *algorithm)
+{
+    if (!algorithm)
+        return GEMM_ERR_NULL_PTR;
+    ConvPlan cp;
+    const int rc = conv_plan(params, input_bytes, cp);
+    if (rc == GEMM_OK)
+        *algorithm = dgor::conv_igemm_applies(cp.cv, input_bytes) ? GEMM_CONV_IMPLICIT : GEMM_CONV_IM2COL;
     return rc;
 }
 

@@ -91,10 +91,15 @@ hipError_t launch_conv_output(const Conv2d &cv, const float *yp, float *y, int n
                               size_t split_stride, hipStream_t stream);
 // The implicit-GEMM convolution for 16-bit inputs (no im2col matrix): taken
 // when its 128-filter x 256-pixel tiles number at least 256.  wa is K x CRSp
-// with 16-byte aligned rows; y is written directly.
+// with 16-byte aligned rows; y is written directly.  With stride 1 along w
+// and Q a multiple of 4 it gathers with 12-byte loads from a zero-padded
+// copy of x that it first writes to xp (conv_padded_input_elems elements,
+// plus 8 of slack that are read but never used; xp 4-byte aligned).
 bool conv_igemm_applies(const Conv2d &cv, int elem_bytes);
+bool conv_igemm_vec_applies(const Conv2d &cv, int elem_bytes);
+long long conv_padded_input_elems(const Conv2d &cv);
 hipError_t launch_conv_igemm(const Conv2d &cv, bool bf16, const void *x, const void *wa, float *y, int crsp,
-                             hipStream_t stream);
+                             void *xp, hipStream_t stream);
 hipError_t launch_naive_8bit(const Problem &p, int fmt, hipStream_t stream);
 
 // The arguments of the ring kernels for a plain row-major product.

@@ -298,6 +298,209 @@ __global__ __launch_bounds__(256) void conv_igemm(const uint16_t *__restrict__ x
     }
 }
 
+// Zero-padded copy of x for the vector gather: xp is N x C x Hp x Wp with
+// Hp = H + 2 ph and Wp = W + 2 pw, x at rows ph.., columns pw.., zeros
+// around it.  One wavefront per row of xp, its lanes along the row.
+__global__ __launch_bounds__(256) void pad_input(const uint16_t *__restrict__ x, uint16_t *__restrict__ xp, Conv2d cv,
+                                                 int Hp, int Wp, int rows)
+{
+    const int lane = threadIdx.x & 63;
+    for (int row = blockIdx.x * 4 + (int)(threadIdx.x >> 6); row < rows; row += gridDim.x * 4) {
+        const int nc = row / Hp, h = row - nc * Hp - cv.ph;
+        const bool hv = (unsigned)h < (unsigned)cv.H;
+        const size_t src_row = hv ? ((size_t)nc * cv.H + h) * cv.W : 0;
+        uint16_t *dst = xp + (size_t)row * Wp;
+        for (int c = lane; c < Wp; c += 64) {
+            const int w = c - cv.pw;
+            dst[c] = hv && (unsigned)w < (unsigned)cv.W ? x[src_row + w] : (uint16_t)0;
+        }
+    }
+}
+
+// Implicit GEMM with a vector gather, for stride 1 along w and Q a multiple
+// of 4: the four pixels j, j + 1, j + 2, j + 3 (j a multiple of 4) then sit
+// in one output row and read four adjacent elements of the padded input for
+// every tap, so one 12-byte load at the even element at or below the first
+// (then shifted by 0 or 2 bytes) fetches them; the padding makes every tap
+// inside the copy, so no lane is masked but those past NPQ or CRS.
+// Wavefront w gathers taps 8 w .. 8 w + 7 of each 32-deep stage for all 256
+// pixels of the tile (lane l: pixels 4 l .. 4 l + 3), transposes them in
+// registers and stores, per pixel, 16 bytes (8 taps, k ascending) into slot
+// p ^ ((p >> 3) & 3) of the stage's tap-group-w block: the XOR keeps both
+// these stores (lanes 4 slots apart) and the MFMA operand reads (16
+// consecutive pixels) on distinct banks.  Tiles, A staging, the two-stage
+// pipeline and the output are those of the kernel above.
+template <bool BF16, int BM>
+__global__ __launch_bounds__(256) void conv_igemm_vec(const uint16_t *__restrict__ xp, const uint16_t *__restrict__ wa,
+                                                      float *__restrict__ y, Conv2d cv, int crsp, int tiles_m, int Hp,
+                                                      int Wp, int xp_elems)
+{
+    constexpr int BN = 256, BK = 32, ROWB = 80, FM = BM / 16, AV = BM / 64;
+    constexpr int A_BYTES = BM * ROWB, GROUP = BN * 16, STAGE = A_BYTES + 4 * GROUP;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * STAGE];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int tm = blockIdx.x % tiles_m, tn = blockIdx.x / tiles_m;
+    const int m0 = tm * BM, j0 = tn * BN;
+    const int RS = cv.R * cv.S, crs_n = cv.C * RS, PQ = cv.P * cv.Q, npq = cv.N * PQ;
+
+    constexpr uint32_t OOB = 0x80000000u;
+    const int jp = j0 + 4 * lane;   // this lane's first pixel; NPQ is a multiple of 4
+    const bool jv = jp < npq;
+    const int n = jv ? jp / PQ : 0, pq = jv ? jp - n * PQ : 0, p = pq / cv.Q, q = pq - p * cv.Q;
+    const int lane_base = (n * cv.C * Hp + p * cv.sh) * Wp + q;   // xp < 2^30 elements
+    const uint32_t lb_odd = (uint32_t)lane_base & 1u;
+    // the copy plus 8 elements of slack: a load may reach 2 elements past it
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(xp, ((long long)xp_elems + 8) * 2);
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(wa, (long long)cv.K * crsp * 2);
+    // this wavefront's next tap (c, r, s) and its index; the gather steps
+    // through 8 taps, then skips the 24 the other wavefronts take
+    int gk = 8 * wave;
+    int gc = gk / RS, gr = (gk - gc * RS) / cv.S, gs = gk - gc * RS - gr * cv.S;
+    const int skip_c = 24 / RS, skip_r = (24 - skip_c * RS) / cv.S, skip_s = 24 - skip_c * RS - skip_r * cv.S;
+    // raw 12-byte loads of the 8 taps, and the parity of each tap's offset
+    auto gather = [&](uint32_t (&dst)[8][3], uint32_t &par) __attribute__((always_inline)) {
+        uint32_t pm = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int toff = (gc * Hp + gr * cv.dh) * Wp + gs * cv.dw;
+            const bool ok = jv & (gk + e < crs_n);
+            const uint32_t off = ok ? (uint32_t)((lane_base + toff) & ~1) * 2u : OOB;
+            const auto v = __builtin_amdgcn_raw_buffer_load_b96(rx, off, 0, 0);
+            dst[e][0] = v[0];
+            dst[e][1] = v[1];
+            dst[e][2] = v[2];
+            pm |= (uint32_t)(toff & 1) << e;
+            if (++gs == cv.S) {
+                gs = 0;
+                if (++gr == cv.R) {
+                    gr = 0;
+                    ++gc;
+                }
+            }
+        }
+        gk += BK;
+        gs += skip_s;
+        if (gs >= cv.S) {
+            gs -= cv.S;
+            ++gr;
+        }
+        gr += skip_r;
+        if (gr >= cv.R) {
+            gr -= cv.R;
+            ++gc;
+        }
+        gc += skip_c;
+        par = pm;
+    };
+    auto load_a = [&](int st, uint4 (&dst)[AV]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < AV; ++i) {
+            const int u = tid + 256 * i, row = u >> 2, kq = (u & 3) * 8, kk = st * BK + kq;
+            const bool ok = (m0 + row < cv.K) & (kk < crsp);
+            const uint32_t off = ok ? (uint32_t)((m0 + row) * crsp + kk) * 2u : OOB;
+            dst[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, 0));
+        }
+    };
+    auto slot = [](int px) { return px ^ ((px >> 3) & 3); };
+    auto store = [&](int buf, const uint32_t (&rb)[8][3], uint32_t par, const uint4 (&ra)[AV])
+                     __attribute__((always_inline)) {
+        uint8_t *st = lds + buf * STAGE;
+#pragma unroll
+        for (int i = 0; i < AV; ++i) {
+            const int u = tid + 256 * i;
+            *reinterpret_cast<uint4 *>(st + (u >> 2) * ROWB + (u & 3) * 16) = ra[i];
+        }
+        // pixels (0, 1) and (2, 3) of each tap, shifted into place
+        uint32_t lo[8], hi[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t sh = ((((par >> e) & 1u) ^ lb_odd)) * 2u;
+            lo[e] = __builtin_amdgcn_alignbyte(rb[e][1], rb[e][0], sh);
+            hi[e] = __builtin_amdgcn_alignbyte(rb[e][2], rb[e][1], sh);
+        }
+        uint8_t *grp = st + A_BYTES + wave * GROUP;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t *src = i < 2 ? lo : hi;
+            const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;   // high or low halves
+            uint32_t v[4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+                v[m] = __builtin_amdgcn_perm(src[2 * m + 1], src[2 * m], sel);   // taps 2m, 2m + 1
+            *reinterpret_cast<uint4 *>(grp + slot(4 * lane + i) * 16) = make_uint4(v[0], v[1], v[2], v[3]);
+        }
+    };
+
+    const int g = lane >> 4, s16 = lane & 15;
+    floatx4 acc[FM][4];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                asm("v_accvgpr_write_b32 %0, 0" : "=a"(acc[i][jb][r]));
+    auto compute = [&](int buf) __attribute__((always_inline)) {
+        const uint8_t *st = lds + buf * STAGE;
+        uint4 a[FM], b[4];
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+            a[i] = *reinterpret_cast<const uint4 *>(st + (16 * i + s16) * ROWB + 16 * g);
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb)
+            b[jb] = *reinterpret_cast<const uint4 *>(st + A_BYTES + g * GROUP + slot(64 * wave + 16 * jb + s16) * 16);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int jb = 0; jb < 4; ++jb)
+                acc[i][jb] = igemm_mma<BF16>(a[i], b[jb], acc[i][jb]);
+    };
+
+    const int steps = (crsp + BK - 1) / BK;
+    uint32_t rb[2][8][3], par[2];
+    uint4 ra[2][AV];
+    gather(rb[0], par[0]);
+    load_a(0, ra[0]);
+    gather(rb[1], par[1]);   // past the last stage every tap is past CRS
+    load_a(1, ra[1]);
+    store(0, rb[0], par[0], ra[0]);
+    __syncthreads();
+    auto stage = [&](int t, auto cur_c) __attribute__((always_inline)) {
+        constexpr int cur = decltype(cur_c)::value;
+        gather(rb[cur], par[cur]);   // stage t + 2
+        load_a(t + 2, ra[cur]);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(cur);
+        __builtin_amdgcn_sched_barrier(0);
+        if (t + 1 < steps)
+            store(cur ^ 1, rb[cur ^ 1], par[cur ^ 1], ra[cur ^ 1]);
+        __syncthreads();
+    };
+    for (int t = 0; t < steps; t += 2) {
+        stage(t, std::integral_constant<int, 0>{});
+        if (t + 1 < steps)
+            stage(t + 1, std::integral_constant<int, 1>{});
+    }
+
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb) {
+        const int jo = j0 + 64 * wave + 16 * jb + s16;
+        if (jo >= npq)
+            continue;
+        const int no = jo / PQ, pqo = jo - no * PQ;
+        float *yo = y + (size_t)no * cv.K * PQ + pqo;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int k = m0 + 16 * i + 4 * g + r;
+                if (k < cv.K)
+                    yo[(size_t)k * PQ] = acc[i][jb][r];
+            }
+    }
+}
+
 unsigned blocks_for(size_t n)
 {
     const size_t b = (n + 255) / 256;
@@ -342,29 +545,52 @@ bool conv_igemm_applies(const Conv2d &cv, int elem_bytes)
            (long long)cv.K * cv.C * cv.R * cv.S < (1LL << 29);
 }
 
-hipError_t launch_conv_igemm(const Conv2d &cv, bool bf16, const void *x, const void *wa, float *y, int crsp,
-                             hipStream_t s)
+long long conv_padded_input_elems(const Conv2d &cv)
+{
+    return (long long)cv.N * cv.C * (cv.H + 2LL * cv.ph) * (cv.W + 2LL * cv.pw);
+}
+
+bool conv_igemm_vec_applies(const Conv2d &cv, int elem_bytes)
+{
+    return conv_igemm_applies(cv, elem_bytes) && cv.sw == 1 && cv.Q % 4 == 0 &&
+           conv_padded_input_elems(cv) + 8 < (1LL << 30);
+}
+
+namespace {
+template <bool BF16>
+hipError_t launch_igemm_t(const Conv2d &cv, const void *x, const void *wa, float *y, int crsp, void *xp,
+                          hipStream_t s)
 {
     const long long npq = (long long)cv.N * cv.P * cv.Q;
-    const int tn = (int)((npq + 255) / 256);
-    if (cv.K <= 64) {
-        const dim3 grid((unsigned)(((cv.K + 63) / 64) * tn));
-        if (bf16)
-            hipLaunchKernelGGL((conv_igemm<true, 64>), grid, dim3(256), 0, s, (const uint16_t *)x,
-                               (const uint16_t *)wa, y, cv, crsp, (cv.K + 63) / 64);
+    const int tn = (int)((npq + 255) / 256), bm = cv.K <= 64 ? 64 : 128, tiles_m = (cv.K + bm - 1) / bm;
+    const dim3 grid((unsigned)(tiles_m * tn));
+    if (conv_igemm_vec_applies(cv, 2)) {
+        const int Hp = cv.H + 2 * cv.ph, Wp = cv.W + 2 * cv.pw, rows = cv.N * cv.C * Hp;
+        const int blocks = (rows + 3) / 4 < 262144 ? (rows + 3) / 4 : 262144;
+        hipLaunchKernelGGL(pad_input, dim3((unsigned)blocks), dim3(256), 0, s, (const uint16_t *)x, (uint16_t *)xp,
+                           cv, Hp, Wp, rows);
+        const int elems = (int)conv_padded_input_elems(cv);
+        if (bm == 64)
+            hipLaunchKernelGGL((conv_igemm_vec<BF16, 64>), grid, dim3(256), 0, s, (const uint16_t *)xp,
+                               (const uint16_t *)wa, y, cv, crsp, tiles_m, Hp, Wp, elems);
         else
-            hipLaunchKernelGGL((conv_igemm<false, 64>), grid, dim3(256), 0, s, (const uint16_t *)x,
-                               (const uint16_t *)wa, y, cv, crsp, (cv.K + 63) / 64);
+            hipLaunchKernelGGL((conv_igemm_vec<BF16, 128>), grid, dim3(256), 0, s, (const uint16_t *)xp,
+                               (const uint16_t *)wa, y, cv, crsp, tiles_m, Hp, Wp, elems);
+    } else if (bm == 64) {
+        hipLaunchKernelGGL((conv_igemm<BF16, 64>), grid, dim3(256), 0, s, (const uint16_t *)x, (const uint16_t *)wa,
+                           y, cv, crsp, tiles_m);
     } else {
-        const dim3 grid((unsigned)(((cv.K + 127) / 128) * tn));
-        if (bf16)
-            hipLaunchKernelGGL((conv_igemm<true, 128>), grid, dim3(256), 0, s, (const uint16_t *)x,
-                               (const uint16_t *)wa, y, cv, crsp, (cv.K + 127) / 128);
-        else
-            hipLaunchKernelGGL((conv_igemm<false, 128>), grid, dim3(256), 0, s, (const uint16_t *)x,
-                               (const uint16_t *)wa, y, cv, crsp, (cv.K + 127) / 128);
+        hipLaunchKernelGGL((conv_igemm<BF16, 128>), grid, dim3(256), 0, s, (const uint16_t *)x,
+                           (const uint16_t *)wa, y, cv, crsp, tiles_m);
     }
     return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_conv_igemm(const Conv2d &cv, bool bf16, const void *x, const void *wa, float *y, int crsp, void *xp,
+                             hipStream_t s)
+{
+    return bf16 ? launch_igemm_t<true>(cv, x, wa, y, crsp, xp, s) : launch_igemm_t<false>(cv, x, wa, y, crsp, xp, s);
 }
 
 hipError_t launch_conv_output(const Conv2d &cv, const float *yp, float *y, int npqp, int splits,

@@ -249,9 +249,19 @@ int gemm_bf16_f32acc_ex(int opA, int opB, int M, int N, int K, float alpha,
  *       * w[k][c][r][s],  input positions outside the image contributing 0.
  * Products are exact and summed in FP32 by the GEMM kernels (16-bit inputs:
  * FP32 accumulation and output, as gemm_f16_f32acc / gemm_bf16_f32acc).
+ * 16-bit layers with at least 256 tiles of 128 filters x 256 output pixels
+ * (ceil(K / 128) * ceil(N P Q / 256) >= 256) take an implicit GEMM instead:
+ * one kernel gathers the patches from x straight into on-chip memory, sums
+ * each output over c, r, s in 32-deep steps and writes y.  The workspace then
+ * holds the padded weights, only when C R S is not a multiple of 8 or w is
+ * not 16-byte aligned, and, with stride_w 1 and Q a multiple of 4, a
+ * zero-padded copy of x (N x C x (H + 2 pad_h) x (W + 2 pad_w), in the im2col
+ * matrix's place, which is made at least that large) that the gather reads
+ * with wide loads.  gemm_conv2d_algorithm reports the path.
  * The library allocates nothing: the caller passes a device workspace of at
  * least the size gemm_conv2d_workspace reports.  It holds the padded weights
- * (K x CRSp), the im2col matrix (CRSp x NPQp) and the GEMM result
+ * (K x CRSp), the im2col matrix (CRSp x NPQp, or the padded copy of x when
+ * that is larger and the implicit GEMM reads one) and the GEMM result
  * (K x NPQp, FP32), where CRS = C R S and NPQ = N P Q are rounded up to
  * multiples of 8.  When K >= 192 and CRSp >= 64 the GEMM is split over k into chunks of
  * a multiple of 64 (at least 64) until its 256 x 256 tiles times the splits
@@ -277,6 +287,13 @@ typedef struct {
  * size (4 for gemm_conv2d_f32, 2 for the 16-bit forms), in *bytes.  Host
  * arithmetic only.  Errors as the convolution entry points. */
 int gemm_conv2d_workspace(const gemm_conv2d_params *params, int input_bytes, size_t *bytes);
+
+/* Which path a convolution with these parameters and input element size
+ * takes, in *algorithm: GEMM_CONV_IM2COL (im2col matrix, then the GEMM
+ * kernels) or GEMM_CONV_IMPLICIT (the implicit GEMM; 16-bit inputs only).
+ * Host arithmetic only.  Errors as gemm_conv2d_workspace. */
+typedef enum { GEMM_CONV_IM2COL = 0, GEMM_CONV_IMPLICIT = 1 } gemm_conv_algorithm;
+int gemm_conv2d_algorithm(const gemm_conv2d_params *params, int input_bytes, int *algorithm);
 
 int gemm_conv2d_f32(const gemm_conv2d_params *params, const float *x, const float *w, float *y,
                     void *workspace, size_t workspace_bytes, void *stream);

@@ -290,6 +290,12 @@ def test_conv2d_workspace_layout_and_validation():
     # CRS 27 rounds up to 32 (below one chunk: the planner's tiles, no split)
     p = cp(2, 3, 224, 224, 64, 3, 3, (2, 2), (1, 1))
     assert dg.conv2d_workspace(p, 2) == r(64 * 32 * 2) + r(32 * 25088 * 2) + r(64 * 25088 * 4)
+    # a padded 1 x 1 layer on the implicit GEMM's vector gather: the padded
+    # copy of x (16 x 8 x 64 x 64, plus 8 elements) outgrows the im2col matrix
+    p = cp(16, 8, 62, 62, 128, 1, 1, (1, 1), (1, 1))
+    assert dg.conv2d_algorithm(p, 2) == dg.CONV_IMPLICIT
+    assert dg.conv2d_workspace(p, 2) == r(128 * 8 * 2) + r((16 * 8 * 64 * 64 + 8) * 2) + r(128 * 65536 * 4)
+    assert dg.conv2d_workspace(p, 4) == r(128 * 8 * 4) + r(8 * 65536 * 4) + r(128 * 65536 * 4)
     # a 7 x 7 stem with 256 filters: CRS 147 -> 152, 98 tiles -> 2 chunks of 128 and 24
     p = cp(2, 3, 224, 224, 256, 7, 7, (2, 2), (3, 3))
     assert _conv_splits(256, 152, 25088) == 2
@@ -305,6 +311,25 @@ def test_conv2d_workspace_layout_and_validation():
         dg.conv2d_workspace(cp(1, 1, 4, 4, 1, 1, 1), 3)
     lib = binding.load()
     assert lib.gemm_conv2d_workspace(None, 4, None) == binding.GEMM_ERR_NULL_PTR
+
+
+def test_conv2d_algorithm_follows_the_tile_count():
+    """16-bit layers with at least 256 implicit-GEMM tiles (128 filters x 256
+    output pixels) take the implicit GEMM; FP32 and smaller layers im2col."""
+    cp = binding.conv_params
+    alg = dg.conv2d_algorithm
+    p56 = cp(32, 64, 56, 56, 64, 3, 3, (1, 1), (1, 1))          # 392 tiles
+    p14 = cp(32, 256, 14, 14, 256, 3, 3, (1, 1), (1, 1))        # 2 x 25 tiles
+    assert alg(p56, 2) == dg.CONV_IMPLICIT and alg(p56, 4) == dg.CONV_IM2COL
+    assert alg(p14, 2) == dg.CONV_IM2COL
+    assert alg(cp(16, 4, 64, 64, 128, 1, 1), 2) == dg.CONV_IMPLICIT    # NPQ 65536: 256 tiles
+    assert alg(cp(15, 4, 64, 68, 128, 1, 1), 2) == dg.CONV_IM2COL      # NPQ 65280: 255 tiles
+    assert alg(cp(15, 4, 64, 68, 129, 1, 1), 2) == dg.CONV_IMPLICIT    # 2 x 255 tiles
+    assert alg(cp(16, 0, 64, 64, 128, 1, 1), 2) == dg.CONV_IM2COL      # no channels
+    with pytest.raises(dg.GemmError) as e:
+        alg(cp(1, 1, 4, 4, 1, 0, 1), 2)
+    assert e.value.status == binding.GEMM_ERR_INVALID_DIM
+    assert binding.load().gemm_conv2d_algorithm(None, 2, None) == binding.GEMM_ERR_NULL_PTR
 
 
 def test_conv2d_entry_points_validate_before_touching_a_device():

@@ -111,17 +111,24 @@ def test_conv2d_layers(fmt, case):
 
 
 # 16-bit layers whose implicit-GEMM tiles (128 filters x 256 pixels) number
-# at least 256, so they take the implicit-GEMM kernel (no im2col matrix):
+# at least 256, so they take the implicit-GEMM kernels (no im2col matrix):
 # BM = 64 and 128 (K <= 64 and K > 64, ragged), C R S a multiple of 8 (W used
 # as it is) and not (padded copy), stride, dilation and a 1 x 1 filter, and
-# NPQ not a multiple of 256.  Few channels keep the oracle quick.
+# NPQ not a multiple of 256.  Stride 1 along w with Q a multiple of 4 takes
+# the vector gather from the padded copy of x (marked vec), the rest the
+# element gather.  Few channels keep the oracle quick.
 IGEMM = [
-    (32, 8, 56, 56, 16, 3, 3, (1, 1), (1, 1), (1, 1)),      # CRS 72, K 16
-    (30, 3, 58, 57, 40, 3, 3, (1, 1), (1, 1), (1, 1)),      # CRS 27 (padded), NPQ 99180
-    (16, 16, 66, 66, 200, 3, 3, (1, 1), (1, 1), (1, 1)),    # K 200: two 128-filter tiles
+    (32, 8, 56, 56, 16, 3, 3, (1, 1), (1, 1), (1, 1)),      # vec, CRS 72, K 16
+    (30, 3, 58, 57, 40, 3, 3, (1, 1), (1, 1), (1, 1)),      # Q 57: CRS 27 (padded), NPQ 99180
+    (16, 16, 66, 66, 200, 3, 3, (1, 1), (1, 1), (1, 1)),    # Q 66: K 200, two 128-filter tiles
     (16, 8, 130, 130, 24, 5, 5, (2, 2), (2, 2), (1, 1)),    # stride 2, 5 x 5
-    (8, 4, 128, 128, 33, 3, 3, (1, 1), (2, 2), (2, 2)),     # dilation 2
-    (64, 32, 32, 32, 64, 1, 1, (1, 1), (0, 0), (1, 1)),     # 1 x 1, CRS 32
+    (8, 4, 128, 128, 33, 3, 3, (1, 1), (2, 2), (2, 2)),     # vec, dilation 2
+    (64, 32, 32, 32, 64, 1, 1, (1, 1), (0, 0), (1, 1)),     # vec, 1 x 1, CRS 32
+    (16, 3, 64, 64, 96, 3, 3, (1, 1), (1, 1), (1, 1)),      # vec, K 96 on the 128 tile, CRS 27
+    (16, 4, 130, 64, 48, 3, 3, (2, 1), (1, 1), (1, 1)),     # vec, stride 2 along h only
+    (16, 4, 64, 63, 40, 2, 2, (1, 1), (1, 1), (1, 1)),      # vec, odd W: odd padded rows
+    (16, 8, 64, 64, 130, 3, 3, (1, 1), (1, 1), (1, 1)),     # vec, K 130: a 2-filter second tile
+    (16, 8, 62, 62, 128, 1, 1, (1, 1), (1, 1), (1, 1)),     # vec, padded copy above the im2col size
 ]
 
 
@@ -129,9 +136,8 @@ IGEMM = [
 @pytest.mark.parametrize("case", IGEMM, ids=lambda c: "x".join(map(str, c[:7])))
 def test_conv2d_implicit_gemm_layers(fmt, case):
     N, C, H, W, K, R, S, st, pd, dl = case
-    P = (H + 2 * pd[0] - dl[0] * (R - 1) - 1) // st[0] + 1
-    Q = (W + 2 * pd[1] - dl[1] * (S - 1) - 1) // st[1] + 1
-    assert -(-K // 128) * -(-(N * P * Q) // 256) >= 256   # the implicit-GEMM rule
+    prm = binding.conv_params(N, C, H, W, K, R, S, st, pd, dl)
+    assert dg.conv2d_algorithm(prm, 2) == dg.CONV_IMPLICIT
     _case(fmt, case, 5500, True)
     _case(fmt, case, 5600, False)
 
