@@ -93,8 +93,9 @@ hipError_t launch_conv_output(const Conv2d &cv, const float *yp, float *y, int n
 // when its 128-filter x 256-pixel tiles number at least 256.  wa is K x CRSp
 // with 16-byte aligned rows; y is written directly.  With stride 1 along w
 // and Q a multiple of 4 it gathers with 12-byte loads from a zero-padded
-// copy of x that it first writes to xp (conv_padded_input_elems elements,
-// plus 8 of slack that are read but never used; xp 4-byte aligned).
+// copy of x that it first writes to xp (N x C x (H + 2 ph) x (W + 2 pw
+// rounded up to a multiple of 8): conv_padded_input_elems elements, plus 8
+// of slack that are read but never used; xp 16-byte aligned).
 bool conv_igemm_applies(const Conv2d &cv, int elem_bytes);
 bool conv_igemm_vec_applies(const Conv2d &cv, int elem_bytes);
 long long conv_padded_input_elems(const Conv2d &cv);

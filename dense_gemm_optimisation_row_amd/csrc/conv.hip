@@ -299,21 +299,30 @@ __global__ __launch_bounds__(256) void conv_igemm(const uint16_t *__restrict__ x
 }
 
 // Zero-padded copy of x for the vector gather: xp is N x C x Hp x Wp with
-// Hp = H + 2 ph and Wp = W + 2 pw, x at rows ph.., columns pw.., zeros
-// around it.  One wavefront per row of xp, its lanes along the row.
+// Hp = H + 2 ph and Wp = W + 2 pw rounded up to a multiple of 8, x at rows
+// ph.., columns pw.., zeros elsewhere.  One thread per 8 consecutive
+// elements of a row of xp: eight 2-byte loads of x (a position outside the
+// image takes an out-of-range offset and reads zero) and one 16-byte store.
 __global__ __launch_bounds__(256) void pad_input(const uint16_t *__restrict__ x, uint16_t *__restrict__ xp, Conv2d cv,
-                                                 int Hp, int Wp, int rows)
+                                                 int Hp, int Wp, int chunks)
 {
-    const int lane = threadIdx.x & 63;
-    for (int row = blockIdx.x * 4 + (int)(threadIdx.x >> 6); row < rows; row += gridDim.x * 4) {
+    constexpr uint32_t OOB = 0x80000000u;
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, (long long)cv.N * cv.C * cv.H * cv.W * 2);
+    const int per_row = Wp / 8;
+    for (int ch = blockIdx.x * 256 + threadIdx.x; ch < chunks; ch += gridDim.x * 256) {
+        const int row = ch / per_row, col0 = (ch - row * per_row) * 8;
         const int nc = row / Hp, h = row - nc * Hp - cv.ph;
         const bool hv = (unsigned)h < (unsigned)cv.H;
-        const size_t src_row = hv ? ((size_t)nc * cv.H + h) * cv.W : 0;
-        uint16_t *dst = xp + (size_t)row * Wp;
-        for (int c = lane; c < Wp; c += 64) {
-            const int w = c - cv.pw;
-            dst[c] = hv && (unsigned)w < (unsigned)cv.W ? x[src_row + w] : (uint16_t)0;
+        const int base = (nc * cv.H + h) * cv.W + col0 - cv.pw;   // x < 2^30 elements
+        uint32_t v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const bool ok = hv & ((unsigned)(col0 + e - cv.pw) < (unsigned)cv.W);
+            v[e] = __builtin_amdgcn_raw_buffer_load_b16(rx, ok ? (uint32_t)(base + e) * 2u : OOB, 0, 0);
         }
+        *reinterpret_cast<uint4 *>(xp + (size_t)ch * 8) =
+            make_uint4((v[0] & 0xffffu) | (v[1] << 16), (v[2] & 0xffffu) | (v[3] << 16),
+                       (v[4] & 0xffffu) | (v[5] << 16), (v[6] & 0xffffu) | (v[7] << 16));
     }
 }
 
@@ -468,7 +477,7 @@ __global__ __launch_bounds__(256) void conv_igemm_vec(const uint16_t *__restrict
     __syncthreads();
     auto stage = [&](int t, auto cur_c) __attribute__((always_inline)) {
         constexpr int cur = decltype(cur_c)::value;
-        gather(rb[cur], par[cur]);   // stage t + 2
+        gather(rb[cur], par[cur]);
         load_a(t + 2, ra[cur]);
         __builtin_amdgcn_sched_barrier(0);
         compute(cur);
@@ -547,7 +556,7 @@ bool conv_igemm_applies(const Conv2d &cv, int elem_bytes)
 
 long long conv_padded_input_elems(const Conv2d &cv)
 {
-    return (long long)cv.N * cv.C * (cv.H + 2LL * cv.ph) * (cv.W + 2LL * cv.pw);
+    return (long long)cv.N * cv.C * (cv.H + 2LL * cv.ph) * ((cv.W + 2LL * cv.pw + 7) / 8 * 8);
 }
 
 bool conv_igemm_vec_applies(const Conv2d &cv, int elem_bytes)
@@ -565,11 +574,11 @@ hipError_t launch_igemm_t(const Conv2d &cv, const void *x, const void *wa, float
     const int tn = (int)((npq + 255) / 256), bm = cv.K <= 64 ? 64 : 128, tiles_m = (cv.K + bm - 1) / bm;
     const dim3 grid((unsigned)(tiles_m * tn));
     if (conv_igemm_vec_applies(cv, 2)) {
-        const int Hp = cv.H + 2 * cv.ph, Wp = cv.W + 2 * cv.pw, rows = cv.N * cv.C * Hp;
-        const int blocks = (rows + 3) / 4 < 262144 ? (rows + 3) / 4 : 262144;
+        const int Hp = cv.H + 2 * cv.ph, Wp = (cv.W + 2 * cv.pw + 7) / 8 * 8;
+        const int elems = (int)conv_padded_input_elems(cv), chunks = elems / 8;
+        const int blocks = (chunks + 255) / 256 < 65536 ? (chunks + 255) / 256 : 65536;
         hipLaunchKernelGGL(pad_input, dim3((unsigned)blocks), dim3(256), 0, s, (const uint16_t *)x, (uint16_t *)xp,
-                           cv, Hp, Wp, rows);
-        const int elems = (int)conv_padded_input_elems(cv);
+                           cv, Hp, Wp, chunks);
         if (bm == 64)
             hipLaunchKernelGGL((conv_igemm_vec<BF16, 64>), grid, dim3(256), 0, s, (const uint16_t *)xp,
                                (const uint16_t *)wa, y, cv, crsp, tiles_m, Hp, Wp, elems);

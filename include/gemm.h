@@ -255,7 +255,8 @@ int gemm_bf16_f32acc_ex(int opA, int opB, int M, int N, int K, float alpha,
  * each output over c, r, s in 32-deep steps and writes y.  The workspace then
  * holds the padded weights, only when C R S is not a multiple of 8 or w is
  * not 16-byte aligned, and, with stride_w 1 and Q a multiple of 4, a
- * zero-padded copy of x (N x C x (H + 2 pad_h) x (W + 2 pad_w), in the im2col
+ * zero-padded copy of x (N x C x (H + 2 pad_h) x (W + 2 pad_w rounded up to a
+ * multiple of 8), in the im2col
  * matrix's place, which is made at least that large) that the gather reads
  * with wide loads.  gemm_conv2d_algorithm reports the path.
  * The library allocates nothing: the caller passes a device workspace of at
