@@ -93,3 +93,37 @@ def test_ring_kernel_spills_nothing(ring):
         if want_agpr is not None:
             assert agpr and int(agpr.group(1)) == want_agpr, f"{sym}: accumulators not held in {want_agpr} AGPRs"
         assert "scratch_" not in body, sym
+
+
+@pytest.fixture(scope="module")
+def conv_asm(tmp_path_factory):
+    if shutil.which("hipcc") is None and not os.path.exists("/opt/rocm/bin/hipcc"):
+        pytest.skip("hipcc not available")
+    out = tmp_path_factory.mktemp("isa") / "conv.s"
+    cmd = [hipbuild.hipcc(), *hipbuild.FLAGS, "-S", "--cuda-device-only",
+           os.path.join(hipbuild.CSRC, "conv.hip"), "-o", str(out)]
+    subprocess.run(cmd, check=True, capture_output=True, text=True)
+    return out.read_text()
+
+
+@pytest.mark.parametrize("kernel", ["conv_igemm_vec", "conv_igemm"])
+def test_implicit_gemm_kernels_keep_accumulators_and_gather_as_designed(conv_asm, kernel):
+    """Both formats x both tile heights; no spills; the accumulators of BM
+    filters x 256 pixels over four wavefronts (BM values per lane) in AGPRs;
+    the vector form gathers with 12-byte loads only, the element form with
+    2-byte loads only."""
+    found = [(sym, body) for sym, body in _instances(conv_asm, kernel)
+             if kernel == "conv_igemm_vec" or "conv_igemm_vec" not in sym]
+    assert len(found) == 4
+    for sym, body in found:
+        bm = 64 if "Li64E" in sym else 128
+        priv = re.search(rf"^\s*\.set\s+{re.escape(sym)}\.private_seg_size,\s*(\d+)", conv_asm, flags=re.M)
+        agpr = re.search(rf"^\s*\.set\s+{re.escape(sym)}\.num_agpr,\s*(\d+)", conv_asm, flags=re.M)
+        assert priv and int(priv.group(1)) == 0, f"{sym}: scratch (spill) memory in use"
+        assert agpr and int(agpr.group(1)) == bm, f"{sym}: accumulators not held in {bm} AGPRs"
+        assert "scratch_" not in body, sym
+        wide, narrow = body.count("buffer_load_dwordx3"), body.count("buffer_load_ushort")
+        if kernel == "conv_igemm_vec":
+            assert wide > 0 and narrow == 0, (sym, wide, narrow)
+        else:
+            assert wide == 0 and narrow > 0, (sym, wide, narrow)
