@@ -301,28 +301,44 @@ __global__ __launch_bounds__(256) void conv_igemm(const uint16_t *__restrict__ x
 // Zero-padded copy of x for the vector gather: xp is N x C x Hp x Wp with
 // Hp = H + 2 ph and Wp = W + 2 pw rounded up to a multiple of 8, x at rows
 // ph.., columns pw.., zeros elsewhere.  One thread per 8 consecutive
-// elements of a row of xp: eight 2-byte loads of x (a position outside the
-// image takes an out-of-range offset and reads zero) and one 16-byte store.
+// elements of a row of xp, written with one 16-byte store.  A chunk that
+// lies wholly inside a row of x (all but the edges) is read with a 16-byte
+// and a 4-byte load from the even element at or below its first, shifted
+// into place; an edge chunk with eight 2-byte loads, a position outside the
+// image taking an out-of-range offset (which reads zero).
 __global__ __launch_bounds__(256) void pad_input(const uint16_t *__restrict__ x, uint16_t *__restrict__ xp, Conv2d cv,
                                                  int Hp, int Wp, int chunks)
 {
     constexpr uint32_t OOB = 0x80000000u;
-    const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, (long long)cv.N * cv.C * cv.H * cv.W * 2);
+    const int x_elems = cv.N * cv.C * cv.H * cv.W;   // < 2^30
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, (long long)x_elems * 2);
     const int per_row = Wp / 8;
     for (int ch = blockIdx.x * 256 + threadIdx.x; ch < chunks; ch += gridDim.x * 256) {
         const int row = ch / per_row, col0 = (ch - row * per_row) * 8;
-        const int nc = row / Hp, h = row - nc * Hp - cv.ph;
+        const int nc = row / Hp, h = row - nc * Hp - cv.ph, w0 = col0 - cv.pw;
         const bool hv = (unsigned)h < (unsigned)cv.H;
-        const int base = (nc * cv.H + h) * cv.W + col0 - cv.pw;   // x < 2^30 elements
-        uint32_t v[8];
+        const int first = (nc * cv.H + h) * cv.W + w0, e0 = first & ~1;
+        uint32_t o[4];
+        if (hv && w0 >= 0 && w0 + 8 <= cv.W && e0 + 10 <= x_elems) {
+            const uint4 d = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, (uint32_t)e0 * 2u, 0, 0));
+            const uint32_t d4 = __builtin_amdgcn_raw_buffer_load_b32(rx, (uint32_t)e0 * 2u + 16u, 0, 0);
+            const uint32_t sh = (uint32_t)(first - e0) * 2u;
+            o[0] = __builtin_amdgcn_alignbyte(d.y, d.x, sh);
+            o[1] = __builtin_amdgcn_alignbyte(d.z, d.y, sh);
+            o[2] = __builtin_amdgcn_alignbyte(d.w, d.z, sh);
+            o[3] = __builtin_amdgcn_alignbyte(d4, d.w, sh);
+        } else {
+            uint32_t v[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const bool ok = hv & ((unsigned)(col0 + e - cv.pw) < (unsigned)cv.W);
-            v[e] = __builtin_amdgcn_raw_buffer_load_b16(rx, ok ? (uint32_t)(base + e) * 2u : OOB, 0, 0);
+            for (int e = 0; e < 8; ++e) {
+                const bool ok = hv & ((unsigned)(w0 + e) < (unsigned)cv.W);
+                v[e] = __builtin_amdgcn_raw_buffer_load_b16(rx, ok ? (uint32_t)(first + e) * 2u : OOB, 0, 0);
+            }
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+                o[m] = (v[2 * m] & 0xffffu) | (v[2 * m + 1] << 16);
         }
-        *reinterpret_cast<uint4 *>(xp + (size_t)ch * 8) =
-            make_uint4((v[0] & 0xffffu) | (v[1] << 16), (v[2] & 0xffffu) | (v[3] << 16),
-                       (v[4] & 0xffffu) | (v[5] << 16), (v[6] & 0xffffu) | (v[7] << 16));
+        *reinterpret_cast<uint4 *>(xp + (size_t)ch * 8) = make_uint4(o[0], o[1], o[2], o[3]);
     }
 }
 
