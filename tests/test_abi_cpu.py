@@ -287,6 +287,7 @@ def test_conv2d_workspace_layout_and_validation():
     p = cp(32, 64, 56, 56, 64, 3, 3, (1, 1), (1, 1))
     assert _conv_splits(64, 576, 100352) == 1
     assert dg.conv2d_workspace(p, 2) == r(64 * 576 * 2) + r(576 * 100352 * 2) + r(64 * 100352 * 4)
+    assert dg.conv2d_workspace(p, 4) == r(64 * 576 * 4) + r(576 * 100352 * 4) + r(64 * 100352 * 4)
     # CRS 27 rounds up to 32 (below one chunk: the planner's tiles, no split)
     p = cp(2, 3, 224, 224, 64, 3, 3, (2, 2), (1, 1))
     assert dg.conv2d_workspace(p, 2) == r(64 * 32 * 2) + r(32 * 25088 * 2) + r(64 * 25088 * 4)

@@ -129,6 +129,9 @@ IGEMM = [
     (16, 4, 64, 63, 40, 2, 2, (1, 1), (1, 1), (1, 1)),      # vec, odd W: odd padded rows
     (16, 8, 64, 64, 130, 3, 3, (1, 1), (1, 1), (1, 1)),     # vec, K 130: a 2-filter second tile
     (16, 8, 62, 62, 128, 1, 1, (1, 1), (1, 1), (1, 1)),     # vec, padded copy above the im2col size
+    (16, 5, 64, 65, 40, 2, 4, (1, 1), (1, 1), (1, 1)),      # vec, S 4, odd W, 2 filter rows
+    (20, 4, 60, 61, 64, 5, 4, (1, 1), (2, 1), (1, 1)),      # vec, S 4, 5 filter rows, pad (2, 1)
+    (16, 6, 66, 65, 64, 3, 4, (1, 1), (1, 1), (2, 1)),      # vec, S 4, dilation 2 along h
 ]
 
 
@@ -174,3 +177,29 @@ def test_conv2d_workspace_errors_on_the_gpu():
     rc = binding.raw_conv2d("f32", p, x.data_ptr(), w.data_ptr(), y.data_ptr(), ws.data_ptr(), need, None)
     torch.cuda.synchronize()
     assert rc == binding.GEMM_OK and torch.all(y == 18.0).item()
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+def test_conv2d_implicit_gemm_inf_reaches_only_its_outputs(fmt):
+    """An infinite input element on an implicit-GEMM layer (vector gather:
+    the wide loads also fetch elements outside each pixel's taps, which must
+    never enter a product) makes exactly the outputs whose receptive field
+    covers it infinite, as in the direct convolution; every other output
+    stays finite and exact (small-integer inputs, positive weights)."""
+    case = (32, 8, 56, 56, 16, 3, 3, (1, 1), (1, 1), (1, 1))
+    N, C, H, W, K, R, S, st, pd, dl = case
+    assert dg.conv2d_algorithm(binding.conv_params(N, C, H, W, K, R, S, st, pd, dl), 2) == dg.CONV_IMPLICIT
+    say("conv inf", fmt, case)
+    x = draw(fmt, (N, C, H, W), 5700, "int").copy()
+    vals = np.random.default_rng(5701).integers(1, 5, (K, C, R, S)).astype(np.float32)
+    # weights 1..4 (bfloat16: the top half of the binary32 bits, exact here)
+    w = vals.astype(np.float16) if fmt == "f16" else (vals.view(np.uint32) >> 16).astype(np.uint16)
+    inf = np.float16(np.inf) if fmt == "f16" else np.uint16(0x7F80)
+    x[3, 5, 20, 30] = inf
+    x[7, 0, 0, 0] = inf        # the first element of an image: a top-left corner
+    ref = oracle.conv2d(fmt, x, w, st, pd, dl).astype(np.float64)
+    got = run(fmt, x, w, st, pd, dl)
+    assert np.isposinf(ref).sum() > 0
+    assert np.array_equal(np.isposinf(got), np.isposinf(ref)) and not np.isnan(got).any()
+    fin = np.isfinite(ref)
+    assert np.array_equal(got[fin], ref[fin])
