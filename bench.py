@@ -26,6 +26,12 @@ and the convolution workloads (im2col + GEMM) under "conv_workloads";
 --conv-only times just the latter.
 --copy-calibration runs a plain device-to-device copy of known size first;
 used only by the hardware-counter runs that calibrate HBM byte counts.
+
+After the timed region each headline kernel (and the whole step) is also run
+back to back for a couple of seconds ("sustained") while a child process
+samples the GPU's clock and socket power through the amdsmi library; the
+medians go into "sustained" (the clock a power-capped kernel settles at is
+what its throughput follows).  --no-sustained skips this.
 """
 from __future__ import annotations
 
@@ -125,7 +131,14 @@ def main() -> int:
                     help="skip timing the smaller parity workloads after the main run")
     ap.add_argument("--conv-only", action="store_true",
                     help="time only the convolution workloads (for kernel traces of the im2col path)")
+    ap.add_argument("--no-sustained", action="store_true",
+                    help="skip the sustained runs with clock and power sampling")
+    ap.add_argument("--sustained-seconds", type=float, default=2.0)
+    ap.add_argument("--smi-sampler", type=float, default=0.0, help=argparse.SUPPRESS)
     args = ap.parse_args()
+
+    if args.smi_sampler > 0:
+        return smi_sampler(args.smi_sampler)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -250,6 +263,13 @@ def main() -> int:
         out["all_workloads"] = all_workloads(dg, inputs, torch, dev, stream, dev_in, wl)
         out["conv_workloads"] = conv_workloads(dg, inputs, torch, dev, stream)
 
+    if not args.no_sustained:
+        calls = {k: (lambda k=k: call(k)) for k in kinds}
+        if len(kinds) > 1:
+            calls["step"] = lambda: [call(k) for k in kinds]
+        out["sustained"] = sustained(calls, {k: wl[k].flops for k in kinds} | (
+            {"step": flops_step} if len(kinds) > 1 else {}), torch, args.sustained_seconds)
+
     if args.ladder:
         out["ladder"] = ladder(dg, inputs, torch, dev, stream)
 
@@ -295,8 +315,15 @@ def all_workloads(dg, inputs, torch, dev, stream, dev_in, wl):
         ms = _time_calls(lambda: f(a, b, c, stream), torch, stream, reps)
         tf = w.flops / (ms * 1e-3) / 1e12
         p = dg.plan(kind, w.M, w.N, w.K)
+        # algorithmic bytes: each input read once, C (4-byte elements) written once
+        nbytes = (w.M * w.K + w.K * w.N) * a.element_size() + 4 * w.M * w.N
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        # the roofline's bound: HBM when the arithmetic intensity is below the ridge
+        bound = "hbm" if w.flops / nbytes < PEAK_TFLOPS[kind] * 1e12 / (HBM_PEAK_GBS * 1e9) else "mfma"
         res[name] = {"M": w.M, "N": w.N, "K": w.K, "dtype": w.dtype, "ms": round(ms, 5),
                      "tflops": round(tf, 3), "frac_of_peak": round(tf / PEAK_TFLOPS[kind], 4),
+                     "algorithmic_bytes": nbytes, "achieved_gbs": round(gbs, 1),
+                     "frac_of_hbm": round(gbs / HBM_PEAK_GBS, 4), "bound": bound,
                      "kernel": dg.variant_name(p["variant"]), "tile": [p["tile_m"], p["tile_n"]]}
     return res
 
@@ -360,39 +387,163 @@ def ladder(dg, inputs, torch, dev, stream):
     return res
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(kinds, wl, seconds):
-    """The oracle as it stands, on a bounded row sample of the same inputs."""
+    """The oracle as it stands, on the host's cores: every workload of the
+    step in full when that fits about ``seconds`` of host time (it does for
+    the default step: about 1.5 s for FP32 4096^3 and 10 s for FP16-in
+    8192^3 on 16 threads), else on a leading block of rows; plus one thread
+    on FP32 1024^3 for a per-core figure."""
     import numpy as np
 
     import oracle
     from dense_gemm_optimisation_row_amd import inputs
 
     threads = oracle.threads(0)
+    fns = {"f32": oracle.gemm_f32, "f16": oracle.gemm_f16, "bf16": oracle.gemm_bf16,
+           "e4m3": oracle.gemm_e4m3, "e5m2": oracle.gemm_e5m2, "i8": oracle.gemm_i8}
     rates = {}
     samples = []
-    budget = seconds / len(kinds)
+    full_s = {}
+    budget = 2.5 * seconds / len(kinds)
     for k in kinds:
         w = wl[k]
         A, B = inputs.workload_matrices(w)
-        fn = {"f32": oracle.gemm_f32, "f16": oracle.gemm_f16, "bf16": oracle.gemm_bf16,
-              "e4m3": oracle.gemm_e4m3, "e5m2": oracle.gemm_e5m2, "i8": oracle.gemm_i8}[k]
+        fn = fns[k]
         rows = max(threads, 8)
         t0 = time.perf_counter()
         fn(A[:rows], B)
         dt = time.perf_counter() - t0
-        rows2 = int(min(w.M, max(rows, rows * budget / max(dt, 1e-3))))
+        rows2 = w.M if dt * w.M / rows <= budget else int(max(rows, rows * budget / max(dt, 1e-3)))
         t0 = time.perf_counter()
         fn(A[:rows2], B)
         dt = time.perf_counter() - t0
         rates[k] = 2.0 * rows2 * w.N * w.K / dt        # flop/s
-        samples.append(f"{rows2} of {w.M} rows of {w.name} ({dt:.1f} s)")
+        if rows2 == w.M:
+            full_s[w.name] = round(dt, 3)
+            samples.append(f"all {w.M} rows of {w.name} ({dt:.1f} s)")
+        else:
+            samples.append(f"{rows2} of {w.M} rows of {w.name} ({dt:.1f} s)")
         del A, B
+    # per core: one thread on the pages' size (FP32 1024^3)
+    w1 = inputs.WORKLOADS["f32_1024"]
+    A, B = inputs.workload_matrices(w1)
+    t0 = time.perf_counter()
+    oracle.gemm_f32(A, B, nthreads=1)
+    dt1 = time.perf_counter() - t0
     step_flops = sum(wl[k].flops for k in kinds)
     step_seconds = sum(wl[k].flops / rates[k] for k in kinds)
     return {"value": round(step_flops / step_seconds / 1e12, 6), "unit": "TFLOP/s",
             "cores": threads, "kind": "oracle",
             "sample": "; ".join(samples) + " (FP64-accumulating C loop nest, OpenMP over rows)",
-            "per_workload_gflops": {wl[k].name: round(rates[k] / 1e9, 3) for k in kinds}}
+            "cpu_model": cpu_model(),
+            "step_seconds": round(step_seconds, 3),
+            "full_seconds": full_s,
+            "per_workload_gflops": {wl[k].name: round(rates[k] / 1e9, 3) for k in kinds},
+            "one_thread_f32_1024": {"seconds": round(dt1, 3), "gflops_per_core": round(w1.flops / dt1 / 1e9, 3)}}
+
+
+def smi_sampler(period: float) -> int:
+    """Child-process loop: one JSON line of GPU 0's clocks and power every
+    ``period`` seconds, read through the amdsmi library, until killed."""
+    import amdsmi
+
+    amdsmi.amdsmi_init()
+    h = amdsmi.amdsmi_get_processor_handles()[0]
+
+    def num(v):
+        return v if isinstance(v, (int, float)) else None
+
+    while True:
+        rec = {"t": time.time()}
+        try:
+            m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+            clks = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float)) and 0 < c < 10000]
+            rec["sclk_mhz"] = sum(clks) / len(clks) if clks else num(m.get("current_gfxclk"))
+            rec["power_w"] = num(m.get("current_socket_power"))
+            rec["energy"] = num(m.get("energy_accumulator"))
+            rec["ppt_acc"] = num(m.get("ppt_residency_acc"))
+            rec["acc_counter"] = num(m.get("accumulation_counter"))
+            rec["hotspot_c"] = num(m.get("temperature_hotspot"))
+        except Exception as e:   # report, keep sampling
+            rec["error"] = str(e)[:200]
+        print(json.dumps(rec), flush=True)
+        time.sleep(period)
+
+
+def sustained(calls, flops, torch, seconds):
+    """Each call run back to back for ``seconds`` while a child process samples
+    the GPU clock and socket power; returns per call the mean time per call
+    and the medians of the samples taken in the second half of the run (after
+    the clock has settled), plus the fraction of that time the power limit
+    was holding the clock down (the firmware's PPT residency counter)."""
+    import statistics
+    import subprocess
+    import threading
+
+    proc = subprocess.Popen([sys.executable, os.path.abspath(__file__), "--smi-sampler", "0.02"],
+                            stdout=subprocess.PIPE, stderr=subprocess.DEVNULL, text=True)
+    lines = []
+    first = threading.Event()
+
+    def reader():
+        for ln in proc.stdout:
+            try:
+                lines.append(json.loads(ln))
+            except ValueError:
+                continue
+            first.set()
+
+    th = threading.Thread(target=reader, daemon=True)
+    th.start()
+    res = {}
+    try:
+        if not first.wait(30.0):
+            return {"error": "amdsmi sampler produced no sample"}
+        for name, fn in calls.items():
+            fn()
+            torch.cuda.synchronize()
+            t_begin = time.time()
+            n = 0
+            t_half = None
+            while time.time() - t_begin < seconds:
+                for _ in range(10):
+                    fn()
+                n += 10
+                torch.cuda.synchronize()
+                if t_half is None and time.time() - t_begin >= seconds / 2:
+                    t_half = (time.time(), n)
+            t_end = time.time()
+            ms = (t_end - t_half[0]) / max(1, n - t_half[1]) * 1e3
+            win = [r for r in lines if t_half[0] <= r["t"] <= t_end and "error" not in r]
+            rec = {"ms_per_call": round(ms, 5), "tflops": round(flops[name] / (ms * 1e-3) / 1e12, 2),
+                   "samples": len(win)}
+            vals = lambda key: [r[key] for r in win if r.get(key) is not None]
+            if vals("sclk_mhz"):
+                rec["sclk_mhz"] = round(statistics.median(vals("sclk_mhz")), 1)
+            if vals("power_w"):
+                rec["socket_power_w"] = round(statistics.median(vals("power_w")), 1)
+            ok = [r for r in win if r.get("ppt_acc") is not None and r.get("acc_counter") is not None]
+            if len(ok) >= 2 and ok[-1]["acc_counter"] > ok[0]["acc_counter"]:
+                rec["power_limited_frac"] = round((ok[-1]["ppt_acc"] - ok[0]["ppt_acc"]) /
+                                                  (ok[-1]["acc_counter"] - ok[0]["acc_counter"]), 3)
+            hs = vals("hotspot_c")
+            if hs:
+                rec["hotspot_c"] = max(hs)
+            res[name] = rec
+    finally:
+        proc.kill()
+        proc.wait()
+    return res
 
 
 if __name__ == "__main__":

@@ -6,9 +6,10 @@ Bars (elementwise, FP32 output):
   * binary16 inputs: |C - C_ref| <= 2e-3 sqrt(K) max|C_ref|.
 Shapes span several tiles of each kernel configuration and end in ragged
 tails in M, N and K.  The full-size workloads are checked in the launch
-configuration the benchmark times: in full where the oracle is quick, else on
-sampled elements plus an invariant over every output (C v = A (B v) for a
-random +-1 vector v, exact on integer inputs).
+configuration the benchmark times: the smaller ones in full here; the
+headline sizes (FP32 4096^3, 16-bit 8192^3) in full in test_full_gpu.py, and
+here as a quick pre-check on sampled elements plus an invariant over every
+output (C v = A (B v) for a random +-1 vector v, exact on integer inputs).
 """
 import numpy as np
 import pytest
