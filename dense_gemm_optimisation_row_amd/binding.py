@@ -221,21 +221,48 @@ def _ptr(t):
     return t.data_ptr() if t.numel() else None
 
 
+_DTYPES = {}
+
+
 def _dtypes(kind):
     """(input dtype, output dtype) of a format."""
-    import torch
-    return {"f32": (torch.float32, torch.float32), "f16": (torch.float16, torch.float32),
-            "bf16": (torch.bfloat16, torch.float32), "e4m3": (torch.float8_e4m3fn, torch.float32),
-            "e5m2": (torch.float8_e5m2, torch.float32), "i8": (torch.int8, torch.int32)}[kind]
+    if not _DTYPES:
+        import torch
+        _DTYPES.update({"f32": (torch.float32, torch.float32), "f16": (torch.float16, torch.float32),
+                        "bf16": (torch.bfloat16, torch.float32), "e4m3": (torch.float8_e4m3fn, torch.float32),
+                        "e5m2": (torch.float8_e5m2, torch.float32), "i8": (torch.int8, torch.int32)})
+    return _DTYPES[kind]
+
+
+_ENTRY_CACHE = {}
+
+
+def _entry(kind, variant):
+    """The library function of a format (automatic or forced variant), looked
+    up once."""
+    key = (kind, variant is None)
+    f = _ENTRY_CACHE.get(key)
+    if f is None:
+        f = getattr(load(), _STEM[kind] + ("" if variant is None else "_variant"))
+        _ENTRY_CACHE[key] = f
+    return f
 
 
 def _call(kind, variant, A, B, C, stream):
     import torch
     kind = kind_of(kind)
     M, N, K, C = _check(A, B, C, *_dtypes(kind))
-    with torch.cuda.device(A.device):
-        rc = raw_gemm(kind, variant, M, N, K, _ptr(A), _ptr(B), _ptr(C),
-                      _stream_handle(A.device, stream))
+    f = _entry(kind, variant)
+    args = (M, N, K, _ptr(A), _ptr(B), _ptr(C))
+    if variant is not None:
+        args = (variant,) + args
+    # the call runs on A's device: switch only when another is current (the
+    # switch costs more than a small GEMM's launch)
+    if A.device.index == torch.cuda.current_device():
+        rc = int(f(*args, _stream_handle(A.device, stream)))
+    else:
+        with torch.cuda.device(A.device):
+            rc = int(f(*args, _stream_handle(A.device, stream)))
     if rc != GEMM_OK:
         raise GemmError(rc, _STEM[kind])
     return C

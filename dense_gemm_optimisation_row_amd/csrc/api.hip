@@ -154,18 +154,29 @@ int plan_f32(int variant, int M, int N, int K, const void *A, const void *B, con
             p->vector_c = 0;
             break;
         }
-        dgor::F32NarrowPlan nw;
-        if (dgor::f32_narrow_plan(M, N, K, nw)) {
-            p->tile_m = 16 * nw.rb;
-            p->tile_n = 16 * nw.nb;
-            p->tile_k = 4 * nw.kq_len;
-            p->threads = 256 * nw.rb;
-            p->lds_stages = 1;
-            p->lds_bytes = nw.b_floats * 4;
-            p->tile_bytes = (p->tile_m * p->tile_k + p->tile_k * p->tile_n) * 4;
-            p->outputs_per_thread = p->tile_m * p->tile_n / p->threads;
+        dgor::F32SkinnyPlan nw;
+        if (dgor::f32_skinny_plan(M, N, K, B, nw)) {
+            // one workgroup per 16 rows (grid_y), all columns (tile_n: the
+            // MFMA blocks, plus 1 for a column summed on the vector ALUs) and
+            // all of K in eight runs of 16-deep slices.  LDS holds the
+            // partial sums (8 wavefronts x nb blocks x 1 KB; with the fringe
+            // column its partial sums and, when B goes to registers, B's
+            // last column) and, as one stage, the wavefronts' runs of B rows
+            // when they fit (8 x 16 KB)
+            p->tile_m = 16;
+            p->tile_n = 16 * nw.nb + (nw.fringe ? 1 : 0);
+            p->tile_k = 16 * ((K + 15) / 16);
+            p->threads = 512;
+            p->lds_stages = nw.ldsb ? 1 : 0;
+            p->lds_bytes = 8 * nw.nb * 1024 + (nw.fringe ? 4 * ((nw.ldsb ? 0 : dgor::kF32SkinnyMaxK) + 512) : 0) +
+                           32 + (nw.ldsb ? 8 * dgor::kF32SkinnyBRegion : 0);
+            p->tile_bytes = (16 * K + K * N) * 4;
+            p->outputs_per_thread = (16 * N + 511) / 512;
             p->vector_c = 0;
-            break;
+            finish(p, M, N, K);
+            p->grid_x = 1;
+            p->grid_y = nw.blocks;
+            return GEMM_OK;
         }
         const MfmaConfig &c = dgor::kF32Configs[pick_config(dgor::kF32Configs, M, N, true)];
         p->tile_m = c.bm;

@@ -178,24 +178,33 @@ inline bool f32_small_ring_applies(int tile_m, int tile_n, int N, int K, bool ve
            (long long)(K + kF32SmallDepth) * N < (1LL << 29);
 }
 
-// Tall, narrow FP32 problems (1 <= N <= 64, K <= kF32NarrowMaxK, any
-// alignment): workgroups of 16 rb rows (4 rb wavefronts), nb = ceil(N / 16)
-// column blocks of 16, four wavefronts per row block each taking kq_len of K
-// (a multiple of 16), and B's first b_floats floats (4 kq_len rows plus a
-// 64-float guard, rounded to whole 1 KB loads) in LDS.  Two row blocks per
-// workgroup when one would need more than 256 workgroups.
-constexpr int kF32NarrowMaxK = 1024;
-constexpr int kF32NarrowLdsFloats = 40960;   // 160 KB
-struct F32NarrowPlan { int nb, rb, kq_len, b_floats; };
-inline bool f32_narrow_plan(int M, int N, int K, F32NarrowPlan &n)
+// Tall, narrow FP32 problems (1 <= N <= 64, 1 <= K <= kF32SkinnyMaxK, any
+// alignment): workgroups of 16 rows and 8 wavefronts, nb MFMA blocks of 16
+// columns; with fringe (N % 16 == 1, N > 16) the last column is summed on the
+// vector ALUs instead of in a block of its own; with tail (M % 16 == 1 and at
+// least N whole row blocks) the last row is spread over workgroups 0..N-1
+// instead of getting one of its own; with ldsb (B 16-byte aligned, a
+// wavefront's run of B rows within kF32SkinnyBRegion bytes, and at most 3
+// blocks, so that the 8 regions and the partial sums fit the 160 KB of LDS)
+// each wavefront copies its rows of B into LDS, else B goes straight into
+// registers.
+constexpr int kF32SkinnyMaxK = 1024;
+constexpr int kF32SkinnyBRegion = 16384;
+struct F32SkinnyPlan { int nb, blocks; bool fringe, tail, ldsb; };
+inline bool f32_skinny_plan(int M, int N, int K, const void *B, F32SkinnyPlan &n)
 {
-    if (N < 1 || N > 64 || K < 1 || K > kF32NarrowMaxK || (long long)M * K * 4 >= (1LL << 31))
+    if (N < 1 || N > 64 || K < 1 || K > kF32SkinnyMaxK || M < 1 || (long long)M * K * 4 >= (1LL << 31))
         return false;
-    n.nb = (N + 15) / 16;
-    n.rb = (M + 15) / 16 > 256 ? 2 : 1;
-    n.kq_len = ((K + 3) / 4 + 15) / 16 * 16;
-    n.b_floats = (4 * n.kq_len * N + 64 + 255) / 256 * 256;
-    return n.b_floats <= kF32NarrowLdsFloats;
+    n.fringe = N > 16 && N % 16 == 1;
+    n.nb = n.fringe ? N / 16 : (N + 15) / 16;
+    const int full = M / 16, rem = M % 16;
+    n.tail = rem == 1 && full >= N;
+    n.blocks = full + (rem != 0 && !n.tail ? 1 : 0);
+    // the longest run of rows a wavefront takes: ceil(slices / 8) slices
+    const int run_rows = 16 * (((K + 15) / 16 + 7) / 8);
+    const int run_bytes = (run_rows * N * 4 + 1023) / 1024 * 1024;
+    n.ldsb = ((uintptr_t)B & 15) == 0 && run_bytes <= kF32SkinnyBRegion && n.nb <= 3;
+    return true;
 }
 
 // FP32 problems with both operands in 128-bit loads and at least one

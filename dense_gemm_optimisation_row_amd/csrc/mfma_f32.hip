@@ -796,140 +796,302 @@ __global__ __launch_bounds__(128 * WN) void mfma_f32_small_ring_kernel(int M, in
 }
 
 // ---------------------------------------------------------------------------
-// Tall, narrow FP32 problems (N <= 64, K <= 1024, any alignment).  Reading A
-// once is most of their time (B and C are small), so every wavefront issues
-// all of its A loads at once instead of meeting memory latency stage by
-// stage.  A workgroup takes 16 RB rows with 4 RB wavefronts: wavefront w
-// takes row block w / 4 and k in [q kq_len, (q + 1) kq_len), q = w % 4
-// (kq_len a multiple of 16), with the first 4 kq_len rows of B (zeros past K,
-// then a 64-float guard) copied whole into LDS.  The four partial sums of a
-// row block are added in LDS in order of q.  The matrix instruction is
-// v_mfma_f32_16x16x4_f32 with the k assignment of the 64 x 64 ring kernel
-// (lane l: A[l % 16][k], B[k][l % 16], k = 16 s + 4 (l / 16) + e for the
-// instructions e = 0..3 of slice s), so a lane's A values of a slice are four
-// consecutive floats of its row: one 16-byte load (rows need only 4-byte
-// alignment), or four 4-byte loads for the one unit that runs past K.
-// Column blocks past N read whatever follows in LDS and are not stored.
-template <int NB, int RB>
-__global__ __launch_bounds__(256 * RB) void mfma_f32_narrow_kernel(int M, int N, int K, int kq_len, int b_floats,
-                                                                   int b_vec, const float *__restrict__ A,
-                                                                   const float *__restrict__ B,
-                                                                   float *__restrict__ C)
+// Tall, narrow FP32 problems (N <= 64, K <= 1024, any alignment).  Their time
+// is one read of A from HBM (B and C are small), so every compute unit streams
+// its share of A from the start, and no k-loop waits on memory stage by stage.
+// A workgroup takes 16 rows, all N columns and all of K with eight wavefronts
+// (two per SIMD); wavefront w takes a contiguous run [kb, ke) of the 16-deep
+// k-slices, the runs as even as the slice count allows.  Each lane issues all
+// of its loads at once: its A values straight into registers (16-byte units,
+// four consecutive k of its row; four 4-byte loads for the one unit that runs
+// past K), from HBM; and B, which every workgroup reads whole and so stays in
+// L2, either
+//   LDSB: the wavefront's own rows kb..ke of B copied into its own 16 KB of
+//     LDS by direct global->LDS loads of whole 1 KB runs (no barrier: only
+//     the wavefront reads them), then read two floats at a time; or
+//   otherwise (B rows of a run too long for 16 KB, or B not 16-byte aligned):
+//     one load of NB adjacent floats per lane and k, straight into registers.
+// It then runs v_mfma_f32_16x16x4_f32 slice by slice as the loads land (the
+// compiler waits with vmcnt on the registers a slice needs).  The k
+// assignment is that of the 64 x 64 ring kernel: in instruction e of slice s,
+// lane l holds A[l % 16][k] and, for column block c, B[k][NB (l % 16) + c],
+// with k = kb + 16 s + 4 (l / 16) + e (column block c holds the columns
+// NB j + c, so a lane's B values of one k are adjacent).  The eight partial
+// sums of an output are added in LDS in order of w, so results do not depend
+// on timing.
+//   FRINGE (N % 16 == 1, N > 16): the last column is not given a 16-column
+//     block of its own (that block would cost as much matrix-core time as a
+//     full one); its sums are formed on the vector ALUs from the A registers.
+//   tail (M % 16 == 1 with at least N whole row blocks): the last row gets no
+//     workgroup of its own (that workgroup would share a compute unit with
+//     another and double its matrix-core time); workgroup j < N instead forms
+//     C[M - 1][j] as a dot product spread over its 512 lanes (two products a
+//     lane, a butterfly sum in each wavefront, then the eight wavefront sums
+//     in order).
+template <int NB, bool FRINGE, bool LDSB>
+__global__ __launch_bounds__(512) void mfma_f32_skinny_kernel(int M, int N, int K, int tail, const float *A,
+                                                              const float *B, float *C)
 {
-    constexpr int QMAX = kF32NarrowMaxK / 64;   // 16-deep slices per wavefront
-    __shared__ __attribute__((aligned(1024))) float lds[kF32NarrowLdsFloats];
+    constexpr int QMAX = kF32SkinnyMaxK / (16 * 8);   // slices per wavefront at most
+    constexpr int REGION = LDSB ? kF32SkinnyBRegion : 4;   // bytes of B per wavefront
+    __shared__ __attribute__((aligned(1024))) uint8_t bsh[LDSB ? 8 * REGION : 16];
+    __shared__ floatx4 part[8][NB][64];
+    __shared__ float fcol[FRINGE && !LDSB ? kF32SkinnyMaxK : 1];
+    __shared__ float fpart[FRINGE ? 8 * 64 : 1];
+    __shared__ float tpart[8];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-    const int rb = wave >> 2, q = wave & 3;
     const int r16 = lane & 15, h = lane >> 4;
-    const int m0 = blockIdx.x * 16 * RB;
+    const int m0 = blockIdx.x * 16, row = m0 + r16;
+    const int total = (K + 15) / 16;
+    const int s_lo = wave * total / 8, s_hi = (wave + 1) * total / 8;
+    const int slices = s_hi - s_lo, kb = 16 * s_lo, ke = min(K, 16 * s_hi);
     constexpr uint32_t OOB = 0x80000000u;
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, (long long)M * K * 4);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(B, (long long)K * N * 4);
+    const float *bw = reinterpret_cast<const float *>(bsh + (LDSB ? wave * REGION : 0));
 
-    // B's first b_floats floats (zeros past K N) into LDS: 1 KB a load when B
-    // is 16-byte aligned and K N a multiple of 4, else 256 bytes
-    {
+    // LDSB: rows kb..ke of B (a contiguous run of bytes, 16-byte aligned as
+    // kb is a multiple of 16 and B is 16-byte aligned) into this wavefront's
+    // region, whole 1 KB runs; past K they read zeros.  Issued first: the
+    // wait before the first read of them counts only the loads issued after.
+    if constexpr (LDSB) {
         const intx4 rsb = rsrc_words(B, (long long)K * N * 4);
-        const uint32_t base = lds_address(lds);
-        if (b_vec) {
-            for (int i = wave; i < b_floats / 256; i += 4 * RB)
-                load_to_lds(rsb, base + (uint32_t)(i * 1024), (uint32_t)(i * 1024 + lane * 16));
-        } else {
-            for (int i = wave; i < b_floats / 64; i += 4 * RB)
-                load_dword_to_lds(rsb, base + (uint32_t)(i * 256), (uint32_t)(i * 256 + lane * 4));
+        const uint32_t dst = lds_address(bsh) + (uint32_t)(wave * REGION);
+        const uint32_t src = (uint32_t)(kb * N) * 4u;
+        const int runs = ((ke - kb) * N * 4 + 1023) / 1024;
+        for (int j = 0; j < runs; ++j)
+            load_to_lds(rsb, dst + (uint32_t)(j * 1024), src + (uint32_t)(j * 1024 + lane * 16));
+    }
+    // the unit of the last slice that runs past K (K not a multiple of 4):
+    // four 4-byte loads, taken in place of that slice's (then empty) 16-byte
+    // unit when its MFMAs run (issued early, so that reading them, which the
+    // compiler may do as early as slice 0, waits for no slice's loads)
+    const int k_last = kb + 16 * (slices - 1) + 4 * h;
+    const bool cross = slices > 0 && row < M && k_last < ke && k_last + 4 > ke;
+    float x[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        x[e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+            ra, cross && k_last + e < ke ? (uint32_t)(row * K + k_last + e) * 4u : OOB, 0, 0));
+    // B's last column (FRINGE, B in registers): thread t loads k = t and t + 512
+    float fv[2] = {0.f, 0.f};
+    if (FRINGE && !LDSB) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int k = (int)threadIdx.x + 512 * i;
+            fv[i] = __uint_as_float(
+                __builtin_amdgcn_raw_buffer_load_b32(rb, k < K ? (uint32_t)(k * N + N - 1) * 4u : OOB, 0, 0));
         }
     }
-    // A[m0 + 16 rb + r16][k0 + 16 s + 4 h + e], zero outside A or past this
-    // wavefront's slices
-    const int k0 = q * kq_len, slices = kq_len / 16;
-    const int row = m0 + 16 * rb + r16;
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, (long long)M * K * 4);
+    // the tail row's products: this wavefront's k, two a lane
+    const bool tl = tail && (int)blockIdx.x < N;
+    float ta[2], tb[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int k = kb + lane + 64 * i;
+        const bool ok = tl && k < ke;
+        ta[i] = __uint_as_float(
+            __builtin_amdgcn_raw_buffer_load_b32(ra, ok ? (uint32_t)((M - 1) * K + k) * 4u : OOB, 0, 0));
+        tb[i] = __uint_as_float(
+            __builtin_amdgcn_raw_buffer_load_b32(rb, ok ? (uint32_t)(k * N + blockIdx.x) * 4u : OOB, 0, 0));
+    }
+    // A (and, without LDSB, B) of every slice.  No load sits under a branch:
+    // one that did would make the compiler wait for earlier loads at the join.
+    // Loads of one NB-float group of B keep a wavefront's loads under the 63
+    // the wait counter can tell apart.
     floatx4 a[QMAX];
+    float b[LDSB ? 1 : QMAX][4][NB];
 #pragma unroll
     for (int s = 0; s < QMAX; ++s) {
-        const int k = k0 + 16 * s + 4 * h;
-        const bool live = s < slices && row < M;
-        const uint32_t off = (uint32_t)(row * K + k) * 4u;
-        a[s] = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(ra, live && k + 4 <= K ? off : OOB,
-                                                                                 0, 0));
-        if (live && k < K && k + 4 > K) {   // the unit that runs past K
+        const int k = kb + 16 * s + 4 * h;
+        const bool live = s < slices && row < M && k + 4 <= ke;
+        a[s] = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(
+                                               ra, live ? (uint32_t)(row * K + k) * 4u : OOB, 0, 0));
+        if constexpr (!LDSB) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                a[s][e] = __uint_as_float(
-                    __builtin_amdgcn_raw_buffer_load_b32(ra, k + e < K ? off + 4u * e : OOB, 0, 0));
+            for (int e = 0; e < 4; ++e) {
+                const int kk = k + e;
+                const uint32_t off = s < slices && kk < ke ? (uint32_t)(kk * N + NB * r16) * 4u : OOB;
+                if constexpr (NB == 1) {
+                    b[s][e][0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb, off, 0, 0));
+                } else if constexpr (NB == 2) {
+                    const auto v = __builtin_amdgcn_raw_buffer_load_b64(rb, off, 0, 0);
+                    b[s][e][0] = __uint_as_float(v[0]);
+                    b[s][e][1] = __uint_as_float(v[1]);
+                } else if constexpr (NB == 3) {
+                    const auto v = __builtin_amdgcn_raw_buffer_load_b96(rb, off, 0, 0);
+#pragma unroll
+                    for (int c = 0; c < 3; ++c)
+                        b[s][e][c] = __uint_as_float(v[c]);
+                } else {
+                    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0);
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        b[s][e][c] = __uint_as_float(v[c]);
+                }
+            }
         }
+        // issue the slices in order (the scheduler would otherwise group the
+        // loads by kind and leave slice 0's A among the last)
+        __builtin_amdgcn_sched_barrier(0);
     }
-    // all of them issued here, not moved next to their uses
-#pragma unroll
-    for (int s = 0; s < QMAX; ++s)
-        asm volatile("" : "+v"(a[s]));
-    // B's copy is not tracked by the compiler's counters
-    __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
-    __builtin_amdgcn_s_barrier();
+    // every load above is issued before the first MFMA: none may be sunk
+    // into the slice branches below (the memory clobber forbids moving a
+    // load past it, and reads no register, so it waits for nothing)
+    asm volatile("" ::: "memory");
+    if constexpr (LDSB) {
+        // the copies of B have landed once no more than the loads issued
+        // after them (x, tail, A) are outstanding
+        __builtin_amdgcn_s_waitcnt(wait_vmcnt(4 + 4 + QMAX));
+        asm volatile("" ::: "memory");
+    }
 
     floatx4 acc[NB];
 #pragma unroll
     for (int c = 0; c < NB; ++c)
         acc[c] = floatx4{0.f, 0.f, 0.f, 0.f};
+    // with LDSB, the last column of this lane's row over this lane's k is
+    // summed here too, from the wavefront's rows of B, beside the MFMAs
+    float f = 0.f;
 #pragma unroll
     for (int s = 0; s < QMAX; ++s) {
-        if (s < slices) {   // wave-uniform; rows past 4 kq_len are not in LDS
-            float bv[4][NB];   // the slice's B values, read before its MFMAs
+        if (s < slices) {   // wave-uniform
+            if (s == slices - 1) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
+                for (int e = 0; e < 4; ++e)
+                    a[s][e] = cross ? x[e] : a[s][e];
+            }
+            float bv[4][NB], fb[4];
 #pragma unroll
-                for (int c = 0; c < NB; ++c)
-                    bv[e][c] = lds[(k0 + 16 * s + 4 * h + e) * N + 16 * c + r16];
+            for (int e = 0; e < 4; ++e) {
+                if constexpr (LDSB) {   // rows past ke hold no copy of B
+                    const int kk = kb + 16 * s + 4 * h + e;
+#pragma unroll
+                    for (int c = 0; c < NB; ++c)
+                        bv[e][c] = kk < ke ? bw[(kk - kb) * N + NB * r16 + c] : 0.f;
+                    if constexpr (FRINGE)
+                        fb[e] = kk < ke ? bw[(kk - kb) * N + N - 1] : 0.f;
+                } else {
+#pragma unroll
+                    for (int c = 0; c < NB; ++c)
+                        bv[e][c] = b[s][e][c];
+                }
+            }
 #pragma unroll
             for (int e = 0; e < 4; ++e)
 #pragma unroll
                 for (int c = 0; c < NB; ++c)
                     acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s][e], bv[e][c], acc[c], 0, 0, 0);
+            if constexpr (FRINGE && LDSB) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    f = fmaf(a[s][e], fb[e], f);
+            }
         }
     }
-
-    // partial sums: wavefront w's block c at floats (w NB + c) 256; the four
-    // of an output block are added in order of q and stored (lane l holds
-    // rows 4 (l / 16) + r, column l % 16 of a 16 x 16 block)
-    __syncthreads();   // B is no longer read
+    if constexpr (FRINGE && LDSB)
+        fpart[wave * 64 + lane] = f;
+    // partial sums into LDS: wavefront w's block c at part[w][c]; lane l
+    // holds rows 4 (l / 16) + r of column NB (l % 16) + c
 #pragma unroll
     for (int c = 0; c < NB; ++c)
-        *reinterpret_cast<floatx4 *>(lds + (wave * NB + c) * 256 + lane * 4) = acc[c];
+        part[wave][c][lane] = acc[c];
+    if (FRINGE && !LDSB) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int k = (int)threadIdx.x + 512 * i;
+            if (k < K)
+                fcol[k] = fv[i];
+        }
+    }
+    // tail: this wavefront's sum of its products (butterfly, fixed order)
+    float tv = ta[0] * tb[0] + ta[1] * tb[1];
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1)
+        tv += __shfl_xor(tv, d);
+    if (lane == 0)
+        tpart[wave] = tv;
     __syncthreads();
-    const __amdgpu_buffer_rsrc_t rc = make_rsrc(C, (long long)M * N * 4);
-    // output block p = (row block p / NB, column block p % NB); wavefront w
-    // takes p = w, w + 4 RB, ...
+
+    if constexpr (FRINGE && !LDSB) {   // B's last column is in LDS only now
 #pragma unroll
-    for (int i = 0; i < (RB * NB + 4 * RB - 1) / (4 * RB); ++i) {
-        const int p = wave + 4 * RB * i;
-        if (p >= RB * NB)
-            break;
-        const int b = p / NB, c = p % NB, col = 16 * c + r16;
-        floatx4 v = *reinterpret_cast<const floatx4 *>(lds + ((4 * b) * NB + c) * 256 + lane * 4);
+        for (int s = 0; s < QMAX; ++s) {
+            if (s < slices) {
 #pragma unroll
-        for (int w = 1; w < 4; ++w)
-            v += *reinterpret_cast<const floatx4 *>(lds + ((4 * b + w) * NB + c) * 256 + lane * 4);
+                for (int e = 0; e < 4; ++e) {
+                    const int k = kb + 16 * s + 4 * h + e;
+                    f = fmaf(a[s][e], k < ke ? fcol[k] : 0.f, f);
+                }
+            }
+        }
+        fpart[wave * 64 + lane] = f;
+        __syncthreads();
+    }
+
+    // sums in order of w, and the stores: wavefront c < NB takes block c
+    if (wave < NB) {
+        floatx4 v = part[0][wave][lane];
+#pragma unroll
+        for (int w = 1; w < 8; ++w)
+            v += part[w][wave][lane];
+        const int col = NB * r16 + wave;
+        const __amdgpu_buffer_rsrc_t rc = make_rsrc(C, (long long)M * N * 4);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int orow = m0 + 16 * b + 4 * h + r;
+            const int orow = m0 + 4 * h + r;
             const uint32_t vo = (orow < M && col < N) ? (uint32_t)(orow * N + col) * 4u : OOB;
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[r]), rc, vo, 0, 0);
         }
     }
+    if (FRINGE && wave == 7 && lane < 16 && m0 + lane < M) {
+        float v = 0.f;
+#pragma unroll
+        for (int w = 0; w < 8; ++w)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                v += fpart[w * 64 + 16 * g + lane];
+        C[(size_t)(m0 + lane) * N + N - 1] = v;
+    }
+    if (tl && wave == 6 && lane == 0) {
+        float v = tpart[0];
+#pragma unroll
+        for (int w = 1; w < 8; ++w)
+            v += tpart[w];
+        C[(size_t)(M - 1) * N + blockIdx.x] = v;
+    }
 }
 
-template <int NB>
-void launch_narrow_nb(const Problem &p, const F32NarrowPlan &n, hipStream_t s)
+template <int NB, bool FRINGE>
+void launch_skinny_t(const Problem &p, const F32SkinnyPlan &n, hipStream_t s)
 {
-    const dim3 grid((unsigned)((p.M + 16 * n.rb - 1) / (16 * n.rb)));
-    // 16-byte copies of B only when its extent is whole 16-byte units: a
-    // copy that ran past the end would be partly out of range
-    const int b_vec = n.b_floats % 256 == 0 && ((uintptr_t)p.B & 15) == 0 && (long long)p.K * p.N % 4 == 0;
-    if (n.rb == 2)
-        hipLaunchKernelGGL((mfma_f32_narrow_kernel<NB, 2>), grid, dim3(512), 0, s, p.M, p.N, p.K, n.kq_len,
-                           n.b_floats, b_vec, (const float *)p.A, (const float *)p.B, p.C);
-    else
-        hipLaunchKernelGGL((mfma_f32_narrow_kernel<NB, 1>), grid, dim3(256), 0, s, p.M, p.N, p.K, n.kq_len,
-                           n.b_floats, b_vec, (const float *)p.A, (const float *)p.B, p.C);
+    if constexpr (NB <= 3) {   // four blocks' partial sums leave no room for the B regions
+        if (n.ldsb) {
+            hipLaunchKernelGGL((mfma_f32_skinny_kernel<NB, FRINGE, true>), dim3((unsigned)n.blocks), dim3(512), 0, s,
+                               p.M, p.N, p.K, n.tail ? 1 : 0, (const float *)p.A, (const float *)p.B, p.C);
+            return;
+        }
+    }
+        hipLaunchKernelGGL((mfma_f32_skinny_kernel<NB, FRINGE, false>), dim3((unsigned)n.blocks), dim3(512), 0, s,
+                           p.M, p.N, p.K, n.tail ? 1 : 0, (const float *)p.A, (const float *)p.B, p.C);
+}
+
+void launch_skinny(const Problem &p, const F32SkinnyPlan &n, hipStream_t s)
+{
+    if (n.fringe) {
+        switch (n.nb) {
+        case 1: launch_skinny_t<1, true>(p, n, s); break;
+        case 2: launch_skinny_t<2, true>(p, n, s); break;
+        default: launch_skinny_t<3, true>(p, n, s); break;
+        }
+        return;
+    }
+    switch (n.nb) {
+    case 1: launch_skinny_t<1, false>(p, n, s); break;
+    case 2: launch_skinny_t<2, false>(p, n, s); break;
+    case 3: launch_skinny_t<3, false>(p, n, s); break;
+    default: launch_skinny_t<4, false>(p, n, s); break;
+    }
 }
 
 template <int BM, int BN, int BK, int WM, int WN>
@@ -980,14 +1142,9 @@ hipError_t launch_mfma_f32(const Problem &p, const gemm_plan &plan, hipStream_t 
         }
         return launch_cfg<64, 64, 16, 2, 2>(p, plan, s);
     }
-    F32NarrowPlan n;
-    if (f32_narrow_plan(p.M, p.N, p.K, n) && plan.tile_m == 16 * n.rb && plan.tile_n == 16 * n.nb) {
-        switch (n.nb) {
-        case 1: launch_narrow_nb<1>(p, n, s); break;
-        case 2: launch_narrow_nb<2>(p, n, s); break;
-        case 3: launch_narrow_nb<3>(p, n, s); break;
-        default: launch_narrow_nb<4>(p, n, s); break;
-        }
+    F32SkinnyPlan n;
+    if (f32_skinny_plan(p.M, p.N, p.K, p.B, n) && plan.tile_m == 16 && plan.grid_y == n.blocks) {
+        launch_skinny(p, n, s);
         return hipGetLastError();
     }
     if (plan.tile_m == 32 && plan.tile_n == 64)

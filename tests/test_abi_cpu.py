@@ -108,6 +108,14 @@ def test_grid_is_ceil_div_for_every_variant():
             for (M, N, K) in [(1, 1, 1), (1000, 1000, 1000), (4097, 33, 777), (256, 256, 256)]:
                 p = dg.plan(half, M, N, K, variant=v)
                 assert p["variant"] == v and p["launches"] == 1
+                if not half and v == dg.R6_MFMA_F32 and N <= 64 and p["tile_m"] == 16:
+                    # the tall, narrow kernel: all columns in one workgroup; a
+                    # last row of its own is spread over the first N
+                    # workgroups when there are at least N whole row blocks
+                    tail = M % 16 == 1 and M // 16 >= N
+                    assert p["grid_x"] == 1 and p["tile_n"] >= N
+                    assert p["grid_y"] == (M // 16 if tail else -(-M // 16))
+                    continue
                 assert p["grid_x"] == -(-N // p["tile_n"]) and p["grid_y"] == -(-M // p["tile_m"])
                 assert (p["grid_x"] - 1) * p["tile_n"] < N and (p["grid_y"] - 1) * p["tile_m"] < M
                 if p["tile_k"]:
@@ -127,15 +135,30 @@ def test_auto_picks_matrix_cores_and_tile_by_size():
     assert odd["grid_x"] * odd["grid_y"] >= 512
     small = dg.plan(False, 1024, 1024, 1024)
     assert small["variant"] == dg.R6_MFMA_F32 and small["grid_x"] * small["grid_y"] >= 256
-    # tall and narrow (N <= 64, K <= 1024): 16-row blocks, 16-column blocks
-    # up to N, two row blocks per workgroup past 256 blocks; B in LDS
+    # tall and narrow (N <= 64, K <= 1024): one workgroup of 512 threads per
+    # 16 rows, all columns and all of K.  4097 x 33: two 16-column MFMA
+    # blocks plus the 33rd column on the vector ALUs (tile_n 33), and the
+    # 4097th row spread over workgroups 0..32 rather than given a 257th
     skinny = dg.plan(False, 4097, 33, 777)
-    assert (skinny["tile_m"], skinny["tile_n"], skinny["grid_x"], skinny["grid_y"]) == (32, 48, 1, 129)
-    assert skinny["tile_k"] == 4 * 208 and skinny["lds_bytes"] == 4 * ((4 * 208 * 33 + 64 + 255) // 256 * 256)
-    assert skinny["threads"] == 512
+    assert (skinny["tile_m"], skinny["tile_n"], skinny["grid_x"], skinny["grid_y"]) == (16, 33, 1, 256)
+    # B (16-byte aligned; a wavefront's run of 7 slices = 112 rows x 132
+    # bytes fits 16 KB) copied into LDS, one region per wavefront
+    assert skinny["tile_k"] == 784 and skinny["threads"] == 512 and skinny["lds_stages"] == 1
+    assert skinny["lds_bytes"] == 8 * 2 * 1024 + 4 * 512 + 32 + 8 * 16384
+    # B off 16-byte alignment, or rows too long for 16 KB: B in registers
+    odd_b = dg.plan(False, 4097, 33, 777, B=0x1004)
+    assert odd_b["lds_stages"] == 0 and odd_b["lds_bytes"] == 8 * 2 * 1024 + 4 * (1024 + 512) + 32
+    assert dg.plan(False, 4097, 33, 1024)["lds_stages"] == 0     # 128 rows x 132 bytes
+    assert dg.plan(False, 4097, 64, 256)["lds_stages"] == 0      # four blocks
+    # a last row block of 2..15 rows, or one row with fewer whole blocks than
+    # columns: a workgroup of its own
+    assert dg.plan(False, 4098, 33, 777)["grid_y"] == 257
+    assert dg.plan(False, 33, 40, 777)["grid_y"] == 3
+    assert dg.plan(False, 4097, 32, 777)["grid_y"] == 256 and dg.plan(False, 4097, 32, 777)["tile_n"] == 32
     assert (dg.plan(False, 4000, 64, 512)["tile_m"], dg.plan(False, 4000, 64, 512)["tile_n"]) == (16, 64)
-    # B too large for LDS, or K past 1024: the 32 x 64 tile
-    assert (dg.plan(False, 4097, 64, 1024)["tile_m"], dg.plan(False, 4097, 64, 1024)["tile_n"]) == (32, 64)
+    assert (dg.plan(False, 4097, 64, 1024)["tile_m"], dg.plan(False, 4097, 64, 1024)["tile_n"]) == (16, 64)
+    assert dg.plan(False, 100, 20, 9)["tile_n"] == 32          # N % 16 > 1: a padded block
+    # K past 1024: the 32 x 64 tile
     assert (dg.plan(False, 4097, 16, 2048)["tile_m"], dg.plan(False, 4097, 16, 2048)["tile_n"]) == (32, 64)
     h = dg.plan(True, 8192, 8192, 8192)
     assert h["variant"] == dg.R7_MFMA_F16 and (h["tile_m"], h["tile_n"]) == (256, 256)

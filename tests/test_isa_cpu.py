@@ -17,7 +17,7 @@ from dense_gemm_optimisation_row_amd import build as hipbuild
 
 RING_KERNELS = [("mfma_f16.hip", "mfma_f16_pipe_kernel"), ("mfma_f16.hip", "mfma_f16_pair_kernel"),
                 ("mfma_f32.hip", "mfma_f32_ring_kernel"), ("mfma_f32.hip", "mfma_f32_small_ring_kernel"),
-                ("mfma_f32.hip", "mfma_f32_narrow_kernel"), ("mfma_8bit.hip", "mfma_8bit_ring_kernel")]
+                ("mfma_8bit.hip", "mfma_8bit_ring_kernel")]
 
 
 @pytest.fixture(scope="module", params=RING_KERNELS, ids=lambda v: v[1])
@@ -50,10 +50,9 @@ def test_every_layout_variant_is_generated(ring):
     # 16-bit: op(B) x (overwrite, accumulate) x two formats for each of a
     # k-contiguous A (pair kernel) and a k-strided A (pipe kernel); FP32:
     # op(A) x op(B) x (overwrite, accumulate); 8-bit: the row-major product in
-    # three formats; the 64 x 64 ring once; the narrow kernel for 1..4 column
-    # blocks x 1..2 row blocks
+    # three formats; the 64 x 64 ring once
     want = {"mfma_f16_pipe_kernel": 8, "mfma_f16_pair_kernel": 8, "mfma_f32_ring_kernel": 8,
-            "mfma_f32_small_ring_kernel": 1, "mfma_f32_narrow_kernel": 8, "mfma_8bit_ring_kernel": 3}[kernel]
+            "mfma_f32_small_ring_kernel": 1, "mfma_8bit_ring_kernel": 3}[kernel]
     assert len(_instances(asm, kernel)) == want
 
 
@@ -82,10 +81,9 @@ def test_m0_is_touched_only_by_the_load_helper(ring):
 def test_ring_kernel_spills_nothing(ring):
     asm, kernel = ring
     # accumulators per lane: 256 x 256 tiles over four wavefronts hold all
-    # 256 AGPRs, over eight (the FP32 ring) 128; the 64 x 64 and narrow tiles
-    # hold few (not checked)
-    want_agpr = {"mfma_f32_small_ring_kernel": None, "mfma_f32_narrow_kernel": None,
-                 "mfma_f32_ring_kernel": 128}.get(kernel, 256)
+    # 256 AGPRs, over eight (the FP32 ring) 128; the 64 x 64 tile holds few
+    # (not checked)
+    want_agpr = {"mfma_f32_small_ring_kernel": None, "mfma_f32_ring_kernel": 128}.get(kernel, 256)
     for sym, body in _instances(asm, kernel):
         priv = re.search(rf"^\s*\.set\s+{re.escape(sym)}\.private_seg_size,\s*(\d+)", asm, flags=re.M)
         agpr = re.search(rf"^\s*\.set\s+{re.escape(sym)}\.num_agpr,\s*(\d+)", asm, flags=re.M)
@@ -127,3 +125,57 @@ def test_implicit_gemm_kernels_keep_accumulators_and_gather_as_designed(conv_asm
             assert wide > 0 and narrow == 0, (sym, wide, narrow)
         else:
             assert wide == 0 and narrow > 0, (sym, wide, narrow)
+
+
+@pytest.fixture(scope="module")
+def f32_asm(tmp_path_factory):
+    if shutil.which("hipcc") is None and not os.path.exists("/opt/rocm/bin/hipcc"):
+        pytest.skip("hipcc not available")
+    out = tmp_path_factory.mktemp("isa") / "mfma_f32.s"
+    cmd = [hipbuild.hipcc(), *hipbuild.FLAGS, "-S", "--cuda-device-only",
+           os.path.join(hipbuild.CSRC, "mfma_f32.hip"), "-o", str(out)]
+    subprocess.run(cmd, check=True, capture_output=True, text=True)
+    return out.read_text()
+
+
+def test_skinny_kernel_issues_every_load_before_its_first_mfma(f32_asm):
+    """The tall, narrow FP32 kernel streams: every load of a lane is issued
+    before its first MFMA, with no wait among them (a wait there would
+    serialise the slices on memory latency), and nothing spills.  Thirteen
+    instantiations: 1..4 MFMA column blocks, and 1..3 with the last column
+    on the vector ALUs, each with B in registers; and the six with at most 3
+    blocks again with B copied into LDS, whose global->LDS loads come from
+    inline assembly that sets M0, so there the compiler must touch M0
+    nowhere else."""
+    found = _instances(f32_asm, "mfma_f32_skinny_kernel")
+    assert len(found) == 13
+    for sym, body in found:
+        ldsb = "Lb1EEEv" in sym
+        asm_loads, outside_m0, inside = 0, [], False
+        for ln in body.splitlines():
+            if "ASMSTART" in ln:
+                inside = True
+                continue
+            if "ASMEND" in ln:
+                inside = False
+                continue
+            code = ln.split(";")[0]
+            if inside and "buffer_load_dwordx4" in code and " lds" in code:
+                asm_loads += 1
+            elif re.search(r"\bm0\b", code) and not inside:
+                outside_m0.append(code.strip())
+        assert (asm_loads > 0) == ldsb, sym
+        assert outside_m0 == [], f"{sym}: compiler-generated M0 accesses: {outside_m0[:5]}"
+        lines = body.splitlines()
+        first = next(i for i, ln in enumerate(lines) if "v_mfma" in ln)
+        head = lines[:first]
+        loads = sum("buffer_load" in ln for ln in head)
+        assert loads == sum("buffer_load" in ln for ln in lines), f"{sym}: a load after the first MFMA"
+        waits = [ln.strip() for ln in head if "vmcnt" in ln]
+        first_load = next(i for i, ln in enumerate(head) if "buffer_load" in ln)
+        last_load = max(i for i, ln in enumerate(head) if "buffer_load" in ln)
+        assert not any("vmcnt" in ln for ln in head[first_load:last_load]), f"{sym}: a wait among the loads"
+        assert loads <= 63, f"{sym}: {loads} loads, more than the wait counter tells apart"
+        priv = re.search(rf"^\s*\.set\s+{re.escape(sym)}\.private_seg_size,\s*(\d+)", f32_asm, flags=re.M)
+        assert priv and int(priv.group(1)) == 0, f"{sym}: scratch (spill) memory in use"
+        assert waits, sym

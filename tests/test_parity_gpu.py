@@ -105,8 +105,9 @@ CONFIG_SHAPES = [
     (False, (4000, 4100, 200), (256, 256)),   # FP32 256 x 256 ring, ragged M/N/K
     (False, (2049, 4100, 100), (128, 128)),   # FP32 128 x 128 tiles
     (False, (1000, 1000, 1000), (64, 64)),    # FP32 64 x 64 tiles
-    (False, (4097, 33, 777), (32, 48)),       # FP32 tall, narrow: B in LDS, 2 row blocks
-    (False, (4097, 64, 1024), (32, 64)),      # FP32 narrow tiles (B too large for LDS)
+    (False, (4097, 33, 777), (16, 33)),       # FP32 tall, narrow: 2 MFMA blocks + a vector column, tail row
+    (False, (4097, 64, 1024), (16, 64)),      # FP32 tall, narrow: 4 MFMA blocks, K = 1024
+    (False, (4097, 16, 2048), (32, 64)),      # FP32 narrow tiles (K past 1024)
     (True, (8191, 4097, 72), (256, 256)),     # FP16 256 x 256 tiles, unaligned rows
     (True, (8000, 4104, 200), (256, 256)),    # FP16 256 x 256 tiles, 128-bit rows, ragged M/N/K
     (True, (2047, 4095, 200), (128, 128)),    # FP16 128 x 128 tiles
@@ -184,21 +185,31 @@ def test_f32_mid_tile_stage_counts(shape):
     assert_within(run(False, dg.AUTO, A, B), oracle.gemm_f32(A, B), tol_f32(K), f"floats {shape}")
 
 
-# Tall, narrow FP32 problems (N <= 64, K <= 1024) take a kernel that holds B
-# in LDS and splits K four ways: N across 1..4 column blocks (ragged), K
-# from 1 to 1024 (the split lands mid-slice, or leaves wavefronts empty),
-# one and two row blocks per workgroup, fewer rows than a block, and base
-# pointers one float off 16-byte alignment (the kernel reads 4 bytes a lane).
-NARROW_SHAPES = [(4100, 33, 777), (4097, 1, 1), (300, 16, 17), (257, 17, 3), (5000, 48, 64),
-                 (1000, 63, 600), (4097, 64, 576), (9, 40, 900), (16, 15, 5), (4096, 2, 1024)]
+# Tall, narrow FP32 problems (N <= 64, K <= 1024) take a kernel of 16-row
+# workgroups that load A and B straight into registers and split K eight
+# ways: N across 1..4 column blocks (ragged, and N % 16 == 1 with its last
+# column on the vector ALUs), K from 1 to 1024 (K not a multiple of 4, fewer
+# slices than wavefronts, uneven runs), the last row spread over the
+# workgroups (M % 16 == 1 with at least N whole blocks) or in a block of its
+# own, more than 256 workgroups, fewer rows than a block, and base pointers
+# one float off 16-byte alignment (the kernel needs 4-byte alignment only;
+# there B goes straight into registers instead of being copied into LDS).
+NARROW_SHAPES = [(4100, 33, 777), (4097, 33, 777), (4097, 1, 1), (300, 16, 17), (257, 17, 3),
+                 (5000, 48, 64), (1000, 63, 600), (4097, 64, 576), (9, 40, 900), (16, 15, 5),
+                 (4096, 2, 1024), (8193, 49, 1023), (33, 17, 130), (17, 33, 5), (4097, 64, 1024),
+                 (529, 33, 1), (513, 17, 999)]
 
 
 @pytest.mark.parametrize("shape", NARROW_SHAPES, ids=lambda s: "x".join(map(str, s)))
 def test_f32_tall_narrow(shape):
     M, N, K = shape
     p = dg.plan(False, M, N, K)
-    assert p["tile_n"] == 16 * -(-N // 16) and p["tile_m"] in (16, 32) and p["grid_x"] == 1
-    assert p["lds_stages"] == 1 and p["tile_k"] % 64 == 0 and p["tile_k"] >= K
+    fringe = N > 16 and N % 16 == 1
+    assert p["tile_n"] == (16 * (N // 16) + 1 if fringe else 16 * -(-N // 16))
+    assert p["tile_m"] == 16 and p["grid_x"] == 1 and p["threads"] == 512
+    tail = M % 16 == 1 and M // 16 >= N
+    assert p["grid_y"] == M // 16 + (1 if M % 16 and not tail else 0)
+    assert p["lds_stages"] in (0, 1) and p["tile_k"] == 16 * -(-K // 16)
     say("f32 tall narrow", shape)
     A, B = ints(M, N, K, 91)
     assert_bits_equal(run(False, dg.AUTO, A, B), oracle.gemm_f32(A, B), f"ints {shape}")
