@@ -31,7 +31,11 @@ After the timed region each headline kernel (and the whole step) is also run
 back to back for a couple of seconds ("sustained") while a child process
 samples the GPU's clock and socket power through the amdsmi library; the
 medians go into "sustained" (the clock a power-capped kernel settles at is
-what its throughput follows).  --no-sustained skips this.
+what its throughput follows).  With the FP16 kernel in the step, the
+matrix-core ceiling is measured the same way: a calibration kernel (its own
+library) that issues the FP16 tile's MFMA stream on the workload's operand
+values held in registers, with no memory traffic; "f16_frac_of_mfma_ceiling"
+is the GEMM's sustained rate over it.  --no-sustained skips all of this.
 """
 from __future__ import annotations
 
@@ -264,11 +268,23 @@ def main() -> int:
         out["conv_workloads"] = conv_workloads(dg, inputs, torch, dev, stream)
 
     if not args.no_sustained:
-        calls = {k: (lambda k=k: call(k)) for k in kinds}
+        calls, flops = {}, {}
+        for k in kinds:
+            calls[k], flops[k] = (lambda k=k: call(k)), wl[k].flops
+            if k == "f16":
+                # the matrix-core ceiling of the same tile stream on the same
+                # inputs (calibration kernel: MFMAs only, operands held in
+                # registers), right after the GEMM, under the same power limit
+                ceil_fn = mfma_f16_ceiling_call(dev_in["f16"], wl["f16"], torch, stream)
+                if ceil_fn is not None:
+                    calls["f16_mfma_ceiling"], flops["f16_mfma_ceiling"] = ceil_fn, wl[k].flops
         if len(kinds) > 1:
-            calls["step"] = lambda: [call(k) for k in kinds]
-        out["sustained"] = sustained(calls, {k: wl[k].flops for k in kinds} | (
-            {"step": flops_step} if len(kinds) > 1 else {}), torch, args.sustained_seconds)
+            calls["step"], flops["step"] = (lambda: [call(k) for k in kinds]), flops_step
+        out["sustained"] = sustained(calls, flops, torch, args.sustained_seconds)
+        if "f16_mfma_ceiling" in out["sustained"] and "f16" in out["sustained"]:
+            g, c = out["sustained"]["f16"], out["sustained"]["f16_mfma_ceiling"]
+            if "tflops" in g and "tflops" in c:
+                out["sustained"]["f16_frac_of_mfma_ceiling"] = round(g["tflops"] / c["tflops"], 4)
 
     if args.ladder:
         out["ladder"] = ladder(dg, inputs, torch, dev, stream)
@@ -442,6 +458,31 @@ def ladder(dg, inputs, torch, dev, stream):
                   file=sys.stderr, flush=True)
         del a, b, c
     return res
+
+
+def mfma_f16_ceiling_call(dev_in, w, torch, stream):
+    """A callable that runs the matrix-core rate calibration kernel (its own
+    library, libdgor_calibrate.so) on the FP16 workload's inputs, or None if
+    that library was not built."""
+    import ctypes
+
+    path = os.path.join(ROOT, "dense_gemm_optimisation_row_amd", "libdgor_calibrate.so")
+    if not os.path.exists(path):
+        print(f"# {path} missing: no matrix-core ceiling", file=sys.stderr, flush=True)
+        return None
+    lib = ctypes.CDLL(path)
+    f = lib.dgor_calibrate_mfma_f16
+    f.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int] * 3 + [ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    a, b, _ = dev_in
+    c = torch.empty((w.M, w.N), dtype=torch.float32, device=a.device)
+    h = int(stream.cuda_stream)
+
+    def run():
+        rc = f(a.data_ptr(), b.data_ptr(), c.data_ptr(), w.M, w.N, w.K, h)
+        if rc != 0:
+            raise RuntimeError(f"calibration kernel launch failed ({rc})")
+    return run
 
 
 def cpu_model() -> str:

@@ -23,6 +23,10 @@ OBJDIR = os.path.join(ROOT, "_build", "obj")
 LIB = os.path.join(PKG, "libdgor_gemm.so")
 
 SOURCES = ["api.hip", "ladder.hip", "mfma_f32.hip", "mfma_f16.hip", "mfma_8bit.hip", "conv.hip"]
+# The matrix-core rate calibration kernel: a library of its own, which the
+# GEMM library never loads (only the benchmark's calibration leg calls it).
+CAL_SOURCES = ["calibrate.hip"]
+CAL_LIB = os.path.join(PKG, "libdgor_calibrate.so")
 ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
@@ -48,20 +52,27 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile all sources and link the library; return its path."""
-    os.makedirs(OBJDIR, exist_ok=True)
-    jobs = min(len(SOURCES), max(1, min(8, os.cpu_count() or 1)))
-    with ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib):
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile all sources, link the GEMM library and the calibration
+    library; return the GEMM library's path."""
+    os.makedirs(OBJDIR, exist_ok=True)
+    srcs = SOURCES + CAL_SOURCES
+    jobs = min(len(srcs), max(1, min(8, os.cpu_count() or 1)))
+    with ThreadPoolExecutor(jobs) as ex:
+        objs = list(ex.map(_compile, srcs))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], CAL_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {CAL_LIB}")
     return LIB
 
 
