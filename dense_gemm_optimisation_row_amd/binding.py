@@ -99,46 +99,57 @@ class Plan(ctypes.Structure):
 
 
 _lib = None
+_libs = {}
 
 
 def load(path: str = LIB_PATH):
-    """Load the library once (raises if it has not been built)."""
+    """Load the library once (raises if it has not been built).  ``path``
+    selects another build of the same ABI (the LDS-poisoning debug build);
+    calls through the module's functions always use the product library."""
     global _lib
+    if path != LIB_PATH:
+        if path not in _libs:
+            _libs[path] = _configure(path)
+        return _libs[path]
     if _lib is None:
-        if not os.path.exists(path):
-            raise RuntimeError(
-                f"HIP library {path} is missing: build it with "
-                "`python -m dense_gemm_optimisation_row_amd.build`")
-        lib = ctypes.CDLL(path)
-        i, p = ctypes.c_int, ctypes.c_void_p
-        for kind, stem in _STEM.items():
-            f = getattr(lib, stem)
-            f.argtypes = [i, i, i, p, p, p, p]
-            f.restype = i
-            f = getattr(lib, stem + "_variant")
-            f.argtypes = [i, i, i, i, p, p, p, p]
-            f.restype = i
-            f = getattr(lib, stem + "_plan")
-            f.argtypes = [i, i, i, i, p, p, p, ctypes.POINTER(Plan)]
-            f.restype = i
-            if kind in _EX_KINDS:
-                f = getattr(lib, stem + "_ex")
-                f.argtypes = [i, i, i, i, i, ctypes.c_float, p, i, p, i, ctypes.c_float, p, i, p]
-                f.restype = i
-        lib.gemm_conv2d_workspace.argtypes = [ctypes.POINTER(ConvParams), i, ctypes.POINTER(ctypes.c_size_t)]
-        lib.gemm_conv2d_workspace.restype = i
-        lib.gemm_conv2d_algorithm.argtypes = [ctypes.POINTER(ConvParams), i, ctypes.POINTER(i)]
-        lib.gemm_conv2d_algorithm.restype = i
-        for stem in _CONV_STEM.values():
-            f = getattr(lib, stem)
-            f.argtypes = [ctypes.POINTER(ConvParams), p, p, p, p, ctypes.c_size_t, p]
-            f.restype = i
-        lib.gemm_status_string.argtypes = [i]
-        lib.gemm_status_string.restype = ctypes.c_char_p
-        lib.gemm_variant_name.argtypes = [i]
-        lib.gemm_variant_name.restype = ctypes.c_char_p
-        _lib = lib
+        _lib = _configure(path)
     return _lib
+
+
+def _configure(path: str):
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"HIP library {path} is missing: build it with "
+            "`python -m dense_gemm_optimisation_row_amd.build`")
+    lib = ctypes.CDLL(path)
+    i, p = ctypes.c_int, ctypes.c_void_p
+    for kind, stem in _STEM.items():
+        f = getattr(lib, stem)
+        f.argtypes = [i, i, i, p, p, p, p]
+        f.restype = i
+        f = getattr(lib, stem + "_variant")
+        f.argtypes = [i, i, i, i, p, p, p, p]
+        f.restype = i
+        f = getattr(lib, stem + "_plan")
+        f.argtypes = [i, i, i, i, p, p, p, ctypes.POINTER(Plan)]
+        f.restype = i
+        if kind in _EX_KINDS:
+            f = getattr(lib, stem + "_ex")
+            f.argtypes = [i, i, i, i, i, ctypes.c_float, p, i, p, i, ctypes.c_float, p, i, p]
+            f.restype = i
+    lib.gemm_conv2d_workspace.argtypes = [ctypes.POINTER(ConvParams), i, ctypes.POINTER(ctypes.c_size_t)]
+    lib.gemm_conv2d_workspace.restype = i
+    lib.gemm_conv2d_algorithm.argtypes = [ctypes.POINTER(ConvParams), i, ctypes.POINTER(i)]
+    lib.gemm_conv2d_algorithm.restype = i
+    for stem in _CONV_STEM.values():
+        f = getattr(lib, stem)
+        f.argtypes = [ctypes.POINTER(ConvParams), p, p, p, p, ctypes.c_size_t, p]
+        f.restype = i
+    lib.gemm_status_string.argtypes = [i]
+    lib.gemm_status_string.restype = ctypes.c_char_p
+    lib.gemm_variant_name.argtypes = [i]
+    lib.gemm_variant_name.restype = ctypes.c_char_p
+    return lib
 
 
 def status_string(status: int) -> str:

@@ -1,4 +1,7 @@
-"""Build the HIP library in-tree: ``libdgor_gemm.so`` beside this file.
+"""Build the HIP libraries in-tree, beside this file: ``libdgor_gemm.so`` (the
+product), ``libdgor_calibrate.so`` (the benchmark's matrix-core calibration
+kernel) and ``libdgor_gemm_poison.so`` (the product built with LDS poisoning,
+for the race tests).
 
 Every source in ``csrc/`` is compiled for gfx950 with hipcc (in parallel),
 then linked into one shared library that exports the C ABI of
@@ -27,6 +30,11 @@ SOURCES = ["api.hip", "ladder.hip", "mfma_f32.hip", "mfma_f16.hip", "mfma_8bit.h
 # GEMM library never loads (only the benchmark's calibration leg calls it).
 CAL_SOURCES = ["calibrate.hip"]
 CAL_LIB = os.path.join(PKG, "libdgor_calibrate.so")
+# The same GEMM library built with -DDGOR_LDS_POISON: every global->LDS load
+# first fills its destination with all-ones, so a read that races a load or
+# runs ahead of the barrier retiring a buffer sees NaN (a debug build for the
+# race tests; the product loads LIB).
+POISON_LIB = os.path.join(PKG, "libdgor_gemm_poison.so")
 ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
@@ -43,9 +51,9 @@ def hipcc() -> str:
     return exe
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, poison: bool = False) -> str:
+    obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ("_poison.o" if poison else ".o"))
+    cmd = [hipcc(), *FLAGS, *(["-DDGOR_LDS_POISON"] if poison else []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
@@ -65,14 +73,16 @@ def build(verbose: bool = False) -> str:
     """Compile all sources, link the GEMM library and the calibration
     library; return the GEMM library's path."""
     os.makedirs(OBJDIR, exist_ok=True)
-    srcs = SOURCES + CAL_SOURCES
-    jobs = min(len(srcs), max(1, min(8, os.cpu_count() or 1)))
+    jobs_list = [(src, False) for src in SOURCES + CAL_SOURCES] + [(src, True) for src in SOURCES]
+    jobs = min(len(jobs_list), max(1, min(8, os.cpu_count() or 1)))
     with ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, srcs))
-    _link(objs[:len(SOURCES)], LIB)
-    _link(objs[len(SOURCES):], CAL_LIB)
+        objs = list(ex.map(lambda j: _compile(*j), jobs_list))
+    n = len(SOURCES)
+    _link(objs[:n], LIB)
+    _link(objs[n:n + len(CAL_SOURCES)], CAL_LIB)
+    _link(objs[n + len(CAL_SOURCES):], POISON_LIB)
     if verbose:
-        print(f"built {LIB} and {CAL_LIB}")
+        print(f"built {LIB}, {CAL_LIB} and {POISON_LIB}")
     return LIB
 
 

@@ -38,6 +38,24 @@ __device__ __forceinline__ uint32_t lds_address(const void *p)
     return (uint32_t)(uintptr_t)(lds_void *)p;
 }
 
+// LDS poison (debug builds compiled with -DDGOR_LDS_POISON only): right
+// before a global->LDS load is issued into a region, this wavefront fills the
+// bytes the load will write with all-ones (a NaN in FP32, FP16, BF16 and both
+// FP8 formats; -1 in INT8) and waits for those writes.  The load is issued
+// only once the barrier that retires the region's last reads has passed, so
+// a correct kernel never reads the poison: a read that runs ahead of that
+// barrier, or of the wait for the load, returns the poison and corrupts C.
+#ifdef DGOR_LDS_POISON
+__device__ __forceinline__ void poison_lds(uint32_t lds, uint32_t bytes_per_lane)
+{
+    typedef __attribute__((address_space(3))) uint32_t lds_u32;
+    lds_u32 *p = (lds_u32 *)(uintptr_t)(lds + bytes_per_lane * (threadIdx.x & 63));
+    for (uint32_t i = 0; i < bytes_per_lane / 4; ++i)
+        p[i] = 0xffffffffu;
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the writes have landed
+}
+#endif
+
 // One global->LDS load of 64 x 16 bytes: lane p reads 16 bytes at byte offset
 // voff of the descriptor's range (zeros when out of range) and writes them to
 // LDS address lds + 16 p.  M0 carries the LDS address; one wait state
@@ -48,6 +66,9 @@ __device__ __forceinline__ uint32_t lds_address(const void *p)
 // caller waits for it with vmcnt.
 __device__ __forceinline__ void load_to_lds(intx4 rsrc, uint32_t lds, uint32_t voff)
 {
+#ifdef DGOR_LDS_POISON
+    poison_lds(lds, 16);
+#endif
     asm volatile("s_mov_b32 m0, %0\n\t"
                  "s_nop 0\n\t"
                  "buffer_load_dwordx4 %1, %2, 0 offen lds"
@@ -60,6 +81,9 @@ __device__ __forceinline__ void load_to_lds(intx4 rsrc, uint32_t lds, uint32_t v
 // and writes it to LDS address lds + 4 p (a 256-byte run per load).
 __device__ __forceinline__ void load_dword_to_lds(intx4 rsrc, uint32_t lds, uint32_t voff)
 {
+#ifdef DGOR_LDS_POISON
+    poison_lds(lds, 4);
+#endif
     asm volatile("s_mov_b32 m0, %0\n\t"
                  "s_nop 0\n\t"
                  "buffer_load_dword %1, %2, 0 offen lds"

@@ -179,3 +179,33 @@ def test_skinny_kernel_issues_every_load_before_its_first_mfma(f32_asm):
         priv = re.search(rf"^\s*\.set\s+{re.escape(sym)}\.private_seg_size,\s*(\d+)", f32_asm, flags=re.M)
         assert priv and int(priv.group(1)) == 0, f"{sym}: scratch (spill) memory in use"
         assert waits, sym
+
+
+def test_poison_build_fills_every_direct_load_destination_first(tmp_path):
+    """The LDS-poisoning debug build (-DDGOR_LDS_POISON) writes the poison
+    before each global->LDS load, and waits for it: in the 16-bit pair ring,
+    every direct load is preceded by LDS writes and an lgkmcnt(0) wait since
+    the previous direct load."""
+    if shutil.which("hipcc") is None and not os.path.exists("/opt/rocm/bin/hipcc"):
+        pytest.skip("hipcc not available")
+    out = tmp_path / "mfma_f16_poison.s"
+    cmd = [hipbuild.hipcc(), *hipbuild.FLAGS, "-DDGOR_LDS_POISON", "-S", "--cuda-device-only",
+           os.path.join(hipbuild.CSRC, "mfma_f16.hip"), "-o", str(out)]
+    subprocess.run(cmd, check=True, capture_output=True, text=True)
+    text = out.read_text()
+    found = _instances(text, "mfma_f16_pair_kernel")
+    assert len(found) == 8
+    for sym, body in found:
+        writes = waited = False
+        loads = 0
+        for line in body.splitlines():
+            code = line.split(";")[0]
+            if "ds_write" in code:
+                writes, waited = True, False
+            elif "s_waitcnt" in code and "lgkmcnt(0)" in code and writes:
+                waited = True
+            elif "buffer_load_dwordx4" in code and " lds" in code:
+                assert writes and waited, f"{sym}: a direct load without its poison before it"
+                writes = waited = False
+                loads += 1
+        assert loads > 0, sym
