@@ -402,8 +402,9 @@ def graph_time(fn, torch, out, calls=20, replays=20):
 
 
 def conv_workloads(dg, inputs, torch, dev, stream):
-    """Convolutions (im2col + GEMM, or the implicit GEMM for 16-bit layers
-    with enough tiles): 2 N K P Q C R S per call over the whole call,
+    """Convolutions (im2col + GEMM, or for 16-bit layers with enough tiles an
+    implicit GEMM: on a channels-last copy of x when C is a multiple of 32,
+    else gathering from x): 2 N K P Q C R S per call over the whole call,
     workspace allocated once."""
     import numpy as np
 
@@ -421,15 +422,19 @@ def conv_workloads(dg, inputs, torch, dev, stream):
         reps = max(3, min(200, int(100.0 / max(est, 1e-3))))
         ms = _time_calls(f, torch, stream, reps)
         tf = w.flops / (ms * 1e-3) / 1e12
-        implicit = dg.conv2d_algorithm(prm, xd.element_size()) == dg.CONV_IMPLICIT
-        gemm_plan = dg.plan(w.dtype, w.K, -(-w.N * P * Q // 8) * 8, -(-w.C * w.R * w.S // 8) * 8)
+        alg = dg.conv2d_algorithm(prm, xd.element_size())
+        if alg == dg.CONV_IMPLICIT_NHWC:
+            name_alg, tile = "implicit_gemm_channels_last", [64, 256] if w.K <= 64 else [128, 64]
+        elif alg == dg.CONV_IMPLICIT:
+            name_alg, tile = "implicit_gemm", [128 if w.K > 64 else 64, 256]
+        else:
+            gp = dg.plan(w.dtype, w.K, -(-w.N * P * Q // 8) * 8, -(-w.C * w.R * w.S // 8) * 8)
+            name_alg, tile = "im2col_gemm", [gp["tile_m"], gp["tile_n"]]
         res[name] = {"N": w.N, "C": w.C, "H": w.H, "W": w.W, "K": w.K, "R": w.R, "S": w.S,
                      "stride": w.stride, "pad": w.pad, "dtype": w.dtype, "ms": round(ms, 5),
                      "tflops": round(tf, 3), "frac_of_peak": round(tf / PEAK_TFLOPS[w.dtype], 4),
                      "gemm": [w.K, w.N * P * Q, w.C * w.R * w.S],
-                     "algorithm": "implicit_gemm" if implicit else "im2col_gemm",
-                     "gemm_tile": [128 if w.K > 64 else 64, 256] if implicit else
-                     [gemm_plan["tile_m"], gemm_plan["tile_n"]],
+                     "algorithm": name_alg, "gemm_tile": tile,
                      "workspace_bytes": int(ws.numel())}
         del xd, wd, y, ws
     return res

@@ -13,6 +13,6 @@ from .binding import (  # noqa: F401
     gemm_f16_f32acc, gemm_f16_f32acc_ex, gemm_f16_f32acc_variant, gemm_f32, gemm_f32_ex,
     gemm_f32_variant, gemm_e4m3_f32acc, gemm_e4m3_f32acc_variant, gemm_e5m2_f32acc,
     gemm_e5m2_f32acc_variant, gemm_i8_i32acc, gemm_i8_i32acc_variant, kind_of, plan, status_string,
-    CONV_IM2COL, CONV_IMPLICIT, conv2d, conv2d_algorithm, conv2d_workspace, conv_params,
+    CONV_IM2COL, CONV_IMPLICIT, CONV_IMPLICIT_NHWC, conv2d, conv2d_algorithm, conv2d_workspace, conv_params,
     variant_name,
 )

@@ -415,12 +415,13 @@ def conv2d_workspace(params: ConvParams, input_bytes: int) -> int:
     return int(out.value)
 
 
-CONV_IM2COL, CONV_IMPLICIT = 0, 1   # gemm_conv_algorithm
+CONV_IM2COL, CONV_IMPLICIT, CONV_IMPLICIT_NHWC = 0, 1, 2   # gemm_conv_algorithm
 
 
 def conv2d_algorithm(params: ConvParams, input_bytes: int) -> int:
-    """The path gemm_conv2d_* takes: CONV_IM2COL or CONV_IMPLICIT (host
-    arithmetic; raises on bad params)."""
+    """The path gemm_conv2d_* takes: CONV_IM2COL, CONV_IMPLICIT (the gather
+    implicit GEMM) or CONV_IMPLICIT_NHWC (the channels-last implicit GEMM);
+    host arithmetic; raises on bad params."""
     out = ctypes.c_int()
     rc = load().gemm_conv2d_algorithm(ctypes.byref(params), int(input_bytes), ctypes.byref(out))
     if rc != GEMM_OK:

@@ -25,7 +25,7 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(ROOT, "_build", "obj")
 LIB = os.path.join(PKG, "libdgor_gemm.so")
 
-SOURCES = ["api.hip", "ladder.hip", "mfma_f32.hip", "mfma_f16.hip", "mfma_8bit.hip", "conv.hip"]
+SOURCES = ["api.hip", "ladder.hip", "mfma_f32.hip", "mfma_f16.hip", "mfma_8bit.hip", "conv.hip", "conv_nhwc.hip"]
 # The matrix-core rate calibration kernel: a library of its own, which the
 # GEMM library never loads (only the benchmark's calibration leg calls it).
 CAL_SOURCES = ["calibrate.hip"]
@@ -51,9 +51,17 @@ def hipcc() -> str:
     return exe
 
 
+# Per-file flags.  The channels-last convolution kernels keep their (at most
+# 128 a lane) accumulators in ordinary registers: left to choose, the
+# compiler starts them in the accumulator registers and moves them between
+# the two register files on every k-stage.
+FILE_FLAGS = {"conv_nhwc.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def _compile(src: str, poison: bool = False) -> str:
     obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ("_poison.o" if poison else ".o"))
-    cmd = [hipcc(), *FLAGS, *(["-DDGOR_LDS_POISON"] if poison else []), "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *FLAGS, *FILE_FLAGS.get(src, []), *(["-DDGOR_LDS_POISON"] if poison else []), "-c",
+           os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")

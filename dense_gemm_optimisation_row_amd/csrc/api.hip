@@ -440,6 +440,8 @@ size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // im2col matrix, FP32 GEMM result, each starting on a 256-byte boundary.
 struct ConvPlan {
     dgor::Conv2d cv;
+    int algorithm;    // gemm_conv_algorithm
+    dgor::NhwcPlan nhwc;
     int crsp, npqp;
     bool ring;        // the GEMM runs on the 256 x 256 ring kernels, split over k
     int splits, k_chunk;
@@ -487,15 +489,30 @@ int conv_plan(const gemm_conv2d_params *pr, int elem_bytes, ConvPlan &cp)
         cp.k_chunk = (int)chunk;
         cp.splits = (int)((crsp + chunk - 1) / chunk);
     }
-    cp.off_col = round_up((size_t)q.K * (size_t)crsp * elem_bytes, kWsAlign);
-    // the im2col matrix, or the implicit GEMM's padded copy of x
-    size_t col_bytes = (size_t)crsp * (size_t)npqp * elem_bytes;
-    if (dgor::conv_igemm_vec_applies(cp.cv, elem_bytes)) {
-        const size_t xp_bytes = ((size_t)dgor::conv_padded_input_elems(cp.cv) + 8) * 2;
-        col_bytes = col_bytes > xp_bytes ? col_bytes : xp_bytes;
-    }
-    cp.off_y = cp.off_col + round_up(col_bytes, kWsAlign);
     cp.split_stride = round_up((size_t)q.K * (size_t)npqp * 4, kWsAlign) / 4;
+    if (dgor::conv_nhwc_plan(cp.cv, elem_bytes, cp.nhwc)) {
+        // channels-last implicit GEMM: Wr, then the channels-last copy of x
+        cp.algorithm = GEMM_CONV_IMPLICIT_NHWC;
+        cp.off_col = round_up(cp.nhwc.wr_bytes, kWsAlign);
+        cp.off_y = cp.off_col + round_up(cp.nhwc.xp_bytes, kWsAlign);
+        cp.bytes = cp.off_y;
+        return GEMM_OK;
+    }
+    cp.off_col = round_up((size_t)q.K * (size_t)crsp * elem_bytes, kWsAlign);
+    if (dgor::conv_igemm_applies(cp.cv, elem_bytes)) {
+        // implicit GEMM with a gather: the padded weights, then (vector
+        // gather only) the zero-padded copy of x; no im2col matrix and no
+        // GEMM result
+        cp.algorithm = GEMM_CONV_IMPLICIT;
+        const size_t xp_bytes = dgor::conv_igemm_vec_applies(cp.cv, elem_bytes)
+                                    ? ((size_t)dgor::conv_padded_input_elems(cp.cv) + 8) * 2 : 0;
+        cp.off_y = cp.off_col + round_up(xp_bytes, kWsAlign);
+        cp.bytes = cp.off_y;
+        return GEMM_OK;
+    }
+    // im2col: the padded weights, the im2col matrix, the GEMM result(s)
+    cp.algorithm = GEMM_CONV_IM2COL;
+    cp.off_y = cp.off_col + round_up((size_t)crsp * (size_t)npqp * elem_bytes, kWsAlign);
     cp.bytes = cp.off_y + (size_t)cp.splits * cp.split_stride * 4;
     return GEMM_OK;
 }
@@ -526,9 +543,12 @@ int run_conv(In in, const gemm_conv2d_params *pr, const void *x, const void *w, 
     float *yp = (float *)(base + cp.off_y);
     // W (K x CRS) is already the GEMM's K x CRSp operand when CRS is a
     // multiple of 8 and W is 16-byte aligned: no padded copy then
+    if (cp.algorithm == GEMM_CONV_IMPLICIT_NHWC)
+        return dgor::launch_conv_nhwc(cv, cp.nhwc, in == In::BF16, x, w, y, col, base, s) == hipSuccess
+                   ? GEMM_OK : GEMM_ERR_LAUNCH;
     const bool w_direct = cp.crsp == cv.C * cv.R * cv.S && aligned16(w);
     const void *wp = w_direct ? w : base;
-    if (dgor::conv_igemm_applies(cv, eb)) {   // 16-bit, enough tiles: no im2col matrix
+    if (cp.algorithm == GEMM_CONV_IMPLICIT) {   // 16-bit, enough tiles: no im2col matrix
         if (!w_direct &&
             dgor::launch_conv_prepare(cv, eb, x, w, base, nullptr, cp.crsp, cp.npqp, s) != hipSuccess)
             return GEMM_ERR_LAUNCH;
@@ -686,7 +706,7 @@ int gemm_conv2d_algorithm(const gemm_conv2d_params *params, int input_bytes, int
     ConvPlan cp;
     const int rc = conv_plan(params, input_bytes, cp);
     if (rc == GEMM_OK)
-        *algorithm = dgor::conv_igemm_applies(cp.cv, input_bytes) ? GEMM_CONV_IMPLICIT : GEMM_CONV_IM2COL;
+        *algorithm = cp.algorithm;
     return rc;
 }
 

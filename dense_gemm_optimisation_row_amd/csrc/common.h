@@ -95,12 +95,21 @@ hipError_t launch_conv_output(const Conv2d &cv, const float *yp, float *y, int n
 // and Q a multiple of 4 it gathers with 12-byte loads from a zero-padded
 // copy of x that it first writes to xp (N x C x (H + 2 ph) x (W + 2 pw
 // rounded up to a multiple of 8): conv_padded_input_elems elements, plus 8
-// of slack that are read but never used; xp 16-byte aligned).
+// of slack that are read but never used; xp 16-byte aligned), when x starts
+// 4-byte aligned.
 bool conv_igemm_applies(const Conv2d &cv, int elem_bytes);
 bool conv_igemm_vec_applies(const Conv2d &cv, int elem_bytes);
 long long conv_padded_input_elems(const Conv2d &cv);
 hipError_t launch_conv_igemm(const Conv2d &cv, bool bf16, const void *x, const void *wa, float *y, int crsp,
                              void *xp, hipStream_t stream);
+// The channels-last implicit GEMM for 16-bit inputs with C a multiple of
+// 32 (conv_nhwc.hip): tiles of bm filters x bn pixels in bk-deep stages; the
+// workspace holds Wr (K x R S C, wr_bytes) and then the zero-padded
+// channels-last copy of x (N x (H + 2 ph) x (W + 2 pw) x C, xp_bytes).
+struct NhwcPlan { int bm, bn, bk; size_t xp_bytes, wr_bytes; };
+bool conv_nhwc_plan(const Conv2d &cv, int elem_bytes, NhwcPlan &np);
+hipError_t launch_conv_nhwc(const Conv2d &cv, const NhwcPlan &np, bool bf16, const void *x, const void *w, float *y,
+                            void *xp, void *wr, hipStream_t stream);
 hipError_t launch_naive_8bit(const Problem &p, int fmt, hipStream_t stream);
 
 // The arguments of the ring kernels for a plain row-major product.

@@ -589,7 +589,10 @@ hipError_t launch_igemm_t(const Conv2d &cv, const void *x, const void *wa, float
     const long long npq = (long long)cv.N * cv.P * cv.Q;
     const int tn = (int)((npq + 255) / 256), bm = cv.K <= 64 ? 64 : 128, tiles_m = (cv.K + bm - 1) / bm;
     const dim3 grid((unsigned)(tiles_m * tn));
-    if (conv_igemm_vec_applies(cv, 2)) {
+    // the padded copy reads x with 4- and 16-byte loads from even elements:
+    // x must then start 4-byte aligned (else the element gather, which reads
+    // 2 bytes at a time)
+    if (conv_igemm_vec_applies(cv, 2) && ((uintptr_t)x & 3) == 0) {
         const int Hp = cv.H + 2 * cv.ph, Wp = (cv.W + 2 * cv.pw + 7) / 8 * 8;
         const int elems = (int)conv_padded_input_elems(cv), chunks = elems / 8;
         const int blocks = (chunks + 255) / 256 < 65536 ? (chunks + 255) / 256 : 65536;

@@ -237,7 +237,8 @@ int gemm_bf16_f32acc_ex(int opA, int opB, int M, int N, int K, float alpha,
                         float beta, float *C, int ldc, void *stream);
 
 /*
- * Two-dimensional convolution through im2col and one GEMM -- the operator
+ * Two-dimensional convolution as matrix multiplication (through im2col and
+ * one GEMM, or an implicit GEMM that forms no im2col matrix) -- the operator
  * "Lesson 8: how a GPU does matrix multiply" names as the next lesson
  * (convolution as matrix multiplication; input feature maps, weights and
  * output feature maps; direct convolution against im2col).  As deep-learning
@@ -249,22 +250,27 @@ int gemm_bf16_f32acc_ex(int opA, int opB, int M, int N, int K, float alpha,
  *       * w[k][c][r][s],  input positions outside the image contributing 0.
  * Products are exact and summed in FP32 by the GEMM kernels (16-bit inputs:
  * FP32 accumulation and output, as gemm_f16_f32acc / gemm_bf16_f32acc).
- * 16-bit layers with at least 256 tiles of 128 filters x 256 output pixels
- * (ceil(K / 128) * ceil(N P Q / 256) >= 256) take an implicit GEMM instead:
- * one kernel gathers the patches from x straight into on-chip memory, sums
- * each output over c, r, s in 32-deep steps and writes y.  The workspace then
- * holds the padded weights, only when C R S is not a multiple of 8 or w is
- * not 16-byte aligned, and, with stride_w 1 and Q a multiple of 4, a
- * zero-padded copy of x (N x C x (H + 2 pad_h) x (W + 2 pad_w rounded up to a
- * multiple of 8), in the im2col
- * matrix's place, which is made at least that large) that the gather reads
- * with wide loads.  gemm_conv2d_algorithm reports the path.
+ * 16-bit layers with C a multiple of 32 (and x rows of at most 512 pixels,
+ * and at least 96 tiles of 64 or 128 filters x 64 or 256 pixels) take an
+ * implicit GEMM on a channels-last copy of x: one pass writes that copy
+ * (N x (H + 2 pad_h) x (W + 2 pad_w) x C, zeros in the border) and the
+ * weights reordered to K x R x S x C; the GEMM kernel then sums each output
+ * over r, s, c (c fastest) and writes y.  The workspace holds the reordered
+ * weights and then the copy, each starting on a 256-byte boundary.
+ * Other 16-bit layers with at least 256 tiles of 128 filters x 256 output pixels
+ * (ceil(K / 128) * ceil(N P Q / 256) >= 256) take an implicit GEMM that
+ * gathers the patches from x straight into on-chip memory, sums each output
+ * over c, r, s in 32-deep steps and writes y.  The padded weights are used
+ * only when C R S is not a multiple of 8 or w is not 16-byte aligned; with
+ * stride_w 1 and Q a multiple of 4 the kernel first writes a zero-padded copy
+ * of x (N x C x (H + 2 pad_h) x (W + 2 pad_w rounded up to a multiple of 8))
+ * that the gather reads with wide loads; the workspace then holds only the
+ * padded weights and that copy.  gemm_conv2d_algorithm reports the path.
  * The library allocates nothing: the caller passes a device workspace of at
- * least the size gemm_conv2d_workspace reports.  It holds the padded weights
- * (K x CRSp), the im2col matrix (CRSp x NPQp, or the padded copy of x when
- * that is larger and the implicit GEMM reads one) and the GEMM result
- * (K x NPQp, FP32), where CRS = C R S and NPQ = N P Q are rounded up to
- * multiples of 8.  When K >= 192 and CRSp >= 64 the GEMM is split over k into chunks of
+ * least the size gemm_conv2d_workspace reports.  On the im2col path it holds
+ * the padded weights (K x CRSp), the im2col matrix (CRSp x NPQp) and the GEMM
+ * result (K x NPQp, FP32), where CRS = C R S and NPQ = N P Q are rounded up
+ * to multiples of 8.  When K >= 192 and CRSp >= 64 the GEMM is split over k into chunks of
  * a multiple of 64 (at least 64) until its 256 x 256 tiles times the splits
  * reach 256, and the workspace holds one FP32 result per split; the output
  * pass adds them in split order.  Errors: negative sizes, R, S, strides or dilations below
@@ -291,9 +297,11 @@ int gemm_conv2d_workspace(const gemm_conv2d_params *params, int input_bytes, siz
 
 /* Which path a convolution with these parameters and input element size
  * takes, in *algorithm: GEMM_CONV_IM2COL (im2col matrix, then the GEMM
- * kernels) or GEMM_CONV_IMPLICIT (the implicit GEMM; 16-bit inputs only).
- * Host arithmetic only.  Errors as gemm_conv2d_workspace. */
-typedef enum { GEMM_CONV_IM2COL = 0, GEMM_CONV_IMPLICIT = 1 } gemm_conv_algorithm;
+ * kernels), GEMM_CONV_IMPLICIT (the implicit GEMM gathering from x; 16-bit
+ * inputs only) or GEMM_CONV_IMPLICIT_NHWC (the implicit GEMM on a
+ * channels-last copy of x; 16-bit inputs with C a multiple of 32).  Host
+ * arithmetic only.  Errors as gemm_conv2d_workspace. */
+typedef enum { GEMM_CONV_IM2COL = 0, GEMM_CONV_IMPLICIT = 1, GEMM_CONV_IMPLICIT_NHWC = 2 } gemm_conv_algorithm;
 int gemm_conv2d_algorithm(const gemm_conv2d_params *params, int input_bytes, int *algorithm);
 
 int gemm_conv2d_f32(const gemm_conv2d_params *params, const float *x, const float *w, float *y,

@@ -302,24 +302,31 @@ def test_conv2d_workspace_layout_and_validation():
     r = lambda v: -(-v // 256) * 256
     # 32 x 256 x 14 x 14, 256 filters 3 x 3, padding 1: CRS 2304, NPQ 6272 (multiples
     # of 8); 25 tiles, so the GEMM is split over k into chunks of 256 (9 partials)
+    # (FP32: im2col; 16-bit: the channels-last implicit GEMM, whose workspace is
+    # the reordered weights K x R S C and the copy of x N x 16 x 16 x C)
     p = cp(32, 256, 14, 14, 256, 3, 3, (1, 1), (1, 1))
     assert _conv_splits(256, 2304, 6272) == 9
-    for eb in (2, 4):
-        assert dg.conv2d_workspace(p, eb) == r(256 * 2304 * eb) + r(2304 * 6272 * eb) + 9 * r(256 * 6272 * 4)
-    # 392 tiles: no split
+    assert dg.conv2d_workspace(p, 4) == r(256 * 2304 * 4) + r(2304 * 6272 * 4) + 9 * r(256 * 6272 * 4)
+    assert dg.conv2d_workspace(p, 2) == r(256 * 2304 * 2) + r(32 * 16 * 16 * 256 * 2)
+    # 392 tiles: no split on the im2col path (FP32); 16-bit channels last
     p = cp(32, 64, 56, 56, 64, 3, 3, (1, 1), (1, 1))
     assert _conv_splits(64, 576, 100352) == 1
-    assert dg.conv2d_workspace(p, 2) == r(64 * 576 * 2) + r(576 * 100352 * 2) + r(64 * 100352 * 4)
     assert dg.conv2d_workspace(p, 4) == r(64 * 576 * 4) + r(576 * 100352 * 4) + r(64 * 100352 * 4)
+    assert dg.conv2d_workspace(p, 2) == r(64 * 576 * 2) + r(32 * 58 * 58 * 64 * 2)
     # CRS 27 rounds up to 32 (below one chunk: the planner's tiles, no split)
     p = cp(2, 3, 224, 224, 64, 3, 3, (2, 2), (1, 1))
     assert dg.conv2d_workspace(p, 2) == r(64 * 32 * 2) + r(32 * 25088 * 2) + r(64 * 25088 * 4)
-    # a padded 1 x 1 layer on the implicit GEMM's vector gather: the padded
-    # copy of x (16 x 8 x 64 x 64, plus 8 elements) outgrows the im2col matrix
+    # a padded 1 x 1 layer on the gathering implicit GEMM's vector form: the
+    # padded weights and the padded copy of x (16 x 8 x 64 x 64, plus 8
+    # elements), no im2col matrix and no GEMM result
     p = cp(16, 8, 62, 62, 128, 1, 1, (1, 1), (1, 1))
     assert dg.conv2d_algorithm(p, 2) == dg.CONV_IMPLICIT
-    assert dg.conv2d_workspace(p, 2) == r(128 * 8 * 2) + r((16 * 8 * 64 * 64 + 8) * 2) + r(128 * 65536 * 4)
+    assert dg.conv2d_workspace(p, 2) == r(128 * 8 * 2) + r((16 * 8 * 64 * 64 + 8) * 2)
     assert dg.conv2d_workspace(p, 4) == r(128 * 8 * 4) + r(8 * 65536 * 4) + r(128 * 65536 * 4)
+    # the element gather (stride 2 along w): the padded weights only
+    p = cp(16, 8, 130, 130, 24, 5, 5, (2, 2), (2, 2))
+    assert dg.conv2d_algorithm(p, 2) == dg.CONV_IMPLICIT
+    assert dg.conv2d_workspace(p, 2) == r(24 * 200 * 2)
     # a 7 x 7 stem with 256 filters: CRS 147 -> 152, 98 tiles -> 2 chunks of 128 and 24
     p = cp(2, 3, 224, 224, 256, 7, 7, (2, 2), (3, 3))
     assert _conv_splits(256, 152, 25088) == 2
@@ -338,22 +345,24 @@ def test_conv2d_workspace_layout_and_validation():
 
 
 def test_conv2d_algorithm_follows_the_tile_count():
-    """16-bit layers with at least 256 implicit-GEMM tiles (128 filters x 256
-    output pixels) take the implicit GEMM; FP32 and smaller layers im2col."""
+    """16-bit layers with C a multiple of 32, filters of at most 64 taps and at
+    least 96 channels-last tiles (64 filters x 256 pixels when K <= 64, else
+    128 x 64) take the channels-last implicit GEMM; other 16-bit layers with
+    at least 256 gathering tiles (128 filters x 256 output pixels) the
+    gathering implicit GEMM; FP32 and smaller layers im2col."""
     cp = binding.conv_params
     alg = dg.conv2d_algorithm
-    p56 = cp(32, 64, 56, 56, 64, 3, 3, (1, 1), (1, 1))          # 392 tiles
-    p14 = cp(32, 256, 14, 14, 256, 3, 3, (1, 1), (1, 1))        # 2 x 25 tiles
-    assert alg(p56, 2) == dg.CONV_IMPLICIT and alg(p56, 4) == dg.CONV_IM2COL
-    assert alg(p14, 2) == dg.CONV_IM2COL
-    assert alg(cp(16, 4, 64, 64, 128, 1, 1), 2) == dg.CONV_IMPLICIT    # NPQ 65536: 256 tiles
-    assert alg(cp(15, 4, 64, 68, 128, 1, 1), 2) == dg.CONV_IM2COL      # NPQ 65280: 255 tiles
-    assert alg(cp(15, 4, 64, 68, 129, 1, 1), 2) == dg.CONV_IMPLICIT    # 2 x 255 tiles
-    assert alg(cp(16, 0, 64, 64, 128, 1, 1), 2) == dg.CONV_IM2COL      # no channels
-    with pytest.raises(dg.GemmError) as e:
-        alg(cp(1, 1, 4, 4, 1, 0, 1), 2)
-    assert e.value.status == binding.GEMM_ERR_INVALID_DIM
-    assert binding.load().gemm_conv2d_algorithm(None, 2, None) == binding.GEMM_ERR_NULL_PTR
+    p56 = cp(32, 64, 56, 56, 64, 3, 3, (1, 1), (1, 1))          # 392 tiles of 64 x 256
+    p14 = cp(32, 256, 14, 14, 256, 3, 3, (1, 1), (1, 1))        # 2 x 98 tiles of 128 x 64
+    assert alg(p56, 2) == dg.CONV_IMPLICIT_NHWC and alg(p56, 4) == dg.CONV_IM2COL
+    assert alg(p14, 2) == dg.CONV_IMPLICIT_NHWC and alg(p14, 4) == dg.CONV_IM2COL
+    assert alg(cp(4, 128, 28, 28, 256, 3, 3, (2, 2), (1, 1)), 2) == dg.CONV_IM2COL   # 2 x 13 tiles
+    assert alg(cp(384, 32, 8, 8, 64, 1, 1), 2) == dg.CONV_IMPLICIT_NHWC   # NPQ 24576: 96 tiles
+    assert alg(cp(380, 32, 8, 8, 64, 1, 1), 2) == dg.CONV_IM2COL          # 95 tiles
+    assert alg(cp(2, 32, 8, 8, 96, 3, 3, (1, 1), (1, 1)), 2) == dg.CONV_IM2COL   # 1 x 2 tiles
+    assert alg(cp(64, 48, 32, 32, 64, 1, 1), 2) == dg.CONV_IMPLICIT     # C 48: gathering, 256 tiles
+    assert alg(cp(4, 64, 16, 600, 64, 1, 1), 2) == dg.CONV_IMPLICIT_NHWC   # wide rows: 150 tiles
+    assert alg(cp(4, 32, 40, 40, 64, 9, 9, (1, 1), (4, 4)), 2) == dg.CONV_IM2COL   # 81 taps
 
 
 def test_conv2d_entry_points_validate_before_touching_a_device():

@@ -209,3 +209,38 @@ def test_poison_build_fills_every_direct_load_destination_first(tmp_path):
                 writes = waited = False
                 loads += 1
         assert loads > 0, sym
+
+
+def test_channels_last_conv_kernel_streams_cleanly(tmp_path):
+    """The channels-last convolution kernel (built with its file's flags): no
+    spills, no accumulator moves between register files inside the k-loop,
+    and, as it loads through the inline-assembly global->LDS helper, no M0
+    access of the compiler's own.  Six instantiations: two formats x three
+    tile configurations."""
+    if shutil.which("hipcc") is None and not os.path.exists("/opt/rocm/bin/hipcc"):
+        pytest.skip("hipcc not available")
+    out = tmp_path / "conv_nhwc.s"
+    cmd = [hipbuild.hipcc(), *hipbuild.FLAGS, *hipbuild.FILE_FLAGS["conv_nhwc.hip"], "-S", "--cuda-device-only",
+           os.path.join(hipbuild.CSRC, "conv_nhwc.hip"), "-o", str(out)]
+    subprocess.run(cmd, check=True, capture_output=True, text=True)
+    text = out.read_text()
+    found = _instances(text, "conv_nhwc_kernel")
+    assert len(found) == 6
+    for sym, body in found:
+        priv = re.search(rf"^\s*\.set\s+{re.escape(sym)}\.private_seg_size,\s*(\d+)", text, flags=re.M)
+        assert priv and int(priv.group(1)) == 0, f"{sym}: scratch (spill) memory in use"
+        assert "v_accvgpr_mov" not in body and "scratch_" not in body, sym
+        inside, outside_m0, dma = False, [], 0
+        for line in body.splitlines():
+            if "ASMSTART" in line:
+                inside = True
+                continue
+            if "ASMEND" in line:
+                inside = False
+                continue
+            code = line.split(";")[0]
+            if inside and "buffer_load_dwordx4" in code and " lds" in code:
+                dma += 1
+            elif re.search(r"\bm0\b", code) and not inside:
+                outside_m0.append(code.strip())
+        assert dma > 0 and outside_m0 == [], (sym, outside_m0[:3])

@@ -189,3 +189,72 @@ def test_random_convolutions(case):
     assert got.shape == ref.shape
     bad = got != ref
     assert not bad.any(), f"{case}: {int(bad.sum())} elements differ"
+
+
+# convolutions that take the implicit GEMMs: seeded random geometries (stride,
+# padding and dilation per axis, rectangular filters) sized for enough tiles.
+# Channels last: C a multiple of 32 and at least 96 tiles; gathering: C below
+# 32 and at least 256 tiles of 128 filters x 256 pixels.  Integer inputs,
+# bit-exact; each case asserts the path it takes.
+IMPLICIT_CASES = []
+_rng = np.random.default_rng(7901)
+
+
+def _out(n, k, p, d, s):
+    return (n + 2 * p - d * (k - 1) - 1) // s + 1
+
+
+def _nhwc_tiles(N, H, W, K, R, S, st, pd, dl):
+    npq = N * _out(H, R, pd[0], dl[0], st[0]) * _out(W, S, pd[1], dl[1], st[1])
+    return -(-npq // 256) if K <= 64 else -(-K // 128) * -(-npq // 64), npq
+
+
+for _fmt in ("f16", "bf16"):
+    for _i in range(10):
+        nhwc = _i < 6
+        while True:   # draw until the case takes the path it is meant for, at a size the oracle finishes quickly
+            R, S = int(_rng.integers(1, 4)), int(_rng.integers(1, 4))
+            st = (int(_rng.integers(1, 3)), int(_rng.integers(1, 3)))
+            dl = (int(_rng.integers(1, 3)), int(_rng.integers(1, 3)))
+            pd = (int(_rng.integers(0, 3)), int(_rng.integers(0, 3)))
+            if nhwc:
+                C = 32 * int(_rng.integers(1, 4))
+                K = int(_rng.integers(1, 65)) if _i < 3 else int(_rng.integers(65, 161))
+                N, H, W = int(_rng.integers(16, 81)), int(_rng.integers(20, 49)), int(_rng.integers(20, 49))
+                tiles, npq = _nhwc_tiles(N, H, W, K, R, S, st, pd, dl)
+                if tiles >= 96 and 2 * npq * K * C * R * S <= 4e9:
+                    break
+            else:
+                C, K, N = int(_rng.integers(1, 32)), int(_rng.integers(1, 129)), int(_rng.integers(48, 65))
+                H, W = int(_rng.integers(44, 57)), int(_rng.integers(44, 57))
+                st = (1, 1)   # enough pixels for 256 tiles
+                break
+        IMPLICIT_CASES.append((_fmt, nhwc, N, C, H, W, K, R, S, st, pd, dl))
+
+
+@pytest.mark.parametrize("case", IMPLICIT_CASES, ids=lambda c: "_".join(map(str, c[:9])))
+def test_random_implicit_gemm_convolutions(case):
+    import torch
+    from helpers import to_dev
+    fmt, nhwc, N, C, H, W, K, R, S, st, pd, dl = case
+    P = (H + 2 * pd[0] - dl[0] * (R - 1) - 1) // st[0] + 1
+    Q = (W + 2 * pd[1] - dl[1] * (S - 1) - 1) // st[1] + 1
+    prm = binding.conv_params(N, C, H, W, K, R, S, st, pd, dl)
+    algo = dg.conv2d_algorithm(prm, 2)
+    if nhwc:
+        tiles = _nhwc_tiles(N, H, W, K, R, S, st, pd, dl)[0]
+        assert (algo == dg.CONV_IMPLICIT_NHWC) == (tiles >= 96), (case, tiles, algo)
+    else:
+        tiles = -(-K // 128) * -(-(N * P * Q) // 256)
+        assert (algo == dg.CONV_IMPLICIT) == (tiles >= 256), (case, tiles, algo)
+    say("sweep implicit conv", case, "algorithm", algo)
+    n = N * C * H * W
+    x = inputs.matrices(1, 1, n, 8000 + n, "int", fmt)[0].reshape(N, C, H, W)
+    w = inputs.matrices(1, 1, K * C * R * S, 8100 + K, "int", fmt)[0].reshape(K, C, R, S)
+    y = dg.conv2d(fmt, to_dev(x), to_dev(w), st, pd, dl)
+    torch.cuda.synchronize()
+    ref = oracle.conv2d(fmt, x, w, st, pd, dl)
+    got = y.cpu().numpy()
+    assert got.shape == ref.shape
+    bad = got != ref
+    assert not bad.any(), f"{case}: {int(bad.sum())} elements differ"
