@@ -250,8 +250,9 @@ int gemm_bf16_f32acc_ex(int opA, int opB, int M, int N, int K, float alpha,
  *       * w[k][c][r][s],  input positions outside the image contributing 0.
  * Products are exact and summed in FP32 by the GEMM kernels (16-bit inputs:
  * FP32 accumulation and output, as gemm_f16_f32acc / gemm_bf16_f32acc).
- * 16-bit layers with C a multiple of 32 (and x rows of at most 512 pixels,
- * and at least 96 tiles of 64 or 128 filters x 64 or 256 pixels) take an
+ * 16-bit layers with C a multiple of 32, filters of at most 64 taps (R S)
+ * and at least 96 tiles (64 filters x 256 output pixels when K <= 64, else
+ * 128 filters x 64 pixels) take an
  * implicit GEMM on a channels-last copy of x: one pass writes that copy
  * (N x (H + 2 pad_h) x (W + 2 pad_w) x C, zeros in the border) and the
  * weights reordered to K x R x S x C; the GEMM kernel then sums each output
