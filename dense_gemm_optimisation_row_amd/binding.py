@@ -34,6 +34,7 @@ GEMM_ERR_INVALID_VARIANT = -5
 GEMM_ERR_RUNTIME = -6
 GEMM_ERR_INVALID_LAYOUT = -7
 GEMM_ERR_WORKSPACE = -8
+GEMM_ERR_SCRATCH_LIMIT = -9
 GEMM_OP_N, GEMM_OP_T = 0, 1
 
 AUTO = -1
@@ -53,6 +54,7 @@ EXPORTS = ("gemm_f32", "gemm_f16_f32acc", "gemm_bf16_f32acc",
            "gemm_e4m3_f32acc_plan", "gemm_e5m2_f32acc_plan", "gemm_i8_i32acc_plan",
            "gemm_f32_ex", "gemm_f16_f32acc_ex", "gemm_bf16_f32acc_ex",
            "gemm_conv2d_workspace", "gemm_conv2d_algorithm", "gemm_conv2d_f32", "gemm_conv2d_f16_f32acc", "gemm_conv2d_bf16_f32acc",
+           "gemm_conv2d_f16_f32acc_noalloc",
            "gemm_status_string", "gemm_variant_name")
 
 # Entry-point name stem per input format.
@@ -145,6 +147,8 @@ def _configure(path: str):
         f = getattr(lib, stem)
         f.argtypes = [ctypes.POINTER(ConvParams), p, p, p, p, ctypes.c_size_t, p]
         f.restype = i
+    lib.gemm_conv2d_f16_f32acc_noalloc.argtypes = [ctypes.POINTER(ConvParams), p, p, p, p]
+    lib.gemm_conv2d_f16_f32acc_noalloc.restype = i
     lib.gemm_status_string.argtypes = [i]
     lib.gemm_status_string.restype = ctypes.c_char_p
     lib.gemm_variant_name.argtypes = [i]
@@ -434,6 +438,13 @@ def raw_conv2d(kind, params: ConvParams, x: int | None, w: int | None, y: int | 
     """gemm_conv2d_* with plain integers; returns the status code."""
     f = getattr(load(), _CONV_STEM[kind_of(kind)])
     return int(f(ctypes.byref(params), x, w, y, workspace, workspace_bytes, stream))
+
+
+def gemm_conv2d_f16_f32acc_noalloc(params: ConvParams, x: int | None, w: int | None, y: int | None,
+                                   stream: int | None) -> int:
+    """gemm_conv2d_f16_f32acc_noalloc with plain integers (device pointers of
+    the binary16 x and w and the FP32 y); returns the status code."""
+    return int(load().gemm_conv2d_f16_f32acc_noalloc(ctypes.byref(params), x, w, y, stream))
 
 
 def conv2d(kind, x, w, stride=(1, 1), padding=(0, 0), dilation=(1, 1), y=None, workspace=None, stream=None):

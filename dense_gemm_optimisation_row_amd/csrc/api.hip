@@ -8,6 +8,7 @@
 // ceil(N / tile_n) workgroups along N and ceil(M / tile_m) along M.
 #include <atomic>
 #include <math.h>
+#include <mutex>
 #include <stdint.h>
 
 #include "common.h"
@@ -517,6 +518,17 @@ int conv_plan(const gemm_conv2d_params *pr, int elem_bytes, ConvPlan &cp)
     return GEMM_OK;
 }
 
+// GEMM_ERR_NULL_PTR for a NULL tensor of nonzero extent; *empty when y has
+// no elements (nothing to launch).
+int conv_pointers(const ConvPlan &cp, const void *x, const void *w, const float *y, bool &empty)
+{
+    const dgor::Conv2d &cv = cp.cv;
+    const long long xs = (long long)cv.N * cv.C * cv.H * cv.W, wsz = (long long)cv.K * cv.C * cv.R * cv.S;
+    const long long ys = (long long)cv.N * cv.K * cv.P * cv.Q;
+    empty = ys == 0;
+    return (xs > 0 && !x) || (wsz > 0 && !w) || (ys > 0 && !y) ? GEMM_ERR_NULL_PTR : GEMM_OK;
+}
+
 int run_conv(In in, const gemm_conv2d_params *pr, const void *x, const void *w, float *y, void *ws,
              size_t ws_bytes, void *stream)
 {
@@ -526,12 +538,10 @@ int run_conv(In in, const gemm_conv2d_params *pr, const void *x, const void *w, 
     if (rc != GEMM_OK)
         return rc;
     const dgor::Conv2d &cv = cp.cv;
-    const long long xs = (long long)cv.N * cv.C * cv.H * cv.W, wsz = (long long)cv.K * cv.C * cv.R * cv.S;
-    const long long ys = (long long)cv.N * cv.K * cv.P * cv.Q;
-    if ((xs > 0 && !x) || (wsz > 0 && !w) || (ys > 0 && !y))
-        return GEMM_ERR_NULL_PTR;
-    if (ys == 0)
-        return GEMM_OK;
+    bool empty = false;
+    const int pc = conv_pointers(cp, x, w, y, empty);
+    if (pc != GEMM_OK || empty)
+        return pc;
     if (!ws || ws_bytes < cp.bytes || ((uintptr_t)ws & (kWsAlign - 1)))
         return GEMM_ERR_WORKSPACE;
     const int dev = check_device();
@@ -575,6 +585,40 @@ int run_conv(In in, const gemm_conv2d_params *pr, const void *x, const void *w, 
     }
     return dgor::launch_conv_output(cv, yp, y, cp.npqp, cp.splits, cp.split_stride, s) == hipSuccess
                ? GEMM_OK : GEMM_ERR_LAUNCH;
+}
+
+}  // namespace
+
+// Scratch of the no-allocation convolution entry point: a fixed array in
+// the code object, so each GPU the library runs on holds its own copy from
+// the module's load until the process ends.  Host code never passes the
+// array's name to a kernel (on the host it only stands for the symbol): it
+// uses the device address hipGetSymbolAddress reports, looked up once per
+// device with that device current.
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+namespace {
+
+std::once_flag g_scratch_once[kDevCache];
+void *g_scratch_ptr[kDevCache];
+hipError_t g_scratch_err[kDevCache];
+
+// The current device's scratch address in *ptr, or GEMM_ERR_RUNTIME.
+int device_scratch(void **ptr)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevCache)
+        return GEMM_ERR_RUNTIME;
+    std::call_once(g_scratch_once[dev], [dev] {
+        void *p = nullptr;
+        g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        g_scratch_ptr[dev] = p;
+    });
+    if (g_scratch_err[dev] != hipSuccess || g_scratch_ptr[dev] == nullptr)
+        return GEMM_ERR_RUNTIME;
+    *ptr = g_scratch_ptr[dev];
+    return GEMM_OK;
 }
 
 }  // namespace
@@ -728,6 +772,26 @@ int gemm_conv2d_bf16_f32acc(const gemm_conv2d_params *params, const uint16_t *x,
     return run_conv(In::BF16, params, x, w, y, workspace, workspace_bytes, stream);
 }
 
+int gemm_conv2d_f16_f32acc_noalloc(const gemm_conv2d_params *params, const uint16_t *x, const uint16_t *w, float *y,
+                                   void *stream)
+{
+    ConvPlan cp;
+    const int rc = conv_plan(params, 2, cp);
+    if (rc != GEMM_OK)
+        return rc;
+    bool empty = false;
+    const int pc = conv_pointers(cp, x, w, y, empty);
+    if (pc != GEMM_OK || empty)
+        return pc;
+    if (cp.bytes > kNoAllocScratchBytes)
+        return GEMM_ERR_SCRATCH_LIMIT;
+    void *ws = nullptr;
+    const int sc = device_scratch(&ws);
+    if (sc != GEMM_OK)
+        return sc;
+    return run_conv(In::F16, params, x, w, y, ws, kNoAllocScratchBytes, stream);
+}
+
 int gemm_f32_ex(int opA, int opB, int M, int N, int K, float alpha, const float *A, int lda, const float *B,
                 int ldb, float beta, float *C, int ldc, void *stream)
 {
@@ -758,6 +822,7 @@ const char *gemm_status_string(int status)
     case GEMM_ERR_RUNTIME: return "HIP runtime query failed";
     case GEMM_ERR_INVALID_LAYOUT: return "invalid operand layout (op flag or leading dimension)";
     case GEMM_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case GEMM_ERR_SCRATCH_LIMIT: return "needs more scratch than the no-allocation entry point's fixed array (16 MiB)";
     default: return "unknown status";
     }
 }

@@ -50,7 +50,8 @@ typedef enum {
     GEMM_ERR_INVALID_VARIANT = -5,
     GEMM_ERR_RUNTIME = -6,
     GEMM_ERR_INVALID_LAYOUT = -7,
-    GEMM_ERR_WORKSPACE = -8
+    GEMM_ERR_WORKSPACE = -8,
+    GEMM_ERR_SCRATCH_LIMIT = -9
 } gemm_status;
 
 /*
@@ -311,6 +312,22 @@ int gemm_conv2d_f16_f32acc(const gemm_conv2d_params *params, const uint16_t *x, 
                            float *y, void *workspace, size_t workspace_bytes, void *stream);
 int gemm_conv2d_bf16_f32acc(const gemm_conv2d_params *params, const uint16_t *x, const uint16_t *w,
                             float *y, void *workspace, size_t workspace_bytes, void *stream);
+
+/* gemm_conv2d_f16_f32acc without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  The workspace is a fixed 16 MiB
+ * array inside the library (one per GPU, held from the library's load on
+ * that GPU until the process ends); the call allocates nothing and launches
+ * the same kernels as gemm_conv2d_f16_f32acc, so y is bit for bit the same.
+ * A layer whose gemm_conv2d_workspace size (input_bytes 2) exceeds 16 MiB ->
+ * GEMM_ERR_SCRATCH_LIMIT, with nothing launched; its first call on a device
+ * looks up that device's array (a failure -> GEMM_ERR_RUNTIME); other errors
+ * as gemm_conv2d_f16_f32acc.  Every call on one GPU uses that GPU's one
+ * array and leaves its contents behind (each call writes all it reads):
+ * calls that overlap on one GPU -- on different streams, or from different
+ * threads without ordering -- race on it. */
+int gemm_conv2d_f16_f32acc_noalloc(const gemm_conv2d_params *params, const uint16_t *x, const uint16_t *w,
+                                   float *y, void *stream);
 
 /* Static, NUL-terminated descriptions; never NULL ("unknown ..." for values
  * outside the enums). */

@@ -395,3 +395,21 @@ def test_no_device_is_reported_not_crashed():
     for kind in ("f32", "f16", "bf16"):
         rc = binding.raw_gemm_ex(kind, 1, 0, 4, 4, 4, 2.0, 16, 4, 16, 4, 0.5, 16, 4, None)
         assert rc in (binding.GEMM_ERR_RUNTIME, binding.GEMM_ERR_UNSUPPORTED_DEVICE)
+
+
+def test_no_allocation_conv2d_host_checks():
+    """The no-allocation FP16 convolution rejects bad sizes and layers whose
+    workspace exceeds its fixed 16 MiB before any HIP call (so this runs
+    without a GPU): the 14 x 14 and 56 x 56 benchmarked layers fit; a
+    56 x 56 layer at twice the batch (xp 27.6 MB) does not."""
+    cp = binding.conv_params
+    lim = 16 << 20
+    assert dg.conv2d_workspace(cp(32, 256, 14, 14, 256, 3, 3, (1, 1), (1, 1)), 2) <= lim
+    assert dg.conv2d_workspace(cp(32, 64, 56, 56, 64, 3, 3, (1, 1), (1, 1)), 2) <= lim
+    big = cp(64, 64, 56, 56, 64, 3, 3, (1, 1), (1, 1))
+    assert dg.conv2d_workspace(big, 2) > lim
+    f = binding.gemm_conv2d_f16_f32acc_noalloc
+    assert f(big, 16, 16, 16, None) == binding.GEMM_ERR_SCRATCH_LIMIT
+    assert f(cp(1, 4, 9, 9, 5, 3, 3, (0, 1)), 16, 16, 16, None) == binding.GEMM_ERR_INVALID_DIM
+    assert f(cp(1, 4, 9, 9, 5, 3, 3), None, 16, 16, None) == binding.GEMM_ERR_NULL_PTR
+    assert "16 MiB" in binding.status_string(binding.GEMM_ERR_SCRATCH_LIMIT)
