@@ -334,11 +334,71 @@ __device__ __forceinline__ int stage_range(int k0, int K, int t0, int ext, int l
 
 }  // namespace ring16
 
+// Epilogue of the 16-bit ring kernels.  A wavefront's 128 x 128 block of C
+// sits in its accumulators in the 16 x 16 MFMA layout (lane (g, s) holds
+// rows 16 i + 4 g + r, column 16 j + s), so a store straight from them
+// covers 64-byte pieces of four rows.  Instead the block goes out through
+// LDS in four rounds of 32 rows: the wavefront writes alpha times its
+// accumulators for those rows into its own LDS region, reads them back 16
+// bytes a lane along the rows, and stores those 16 bytes (a wavefront's
+// store is two whole 512-byte rows), so C is written once, in whole 128-byte
+// lines.  The rows of the region are padded by 16 bytes, which puts the 64
+// lanes of every 4-byte write on distinct banks.  Cw is the block's first
+// element; rows_left and cols_left count the block's rows and columns
+// inside C; vec: Cw is 16-byte aligned and ldc a multiple of 4 (else each
+// element is stored on its own).  The caller has made sure that no
+// wavefront still reads the ring or has a load in flight into it.
+namespace cstage {
+constexpr int ROW_BYTES = 128 * 4 + 16;
+constexpr int WAVE_BYTES = 32 * ROW_BYTES;   // 16.5 KB a wavefront
+}  // namespace cstage
+
+__device__ __forceinline__ void store_c_staged(const floatx4 (&acc)[8][8], float alpha, uint8_t *lds, int wave,
+                                               int lane, float *Cw, int ldc, int rows_left, int cols_left, bool vec)
+{
+    using namespace cstage;
+    typedef unsigned uintx4 __attribute__((ext_vector_type(4)));
+    constexpr uint32_t OOB = 0x80000000u;
+    uint8_t *w = lds + wave * WAVE_BYTES;
+    const int g = lane >> 4, s16 = lane & 15;
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(
+        Cw, rows_left > 0 && cols_left > 0 ? ((long long)(rows_left - 1) * ldc + cols_left) * 4 : 0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    *reinterpret_cast<float *>(w + (16 * ii + 4 * g + r) * ROW_BYTES + (16 * j + s16) * 4) =
+                        dgor_acc_read(acc[2 * q + ii][j][r]) * alpha;
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+            const int u = lane + 64 * t, row = u >> 5, col = 4 * (u & 31);
+            const floatx4 v = *reinterpret_cast<const floatx4 *>(w + row * ROW_BYTES + col * 4);
+            const int grow = 32 * q + row;
+            if (grow < rows_left) {
+                const uint32_t o = (uint32_t)(grow * ldc + col) * 4u;
+                if (vec && col + 4 <= cols_left) {
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(uintx4, v), rc, o, 0, 0);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[e]), rc,
+                                                              col + e < cols_left ? o + 4u * e : OOB, 0, 0);
+                }
+            }
+        }
+    }
+}
+
 template <class Op, bool TA, bool TB, bool ACC>
 __global__ __launch_bounds__(256) void mfma_f16_pipe_kernel(RingArgs args)
 {
     const int bid = dgor_ring_split(args, 2);   // split-K: this workgroup's k-range and tile
     using namespace pipe;
+    static_assert(4 * cstage::WAVE_BYTES <= LDS_BYTES, "the epilogue stages through the ring's LDS");
     __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
     const uint32_t ring = lds_address(lds);
     const int M = args.M, N = args.N, K = args.K, lda = args.lda, ldb = args.ldb;
@@ -511,27 +571,20 @@ __global__ __launch_bounds__(256) void mfma_f16_pipe_kernel(RingArgs args)
     // no load may still be writing this workgroup's LDS when it ends
     __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
 
-    // Epilogue: write alpha times the accumulators (ACC: they started from
-    // C), each moved out of its AGPR, scaled and stored on its own
-    // (arithmetic on the array as a whole would pull it into ordinary
-    // registers, which do not fit beside the fragments; a runtime branch on
-    // alpha == 1 here makes the compiler restructure the whole kernel).  The
-    // offsets are recomputed from opaque copies: shared with the loads above,
-    // they would stay live across the loop and crowd it out.
-    int col_e = c_col, rows_e = c_rows_left;
-    asm volatile("" : "+v"(col_e), "+v"(rows_e));
+    // Epilogue: alpha times the accumulators (ACC: they started from C),
+    // each moved out of its AGPR and scaled on its own (arithmetic on the
+    // array as a whole would pull it into ordinary registers, which do not
+    // fit beside the fragments), staged through LDS once every wavefront is
+    // done with the ring.
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt_lgkm0(0));
+    __builtin_amdgcn_s_barrier();
     dgor_acc_hazard_wait();
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                uint32_t vo, so;
-                c_offset(col_e, rows_e, i, j, r, vo, so);
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dgor_acc_read(acc[i][j][r]) * args.alpha), rc,
-                                                      vo, so, 0);
-            }
+    {
+        const int rows_w = M - m0 - wr, cols_w = N - n0 - wc;
+        float *Cw = args.C + (size_t)(m0 + wr) * ldc + n0 + wc;
+        const bool vec = ((uintptr_t)Cw & 15) == 0 && (ldc & 3) == 0;
+        store_c_staged(acc, args.alpha, lds, wave, lane, Cw, ldc, rows_w, cols_w, vec);
+    }
 }
 
 // The ring kernel for a k-contiguous A (A given as M x K), with A staged two
@@ -566,6 +619,7 @@ __global__ __launch_bounds__(256) void mfma_f16_pair_kernel(RingArgs args)
     const int bid = dgor_ring_split(args, 2);   // split-K: this workgroup's k-range and tile
     using namespace pair16;
     constexpr int BK = pipe::BK;                        // 32 k per stage
+    static_assert(4 * cstage::WAVE_BYTES <= LDS_BYTES, "the epilogue stages through the ring's LDS");
     __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
     const uint32_t ring = lds_address(lds);
     const int M = args.M, N = args.N, K = args.K, lda = args.lda, ldb = args.ldb;
@@ -787,22 +841,17 @@ __global__ __launch_bounds__(256) void mfma_f16_pair_kernel(RingArgs args)
     // no load may still be writing this workgroup's LDS when it ends
     __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
 
-    // Epilogue: as in the four-stage ring (offsets recomputed from opaque
-    // copies; alpha applied one accumulator at a time).
-    int col_e = c_col, rows_e = c_rows_left;
-    asm volatile("" : "+v"(col_e), "+v"(rows_e));
+    // Epilogue: as in the four-stage ring, through LDS once every
+    // wavefront is done with the ring.
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt_lgkm0(0));
+    __builtin_amdgcn_s_barrier();
     dgor_acc_hazard_wait();
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                uint32_t vo, so;
-                c_offset(col_e, rows_e, i, j, r, vo, so);
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dgor_acc_read(acc[i][j][r]) * args.alpha), rc,
-                                                      vo, so, 0);
-            }
+    {
+        const int rows_w = M - m0 - wr, cols_w = N - n0 - wc;
+        float *Cw = args.C + (size_t)(m0 + wr) * ldc + n0 + wc;
+        const bool vec = ((uintptr_t)Cw & 15) == 0 && (ldc & 3) == 0;
+        store_c_staged(acc, args.alpha, lds, wave, lane, Cw, ldc, rows_w, cols_w, vec);
+    }
 }
 
 template <class Op, int BM, int BN, int BK, int WM, int WN>
