@@ -244,3 +244,34 @@ def test_channels_last_conv_kernel_streams_cleanly(tmp_path):
             elif re.search(r"\bm0\b", code) and not inside:
                 outside_m0.append(code.strip())
         assert dma > 0 and outside_m0 == [], (sym, outside_m0[:3])
+
+
+def test_calibration_loop_is_bare_mfmas(tmp_path):
+    """The matrix-core rate calibration kernel (calibrate.hip, its own
+    library) measures the ceiling of the 256 x 256 tile's MFMA stream only if
+    its k-loop is that stream and nothing else: the loop body holds the two
+    stages' 128 v_mfma_f32_16x16x32_f16 of a trip, no accumulator moves, no
+    memory instruction, and the kernel spills nothing."""
+    if shutil.which("hipcc") is None and not os.path.exists("/opt/rocm/bin/hipcc"):
+        pytest.skip("hipcc not available")
+    out = tmp_path / "calibrate.s"
+    cmd = [hipbuild.hipcc(), *hipbuild.FLAGS, "-S", "--cuda-device-only",
+           os.path.join(hipbuild.CSRC, "calibrate.hip"), "-o", str(out)]
+    subprocess.run(cmd, check=True, capture_output=True, text=True)
+    text = out.read_text()
+    [(sym, body)] = _instances(text, "mfma_f16_rate_kernel")
+    priv = re.search(rf"^\s*\.set\s+{re.escape(sym)}\.private_seg_size,\s*(\d+)", text, flags=re.M)
+    assert priv and int(priv.group(1)) == 0, "scratch (spill) memory in use"
+    # the loop: from the block a backward branch returns to, up to that branch
+    loops = []
+    for m in re.finditer(r"^\s*s_cbranch_\w+\s+(\.LBB\w+)", body, flags=re.M):
+        label = re.search(rf"^{re.escape(m.group(1))}:", body, flags=re.M)
+        if label and label.start() < m.start():
+            loops.append(body[label.end():m.start()])
+    assert len(loops) == 1, f"{len(loops)} loops"
+    code = [ln.split(";")[0].strip() for ln in loops[0].splitlines()]
+    code = [c for c in code if c and not c.startswith(".")]
+    mfma = [c for c in code if c.startswith("v_mfma_f32_16x16x32_f16")]
+    assert len(mfma) == 128, len(mfma)
+    assert not [c for c in code if c.startswith(("v_accvgpr", "buffer_", "global_", "ds_", "scratch_", "v_mov"))], \
+        [c for c in code if not c.startswith("v_mfma")]
