@@ -309,13 +309,36 @@ def _time_calls(fn, torch, stream, reps):
     return e0.elapsed_time(e1) / reps
 
 
+def _time_cold(fn, torch, stream, flush, reps):
+    """Milliseconds per call of ``fn`` with the caches cold: before each call
+    a fill of ``flush`` (larger than the memory-side cache and every L2
+    together) evicts the operands, and only the call itself lies between the
+    events."""
+    total = 0.0
+    for i in range(reps):
+        with torch.cuda.stream(stream):
+            flush.fill_(i & 0xff)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        total += e0.elapsed_time(e1)
+    return total / reps
+
+
 def all_workloads(dg, inputs, torch, dev, stream, dev_in, wl):
     """2MNK/t and fraction of the matrix peak for every workload, each timed
     on its own after the main timed region (the headline ones reuse their
-    resident inputs)."""
+    resident inputs).  Calls of at least 0.1 ms are also timed with the
+    caches cold (their operands, 128 to 384 MiB, are about the size of the
+    256 MB memory-side cache, so warm back-to-back calls may be served from
+    it)."""
     import numpy as np
 
     res = {}
+    flush = None
     for name, w in inputs.WORKLOADS.items():
         kind = w.dtype
         if wl.get(kind) is not None and wl[kind].name == name and kind in dev_in:
@@ -341,6 +364,13 @@ def all_workloads(dg, inputs, torch, dev, stream, dev_in, wl):
                      "algorithmic_bytes": nbytes, "achieved_gbs": round(gbs, 1),
                      "frac_of_hbm": round(gbs / HBM_PEAK_GBS, 4), "bound": bound,
                      "kernel": dg.variant_name(p["variant"]), "tile": [p["tile_m"], p["tile_n"]]}
+        if ms >= 0.1:
+            if flush is None:
+                flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)   # 1 GiB
+            cms = _time_cold(lambda: f(a, b, c, stream), torch, stream, flush, 10)
+            ctf = w.flops / (cms * 1e-3) / 1e12
+            res[name].update({"ms_cold": round(cms, 5), "tflops_cold": round(ctf, 3),
+                              "frac_of_peak_cold": round(ctf / PEAK_TFLOPS[kind], 4)})
         if ms < 0.1:
             # short calls: also timed as a replayed HIP graph of back-to-back
             # calls, which takes the host's per-call launch cost out
@@ -354,6 +384,7 @@ def all_workloads(dg, inputs, torch, dev, stream, dev_in, wl):
                                   "achieved_gbs_graph": round(ggbs, 1),
                                   "frac_of_hbm_graph": round(ggbs / HBM_PEAK_GBS, 4),
                                   "graph_matches_eager": same})
+    del flush
     return res
 
 
