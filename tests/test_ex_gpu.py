@@ -221,3 +221,47 @@ def test_ex_large_transposed_sampled(case, layout):
     plain = tol_f32(K) if fmt == "f32" else tol_f16(K, np.abs(ab))
     tol = alpha * plain + 8 * EPS32 * (alpha * float(np.abs(ab).max()) + abs(beta))
     assert np.max(np.abs(got - want)) <= tol
+
+
+def _run_c_case(fmt, op_a, op_b, shape, c_pad, c_off, alpha, beta, seed):
+    """Unpadded A and B (so the ring kernels run on the multiple-of-8 shapes)
+    with C's rows ``c_pad`` elements apart beyond N and C's first element
+    ``c_off`` floats into its buffer: the ring epilogue's element-wise stores
+    whenever C is not 16-byte aligned or ldc not a multiple of 4.  Integer
+    inputs, bit-exact; every element around C must keep its sentinel."""
+    import torch
+    M, N, K = shape
+    A, B = _mats(fmt, M, N, K, seed, "int")
+    C0 = np.random.default_rng(seed + 1).integers(-1000, 1001, (M, N)).astype(np.float32)
+    lda, ldb, ldc = (M if op_a else K), (K if op_b else N), N + c_pad
+    As, Bs = _store(A, op_a, lda, _nan_of(A)), _store(B, op_b, ldb, _nan_of(B))
+    Cs = np.full(M * ldc, -3.5, np.float32)
+    Cs.reshape(M, ldc)[:, :N] = C0
+    buf = np.concatenate([np.full(c_off, -7.25, np.float32), Cs, np.full(4, -7.25, np.float32)])
+    a, b, cbuf = to_dev(As), to_dev(Bs), to_dev(buf)
+    c_ptr = cbuf.data_ptr() + 4 * c_off
+    assert (c_ptr % 16 == 0) == (c_off % 4 == 0)
+    rc = binding.raw_gemm_ex(fmt, op_a, op_b, M, N, K, alpha, a.data_ptr(), lda, b.data_ptr(), ldb,
+                             beta, c_ptr, ldc, None)
+    assert rc == binding.GEMM_OK, binding.status_string(rc)
+    torch.cuda.synchronize()
+    out = cbuf.cpu().numpy()
+    what = f"{fmt} op{op_a}{op_b} {shape} ldc N+{c_pad} C +{c_off} floats alpha {alpha} beta {beta}"
+    assert np.all(out[:c_off] == np.float32(-7.25)) and np.all(out[c_off + M * ldc:] == np.float32(-7.25)), \
+        f"{what}: written outside C's storage"
+    got = out[c_off:c_off + M * ldc].reshape(M, ldc)
+    want = _oracle(fmt, op_a, op_b, M, N, K, alpha, As, lda, Bs, ldb, beta, Cs, ldc).reshape(M, ldc)
+    assert np.all(got[:, N:] == np.float32(-3.5)), f"{what}: C padding written"
+    bad = got[:, :N] != want[:, :N]
+    assert not bad.any(), f"{what}: {int(bad.sum())} elements differ, first {np.argwhere(bad)[0]}"
+
+
+@pytest.mark.parametrize("fmt", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("layout", LAYOUTS, ids=lambda l: f"op{l[0]}{l[1]}")
+def test_ring_epilogue_with_unaligned_c(fmt, layout):
+    op_a, op_b = layout
+    for shape in SHAPES[:2]:
+        for c_pad, c_off in ((1, 0), (3, 0), (0, 1), (4, 2), (0, 3)):
+            say("ex unaligned C", fmt, layout, shape, c_pad, c_off)
+            for alpha, beta in ((1.0, 0.0), (2.0, 0.5)):
+                _run_c_case(fmt, op_a, op_b, shape, c_pad, c_off, alpha, beta, 3300 + c_pad + 10 * c_off)
