@@ -15,7 +15,8 @@ wrong.  So every case here runs on small-integer inputs and must equal the
 oracle bit for bit: the stage-count cases of every ring (one to several
 stages, full and ragged, prologue and drain), the transposed-A pipe ring, the
 128 x 128 two-stage kernel, the tall, narrow kernel's per-wavefront B copies,
-and FP32 4096^3 in full.
+FP32 4096^3 in full, and the channels-last convolution kernel's ring (both
+tile configurations, 1 to 9 stages).
 """
 import numpy as np
 import pytest
@@ -108,3 +109,42 @@ def test_f32_4096_in_full_with_poisoned_lds(lib):
     say("poisoned LDS", "f32_4096 integer variant in full")
     A, B = inputs.workload_matrices("f32_4096", True)
     assert_bits_equal(_run(lib, "f32", A, B), oracle.gemm_f32(A, B), "f32_4096 ints (poisoned LDS)")
+
+
+# channels-last convolution layers (16-bit, C a multiple of 32): both tile
+# configurations, 1, 2, 3 and 9 stages of their ring, ragged filter tiles
+CONV_CASES = [
+    (32, 32, 28, 28, 64, 1, 1, (1, 1), (0, 0)),    # 64 x 256 x 32 tiles, 1 stage
+    (32, 64, 28, 28, 64, 1, 1, (1, 1), (0, 0)),    # 2 stages
+    (32, 32, 28, 28, 48, 3, 3, (1, 1), (1, 1)),    # 9 stages, 48 of 64 filters
+    (8, 96, 28, 28, 96, 1, 1, (1, 1), (0, 0)),     # 128 x 64 x 32 tiles, 3 stages
+    (8, 64, 28, 28, 200, 3, 3, (1, 1), (1, 1)),    # 128 x 64 x 64 tiles, 9 stages, 2 filter tiles
+    (8, 128, 28, 28, 128, 1, 1, (1, 1), (0, 0)),   # 2 stages
+    (8, 64, 28, 28, 130, 1, 1, (1, 1), (0, 0)),    # 1 stage, a 2-filter last tile
+]
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+@pytest.mark.parametrize("case", CONV_CASES, ids=lambda c: "x".join(map(str, c[:7])))
+def test_channels_last_conv_with_poisoned_lds(lib, fmt, case):
+    import torch
+    N, C, H, W, K, R, S, st, pd = case
+    prm = binding.conv_params(N, C, H, W, K, R, S, st, pd)
+    assert binding.conv2d_algorithm(prm, 2) == binding.CONV_IMPLICIT_NHWC
+    say("poisoned LDS, channels-last conv", fmt, case)
+    x = inputs.matrices(1, 1, N * C * H * W, 9300 + K, "int", fmt)[0].reshape(N, C, H, W)
+    w = inputs.matrices(1, 1, K * C * R * S, 9400 + K, "int", fmt)[0].reshape(K, C, R, S)
+    P = (H + 2 * pd[0] - R) // st[0] + 1
+    Q = (W + 2 * pd[1] - S) // st[1] + 1
+    y = torch.full((N, K, P, Q), 7.0, device="cuda")
+    ws = torch.empty(binding.conv2d_workspace(prm, 2), dtype=torch.uint8, device="cuda")
+    xd, wd = _dev(x), _dev(w)
+    stem = "gemm_conv2d_f16_f32acc" if fmt == "f16" else "gemm_conv2d_bf16_f32acc"
+    import ctypes
+    rc = getattr(lib, stem)(ctypes.byref(prm), xd.data_ptr(), wd.data_ptr(), y.data_ptr(), ws.data_ptr(),
+                            ws.numel(), None)
+    assert rc == binding.GEMM_OK, binding.status_string(rc)
+    torch.cuda.synchronize()
+    got = y.cpu().numpy()
+    assert np.all(np.isfinite(got)), "poison (NaN) reached y"
+    assert_bits_equal(got, oracle.conv2d(fmt, x, w, st, pd), f"{fmt} conv {case} (poisoned LDS)")
