@@ -156,21 +156,20 @@ int plan_f32(int variant, int M, int N, int K, const void *A, const void *B, con
             break;
         }
         dgor::F32SkinnyPlan nw;
-        if (dgor::f32_skinny_plan(M, N, K, B, nw)) {
+        if (dgor::f32_skinny_plan(M, N, K, nw)) {
             // one workgroup per 16 rows (grid_y), all columns (tile_n: the
             // MFMA blocks, plus 1 for a column summed on the vector ALUs) and
-            // all of K in eight runs of 16-deep slices.  LDS holds the
-            // partial sums (8 wavefronts x nb blocks x 1 KB; with the fringe
-            // column its partial sums and, when B goes to registers, B's
-            // last column) and, as one stage, the wavefronts' runs of B rows
-            // when they fit (8 x 16 KB)
+            // all of K in eight runs of 16-deep slices; with at most two
+            // blocks each wavefront holds its whole run of B in LDS (8
+            // slices), else it streams the run through a ring of LDS slots
             p->tile_m = 16;
             p->tile_n = 16 * nw.nb + (nw.fringe ? 1 : 0);
             p->tile_k = 16 * ((K + 15) / 16);
             p->threads = 512;
-            p->lds_stages = nw.ldsb ? 1 : 0;
-            p->lds_bytes = 8 * nw.nb * 1024 + (nw.fringe ? 4 * ((nw.ldsb ? 0 : dgor::kF32SkinnyMaxK) + 512) : 0) +
-                           32 + (nw.ldsb ? 8 * dgor::kF32SkinnyBRegion : 0);
+            const bool resident = nw.nb <= 2;
+            p->lds_stages = resident ? dgor::kF32SkinnyMaxK / 128 : dgor::skinny_slots(nw.nb);
+            p->lds_bytes = 8 * (resident ? dgor::skinny_resident_wave_bytes(nw.nb, nw.fringe)
+                                         : dgor::skinny_wave_bytes(nw.nb, nw.fringe)) + 32;
             p->tile_bytes = (16 * K + K * N) * 4;
             p->outputs_per_thread = (16 * N + 511) / 512;
             p->vector_c = 0;

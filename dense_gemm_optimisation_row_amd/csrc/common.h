@@ -187,32 +187,41 @@ inline bool f32_small_ring_applies(int tile_m, int tile_n, int N, int K, bool ve
            (long long)(K + kF32SmallDepth) * N < (1LL << 29);
 }
 
-// Tall, narrow FP32 problems (1 <= N <= 64, 1 <= K <= kF32SkinnyMaxK, any
-// alignment): workgroups of 16 rows and 8 wavefronts, nb MFMA blocks of 16
-// columns; with fringe (N % 16 == 1, N > 16) the last column is summed on the
-// vector ALUs instead of in a block of its own; with tail (M % 16 == 1 and at
-// least N whole row blocks) the last row is spread over workgroups 0..N-1
-// instead of getting one of its own; with ldsb (B 16-byte aligned, a
-// wavefront's run of B rows within kF32SkinnyBRegion bytes, and at most 3
-// blocks, so that the 8 regions and the partial sums fit the 160 KB of LDS)
-// each wavefront copies its rows of B into LDS, else B goes straight into
-// registers.
+// Tall, narrow FP32 problems (1 <= N <= 64, 1 <= K <= kF32SkinnyMaxK, A and
+// B 4-byte aligned): workgroups of 16 rows and 8 wavefronts, nb MFMA blocks
+// of 16 columns; with fringe (N % 16 == 1, N > 16) the last column is summed
+// on the vector ALUs instead of in a block of its own; with tail (M % 16 == 1
+// and at least N whole row blocks) the last row is spread over workgroups
+// 0..N-1 instead of getting one of its own.  Each wavefront streams its
+// 16-deep k-slices through its own ring of skinny_slots(nb) LDS slots of
+// skinny_slot_bytes(nb, fringe) bytes (the 16 x 16 piece of A, 16 rows of B's
+// first 16 nb columns, B's last column), plus 1 KB for the tail row's
+// products: at most 147,456 bytes for the 8 wavefronts.
 constexpr int kF32SkinnyMaxK = 1024;
-constexpr int kF32SkinnyBRegion = 16384;
-struct F32SkinnyPlan { int nb, blocks; bool fringe, tail, ldsb; };
-inline bool f32_skinny_plan(int M, int N, int K, const void *B, F32SkinnyPlan &n)
+constexpr int skinny_slots(int nb) { return nb <= 3 ? 4 : 3; }
+constexpr int skinny_slot_bytes(int nb, bool fringe) { return 1024 * (1 + nb) + (fringe ? 256 : 0); }
+constexpr int skinny_wave_bytes(int nb, bool fringe)
 {
-    if (N < 1 || N > 64 || K < 1 || K > kF32SkinnyMaxK || M < 1 || (long long)M * K * 4 >= (1LL << 31))
+    return skinny_slots(nb) * skinny_slot_bytes(nb, fringe) + 1024;
+}
+// With at most two column blocks a wavefront instead keeps its whole run of
+// B (8 slices of nb KB) and, with fringe, B's last column (512 bytes) in LDS
+// at once.
+constexpr int skinny_resident_wave_bytes(int nb, bool fringe)
+{
+    return (kF32SkinnyMaxK / 128) * 1024 * nb + (fringe ? 512 : 0);
+}
+struct F32SkinnyPlan { int nb, blocks; bool fringe, tail; };
+inline bool f32_skinny_plan(int M, int N, int K, F32SkinnyPlan &n)
+{
+    if (N < 1 || N > 64 || K < 1 || K > kF32SkinnyMaxK || M < 1 || (long long)M * K * 4 >= (1LL << 31) ||
+        (long long)M * N * 4 >= (1LL << 31))
         return false;
     n.fringe = N > 16 && N % 16 == 1;
     n.nb = n.fringe ? N / 16 : (N + 15) / 16;
     const int full = M / 16, rem = M % 16;
     n.tail = rem == 1 && full >= N;
     n.blocks = full + (rem != 0 && !n.tail ? 1 : 0);
-    // the longest run of rows a wavefront takes: ceil(slices / 8) slices
-    const int run_rows = 16 * (((K + 15) / 16 + 7) / 8);
-    const int run_bytes = (run_rows * N * 4 + 1023) / 1024 * 1024;
-    n.ldsb = ((uintptr_t)B & 15) == 0 && run_bytes <= kF32SkinnyBRegion && n.nb <= 3;
     return true;
 }
 

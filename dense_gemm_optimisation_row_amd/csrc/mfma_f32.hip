@@ -796,245 +796,24 @@ __global__ __launch_bounds__(128 * WN) void mfma_f32_small_ring_kernel(int M, in
 }
 
 // ---------------------------------------------------------------------------
-// Tall, narrow FP32 problems (N <= 64, K <= 1024, any alignment).  Their time
-// is one read of A from HBM (B and C are small), so every compute unit streams
-// its share of A from the start, and no k-loop waits on memory stage by stage.
-// A workgroup takes 16 rows, all N columns and all of K with eight wavefronts
-// (two per SIMD); wavefront w takes a contiguous run [kb, ke) of the 16-deep
-// k-slices, the runs as even as the slice count allows.  Each lane issues all
-// of its loads at once: its A values straight into registers (16-byte units,
-// four consecutive k of its row; four 4-byte loads for the one unit that runs
-// past K), from HBM; and B, which every workgroup reads whole and so stays in
-// L2, either
-//   LDSB: the wavefront's own rows kb..ke of B copied into its own 16 KB of
-//     LDS by direct global->LDS loads of whole 1 KB runs (no barrier: only
-//     the wavefront reads them), then read two floats at a time; or
-//   otherwise (B rows of a run too long for 16 KB, or B not 16-byte aligned):
-//     one load of NB adjacent floats per lane and k, straight into registers.
-// It then runs v_mfma_f32_16x16x4_f32 slice by slice as the loads land (the
-// compiler waits with vmcnt on the registers a slice needs).  The k
-// assignment is that of the 64 x 64 ring kernel: in instruction e of slice s,
-// lane l holds A[l % 16][k] and, for column block c, B[k][NB (l % 16) + c],
-// with k = kb + 16 s + 4 (l / 16) + e (column block c holds the columns
-// NB j + c, so a lane's B values of one k are adjacent).  The eight partial
-// sums of an output are added in LDS in order of w, so results do not depend
-// on timing.
-//   FRINGE (N % 16 == 1, N > 16): the last column is not given a 16-column
-//     block of its own (that block would cost as much matrix-core time as a
-//     full one); its sums are formed on the vector ALUs from the A registers.
-//   tail (M % 16 == 1 with at least N whole row blocks): the last row gets no
-//     workgroup of its own (that workgroup would share a compute unit with
-//     another and double its matrix-core time); workgroup j < N instead forms
-//     C[M - 1][j] as a dot product spread over its 512 lanes (two products a
-//     lane, a butterfly sum in each wavefront, then the eight wavefront sums
-//     in order).
-template <int NB, bool FRINGE, bool LDSB>
-__global__ __launch_bounds__(512) void mfma_f32_skinny_kernel(int M, int N, int K, int tail, const float *A,
-                                                              const float *B, float *C)
+// The end of both tall, narrow kernels, after the barrier that follows the
+// partial sums: wavefront w's sums of column block c sit at 64 floatx4 from
+// sh + w * area + 1024 c, its sums of the last column (FRINGE) at 64 floats
+// from sh + w * area + 1024 NB, its tail-row sum at tpart[w].  They are added
+// in order of w, and wavefront c < NB stores block c.
+template <int NB, bool FRINGE>
+__device__ __forceinline__ void skinny_finish(const uint8_t *sh, int area, const float *tpart, int M, int N,
+                                              bool tl, float *C)
 {
-    constexpr int QMAX = kF32SkinnyMaxK / (16 * 8);   // slices per wavefront at most
-    constexpr int REGION = LDSB ? kF32SkinnyBRegion : 4;   // bytes of B per wavefront
-    __shared__ __attribute__((aligned(1024))) uint8_t bsh[LDSB ? 8 * REGION : 16];
-    __shared__ floatx4 part[8][NB][64];
-    __shared__ float fcol[FRINGE && !LDSB ? kF32SkinnyMaxK : 1];
-    __shared__ float fpart[FRINGE ? 8 * 64 : 1];
-    __shared__ float tpart[8];
+    constexpr uint32_t OOB = 0x80000000u;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-    const int r16 = lane & 15, h = lane >> 4;
-    const int m0 = blockIdx.x * 16, row = m0 + r16;
-    const int total = (K + 15) / 16;
-    const int s_lo = wave * total / 8, s_hi = (wave + 1) * total / 8;
-    const int slices = s_hi - s_lo, kb = 16 * s_lo, ke = min(K, 16 * s_hi);
-    constexpr uint32_t OOB = 0x80000000u;
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, (long long)M * K * 4);
-    const __amdgpu_buffer_rsrc_t rb = make_rsrc(B, (long long)K * N * 4);
-    const float *bw = reinterpret_cast<const float *>(bsh + (LDSB ? wave * REGION : 0));
-
-    // LDSB: rows kb..ke of B (a contiguous run of bytes, 16-byte aligned as
-    // kb is a multiple of 16 and B is 16-byte aligned) into this wavefront's
-    // region, whole 1 KB runs; past K they read zeros.  Issued first: the
-    // wait before the first read of them counts only the loads issued after.
-    if constexpr (LDSB) {
-        const intx4 rsb = rsrc_words(B, (long long)K * N * 4);
-        const uint32_t dst = lds_address(bsh) + (uint32_t)(wave * REGION);
-        const uint32_t src = (uint32_t)(kb * N) * 4u;
-        const int runs = ((ke - kb) * N * 4 + 1023) / 1024;
-        for (int j = 0; j < runs; ++j)
-            load_to_lds(rsb, dst + (uint32_t)(j * 1024), src + (uint32_t)(j * 1024 + lane * 16));
-    }
-    // the unit of the last slice that runs past K (K not a multiple of 4):
-    // four 4-byte loads, taken in place of that slice's (then empty) 16-byte
-    // unit when its MFMAs run (issued early, so that reading them, which the
-    // compiler may do as early as slice 0, waits for no slice's loads)
-    const int k_last = kb + 16 * (slices - 1) + 4 * h;
-    const bool cross = slices > 0 && row < M && k_last < ke && k_last + 4 > ke;
-    float x[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-        x[e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-            ra, cross && k_last + e < ke ? (uint32_t)(row * K + k_last + e) * 4u : OOB, 0, 0));
-    // B's last column (FRINGE, B in registers): thread t loads k = t and t + 512
-    float fv[2] = {0.f, 0.f};
-    if (FRINGE && !LDSB) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int k = (int)threadIdx.x + 512 * i;
-            fv[i] = __uint_as_float(
-                __builtin_amdgcn_raw_buffer_load_b32(rb, k < K ? (uint32_t)(k * N + N - 1) * 4u : OOB, 0, 0));
-        }
-    }
-    // the tail row's products: this wavefront's k, two a lane
-    const bool tl = tail && (int)blockIdx.x < N;
-    float ta[2], tb[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int k = kb + lane + 64 * i;
-        const bool ok = tl && k < ke;
-        ta[i] = __uint_as_float(
-            __builtin_amdgcn_raw_buffer_load_b32(ra, ok ? (uint32_t)((M - 1) * K + k) * 4u : OOB, 0, 0));
-        tb[i] = __uint_as_float(
-            __builtin_amdgcn_raw_buffer_load_b32(rb, ok ? (uint32_t)(k * N + blockIdx.x) * 4u : OOB, 0, 0));
-    }
-    // A (and, without LDSB, B) of every slice.  No load sits under a branch:
-    // one that did would make the compiler wait for earlier loads at the join.
-    // Loads of one NB-float group of B keep a wavefront's loads under the 63
-    // the wait counter can tell apart.
-    floatx4 a[QMAX];
-    float b[LDSB ? 1 : QMAX][4][NB];
-#pragma unroll
-    for (int s = 0; s < QMAX; ++s) {
-        const int k = kb + 16 * s + 4 * h;
-        const bool live = s < slices && row < M && k + 4 <= ke;
-        a[s] = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(
-                                               ra, live ? (uint32_t)(row * K + k) * 4u : OOB, 0, 0));
-        if constexpr (!LDSB) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int kk = k + e;
-                const uint32_t off = s < slices && kk < ke ? (uint32_t)(kk * N + NB * r16) * 4u : OOB;
-                if constexpr (NB == 1) {
-                    b[s][e][0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb, off, 0, 0));
-                } else if constexpr (NB == 2) {
-                    const auto v = __builtin_amdgcn_raw_buffer_load_b64(rb, off, 0, 0);
-                    b[s][e][0] = __uint_as_float(v[0]);
-                    b[s][e][1] = __uint_as_float(v[1]);
-                } else if constexpr (NB == 3) {
-                    const auto v = __builtin_amdgcn_raw_buffer_load_b96(rb, off, 0, 0);
-#pragma unroll
-                    for (int c = 0; c < 3; ++c)
-                        b[s][e][c] = __uint_as_float(v[c]);
-                } else {
-                    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0);
-#pragma unroll
-                    for (int c = 0; c < 4; ++c)
-                        b[s][e][c] = __uint_as_float(v[c]);
-                }
-            }
-        }
-        // issue the slices in order (the scheduler would otherwise group the
-        // loads by kind and leave slice 0's A among the last)
-        __builtin_amdgcn_sched_barrier(0);
-    }
-    // every load above is issued before the first MFMA: none may be sunk
-    // into the slice branches below (the memory clobber forbids moving a
-    // load past it, and reads no register, so it waits for nothing)
-    asm volatile("" ::: "memory");
-    if constexpr (LDSB) {
-        // the copies of B have landed once no more than the loads issued
-        // after them (x, tail, A) are outstanding
-        __builtin_amdgcn_s_waitcnt(wait_vmcnt(4 + 4 + QMAX));
-        asm volatile("" ::: "memory");
-    }
-
-    floatx4 acc[NB];
-#pragma unroll
-    for (int c = 0; c < NB; ++c)
-        acc[c] = floatx4{0.f, 0.f, 0.f, 0.f};
-    // with LDSB, the last column of this lane's row over this lane's k is
-    // summed here too, from the wavefront's rows of B, beside the MFMAs
-    float f = 0.f;
-#pragma unroll
-    for (int s = 0; s < QMAX; ++s) {
-        if (s < slices) {   // wave-uniform
-            if (s == slices - 1) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    a[s][e] = cross ? x[e] : a[s][e];
-            }
-            float bv[4][NB], fb[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                if constexpr (LDSB) {   // rows past ke hold no copy of B
-                    const int kk = kb + 16 * s + 4 * h + e;
-#pragma unroll
-                    for (int c = 0; c < NB; ++c)
-                        bv[e][c] = kk < ke ? bw[(kk - kb) * N + NB * r16 + c] : 0.f;
-                    if constexpr (FRINGE)
-                        fb[e] = kk < ke ? bw[(kk - kb) * N + N - 1] : 0.f;
-                } else {
-#pragma unroll
-                    for (int c = 0; c < NB; ++c)
-                        bv[e][c] = b[s][e][c];
-                }
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-#pragma unroll
-                for (int c = 0; c < NB; ++c)
-                    acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s][e], bv[e][c], acc[c], 0, 0, 0);
-            if constexpr (FRINGE && LDSB) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    f = fmaf(a[s][e], fb[e], f);
-            }
-        }
-    }
-    if constexpr (FRINGE && LDSB)
-        fpart[wave * 64 + lane] = f;
-    // partial sums into LDS: wavefront w's block c at part[w][c]; lane l
-    // holds rows 4 (l / 16) + r of column NB (l % 16) + c
-#pragma unroll
-    for (int c = 0; c < NB; ++c)
-        part[wave][c][lane] = acc[c];
-    if (FRINGE && !LDSB) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int k = (int)threadIdx.x + 512 * i;
-            if (k < K)
-                fcol[k] = fv[i];
-        }
-    }
-    // tail: this wavefront's sum of its products (butterfly, fixed order)
-    float tv = ta[0] * tb[0] + ta[1] * tb[1];
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1)
-        tv += __shfl_xor(tv, d);
-    if (lane == 0)
-        tpart[wave] = tv;
-    __syncthreads();
-
-    if constexpr (FRINGE && !LDSB) {   // B's last column is in LDS only now
-#pragma unroll
-        for (int s = 0; s < QMAX; ++s) {
-            if (s < slices) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int k = kb + 16 * s + 4 * h + e;
-                    f = fmaf(a[s][e], k < ke ? fcol[k] : 0.f, f);
-                }
-            }
-        }
-        fpart[wave * 64 + lane] = f;
-        __syncthreads();
-    }
-
-    // sums in order of w, and the stores: wavefront c < NB takes block c
+    const int r16 = lane & 15, h = lane >> 4, m0 = blockIdx.x * 16;
     if (wave < NB) {
-        floatx4 v = part[0][wave][lane];
+        floatx4 v = reinterpret_cast<const floatx4 *>(sh)[64 * wave + lane];
 #pragma unroll
         for (int w = 1; w < 8; ++w)
-            v += part[w][wave][lane];
+            v += reinterpret_cast<const floatx4 *>(sh + w * area)[64 * wave + lane];
         const int col = NB * r16 + wave;
         const __amdgpu_buffer_rsrc_t rc = make_rsrc(C, (long long)M * N * 4);
 #pragma unroll
@@ -1050,7 +829,7 @@ __global__ __launch_bounds__(512) void mfma_f32_skinny_kernel(int M, int N, int 
         for (int w = 0; w < 8; ++w)
 #pragma unroll
             for (int g = 0; g < 4; ++g)
-                v += fpart[w * 64 + 16 * g + lane];
+                v += reinterpret_cast<const float *>(sh + w * area + 1024 * NB)[16 * g + lane];
         C[(size_t)(m0 + lane) * N + N - 1] = v;
     }
     if (tl && wave == 6 && lane == 0) {
@@ -1062,18 +841,368 @@ __global__ __launch_bounds__(512) void mfma_f32_skinny_kernel(int M, int N, int 
     }
 }
 
+// Tall, narrow FP32 problems (N <= 64, K <= 1024, A and B 4-byte aligned).
+// Their time is one read of A from HBM (B and C are small), so every compute
+// unit streams its share of A from the start.  This kernel takes three and
+// four column blocks; the resident form below takes one and two.  A workgroup takes 16 rows, all
+// N columns and all of K with eight wavefronts (two per SIMD); wavefront w
+// takes a contiguous run [kb, ke) of the 16-deep k-slices, the runs as even
+// as the slice count allows, and streams it through its own ring of LDS
+// slots, so no wavefront waits for another until the partial sums are added.
+// A slice is LW direct global->LDS loads into one slot:
+//   A: lane (r, h) = (l % 16, l / 16) fetches A[m0 + r][k0 + 4h .. + 3] (16
+//      bytes, 4-byte aligned; a unit that runs past K brings the next row's
+//      values, which are zeroed on reading, and past the end of A reads zero);
+//   B: the slice's 16 rows of B's first 16 NB columns, NB loads of 64 units
+//      of 16 bytes.  Row 4g + e of the slice sits at position 4g + ((e + g) &
+//      3): the four rows the lane groups h read at once then fall in distinct
+//      banks;
+//   fringe (FRINGE): B's last column of the slice's rows, 4 bytes a lane.
+// Rows past ke read zero (B rows past K hold zeros, and a row of the next
+// run is never fetched, so no value outside [kb, ke) enters a sum).  D = R - 1
+// slices are in flight while one is computed; the wait for slice s counts the
+// loads issued after it, and a slot is refilled only once its last reads have
+// returned.  A slice's arithmetic: in instruction e, lane l holds A[l % 16][k]
+// and, for column block c, B[k][NB (l % 16) + c], with k = k0 + 4 (l / 16) +
+// e (column block c holds the columns NB j + c, so a lane's NB values of one
+// row are adjacent: one 8-byte read for NB = 2, one 16-byte read for NB = 4).
+// The eight partial sums of an output are added in LDS in order of w, so
+// results do not depend on timing.
+//   FRINGE (N % 16 == 1, N > 16): the last column is not given a 16-column
+//     block of its own (that block would cost as much matrix-core time as a
+//     full one); its sums are formed on the vector ALUs.
+//   tail (M % 16 == 1 with at least N whole row blocks): the last row gets no
+//     workgroup of its own (that workgroup would share a compute unit with
+//     another and double its matrix-core time); workgroup j < N instead forms
+//     C[M - 1][j] as a dot product spread over its 512 lanes (two products a
+//     lane, a butterfly sum in each wavefront, then the eight wavefront sums
+//     in order).
+template <int NB, bool FRINGE>
+__global__ __launch_bounds__(512) void mfma_f32_skinny_kernel(int M, int N, int K, int tail, const float *A,
+                                                              const float *B, float *C)
+{
+    constexpr int R = skinny_slots(NB);                  // ring slots per wavefront
+    constexpr int D = R - 1;                             // slices in flight ahead of the computed one
+    constexpr int SLOT = skinny_slot_bytes(NB, FRINGE);
+    constexpr int AREA = skinny_wave_bytes(NB, FRINGE);  // ring + the tail row's products
+    constexpr int LW = 1 + NB + (FRINGE ? 1 : 0);        // loads per slice
+    constexpr int U = 4 * NB;                            // 16-byte units per B row
+    constexpr int QMAX = kF32SkinnyMaxK / (16 * 8);      // slices per wavefront at most
+    constexpr uint32_t OOB = 0x80000000u;
+    __shared__ __attribute__((aligned(1024))) uint8_t sh[8 * AREA];
+    __shared__ float tpart[8];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int r16 = lane & 15, h = lane >> 4;
+    const int m0 = blockIdx.x * 16, row = m0 + r16;
+    const int total = (K + 15) / 16;
+    const int s_lo = wave * total / 8, s_hi = (wave + 1) * total / 8;
+    const int slices = s_hi - s_lo, kb = 16 * s_lo, ke = min(K, 16 * s_hi);
+    const intx4 ra = rsrc_words(A, (long long)M * K * 4);
+    const intx4 rb = rsrc_words(B, (long long)K * N * 4);
+    uint8_t *mine = sh + wave * AREA;
+    const uint32_t ring = lds_address(mine);
+
+    // this lane's B units: unit t = 64 j + lane of the slice sits at position
+    // p = t / U, column unit t % U, and holds row i of the slice
+    int b_row[NB];
+    uint32_t b_off[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+        const int t = 64 * j + lane, p = t / U, u = t % U, g = p >> 2;
+        b_row[j] = 4 * g + (((p & 3) - g) & 3);
+        b_off[j] = (uint32_t)(b_row[j] * N + 4 * u) * 4u;
+    }
+    // the positions this lane reads B rows 4h + e from
+    int b_rd[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        b_rd[e] = 1024 + (4 * h + ((e + h) & 3)) * U * 16 + NB * r16 * 4;
+
+    auto issue = [&](int s) __attribute__((always_inline)) {
+        const int k0 = kb + 16 * s;
+        const uint32_t slot = ring + (uint32_t)((s % R) * SLOT);
+        const int ka = k0 + 4 * h;
+        load_to_lds(ra, slot, row < M && ka < ke ? (uint32_t)(row * K + ka) * 4u : OOB);
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+            load_to_lds(rb, slot + 1024u * (j + 1),
+                        k0 + b_row[j] < ke ? (uint32_t)(k0 * N) * 4u + b_off[j] : OOB);
+        if constexpr (FRINGE)
+            load_dword_to_lds(rb, slot + 1024u * (NB + 1),
+                              lane < 16 && k0 + lane < ke ? (uint32_t)((k0 + lane) * N + N - 1) * 4u : OOB);
+    };
+
+    // the tail row's products, issued first (older than every slice, so the
+    // slice waits need not count them): this wavefront's k, two a lane
+    const bool tl = tail && (int)blockIdx.x < N;
+    if (tl) {
+        const uint32_t dst = ring + (uint32_t)(R * SLOT);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int k = kb + lane + 64 * i;
+            load_dword_to_lds(ra, dst + 256u * i, k < ke ? (uint32_t)((M - 1) * K + k) * 4u : OOB);
+            load_dword_to_lds(rb, dst + 256u * (2 + i), k < ke ? (uint32_t)(k * N + (int)blockIdx.x) * 4u : OOB);
+        }
+    }
+#pragma unroll
+    for (int s = 0; s < D; ++s)
+        if (s < slices)
+            issue(s);
+
+    floatx4 acc[NB];
+#pragma unroll
+    for (int c = 0; c < NB; ++c)
+        acc[c] = floatx4{0.f, 0.f, 0.f, 0.f};
+    float f = 0.f;
+#pragma unroll
+    for (int s = 0; s < QMAX; ++s) {
+        if (s < slices) {   // wave-uniform
+            if (s + D < slices) {
+                // slice s + D refills slice s - 1's slot, whose reads have returned
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                issue(s + D);
+            }
+            // slice s has landed once no more than the loads of the slices
+            // issued after it are outstanding
+            switch (min(D, slices - 1 - s)) {
+            case 0: __builtin_amdgcn_s_waitcnt(wait_vmcnt(0)); break;
+            case 1: __builtin_amdgcn_s_waitcnt(wait_vmcnt(LW)); break;
+            case 2: __builtin_amdgcn_s_waitcnt(wait_vmcnt(2 * LW)); break;
+            default: __builtin_amdgcn_s_waitcnt(wait_vmcnt(3 * LW)); break;
+            }
+            asm volatile("" ::: "memory");
+            const uint8_t *slot = mine + (s % R) * SLOT;
+            floatx4 av = *reinterpret_cast<const floatx4 *>(slot + 16 * lane);
+            const int ka = kb + 16 * s + 4 * h;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                av[e] = ka + e < K ? av[e] : 0.f;
+            float bv[4][NB];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float *q = reinterpret_cast<const float *>(slot + b_rd[e]);
+                if constexpr (NB == 2) {
+                    const float2 v = *reinterpret_cast<const float2 *>(q);
+                    bv[e][0] = v.x;
+                    bv[e][1] = v.y;
+                } else if constexpr (NB == 4) {
+                    const floatx4 v = *reinterpret_cast<const floatx4 *>(q);
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        bv[e][c] = v[c];
+                } else {
+#pragma unroll
+                    for (int c = 0; c < NB; ++c)
+                        bv[e][c] = q[c];
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int c = 0; c < NB; ++c)
+                    acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[e], bv[e][c], acc[c], 0, 0, 0);
+            if constexpr (FRINGE) {
+                const floatx4 fb = *reinterpret_cast<const floatx4 *>(slot + 1024 * (NB + 1) + 16 * h);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    f = fmaf(av[e], fb[e], f);
+            }
+        }
+    }
+    // every load has landed (the tail row's too) and no read of the ring is
+    // outstanding: the partial sums go into this wavefront's first slot
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    float tv = 0.f;
+    if (tl) {   // this wavefront's sum of the tail row's products (butterfly, fixed order)
+        const float *tp = reinterpret_cast<const float *>(mine + R * SLOT);
+        tv = tp[lane] * tp[128 + lane] + tp[64 + lane] * tp[192 + lane];
+#pragma unroll
+        for (int d = 32; d >= 1; d >>= 1)
+            tv += __shfl_xor(tv, d);
+    }
+    // wavefront w's block c at part_w[c]; lane l holds rows 4 (l / 16) + r
+    // of column NB (l % 16) + c
+    floatx4 *part = reinterpret_cast<floatx4 *>(mine);
+#pragma unroll
+    for (int c = 0; c < NB; ++c)
+        part[64 * c + lane] = acc[c];
+    if constexpr (FRINGE)
+        reinterpret_cast<float *>(mine + 1024 * NB)[lane] = f;
+    if (lane == 0)
+        tpart[wave] = tv;
+    __syncthreads();
+    skinny_finish<NB, FRINGE>(sh, AREA, tpart, M, N, tl, C);
+}
+
+// The same problems with at most two column blocks (N <= 32, or N = 33 with
+// the last column on the vector ALUs) keep a wavefront's whole run of B in
+// its LDS (8 slices x NB KB), so every load can be issued at once: first the
+// B units of every slice and B's last column (direct global->LDS loads, B in
+// the layout above), then the tail row's products and the A units straight
+// into registers.  The compiler counts only the loads it issued itself,
+// which come last, so its waits on A are exact, and one wait for the B
+// copies precedes the first read of them.  Slice s then needs its A
+// registers only: the slices start as A lands, and each reads B with
+// NB-float reads free of bank conflicts (against twelve conflicting 4-byte
+// reads a slice with B rows packed as in memory).
+template <int NB, bool FRINGE>
+__global__ __launch_bounds__(512) void mfma_f32_skinny_resident_kernel(int M, int N, int K, int tail,
+                                                                       const float *A, const float *B, float *C)
+{
+    static_assert(NB <= 2, "a wavefront's B run must fit its share of LDS");
+    constexpr int QMAX = kF32SkinnyMaxK / (16 * 8);            // slices per wavefront at most
+    constexpr int U = 4 * NB;                                  // 16-byte units per B row
+    constexpr int FCOL = QMAX * 1024 * NB;                     // B's last column: 4 bytes a row
+    constexpr int AREA = skinny_resident_wave_bytes(NB, FRINGE);
+    constexpr uint32_t OOB = 0x80000000u;
+    __shared__ __attribute__((aligned(1024))) uint8_t sh[8 * AREA];
+    __shared__ float tpart[8];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int r16 = lane & 15, h = lane >> 4;
+    const int m0 = blockIdx.x * 16, row = m0 + r16;
+    const int total = (K + 15) / 16;
+    const int s_lo = wave * total / 8, s_hi = (wave + 1) * total / 8;
+    const int slices = s_hi - s_lo, kb = 16 * s_lo, ke = min(K, 16 * s_hi);
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, (long long)M * K * 4);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(B, (long long)K * N * 4);
+    const intx4 rbw = rsrc_words(B, (long long)K * N * 4);
+    uint8_t *mine = sh + wave * AREA;
+    const uint32_t base = lds_address(mine);
+
+    // B: slice s's units at base + 1024 NB s, unit t = 64 j + lane of the
+    // slice at position t / U (rows rotated as in the ring kernel)
+    {
+        int b_row[NB];
+        uint32_t b_off[NB];
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            const int t = 64 * j + lane, p = t / U, u = t % U, g = p >> 2;
+            b_row[j] = 4 * g + (((p & 3) - g) & 3);
+            b_off[j] = (uint32_t)(b_row[j] * N + 4 * u) * 4u;
+        }
+#pragma unroll
+        for (int s = 0; s < QMAX; ++s) {
+            if (s < slices) {
+                const int k0 = kb + 16 * s;
+#pragma unroll
+                for (int j = 0; j < NB; ++j)
+                    load_to_lds(rbw, base + (uint32_t)(1024 * (NB * s + j)),
+                                k0 + b_row[j] < ke ? (uint32_t)(k0 * N) * 4u + b_off[j] : OOB);
+            }
+        }
+        if constexpr (FRINGE) {   // rows kb .. ke - 1 of the last column
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int k = kb + lane + 64 * i;
+                load_dword_to_lds(rbw, base + (uint32_t)(FCOL + 256 * i),
+                                  k < ke ? (uint32_t)(k * N + N - 1) * 4u : OOB);
+            }
+        }
+    }
+    // the tail row's products: this wavefront's k, two a lane
+    const bool tl = tail && (int)blockIdx.x < N;
+    float ta[2], tb[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int k = kb + lane + 64 * i;
+        const bool ok = tl && k < ke;
+        ta[i] = __uint_as_float(
+            __builtin_amdgcn_raw_buffer_load_b32(ra, ok ? (uint32_t)((M - 1) * K + k) * 4u : OOB, 0, 0));
+        tb[i] = __uint_as_float(
+            __builtin_amdgcn_raw_buffer_load_b32(rb, ok ? (uint32_t)(k * N + blockIdx.x) * 4u : OOB, 0, 0));
+    }
+    // A of every slice, in slice order.  No load sits under a branch: one
+    // that did would make the compiler wait for earlier loads at the join.
+    // A unit that runs past K brings the next row's values (zeroed below).
+    floatx4 a[QMAX];
+#pragma unroll
+    for (int s = 0; s < QMAX; ++s) {
+        const int k = kb + 16 * s + 4 * h;
+        a[s] = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(
+                                               ra, s < slices && row < M && k < ke ? (uint32_t)(row * K + k) * 4u : OOB,
+                                               0, 0));
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // every load is issued before the first MFMA (none may be sunk into the
+    // slice branches below); the B copies have landed once no more than the
+    // loads issued after them (tail, A) are outstanding
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(4 + QMAX));
+    asm volatile("" ::: "memory");
+
+    int b_rd[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        b_rd[e] = (4 * h + ((e + h) & 3)) * U * 16 + NB * r16 * 4;
+    floatx4 acc[NB];
+#pragma unroll
+    for (int c = 0; c < NB; ++c)
+        acc[c] = floatx4{0.f, 0.f, 0.f, 0.f};
+    float f = 0.f;
+#pragma unroll
+    for (int s = 0; s < QMAX; ++s) {
+        if (s < slices) {   // wave-uniform
+            floatx4 av = a[s];
+            const int ka = kb + 16 * s + 4 * h;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                av[e] = ka + e < K ? av[e] : 0.f;
+            float bv[4][NB];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float *q = reinterpret_cast<const float *>(mine + 1024 * NB * s + b_rd[e]);
+                if constexpr (NB == 2) {
+                    const float2 v = *reinterpret_cast<const float2 *>(q);
+                    bv[e][0] = v.x;
+                    bv[e][1] = v.y;
+                } else {
+                    bv[e][0] = q[0];
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int c = 0; c < NB; ++c)
+                    acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[e], bv[e][c], acc[c], 0, 0, 0);
+            if constexpr (FRINGE) {
+                const floatx4 fb = *reinterpret_cast<const floatx4 *>(mine + FCOL + 64 * s + 16 * h);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    f = fmaf(av[e], fb[e], f);
+            }
+        }
+    }
+    // the partial sums go into this wavefront's own B slices (their reads
+    // have returned)
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    floatx4 *part = reinterpret_cast<floatx4 *>(mine);
+#pragma unroll
+    for (int c = 0; c < NB; ++c)
+        part[64 * c + lane] = acc[c];
+    if constexpr (FRINGE)
+        reinterpret_cast<float *>(mine + 1024 * NB)[lane] = f;
+    // tail: this wavefront's sum of its products (butterfly, fixed order)
+    float tv = ta[0] * tb[0] + ta[1] * tb[1];
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1)
+        tv += __shfl_xor(tv, d);
+    if (lane == 0)
+        tpart[wave] = tv;
+    __syncthreads();
+    skinny_finish<NB, FRINGE>(sh, AREA, tpart, M, N, tl, C);
+}
+
 template <int NB, bool FRINGE>
 void launch_skinny_t(const Problem &p, const F32SkinnyPlan &n, hipStream_t s)
 {
-    if constexpr (NB <= 3) {   // four blocks' partial sums leave no room for the B regions
-        if (n.ldsb) {
-            hipLaunchKernelGGL((mfma_f32_skinny_kernel<NB, FRINGE, true>), dim3((unsigned)n.blocks), dim3(512), 0, s,
-                               p.M, p.N, p.K, n.tail ? 1 : 0, (const float *)p.A, (const float *)p.B, p.C);
-            return;
-        }
-    }
-        hipLaunchKernelGGL((mfma_f32_skinny_kernel<NB, FRINGE, false>), dim3((unsigned)n.blocks), dim3(512), 0, s,
-                           p.M, p.N, p.K, n.tail ? 1 : 0, (const float *)p.A, (const float *)p.B, p.C);
+    if constexpr (NB <= 2)
+        hipLaunchKernelGGL((mfma_f32_skinny_resident_kernel<NB, FRINGE>), dim3((unsigned)n.blocks), dim3(512), 0,
+                           s, p.M, p.N, p.K, n.tail ? 1 : 0, (const float *)p.A, (const float *)p.B, p.C);
+    else
+        hipLaunchKernelGGL((mfma_f32_skinny_kernel<NB, FRINGE>), dim3((unsigned)n.blocks), dim3(512), 0, s, p.M,
+                           p.N, p.K, n.tail ? 1 : 0, (const float *)p.A, (const float *)p.B, p.C);
 }
 
 void launch_skinny(const Problem &p, const F32SkinnyPlan &n, hipStream_t s)
@@ -1143,7 +1272,7 @@ hipError_t launch_mfma_f32(const Problem &p, const gemm_plan &plan, hipStream_t 
         return launch_cfg<64, 64, 16, 2, 2>(p, plan, s);
     }
     F32SkinnyPlan n;
-    if (f32_skinny_plan(p.M, p.N, p.K, p.B, n) && plan.tile_m == 16 && plan.grid_y == n.blocks) {
+    if (f32_skinny_plan(p.M, p.N, p.K, n) && plan.tile_m == 16 && plan.grid_y == n.blocks) {
         launch_skinny(p, n, s);
         return hipGetLastError();
     }

@@ -141,15 +141,26 @@ def test_auto_picks_matrix_cores_and_tile_by_size():
     # 4097th row spread over workgroups 0..32 rather than given a 257th
     skinny = dg.plan(False, 4097, 33, 777)
     assert (skinny["tile_m"], skinny["tile_n"], skinny["grid_x"], skinny["grid_y"]) == (16, 33, 1, 256)
-    # B (16-byte aligned; a wavefront's run of 7 slices = 112 rows x 132
-    # bytes fits 16 KB) copied into LDS, one region per wavefront
-    assert skinny["tile_k"] == 784 and skinny["threads"] == 512 and skinny["lds_stages"] == 1
-    assert skinny["lds_bytes"] == 8 * 2 * 1024 + 4 * 512 + 32 + 8 * 16384
-    # B off 16-byte alignment, or rows too long for 16 KB: B in registers
+    # two column blocks: each wavefront holds its whole run of B in LDS (8
+    # slices of 16 rows x 32 columns, and the last column in 512 bytes)
+    assert skinny["tile_k"] == 784 and skinny["threads"] == 512 and skinny["lds_stages"] == 8
+    assert skinny["lds_bytes"] == 8 * (8 * 2048 + 512) + 32
+    # alignment of B does not change the plan
     odd_b = dg.plan(False, 4097, 33, 777, B=0x1004)
-    assert odd_b["lds_stages"] == 0 and odd_b["lds_bytes"] == 8 * 2 * 1024 + 4 * (1024 + 512) + 32
-    assert dg.plan(False, 4097, 33, 1024)["lds_stages"] == 0     # 128 rows x 132 bytes
-    assert dg.plan(False, 4097, 64, 256)["lds_stages"] == 0      # four blocks
+    assert (odd_b["lds_stages"], odd_b["lds_bytes"]) == (skinny["lds_stages"], skinny["lds_bytes"])
+    assert dg.plan(False, 4097, 33, 1024)["lds_stages"] == 8
+    # three or four blocks: a ring of 4 (3) LDS slots a wavefront (A's 1 KB,
+    # B's 16 rows x 16 NB columns, the last column in 256 bytes) plus 1 KB
+    # for the tail row's products
+    wide = dg.plan(False, 4097, 64, 1024)
+    assert wide["tile_n"] == 64 and wide["lds_stages"] == 3
+    assert wide["lds_bytes"] == 8 * (3 * (1024 + 4096) + 1024) + 32 <= 160 * 1024
+    mid = dg.plan(False, 4097, 49, 777)
+    assert mid["tile_n"] == 49 and mid["lds_stages"] == 4
+    assert mid["lds_bytes"] == 8 * (4 * (1024 + 3072 + 256) + 1024) + 32 <= 160 * 1024
+    assert dg.plan(False, 4097, 64, 256)["lds_stages"] == 3
+    # M N past 2^31 bytes of C: not the tall, narrow kernel
+    assert dg.plan(False, 1 << 24, 64, 1)["tile_m"] != 16
     # a last row block of 2..15 rows, or one row with fewer whole blocks than
     # columns: a workgroup of its own
     assert dg.plan(False, 4098, 33, 777)["grid_y"] == 257

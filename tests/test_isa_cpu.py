@@ -138,47 +138,74 @@ def f32_asm(tmp_path_factory):
     return out.read_text()
 
 
-def test_skinny_kernel_issues_every_load_before_its_first_mfma(f32_asm):
-    """The tall, narrow FP32 kernel streams: every load of a lane is issued
-    before its first MFMA, with no wait among them (a wait there would
-    serialise the slices on memory latency), and nothing spills.  Thirteen
-    instantiations: 1..4 MFMA column blocks, and 1..3 with the last column
-    on the vector ALUs, each with B in registers; and the six with at most 3
-    blocks again with B copied into LDS, whose global->LDS loads come from
-    inline assembly that sets M0, so there the compiler must touch M0
-    nowhere else."""
+def _loads_and_m0(body):
+    """(direct-load helper loads, compiler-generated loads, M0 accesses
+    outside the helpers) of a kernel body, in order."""
+    helper, compiler, m0, inside = [], [], [], False
+    for i, ln in enumerate(body.splitlines()):
+        if "ASMSTART" in ln:
+            inside = True
+            continue
+        if "ASMEND" in ln:
+            inside = False
+            continue
+        code = ln.split(";")[0]
+        if inside and re.search(r"buffer_load_dword(x4)?\b.* lds", code):
+            helper.append(i)
+        elif not inside and re.search(r"\b(buffer|global|flat)_load", code):
+            compiler.append(i)
+        elif re.search(r"\bm0\b", code) and not inside:
+            m0.append(code.strip())
+    return helper, compiler, m0
+
+
+def _no_scratch(asm, sym):
+    priv = re.search(rf"^\s*\.set\s+{re.escape(sym)}\.private_seg_size,\s*(\d+)", asm, flags=re.M)
+    assert priv and int(priv.group(1)) == 0, f"{sym}: scratch (spill) memory in use"
+
+
+def test_skinny_ring_kernel_streams_through_direct_loads_only(f32_asm):
+    """The tall, narrow FP32 kernel for three and four column blocks streams
+    each wavefront's slices through its own ring of LDS slots: every global
+    read comes from the inline-assembly direct-load helpers (which set M0, so
+    the compiler must touch M0 nowhere else), so the only waits on memory
+    are the hand-placed ones; its prologue issues three slices (two with four
+    blocks) before the first MFMA; nothing spills.  Three instantiations:
+    3 and 4 blocks, and 3 with the last column on the vector ALUs."""
     found = _instances(f32_asm, "mfma_f32_skinny_kernel")
-    assert len(found) == 13
+    assert len(found) == 3
     for sym, body in found:
-        ldsb = "Lb1EEEv" in sym
-        asm_loads, outside_m0, inside = 0, [], False
-        for ln in body.splitlines():
-            if "ASMSTART" in ln:
-                inside = True
-                continue
-            if "ASMEND" in ln:
-                inside = False
-                continue
-            code = ln.split(";")[0]
-            if inside and "buffer_load_dwordx4" in code and " lds" in code:
-                asm_loads += 1
-            elif re.search(r"\bm0\b", code) and not inside:
-                outside_m0.append(code.strip())
-        assert (asm_loads > 0) == ldsb, sym
-        assert outside_m0 == [], f"{sym}: compiler-generated M0 accesses: {outside_m0[:5]}"
+        nb = int(re.search(r"kernelILi(\d)E", sym).group(1))
+        fringe = "ELb1EE" in sym
+        helper, compiler, m0 = _loads_and_m0(body)
+        assert compiler == [], f"{sym}: loads outside the direct-load helpers"
+        assert m0 == [], f"{sym}: compiler-generated M0 accesses: {m0[:5]}"
+        first_mfma = next(i for i, ln in enumerate(body.splitlines()) if "v_mfma" in ln)
+        depth = 2 if nb == 4 else 3
+        assert sum(i < first_mfma for i in helper) >= depth * (1 + nb + (1 if fringe else 0)), sym
+        _no_scratch(f32_asm, sym)
+
+
+def test_skinny_resident_kernel_issues_every_load_before_its_first_mfma(f32_asm):
+    """The tall, narrow FP32 kernel for one and two column blocks issues all
+    of a lane's loads before its first MFMA, with no wait among them: first
+    the direct global->LDS copies of B (helpers that set M0; the compiler
+    touches M0 nowhere else), then its own loads of the tail row and of A,
+    at most 63 (what the wait counter tells apart), so that its waits on A
+    count only loads issued after; nothing spills.  Four instantiations: 1
+    and 2 blocks, each with and without the last column on the vector ALUs."""
+    found = _instances(f32_asm, "mfma_f32_skinny_resident_kernel")
+    assert len(found) == 4
+    for sym, body in found:
+        helper, compiler, m0 = _loads_and_m0(body)
         lines = body.splitlines()
-        first = next(i for i, ln in enumerate(lines) if "v_mfma" in ln)
-        head = lines[:first]
-        loads = sum("buffer_load" in ln for ln in head)
-        assert loads == sum("buffer_load" in ln for ln in lines), f"{sym}: a load after the first MFMA"
-        waits = [ln.strip() for ln in head if "vmcnt" in ln]
-        first_load = next(i for i, ln in enumerate(head) if "buffer_load" in ln)
-        last_load = max(i for i, ln in enumerate(head) if "buffer_load" in ln)
-        assert not any("vmcnt" in ln for ln in head[first_load:last_load]), f"{sym}: a wait among the loads"
-        assert loads <= 63, f"{sym}: {loads} loads, more than the wait counter tells apart"
-        priv = re.search(rf"^\s*\.set\s+{re.escape(sym)}\.private_seg_size,\s*(\d+)", f32_asm, flags=re.M)
-        assert priv and int(priv.group(1)) == 0, f"{sym}: scratch (spill) memory in use"
-        assert waits, sym
+        first_mfma = next(i for i, ln in enumerate(lines) if "v_mfma" in ln)
+        assert helper and compiler and m0 == [], sym
+        assert max(helper) < min(compiler), f"{sym}: a compiler load before a B copy"
+        assert max(compiler) < first_mfma, f"{sym}: a load after the first MFMA"
+        assert len(compiler) <= 63
+        assert not any("vmcnt" in ln for ln in lines[min(helper):max(compiler)]), f"{sym}: a wait among the loads"
+        _no_scratch(f32_asm, sym)
 
 
 def test_poison_build_fills_every_direct_load_destination_first(tmp_path):

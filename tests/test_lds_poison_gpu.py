@@ -86,8 +86,15 @@ CASES = [
     ("e4m3", 520, 784, [16, 64, 80, 144, 320]),                 # 8-bit ring
     ("e5m2", 520, 784, [16, 80, 208]),
     ("i8", 520, 784, [16, 48, 64, 128, 192, 320]),
-    ("f32", 4097, 33, [777, 1, 100]),                           # tall, narrow: B rows copied per wavefront
+    # tall, narrow: one and two column blocks hold a wavefront's B run in LDS;
+    # three and four stream it through rings of 4 and 3 slots, where K gives
+    # 0 to 8 slices a wavefront, so the prologue, the refills and the drain
+    # each run with every count of slices in flight
+    ("f32", 4097, 33, [777, 1, 100, 200, 500, 1024]),
     ("f32", 4100, 17, [600]),
+    ("f32", 1000, 64, [1024, 300, 40]),
+    ("f32", 530, 40, [999]),
+    ("f32", 600, 49, [800, 70]),
 ]
 
 
