@@ -15,9 +15,10 @@
 // FP32, as in the GEMM; only their order differs from the direct loop.
 //
 // Two kernels:
-//   nhwc_prepare: xp from x through LDS-tiled transposes (a block per 64
-//     pixels of xp and 64 or 32 channels), and Wr from w (a block per
-//     filter and channel block);
+//   nhwc_prepare: xp from x through LDS-tiled transposes (a block per
+//     image, run of rows and 64 or 32 channels, or per 64 pixels of xp when
+//     W is odd or x not 4-byte aligned), and Wr from w (a block per filter
+//     and channel block);
 //   conv_nhwc_kernel<BF16, BM, BN, BK, WGM, NST, NW>: BM filters x BN
 //     pixels per workgroup, BK-deep stages (a multiple of 32 within one tap:
 //     C % BK == 0) in a ring of NST LDS buffers, NW wavefronts in a
@@ -56,21 +57,87 @@ __device__ __forceinline__ floatx4 nhwc_mma(halfx8 a, halfx8 b, floatx4 c)
         return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-// Blocks [0, xp_blocks): 64 consecutive pixels of xp (n, hp, wp flattened)
-// and CH channels (64 when C allows, else 32).  Each channel's 64 pixels are
-// read as one coalesced run of x (zeros in the border) into an LDS tile,
-// which is then written channels-last, 16 bytes (8 channels of one pixel) a
-// thread, CH channels of a pixel contiguous.  Blocks past that: filter k and
-// CH channels of w: the CH R S contiguous values are read into LDS and
-// written as R S runs of CH channels of Wr.  R S is at most 64.
-constexpr int kPrepPix = 64, kPrepRow = 66;   // tile rows padded against bank conflicts
+// Blocks [0, xp_blocks) write xp, in one of two ways.
+//   rows (W even and at most 64, x 4-byte aligned): a block per image n,
+//     run of RH = 64 / W image rows h0 .. h0 + RH - 1 and CH channels (64
+//     when C allows, else 32).  Each channel's RH W values are one
+//     contiguous run of x, read 16 bytes a lane (a compute unit issues
+//     memory instructions at a fixed rate whatever their width, so 2-byte
+//     loads cost eight times the issue of these) into a row of the LDS tile.
+//     The block then writes the xp rows of its image rows, border columns
+//     included, and the first and last blocks of an image also the border
+//     rows.
+//   pixels: a block per 64 consecutive pixels of xp (n, hp, wp flattened),
+//     each channel's 64 pixels read one value a lane (zeros in the border).
+// Either way the tile is written channels-last, 16 bytes (8 channels of
+// one pixel) a thread, CH channels of a pixel contiguous.  Blocks past
+// that: filter k and CH channels of w: the CH R S contiguous values are read
+// into LDS and written as R S runs of CH channels of Wr.  R S is at most 64.
+// Tile rows: 64 values (a run of RH W <= 64, its last 16-byte unit
+// included) padded to 66 against bank conflicts.
+constexpr int kPrepPix = 64, kPrepRow = 66;
+
+struct PrepRows { int rh, groups; };          // rows mode: image rows per block, blocks per image
+inline PrepRows prep_rows(const Conv2d &cv)
+{
+    PrepRows r;
+    r.rh = cv.W <= 64 ? min(64 / cv.W, cv.H) : 1;
+    r.groups = (cv.H + r.rh - 1) / r.rh;
+    return r;
+}
+inline bool prep_rows_apply(const Conv2d &cv, const void *x)
+{
+    return cv.W % 2 == 0 && cv.W <= 64 && ((uintptr_t)x & 3) == 0;
+}
 
 __global__ __launch_bounds__(256) void nhwc_prepare(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
                                                     uint16_t *__restrict__ xp, uint16_t *__restrict__ wr, Conv2d cv,
-                                                    int Hp, int Wp, int ch, int xp_blocks)
+                                                    int Hp, int Wp, int ch, int xp_blocks, PrepRows pr, int rows_mode)
 {
-    __shared__ uint16_t tile[64 * kPrepRow];
+    __shared__ __attribute__((aligned(16))) uint16_t tile[64 * kPrepRow];
     const int tid = threadIdx.x, cblocks = cv.C / ch, units = ch / 8;
+    if ((int)blockIdx.x < xp_blocks && rows_mode) {
+        const int cb = blockIdx.x % cblocks, t = blockIdx.x / cblocks;
+        const int g = t % pr.groups, n = t / pr.groups;
+        const int h0 = g * pr.rh, rows = min(pr.rh, cv.H - h0), run = rows * cv.W, nu = (run + 7) / 8;
+        const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, (long long)cv.N * cv.C * cv.H * cv.W * 2);
+        const size_t plane = (size_t)cv.H * cv.W;
+        const size_t first = ((size_t)n * cv.C + (size_t)cb * ch) * plane + (size_t)h0 * cv.W;
+        for (int e = tid; e < ch * nu; e += 256) {
+            const int c = e / nu, u = e - c * nu;
+            // a unit past the run brings the next values of x (or zeros past
+            // its end): they land past the run in the tile row, never read
+            const uint4 v = __builtin_bit_cast(
+                uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                           rx, (uint32_t)((first + (size_t)c * plane + 8 * u) * 2), 0, 0));
+            uint32_t *dst = reinterpret_cast<uint32_t *>(tile + c * kPrepRow + 8 * u);
+            dst[0] = v.x;
+            dst[1] = v.y;
+            dst[2] = v.z;
+            dst[3] = v.w;
+        }
+        __syncthreads();
+        // xp rows: this block's image rows, and the border rows above the
+        // first and below the last
+        const int hp_lo = g == 0 ? 0 : h0 + cv.ph;
+        const int hp_hi = g == pr.groups - 1 ? Hp : h0 + cv.ph + rows;
+        const int count = (hp_hi - hp_lo) * Wp * units;
+        for (int e = tid; e < count; e += 256) {
+            const int u = e % units, t2 = e / units, wp = t2 % Wp, hp = hp_lo + t2 / Wp;
+            const int h = hp - cv.ph - h0, wc = wp - cv.pw;
+            uint32_t v[4] = {0u, 0u, 0u, 0u};
+            if ((unsigned)h < (unsigned)rows && (unsigned)wc < (unsigned)cv.W) {
+                const int px = h * cv.W + wc;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    v[i] = (uint32_t)tile[(8 * u + 2 * i) * kPrepRow + px] |
+                           ((uint32_t)tile[(8 * u + 2 * i + 1) * kPrepRow + px] << 16);
+            }
+            *reinterpret_cast<uint4 *>(xp + (((size_t)n * Hp + hp) * Wp + wp) * cv.C + cb * ch + 8 * u) =
+                make_uint4(v[0], v[1], v[2], v[3]);
+        }
+        return;
+    }
     if ((int)blockIdx.x < xp_blocks) {
         const int cb = blockIdx.x % cblocks;
         const long long pix0 = (long long)(blockIdx.x / cblocks) * kPrepPix;
@@ -373,10 +440,13 @@ void launch_nhwc_prepare(const Conv2d &cv, const void *x, const void *w, void *x
 {
     const int Hp = cv.H + 2 * cv.ph, Wp = cv.W + 2 * cv.pw, ch = nhwc_prepare_ch(cv);
     const long long npix = (long long)cv.N * Hp * Wp;
-    const int xp_blocks = (int)((npix + kPrepPix - 1) / kPrepPix) * (cv.C / ch);
+    const PrepRows pr = prep_rows(cv);
+    const bool rows = prep_rows_apply(cv, x);
+    const int xp_blocks = (rows ? cv.N * pr.groups : (int)((npix + kPrepPix - 1) / kPrepPix)) * (cv.C / ch);
     const int w_blocks = cv.K * (cv.C / ch);
     hipLaunchKernelGGL(nhwc_prepare, dim3((unsigned)(xp_blocks + w_blocks)), dim3(256), 0, s, (const uint16_t *)x,
-                       (const uint16_t *)w, (uint16_t *)xp, (uint16_t *)wr, cv, Hp, Wp, ch, xp_blocks);
+                       (const uint16_t *)w, (uint16_t *)xp, (uint16_t *)wr, cv, Hp, Wp, ch, xp_blocks, pr,
+                       rows ? 1 : 0);
 }
 
 template <bool BF16>
