@@ -12,18 +12,18 @@ and compared with the matrix peak of its input type.
 Prints ONE JSON line (rank 0; this benchmark runs on one GPU only).
 
   python bench.py [--steps K] [--warmup W] [--only f32|f16|bf16|e4m3|e5m2|i8]
-                  [--ladder] [--no-cpu-baseline] [--copy-calibration]
+                  [--ladder | --no-ladder] [--no-cpu-baseline] [--copy-calibration]
 
 --only times one workload instead of the two-kernel step: the two headline
 ones, or the 8192^3 workloads of the BF16, FP8 (E4M3, E5M2) and INT8 entry
 points (2MNK integer operations per second for INT8).
 
---ladder additionally times every kernel variant (rung) at 1024^3 and
-4096^3 FP32 and 8192^3 FP16 and adds a "ladder" object to the line.
 Unless --no-all-workloads is given, every named workload (the BF16, FP8 and
 INT8 entry points included) is then timed on its own under "all_workloads",
-and the convolution workloads (im2col + GEMM) under "conv_workloads";
---conv-only times just the latter.
+the convolution workloads under "conv_workloads", and every kernel variant
+(rung) at 1024^3 and 4096^3 FP32 and 8192^3 FP16 under "ladder" (a few
+seconds; --no-ladder skips it, --ladder adds it to any run); --conv-only
+times just the convolutions.
 --copy-calibration runs a plain device-to-device copy of known size first;
 used only by the hardware-counter runs that calibrate HBM byte counts.
 
@@ -126,7 +126,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--only", choices=["all", "f32", "f16", "bf16", "e4m3", "e5m2", "i8"], default="all")
-    ap.add_argument("--ladder", action="store_true")
+    ap.add_argument("--ladder", action="store_true", help="time every rung even without the all-workloads leg")
+    ap.add_argument("--no-ladder", action="store_true", help="skip timing every rung after the all-workloads leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target host time of the CPU-baseline sample")
@@ -286,7 +287,7 @@ def main() -> int:
             if "tflops" in g and "tflops" in c:
                 out["sustained"]["f16_frac_of_mfma_ceiling"] = round(g["tflops"] / c["tflops"], 4)
 
-    if args.ladder:
+    if args.ladder or not (args.no_ladder or args.no_all_workloads):
         out["ladder"] = ladder(dg, inputs, torch, dev, stream)
 
     if not args.no_cpu_baseline:
