@@ -17,7 +17,7 @@ from dense_gemm_optimisation_row_amd import build as hipbuild
 
 RING_KERNELS = [("mfma_f16.hip", "mfma_f16_pipe_kernel"), ("mfma_f16.hip", "mfma_f16_pair_kernel"),
                 ("mfma_f32.hip", "mfma_f32_ring_kernel"), ("mfma_f32.hip", "mfma_f32_small_ring_kernel"),
-                ("mfma_8bit.hip", "mfma_8bit_ring_kernel")]
+                ("mfma_8bit.hip", "mfma_8bit_ring_kernel"), ("mfma_8bit.hip", "mfma_i8_pair_kernel")]
 
 
 @pytest.fixture(scope="module", params=RING_KERNELS, ids=lambda v: v[1])
@@ -50,9 +50,9 @@ def test_every_layout_variant_is_generated(ring):
     # 16-bit: op(B) x (overwrite, accumulate) x two formats for each of a
     # k-contiguous A (pair kernel) and a k-strided A (pipe kernel); FP32:
     # op(A) x op(B) x (overwrite, accumulate); 8-bit: the row-major product in
-    # three formats; the 64 x 64 ring once
+    # the two FP8 formats, and once for INT8; the 64 x 64 ring once
     want = {"mfma_f16_pipe_kernel": 8, "mfma_f16_pair_kernel": 8, "mfma_f32_ring_kernel": 8,
-            "mfma_f32_small_ring_kernel": 1, "mfma_8bit_ring_kernel": 3}[kernel]
+            "mfma_f32_small_ring_kernel": 1, "mfma_8bit_ring_kernel": 2, "mfma_i8_pair_kernel": 1}[kernel]
     assert len(_instances(asm, kernel)) == want
 
 
