@@ -183,6 +183,29 @@ def test_8bit_k0_empty_and_misaligned(fmt):
                                 None) == binding.GEMM_ERR_INVALID_DIM
 
 
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("c_off", [1, 3])
+def test_8bit_ring_with_c_off_16_byte_alignment(fmt, c_off):
+    """The ring with aligned A and B and C starting c_off elements (4 c_off
+    bytes) past a 16-byte boundary: the stores fall back to one element at a
+    time (the INT8 kernel's LDS-staged epilogue and the FP8 kernel's direct
+    stores alike).  Ragged tiles; every element around C keeps its sentinel."""
+    import torch
+    M, N, K = 300, 272, 208
+    say("8bit ring, C off 16-byte alignment", fmt, c_off)
+    A, B = mats(fmt, M, N, K, 4600 + c_off, "int")
+    assert dg.plan(fmt, M, N, K)["variant"] == dg.R8_MFMA_8BIT
+    out_dtype = torch.int32 if fmt == "i8" else torch.float32
+    buf = torch.full((M * N + 8,), -77, dtype=out_dtype, device="cuda")
+    a, b = to_dev(A, fmt), to_dev(B, fmt)
+    assert binding.raw_gemm(fmt, None, M, N, K, a.data_ptr(), b.data_ptr(), buf.data_ptr() + 4 * c_off,
+                            None) == binding.GEMM_OK
+    torch.cuda.synchronize()
+    got = buf.cpu().numpy()
+    assert np.all(got[:c_off] == -77) and np.all(got[c_off + M * N:] == -77), "a store outside C"
+    check(fmt, got[c_off:c_off + M * N].reshape(M, N), A, B, f"{fmt} C offset {c_off}", exact=True)
+
+
 @pytest.mark.parametrize("name", ["e4m3_8192", "e5m2_8192", "i8_8192"])
 def test_8bit_workload_sampled_and_invariant(name):
     """The benchmarked configuration: 8192^3 through the ring, 4096 sampled
