@@ -176,8 +176,9 @@ inline bool direct_lds_applies(int tile_m, int top_tile, bool vec_a, bool vec_b,
 // FP32 problems that take the 64 x 64 tile with both operands in 128-bit
 // loads run a ring of kF32SmallStages LDS stages kF32SmallDepth deep, loaded
 // straight from global memory; lane byte offsets (k + depth) N 4 of B must
-// stay below 2^31.
-constexpr int kF32SmallDepth = 64;
+// stay below 2^31.  At 32 deep the ring takes 64 KB, so two workgroups share
+// a compute unit when the shape has more tiles than there are units.
+constexpr int kF32SmallDepth = 32;
 constexpr int kF32SmallStages = 4;
 constexpr int kF32SmallWavesN = 4;   // wavefronts along N (2 along M): 32 x 64 / kF32SmallWavesN each
 constexpr int kF32SmallLdsBytes = kF32SmallStages * (64 * kF32SmallDepth + kF32SmallDepth * 64) * 4;
