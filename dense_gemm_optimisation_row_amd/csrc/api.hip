@@ -78,6 +78,37 @@ int pick_config(const MfmaConfig (&cfg)[NC], int M, int N, bool narrow_ok)
     return full - 1;
 }
 
+// Expected fraction of the matrix peak of a tile choice: the kernel's own
+// rate (rate_few with under two tiles per compute unit, whose first loads
+// and last stores nothing else hides; rate_many from two up) times how
+// evenly the tiles spread over the 256 compute units, since the unit with
+// the most tiles sets the time.  Measured rates: the FP32 256 x 256 ring
+// 0.93; the 128 x 128 direct-load kernel 0.75 and 0.87; the 64 x 64 ring 0.66
+// and 0.83.
+double tile_estimate(long tiles, double rate_few, double rate_many)
+{
+    const long per = (tiles + 255) / 256;
+    return (tiles < 512 ? rate_few : rate_many) * (double)tiles / (256.0 * (double)per);
+}
+
+// The FP32 tile for operands that take 128-bit direct loads: 256, 128 or 64
+// (0: none of the direct-load kernels applies).
+int f32_direct_tile(int M, int N, int K, bool vec_a, bool vec_b)
+{
+    auto tiles = [&](int t) { return (long)ceil_div(M, t) * ceil_div(N, t); };
+    const double e256 =
+        dgor::f32_ring_applies(M, N, K, vec_a, vec_b) ? tile_estimate(tiles(256), 0.93, 0.93) : -1;
+    const double e128 =
+        dgor::direct_lds_applies(128, 128, vec_a, vec_b, N, K) ? tile_estimate(tiles(128), 0.75, 0.87) : -1;
+    const double e64 =
+        dgor::f32_small_ring_applies(64, 64, N, K, vec_a, vec_b) ? tile_estimate(tiles(64), 0.66, 0.83) : -1;
+    if (e256 > 0 && e256 >= e128 && e256 >= e64)
+        return 256;
+    if (e64 > 0 && e64 >= e128)
+        return 64;
+    return e128 > 0 ? 128 : 0;
+}
+
 int plan_f32(int variant, int M, int N, int K, const void *A, const void *B, const void *C,
              gemm_plan *p)
 {
@@ -144,7 +175,8 @@ int plan_f32(int variant, int M, int N, int K, const void *A, const void *B, con
         p->outputs_per_thread = 64;
         break;
     case GEMM_R6_MFMA_F32: {
-        if (dgor::f32_ring_applies(M, N, K, p->vector_a, p->vector_b)) {
+        const int direct = f32_direct_tile(M, N, K, p->vector_a, p->vector_b);
+        if (direct == dgor::kF32RingTile) {
             p->tile_m = p->tile_n = dgor::kF32RingTile;
             p->tile_k = dgor::kF32RingDepth;
             p->threads = 64 * dgor::kF32RingWaves;
@@ -178,7 +210,11 @@ int plan_f32(int variant, int M, int N, int K, const void *A, const void *B, con
             p->grid_y = nw.blocks;
             return GEMM_OK;
         }
-        const MfmaConfig &c = dgor::kF32Configs[pick_config(dgor::kF32Configs, M, N, true)];
+        // the 128 x 128 or 64 x 64 direct-load kernel where one applies and
+        // N > 64, else the register-staged tiles
+        const int ci = direct == 128 && N > 64 ? 0 : direct == 64 && N > 64 ? 1
+                                                    : pick_config(dgor::kF32Configs, M, N, true);
+        const MfmaConfig &c = dgor::kF32Configs[ci];
         p->tile_m = c.bm;
         p->tile_n = c.bn;
         p->tile_k = c.bk;
@@ -235,7 +271,13 @@ int plan_f16(int variant, int M, int N, int K, const void *A, const void *B, con
         p->outputs_per_thread = 1;
         p->vector_a = p->vector_b = 0;
     } else {
-        const MfmaConfig &c = dgor::kF16Configs[pick_config(dgor::kF16Configs, M, N, false)];
+        // the 256 x 256 ring (direct loads) from half a tile per compute
+        // unit up: measured at 3072^3 (144 tiles) it runs 32% of the peak
+        // against 24% for the register-staged 128 x 128 tiles, at 4096^3 52%
+        // against 29%; at 2048^3 (64 tiles) the 64 x 64 tiles are ahead
+        const long t256 = (long)ceil_div(M, 256) * ceil_div(N, 256);
+        const bool ring = t256 >= 128 && dgor::direct_lds_applies(256, 256, p->vector_a, p->vector_b, N, K);
+        const MfmaConfig &c = dgor::kF16Configs[ring ? 0 : pick_config(dgor::kF16Configs, M, N, false)];
         p->tile_m = c.bm;
         p->tile_n = c.bn;
         p->tile_k = c.bk;

@@ -175,6 +175,27 @@ def test_auto_picks_matrix_cores_and_tile_by_size():
     assert h["variant"] == dg.R7_MFMA_F16 and (h["tile_m"], h["tile_n"]) == (256, 256)
 
 
+def test_direct_load_tile_follows_the_spread_of_tiles_over_compute_units():
+    """Aligned FP32 operands take whichever of the 256, 128 and 64 square
+    direct-load tiles has the best measured rate times the evenness of its
+    tiles over the 256 compute units; 16-bit operands take the 256 x 256 ring
+    from 128 of its tiles."""
+    tile = lambda half, M, N, K: dg.plan(half, M, N, K)["tile_m"]
+    assert tile(False, 4096, 4096, 4096) == 256     # 256 tiles, one per unit
+    assert tile(False, 8192, 8192, 8192) == 256     # 1024: four per unit
+    assert tile(False, 6144, 6144, 6144) == 128     # 576 ring tiles leave a quarter round; 2304 of 128^2
+    assert tile(False, 5120, 5120, 5120) == 64      # 400 ring tiles, 1600 of 128^2 (7 on some units)
+    assert tile(False, 3072, 3072, 3072) == 64      # 576 of 128^2 (three on some units) against 2304 of 64^2
+    assert tile(False, 4096, 2048, 2048) == 128     # 512 of 128^2: two per unit
+    assert tile(False, 2048, 2048, 2048) == 64      # 256 of 128^2, one per unit: 1024 of 64^2
+    assert tile(False, 1024, 1024, 1024) == 64
+    assert tile(True, 4096, 4096, 4096) == 256
+    assert tile(True, 3072, 3072, 3072) == 256      # 144 ring tiles
+    assert tile(True, 2048, 2048, 2048) == 64       # 64 ring tiles: too few
+    # K % 8 != 0: A's rows are not whole 16-byte units, so no direct loads
+    assert tile(True, 4096, 4096, 4095) == 128 and dg.plan(True, 4096, 4096, 4095)["vector_a"] == 0
+
+
 def test_vector_path_needs_divisible_rows_and_16_byte_alignment():
     p = dg.plan(False, 64, 64, 64)
     assert p["vector_a"] == p["vector_b"] == 1

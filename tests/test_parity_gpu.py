@@ -102,8 +102,8 @@ def test_bf16_variants_small_shapes(variant, shape):
 # Shapes large enough that the automatic choice takes each matrix-core tile
 # configuration, with ragged edges in all three dimensions.
 CONFIG_SHAPES = [
-    (False, (4000, 4100, 200), (256, 256)),   # FP32 256 x 256 ring, ragged M/N/K
-    (False, (2049, 4100, 100), (128, 128)),   # FP32 128 x 128 tiles
+    (False, (4000, 4092, 200), (256, 256)),   # FP32 256 x 256 ring, ragged M/N/K
+    (False, (4000, 2044, 100), (128, 128)),   # FP32 128 x 128 direct-load tiles (512 of them)
     (False, (1000, 1000, 1000), (64, 64)),    # FP32 64 x 64 tiles
     (False, (4097, 33, 777), (16, 33)),       # FP32 tall, narrow: 2 MFMA blocks + a vector column, tail row
     (False, (4097, 64, 1024), (16, 64)),      # FP32 tall, narrow: 4 MFMA blocks, K = 1024
@@ -111,6 +111,7 @@ CONFIG_SHAPES = [
     (True, (8191, 4097, 72), (256, 256)),     # FP16 256 x 256 tiles, unaligned rows
     (True, (8000, 4104, 200), (256, 256)),    # FP16 256 x 256 tiles, 128-bit rows, ragged M/N/K
     (True, (2047, 4095, 200), (128, 128)),    # FP16 128 x 128 tiles
+    (True, (3000, 3080, 200), (256, 256)),    # FP16 256 x 256 ring with 156 tiles
     (True, (1000, 1000, 1000), (64, 64)),     # FP16 64 x 64 tiles
     ("bf16", (8000, 4104, 200), (256, 256)),  # BF16 ring, ragged M/N/K
     ("bf16", (8191, 4097, 72), (256, 256)),   # BF16 256 x 256, unaligned rows
@@ -156,7 +157,7 @@ def test_f16_large_tile_stage_counts(K, fmt):
 # give 1, 1, 2, 2, 3, 3, 4 and 5 stages, full and ragged.
 @pytest.mark.parametrize("K", [4, 16, 20, 32, 36, 48, 52, 68])
 def test_f32_large_tile_stage_counts(K):
-    M, N = 4000, 4100
+    M, N = 4000, 4092
     p = dg.plan(False, M, N, K)
     assert (p["tile_m"], p["tile_n"]) == (256, 256)
     say("f32 large tile stages", (M, N, K))
