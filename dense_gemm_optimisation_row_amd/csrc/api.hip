@@ -271,13 +271,16 @@ int plan_f16(int variant, int M, int N, int K, const void *A, const void *B, con
         p->outputs_per_thread = 1;
         p->vector_a = p->vector_b = 0;
     } else {
-        // the 256 x 256 ring (direct loads) from half a tile per compute
-        // unit up: measured at 3072^3 (144 tiles) it runs 32% of the peak
-        // against 24% for the register-staged 128 x 128 tiles, at 4096^3 52%
-        // against 29%; at 2048^3 (64 tiles) the 64 x 64 tiles are ahead
+        // operands that take direct loads: the 256 x 256 ring from half a
+        // tile per compute unit up, else the 128 x 128 ring (measured: 3072^3,
+        // 144 tiles of 256^2, 32% of the peak against 31%; 2560^3, 100
+        // tiles, 22% against 33%; the register-staged tiles 15-24% at these
+        // sizes); other operands: the register-staged tiles
         const long t256 = (long)ceil_div(M, 256) * ceil_div(N, 256);
         const bool ring = t256 >= 128 && dgor::direct_lds_applies(256, 256, p->vector_a, p->vector_b, N, K);
-        const MfmaConfig &c = dgor::kF16Configs[ring ? 0 : pick_config(dgor::kF16Configs, M, N, false)];
+        const bool ring128 = !ring && dgor::f16_ring128_applies(p->vector_a, p->vector_b, N, K);
+        const MfmaConfig &c =
+            dgor::kF16Configs[ring ? 0 : ring128 ? 1 : pick_config(dgor::kF16Configs, M, N, false)];
         p->tile_m = c.bm;
         p->tile_n = c.bn;
         p->tile_k = c.bk;
@@ -285,6 +288,9 @@ int plan_f16(int variant, int M, int N, int K, const void *A, const void *B, con
         if (dgor::direct_lds_applies(c.bm, dgor::kF16Configs[0].bm, p->vector_a, p->vector_b, N, K)) {
             p->lds_stages = dgor::kF16RingStages;
             p->lds_bytes = dgor::kF16RingLdsBytes;
+        } else if (c.bm == 128 && dgor::f16_ring128_applies(p->vector_a, p->vector_b, N, K)) {
+            p->lds_stages = dgor::kF16RingStages;
+            p->lds_bytes = dgor::kF16Ring128LdsBytes;
         } else {
             p->lds_stages = 2;
             p->lds_bytes = dgor::mfma_f16_lds_bytes(c);

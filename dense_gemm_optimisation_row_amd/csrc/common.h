@@ -172,6 +172,14 @@ inline bool direct_lds_applies(int tile_m, int top_tile, bool vec_a, bool vec_b,
 {
     return tile_m == top_tile && vec_a && vec_b && K < (1 << 22) && N < (1 << 22);
 }
+// The 16-bit 128 x 128 tile (plain layout) runs the same ring at half the
+// size: three 16 KB A buffers and four 8 KB B stages, 80 KB, so two
+// workgroups share a compute unit.
+constexpr int kF16Ring128LdsBytes = 3 * 128 * 64 * 2 + kF16RingStages * 32 * 128 * 2;
+inline bool f16_ring128_applies(bool vec_a, bool vec_b, int N, int K)
+{
+    return vec_a && vec_b && K < (1 << 22) && N < (1 << 22);
+}
 
 // FP32 problems that take the 64 x 64 tile with both operands in 128-bit
 // loads run a ring of kF32SmallStages LDS stages kF32SmallDepth deep, loaded

@@ -854,6 +854,266 @@ __global__ __launch_bounds__(256) void mfma_f16_pair_kernel(RingArgs args)
     }
 }
 
+// Epilogue of the 128 x 128 ring: a wavefront's block of 64 columns and FM
+// 16-row MFMA blocks leaves through its own 8 KB LDS region in FM / 2 rounds
+// of 32 rows, as in the 256 x 256 rings; element (row, col) of a round sits
+// at row 256 + 16 ((col / 4) ^ 4 ((row / 4) % 4)) + 4 (col % 4), which keeps
+// both the 4-byte writes (lane (g, s) of block j at unit 4 (j ^ g) + s / 4)
+// and the 16-byte reads along the rows free of bank conflicts.
+template <int FM>
+__device__ __forceinline__ void store_c_staged_w64(const floatx4 (&acc)[FM][4], float alpha, uint8_t *lds, int wave,
+                                                   int lane, float *Cw, int ldc, int rows_left, int cols_left, bool vec)
+{
+    typedef unsigned uintx4 __attribute__((ext_vector_type(4)));
+    constexpr uint32_t OOB = 0x80000000u;
+    uint8_t *w = lds + wave * 8192;
+    const int g = lane >> 4, s16 = lane & 15;
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(
+        Cw, rows_left > 0 && cols_left > 0 ? ((long long)(rows_left - 1) * ldc + cols_left) * 4 : 0);
+#pragma unroll
+    for (int q = 0; q < FM / 2; ++q) {
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    *reinterpret_cast<float *>(w + (16 * ii + 4 * g + r) * 256 + (4 * (j ^ g) + (s16 >> 2)) * 16 +
+                                               (s16 & 3) * 4) = dgor_acc_read(acc[2 * q + ii][j][r]) * alpha;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const int row = (lane >> 4) + 4 * t, c = lane & 15;
+            const floatx4 v = *reinterpret_cast<const floatx4 *>(w + row * 256 + ((c ^ (4 * (t & 3))) * 16));
+            const int grow = 32 * q + row, col = 4 * c;
+            if (grow < rows_left) {
+                const uint32_t o = (uint32_t)(grow * ldc + col) * 4u;
+                if (vec && col + 4 <= cols_left) {
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(uintx4, v), rc, o, 0, 0);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[e]), rc,
+                                                              col + e < cols_left ? o + 4u * e : OOB, 0, 0);
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// The 128 x 128 ring for mid-size problems (A given as M x K, B as K x N, C =
+// A B): the pair ring's design at half the tile, four wavefronts of 64 x 64
+// (4 x 4 blocks of v_mfma_f32_16x16x32, 64 accumulators a lane) and 80 KB of
+// LDS, so two workgroups share a compute unit and cover each other's waits.
+//   A pair buffer (16 KB): 128 rows of 128 bytes, unit c of row r at
+//     8 r + (c ^ ((r >> 1) & 7)); wave w's load j (0..3) fills rows
+//     32 w + 8 j .. + 7, two loads a stage (half par of the pair).
+//   B stage (8 KB): 32 k rows of 256 bytes, unit u of row k at
+//     16 k + (u ^ (2 (k & 3) + 8 ((k >> 3) & 1))); wave w's load q (0..1)
+//     fills k rows 4 (2 w + q) .. + 3.  A transposing-read cycle (32 lanes)
+//     takes two 16-byte units of each of k rows 8 g .. 8 g + 3, g = 0, 1:
+//     the swizzle gives the eight rows eight distinct unit pairs.
+//   Pipeline, waits and the fragment order as in the pair ring, with 16
+//   MFMAs, 8 fragment reads and 4 loads a wavefront and stage.
+namespace pair128 {
+constexpr int A_PAIR_BYTES = 128 * 64 * 2;           // 16 KB
+constexpr int A_PAIRS = 3;
+constexpr int B_BYTES = 32 * 128 * 2;                // 8 KB
+constexpr int B_REGION = A_PAIRS * A_PAIR_BYTES;     // 48 KB
+constexpr int LDS_BYTES = B_REGION + 4 * B_BYTES;    // 80 KB: two workgroups a CU
+}  // namespace pair128
+
+template <class Op>
+__global__ __launch_bounds__(256, 2) void mfma_f16_pair128_kernel(RingArgs args)
+{
+    using namespace pair128;
+    constexpr int BK = pipe::BK;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
+    const uint32_t ring = lds_address(lds);
+    const int M = args.M, N = args.N, K = args.K, lda = args.lda, ldb = args.ldb;
+    const uint16_t *__restrict__ A = (const uint16_t *)args.A;
+    const uint16_t *__restrict__ B = (const uint16_t *)args.B;
+
+    int tm, tn;
+    dgor_tile_of_block((int)blockIdx.x, args.tiles_m, args.tiles_n, args.group_m, tm, tn);
+    const int m0 = tm * 128, n0 = tn * 128;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int wr = (wave >> 1) * 64, wc = (wave & 1) * 64;
+    constexpr uint32_t OOB = 0x80000000u;
+
+    uint32_t a_off[2];
+    int a_kc[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int r = 32 * wave + 8 * j + (lane >> 3);
+        const int c = (lane & 7) ^ ((4 * j + (lane >> 4)) & 7);
+        a_off[j] = (uint32_t)(r * lda + 8 * c) * 2u;
+        a_kc[j] = 8 * c;
+    }
+    const uint32_t a_row16 = (uint32_t)(16 * lda) * 2u;
+    uint32_t b_off[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int k = 4 * (2 * wave + q) + (lane >> 4);
+        const int u = (lane & 15) ^ (2 * (k & 3) + 8 * ((k >> 3) & 1));
+        b_off[q] = n0 + 8 * u < N ? (uint32_t)(k * ldb + 8 * u) * 2u : OOB;
+    }
+    const uint32_t lds_a = ring + (uint32_t)(4 * wave * 1024);
+    const uint32_t lds_b = ring + (uint32_t)(B_REGION + 2 * wave * 1024);
+    struct PairLoads { intx4 r; int k_left; uint32_t dst; };
+    auto a_rsrc = [&](int P, uint32_t buf) {
+        PairLoads L;
+        const int k0 = 2 * BK * P;
+        L.k_left = K - k0;
+        L.r = rsrc_words(A + (size_t)m0 * lda + k0, 0);
+        L.r.z = L.k_left <= 0 ? 0
+              : (m0 + 128 <= M ? 0x7fffffff
+                               : (int)(((uint32_t)(M - m0 - 1) * (uint32_t)lda + (uint32_t)L.k_left) * 2u));
+        L.dst = lds_a + buf;
+        return L;
+    };
+    auto load_a = [&](const PairLoads &L, int j) {
+        const uint32_t off = a_kc[j & 1] >= L.k_left ? OOB : a_off[j & 1] + (uint32_t)(j >> 1) * a_row16;
+        load_to_lds(L.r, L.dst + (uint32_t)(j * 1024), off);
+    };
+    struct BLoads { intx4 r; uint32_t dst; };
+    auto b_rsrc = [&](int st) {
+        BLoads L;
+        const int k0 = st * BK;
+        L.r = rsrc_words(B + (size_t)k0 * ldb + n0, 0);
+        L.r.z = ring16::stage_range<true>(k0, K, n0, N, ldb);
+        L.dst = lds_b + (uint32_t)((st & 3) * B_BYTES);
+        return L;
+    };
+    auto load_b = [&](const BLoads &L, int q) { load_to_lds(L.r, L.dst + (uint32_t)(q * 1024), b_off[q]); };
+
+    const int s16 = lane & 15, g = lane >> 4;
+    const uint32_t a_lane = (uint32_t)((wr + s16) * 128) | (uint32_t)((g ^ ((s16 >> 1) & 7)) * 16);
+    const int ks_x = 2 * ((s16 >> 2) & 3) + 8 * (g & 1);
+    uint32_t ks_unit[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        ks_unit[j] = (uint32_t)(((wc / 8 + 2 * j + ((s16 & 3) >> 1)) ^ ks_x) * 16);
+    const uint32_t b_lane = (uint32_t)(B_REGION + (8 * g + (s16 >> 2)) * 256 + 8 * (s16 & 1));
+    struct ReadSrc { uint32_t a_buf; int a_half; uint32_t b_buf; };
+    auto read_a = [&](const ReadSrc &R, int i) -> halfx8 {
+        const uint32_t addr = (a_lane ^ (uint32_t)(64 * R.a_half)) + R.a_buf + (uint32_t)(i * 2048);
+        return *reinterpret_cast<const halfx8 *>(lds + addr);
+    };
+    auto read_b = [&](const ReadSrc &R, int j) -> halfx8 {
+        const uint8_t *p = lds + b_lane + R.b_buf + ks_unit[j];
+        const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4 *)p);
+        const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4 *)(p + 1024));
+        return __builtin_bit_cast(halfx8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    // read r (0..7): A block 0, the four B blocks, then A blocks 1..3
+    auto fread = [&](const ReadSrc &R, int r, halfx8 *fa, halfx8 *fb) {
+        if (r == 0 || r >= 5)
+            fa[r == 0 ? 0 : r - 4] = read_a(R, r == 0 ? 0 : r - 4);
+        else
+            fb[r - 1] = read_b(R, r - 1);
+    };
+
+    floatx4 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                asm("v_accvgpr_write_b32 %0, 0" : "=a"(acc[i][j][r]));
+
+    struct StageLoads { BLoads b; PairLoads a; };
+    auto stage = [&](int par, const StageLoads &L, const ReadSrc &R, halfx8 *ca, halfx8 *cb, halfx8 *na,
+                     halfx8 *nb) {
+#pragma unroll
+        for (int m = 0; m < 16; ++m) {
+            const int i = m >> 2, j = m & 3;
+            acc[i][j] = Op::mfma16(ca[i], cb[j], acc[i][j]);
+            if (m < 8)
+                fread(R, m, na, nb);
+            if (m >= 8 && (m & 1)) {
+                const int ld = (m - 8) >> 1;   // 0..3
+                if (ld < 2)
+                    load_b(L.b, ld);
+                else
+                    load_a(L.a, 2 * par + ld - 2);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    auto stage_begin = [&](int t, uint32_t a_load_buf) {
+        if (t == 0)
+            __builtin_amdgcn_s_waitcnt(wait_vmcnt_lgkm0(6));
+        else
+            __builtin_amdgcn_s_waitcnt(wait_vmcnt_lgkm0(4));
+        __builtin_amdgcn_s_barrier();
+        const StageLoads L{b_rsrc(t + 3), a_rsrc((t >> 1) + 2, a_load_buf)};
+        __builtin_amdgcn_sched_barrier(0);
+        return L;
+    };
+    auto b_buf = [](int st) { return (uint32_t)((st & 3) * B_BYTES); };
+    auto next_pair = [](uint32_t pb) { return pb == (uint32_t)((A_PAIRS - 1) * A_PAIR_BYTES) ? 0u : pb + A_PAIR_BYTES; };
+
+    halfx8 fa0[4], fa1[4], fb0[4], fb1[4];
+    {
+        const PairLoads L = a_rsrc(0, 0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            load_a(L, j);
+    }
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+        const BLoads L = b_rsrc(st);
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+            load_b(L, q);
+    }
+    {
+        const PairLoads L = a_rsrc(1, A_PAIR_BYTES);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            load_a(L, j);
+    }
+    {
+        const BLoads L = b_rsrc(2);
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+            load_b(L, q);
+    }
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(8));
+    __builtin_amdgcn_s_barrier();
+    {
+        const ReadSrc R0{0u, 0, b_buf(0)};
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+            fread(R0, r, fa0, fb0);
+    }
+
+    const int steps = (K + BK - 1) / BK;
+    uint32_t pa = 0;
+    for (int t = 0; t < steps; t += 2) {
+        const uint32_t pa1 = next_pair(pa), pa2 = next_pair(pa1);
+        StageLoads L = stage_begin(t, pa2);
+        stage(0, L, ReadSrc{pa, 1, b_buf(t + 1)}, fa0, fb0, fa1, fb1);
+        if (t + 1 < steps) {
+            L = stage_begin(t + 1, pa2);
+            stage(1, L, ReadSrc{pa1, 0, b_buf(t + 2)}, fa1, fb1, fa0, fb0);
+        }
+        pa = pa1;
+    }
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt_lgkm0(0));
+    __builtin_amdgcn_s_barrier();
+    dgor_acc_hazard_wait();
+    {
+        const int ldc = args.ldc;
+        float *Cw = args.C + (size_t)(m0 + wr) * ldc + n0 + wc;
+        const bool vec = ((uintptr_t)Cw & 15) == 0 && (ldc & 3) == 0;
+        store_c_staged_w64<4>(acc, args.alpha, lds, wave, lane, Cw, ldc, M - m0 - wr, N - n0 - wc, vec);
+    }
+}
+
 template <class Op, int BM, int BN, int BK, int WM, int WN>
 hipError_t launch_cfg(const Problem &p, const gemm_plan &plan, hipStream_t s)
 {
@@ -910,8 +1170,14 @@ hipError_t launch_op(const Problem &p, const gemm_plan &plan, hipStream_t s)
         }
         return launch_cfg<Op, 256, 256, 32, 2, 2>(p, plan, s);
     }
-    if (plan.tile_m == 128 && plan.tile_n == 128)
+    if (plan.tile_m == 128 && plan.tile_n == 128) {
+        if (f16_ring128_applies(p.vec_a, p.vec_b, p.N, p.K)) {
+            hipLaunchKernelGGL((mfma_f16_pair128_kernel<Op>), dim3(plan.grid_x * plan.grid_y), dim3(256), 0, s,
+                               ring_args_nn(p, plan));
+            return hipGetLastError();
+        }
         return launch_cfg<Op, 128, 128, 32, 2, 2>(p, plan, s);
+    }
     if (plan.tile_m == 64 && plan.tile_n == 64)
         return launch_cfg<Op, 64, 64, 32, 1, 2>(p, plan, s);
     return hipErrorInvalidValue;

@@ -191,7 +191,9 @@ def test_direct_load_tile_follows_the_spread_of_tiles_over_compute_units():
     assert tile(False, 1024, 1024, 1024) == 64
     assert tile(True, 4096, 4096, 4096) == 256
     assert tile(True, 3072, 3072, 3072) == 256      # 144 ring tiles
-    assert tile(True, 2048, 2048, 2048) == 64       # 64 ring tiles: too few
+    assert tile(True, 2048, 2048, 2048) == 128      # 64 ring tiles: too few; the 128 x 128 ring
+    assert dg.plan(True, 2048, 2048, 2048)["lds_bytes"] == 81920
+    assert tile(True, 1000, 1001, 1000) == 64       # rows not whole 16-byte units: register-staged
     # K % 8 != 0: A's rows are not whole 16-byte units, so no direct loads
     assert tile(True, 4096, 4096, 4095) == 128 and dg.plan(True, 4096, 4096, 4095)["vector_a"] == 0
 

@@ -80,6 +80,8 @@ def _check(lib, fmt, M, N, K, seed, trans_a=False):
 CASES = [
     ("f16", 8000, 4104, [8, 32, 40, 64, 72, 96, 104, 136]),     # 16-bit 256^2 pair ring
     ("bf16", 8000, 4104, [8, 40, 104, 136]),
+    ("f16", 1000, 1032, [8, 32, 40, 72, 136]),                  # 16-bit 128^2 ring
+    ("bf16", 1000, 1032, [8, 40, 136]),
     ("f32", 4000, 4092, [4, 16, 20, 32, 36, 48, 52, 68]),       # FP32 256^2 ring
     ("f32", 1000, 1000, [32, 64, 96, 128, 200, 384]),           # FP32 64^2 ring (32-deep stages)
     ("f32", 4000, 2044, [16, 100]),                             # FP32 128^2 two-stage kernel

@@ -110,13 +110,15 @@ CONFIG_SHAPES = [
     (False, (4097, 16, 2048), (32, 64)),      # FP32 narrow tiles (K past 1024)
     (True, (8191, 4097, 72), (256, 256)),     # FP16 256 x 256 tiles, unaligned rows
     (True, (8000, 4104, 200), (256, 256)),    # FP16 256 x 256 tiles, 128-bit rows, ragged M/N/K
-    (True, (2047, 4095, 200), (128, 128)),    # FP16 128 x 128 tiles
+    (True, (2047, 4095, 200), (128, 128)),    # FP16 128 x 128 tiles, register-staged (unaligned rows)
     (True, (3000, 3080, 200), (256, 256)),    # FP16 256 x 256 ring with 156 tiles
-    (True, (1000, 1000, 1000), (64, 64)),     # FP16 64 x 64 tiles
+    (True, (1000, 1000, 1000), (128, 128)),   # FP16 128 x 128 ring
+    (True, (1000, 1001, 1000), (64, 64)),     # FP16 64 x 64 tiles (unaligned rows)
     ("bf16", (8000, 4104, 200), (256, 256)),  # BF16 ring, ragged M/N/K
     ("bf16", (8191, 4097, 72), (256, 256)),   # BF16 256 x 256, unaligned rows
-    ("bf16", (2047, 4095, 200), (128, 128)),  # BF16 128 x 128 tiles
-    ("bf16", (1000, 1000, 1000), (64, 64)),   # BF16 64 x 64 tiles
+    ("bf16", (2047, 4095, 200), (128, 128)),  # BF16 128 x 128 tiles, register-staged
+    ("bf16", (1000, 1000, 1000), (128, 128)), # BF16 128 x 128 ring
+    ("bf16", (1000, 1001, 1000), (64, 64)),   # BF16 64 x 64 tiles
 ]
 
 
@@ -149,6 +151,22 @@ def test_f16_large_tile_stage_counts(K, fmt):
     A, B = ints(M, N, K, 61 + K, fmt)
     assert_bits_equal(run(fmt, dg.AUTO, A, B), oracle_gemm(A, B), f"ints K={K}")
     A, B = floats(M, N, K, 62 + K, fmt)
+    ref = oracle_gemm(A, B)
+    assert_within(run(fmt, dg.AUTO, A, B), ref, tol_f16(K, ref), f"floats K={K}")
+
+
+# The 128 x 128 16-bit ring: the same stage counts on a shape with ragged
+# M and N (1000 = 7 x 128 + 104, 1032 = 8 x 128 + 8) that takes it.
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+@pytest.mark.parametrize("K", [8, 32, 40, 64, 72, 96, 104, 136])
+def test_f16_mid_tile_ring_stage_counts(K, fmt):
+    M, N = 1000, 1032
+    p = dg.plan(True, M, N, K)
+    assert (p["tile_m"], p["tile_n"], p["lds_bytes"]) == (128, 128, 81920)
+    say(fmt, "128 x 128 ring stages", (M, N, K))
+    A, B = ints(M, N, K, 63 + K, fmt)
+    assert_bits_equal(run(fmt, dg.AUTO, A, B), oracle_gemm(A, B), f"ints K={K}")
+    A, B = floats(M, N, K, 64 + K, fmt)
     ref = oracle_gemm(A, B)
     assert_within(run(fmt, dg.AUTO, A, B), ref, tol_f16(K, ref), f"floats K={K}")
 
