@@ -343,9 +343,23 @@ int run(In in, int variant, int M, int N, int K, const void *A, const void *B, f
 
 // ----------------------------------------------------------- 8-bit inputs --
 
-// Plan for the 8-bit entry points: R8 (the 256 x 256 x 64 ring) when both
-// operands can be read with 16-byte loads, else R0.  INT8 caps K so that the
-// INT32 sum cannot overflow.
+// The INT8 ring tile: 128 when the 128 x 128 ring's estimate beats the
+// 256 x 256 ring's.  Both are rate x the balance of tiles over the compute
+// units (tile_estimate); measured fractions of peak: the 256 x 256 ring 0.48
+// at one tile a unit and 0.52 with more, the 128 x 128 ring 0.30 below two
+// tiles a unit and 0.37 with more.
+int i8_ring_tile(int M, int N)
+{
+    auto tiles = [&](int t) { return (long)ceil_div(M, t) * ceil_div(N, t); };
+    return tile_estimate(tiles(dgor::kRing8SmallTile), 0.30, 0.37) > tile_estimate(tiles(dgor::kRing8Tile), 0.48, 0.52)
+               ? dgor::kRing8SmallTile
+               : dgor::kRing8Tile;
+}
+
+// Plan for the 8-bit entry points: R8 (the 256 x 256 x 64 ring, or for INT8
+// the 128 x 128 one when i8_ring_tile says so) when both operands can be
+// read with 16-byte loads, else R0.  INT8 caps K so that the INT32 sum
+// cannot overflow.
 int plan_8(int fmt, int variant, int M, int N, int K, const void *A, const void *B, gemm_plan *p)
 {
     if (!p)
@@ -374,13 +388,14 @@ int plan_8(int fmt, int variant, int M, int N, int K, const void *A, const void 
         p->outputs_per_thread = 1;
         p->vector_a = p->vector_b = 0;
     } else {
-        p->tile_m = p->tile_n = dgor::kRing8Tile;
+        const int t = fmt == dgor::kFmtI8 ? i8_ring_tile(M, N) : dgor::kRing8Tile;
+        p->tile_m = p->tile_n = t;
         p->tile_k = dgor::kRing8Depth;
         p->threads = 256;
         p->lds_stages = dgor::kRing8Stages;
-        p->lds_bytes = dgor::kRing8LdsBytes;
-        p->tile_bytes = 2 * dgor::kRing8Tile * dgor::kRing8Depth;
-        p->outputs_per_thread = dgor::kRing8Tile * dgor::kRing8Tile / 256;
+        p->lds_bytes = t == dgor::kRing8Tile ? dgor::kRing8LdsBytes : dgor::kRing8SmallLdsBytes;
+        p->tile_bytes = 2 * t * dgor::kRing8Depth;
+        p->outputs_per_thread = t * t / 256;
     }
     finish(p, M, N, K);
     return GEMM_OK;
@@ -407,7 +422,7 @@ int run8(int fmt, int variant, int M, int N, int K, const void *A, const void *B
     else if (plan.variant == GEMM_R0_NAIVE)
         err = dgor::launch_naive_8bit(p, fmt, s);
     else
-        err = dgor::launch_ring8(dgor::ring_args_nn(p, plan), fmt, s);
+        err = dgor::launch_ring8(dgor::ring_args_nn(p, plan), fmt, plan.tile_m, s);
     return err == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
 }
 

@@ -4,9 +4,11 @@
 // among the matrix units' input formats; its sections 24-25 give the
 // staged, double-buffered K-loop these kernels deepen into a ring).
 //
-// Two kernels with one data movement.  A workgroup of four wavefronts
-// computes a 256 x 256 tile of C in 64-deep k-steps; each wavefront a
-// 128 x 128 quarter with 256 accumulator registers per lane.
+// Two kernels with one data movement, and a half-size INT8 variant for
+// mid-size products (mfma_i8_pair128_kernel, described where it is
+// defined).  A workgroup of four wavefronts computes a 256 x 256 tile of C
+// in 64-deep k-steps; each wavefront a 128 x 128 quarter with 256
+// accumulator registers per lane.
 //   FP8 (mfma_8bit_ring_kernel): 4 x 4 blocks of 32 x 32, one
 //     v_mfma_scale_f32_32x32x64_f8f6f4 (unit scales) per block and k-step.
 //   INT8 (mfma_i8_pair_kernel): 8 x 8 blocks of 16 x 16, one
@@ -631,6 +633,267 @@ __global__ __launch_bounds__(256) void mfma_i8_pair_kernel(RingArgs args)
     }
 }
 
+// Epilogue of the INT8 128 x 128 ring: a wavefront's 64 x 64 block leaves
+// through its own 8 KB LDS region in two rounds of 32 rows; element (row,
+// col) of a round sits at row 256 + 16 ((col / 4) ^ 4 ((row / 4) % 4)) +
+// 4 (col % 4), so both the 4-byte writes (lane (g, s) of block j at unit
+// 4 (j ^ g) + s / 4) and the 16-byte reads along the rows are free of bank
+// conflicts.  Arguments as in store_c_staged_i32.
+__device__ __forceinline__ void store_c_staged_w64_i32(const intx4 (&acc)[4][4], uint8_t *lds, int wave, int lane,
+                                                       int *Cw, int ldc, int rows_left, int cols_left, bool vec)
+{
+    constexpr uint32_t OOB = 0x80000000u;
+    uint8_t *w = lds + wave * 8192;
+    const int g = lane >> 4, s16 = lane & 15;
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(
+        Cw, rows_left > 0 && cols_left > 0 ? ((long long)(rows_left - 1) * ldc + cols_left) * 4 : 0);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    *reinterpret_cast<int *>(w + (16 * ii + 4 * g + r) * 256 + (4 * (j ^ g) + (s16 >> 2)) * 16 +
+                                             (s16 & 3) * 4) = acc_read_i32(acc[2 * q + ii][j][r]);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const int row = (lane >> 4) + 4 * t, c = lane & 15;
+            const intx4 v = *reinterpret_cast<const intx4 *>(w + row * 256 + ((c ^ (4 * (t & 3))) * 16));
+            const int grow = 32 * q + row, col = 4 * c;
+            if (grow < rows_left) {
+                const uint32_t o = (uint32_t)(grow * ldc + col) * 4u;
+                if (vec && col + 4 <= cols_left) {
+                    __builtin_amdgcn_raw_buffer_store_b128(v, rc, o, 0, 0);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        __builtin_amdgcn_raw_buffer_store_b32(v[e], rc, col + e < cols_left ? o + 4u * e : OOB, 0, 0);
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// INT8 at mid sizes: the pair ring at half the tile.  A 128 x 128 tile has
+// four wavefronts of 64 x 64 (4 x 4 blocks of v_mfma_i32_16x16x64_i8, 64
+// accumulators a lane) and 80 KB of LDS, so two workgroups share a compute
+// unit and cover each other's waits, and a 2048^3 product has a tile for
+// every compute unit where the 256 x 256 tiles leave three quarters idle.
+//   A pair buffer (16 KB): 128 rows of 128 bytes, unit c of row r at
+//     8 r + (c ^ ((r >> 1) & 7)); wave w's load j (0..3) fills rows
+//     32 w + 8 j .. + 7, two loads a step (half par of the pair).
+//   B step (8 KB): 64 k rows of 128 bytes, unit u of row k at
+//     8 k + (u ^ x(k)), x(k) = ((k >> 1) & 3) + 4 ((k >> 4) & 1); wave w's
+//     load q (0..1) fills k rows 8 (2 w + q) .. + 7, lane p taking physical
+//     unit p % 8 of row 8 (2 w + q) + p / 8.  A transposing-read cycle (32
+//     lanes) takes one 16-byte unit of each of k rows kb .. kb + 7 and of
+//     kb + 16 .. kb + 23: the swizzle gives the sixteen rows sixteen distinct
+//     units modulo the 256 bytes of banks.
+//   Fragments as in the 256 x 256 kernel (A block i: row wr + 16 i + s16,
+//   logical unit 4 h + g; B block j: k rows 16 g .. 16 g + 15 of column
+//   wc + 16 j + s16, two transposing reads 8 k rows apart).
+//   Pipeline, waits and the fragment order as in the pair ring, with 16
+//   MFMAs, 8 fragment reads and 4 loads a wavefront and step.
+namespace ring8_128 {
+constexpr int BK = 64;
+constexpr int A_PAIR_BYTES = 128 * 2 * BK;           // 16 KB
+constexpr int A_PAIRS = 3;
+constexpr int B_BYTES = BK * 128;                    // 8 KB
+constexpr int B_REGION = A_PAIRS * A_PAIR_BYTES;     // 48 KB
+constexpr int LDS_BYTES = B_REGION + 4 * B_BYTES;    // 80 KB
+}  // namespace ring8_128
+
+__global__ __launch_bounds__(256, 2) void mfma_i8_pair128_kernel(RingArgs args)
+{
+    using namespace ring8_128;
+    static_assert(4 * 8192 <= LDS_BYTES, "the epilogue stages through the ring's LDS");
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
+    const uint32_t ring = lds_address(lds);
+    const int M = args.M, N = args.N, K = args.K, lda = args.lda, ldb = args.ldb;
+    const uint8_t *__restrict__ A = (const uint8_t *)args.A;
+    const uint8_t *__restrict__ B = (const uint8_t *)args.B;
+
+    int tm, tn;
+    dgor_tile_of_block((int)blockIdx.x, args.tiles_m, args.tiles_n, args.group_m, tm, tn);
+    const int m0 = tm * 128, n0 = tn * 128;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int wr = (wave >> 1) * 64, wc = (wave & 1) * 64;
+    constexpr uint32_t OOB = 0x80000000u;
+
+    uint32_t a_off[2], b_off[2];
+    int a_kc[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int r = 32 * wave + 8 * j + (lane >> 3);
+        const int c = (lane & 7) ^ ((4 * j + (lane >> 4)) & 7);
+        a_off[j] = (uint32_t)(r * lda + 16 * c);
+        a_kc[j] = 16 * c;
+    }
+    const uint32_t a_row16 = (uint32_t)(16 * lda);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int k = 8 * (2 * wave + q) + (lane >> 3);
+        const int u = (lane & 7) ^ (((k >> 1) & 3) + 4 * ((k >> 4) & 1));
+        b_off[q] = n0 + 16 * u < N ? (uint32_t)(k * ldb + 16 * u) : OOB;
+    }
+    const uint32_t lds_a = ring + (uint32_t)(4 * wave * 1024);
+    const uint32_t lds_b = ring + (uint32_t)(B_REGION + 2 * wave * 1024);
+    struct PairLoads { intx4 r; int k_left; uint32_t dst; };
+    auto a_rsrc = [&](int P, uint32_t buf) {
+        PairLoads L;
+        const int k0 = 2 * BK * P;
+        L.k_left = K - k0;
+        L.r = rsrc_words(A + (size_t)m0 * lda + k0, 0);
+        L.r.z = L.k_left <= 0 ? 0
+              : (m0 + 128 <= M ? 0x7fffffff
+                               : (int)((uint32_t)(M - m0 - 1) * (uint32_t)lda + (uint32_t)L.k_left));
+        L.dst = lds_a + buf;
+        return L;
+    };
+    auto load_a = [&](const PairLoads &L, int j) {
+        const uint32_t off = a_kc[j & 1] >= L.k_left ? OOB : a_off[j & 1] + (uint32_t)(j >> 1) * a_row16;
+        load_to_lds(L.r, L.dst + (uint32_t)(j * 1024), off);
+    };
+    struct BLoads { intx4 r; uint32_t dst; };
+    auto b_rsrc = [&](int st) {
+        BLoads L;
+        const int k0 = BK * st, k_left = K - k0;
+        L.r = rsrc_words(B + (size_t)k0 * ldb + n0, 0);
+        L.r.z = k_left <= 0 ? 0
+              : (k_left >= BK ? 0x7fffffff : (int)((uint32_t)(k_left - 1) * (uint32_t)ldb + (uint32_t)(N - n0)));
+        L.dst = lds_b + (uint32_t)((st & 3) * B_BYTES);
+        return L;
+    };
+    auto load_b = [&](const BLoads &L, int q) { load_to_lds(L.r, L.dst + (uint32_t)(q * 1024), b_off[q]); };
+
+    const int s16 = lane & 15, g = lane >> 4;
+    const uint32_t a_lane = (uint32_t)((wr + s16) * 128) | (uint32_t)((g ^ ((s16 >> 1) & 7)) * 16);
+    const int ks_x = ((s16 >> 2) & 3) + 4 * (g & 1);
+    const uint32_t b_lane = (uint32_t)(B_REGION + (16 * g + (s16 >> 1)) * 128 + 8 * (s16 & 1));
+    uint32_t b_unit[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        b_unit[j] = (uint32_t)(((wc / 16 + j) ^ ks_x) * 16);
+    struct ReadSrc { uint32_t a_buf; int a_half; uint32_t b_buf; };
+    auto read_a = [&](const ReadSrc &R, int i) -> intx4 {
+        const uint32_t addr = (a_lane ^ (uint32_t)(64 * R.a_half)) + R.a_buf + (uint32_t)(i * 2048);
+        return *reinterpret_cast<const intx4 *>(lds + addr);
+    };
+    auto read_b = [&](const ReadSrc &R, int j) -> intx4 {
+        const uint8_t *p = lds + b_lane + R.b_buf + b_unit[j];
+        const intx2 lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_intx2 *)p);
+        const intx2 hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_intx2 *)(p + 1024));
+        return intx4{lo[0], lo[1], hi[0], hi[1]};
+    };
+    auto fread = [&](const ReadSrc &R, int r, intx4 *fa, intx4 *fb) {
+        if (r == 0 || r >= 5)
+            fa[r == 0 ? 0 : r - 4] = read_a(R, r == 0 ? 0 : r - 4);
+        else
+            fb[r - 1] = read_b(R, r - 1);
+    };
+
+    intx4 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                asm("v_accvgpr_write_b32 %0, 0" : "=a"(acc[i][j][r]));
+
+    struct StepLoads { BLoads b; PairLoads a; };
+    auto step = [&](int par, const StepLoads &L, const ReadSrc &R, intx4 *ca, intx4 *cb, intx4 *na, intx4 *nb) {
+#pragma unroll
+        for (int m = 0; m < 16; ++m) {
+            const int i = m >> 2, j = m & 3;
+            acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ca[i], cb[j], acc[i][j], 0, 0, 0);
+            if (m < 8)
+                fread(R, m, na, nb);
+            if (m >= 8 && (m & 1)) {
+                const int ld = (m - 8) >> 1;
+                if (ld < 2)
+                    load_b(L.b, ld);
+                else
+                    load_a(L.a, 2 * par + ld - 2);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    auto step_begin = [&](int s, uint32_t a_load_buf) {
+        if (s == 0)
+            __builtin_amdgcn_s_waitcnt(wait_vmcnt_lgkm0(6));
+        else
+            __builtin_amdgcn_s_waitcnt(wait_vmcnt_lgkm0(4));
+        __builtin_amdgcn_s_barrier();
+        const StepLoads L{b_rsrc(s + 3), a_rsrc((s >> 1) + 2, a_load_buf)};
+        __builtin_amdgcn_sched_barrier(0);
+        return L;
+    };
+    auto b_buf = [](int st) { return (uint32_t)((st & 3) * B_BYTES); };
+    auto next_pair = [](uint32_t pb) { return pb == (uint32_t)((A_PAIRS - 1) * A_PAIR_BYTES) ? 0u : pb + A_PAIR_BYTES; };
+
+    intx4 fa0[4], fa1[4], fb0[4], fb1[4];
+    {
+        const PairLoads L = a_rsrc(0, 0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            load_a(L, j);
+    }
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+        const BLoads L = b_rsrc(st);
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+            load_b(L, q);
+    }
+    {
+        const PairLoads L = a_rsrc(1, A_PAIR_BYTES);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            load_a(L, j);
+    }
+    {
+        const BLoads L = b_rsrc(2);
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+            load_b(L, q);
+    }
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(8));
+    __builtin_amdgcn_s_barrier();
+    {
+        const ReadSrc R0{0u, 0, b_buf(0)};
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+            fread(R0, r, fa0, fb0);
+    }
+
+    const int steps = (K + BK - 1) / BK;
+    uint32_t pa = 0;
+    for (int s = 0; s < steps; s += 2) {
+        const uint32_t pa1 = next_pair(pa), pa2 = next_pair(pa1);
+        StepLoads L = step_begin(s, pa2);
+        step(0, L, ReadSrc{pa, 1, b_buf(s + 1)}, fa0, fb0, fa1, fb1);
+        if (s + 1 < steps) {
+            L = step_begin(s + 1, pa2);
+            step(1, L, ReadSrc{pa1, 0, b_buf(s + 2)}, fa1, fb1, fa0, fb0);
+        }
+        pa = pa1;
+    }
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt_lgkm0(0));
+    __builtin_amdgcn_s_barrier();
+    dgor_acc_hazard_wait();
+    {
+        const int ldc = args.ldc;
+        int *Cw = reinterpret_cast<int *>(args.C) + (size_t)(m0 + wr) * ldc + n0 + wc;
+        const bool vec = ((uintptr_t)Cw & 15) == 0 && (ldc & 3) == 0;
+        store_c_staged_w64_i32(acc, lds, wave, lane, Cw, ldc, M - m0 - wr, N - n0 - wc, vec);
+    }
+}
+
 template <int FMT>
 hipError_t launch_fp8(const RingArgs &a, hipStream_t s)
 {
@@ -640,9 +903,15 @@ hipError_t launch_fp8(const RingArgs &a, hipStream_t s)
 
 }  // namespace
 
-hipError_t launch_ring8(const RingArgs &a, int fmt, hipStream_t s)
+hipError_t launch_ring8(const RingArgs &a, int fmt, int tile, hipStream_t s)
 {
     if (a.accumulate || a.trans_a || a.trans_b || a.splits > 1 || a.alpha != 1.f)
+        return hipErrorInvalidValue;
+    if (tile == kRing8SmallTile && fmt == kFmtI8) {
+        hipLaunchKernelGGL(mfma_i8_pair128_kernel, dim3(a.tiles_m * a.tiles_n), dim3(256), 0, s, a);
+        return hipGetLastError();
+    }
+    if (tile != kRing8Tile)
         return hipErrorInvalidValue;
     switch (fmt) {
     case kFmtE4M3:
