@@ -343,22 +343,27 @@ int run(In in, int variant, int M, int N, int K, const void *A, const void *B, f
 
 // ----------------------------------------------------------- 8-bit inputs --
 
-// The INT8 ring tile: 128 when the 128 x 128 ring's estimate beats the
+// The 8-bit ring tile: 128 when the 128 x 128 ring's estimate beats the
 // 256 x 256 ring's.  Both are rate x the balance of tiles over the compute
-// units (tile_estimate); measured fractions of peak: the 256 x 256 ring 0.48
-// at one tile a unit and 0.52 with more, the 128 x 128 ring 0.30 below two
-// tiles a unit and 0.37 with more.
-int i8_ring_tile(int M, int N)
+// units (tile_estimate), with measured fractions of peak.  INT8: the
+// 256 x 256 ring 0.48 at one tile a unit and 0.52 with more, the 128 x 128
+// ring 0.30 below two tiles a unit and 0.37 with more.  FP8: 0.57 for the
+// 256 x 256 ring with several tiles a unit, and 0.55 below two, where fewer
+// busy units leave power headroom that raises their clock (3072^3, 144
+// tiles, runs at 0.32 against 0.31 on the 128 x 128 ring); the 128 x 128 ring
+// 0.33 and 0.40.
+int ring8_tile(int fmt, int M, int N)
 {
     auto tiles = [&](int t) { return (long)ceil_div(M, t) * ceil_div(N, t); };
-    return tile_estimate(tiles(dgor::kRing8SmallTile), 0.30, 0.37) > tile_estimate(tiles(dgor::kRing8Tile), 0.48, 0.52)
-               ? dgor::kRing8SmallTile
-               : dgor::kRing8Tile;
+    const bool i8 = fmt == dgor::kFmtI8;
+    const double e256 = tile_estimate(tiles(dgor::kRing8Tile), i8 ? 0.48 : 0.55, i8 ? 0.52 : 0.57);
+    const double e128 = tile_estimate(tiles(dgor::kRing8SmallTile), i8 ? 0.30 : 0.33, i8 ? 0.37 : 0.40);
+    return e128 > e256 ? dgor::kRing8SmallTile : dgor::kRing8Tile;
 }
 
-// Plan for the 8-bit entry points: R8 (the 256 x 256 x 64 ring, or for INT8
-// the 128 x 128 one when i8_ring_tile says so) when both operands can be
-// read with 16-byte loads, else R0.  INT8 caps K so that the INT32 sum
+// Plan for the 8-bit entry points: R8 (the 256 x 256 x 64 ring, or the
+// 128 x 128 one when ring8_tile says so) when both operands can be read with
+// 16-byte loads, else R0.  INT8 caps K so that the INT32 sum
 // cannot overflow.
 int plan_8(int fmt, int variant, int M, int N, int K, const void *A, const void *B, gemm_plan *p)
 {
@@ -388,7 +393,7 @@ int plan_8(int fmt, int variant, int M, int N, int K, const void *A, const void 
         p->outputs_per_thread = 1;
         p->vector_a = p->vector_b = 0;
     } else {
-        const int t = fmt == dgor::kFmtI8 ? i8_ring_tile(M, N) : dgor::kRing8Tile;
+        const int t = ring8_tile(fmt, M, N);
         p->tile_m = p->tile_n = t;
         p->tile_k = dgor::kRing8Depth;
         p->threads = 256;

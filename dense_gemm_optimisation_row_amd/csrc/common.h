@@ -77,12 +77,12 @@ constexpr int kFmtE4M3 = 0, kFmtE5M2 = 1, kFmtI8 = 2;
 constexpr int kRing8Tile = 256, kRing8Depth = 64, kRing8Stages = 4;
 constexpr int kRing8LdsBytes = 3 * kRing8Tile * 2 * kRing8Depth + kRing8Stages * kRing8Depth * kRing8Tile;
 constexpr int kI8MaxK = 131072;   // |sum| <= 128 * 128 * K must fit int32
-// INT8 at mid sizes: the same ring at a 128 x 128 tile, 80 KB of LDS (three
-// 16 KB A pair buffers, four 8 KB B steps), two workgroups a compute unit.
+// Mid sizes: the same ring at a 128 x 128 tile, 80 KB of LDS (three 16 KB
+// A pair buffers, four 8 KB B steps), two workgroups a compute unit.
 constexpr int kRing8SmallTile = 128;
 constexpr int kRing8SmallLdsBytes =
     3 * kRing8SmallTile * 2 * kRing8Depth + kRing8Stages * kRing8Depth * kRing8SmallTile;
-// tile: kRing8Tile, or kRing8SmallTile for INT8.
+// tile: kRing8Tile or kRing8SmallTile.
 hipError_t launch_ring8(const RingArgs &args, int fmt, int tile, hipStream_t stream);
 
 // Convolution through im2col: shape (P, Q derived), and the passes around the

@@ -4,9 +4,9 @@
 // among the matrix units' input formats; its sections 24-25 give the
 // staged, double-buffered K-loop these kernels deepen into a ring).
 //
-// Two kernels with one data movement, and a half-size INT8 variant for
-// mid-size products (mfma_i8_pair128_kernel, described where it is
-// defined).  A workgroup of four wavefronts computes a 256 x 256 tile of C
+// Two kernels with one data movement, and half-size variants of both for
+// mid-size products (mfma_i8_pair128_kernel, mfma_fp8_pair128_kernel,
+// described where they are defined).  A workgroup of four wavefronts computes a 256 x 256 tile of C
 // in 64-deep k-steps; each wavefront a 128 x 128 quarter with 256
 // accumulator registers per lane.
 //   FP8 (mfma_8bit_ring_kernel): 4 x 4 blocks of 32 x 32, one
@@ -677,7 +677,7 @@ __device__ __forceinline__ void store_c_staged_w64_i32(const intx4 (&acc)[4][4],
 }
 
 // ---------------------------------------------------------------------------
-// INT8 at mid sizes: the pair ring at half the tile.  A 128 x 128 tile has
+// 8-bit inputs at mid sizes: the pair rings at half the tile.  INT8 first.  A 128 x 128 tile has
 // four wavefronts of 64 x 64 (4 x 4 blocks of v_mfma_i32_16x16x64_i8, 64
 // accumulators a lane) and 80 KB of LDS, so two workgroups share a compute
 // unit and cover each other's waits, and a 2048^3 product has a tile for
@@ -894,10 +894,271 @@ __global__ __launch_bounds__(256, 2) void mfma_i8_pair128_kernel(RingArgs args)
     }
 }
 
-template <int FMT>
-hipError_t launch_fp8(const RingArgs &a, hipStream_t s)
+// Epilogue of the FP8 128 x 128 ring: a wavefront's 64 x 64 block in the
+// 32 x 32 layout leaves through its own 8 KB LDS region in two rounds (one
+// per row of blocks) of 32 rows; element (row, col) of a round sits at
+// row 256 + 16 ((col / 4) ^ 8 ((row / 4) % 2)) + 4 (col % 4), so the 4-byte
+// writes (lanes 0..31 and 32..63 take rows 4 apart, on the two halves of the
+// banks) and the 16-byte reads along the rows are free of bank conflicts.
+// Cw: the block's first element; rows_left / cols_left: its rows and columns
+// inside C; vec: Cw 16-byte aligned and ldc a multiple of 4.
+__device__ __forceinline__ void store_c_staged_w64_32(const floatx16 (&acc)[2][2], uint8_t *lds, int wave, int lane,
+                                                      float *Cw, int ldc, int rows_left, int cols_left, bool vec)
 {
-    hipLaunchKernelGGL(mfma_8bit_ring_kernel<OpFp8<FMT>>, dim3(a.tiles_m * a.tiles_n), dim3(256), 0, s, a);
+    typedef unsigned uintx4 __attribute__((ext_vector_type(4)));
+    constexpr uint32_t OOB = 0x80000000u;
+    uint8_t *w = lds + wave * 8192;
+    const int r32 = lane & 31, g = lane >> 5;
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(
+        Cw, rows_left > 0 && cols_left > 0 ? ((long long)(rows_left - 1) * ldc + cols_left) * 4 : 0);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int row = 8 * (e >> 2) + 4 * g + (e & 3), col = 32 * j + r32;
+                *reinterpret_cast<float *>(w + row * 256 + 16 * ((col >> 2) ^ (8 * g)) + 4 * (col & 3)) =
+                    dgor_acc_read(acc[i][j][e]);
+            }
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const int row = (lane >> 4) + 4 * t, c = lane & 15;
+            const uintx4 v = *reinterpret_cast<const uintx4 *>(w + row * 256 + ((c ^ (8 * (t & 1))) * 16));
+            const int grow = 32 * i + row, col = 4 * c;
+            if (grow < rows_left) {
+                const uint32_t o = (uint32_t)(grow * ldc + col) * 4u;
+                if (vec && col + 4 <= cols_left) {
+                    __builtin_amdgcn_raw_buffer_store_b128(v, rc, o, 0, 0);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        __builtin_amdgcn_raw_buffer_store_b32(v[e], rc, col + e < cols_left ? o + 4u * e : OOB, 0, 0);
+                }
+            }
+        }
+    }
+}
+
+// The FP8 128 x 128 ring: the INT8 one's tile, LDS plan, pipeline and waits
+// with the FP8 kernel's 32 x 32 blocks (2 x 2 a wavefront, one
+// v_mfma_scale_f32_32x32x64_f8f6f4 per block and step).  Its transposing
+// reads take 8 k rows of one 32-column block per cycle (32 lanes: two
+// 16-column halves of 8 bytes each), so B rows use the swizzle
+// x(k) = 2 ((k >> 1) & 3): the four even and the four odd rows of a read
+// get four distinct pairs of units, which with the row parity (128 bytes
+// apart) puts the 32 lanes' 8-byte pieces on 32 distinct bank pairs.  Each
+// of the 4 MFMAs of a step is followed by three of the next step's 12
+// fragment reads and one of its 4 loads.
+template <class Op>
+__global__ __launch_bounds__(256, 2) void mfma_fp8_pair128_kernel(RingArgs args)
+{
+    using namespace ring8_128;
+    static_assert(4 * 8192 <= LDS_BYTES, "the epilogue stages through the ring's LDS");
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
+    const uint32_t ring = lds_address(lds);
+    const int M = args.M, N = args.N, K = args.K, lda = args.lda, ldb = args.ldb;
+    const uint8_t *__restrict__ A = (const uint8_t *)args.A;
+    const uint8_t *__restrict__ B = (const uint8_t *)args.B;
+
+    int tm, tn;
+    dgor_tile_of_block((int)blockIdx.x, args.tiles_m, args.tiles_n, args.group_m, tm, tn);
+    const int m0 = tm * 128, n0 = tn * 128;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int wr = (wave >> 1) * 64, wc = (wave & 1) * 64;
+    constexpr uint32_t OOB = 0x80000000u;
+
+    // ---- loader: as in the INT8 128 x 128 ring, B with x(k) = 2 ((k >> 1) & 3)
+    uint32_t a_off[2], b_off[2];
+    int a_kc[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int r = 32 * wave + 8 * j + (lane >> 3);
+        const int c = (lane & 7) ^ ((4 * j + (lane >> 4)) & 7);
+        a_off[j] = (uint32_t)(r * lda + 16 * c);
+        a_kc[j] = 16 * c;
+    }
+    const uint32_t a_row16 = (uint32_t)(16 * lda);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int k = 8 * (2 * wave + q) + (lane >> 3);
+        const int u = (lane & 7) ^ (2 * ((k >> 1) & 3));
+        b_off[q] = n0 + 16 * u < N ? (uint32_t)(k * ldb + 16 * u) : OOB;
+    }
+    const uint32_t lds_a = ring + (uint32_t)(4 * wave * 1024);
+    const uint32_t lds_b = ring + (uint32_t)(B_REGION + 2 * wave * 1024);
+    struct PairLoads { intx4 r; int k_left; uint32_t dst; };
+    auto a_rsrc = [&](int P, uint32_t buf) {
+        PairLoads L;
+        const int k0 = 2 * BK * P;
+        L.k_left = K - k0;
+        L.r = rsrc_words(A + (size_t)m0 * lda + k0, 0);
+        L.r.z = L.k_left <= 0 ? 0
+              : (m0 + 128 <= M ? 0x7fffffff
+                               : (int)((uint32_t)(M - m0 - 1) * (uint32_t)lda + (uint32_t)L.k_left));
+        L.dst = lds_a + buf;
+        return L;
+    };
+    auto load_a = [&](const PairLoads &L, int j) {
+        const uint32_t off = a_kc[j & 1] >= L.k_left ? OOB : a_off[j & 1] + (uint32_t)(j >> 1) * a_row16;
+        load_to_lds(L.r, L.dst + (uint32_t)(j * 1024), off);
+    };
+    struct BLoads { intx4 r; uint32_t dst; };
+    auto b_rsrc = [&](int st) {
+        BLoads L;
+        const int k0 = BK * st, k_left = K - k0;
+        L.r = rsrc_words(B + (size_t)k0 * ldb + n0, 0);
+        L.r.z = k_left <= 0 ? 0
+              : (k_left >= BK ? 0x7fffffff : (int)((uint32_t)(k_left - 1) * (uint32_t)ldb + (uint32_t)(N - n0)));
+        L.dst = lds_b + (uint32_t)((st & 3) * B_BYTES);
+        return L;
+    };
+    auto load_b = [&](const BLoads &L, int q) { load_to_lds(L.r, L.dst + (uint32_t)(q * 1024), b_off[q]); };
+
+    // ---- fragment reads (the 32 x 32 layout of the 256 x 256 FP8 kernel).
+    // A block i: row wr + 32 i + r32, logical units 4 h + 2 g + u (u = 0, 1),
+    // physical unit ^ ((row >> 1) & 7).  B block j, read q: k row
+    // 32 g + 8 q + s16 / 2, byte 8 (s16 % 2) of logical unit
+    // wc / 16 + 2 j + hg, physical unit ^ 2 ((s16 >> 2) & 3).
+    const int r32 = lane & 31, g = lane >> 5;
+    const int s16 = lane & 15, hg = (lane >> 4) & 1;
+    const uint32_t a_lane = (uint32_t)((wr + r32) * 128) | (uint32_t)(((2 * g) ^ ((r32 >> 1) & 7)) * 16);
+    uint32_t b_lane[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+        b_lane[j] = (uint32_t)(B_REGION + (32 * g + (s16 >> 1)) * 128 + 8 * (s16 & 1) +
+                               16 * (((wc / 16 + 2 * j) | hg) ^ (2 * ((s16 >> 2) & 3))));
+    struct ReadSrc { uint32_t a_buf; int a_half; uint32_t b_buf; };
+    auto read_a = [&](const ReadSrc &R, int blk, int part, intx8 &f) {
+        const uint32_t addr = (a_lane ^ (uint32_t)((4 * R.a_half + part) * 16)) + R.a_buf + (uint32_t)(blk * 32 * 128);
+        const intx4 v = *reinterpret_cast<const intx4 *>(lds + addr);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            f[4 * part + e] = v[e];
+    };
+    auto read_b = [&](const ReadSrc &R, int blk, int part, intx8 &f) {
+        const uint32_t addr = b_lane[blk] + R.b_buf + (uint32_t)(part * 1024);
+        const intx2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_intx2 *)(lds + addr));
+        f[2 * part + 0] = v[0];
+        f[2 * part + 1] = v[1];
+    };
+    // read r (0..11): A block 0 (2 reads), B blocks 0 and 1 (4 each), A block 1
+    auto fread = [&](const ReadSrc &R, int r, intx8 *fa, intx8 *fb) {
+        if (r < 2)
+            read_a(R, 0, r, fa[0]);
+        else if (r < 10)
+            read_b(R, (r - 2) >> 2, (r - 2) & 3, fb[(r - 2) >> 2]);
+        else
+            read_a(R, 1, r - 10, fa[1]);
+    };
+
+    floatx16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                asm("v_accvgpr_write_b32 %0, 0" : "=a"(acc[i][j][e]));
+
+    // One step: its 4 MFMAs, each followed by three of the next step's reads
+    // and one of the step's loads (B step s + 3, then half par of A pair
+    // s / 2 + 2).
+    struct StepLoads { BLoads b; PairLoads a; };
+    auto step = [&](int par, const StepLoads &L, const ReadSrc &R, intx8 *ca, intx8 *cb, intx8 *na, intx8 *nb) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int i = m >> 1, j = m & 1;
+            acc[i][j] = Op::mma(ca[i], cb[j], acc[i][j]);
+#pragma unroll
+            for (int r = 0; r < 3; ++r)
+                fread(R, 3 * m + r, na, nb);
+            if (m < 2)
+                load_b(L.b, m);
+            else
+                load_a(L.a, 2 * par + m - 2);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    auto step_begin = [&](int s, uint32_t a_load_buf) {
+        if (s == 0)
+            __builtin_amdgcn_s_waitcnt(wait_vmcnt_lgkm0(6));
+        else
+            __builtin_amdgcn_s_waitcnt(wait_vmcnt_lgkm0(4));
+        __builtin_amdgcn_s_barrier();
+        const StepLoads L{b_rsrc(s + 3), a_rsrc((s >> 1) + 2, a_load_buf)};
+        __builtin_amdgcn_sched_barrier(0);
+        return L;
+    };
+    auto b_buf = [](int st) { return (uint32_t)((st & 3) * B_BYTES); };
+    auto next_pair = [](uint32_t pb) { return pb == (uint32_t)((A_PAIRS - 1) * A_PAIR_BYTES) ? 0u : pb + A_PAIR_BYTES; };
+
+    intx8 fa0[2], fa1[2], fb0[2], fb1[2];
+    {
+        const PairLoads L = a_rsrc(0, 0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            load_a(L, j);
+    }
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+        const BLoads L = b_rsrc(st);
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+            load_b(L, q);
+    }
+    {
+        const PairLoads L = a_rsrc(1, A_PAIR_BYTES);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            load_a(L, j);
+    }
+    {
+        const BLoads L = b_rsrc(2);
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+            load_b(L, q);
+    }
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(8));
+    __builtin_amdgcn_s_barrier();
+    {
+        const ReadSrc R0{0u, 0, b_buf(0)};
+#pragma unroll
+        for (int r = 0; r < 12; ++r)
+            fread(R0, r, fa0, fb0);
+    }
+
+    const int steps = (K + BK - 1) / BK;
+    uint32_t pa = 0;
+    for (int s = 0; s < steps; s += 2) {
+        const uint32_t pa1 = next_pair(pa), pa2 = next_pair(pa1);
+        StepLoads L = step_begin(s, pa2);
+        step(0, L, ReadSrc{pa, 1, b_buf(s + 1)}, fa0, fb0, fa1, fb1);
+        if (s + 1 < steps) {
+            L = step_begin(s + 1, pa2);
+            step(1, L, ReadSrc{pa1, 0, b_buf(s + 2)}, fa1, fb1, fa0, fb0);
+        }
+        pa = pa1;
+    }
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt_lgkm0(0));
+    __builtin_amdgcn_s_barrier();
+    dgor_acc_hazard_wait();
+    {
+        const int ldc = args.ldc;
+        float *Cw = args.C + (size_t)(m0 + wr) * ldc + n0 + wc;
+        const bool vec = ((uintptr_t)Cw & 15) == 0 && (ldc & 3) == 0;
+        store_c_staged_w64_32(acc, lds, wave, lane, Cw, ldc, M - m0 - wr, N - n0 - wc, vec);
+    }
+}
+
+template <int FMT>
+hipError_t launch_fp8(const RingArgs &a, int tile, hipStream_t s)
+{
+    if (tile == kRing8SmallTile)
+        hipLaunchKernelGGL(mfma_fp8_pair128_kernel<OpFp8<FMT>>, dim3(a.tiles_m * a.tiles_n), dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL(mfma_8bit_ring_kernel<OpFp8<FMT>>, dim3(a.tiles_m * a.tiles_n), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
@@ -907,19 +1168,18 @@ hipError_t launch_ring8(const RingArgs &a, int fmt, int tile, hipStream_t s)
 {
     if (a.accumulate || a.trans_a || a.trans_b || a.splits > 1 || a.alpha != 1.f)
         return hipErrorInvalidValue;
-    if (tile == kRing8SmallTile && fmt == kFmtI8) {
-        hipLaunchKernelGGL(mfma_i8_pair128_kernel, dim3(a.tiles_m * a.tiles_n), dim3(256), 0, s, a);
-        return hipGetLastError();
-    }
-    if (tile != kRing8Tile)
+    if (tile != kRing8Tile && tile != kRing8SmallTile)
         return hipErrorInvalidValue;
     switch (fmt) {
     case kFmtE4M3:
-        return launch_fp8<0>(a, s);
+        return launch_fp8<0>(a, tile, s);
     case kFmtE5M2:
-        return launch_fp8<1>(a, s);
+        return launch_fp8<1>(a, tile, s);
     case kFmtI8:
-        hipLaunchKernelGGL(mfma_i8_pair_kernel, dim3(a.tiles_m * a.tiles_n), dim3(256), 0, s, a);
+        if (tile == kRing8SmallTile)
+            hipLaunchKernelGGL(mfma_i8_pair128_kernel, dim3(a.tiles_m * a.tiles_n), dim3(256), 0, s, a);
+        else
+            hipLaunchKernelGGL(mfma_i8_pair_kernel, dim3(a.tiles_m * a.tiles_n), dim3(256), 0, s, a);
         return hipGetLastError();
     default:
         return hipErrorInvalidValue;

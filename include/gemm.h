@@ -124,10 +124,10 @@ int gemm_bf16_f32acc(int M, int N, int K, const uint16_t *A, const uint16_t *B,
  *     (C is int32_t).  K above 131072 -> GEMM_ERR_INVALID_DIM, since
  *     128 * 128 * K must fit int32.
  * Calls with 16-byte aligned A and B, K and N multiples of 16, K and N
- * below 2^22 take R8 (256 x 256 x 64 tiles through a four-stage LDS ring;
- * INT8 takes 128 x 128 x 64 tiles instead where they spread better over
- * the compute units, as the plan reports); others take R0.  Same
- * conventions and errors as gemm_f32 otherwise.
+ * below 2^22 take R8 (256 x 256 x 64 tiles through a four-stage LDS ring,
+ * or 128 x 128 x 64 tiles where they spread better over the compute units,
+ * as the plan reports); others take R0.  Same conventions and errors as
+ * gemm_f32 otherwise.
  */
 int gemm_e4m3_f32acc(int M, int N, int K, const uint8_t *A, const uint8_t *B,
                      float *C, void *stream);

@@ -17,9 +17,9 @@ Bars (elementwise):
     8 * 2^-13 = 2^-10 of its largest product.  Taken twice over for margin,
     plus FP32 accumulation of the K / 8 group sums (below K 2^-27 S, also
     doubled).  The plain kernel sums in FP32 and meets the same bound.
-Shapes span several 256 x 256 tiles with ragged M and N edges and a k tail;
-INT8 takes 128 x 128 tiles at those sizes, and its 256 x 256 ring is checked
-separately on shapes that have enough tiles for it.
+Shapes span several tiles with ragged M and N edges and a k tail; at most of
+those sizes the ring takes 128 x 128 tiles, and its 256 x 256 tiles are
+checked separately on shapes that have enough tiles for them.
 The 8192^3 workloads are compared in full elsewhere (test_full_gpu.py); here
 they get a quick sampled pre-check plus an invariant over every output (C v
 against A (B v) for a random +-1 vector v).
@@ -104,7 +104,7 @@ def mats(fmt, M, N, K, seed, dist="uniform"):
     return inputs.matrices(M, N, K, seed, dist, fmt)
 
 
-# Multiples of 16 in K and N take R8 (ragged 256-tiles in M and N, k tails of
+# Multiples of 16 in K and N take R8 (ragged tiles in M and N, k tails of
 # 16 .. 48 past a 64-deep step); the rest take R0.
 RING_SHAPES = [(16, 16, 16), (64, 48, 64), (256, 256, 256), (300, 272, 80), (513, 528, 144),
                (1000, 1008, 1024), (37, 1040, 48), (1040, 32, 1008)]
@@ -190,7 +190,7 @@ def test_8bit_k0_empty_and_misaligned(fmt):
 def test_8bit_ring_with_c_off_16_byte_alignment(fmt, c_off):
     """The ring with aligned A and B and C starting c_off elements (4 c_off
     bytes) past a 16-byte boundary: the stores fall back to one element at a
-    time (the INT8 kernel's LDS-staged epilogue and the FP8 kernel's direct
+    time (the LDS-staged epilogues and the 256 x 256 FP8 kernel's direct
     stores alike).  Ragged tiles; every element around C keeps its sentinel."""
     import torch
     M, N, K = 300, 272, 208
@@ -208,40 +208,43 @@ def test_8bit_ring_with_c_off_16_byte_alignment(fmt, c_off):
     check(fmt, got[c_off:c_off + M * N].reshape(M, N), A, B, f"{fmt} C offset {c_off}", exact=True)
 
 
-# INT8 shapes for each ring tile: (M, N, K, tile); ragged M and N edges, k
-# tails of 16 .. 48 past a 64-deep step, one to many steps
-I8_TILE_SHAPES = [(4000, 4016, 16, 256), (4000, 4016, 80, 256), (4000, 4016, 208, 256), (4000, 4016, 1040, 256),
-                  (1000, 1008, 1024, 128), (129, 144, 16, 128), (2000, 1008, 4112, 128), (3000, 3008, 144, 128)]
+# Shapes for each ring tile: (M, N, K, tile); ragged M and N edges, k tails
+# of 16 .. 48 past a 64-deep step, one to many steps
+TILE_SHAPES = [(4000, 4016, 16, 256), (4000, 4016, 80, 256), (4000, 4016, 208, 256), (4000, 4016, 1040, 256),
+               (1000, 1008, 1024, 128), (129, 144, 16, 128), (2000, 1008, 4112, 128), (2500, 2512, 144, 128)]
 
 
-@pytest.mark.parametrize("shape", I8_TILE_SHAPES, ids=lambda s: "x".join(map(str, s)))
-def test_int8_both_ring_tiles(shape):
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("shape", TILE_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_8bit_both_ring_tiles(fmt, shape):
     M, N, K, tile = shape
-    plan = dg.plan("i8", M, N, K)
+    plan = dg.plan(fmt, M, N, K)
     assert plan["variant"] == dg.R8_MFMA_8BIT and plan["tile_m"] == tile
-    say("int8 ring tile", tile, (M, N, K))
-    A, B = mats("i8", M, N, K, 4800 + K)
-    check("i8", run("i8", dg.AUTO, A, B), A, B, f"i8 {shape}")
-    A, B = mats("i8", M, N, K, 4850 + K, "int")
-    check("i8", run("i8", dg.AUTO, A, B), A, B, f"i8 {shape} int")
+    say("8bit ring tile", fmt, tile, (M, N, K))
+    A, B = mats(fmt, M, N, K, 4800 + K)
+    check(fmt, run(fmt, dg.AUTO, A, B), A, B, f"{fmt} {shape}")
+    A, B = mats(fmt, M, N, K, 4850 + K, "int")
+    check(fmt, run(fmt, dg.AUTO, A, B), A, B, f"{fmt} {shape} int", exact=True)
 
 
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("c_off", [1, 3])
-def test_int8_256_ring_with_c_off_16_byte_alignment(c_off):
-    """As the test above, on the INT8 256 x 256 ring (its own epilogue)."""
+def test_8bit_256_ring_with_c_off_16_byte_alignment(fmt, c_off):
+    """As the test above, on the 256 x 256 rings."""
     import torch
     M, N, K = 4000, 4016, 80
-    say("int8 256^2 ring, C off 16-byte alignment", c_off)
-    A, B = mats("i8", M, N, K, 4900 + c_off)
-    assert dg.plan("i8", M, N, K)["tile_m"] == 256
-    buf = torch.full((M * N + 8,), -77, dtype=torch.int32, device="cuda")
-    a, b = to_dev(A, "i8"), to_dev(B, "i8")
-    assert binding.raw_gemm("i8", None, M, N, K, a.data_ptr(), b.data_ptr(), buf.data_ptr() + 4 * c_off,
+    say("8bit 256^2 ring, C off 16-byte alignment", fmt, c_off)
+    A, B = mats(fmt, M, N, K, 4900 + c_off, "int")
+    assert dg.plan(fmt, M, N, K)["tile_m"] == 256
+    out_dtype = torch.int32 if fmt == "i8" else torch.float32
+    buf = torch.full((M * N + 8,), -77, dtype=out_dtype, device="cuda")
+    a, b = to_dev(A, fmt), to_dev(B, fmt)
+    assert binding.raw_gemm(fmt, None, M, N, K, a.data_ptr(), b.data_ptr(), buf.data_ptr() + 4 * c_off,
                             None) == binding.GEMM_OK
     torch.cuda.synchronize()
     got = buf.cpu().numpy()
     assert np.all(got[:c_off] == -77) and np.all(got[c_off + M * N:] == -77), "a store outside C"
-    check("i8", got[c_off:c_off + M * N].reshape(M, N), A, B, f"i8 256^2 C offset {c_off}")
+    check(fmt, got[c_off:c_off + M * N].reshape(M, N), A, B, f"{fmt} 256^2 C offset {c_off}", exact=True)
 
 
 @pytest.mark.parametrize("name", ["e4m3_8192", "e5m2_8192", "i8_8192"])

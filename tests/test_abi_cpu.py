@@ -240,24 +240,27 @@ def test_8bit_plans_take_the_ring_when_operands_are_aligned():
     assert dg.plan("e4m3", 4, 4, 131088)["launches"] == 1
 
 
-def test_int8_ring_tile_follows_the_spread_of_tiles_over_compute_units():
-    """INT8 takes the 128 x 128 ring where its measured rate times the
-    evenness of its tiles over the 256 compute units beats the 256 x 256
-    ring's; FP8 keeps the 256 x 256 ring."""
+def test_8bit_ring_tile_follows_the_spread_of_tiles_over_compute_units():
+    """The 8-bit formats take the 128 x 128 ring where its measured rate times
+    the evenness of its tiles over the 256 compute units beats the 256 x 256
+    ring's."""
     tile = lambda kind, M, N, K: dg.plan(kind, M, N, K)["tile_m"]
-    assert tile("i8", 8192, 8192, 8192) == 256      # 1024 ring tiles
-    assert tile("i8", 4096, 4096, 4096) == 256      # 256 ring tiles, one per unit
-    assert tile("i8", 6144, 6144, 6144) == 256      # 576 ring tiles against 2304 of 128^2
-    assert tile("i8", 3072, 3072, 3072) == 128      # 144 ring tiles against 576 of 128^2
-    assert tile("i8", 4096, 2048, 2048) == 128      # 128 ring tiles: half the units idle
-    assert tile("i8", 2048, 2048, 2048) == 128
-    assert tile("i8", 300, 272, 80) == 128
-    p = dg.plan("i8", 2048, 2048, 2048)
-    # three 16 KB A pair buffers and four 8 KB B steps: two workgroups a unit
-    assert p["lds_bytes"] == 81920 and p["lds_stages"] == 4 and p["tile_k"] == 64
-    assert p["grid_x"] * p["grid_y"] == 256 and p["outputs_per_thread"] == 64 and p["tile_bytes"] == 16384
-    for kind in ("e4m3", "e5m2"):
-        assert tile(kind, 2048, 2048, 2048) == 256 and dg.plan(kind, 2048, 2048, 2048)["lds_bytes"] == 163840
+    for kind in ("e4m3", "e5m2", "i8"):
+        assert tile(kind, 8192, 8192, 8192) == 256      # 1024 ring tiles
+        assert tile(kind, 4096, 4096, 4096) == 256      # 256 ring tiles, one per unit
+        assert tile(kind, 6144, 6144, 6144) == 256      # 576 ring tiles against 2304 of 128^2
+        assert tile(kind, 4096, 2048, 2048) == 128      # 128 ring tiles: half the units idle
+        assert tile(kind, 2560, 2560, 2560) == 128      # 100 ring tiles against 400 of 128^2
+        assert tile(kind, 2048, 2048, 2048) == 128
+        assert tile(kind, 300, 272, 80) == 128
+        p = dg.plan(kind, 2048, 2048, 2048)
+        # three 16 KB A pair buffers and four 8 KB B steps: two workgroups a unit
+        assert p["lds_bytes"] == 81920 and p["lds_stages"] == 4 and p["tile_k"] == 64
+        assert p["grid_x"] * p["grid_y"] == 256 and p["outputs_per_thread"] == 64 and p["tile_bytes"] == 16384
+    # 144 ring tiles against 576 of 128^2: INT8 takes the smaller tile, FP8
+    # (whose larger tile runs faster with units idle) the larger
+    assert tile("i8", 3072, 3072, 3072) == 128
+    assert tile("e4m3", 3072, 3072, 3072) == 256 and tile("e5m2", 3072, 3072, 3072) == 256
 
 
 def test_8bit_entry_points_validate_before_touching_a_device():

@@ -19,7 +19,7 @@ RING_KERNELS = [("mfma_f16.hip", "mfma_f16_pipe_kernel"), ("mfma_f16.hip", "mfma
                 ("mfma_f16.hip", "mfma_f16_pair128_kernel"),
                 ("mfma_f32.hip", "mfma_f32_ring_kernel"), ("mfma_f32.hip", "mfma_f32_small_ring_kernel"),
                 ("mfma_8bit.hip", "mfma_8bit_ring_kernel"), ("mfma_8bit.hip", "mfma_i8_pair_kernel"),
-                ("mfma_8bit.hip", "mfma_i8_pair128_kernel")]
+                ("mfma_8bit.hip", "mfma_i8_pair128_kernel"), ("mfma_8bit.hip", "mfma_fp8_pair128_kernel")]
 
 
 @pytest.fixture(scope="module", params=RING_KERNELS, ids=lambda v: v[1])
@@ -52,12 +52,12 @@ def test_every_layout_variant_is_generated(ring):
     # 16-bit: op(B) x (overwrite, accumulate) x two formats for each of a
     # k-contiguous A (pair kernel) and a k-strided A (pipe kernel); FP32:
     # op(A) x op(B) x (overwrite, accumulate); 8-bit: the row-major product in
-    # the two FP8 formats, and once for INT8 at each of its two tiles; the
+    # the two FP8 formats and once for INT8, at each of the two tiles; the
     # 64 x 64 ring once; the 16-bit 128 x 128 ring in both formats
     want = {"mfma_f16_pipe_kernel": 8, "mfma_f16_pair_kernel": 8, "mfma_f16_pair128_kernel": 2,
             "mfma_f32_ring_kernel": 8,
             "mfma_f32_small_ring_kernel": 1, "mfma_8bit_ring_kernel": 2, "mfma_i8_pair_kernel": 1,
-            "mfma_i8_pair128_kernel": 1}[kernel]
+            "mfma_i8_pair128_kernel": 1, "mfma_fp8_pair128_kernel": 2}[kernel]
     assert len(_instances(asm, kernel)) == want
 
 
@@ -89,7 +89,8 @@ def test_ring_kernel_spills_nothing(ring):
     # 256 AGPRs, over eight (the FP32 ring) 128, 128 x 128 over four 64; the
     # 64 x 64 tile holds few (not checked)
     want_agpr = {"mfma_f32_small_ring_kernel": None, "mfma_f32_ring_kernel": 128,
-                 "mfma_f16_pair128_kernel": 64, "mfma_i8_pair128_kernel": 64}.get(kernel, 256)
+                 "mfma_f16_pair128_kernel": 64, "mfma_i8_pair128_kernel": 64,
+                 "mfma_fp8_pair128_kernel": 64}.get(kernel, 256)
     for sym, body in _instances(asm, kernel):
         priv = re.search(rf"^\s*\.set\s+{re.escape(sym)}\.private_seg_size,\s*(\d+)", asm, flags=re.M)
         agpr = re.search(rf"^\s*\.set\s+{re.escape(sym)}\.num_agpr,\s*(\d+)", asm, flags=re.M)

@@ -85,10 +85,12 @@ CASES = [
     ("f32", 4000, 4092, [4, 16, 20, 32, 36, 48, 52, 68]),       # FP32 256^2 ring
     ("f32", 1000, 1000, [32, 64, 96, 128, 200, 384]),           # FP32 64^2 ring (32-deep stages)
     ("f32", 4000, 2044, [16, 100]),                             # FP32 128^2 two-stage kernel
-    ("e4m3", 520, 784, [16, 64, 80, 144, 320]),                 # 8-bit ring
+    ("e4m3", 520, 784, [16, 64, 80, 144, 320]),                 # 8-bit 128^2 rings
     ("e5m2", 520, 784, [16, 80, 208]),
-    ("i8", 520, 784, [16, 48, 64, 128, 192, 320]),             # INT8 128^2 ring
-    ("i8", 4000, 4016, [16, 48, 64, 128, 192, 320]),           # INT8 256^2 ring
+    ("i8", 520, 784, [16, 48, 64, 128, 192, 320]),
+    ("e4m3", 4000, 4016, [16, 64, 80, 144, 320]),               # 8-bit 256^2 rings
+    ("e5m2", 4000, 4016, [16, 80, 208]),
+    ("i8", 4000, 4016, [16, 48, 64, 128, 192, 320]),
     # tall, narrow: one and two column blocks hold a wavefront's B run in LDS;
     # three and four stream it through rings of 4 and 3 slots, where K gives
     # 0 to 8 slices a wavefront, so the prologue, the refills and the drain
