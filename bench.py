@@ -20,7 +20,8 @@ points (2MNK integer operations per second for INT8).
 
 Unless --no-all-workloads is given, every named workload (the BF16, FP8 and
 INT8 entry points included) is then timed on its own under "all_workloads",
-the convolution workloads under "conv_workloads", and every kernel variant
+every input format at 2048^3 under "mid_sizes", the convolution workloads
+under "conv_workloads", and every kernel variant
 (rung) at 1024^3 and 4096^3 FP32 and 8192^3 FP16 under "ladder" (a few
 seconds; --no-ladder skips it, --ladder adds it to any run); --conv-only
 times just the convolutions.
@@ -266,6 +267,7 @@ def main() -> int:
 
     if not args.no_all_workloads:
         out["all_workloads"] = all_workloads(dg, inputs, torch, dev, stream, dev_in, wl)
+        out["mid_sizes"] = mid_sizes(dg, inputs, torch, dev, stream)
         out["conv_workloads"] = conv_workloads(dg, inputs, torch, dev, stream)
 
     if not args.no_sustained:
@@ -386,6 +388,37 @@ def all_workloads(dg, inputs, torch, dev, stream, dev_in, wl):
                                   "frac_of_hbm_graph": round(ggbs / HBM_PEAK_GBS, 4),
                                   "graph_matches_eager": same})
     del flush
+    return res
+
+
+# mid-size products, where the tile choice sets how many compute units work:
+# every input format at 2048^3 (64 tiles of 256^2, 256 of 128^2)
+MID_SIZES = [(2048, 2048, 2048)]
+
+
+def mid_sizes(dg, inputs, torch, dev, stream):
+    """2MNK/t, fraction of the matrix peak and the planned tile of every
+    input format at the MID_SIZES shapes (uniform[-1, 1) inputs rounded to the
+    format, seed 3000), calls timed back to back."""
+    import numpy as np
+
+    res = {}
+    for M, N, K in MID_SIZES:
+        for kind in ("f32", "f16", "bf16", "e4m3", "e5m2", "i8"):
+            A, B = inputs.matrices(M, N, K, 3000, "uniform", kind)
+            a, b = to_device(torch, np, A, kind, dev), to_device(torch, np, B, kind, dev)
+            c = torch.empty((M, N), dtype=torch.int32 if kind == "i8" else torch.float32, device=dev)
+            f = entry_point(dg, kind)
+            est = _time_calls(lambda: f(a, b, c, stream), torch, stream, 3)
+            reps = max(3, min(200, int(50.0 / max(est, 1e-3))))
+            ms = _time_calls(lambda: f(a, b, c, stream), torch, stream, reps)
+            tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+            p = dg.plan(kind, M, N, K)
+            res[f"{kind}_{M}x{N}x{K}"] = {"ms": round(ms, 5), "tflops": round(tf, 3),
+                                          "frac_of_peak": round(tf / PEAK_TFLOPS[kind], 4),
+                                          "kernel": dg.variant_name(p["variant"]),
+                                          "tile": [p["tile_m"], p["tile_n"]]}
+            del a, b, c
     return res
 
 
