@@ -22,16 +22,21 @@ RING_KERNELS = [("mfma_f16.hip", "mfma_f16_pipe_kernel"), ("mfma_f16.hip", "mfma
                 ("mfma_8bit.hip", "mfma_i8_pair128_kernel"), ("mfma_8bit.hip", "mfma_fp8_pair128_kernel")]
 
 
+_ASM = {}   # source file -> its generated assembly (each source compiled once)
+
+
 @pytest.fixture(scope="module", params=RING_KERNELS, ids=lambda v: v[1])
 def ring(request, tmp_path_factory):
     if shutil.which("hipcc") is None and not os.path.exists("/opt/rocm/bin/hipcc"):
         pytest.skip("hipcc not available")
     src, kernel = request.param
-    out = tmp_path_factory.mktemp("isa") / (src + "." + kernel + ".s")
-    cmd = [hipbuild.hipcc(), *hipbuild.FLAGS, "-S", "--cuda-device-only",
-           os.path.join(hipbuild.CSRC, src), "-o", str(out)]
-    subprocess.run(cmd, check=True, capture_output=True, text=True)
-    return out.read_text(), kernel
+    if src not in _ASM:
+        out = tmp_path_factory.mktemp("isa") / (src + ".s")
+        cmd = [hipbuild.hipcc(), *hipbuild.FLAGS, "-S", "--cuda-device-only",
+               os.path.join(hipbuild.CSRC, src), "-o", str(out)]
+        subprocess.run(cmd, check=True, capture_output=True, text=True)
+        _ASM[src] = out.read_text()
+    return _ASM[src], kernel
 
 
 def _instances(text, name):
