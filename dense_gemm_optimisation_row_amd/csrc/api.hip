@@ -223,10 +223,11 @@ int plan_f32(int variant, int M, int N, int K, const void *A, const void *B, con
             p->lds_stages = dgor::kF32DirectStages;
             p->lds_bytes = dgor::kF32DirectLdsBytes;
         } else if (dgor::f32_small_ring_applies(c.bm, c.bn, N, K, p->vector_a, p->vector_b)) {
-            p->threads = 128 * dgor::kF32SmallWavesN;
+            const int groups = dgor::f32_small_ring_split(M, N, K) ? 2 : 1;
+            p->threads = 128 * dgor::kF32SmallWavesN * groups;
             p->tile_k = dgor::kF32SmallDepth;
             p->lds_stages = dgor::kF32SmallStages;
-            p->lds_bytes = dgor::kF32SmallLdsBytes;
+            p->lds_bytes = dgor::kF32SmallLdsBytes * groups;
         } else {
             p->lds_stages = 2;
             p->lds_bytes = dgor::mfma_f32_lds_bytes(c);

@@ -201,6 +201,15 @@ inline bool f32_small_ring_applies(int tile_m, int tile_n, int N, int K, bool ve
     return tile_m == 64 && tile_n == 64 && vec_a && vec_b && K < (1 << 22) &&
            (long long)(K + kF32SmallDepth) * N < (1LL << 29);
 }
+// With at most one 64 x 64 tile per compute unit and K of at least
+// kF32SmallSplitMinK, the ring's workgroup is two groups of eight wavefronts,
+// each over half of the k-stages with a ring of its own (128 KB, 1024
+// threads); their sums are added in LDS in a fixed order.
+constexpr int kF32SmallSplitMinK = 512;
+inline bool f32_small_ring_split(int M, int N, int K)
+{
+    return (long long)((M + 63) / 64) * ((N + 63) / 64) <= 256 && K >= kF32SmallSplitMinK;
+}
 
 // Tall, narrow FP32 problems (1 <= N <= 64, 1 <= K <= kF32SkinnyMaxK, A and
 // B 4-byte aligned): workgroups of 16 rows and 8 wavefronts, nb MFMA blocks

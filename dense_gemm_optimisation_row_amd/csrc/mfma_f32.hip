@@ -626,13 +626,20 @@ hipError_t launch_ring32_t(const RingArgs &a, hipStream_t s)
 // Each direct load costs its wavefront some issue time in which the matrix
 // core has nothing else to run; with eight wavefronts (two per SIMD, WN = 4)
 // the other wavefront's MFMAs fill it, 9% faster than four at 1024^3.
+// KS = 2 (shapes with at most one tile per compute unit, whose second
+// workgroup slot would stay empty): sixteen wavefronts, two groups of eight,
+// group g taking the g-th half of the k-stages through a ring of its own
+// (128 KB in all); both groups run the same number of stages (the second's
+// last one past K loads zeros), so they meet at the same barriers, and at
+// the end group 1 hands its sums to group 0 through LDS, which adds them in
+// that fixed order and stores C.
 namespace f32small {
 __host__ __device__ constexpr int fa(int r, int U) { return (r * U / 16) & (U - 1); }
 __host__ __device__ constexpr int fb(int k) { return 4 * ((k >> 2) & 3); }
 }  // namespace f32small
 
-template <int BK, int NBUF, int WN>
-__global__ __launch_bounds__(128 * WN) void mfma_f32_small_ring_kernel(int M, int N, int K,
+template <int BK, int NBUF, int WN, int KS>
+__global__ __launch_bounds__(128 * WN * KS) void mfma_f32_small_ring_kernel(int M, int N, int K,
                                                                   const float *__restrict__ A,
                                                                   const float *__restrict__ B,
                                                                   float *__restrict__ C, int tiles_m,
@@ -649,14 +656,21 @@ __global__ __launch_bounds__(128 * WN) void mfma_f32_small_ring_kernel(int M, in
     static_assert(U == 8 || U == 16, "A rows of 8 or 16 units");
     static_assert((NBUF & (NBUF - 1)) == 0 && NBUF >= 4, "ring of a power of two, at least 4");
     static_assert(READS <= MFMAS, "one read after each of the first MFMAs");
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[NBUF * STAGE];
-    const uint32_t lds0 = lds_address(lds);
+    static_assert(KS == 1 || KS == 2, "one or two groups over k");
+    constexpr int RING = NBUF * STAGE;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[KS * RING];
+    const int wave_all = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int grp = wave_all / W, wave = wave_all % W;
+    uint8_t *const ring = lds + grp * RING;
+    const uint32_t lds0 = lds_address(lds) + (uint32_t)(grp * RING);
+    const int steps_all = (K + BK - 1) / BK;
+    const int steps = (steps_all + KS - 1) / KS;   // stages of each group
+    const int kbase = grp * steps * BK;            // the group's first k
 
     int tm, tn;
     dgor_tile_of_block(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int wr = (wave / WN) * 32, wc = (wave % WN) * 16 * BJ;
     constexpr uint32_t OOB = 0x80000000u;
 
@@ -686,15 +700,16 @@ __global__ __launch_bounds__(128 * WN) void mfma_f32_small_ring_kernel(int M, in
         b_k[i] = k;
         b_ok[i] = n0 + 4 * u < N;
     }
-    auto load = [&](int st, int x) {   // load x (0 .. LPS - 1) of stage st
-        const int k0 = st * BK;
+    auto load = [&](int st, int x) {   // load x (0 .. LPS - 1) of the group's stage st
+        const int k0 = kbase + st * BK;
+        const bool in = st < steps;
         const uint32_t buf = lds0 + (uint32_t)((st & (NBUF - 1)) * STAGE);
         if (x < LA) {
-            const bool ok = a_ok[x] && k0 + a_k[x] < K;
+            const bool ok = in && a_ok[x] && k0 + a_k[x] < K;
             load_to_lds(ra, buf + (uint32_t)((wave * LA + x) * 1024), ok ? a_row[x] + (uint32_t)k0 * 4u : OOB);
         } else {
             const int i = x - LA;
-            const bool ok = b_ok[i] && k0 + b_k[i] < K;
+            const bool ok = in && b_ok[i] && k0 + b_k[i] < K;
             load_to_lds(rb, buf + (uint32_t)(A_BYTES + (wave * LB + i) * 1024),
                         ok ? b_row[i] + (uint32_t)k0 * (uint32_t)N * 4u : OOB);
         }
@@ -719,7 +734,7 @@ __global__ __launch_bounds__(128 * WN) void mfma_f32_small_ring_kernel(int M, in
         b_lane[b] = (uint32_t)(A_BYTES + (4 * h) * 256 + (((col >> 2) ^ (4 * h)) * 16) + (col & 3) * 4);
     }
     auto fread = [&](int st, int rd, floatx4 *fa_, floatx4 *fb_) {
-        const uint8_t *buf = lds + (st & (NBUF - 1)) * STAGE;
+        const uint8_t *buf = ring + (st & (NBUF - 1)) * STAGE;
         const int q = rd / RPS, x = rd % RPS;
         if (x < 2) {
             fa_[2 * q + x] = *reinterpret_cast<const floatx4 *>(buf + a_off[2 * q + x]);
@@ -743,7 +758,6 @@ __global__ __launch_bounds__(128 * WN) void mfma_f32_small_ring_kernel(int M, in
     // later stages may fly) and the workgroup meets at the barrier, so every
     // wavefront's part of stage t + 1 is in LDS and nobody still reads the
     // buffer the new loads refill (stage t - 1's, read during stage t - 2).
-    const int steps = (K + BK - 1) / BK;
     auto stage = [&](int t, floatx4 *ca, floatx4 *cb, floatx4 *na, floatx4 *nb) {
         __builtin_amdgcn_s_waitcnt(wait_vmcnt((NBUF - 3) * LPS));
         __builtin_amdgcn_s_barrier();
@@ -780,6 +794,29 @@ __global__ __launch_bounds__(128 * WN) void mfma_f32_small_ring_kernel(int M, in
     }
     // no load may still be writing this workgroup's LDS when it ends
     __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+    if constexpr (KS == 2) {
+        // group 1 hands its sums to group 0 through its own ring: once every
+        // wavefront's reads have returned, block (i, j) of wavefront w at
+        // 16 ((((i BJ + j) W + w) 64) + lane); group 0 adds them to its own
+        floatx4 *part = reinterpret_cast<floatx4 *>(lds + RING);
+        __builtin_amdgcn_s_waitcnt(wait_vmcnt_lgkm0(0));
+        __builtin_amdgcn_s_barrier();
+        if (grp == 1) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < BJ; ++j)
+                    part[((i * BJ + j) * W + wave) * 64 + lane] = acc[i][j];
+        }
+        __builtin_amdgcn_s_barrier();
+        if (grp == 1)
+            return;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < BJ; ++j)
+                acc[i][j] += part[((i * BJ + j) * W + wave) * 64 + lane];
+    }
 
     const __amdgpu_buffer_rsrc_t rc =
         make_rsrc(C + (size_t)m0 * N + n0, ((long long)(M - m0 - 1) * N + N - n0) * 4);
@@ -1264,9 +1301,15 @@ hipError_t launch_mfma_f32(const Problem &p, const gemm_plan &plan, hipStream_t 
     }
     if (plan.tile_m == 64 && plan.tile_n == 64) {
         if (f32_small_ring_applies(64, 64, p.N, p.K, p.vec_a, p.vec_b)) {
-            hipLaunchKernelGGL((mfma_f32_small_ring_kernel<kF32SmallDepth, kF32SmallStages, kF32SmallWavesN>),
-                               dim3(plan.grid_x * plan.grid_y), dim3(128 * kF32SmallWavesN), 0, s, p.M, p.N, p.K,
-                               (const float *)p.A, (const float *)p.B, p.C, plan.grid_y, plan.grid_x, 8);
+            const dim3 grid(plan.grid_x * plan.grid_y);
+            if (plan.threads == 256 * kF32SmallWavesN)   // two groups over k
+                hipLaunchKernelGGL((mfma_f32_small_ring_kernel<kF32SmallDepth, kF32SmallStages, kF32SmallWavesN, 2>),
+                                   grid, dim3(256 * kF32SmallWavesN), 0, s, p.M, p.N, p.K, (const float *)p.A,
+                                   (const float *)p.B, p.C, plan.grid_y, plan.grid_x, 8);
+            else
+                hipLaunchKernelGGL((mfma_f32_small_ring_kernel<kF32SmallDepth, kF32SmallStages, kF32SmallWavesN, 1>),
+                                   grid, dim3(128 * kF32SmallWavesN), 0, s, p.M, p.N, p.K, (const float *)p.A,
+                                   (const float *)p.B, p.C, plan.grid_y, plan.grid_x, 8);
             return hipGetLastError();
         }
         return launch_cfg<64, 64, 16, 2, 2>(p, plan, s);

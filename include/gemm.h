@@ -177,7 +177,7 @@ typedef struct {
     int threads;        /* threads per workgroup */
     int grid_x;         /* workgroups along N */
     int grid_y;         /* workgroups along M */
-    int k_stages;       /* ceil(K / tile_k): k-loop trips of one workgroup */
+    int k_stages;       /* ceil(K / tile_k): k-stages of one workgroup */
     int lds_stages;     /* LDS k-stages in flight (1, 2, or a ring of 4) */
     int lds_bytes;      /* LDS per workgroup, padding included */
     int tile_bytes;     /* bytes of one unpadded A tile plus one B tile */

@@ -198,6 +198,18 @@ def test_direct_load_tile_follows_the_spread_of_tiles_over_compute_units():
     assert tile(True, 4096, 4096, 4095) == 128 and dg.plan(True, 4096, 4096, 4095)["vector_a"] == 0
 
 
+def test_f32_64_ring_splits_k_over_two_groups_with_one_tile_per_unit():
+    """The 64 x 64 ring's workgroup becomes two groups of eight wavefronts
+    over halves of the k-stages (1024 threads, two 64 KB rings) when the shape
+    has at most 256 of its tiles and K >= 512."""
+    for M, N, K in ((1024, 1024, 1024), (1000, 1000, 1000), (1024, 1024, 4096), (512, 512, 512), (40, 1000, 600)):
+        p = dg.plan(False, M, N, K)
+        assert (p["tile_m"], p["threads"], p["lds_bytes"], p["k_stages"]) == (64, 1024, 131072, -(-K // 32))
+    for M, N, K in ((2048, 2048, 2048), (1024, 1024, 256), (256, 256, 256), (1536, 1536, 1536)):
+        p = dg.plan(False, M, N, K)
+        assert (p["tile_m"], p["threads"], p["lds_bytes"]) == (64, 512, 65536)
+
+
 def test_vector_path_needs_divisible_rows_and_16_byte_alignment():
     p = dg.plan(False, 64, 64, 64)
     assert p["vector_a"] == p["vector_b"] == 1

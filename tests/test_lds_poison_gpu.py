@@ -84,6 +84,7 @@ CASES = [
     ("bf16", 1000, 1032, [8, 40, 136]),
     ("f32", 4000, 4092, [4, 16, 20, 32, 36, 48, 52, 68]),       # FP32 256^2 ring
     ("f32", 1000, 1000, [32, 64, 96, 128, 200, 384]),           # FP32 64^2 ring (32-deep stages)
+    ("f32", 1000, 1000, [512, 528, 1040]),                      # the same, two groups over k
     ("f32", 4000, 2044, [16, 100]),                             # FP32 128^2 two-stage kernel
     ("e4m3", 520, 784, [16, 64, 80, 144, 320]),                 # 8-bit 128^2 rings
     ("e5m2", 520, 784, [16, 80, 208]),

@@ -204,6 +204,25 @@ def test_f32_mid_tile_stage_counts(shape):
     assert_within(run(False, dg.AUTO, A, B), oracle.gemm_f32(A, B), tol_f32(K), f"floats {shape}")
 
 
+# With at most 256 such tiles and K >= 512 the 64 x 64 ring's workgroup is
+# two groups of eight wavefronts, each over half of the k-stages: these K
+# give 16 + 16, 17 + 17 (the second group's last stage past K), 32 + 32 and
+# 33 + 33 stages, and 65 + 65 with a k tail; ragged M and N, one row of
+# tiles, a single row.
+@pytest.mark.parametrize("shape", [(1000, 1000, K) for K in (512, 528, 1000, 1040, 2084)]
+                         + [(40, 1000, 600), (1, 1024, 512), (1024, 1024, 1024)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_f32_mid_tile_split_over_k(shape):
+    M, N, K = shape
+    p = dg.plan(False, M, N, K)
+    assert (p["tile_m"], p["tile_n"], p["threads"], p["lds_bytes"]) == (64, 64, 1024, 131072)
+    say("f32 mid tile, two groups over k", shape)
+    A, B = ints(M, N, K, 91 + K)
+    assert_bits_equal(run(False, dg.AUTO, A, B), oracle.gemm_f32(A, B), f"ints {shape}")
+    A, B = floats(M, N, K, 92 + K)
+    assert_within(run(False, dg.AUTO, A, B), oracle.gemm_f32(A, B), tol_f32(K), f"floats {shape}")
+
+
 # Tall, narrow FP32 problems (N <= 64, K <= 1024) take a kernel of 16-row
 # workgroups that load A and B straight into registers and split K eight
 # ways: N across 1..4 column blocks (ragged, and N % 16 == 1 with its last
