@@ -219,11 +219,12 @@ int plan_f32(int variant, int M, int N, int K, const void *A, const void *B, con
         p->tile_n = c.bn;
         p->tile_k = c.bk;
         p->threads = 64 * c.waves_m * c.waves_n;
+        int groups = 1;   // groups of wavefronts over k in one workgroup
         if (dgor::direct_lds_applies(c.bm, dgor::kF32Configs[0].bm, p->vector_a, p->vector_b, N, K)) {
             p->lds_stages = dgor::kF32DirectStages;
             p->lds_bytes = dgor::kF32DirectLdsBytes;
         } else if (dgor::f32_small_ring_applies(c.bm, c.bn, N, K, p->vector_a, p->vector_b)) {
-            const int groups = dgor::f32_small_ring_split(M, N, K) ? 2 : 1;
+            groups = dgor::f32_small_ring_split(M, N, K) ? 2 : 1;
             p->threads = 128 * dgor::kF32SmallWavesN * groups;
             p->tile_k = dgor::kF32SmallDepth;
             p->lds_stages = dgor::kF32SmallStages;
@@ -233,7 +234,7 @@ int plan_f32(int variant, int M, int N, int K, const void *A, const void *B, con
             p->lds_bytes = dgor::mfma_f32_lds_bytes(c);
         }
         p->tile_bytes = (c.bm * p->tile_k + p->tile_k * c.bn) * 4;
-        p->outputs_per_thread = c.bm * c.bn / p->threads;
+        p->outputs_per_thread = c.bm * c.bn * groups / p->threads;
         p->vector_c = 0;
         break;
     }
@@ -286,18 +287,21 @@ int plan_f16(int variant, int M, int N, int K, const void *A, const void *B, con
         p->tile_n = c.bn;
         p->tile_k = c.bk;
         p->threads = 64 * c.waves_m * c.waves_n;
+        int groups = 1;   // groups of wavefronts over k in one workgroup
         if (dgor::direct_lds_applies(c.bm, dgor::kF16Configs[0].bm, p->vector_a, p->vector_b, N, K)) {
             p->lds_stages = dgor::kF16RingStages;
             p->lds_bytes = dgor::kF16RingLdsBytes;
         } else if (c.bm == 128 && dgor::f16_ring128_applies(p->vector_a, p->vector_b, N, K)) {
+            groups = dgor::f16_ring128_split(M, N) ? 2 : 1;
+            p->threads *= groups;
             p->lds_stages = dgor::kF16RingStages;
-            p->lds_bytes = dgor::kF16Ring128LdsBytes;
+            p->lds_bytes = dgor::kF16Ring128LdsBytes * groups;
         } else {
             p->lds_stages = 2;
             p->lds_bytes = dgor::mfma_f16_lds_bytes(c);
         }
         p->tile_bytes = (c.bm * c.bk + c.bk * c.bn) * 2;
-        p->outputs_per_thread = c.bm * c.bn / p->threads;
+        p->outputs_per_thread = c.bm * c.bn * groups / p->threads;
     }
     finish(p, M, N, K);
     return GEMM_OK;
@@ -395,13 +399,14 @@ int plan_8(int fmt, int variant, int M, int N, int K, const void *A, const void 
         p->vector_a = p->vector_b = 0;
     } else {
         const int t = ring8_tile(fmt, M, N);
+        const int groups = t == dgor::kRing8SmallTile && dgor::ring8_small_split(M, N) ? 2 : 1;
         p->tile_m = p->tile_n = t;
         p->tile_k = dgor::kRing8Depth;
-        p->threads = 256;
+        p->threads = 256 * groups;
         p->lds_stages = dgor::kRing8Stages;
-        p->lds_bytes = t == dgor::kRing8Tile ? dgor::kRing8LdsBytes : dgor::kRing8SmallLdsBytes;
+        p->lds_bytes = t == dgor::kRing8Tile ? dgor::kRing8LdsBytes : dgor::kRing8SmallLdsBytes * groups;
         p->tile_bytes = 2 * t * dgor::kRing8Depth;
-        p->outputs_per_thread = t * t / 256;
+        p->outputs_per_thread = t * t * groups / p->threads;
     }
     finish(p, M, N, K);
     return GEMM_OK;
@@ -428,7 +433,7 @@ int run8(int fmt, int variant, int M, int N, int K, const void *A, const void *B
     else if (plan.variant == GEMM_R0_NAIVE)
         err = dgor::launch_naive_8bit(p, fmt, s);
     else
-        err = dgor::launch_ring8(dgor::ring_args_nn(p, plan), fmt, plan.tile_m, s);
+        err = dgor::launch_ring8(dgor::ring_args_nn(p, plan), fmt, plan.tile_m, plan.threads / 256, s);
     return err == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
 }
 

@@ -82,8 +82,15 @@ constexpr int kI8MaxK = 131072;   // |sum| <= 128 * 128 * K must fit int32
 constexpr int kRing8SmallTile = 128;
 constexpr int kRing8SmallLdsBytes =
     3 * kRing8SmallTile * 2 * kRing8Depth + kRing8Stages * kRing8Depth * kRing8SmallTile;
-// tile: kRing8Tile or kRing8SmallTile.
-hipError_t launch_ring8(const RingArgs &args, int fmt, int tile, hipStream_t stream);
+// With at most one 128 x 128 tile per compute unit the ring runs two groups
+// of four wavefronts over halves of the k-steps (512 threads, two 80 KB
+// rings), their sums added in LDS.
+inline bool ring8_small_split(int M, int N)
+{
+    return (long long)((M + 127) / 128) * ((N + 127) / 128) <= 256;
+}
+// tile: kRing8Tile or kRing8SmallTile; groups: 1, or 2 with kRing8SmallTile.
+hipError_t launch_ring8(const RingArgs &args, int fmt, int tile, int groups, hipStream_t stream);
 
 // Convolution through im2col: shape (P, Q derived), and the passes around the
 // GEMM (conv.hip).  elem_bytes is 4 (binary32) or 2 (16-bit inputs).
@@ -185,6 +192,13 @@ constexpr int kF16Ring128LdsBytes = 3 * 128 * 64 * 2 + kF16RingStages * 32 * 128
 inline bool f16_ring128_applies(bool vec_a, bool vec_b, int N, int K)
 {
     return vec_a && vec_b && K < (1 << 22) && N < (1 << 22);
+}
+// With at most one of its tiles per compute unit the 128 x 128 ring runs two
+// groups of four wavefronts over halves of the k-stages (512 threads, two
+// 80 KB rings), their sums added in LDS in a fixed order.
+inline bool f16_ring128_split(int M, int N)
+{
+    return (long long)((M + 127) / 128) * ((N + 127) / 128) <= 256;
 }
 
 // FP32 problems that take the 64 x 64 tile with both operands in 128-bit

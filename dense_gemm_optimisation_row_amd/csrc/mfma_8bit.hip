@@ -69,6 +69,7 @@ namespace {
 
 typedef int intx8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef int intx2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) intx2 lds_intx2;
 
@@ -638,7 +639,8 @@ __global__ __launch_bounds__(256) void mfma_i8_pair_kernel(RingArgs args)
 // col) of a round sits at row 256 + 16 ((col / 4) ^ 4 ((row / 4) % 4)) +
 // 4 (col % 4), so both the 4-byte writes (lane (g, s) of block j at unit
 // 4 (j ^ g) + s / 4) and the 16-byte reads along the rows are free of bank
-// conflicts.  Arguments as in store_c_staged_i32.
+// conflicts.  Arguments as in store_c_staged_i32, except that acc holds the
+// sums already read out of the accumulator registers.
 __device__ __forceinline__ void store_c_staged_w64_i32(const intx4 (&acc)[4][4], uint8_t *lds, int wave, int lane,
                                                        int *Cw, int ldc, int rows_left, int cols_left, bool vec)
 {
@@ -656,7 +658,7 @@ __device__ __forceinline__ void store_c_staged_w64_i32(const intx4 (&acc)[4][4],
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     *reinterpret_cast<int *>(w + (16 * ii + 4 * g + r) * 256 + (4 * (j ^ g) + (s16 >> 2)) * 16 +
-                                             (s16 & 3) * 4) = acc_read_i32(acc[2 * q + ii][j][r]);
+                                             (s16 & 3) * 4) = acc[2 * q + ii][j][r];
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
             const int row = (lane >> 4) + 4 * t, c = lane & 15;
@@ -697,6 +699,12 @@ __device__ __forceinline__ void store_c_staged_w64_i32(const intx4 (&acc)[4][4],
 //   wc + 16 j + s16, two transposing reads 8 k rows apart).
 //   Pipeline, waits and the fragment order as in the pair ring, with 16
 //   MFMAs, 8 fragment reads and 4 loads a wavefront and step.
+//   KS = 2 (at most one tile per compute unit): eight wavefronts in two
+//   groups of four, each over half of the k-steps (A, B and K shifted to the
+//   group's range) through its own 80 KB ring; both groups run the same
+//   number of steps and meet at the same barriers, and group 1 hands its sums
+//   to group 0 through its ring at the end (the FP8 kernel below does the
+//   same).
 namespace ring8_128 {
 constexpr int BK = 64;
 constexpr int A_PAIR_BYTES = 128 * 2 * BK;           // 16 KB
@@ -706,21 +714,29 @@ constexpr int B_REGION = A_PAIRS * A_PAIR_BYTES;     // 48 KB
 constexpr int LDS_BYTES = B_REGION + 4 * B_BYTES;    // 80 KB
 }  // namespace ring8_128
 
-__global__ __launch_bounds__(256, 2) void mfma_i8_pair128_kernel(RingArgs args)
+template <int KS>
+__global__ __launch_bounds__(256 * KS, 2 / KS) void mfma_i8_pair128_kernel(RingArgs args)
 {
     using namespace ring8_128;
     static_assert(4 * 8192 <= LDS_BYTES, "the epilogue stages through the ring's LDS");
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds_all[KS * LDS_BYTES];
+    const int wave_all = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int grp = wave_all >> 2;
+    uint8_t *const lds = lds_all + grp * LDS_BYTES;
     const uint32_t ring = lds_address(lds);
-    const int M = args.M, N = args.N, K = args.K, lda = args.lda, ldb = args.ldb;
-    const uint8_t *__restrict__ A = (const uint8_t *)args.A;
-    const uint8_t *__restrict__ B = (const uint8_t *)args.B;
+    const int M = args.M, N = args.N, lda = args.lda, ldb = args.ldb;
+    // the group's k range: A, B and K shifted to it
+    const int steps = ((args.K + BK - 1) / BK + KS - 1) / KS;
+    const int kbase = grp * steps * BK;
+    const int K = args.K < kbase + steps * BK ? args.K - kbase : steps * BK;
+    const uint8_t *__restrict__ A = (const uint8_t *)args.A + kbase;
+    const uint8_t *__restrict__ B = (const uint8_t *)args.B + (size_t)kbase * ldb;
 
     int tm, tn;
     dgor_tile_of_block((int)blockIdx.x, args.tiles_m, args.tiles_n, args.group_m, tm, tn);
     const int m0 = tm * 128, n0 = tn * 128;
     const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int wave = wave_all & 3;
     const int wr = (wave >> 1) * 64, wc = (wave & 1) * 64;
     constexpr uint32_t OOB = 0x80000000u;
 
@@ -871,7 +887,6 @@ __global__ __launch_bounds__(256, 2) void mfma_i8_pair128_kernel(RingArgs args)
             fread(R0, r, fa0, fb0);
     }
 
-    const int steps = (K + BK - 1) / BK;
     uint32_t pa = 0;
     for (int s = 0; s < steps; s += 2) {
         const uint32_t pa1 = next_pair(pa), pa2 = next_pair(pa1);
@@ -886,11 +901,38 @@ __global__ __launch_bounds__(256, 2) void mfma_i8_pair128_kernel(RingArgs args)
     __builtin_amdgcn_s_waitcnt(wait_vmcnt_lgkm0(0));
     __builtin_amdgcn_s_barrier();
     dgor_acc_hazard_wait();
+    intx4 tot[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                tot[i][j][r] = acc_read_i32(acc[i][j][r]);
+    if constexpr (KS == 2) {
+        // group 1's sums to group 0 through group 1's ring
+        intx4 *part = reinterpret_cast<intx4 *>(lds_all + LDS_BYTES);
+        if (grp == 1) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    part[((i * 4 + j) * 4 + wave) * 64 + lane] = tot[i][j];
+        }
+        __builtin_amdgcn_s_barrier();
+        if (grp == 1)
+            return;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                tot[i][j] += part[((i * 4 + j) * 4 + wave) * 64 + lane];
+    }
     {
         const int ldc = args.ldc;
         int *Cw = reinterpret_cast<int *>(args.C) + (size_t)(m0 + wr) * ldc + n0 + wc;
         const bool vec = ((uintptr_t)Cw & 15) == 0 && (ldc & 3) == 0;
-        store_c_staged_w64_i32(acc, lds, wave, lane, Cw, ldc, M - m0 - wr, N - n0 - wc, vec);
+        store_c_staged_w64_i32(tot, lds, wave, lane, Cw, ldc, M - m0 - wr, N - n0 - wc, vec);
     }
 }
 
@@ -900,8 +942,9 @@ __global__ __launch_bounds__(256, 2) void mfma_i8_pair128_kernel(RingArgs args)
 // row 256 + 16 ((col / 4) ^ 8 ((row / 4) % 2)) + 4 (col % 4), so the 4-byte
 // writes (lanes 0..31 and 32..63 take rows 4 apart, on the two halves of the
 // banks) and the 16-byte reads along the rows are free of bank conflicts.
-// Cw: the block's first element; rows_left / cols_left: its rows and columns
-// inside C; vec: Cw 16-byte aligned and ldc a multiple of 4.
+// acc: the sums, read out of the accumulator registers; Cw: the block's first
+// element; rows_left / cols_left: its rows and columns inside C; vec: Cw
+// 16-byte aligned and ldc a multiple of 4.
 __device__ __forceinline__ void store_c_staged_w64_32(const floatx16 (&acc)[2][2], uint8_t *lds, int wave, int lane,
                                                       float *Cw, int ldc, int rows_left, int cols_left, bool vec)
 {
@@ -919,7 +962,7 @@ __device__ __forceinline__ void store_c_staged_w64_32(const floatx16 (&acc)[2][2
             for (int e = 0; e < 16; ++e) {
                 const int row = 8 * (e >> 2) + 4 * g + (e & 3), col = 32 * j + r32;
                 *reinterpret_cast<float *>(w + row * 256 + 16 * ((col >> 2) ^ (8 * g)) + 4 * (col & 3)) =
-                    dgor_acc_read(acc[i][j][e]);
+                    acc[i][j][e];
             }
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
@@ -950,22 +993,29 @@ __device__ __forceinline__ void store_c_staged_w64_32(const floatx16 (&acc)[2][2
 // apart) puts the 32 lanes' 8-byte pieces on 32 distinct bank pairs.  Each
 // of the 4 MFMAs of a step is followed by three of the next step's 12
 // fragment reads and one of its 4 loads.
-template <class Op>
-__global__ __launch_bounds__(256, 2) void mfma_fp8_pair128_kernel(RingArgs args)
+template <class Op, int KS>
+__global__ __launch_bounds__(256 * KS, 2 / KS) void mfma_fp8_pair128_kernel(RingArgs args)
 {
     using namespace ring8_128;
     static_assert(4 * 8192 <= LDS_BYTES, "the epilogue stages through the ring's LDS");
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds_all[KS * LDS_BYTES];
+    const int wave_all = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int grp = wave_all >> 2;
+    uint8_t *const lds = lds_all + grp * LDS_BYTES;
     const uint32_t ring = lds_address(lds);
-    const int M = args.M, N = args.N, K = args.K, lda = args.lda, ldb = args.ldb;
-    const uint8_t *__restrict__ A = (const uint8_t *)args.A;
-    const uint8_t *__restrict__ B = (const uint8_t *)args.B;
+    const int M = args.M, N = args.N, lda = args.lda, ldb = args.ldb;
+    // the group's k range: A, B and K shifted to it
+    const int steps = ((args.K + BK - 1) / BK + KS - 1) / KS;
+    const int kbase = grp * steps * BK;
+    const int K = args.K < kbase + steps * BK ? args.K - kbase : steps * BK;
+    const uint8_t *__restrict__ A = (const uint8_t *)args.A + kbase;
+    const uint8_t *__restrict__ B = (const uint8_t *)args.B + (size_t)kbase * ldb;
 
     int tm, tn;
     dgor_tile_of_block((int)blockIdx.x, args.tiles_m, args.tiles_n, args.group_m, tm, tn);
     const int m0 = tm * 128, n0 = tn * 128;
     const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int wave = wave_all & 3;
     const int wr = (wave >> 1) * 64, wc = (wave & 1) * 64;
     constexpr uint32_t OOB = 0x80000000u;
 
@@ -1129,7 +1179,6 @@ __global__ __launch_bounds__(256, 2) void mfma_fp8_pair128_kernel(RingArgs args)
             fread(R0, r, fa0, fb0);
     }
 
-    const int steps = (K + BK - 1) / BK;
     uint32_t pa = 0;
     for (int s = 0; s < steps; s += 2) {
         const uint32_t pa1 = next_pair(pa), pa2 = next_pair(pa1);
@@ -1144,19 +1193,55 @@ __global__ __launch_bounds__(256, 2) void mfma_fp8_pair128_kernel(RingArgs args)
     __builtin_amdgcn_s_waitcnt(wait_vmcnt_lgkm0(0));
     __builtin_amdgcn_s_barrier();
     dgor_acc_hazard_wait();
+    floatx16 tot[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                tot[i][j][e] = dgor_acc_read(acc[i][j][e]);
+    if constexpr (KS == 2) {
+        // group 1's sums to group 0 through group 1's ring, 16 bytes a lane
+        // per piece; group 0 adds them in that order
+        floatx4 *part = reinterpret_cast<floatx4 *>(lds_all + LDS_BYTES);
+        if (grp == 1) {
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    part[((b * 4 + c) * 4 + wave) * 64 + lane] =
+                        floatx4{tot[b >> 1][b & 1][4 * c], tot[b >> 1][b & 1][4 * c + 1],
+                                tot[b >> 1][b & 1][4 * c + 2], tot[b >> 1][b & 1][4 * c + 3]};
+        }
+        __builtin_amdgcn_s_barrier();
+        if (grp == 1)
+            return;
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const floatx4 v = part[((b * 4 + c) * 4 + wave) * 64 + lane];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    tot[b >> 1][b & 1][4 * c + e] += v[e];
+            }
+    }
     {
         const int ldc = args.ldc;
         float *Cw = args.C + (size_t)(m0 + wr) * ldc + n0 + wc;
         const bool vec = ((uintptr_t)Cw & 15) == 0 && (ldc & 3) == 0;
-        store_c_staged_w64_32(acc, lds, wave, lane, Cw, ldc, M - m0 - wr, N - n0 - wc, vec);
+        store_c_staged_w64_32(tot, lds, wave, lane, Cw, ldc, M - m0 - wr, N - n0 - wc, vec);
     }
 }
 
 template <int FMT>
-hipError_t launch_fp8(const RingArgs &a, int tile, hipStream_t s)
+hipError_t launch_fp8(const RingArgs &a, int tile, int groups, hipStream_t s)
 {
-    if (tile == kRing8SmallTile)
-        hipLaunchKernelGGL(mfma_fp8_pair128_kernel<OpFp8<FMT>>, dim3(a.tiles_m * a.tiles_n), dim3(256), 0, s, a);
+    if (tile == kRing8SmallTile && groups == 2)
+        hipLaunchKernelGGL((mfma_fp8_pair128_kernel<OpFp8<FMT>, 2>), dim3(a.tiles_m * a.tiles_n), dim3(512), 0, s, a);
+    else if (tile == kRing8SmallTile)
+        hipLaunchKernelGGL((mfma_fp8_pair128_kernel<OpFp8<FMT>, 1>), dim3(a.tiles_m * a.tiles_n), dim3(256), 0, s, a);
     else
         hipLaunchKernelGGL(mfma_8bit_ring_kernel<OpFp8<FMT>>, dim3(a.tiles_m * a.tiles_n), dim3(256), 0, s, a);
     return hipGetLastError();
@@ -1164,20 +1249,23 @@ hipError_t launch_fp8(const RingArgs &a, int tile, hipStream_t s)
 
 }  // namespace
 
-hipError_t launch_ring8(const RingArgs &a, int fmt, int tile, hipStream_t s)
+hipError_t launch_ring8(const RingArgs &a, int fmt, int tile, int groups, hipStream_t s)
 {
     if (a.accumulate || a.trans_a || a.trans_b || a.splits > 1 || a.alpha != 1.f)
         return hipErrorInvalidValue;
-    if (tile != kRing8Tile && tile != kRing8SmallTile)
+    if ((tile != kRing8Tile && tile != kRing8SmallTile) || groups < 1 || groups > 2 ||
+        (groups == 2 && tile != kRing8SmallTile))
         return hipErrorInvalidValue;
     switch (fmt) {
     case kFmtE4M3:
-        return launch_fp8<0>(a, tile, s);
+        return launch_fp8<0>(a, tile, groups, s);
     case kFmtE5M2:
-        return launch_fp8<1>(a, tile, s);
+        return launch_fp8<1>(a, tile, groups, s);
     case kFmtI8:
-        if (tile == kRing8SmallTile)
-            hipLaunchKernelGGL(mfma_i8_pair128_kernel, dim3(a.tiles_m * a.tiles_n), dim3(256), 0, s, a);
+        if (tile == kRing8SmallTile && groups == 2)
+            hipLaunchKernelGGL(mfma_i8_pair128_kernel<2>, dim3(a.tiles_m * a.tiles_n), dim3(512), 0, s, a);
+        else if (tile == kRing8SmallTile)
+            hipLaunchKernelGGL(mfma_i8_pair128_kernel<1>, dim3(a.tiles_m * a.tiles_n), dim3(256), 0, s, a);
         else
             hipLaunchKernelGGL(mfma_i8_pair_kernel, dim3(a.tiles_m * a.tiles_n), dim3(256), 0, s, a);
         return hipGetLastError();

@@ -859,7 +859,8 @@ __global__ __launch_bounds__(256) void mfma_f16_pair_kernel(RingArgs args)
 // of 32 rows, as in the 256 x 256 rings; element (row, col) of a round sits
 // at row 256 + 16 ((col / 4) ^ 4 ((row / 4) % 4)) + 4 (col % 4), which keeps
 // both the 4-byte writes (lane (g, s) of block j at unit 4 (j ^ g) + s / 4)
-// and the 16-byte reads along the rows free of bank conflicts.
+// and the 16-byte reads along the rows free of bank conflicts.  acc holds the
+// sums already read out of the accumulator registers.
 template <int FM>
 __device__ __forceinline__ void store_c_staged_w64(const floatx4 (&acc)[FM][4], float alpha, uint8_t *lds, int wave,
                                                    int lane, float *Cw, int ldc, int rows_left, int cols_left, bool vec)
@@ -879,7 +880,7 @@ __device__ __forceinline__ void store_c_staged_w64(const floatx4 (&acc)[FM][4], 
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     *reinterpret_cast<float *>(w + (16 * ii + 4 * g + r) * 256 + (4 * (j ^ g) + (s16 >> 2)) * 16 +
-                                               (s16 & 3) * 4) = dgor_acc_read(acc[2 * q + ii][j][r]) * alpha;
+                                               (s16 & 3) * 4) = acc[2 * q + ii][j][r] * alpha;
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
             const int row = (lane >> 4) + 4 * t, c = lane & 15;
@@ -915,6 +916,13 @@ __device__ __forceinline__ void store_c_staged_w64(const floatx4 (&acc)[FM][4], 
 //     the swizzle gives the eight rows eight distinct unit pairs.
 //   Pipeline, waits and the fragment order as in the pair ring, with 16
 //   MFMAs, 8 fragment reads and 4 loads a wavefront and stage.
+//   KS = 2 (shapes with at most one tile per compute unit, whose second
+//   workgroup slot would stay empty): eight wavefronts in two groups of
+//   four, group g over the g-th half of the k-stages (A, B and K shifted to
+//   the group's k range) through a ring of its own (160 KB in all); both
+//   groups run the same number of stages, so they meet at the same
+//   barriers; at the end group 1 hands its sums to group 0 through its ring,
+//   which adds them in that fixed order and stores C.
 namespace pair128 {
 constexpr int A_PAIR_BYTES = 128 * 64 * 2;           // 16 KB
 constexpr int A_PAIRS = 3;
@@ -923,22 +931,29 @@ constexpr int B_REGION = A_PAIRS * A_PAIR_BYTES;     // 48 KB
 constexpr int LDS_BYTES = B_REGION + 4 * B_BYTES;    // 80 KB: two workgroups a CU
 }  // namespace pair128
 
-template <class Op>
-__global__ __launch_bounds__(256, 2) void mfma_f16_pair128_kernel(RingArgs args)
+template <class Op, int KS>
+__global__ __launch_bounds__(256 * KS, 2 / KS) void mfma_f16_pair128_kernel(RingArgs args)
 {
     using namespace pair128;
     constexpr int BK = pipe::BK;
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds_all[KS * LDS_BYTES];
+    const int wave_all = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int grp = wave_all >> 2;
+    uint8_t *const lds = lds_all + grp * LDS_BYTES;
     const uint32_t ring = lds_address(lds);
-    const int M = args.M, N = args.N, K = args.K, lda = args.lda, ldb = args.ldb;
-    const uint16_t *__restrict__ A = (const uint16_t *)args.A;
-    const uint16_t *__restrict__ B = (const uint16_t *)args.B;
+    const int M = args.M, N = args.N, lda = args.lda, ldb = args.ldb;
+    const int steps_all = (args.K + BK - 1) / BK;
+    const int steps = (steps_all + KS - 1) / KS;
+    const int kbase = grp * steps * BK;
+    const int K = args.K < kbase + steps * BK ? args.K - kbase : steps * BK;   // the group's k extent
+    const uint16_t *__restrict__ A = (const uint16_t *)args.A + kbase;
+    const uint16_t *__restrict__ B = (const uint16_t *)args.B + (size_t)kbase * ldb;
 
     int tm, tn;
     dgor_tile_of_block((int)blockIdx.x, args.tiles_m, args.tiles_n, args.group_m, tm, tn);
     const int m0 = tm * 128, n0 = tn * 128;
     const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int wave = wave_all & 3;
     const int wr = (wave >> 1) * 64, wc = (wave & 1) * 64;
     constexpr uint32_t OOB = 0x80000000u;
 
@@ -1091,7 +1106,6 @@ __global__ __launch_bounds__(256, 2) void mfma_f16_pair128_kernel(RingArgs args)
             fread(R0, r, fa0, fb0);
     }
 
-    const int steps = (K + BK - 1) / BK;
     uint32_t pa = 0;
     for (int t = 0; t < steps; t += 2) {
         const uint32_t pa1 = next_pair(pa), pa2 = next_pair(pa1);
@@ -1106,13 +1120,50 @@ __global__ __launch_bounds__(256, 2) void mfma_f16_pair128_kernel(RingArgs args)
     __builtin_amdgcn_s_waitcnt(wait_vmcnt_lgkm0(0));
     __builtin_amdgcn_s_barrier();
     dgor_acc_hazard_wait();
+    floatx4 tot[4][4];
+    if constexpr (KS == 2) {
+        floatx4 *part = reinterpret_cast<floatx4 *>(lds_all + LDS_BYTES);
+        if (grp == 1) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    floatx4 v;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        v[r] = dgor_acc_read(acc[i][j][r]);
+                    part[((i * 4 + j) * 4 + wave) * 64 + lane] = v;
+                }
+        }
+        __builtin_amdgcn_s_barrier();
+        if (grp == 1)
+            return;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const floatx4 v = part[((i * 4 + j) * 4 + wave) * 64 + lane];
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    tot[i][j][r] = dgor_acc_read(acc[i][j][r]) + v[r];
+            }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    tot[i][j][r] = dgor_acc_read(acc[i][j][r]);
+    }
     {
         const int ldc = args.ldc;
         float *Cw = args.C + (size_t)(m0 + wr) * ldc + n0 + wc;
         const bool vec = ((uintptr_t)Cw & 15) == 0 && (ldc & 3) == 0;
-        store_c_staged_w64<4>(acc, args.alpha, lds, wave, lane, Cw, ldc, M - m0 - wr, N - n0 - wc, vec);
+        store_c_staged_w64<4>(tot, args.alpha, lds, wave, lane, Cw, ldc, M - m0 - wr, N - n0 - wc, vec);
     }
 }
+
 
 template <class Op, int BM, int BN, int BK, int WM, int WN>
 hipError_t launch_cfg(const Problem &p, const gemm_plan &plan, hipStream_t s)
@@ -1172,8 +1223,12 @@ hipError_t launch_op(const Problem &p, const gemm_plan &plan, hipStream_t s)
     }
     if (plan.tile_m == 128 && plan.tile_n == 128) {
         if (f16_ring128_applies(p.vec_a, p.vec_b, p.N, p.K)) {
-            hipLaunchKernelGGL((mfma_f16_pair128_kernel<Op>), dim3(plan.grid_x * plan.grid_y), dim3(256), 0, s,
-                               ring_args_nn(p, plan));
+            if (plan.threads == 512)   // two groups over k
+                hipLaunchKernelGGL((mfma_f16_pair128_kernel<Op, 2>), dim3(plan.grid_x * plan.grid_y), dim3(512), 0,
+                                   s, ring_args_nn(p, plan));
+            else
+                hipLaunchKernelGGL((mfma_f16_pair128_kernel<Op, 1>), dim3(plan.grid_x * plan.grid_y), dim3(256), 0,
+                                   s, ring_args_nn(p, plan));
             return hipGetLastError();
         }
         return launch_cfg<Op, 128, 128, 32, 2, 2>(p, plan, s);

@@ -181,7 +181,9 @@ typedef struct {
     int lds_stages;     /* LDS k-stages in flight (1, 2, or a ring of 4) */
     int lds_bytes;      /* LDS per workgroup, padding included */
     int tile_bytes;     /* bytes of one unpadded A tile plus one B tile */
-    int outputs_per_thread; /* C elements each thread accumulates */
+    int outputs_per_thread; /* C elements each thread accumulates (over its
+                               group's share of k, where a workgroup runs
+                               two groups of wavefronts over halves of k) */
     int vector_a;       /* 1 if A is read with 128-bit loads */
     int vector_b;       /* 1 if B is read with 128-bit loads */
     int vector_c;       /* 1 if C is written with 128-bit stores */

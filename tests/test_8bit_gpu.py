@@ -208,18 +208,22 @@ def test_8bit_ring_with_c_off_16_byte_alignment(fmt, c_off):
     check(fmt, got[c_off:c_off + M * N].reshape(M, N), A, B, f"{fmt} C offset {c_off}", exact=True)
 
 
-# Shapes for each ring tile: (M, N, K, tile); ragged M and N edges, k tails
-# of 16 .. 48 past a 64-deep step, one to many steps
-TILE_SHAPES = [(4000, 4016, 16, 256), (4000, 4016, 80, 256), (4000, 4016, 208, 256), (4000, 4016, 1040, 256),
-               (1000, 1008, 1024, 128), (129, 144, 16, 128), (2000, 1008, 4112, 128), (2500, 2512, 144, 128)]
+# Shapes for each ring tile: (M, N, K, tile, groups of wavefronts over k);
+# ragged M and N edges, k tails of 16 .. 48 past a 64-deep step, one to many
+# steps (with two groups: none or one past K for the second group, and odd
+# step counts)
+TILE_SHAPES = [(4000, 4016, 16, 256, 1), (4000, 4016, 80, 256, 1), (4000, 4016, 208, 256, 1),
+               (4000, 4016, 1040, 256, 1),
+               (1000, 1008, 1024, 128, 2), (129, 144, 16, 128, 2), (2000, 1008, 4112, 128, 2), (1000, 1008, 208, 128, 2),
+               (2500, 2512, 144, 128, 1), (2000, 2064, 1040, 128, 1), (2000, 2064, 16, 128, 1)]
 
 
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("shape", TILE_SHAPES, ids=lambda s: "x".join(map(str, s)))
 def test_8bit_both_ring_tiles(fmt, shape):
-    M, N, K, tile = shape
+    M, N, K, tile, groups = shape
     plan = dg.plan(fmt, M, N, K)
-    assert plan["variant"] == dg.R8_MFMA_8BIT and plan["tile_m"] == tile
+    assert plan["variant"] == dg.R8_MFMA_8BIT and plan["tile_m"] == tile and plan["threads"] == 256 * groups
     say("8bit ring tile", fmt, tile, (M, N, K))
     A, B = mats(fmt, M, N, K, 4800 + K)
     check(fmt, run(fmt, dg.AUTO, A, B), A, B, f"{fmt} {shape}")

@@ -192,7 +192,10 @@ def test_direct_load_tile_follows_the_spread_of_tiles_over_compute_units():
     assert tile(True, 4096, 4096, 4096) == 256
     assert tile(True, 3072, 3072, 3072) == 256      # 144 ring tiles
     assert tile(True, 2048, 2048, 2048) == 128      # 64 ring tiles: too few; the 128 x 128 ring
-    assert dg.plan(True, 2048, 2048, 2048)["lds_bytes"] == 81920
+    # one tile per unit: two groups of four wavefronts over halves of k, two 80 KB rings
+    assert dg.plan(True, 2048, 2048, 2048)["lds_bytes"] == 163840 and dg.plan(True, 2048, 2048, 2048)["threads"] == 512
+    assert tile(True, 2560, 2560, 2560) == 128 and dg.plan(True, 2560, 2560, 2560)["threads"] == 256   # 400 tiles
+    assert dg.plan(True, 2560, 2560, 2560)["lds_bytes"] == 81920
     assert tile(True, 1000, 1001, 1000) == 64       # rows not whole 16-byte units: register-staged
     # K % 8 != 0: A's rows are not whole 16-byte units, so no direct loads
     assert tile(True, 4096, 4096, 4095) == 128 and dg.plan(True, 4096, 4096, 4095)["vector_a"] == 0
@@ -266,9 +269,12 @@ def test_8bit_ring_tile_follows_the_spread_of_tiles_over_compute_units():
         assert tile(kind, 2048, 2048, 2048) == 128
         assert tile(kind, 300, 272, 80) == 128
         p = dg.plan(kind, 2048, 2048, 2048)
-        # three 16 KB A pair buffers and four 8 KB B steps: two workgroups a unit
-        assert p["lds_bytes"] == 81920 and p["lds_stages"] == 4 and p["tile_k"] == 64
+        # three 16 KB A pair buffers and four 8 KB B steps; with one tile per
+        # unit, two such rings for two groups of wavefronts over halves of k
+        assert p["lds_bytes"] == 163840 and p["threads"] == 512 and p["lds_stages"] == 4 and p["tile_k"] == 64
         assert p["grid_x"] * p["grid_y"] == 256 and p["outputs_per_thread"] == 64 and p["tile_bytes"] == 16384
+        p = dg.plan(kind, 2560, 2560, 2560)   # 400 tiles: one group, two workgroups a unit
+        assert p["tile_m"] == 128 and p["lds_bytes"] == 81920 and p["threads"] == 256
     # 144 ring tiles against 576 of 128^2: INT8 takes the smaller tile, FP8
     # (whose larger tile runs faster with units idle) the larger
     assert tile("i8", 3072, 3072, 3072) == 128

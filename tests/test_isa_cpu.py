@@ -58,12 +58,12 @@ def test_every_layout_variant_is_generated(ring):
     # k-contiguous A (pair kernel) and a k-strided A (pipe kernel); FP32:
     # op(A) x op(B) x (overwrite, accumulate); 8-bit: the row-major product in
     # the two FP8 formats and once for INT8, at each of the two tiles; the
-    # 64 x 64 ring with one and with two groups over k; the 16-bit 128 x 128
-    # ring in both formats
-    want = {"mfma_f16_pipe_kernel": 8, "mfma_f16_pair_kernel": 8, "mfma_f16_pair128_kernel": 2,
+    # 64 x 64 ring with one and with two groups over k; the 16-bit and 8-bit
+    # 128 x 128 rings in each format with one and with two groups over k
+    want = {"mfma_f16_pipe_kernel": 8, "mfma_f16_pair_kernel": 8, "mfma_f16_pair128_kernel": 4,
             "mfma_f32_ring_kernel": 8,
             "mfma_f32_small_ring_kernel": 2, "mfma_8bit_ring_kernel": 2, "mfma_i8_pair_kernel": 1,
-            "mfma_i8_pair128_kernel": 1, "mfma_fp8_pair128_kernel": 2}[kernel]
+            "mfma_i8_pair128_kernel": 2, "mfma_fp8_pair128_kernel": 4}[kernel]
     assert len(_instances(asm, kernel)) == want
 
 

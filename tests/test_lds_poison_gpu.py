@@ -80,15 +80,18 @@ def _check(lib, fmt, M, N, K, seed, trans_a=False):
 CASES = [
     ("f16", 8000, 4104, [8, 32, 40, 64, 72, 96, 104, 136]),     # 16-bit 256^2 pair ring
     ("bf16", 8000, 4104, [8, 40, 104, 136]),
-    ("f16", 1000, 1032, [8, 32, 40, 72, 136]),                  # 16-bit 128^2 ring
+    ("f16", 1000, 1032, [8, 32, 40, 72, 136, 1000]),            # 16-bit 128^2 ring, two groups over k
     ("bf16", 1000, 1032, [8, 40, 136]),
+    ("f16", 2000, 2056, [8, 32, 40, 72, 136]),                  # the same, one group
     ("f32", 4000, 4092, [4, 16, 20, 32, 36, 48, 52, 68]),       # FP32 256^2 ring
     ("f32", 1000, 1000, [32, 64, 96, 128, 200, 384]),           # FP32 64^2 ring (32-deep stages)
     ("f32", 1000, 1000, [512, 528, 1040]),                      # the same, two groups over k
     ("f32", 4000, 2044, [16, 100]),                             # FP32 128^2 two-stage kernel
-    ("e4m3", 520, 784, [16, 64, 80, 144, 320]),                 # 8-bit 128^2 rings
+    ("e4m3", 520, 784, [16, 64, 80, 144, 320]),                 # 8-bit 128^2 rings, two groups over k
     ("e5m2", 520, 784, [16, 80, 208]),
     ("i8", 520, 784, [16, 48, 64, 128, 192, 320]),
+    ("e4m3", 2000, 2064, [16, 80, 208]),                        # the same, one group
+    ("i8", 2000, 2064, [16, 80, 208]),
     ("e4m3", 4000, 4016, [16, 64, 80, 144, 320]),               # 8-bit 256^2 rings
     ("e5m2", 4000, 4016, [16, 80, 208]),
     ("i8", 4000, 4016, [16, 48, 64, 128, 192, 320]),

@@ -155,15 +155,18 @@ def test_f16_large_tile_stage_counts(K, fmt):
     assert_within(run(fmt, dg.AUTO, A, B), ref, tol_f16(K, ref), f"floats K={K}")
 
 
-# The 128 x 128 16-bit ring: the same stage counts on a shape with ragged
-# M and N (1000 = 7 x 128 + 104, 1032 = 8 x 128 + 8) that takes it.
+# The 128 x 128 16-bit ring: the same stage counts on shapes with ragged M
+# and N that take it, with one group of wavefronts (2000 x 2056: 272 tiles)
+# and with two groups over halves of the k-stages (1000 x 1032: 64 tiles;
+# K = 8 .. 40 leave the second group no stage, or one past K; K = 2088 gives
+# 33 + 33 stages with a tail).
 @pytest.mark.parametrize("fmt", ["f16", "bf16"])
-@pytest.mark.parametrize("K", [8, 32, 40, 64, 72, 96, 104, 136])
-def test_f16_mid_tile_ring_stage_counts(K, fmt):
-    M, N = 1000, 1032
+@pytest.mark.parametrize("M,N,K,groups", [(2000, 2056, K, 1) for K in (8, 32, 40, 64, 72, 96, 104, 136)]
+                         + [(1000, 1032, K, 2) for K in (8, 32, 40, 64, 72, 96, 104, 136, 1000, 2088)])
+def test_f16_mid_tile_ring_stage_counts(M, N, K, groups, fmt):
     p = dg.plan(True, M, N, K)
-    assert (p["tile_m"], p["tile_n"], p["lds_bytes"]) == (128, 128, 81920)
-    say(fmt, "128 x 128 ring stages", (M, N, K))
+    assert (p["tile_m"], p["tile_n"], p["threads"], p["lds_bytes"]) == (128, 128, 256 * groups, 81920 * groups)
+    say(fmt, "128 x 128 ring stages", (M, N, K), groups)
     A, B = ints(M, N, K, 63 + K, fmt)
     assert_bits_equal(run(fmt, dg.AUTO, A, B), oracle_gemm(A, B), f"ints K={K}")
     A, B = floats(M, N, K, 64 + K, fmt)
