@@ -922,7 +922,7 @@ __device__ __forceinline__ void store_c_staged_w64(const floatx4 (&acc)[FM][4], 
 //   the group's k range) through a ring of its own (160 KB in all); both
 //   groups run the same number of stages, so they meet at the same
 //   barriers; at the end group 1 hands its sums to group 0 through its ring,
-//   and group 0 adds them to its own in that fixed order and stores C.
+//   which adds them in that fixed order and stores C.
 namespace pair128 {
 constexpr int A_PAIR_BYTES = 128 * 64 * 2;           // 16 KB
 constexpr int A_PAIRS = 3;

@@ -631,8 +631,8 @@ hipError_t launch_ring32_t(const RingArgs &a, hipStream_t s)
 // group g taking the g-th half of the k-stages through a ring of its own
 // (128 KB in all); both groups run the same number of stages (the second's
 // last one past K loads zeros), so they meet at the same barriers, and at
-// the end group 1 hands its sums to group 0 through LDS, and group 0 adds
-// them to its own in that fixed order and stores C.
+// the end group 1 hands its sums to group 0 through LDS, which adds them in
+// that fixed order and stores C.
 namespace f32small {
 __host__ __device__ constexpr int fa(int r, int U) { return (r * U / 16) & (U - 1); }
 __host__ __device__ constexpr int fb(int k) { return 4 * ((k >> 2) & 3); }
