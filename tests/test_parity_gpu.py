@@ -406,6 +406,16 @@ def test_non_default_stream_and_determinism():
     h2 = dg.gemm_f16_f32acc(to_dev(A16), to_dev(B16), stream=s)
     s.synchronize()
     assert torch.equal(h1, h2)
+    # FP8 on the 128 x 128 ring with two groups over k (their FP32 sums
+    # added in a fixed order): the same bits run to run as well
+    E = inputs.matrices(1000, 1008, 1024, 43, "uniform", "e4m3")
+    assert dg.plan("e4m3", 1000, 1008, 1024)["threads"] == 512
+    ea = torch.from_numpy(E[0]).to("cuda").view(torch.float8_e4m3fn)
+    eb = torch.from_numpy(E[1]).to("cuda").view(torch.float8_e4m3fn)
+    f1 = dg.gemm_e4m3_f32acc(ea, eb, stream=s)
+    f2 = dg.gemm_e4m3_f32acc(ea, eb, stream=s)
+    s.synchronize()
+    assert torch.equal(f1, f2)
 
 
 def test_concurrent_calls_from_threads_on_their_own_streams():
